@@ -1,0 +1,342 @@
+/*
+ * CPU oracle for fused MaxSim scoring -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the package's smoke check and the benchmark's CPU-baseline
+ * leg may load this library. The HIP library never links, calls or shares code
+ * with it. It is a plain, slow, obviously correct evaluation of the
+ * definitions, in double precision for floating-point inputs and in 64-bit
+ * integers for int8 inputs, multithreaded only over independent outputs.
+ *
+ * Sources (page title, then the passage):
+ *   [FM]  "Flash-MaxSim" (academ.us article 2605.29517):
+ *         Eq. (1) MaxSim; Sec. 4.1.1 online max with -inf masking;
+ *         Sec. 4.2.1 Eqs. (2)-(3) closed-form gradients;
+ *         Sec. 4.2.2 inverse-grid CSR (bincount, cumsum, stable argsort);
+ *         Sec. 4.3.1 INT8 x INT8; Sec. 4.3.2 padding-free cu_seqlens.
+ *   [LIK] "late-interaction-kernels design notes" (docs/design.md):
+ *         "Problem" (masks), "Forward" pseudocode (strict '>' update,
+ *         argmax starts at 0, finalise m <- finite(m) & q_active ? m : 0),
+ *         "Backward" formulas with q_mask, "Varlen / packed path"
+ *         (empty sequences contribute zero).
+ *
+ * Readings where the pages leave a step open:
+ *   - ties go to the lowest doc-token index (strict '>' in ascending t);
+ *   - a q-masked row still gets the real argmax; only its score term is 0;
+ *   - a doc with no valid token contributes 0 and keeps argmax 0;
+ *   - varlen argmax is [Nq, Nd, max_lq], doc-relative, rows past Lq_i are 0;
+ *   - the CSR holds every source (i, j, s), masked ones included; masks enter
+ *     the gradients only through w = g[i,j] * q_mask[i,s] * live(j), where
+ *     live(j) says doc j has at least one valid token;
+ *   - a CSR column index is the flat source index (i*Nd + j)*Lq + s.
+ *
+ * Every entry point returns 0 on success and a negative value when an input
+ * breaks a stated precondition (argmax outside [0, Ld), non-monotone offsets).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* A minimal parallel-for: each worker takes a contiguous block of items.    */
+/* ------------------------------------------------------------------------ */
+typedef void (*item_fn)(void* ctx, int64_t item);
+
+typedef struct {
+    item_fn fn;
+    void* ctx;
+    int64_t lo, hi;
+} span_t;
+
+static void* run_span(void* p)
+{
+    span_t* s = (span_t*)p;
+    for (int64_t k = s->lo; k < s->hi; ++k) s->fn(s->ctx, k);
+    return NULL;
+}
+
+static void parallel_for(int64_t n, int nthreads, item_fn fn, void* ctx)
+{
+    if (n <= 0) return;
+    if (nthreads < 1) nthreads = 1;
+    if ((int64_t)nthreads > n) nthreads = (int)n;
+    if (nthreads == 1) {
+        for (int64_t k = 0; k < n; ++k) fn(ctx, k);
+        return;
+    }
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    span_t* sp = (span_t*)malloc(sizeof(span_t) * (size_t)nthreads);
+    int started = 0;
+    for (int w = 0; w < nthreads; ++w) {
+        sp[w].fn = fn;
+        sp[w].ctx = ctx;
+        sp[w].lo = n * w / nthreads;
+        sp[w].hi = n * (w + 1) / nthreads;
+        if (pthread_create(&th[w], NULL, run_span, &sp[w]) != 0) break;
+        ++started;
+    }
+    /* anything a failed thread creation left over runs here */
+    for (int w = started; w < nthreads; ++w) run_span(&sp[w]);
+    for (int w = 0; w < started; ++w) pthread_join(th[w], NULL);
+    free(th);
+    free(sp);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One (query, doc) pair of Eq. (1): sum over query rows s of the max over   */
+/* valid doc rows t of <Q[s], D[t]>, following the Forward pseudocode.       */
+/* ------------------------------------------------------------------------ */
+static double pair_f64(const double* Qi, const double* Dj, int64_t Lq, int64_t Ld, int64_t d,
+                       const uint8_t* qm, const uint8_t* dm, int32_t* arg)
+{
+    double acc = 0.0;
+    for (int64_t s = 0; s < Lq; ++s) {
+        const double* q = Qi + s * d;
+        double best = -INFINITY;
+        int64_t at = 0;
+        for (int64_t t = 0; t < Ld; ++t) {
+            if (dm && !dm[t]) continue; /* masked token is -inf: never selected */
+            const double* x = Dj + t * d;
+            double v = 0.0;
+            for (int64_t k = 0; k < d; ++k) v += q[k] * x[k];
+            if (v > best) { /* strict: the lowest index keeps a tie */
+                best = v;
+                at = t;
+            }
+        }
+        if (arg) arg[s] = (int32_t)at;
+        if (isfinite(best) && (!qm || qm[s])) acc += best;
+    }
+    return acc;
+}
+
+typedef struct {
+    const double *Q, *D;
+    int64_t Nq, Nd, Lq, Ld, d;
+    const uint8_t *qm, *dm;
+    double* scores;
+    int32_t* argmax;
+} dense_ctx;
+
+static void dense_item(void* p, int64_t k)
+{
+    dense_ctx* c = (dense_ctx*)p;
+    int64_t i = k / c->Nd, j = k % c->Nd;
+    c->scores[k] = pair_f64(c->Q + i * c->Lq * c->d, c->D + j * c->Ld * c->d, c->Lq, c->Ld, c->d,
+                            c->qm ? c->qm + i * c->Lq : NULL, c->dm ? c->dm + j * c->Ld : NULL,
+                            c->argmax ? c->argmax + k * c->Lq : NULL);
+}
+
+/* Cross-product forward. Q [Nq,Lq,d], D [Nd,Ld,d]; masks [Nq,Lq], [Nd,Ld] of
+ * 0/1 bytes or NULL; scores [Nq,Nd]; argmax [Nq,Nd,Lq] or NULL. */
+int oracle_fwd_f64(const double* Q, const double* D, int64_t Nq, int64_t Nd, int64_t Lq,
+                   int64_t Ld, int64_t d, const uint8_t* q_mask, const uint8_t* d_mask,
+                   double* scores, int32_t* argmax, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return -1;
+    dense_ctx c = {Q, D, Nq, Nd, Lq, Ld, d, q_mask, d_mask, scores, argmax};
+    parallel_for(Nq * Nd, nthreads, dense_item, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Padding-free form: sequence b occupies rows [cu[b], cu[b+1]).             */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const double *Q, *D;
+    const int32_t *cu_q, *cu_d;
+    int64_t Nq, Nd, max_lq, d;
+    double* scores;
+    int32_t* argmax;
+} varlen_ctx;
+
+static void varlen_item(void* p, int64_t k)
+{
+    varlen_ctx* c = (varlen_ctx*)p;
+    int64_t i = k / c->Nd, j = k % c->Nd;
+    int64_t q0 = c->cu_q[i], lq = (int64_t)c->cu_q[i + 1] - q0;
+    int64_t d0 = c->cu_d[j], ld = (int64_t)c->cu_d[j + 1] - d0;
+    int32_t* arg = c->argmax ? c->argmax + k * c->max_lq : NULL;
+    if (arg)
+        for (int64_t s = 0; s < c->max_lq; ++s) arg[s] = 0;
+    c->scores[k] = pair_f64(c->Q + q0 * c->d, c->D + d0 * c->d, lq, ld, c->d, NULL, NULL, arg);
+}
+
+int oracle_fwd_varlen_f64(const double* Q, const int32_t* cu_q, int64_t Nq, int64_t max_lq,
+                          const double* D, const int32_t* cu_d, int64_t Nd, int64_t d,
+                          double* scores, int32_t* argmax, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0) return -1;
+    for (int64_t i = 0; i < Nq; ++i) {
+        int64_t l = (int64_t)cu_q[i + 1] - cu_q[i];
+        if (l < 0 || l > max_lq) return -2;
+    }
+    for (int64_t j = 0; j < Nd; ++j)
+        if (cu_d[j + 1] < cu_d[j]) return -2;
+    varlen_ctx c = {Q, D, cu_q, cu_d, Nq, Nd, max_lq, d, scores, argmax};
+    parallel_for(Nq * Nd, nthreads, varlen_item, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT8 x INT8 with one symmetric scale per tensor: exact integer max-sum,   */
+/* then score = q_scale * d_scale * sum.                                     */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const int8_t *Q, *D;
+    int64_t Nq, Nd, Lq, Ld, d;
+    const uint8_t *qm, *dm;
+    int64_t* score_i;
+    double* score_f;
+    double q_scale, d_scale;
+    int32_t* argmax;
+} i8_ctx;
+
+static void i8_item(void* p, int64_t k)
+{
+    i8_ctx* c = (i8_ctx*)p;
+    int64_t i = k / c->Nd, j = k % c->Nd;
+    const int8_t* Qi = c->Q + i * c->Lq * c->d;
+    const int8_t* Dj = c->D + j * c->Ld * c->d;
+    const uint8_t* qm = c->qm ? c->qm + i * c->Lq : NULL;
+    const uint8_t* dm = c->dm ? c->dm + j * c->Ld : NULL;
+    int32_t* arg = c->argmax ? c->argmax + k * c->Lq : NULL;
+    int64_t acc = 0;
+    for (int64_t s = 0; s < c->Lq; ++s) {
+        const int8_t* q = Qi + s * c->d;
+        int found = 0;
+        int64_t best = 0, at = 0;
+        for (int64_t t = 0; t < c->Ld; ++t) {
+            if (dm && !dm[t]) continue;
+            const int8_t* x = Dj + t * c->d;
+            int64_t v = 0;
+            for (int64_t e = 0; e < c->d; ++e) v += (int64_t)q[e] * (int64_t)x[e];
+            if (!found || v > best) {
+                found = 1;
+                best = v;
+                at = t;
+            }
+        }
+        if (arg) arg[s] = (int32_t)at;
+        if (found && (!qm || qm[s])) acc += best;
+    }
+    c->score_i[k] = acc;
+    if (c->score_f) c->score_f[k] = (double)acc * c->q_scale * c->d_scale;
+}
+
+int oracle_fwd_i8(const int8_t* Q, double q_scale, const int8_t* D, double d_scale, int64_t Nq,
+                  int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
+                  const uint8_t* d_mask, int64_t* score_i, double* score_f, int32_t* argmax,
+                  int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return -1;
+    i8_ctx c = {Q, D, Nq, Nd, Lq, Ld, d, q_mask, d_mask, score_i, score_f, q_scale, d_scale, argmax};
+    parallel_for(Nq * Nd, nthreads, i8_item, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward through the saved argmax: Eqs. (2)-(3) with the q_mask factor of */
+/* the design notes, the CSR by counting sort (histogram, exclusive scan,    */
+/* fill in ascending source order = stable argsort of destinations).         */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const double *Q, *D, *g;
+    int64_t Nq, Nd, Lq, Ld, d;
+    const uint8_t* qm;
+    const uint8_t* live;
+    const int32_t* argmax;
+    const int32_t *row_ptr, *col_idx;
+    double *dQ, *dD;
+} bwd_ctx;
+
+static double weight(const bwd_ctx* c, int64_t i, int64_t j, int64_t s)
+{
+    if (!c->live[j]) return 0.0;
+    if (c->qm && !c->qm[i * c->Lq + s]) return 0.0;
+    return c->g[i * c->Nd + j];
+}
+
+/* Eq. (2): dQ[i,s] = sum over j ascending of w * D[j, argmax[i,j,s]] */
+static void dq_item(void* p, int64_t r)
+{
+    bwd_ctx* c = (bwd_ctx*)p;
+    int64_t i = r / c->Lq, s = r % c->Lq;
+    double* out = c->dQ + r * c->d;
+    for (int64_t k = 0; k < c->d; ++k) out[k] = 0.0;
+    for (int64_t j = 0; j < c->Nd; ++j) {
+        double w = weight(c, i, j, s);
+        if (w == 0.0) continue;
+        int64_t t = c->argmax[(i * c->Nd + j) * c->Lq + s];
+        const double* x = c->D + (j * c->Ld + t) * c->d;
+        for (int64_t k = 0; k < c->d; ++k) out[k] += w * x[k];
+    }
+}
+
+/* Eq. (3): dD[j,t] = sum over the sources listed in CSR row (j,t), in order */
+static void dd_item(void* p, int64_t r)
+{
+    bwd_ctx* c = (bwd_ctx*)p;
+    double* out = c->dD + r * c->d;
+    for (int64_t k = 0; k < c->d; ++k) out[k] = 0.0;
+    for (int64_t e = c->row_ptr[r]; e < c->row_ptr[r + 1]; ++e) {
+        int64_t src = c->col_idx[e];
+        int64_t s = src % c->Lq;
+        int64_t ij = src / c->Lq;
+        int64_t i = ij / c->Nd, j = ij % c->Nd;
+        double w = weight(c, i, j, s);
+        if (w == 0.0) continue;
+        const double* q = c->Q + (i * c->Lq + s) * c->d;
+        for (int64_t k = 0; k < c->d; ++k) out[k] += w * q[k];
+    }
+}
+
+int oracle_bwd_f64(const double* Q, const double* D, int64_t Nq, int64_t Nd, int64_t Lq,
+                   int64_t Ld, int64_t d, const uint8_t* q_mask, const uint8_t* d_mask,
+                   const int32_t* argmax, const double* g, double* dQ, double* dD,
+                   int32_t* row_ptr, int32_t* col_idx, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return -1;
+    int64_t nsrc = Nq * Nd * Lq, nrows = Nd * Ld;
+    if (nsrc > 0 && Ld == 0) return -2; /* no destination exists */
+    for (int64_t e = 0; e < nsrc; ++e)
+        if (argmax[e] < 0 || argmax[e] >= Ld) return -2;
+
+    uint8_t* live = (uint8_t*)calloc((size_t)(Nd > 0 ? Nd : 1), 1);
+    for (int64_t j = 0; j < Nd; ++j) {
+        int any = 0;
+        for (int64_t t = 0; t < Ld && !any; ++t) any = d_mask ? d_mask[j * Ld + t] != 0 : 1;
+        live[j] = (uint8_t)any;
+    }
+
+    /* histogram of destinations (bincount) */
+    int64_t* cnt = (int64_t*)calloc((size_t)(nrows + 1), sizeof(int64_t));
+    for (int64_t src = 0; src < nsrc; ++src) {
+        int64_t j = (src / Lq) % Nd;
+        cnt[j * Ld + argmax[src]] += 1;
+    }
+    /* exclusive scan (cumsum shifted by one) */
+    int64_t run = 0;
+    for (int64_t r = 0; r < nrows; ++r) {
+        row_ptr[r] = (int32_t)run;
+        run += cnt[r];
+    }
+    row_ptr[nrows] = (int32_t)run;
+    /* fill in ascending source order: the stable argsort of destinations */
+    for (int64_t r = 0; r < nrows; ++r) cnt[r] = row_ptr[r];
+    for (int64_t src = 0; src < nsrc; ++src) {
+        int64_t j = (src / Lq) % Nd;
+        int64_t r = j * Ld + argmax[src];
+        col_idx[cnt[r]++] = (int32_t)src;
+    }
+    free(cnt);
+
+    bwd_ctx c = {Q, D, g, Nq, Nd, Lq, Ld, d, q_mask, live, argmax, row_ptr, col_idx, dQ, dD};
+    parallel_for(Nq * Lq, nthreads, dq_item, &c);
+    parallel_for(nrows, nthreads, dd_item, &c);
+    free(live);
+    return 0;
+}
+
+int oracle_version(void) { return 1; }

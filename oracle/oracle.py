@@ -1,0 +1,159 @@
+"""Python front end of the CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this module. It loads ``liboracle.so`` (built from
+``maxsim_oracle.c`` with gcc, never with the HIP toolchain) and passes it
+inputs widened exactly to float64 (fp16/bf16/fp32 -> double is exact) or int8.
+
+Functions follow "Flash-MaxSim" Eq. (1), Sec. 4.2.1-4.2.2, Sec. 4.3 and the
+"late-interaction-kernels design notes" Forward / Backward / Varlen passages;
+the C source lists each reading taken where the pages leave a step open.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "maxsim_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C11 + pthreads)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        lib.oracle_fwd_f64.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i32]
+        lib.oracle_fwd_varlen_f64.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp, i32]
+        lib.oracle_fwd_i8.argtypes = [vp, dbl, vp, dbl, i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                                      vp, i32]
+        lib.oracle_bwd_f64.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, i32]
+        for f in (lib.oracle_fwd_f64, lib.oracle_fwd_varlen_f64, lib.oracle_fwd_i8,
+                  lib.oracle_bwd_f64):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening to a C-contiguous float64 array (torch or numpy input)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().double().contiguous().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _arr(x, dtype) -> Optional[np.ndarray]:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().contiguous().numpy()
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what}: input breaks a precondition (code {rc})")
+
+
+def fwd(Q, D, q_mask=None, d_mask=None, want_argmax=True, threads=None):
+    """Cross-product forward. Returns (scores float64 [Nq,Nd], argmax int32
+    [Nq,Nd,Lq] or None)."""
+    q = _f64(Q)
+    dd = _f64(D)
+    Nq, Lq, d = q.shape
+    Nd, Ld, d2 = dd.shape
+    assert d == d2
+    qm = _arr(q_mask, np.uint8)
+    dm = _arr(d_mask, np.uint8)
+    scores = np.zeros((Nq, Nd), np.float64)
+    arg = np.zeros((Nq, Nd, Lq), np.int32) if want_argmax else None
+    assert np.isfinite(q).all() and np.isfinite(dd).all()
+    rc = _load().oracle_fwd_f64(_p(q), _p(dd), Nq, Nd, Lq, Ld, d, _p(qm), _p(dm), _p(scores),
+                                _p(arg), threads or default_threads())
+    _check(rc, "fwd")
+    return scores, arg
+
+
+def fwd_varlen(Q, cu_q, max_lq, D, cu_d, want_argmax=True, threads=None):
+    """Padding-free forward. Returns (scores [Nq,Nd], argmax [Nq,Nd,max_lq] or None)."""
+    q = _f64(Q)
+    dd = _f64(D)
+    cq = _arr(cu_q, np.int32)
+    cd = _arr(cu_d, np.int32)
+    Nq, Nd = len(cq) - 1, len(cd) - 1
+    d = q.shape[1] if q.ndim == 2 else dd.shape[1]
+    scores = np.zeros((Nq, Nd), np.float64)
+    arg = np.zeros((Nq, Nd, max_lq), np.int32) if want_argmax else None
+    rc = _load().oracle_fwd_varlen_f64(_p(q), _p(cq), Nq, max_lq, _p(dd), _p(cd), Nd, d,
+                                       _p(scores), _p(arg), threads or default_threads())
+    _check(rc, "fwd_varlen")
+    return scores, arg
+
+
+def fwd_i8(Q, q_scale, D, d_scale, q_mask=None, d_mask=None, want_argmax=True, threads=None):
+    """INT8 forward. Returns (score_int int64 [Nq,Nd], score float64 [Nq,Nd],
+    argmax int32 [Nq,Nd,Lq] or None)."""
+    q = _arr(Q, np.int8)
+    dd = _arr(D, np.int8)
+    Nq, Lq, d = q.shape
+    Nd, Ld, _ = dd.shape
+    qm = _arr(q_mask, np.uint8)
+    dm = _arr(d_mask, np.uint8)
+    si = np.zeros((Nq, Nd), np.int64)
+    sf = np.zeros((Nq, Nd), np.float64)
+    arg = np.zeros((Nq, Nd, Lq), np.int32) if want_argmax else None
+    rc = _load().oracle_fwd_i8(_p(q), float(q_scale), _p(dd), float(d_scale), Nq, Nd, Lq, Ld, d,
+                               _p(qm), _p(dm), _p(si), _p(sf), _p(arg),
+                               threads or default_threads())
+    _check(rc, "fwd_i8")
+    return si, sf, arg
+
+
+def bwd(Q, D, argmax, grad_scores, q_mask=None, d_mask=None, threads=None):
+    """Backward through a saved argmax. Returns (dQ float64 [Nq,Lq,d],
+    dD float64 [Nd,Ld,d], row_ptr int32 [Nd*Ld+1], col_idx int32 [Nq*Nd*Lq])."""
+    q = _f64(Q)
+    dd = _f64(D)
+    Nq, Lq, d = q.shape
+    Nd, Ld, _ = dd.shape
+    a = _arr(argmax, np.int32)
+    g = _f64(grad_scores)
+    qm = _arr(q_mask, np.uint8)
+    dm = _arr(d_mask, np.uint8)
+    dQ = np.zeros((Nq, Lq, d), np.float64)
+    dD = np.zeros((Nd, Ld, d), np.float64)
+    rp = np.zeros(Nd * Ld + 1, np.int32)
+    ci = np.zeros(Nq * Nd * Lq, np.int32)
+    rc = _load().oracle_bwd_f64(_p(q), _p(dd), Nq, Nd, Lq, Ld, d, _p(qm), _p(dm), _p(a), _p(g),
+                                _p(dQ), _p(dD), _p(rp), _p(ci), threads or default_threads())
+    _check(rc, "bwd")
+    return dQ, dD, rp, ci

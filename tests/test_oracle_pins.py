@@ -1,0 +1,392 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* a worked example computed by hand (tests/golden/hand_example.json);
+* brute force by materialising S (tests/brute_force.py) on tiny inputs, with
+  masks, dead docs/queries, exact ties and empty varlen sequences;
+* closed forms and invariants the pages state or imply: self-score, chunked
+  sums (late-interaction-kernels design notes, "Long-query chunking"),
+  fully-masked doc -> 0, permutation invariance, power-of-two scaling,
+  padding-free == padded (Flash-MaxSim Sec. 5.5), int8 == scaled float;
+* special cases that reduce to a library routine (Ld = 1, Lq = 1);
+* backward: finite differences, the Euler identity of a bilinear form at a
+  fixed argmax, and the CSR against numpy's bincount/cumsum/stable argsort
+  (the construction Flash-MaxSim Sec. 4.2.2 names).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import brute_force as bf
+from maxsim_scoring_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _exact_grid(rng, shape, scale=8):
+    """Values k/scale with small integer k: every dot product is exact."""
+    return rng.integers(-scale, scale + 1, size=shape).astype(np.float64) / scale
+
+
+# ----------------------------------------------------------------- worked example
+
+def test_hand_example_forward(oracle_mod):
+    g = _gold("hand_example.json")
+    Q = np.array(g["Q"], np.float64)
+    D = np.array(g["D"], np.float64)
+    dm = np.array(g["d_mask"], np.uint8)
+    s, a = oracle_mod.fwd(Q, D, None, dm)
+    assert np.array_equal(s, np.array(g["scores"], np.float64))
+    assert np.array_equal(a, np.array(g["argmax"], np.int32))
+    v = g["q_mask_variant"]
+    s, a = oracle_mod.fwd(Q, D, np.array(v["q_mask"], np.uint8), dm)
+    assert np.array_equal(s, np.array(v["scores"], np.float64))
+    assert np.array_equal(a, np.array(v["argmax"], np.int32))
+
+
+def test_hand_example_backward(oracle_mod):
+    g = _gold("hand_example.json")
+    b = g["backward"]
+    Q = np.array(g["Q"], np.float64)
+    D = np.array(g["D"], np.float64)
+    dm = np.array(g["d_mask"], np.uint8)
+    arg = np.array(g["argmax"], np.int32)
+    dQ, dD, rp, ci = oracle_mod.bwd(Q, D, arg, np.array(b["grad_scores"], np.float64),
+                                    np.array(b["q_mask"], np.uint8), dm)
+    assert np.array_equal(dQ, np.array(b["dQ"], np.float64))
+    assert np.array_equal(dD, np.array(b["dD"], np.float64))
+    assert np.array_equal(rp, np.array(b["row_ptr"], np.int32))
+    assert np.array_equal(ci, np.array(b["col_idx"], np.int32))
+
+
+def test_hand_example_int8(oracle_mod):
+    g = _gold("hand_example.json")
+    t = g["int8"]
+    Q = np.array(g["Q"], np.int8)
+    D = np.array(g["D"], np.int8)
+    dm = np.array(g["d_mask"], np.uint8)
+    si, sf, a = oracle_mod.fwd_i8(Q, t["q_scale"], D, t["d_scale"], None, dm)
+    assert np.array_equal(si, np.array(t["score_int"], np.int64))
+    assert np.array_equal(sf, np.array(t["score"], np.float64))
+    assert np.array_equal(a, np.array(g["argmax"], np.int32))
+
+
+# ----------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(2, 3, 5, 7), (3, 4, 33, 70), (1, 5, 1, 1), (2, 2, 8, 0)])
+def test_brute_force_random(oracle_mod, dtype, shape):
+    Nq, Nd, Lq, Ld = shape
+    w = synth.random_dense(11 + Lq, Nq, Nd, Lq, Ld, dtype=dtype, q_mask_p=0.3, d_mask_p=0.3,
+                           dead_docs=1, dead_queries=1)
+    s, a = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    sb, ab = bf.dense(w.Q, w.D, w.q_mask, w.d_mask)
+    np.testing.assert_allclose(s, sb, rtol=0, atol=1e-12)
+    assert np.array_equal(a, ab)
+    # a dead doc contributes exactly 0 and keeps argmax 0
+    assert np.all(s[:, -1] == 0.0)
+    if Lq:
+        assert np.all(a[:, -1, :] == 0)
+
+
+def test_brute_force_exact_ties(oracle_mod):
+    rng = np.random.default_rng(5)
+    Nq, Nd, Lq, Ld, d = 3, 4, 6, 9, 16
+    Q = _exact_grid(rng, (Nq, Lq, d))
+    D = _exact_grid(rng, (Nd, Ld, d))
+    D[:, 5] = D[:, 2]           # duplicated tokens: exact ties, lowest index must win
+    D[:, 8] = D[:, 2]
+    D[1, :] = D[1, 0]           # a doc whose tokens are all identical
+    dm = (rng.random((Nd, Ld)) > 0.2).astype(np.uint8)
+    dm[:, 2] = 1
+    s, a = oracle_mod.fwd(Q, D, None, dm)
+    sb, ab = bf.dense(Q, D, None, dm)
+    assert np.array_equal(s, sb)
+    assert np.array_equal(a, ab)
+    assert not np.any(a == 5) and not np.any(a == 8)
+
+
+def test_brute_force_varlen_with_empty(oracle_mod):
+    w = synth.random_varlen(21, [3, 0, 17, 1], [5, 0, 1, 40, 0, 2])
+    s, a = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    sb, ab = bf.varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    np.testing.assert_allclose(s, sb, rtol=0, atol=1e-12)
+    assert np.array_equal(a, ab)
+    assert np.all(s[1, :] == 0) and np.all(s[:, 1] == 0) and np.all(s[:, 4] == 0)
+
+
+@pytest.mark.parametrize("kind", ["ternary", "quantised", "extreme"])
+def test_brute_force_int8(oracle_mod, kind):
+    w = synth.random_int8(31, 2, 5, 9, 13, ternary=kind == "ternary", extreme=kind == "extreme",
+                          d_mask_p=0.2, q_mask_p=0.2)
+    si, sf, a = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    sb, ab = bf.dense(w.Q, w.D, w.q_mask, w.d_mask, exact_int=True)
+    assert np.array_equal(si, sb)
+    assert np.array_equal(a, ab)
+    np.testing.assert_allclose(sf, sb * w.q_scale * w.d_scale, rtol=1e-15, atol=0)
+
+
+# ----------------------------------------------------------------- closed forms
+
+def test_self_score_is_sum_of_squared_norms(oracle_mod):
+    """Cauchy-Schwarz: each unit query row scores 1 against itself and less
+    against any other distinct row, so score(Q, Q) = Lq and argmax = identity."""
+    rng = np.random.default_rng(7)
+    Lq, d = 64, 128
+    x = rng.standard_normal((1, Lq, d))
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    s, a = oracle_mod.fwd(x, x)
+    assert abs(s[0, 0] - Lq) < 1e-12
+    assert np.array_equal(a[0, 0], np.arange(Lq))
+    # fp16-rounded rows: score = sum of squared norms of the rounded rows
+    q16 = synth.unit_rows(3, 1, Lq).view(1, Lq, d)
+    s16, a16 = oracle_mod.fwd(q16, q16)
+    ref = float((q16.double() ** 2).sum())
+    assert abs(s16[0, 0] - ref) < 1e-12
+    assert abs(s16[0, 0] - Lq) < Lq * 2.0 ** -10
+    assert np.array_equal(a16[0, 0], np.arange(Lq))
+
+
+def test_ld_one_is_a_dot_product(oracle_mod):
+    rng = np.random.default_rng(8)
+    Q = rng.standard_normal((3, 10, 128))
+    D = rng.standard_normal((4, 1, 128))
+    s, a = oracle_mod.fwd(Q, D)
+    ref = Q.sum(axis=1) @ D[:, 0, :].T
+    np.testing.assert_allclose(s, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(a == 0)
+
+
+def test_lq_one_is_max_of_gemv(oracle_mod):
+    rng = np.random.default_rng(9)
+    Q = rng.standard_normal((2, 1, 128))
+    D = rng.standard_normal((3, 50, 128))
+    s, a = oracle_mod.fwd(Q, D)
+    for i in range(2):
+        for j in range(3):
+            v = D[j] @ Q[i, 0]
+            assert abs(s[i, j] - v.max()) < 1e-12
+            assert a[i, j, 0] == int(np.argmax(v))
+
+
+# ----------------------------------------------------------------- invariants
+
+def test_chunked_query_sum_equals_full(oracle_mod):
+    """Design notes, "Long-query chunking": scoring 128-token chunks as separate
+    queries and summing per query is exact."""
+    w = synth.random_dense(41, 2, 3, 300, 50, dtype=torch.bfloat16, q_mask_p=0.2)
+    s, a = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    parts, args = [], []
+    for c0 in range(0, 300, 128):
+        sl = slice(c0, min(300, c0 + 128))
+        sc, ac = oracle_mod.fwd(w.Q[:, sl], w.D, w.q_mask[:, sl], w.d_mask)
+        parts.append(sc)
+        args.append(ac)
+    np.testing.assert_allclose(sum(parts), s, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.concatenate(args, axis=2), a)
+    # int8: exact
+    wi = synth.random_int8(42, 1, 3, 300, 40)
+    si, _, _ = oracle_mod.fwd_i8(wi.Q, wi.q_scale, wi.D, wi.d_scale)
+    tot = sum(oracle_mod.fwd_i8(wi.Q[:, c:c + 128], wi.q_scale, wi.D, wi.d_scale)[0]
+              for c in range(0, 300, 128))
+    assert np.array_equal(tot, si)
+
+
+def test_masked_query_rows_drop_out(oracle_mod):
+    w = synth.random_dense(43, 2, 3, 20, 30, q_mask_p=0.5)
+    s, a = oracle_mod.fwd(w.Q, w.D, w.q_mask, None)
+    for i in range(2):
+        keep = w.q_mask[i].bool()
+        si, ai = oracle_mod.fwd(w.Q[i:i + 1, keep], w.D)
+        np.testing.assert_allclose(s[i], si[0], rtol=1e-12, atol=1e-12)
+    s_all, a_all = oracle_mod.fwd(w.Q, w.D)
+    assert np.array_equal(a, a_all)  # masked rows keep their real argmax
+
+
+def test_permutation_invariance(oracle_mod):
+    w = synth.random_dense(44, 2, 3, 16, 40, dtype=torch.float16)
+    s, a = oracle_mod.fwd(w.Q, w.D)
+    rng = np.random.default_rng(0)
+    pt = rng.permutation(40)
+    s2, a2 = oracle_mod.fwd(w.Q, w.D[:, pt])
+    np.testing.assert_allclose(s2, s, rtol=0, atol=1e-12)
+    assert np.array_equal(pt[a2], a)
+    ps = rng.permutation(16)
+    s3, a3 = oracle_mod.fwd(w.Q[:, ps], w.D)
+    np.testing.assert_allclose(s3, s, rtol=0, atol=1e-12)
+    assert np.array_equal(a3, a[:, :, ps])
+
+
+def test_power_of_two_scaling(oracle_mod):
+    w = synth.random_dense(45, 2, 2, 8, 25, d_mask_p=0.3)
+    s, a = oracle_mod.fwd(w.Q, w.D, None, w.d_mask)
+    s2, a2 = oracle_mod.fwd(w.Q, w.D.double() * 2.0, None, w.d_mask)
+    assert np.array_equal(s2, 2.0 * s)
+    assert np.array_equal(a2, a)
+
+
+def test_padding_free_equals_padded(oracle_mod):
+    """Flash-MaxSim Sec. 5.5: the cu_seqlens path gives the padded scores."""
+    lens_q = [5, 12]
+    lens_d = [7, 1, 19, 3]
+    w = synth.random_varlen(46, lens_q, lens_d)
+    s, a = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    Lq, Ld = max(lens_q), max(lens_d)
+    Qp = torch.zeros(2, Lq, 128, dtype=w.Q.dtype)
+    Dp = torch.zeros(4, Ld, 128, dtype=w.D.dtype)
+    cq, cd = w.cu_q.tolist(), w.cu_d.tolist()
+    for i in range(2):
+        Qp[i, :lens_q[i]] = w.Q[cq[i]:cq[i + 1]]
+    for j in range(4):
+        Dp[j, :lens_d[j]] = w.D[cd[j]:cd[j + 1]]
+    qm = synth.prefix_mask(np.array(lens_q), Lq)
+    dm = synth.prefix_mask(np.array(lens_d), Ld)
+    sp, ap = oracle_mod.fwd(Qp, Dp, qm, dm)
+    assert np.array_equal(s, sp)
+    for i in range(2):
+        assert np.array_equal(a[i, :, :lens_q[i]], ap[i, :, :lens_q[i]])
+        assert np.all(a[i, :, lens_q[i]:] == 0)
+
+
+def test_int8_equals_scaled_float(oracle_mod):
+    w = synth.random_int8(47, 2, 3, 20, 30)
+    si, sf, a = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D, w.d_scale)
+    s, af = oracle_mod.fwd(w.Q.double() * w.q_scale, w.D.double() * w.d_scale)
+    np.testing.assert_allclose(sf, s, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(a, af)
+
+
+# ----------------------------------------------------------------- backward
+
+def _loss(oracle_mod, Q, D, g, qm, dm):
+    s, _ = oracle_mod.fwd(Q, D, qm, dm, want_argmax=False)
+    return float((g * s).sum())
+
+
+def test_backward_finite_differences(oracle_mod):
+    """Central differences of L = sum g*score in fp64 on inputs whose top-2
+    gaps are far larger than the step, so the argmax is fixed."""
+    rng = np.random.default_rng(12)
+    Nq, Nd, Lq, Ld, d = 2, 3, 3, 4, 5
+    for _ in range(100):
+        Q = rng.standard_normal((Nq, Lq, d))
+        D = rng.standard_normal((Nd, Ld, d))
+        S = np.einsum("isk,jtk->ijst", Q, D)
+        srt = np.sort(S, axis=-1)
+        if (srt[..., -1] - srt[..., -2]).min() > 1e-3:
+            break
+    qm = np.array([[1, 0, 1], [1, 1, 1]], np.uint8)
+    dm = np.array([[1, 1, 1, 1], [0, 0, 0, 0], [1, 1, 1, 1]], np.uint8)
+    g = rng.standard_normal((Nq, Nd))
+    _, arg = oracle_mod.fwd(Q, D, qm, dm)
+    dQ, dD, _, _ = oracle_mod.bwd(Q, D, arg, g, qm, dm)
+    h = 1e-6
+    fdQ = np.zeros_like(Q)
+    for idx in np.ndindex(Q.shape):
+        Qp, Qm = Q.copy(), Q.copy()
+        Qp[idx] += h
+        Qm[idx] -= h
+        fdQ[idx] = (_loss(oracle_mod, Qp, D, g, qm, dm) - _loss(oracle_mod, Qm, D, g, qm, dm)) / (2 * h)
+    fdD = np.zeros_like(D)
+    for idx in np.ndindex(D.shape):
+        Dp, Dm = D.copy(), D.copy()
+        Dp[idx] += h
+        Dm[idx] -= h
+        fdD[idx] = (_loss(oracle_mod, Q, Dp, g, qm, dm) - _loss(oracle_mod, Q, Dm, g, qm, dm)) / (2 * h)
+    np.testing.assert_allclose(dQ, fdQ, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(dD, fdD, rtol=0, atol=1e-7)
+    assert np.all(dQ[0, 1] == 0) and np.all(dD[1] == 0)
+
+
+def test_backward_euler_identity(oracle_mod):
+    """score is bilinear in (Q, D) at a fixed argmax: sum g*score equals
+    <dQ, Q> and <dD, D>."""
+    w = synth.random_dense(51, 4, 5, 12, 30, dtype=torch.bfloat16, q_mask_p=0.3, d_mask_p=0.2,
+                           dead_docs=1)
+    g = synth.upstream_grad(51, 4, 5).double().numpy()
+    s, a = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    dQ, dD, _, _ = oracle_mod.bwd(w.Q, w.D, a, g, w.q_mask, w.d_mask)
+    lhs = float((g * s).sum())
+    np.testing.assert_allclose(float((dQ * w.Q.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(float((dD * w.D.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("hub", [0.0, 0.7])
+def test_csr_matches_stable_argsort(oracle_mod, hub):
+    Nq, Nd, Lq, Ld = 3, 4, 10, 16
+    arg = synth.draw_argmax(61, Nq, Nd, Lq, Ld, None, hub_frac=hub).numpy()
+    Q = np.zeros((Nq, Lq, 2))
+    D = np.zeros((Nd, Ld, 2))
+    g = np.ones((Nq, Nd))
+    _, _, rp, ci = oracle_mod.bwd(Q, D, arg, g)
+    src = np.arange(Nq * Nd * Lq)
+    j = (src // Lq) % Nd
+    dest = j * Ld + arg.reshape(-1)
+    cnt = np.bincount(dest, minlength=Nd * Ld)
+    assert np.array_equal(rp, np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32))
+    assert np.array_equal(ci, np.argsort(dest, kind="stable").astype(np.int32))
+    # the invariants that pin the CSR uniquely
+    assert rp[0] == 0 and rp[-1] == Nq * Nd * Lq and np.all(np.diff(rp) >= 0)
+    assert np.array_equal(np.sort(ci), src)
+    rows = np.repeat(np.arange(Nd * Ld), np.diff(rp))
+    assert np.array_equal(dest[ci], rows)
+    for r in range(Nd * Ld):
+        seg = ci[rp[r]:rp[r + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_backward_gradients_match_scatter_reference(oracle_mod):
+    """dD checked against numpy's unbuffered scatter-add of the per-source
+    contributions, dQ against a gather with numpy fancy indexing."""
+    w = synth.random_dense(71, 3, 4, 9, 14, q_mask_p=0.3, d_mask_p=0.2, dead_docs=1)
+    g = synth.upstream_grad(71, 3, 4).double().numpy()
+    _, a = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    dQ, dD, _, _ = oracle_mod.bwd(w.Q, w.D, a, g, w.q_mask, w.d_mask)
+    Q = w.Q.double().numpy()
+    D = w.D.double().numpy()
+    live = w.d_mask.numpy().any(axis=1)
+    wgt = g[:, :, None] * w.q_mask.numpy()[:, None, :] * live[None, :, None]  # [Nq,Nd,Lq]
+    Nq, Nd, Lq = a.shape
+    jj = np.broadcast_to(np.arange(Nd)[None, :, None], a.shape)
+    gathered = D[jj, a]                                   # [Nq,Nd,Lq,d]
+    refQ = (wgt[..., None] * gathered).sum(axis=1)
+    np.testing.assert_allclose(dQ, refQ, rtol=1e-12, atol=1e-12)
+    refD = np.zeros_like(D)
+    ii = np.broadcast_to(np.arange(Nq)[:, None, None], a.shape)
+    ss = np.broadcast_to(np.arange(Lq)[None, None, :], a.shape)
+    np.add.at(refD, (jj.ravel(), a.ravel()), wgt.ravel()[:, None] * Q[ii.ravel(), ss.ravel()])
+    np.testing.assert_allclose(dD, refD, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------- byte model
+
+def test_io_model_worked_example():
+    from maxsim_scoring_amd import workload as wl
+    g = _gold("io_model.json")
+    p = g["params"]
+    naive = wl.io_naive_model(p["nq_tokens"], p["nd_tokens"], p["d"], p["B"], p["elem_bytes"])
+    fused = wl.io_fused_model(p["nq_tokens"], p["nd_tokens"], p["d"], p["B"], p["elem_bytes"])
+    assert naive == g["io_naive_bytes"]
+    assert fused == g["io_fused_bytes"]
+    fl = wl.flops_naive_model(p["nq_tokens"], p["nd_tokens"], p["d"], p["B"])
+    assert abs(fl / naive - g["ai_naive_flop_per_byte"]) < g["ai_rounding"]
+    assert abs(fl / fused - g["ai_fused_flop_per_byte"]) < g["ai_rounding"]
+
+
+def test_size_examples():
+    from maxsim_scoring_amd import workload as wl
+    g = _gold("sizes.json")
+    for it in g["items"]:
+        b = wl.similarity_tensor_bytes(it["n_pairs"], it["lq"], it["ld"], it["elem"])
+        assert abs(b / 1e9 - it["approx_gb"]) <= it["rel_tol"] * it["approx_gb"]
+    am = g["argmax"]
+    b = wl.argmax_bytes(am["nq"], am["nd"], am["lq"])
+    assert abs(b / 2**20 - am["approx_mb"]) <= am["rel_tol"] * am["approx_mb"]
