@@ -1,0 +1,145 @@
+/*
+ * maxsim.h -- C ABI of the MI355X (gfx950) MaxSim scoring library.
+ *
+ * The operator is late-interaction MaxSim, "Flash-MaxSim" Eq. (1) and the
+ * "Problem" passage of the late-interaction-kernels design notes:
+ *
+ *     score[i, j] = sum_s  max_t  <Q[i, s], D[j, t]>
+ *
+ * with optional 0/1 masks: a masked doc token is -inf before every max, a
+ * masked query row adds 0 to the sum (but still gets its argmax).
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller. The library
+ *     allocates no device memory and keeps no per-call state.
+ *   - Every tensor is C-contiguous, row-major, with the embedding dimension d
+ *     innermost. d must be 128 (other values return MAXSIM_ERR_UNSUPPORTED).
+ *   - Calls are asynchronous on `stream` (NULL = the null stream). Outputs are
+ *     valid after the stream is synchronised; inputs must stay unchanged until
+ *     then. Outputs must not alias inputs or each other.
+ *   - All checks that need no device data run on the host BEFORE anything is
+ *     enqueued; on failure the call returns a non-zero status and enqueues
+ *     nothing. Device-data contents (mask bytes in {0,1}, monotone offsets,
+ *     argmax in [0, Ld), int8 values != -128) are preconditions: breaking them
+ *     gives unspecified values, never an out-of-bounds access.
+ *   - Sizes of 0 are valid. Nq == 0 or Nd == 0 enqueues nothing.
+ *   - Reductions run in a fixed order with no atomics: results are bitwise
+ *     reproducible run to run.
+ *   - Ties among equal maxima go to the lowest doc-token index.
+ */
+#ifndef MAXSIM_H
+#define MAXSIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAXSIM_ABI_VERSION 1
+
+typedef struct ihipStream_t* maxsim_stream_t; /* a hipStream_t */
+
+typedef enum {
+    MAXSIM_OK = 0,
+    MAXSIM_ERR_NULL = 1,        /* a required pointer is NULL */
+    MAXSIM_ERR_SHAPE = 2,       /* a negative size or inconsistent sizes */
+    MAXSIM_ERR_UNSUPPORTED = 3, /* d != 128 or an unknown dtype */
+    MAXSIM_ERR_OVERFLOW = 4,    /* an index or an int32 sum could overflow */
+    MAXSIM_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
+} maxsim_status_t;
+
+typedef enum { MAXSIM_F16 = 0, MAXSIM_BF16 = 1 } maxsim_dtype_t;
+
+/*
+ * Cross-product forward ("Flash-MaxSim" Sec. 4.1; design notes "Forward",
+ * "Mask handling", "Long-query chunking").
+ *   Q        [Nq, Lq, d] of `dtype`             D [Nd, Ld, d] of `dtype`
+ *   q_mask   [Nq, Lq] uint8 0/1 or NULL (all rows kept)
+ *   d_mask   [Nd, Ld] uint8 0/1 or NULL (all tokens valid)
+ *   scores   [Nq, Nd] float32, required, fully overwritten
+ *   argmax   [Nq, Nd, Lq] int32 or NULL: index t in [0, Ld) of the max for
+ *            every query row (masked rows included); 0 when the doc has no
+ *            valid token.
+ * Products are exact in fp32 and accumulated in fp32. Errors: NULL for a
+ * missing Q, D or scores (when the output is non-empty); SHAPE for negative
+ * sizes; UNSUPPORTED for d != 128 or a bad dtype; OVERFLOW when argmax is
+ * requested and Nq*Nd*Lq >= 2^31.
+ */
+maxsim_status_t maxsim_fwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
+                           int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
+                           const uint8_t* d_mask, float* scores, int32_t* argmax,
+                           maxsim_stream_t stream);
+
+/*
+ * Padding-free forward ("Flash-MaxSim" Sec. 4.3.2; design notes "Varlen /
+ * packed path"): sequence b occupies rows [cu[b], cu[b+1]) of its packed
+ * tensor (FlashAttention cu_seqlens convention).
+ *   Q     [cu_q[Nq], d]   cu_q int32 [Nq+1], cu_q[0] = 0, non-decreasing
+ *   D     [cu_d[Nd], d]   cu_d int32 [Nd+1], cu_d[0] = 0, non-decreasing
+ *   max_lq  an upper bound on every query length (rows beyond it are ignored)
+ *   scores  [Nq, Nd] float32, required
+ *   argmax  [Nq, Nd, max_lq] int32 or NULL: doc-relative index; rows s at or
+ *           past the query's length, and every row of an empty doc, are 0.
+ * Empty sequences contribute 0. Token offsets are 64-bit inside the kernels.
+ * Errors: NULL, SHAPE (negative sizes, max_lq < 0), UNSUPPORTED (d, dtype),
+ * OVERFLOW when argmax is requested and Nq*Nd*max_lq >= 2^31.
+ */
+maxsim_status_t maxsim_fwd_varlen(maxsim_dtype_t dtype, const void* Q, const int32_t* cu_q,
+                                  int64_t Nq, int32_t max_lq, const void* D, const int32_t* cu_d,
+                                  int64_t Nd, int64_t d, float* scores, int32_t* argmax,
+                                  maxsim_stream_t stream);
+
+/*
+ * INT8 x INT8 forward with one symmetric scale per tensor ("Flash-MaxSim"
+ * Sec. 4.3.1, quantisation fused into the kernel).
+ *   Q int8 [Nq, Lq, d], D int8 [Nd, Ld, d], values in [-127, 127]
+ *   scores_i32 [Nq, Nd] int32 or NULL: the exact integer max-sum
+ *   scores     [Nq, Nd] float32 or NULL: (double)sum * q_scale * d_scale,
+ *              rounded once to float
+ *   (at least one of the two), argmax as in maxsim_fwd.
+ * Errors as maxsim_fwd, plus NULL when both score outputs are NULL and
+ * OVERFLOW when Lq*d*127^2 >= 2^31 (the int32 sum could overflow).
+ */
+maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, float d_scale,
+                              int64_t Nq, int64_t Nd, int64_t Lq, int64_t Ld, int64_t d,
+                              const uint8_t* q_mask, const uint8_t* d_mask, int32_t* scores_i32,
+                              float* scores, int32_t* argmax, maxsim_stream_t stream);
+
+/*
+ * Backward through a saved forward argmax ("Flash-MaxSim" Sec. 4.2.1
+ * Eqs. (2)-(3), Sec. 4.2.2 inverse-grid CSR, Sec. 4.2.3 destination-owned
+ * reduction; design notes "Backward"):
+ *   dQ[i,s] = sum_j w(i,j,s) * D[j, argmax[i,j,s]]
+ *   dD[j,t] = sum over sources (i,s) with argmax[i,j,s] = t of w(i,j,s) * Q[i,s]
+ * with w(i,j,s) = grad_scores[i,j] * q_mask[i,s] * live(j), live(j) = doc j
+ * has at least one valid token.
+ *   Q, D, masks     as in maxsim_fwd; argmax [Nq, Nd, Lq] int32 in [0, Ld)
+ *   grad_scores     [Nq, Nd] float32
+ *   dQ [Nq, Lq, d], dD [Nd, Ld, d] float32, fully overwritten
+ *   csr_row_ptr [Nd*Ld + 1] int32, csr_col_idx [Nq*Nd*Lq] int32: outputs,
+ *     the inverse map (row r = j*Ld + t lists the flat sources
+ *     (i*Nd + j)*Lq + s that picked it, ascending). They are also the only
+ *     scratch the backward needs.
+ * Sums run in fp32 in a fixed order: dQ over j ascending, dD over the CSR row.
+ * Errors: NULL, SHAPE (negative sizes; Ld == 0 with Nq*Nd*Lq > 0),
+ * UNSUPPORTED, OVERFLOW when Nq*Nd*Lq >= 2^31 or Nd*Ld + 1 >= 2^31.
+ */
+maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
+                           int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
+                           const uint8_t* d_mask, const int32_t* argmax, const float* grad_scores,
+                           float* dQ, float* dD, int32_t* csr_row_ptr, int32_t* csr_col_idx,
+                           maxsim_stream_t stream);
+
+/* A static, human-readable name of a status. Never NULL. */
+const char* maxsim_status_string(maxsim_status_t s);
+
+/* MAXSIM_ABI_VERSION of the built library. */
+int maxsim_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAXSIM_H */

@@ -1,0 +1,13 @@
+"""MaxSim scoring on MI355X (gfx950): fused late-interaction scoring kernels.
+
+The product is the HIP library ``libmaxsim_amd.so`` behind the C ABI in
+``include/maxsim.h``; ``binding`` exposes the same entry points to Python
+(torch tensors in GPU memory, argument marshalling only). ``synth`` draws the
+seeded synthetic workloads and ``workload`` holds the byte/flop model.
+"""
+
+from .binding import (MaxSimError, maxsim_abi_version, maxsim_bwd, maxsim_fwd, maxsim_fwd_i8,
+                      maxsim_fwd_varlen, maxsim_status_string)
+
+__all__ = ["MaxSimError", "maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd",
+           "maxsim_status_string", "maxsim_abi_version"]

@@ -1,0 +1,225 @@
+"""Python binding of the C ABI in include/maxsim.h (argument marshalling only).
+
+Every function takes torch tensors that live on the GPU, checks that they have
+the layout the ABI documents, allocates missing outputs with torch (device
+memory is PyTorch's job here) and calls the C entry point of the same name on
+the current HIP stream. All arithmetic runs in the HIP kernels; there is no
+CPU path. When the library is missing, or a tensor is not on the GPU, the call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmaxsim_amd.so")
+
+MAXSIM_F16 = 0
+MAXSIM_BF16 = 1
+D_MODEL = 128
+
+_lib = None
+
+
+class MaxSimError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, fn: str, status: int):
+        msg = lib().maxsim_status_string(status).decode()
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (loaded once)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        ci = ctypes.c_int
+        L.maxsim_fwd.argtypes = [ci, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.maxsim_fwd_varlen.argtypes = [ci, vp, vp, i64, i32, vp, vp, i64, i64, vp, vp, vp]
+        L.maxsim_fwd_i8.argtypes = [vp, f32, vp, f32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.maxsim_bwd.argtypes = [ci, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp,
+                                 vp, vp]
+        for f in (L.maxsim_fwd, L.maxsim_fwd_varlen, L.maxsim_fwd_i8, L.maxsim_bwd):
+            f.restype = ci
+        L.maxsim_status_string.argtypes = [ci]
+        L.maxsim_status_string.restype = ctypes.c_char_p
+        L.maxsim_abi_version.argtypes = []
+        L.maxsim_abi_version.restype = ci
+        _lib = L
+    return _lib
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(name: str, t: Optional[torch.Tensor], dtype=None) -> None:
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return MAXSIM_F16
+    if t.dtype == torch.bfloat16:
+        return MAXSIM_BF16
+    raise ValueError(f"embeddings must be float16 or bfloat16, got {t.dtype}")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MaxSimError(fn, status)
+
+
+def maxsim_fwd(Q: torch.Tensor, D: torch.Tensor, q_mask: Optional[torch.Tensor] = None,
+               d_mask: Optional[torch.Tensor] = None, want_argmax: bool = False,
+               scores: Optional[torch.Tensor] = None, argmax: Optional[torch.Tensor] = None,
+               stream=None):
+    """Cross-product forward. Q [Nq,Lq,d], D [Nd,Ld,d] fp16/bf16; masks uint8.
+    Returns (scores float32 [Nq,Nd], argmax int32 [Nq,Nd,Lq] or None)."""
+    Nq, Lq, d = Q.shape
+    Nd, Ld, d2 = D.shape
+    if d2 != d or D.dtype != Q.dtype:
+        raise ValueError("Q and D must share d and dtype")
+    _dev("Q", Q)
+    _dev("D", D)
+    _dev("q_mask", q_mask, torch.uint8)
+    _dev("d_mask", d_mask, torch.uint8)
+    if q_mask is not None and tuple(q_mask.shape) != (Nq, Lq):
+        raise ValueError("q_mask must be [Nq, Lq]")
+    if d_mask is not None and tuple(d_mask.shape) != (Nd, Ld):
+        raise ValueError("d_mask must be [Nd, Ld]")
+    if scores is None:
+        scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
+    if argmax is None and want_argmax:
+        argmax = torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=Q.device)
+    _dev("scores", scores, torch.float32)
+    _dev("argmax", argmax, torch.int32)
+    st = lib().maxsim_fwd(_dtype_code(Q), _p(Q), _p(D), Nq, Nd, Lq, Ld, d, _p(q_mask), _p(d_mask),
+                          _p(scores), _p(argmax), _stream(stream))
+    _check("maxsim_fwd", st)
+    return scores, argmax
+
+
+def maxsim_fwd_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D: torch.Tensor,
+                      cu_d: torch.Tensor, want_argmax: bool = False,
+                      scores: Optional[torch.Tensor] = None,
+                      argmax: Optional[torch.Tensor] = None, stream=None):
+    """Padding-free forward. Q [Tq,d], D [Td,d] packed; cu_* int32 [N+1].
+    Returns (scores [Nq,Nd], argmax [Nq,Nd,max_lq] or None)."""
+    if Q.dim() != 2 or D.dim() != 2 or Q.shape[1] != D.shape[1] or Q.dtype != D.dtype:
+        raise ValueError("Q and D must be packed [tokens, d] of one dtype")
+    d = Q.shape[1]
+    for n, t in (("Q", Q), ("D", D)):
+        _dev(n, t)
+    _dev("cu_q", cu_q, torch.int32)
+    _dev("cu_d", cu_d, torch.int32)
+    Nq, Nd = cu_q.numel() - 1, cu_d.numel() - 1
+    if scores is None:
+        scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
+    if argmax is None and want_argmax:
+        argmax = torch.empty((Nq, Nd, max_lq), dtype=torch.int32, device=Q.device)
+    _dev("scores", scores, torch.float32)
+    _dev("argmax", argmax, torch.int32)
+    st = lib().maxsim_fwd_varlen(_dtype_code(Q), _p(Q), _p(cu_q), Nq, int(max_lq), _p(D),
+                                 _p(cu_d), Nd, d, _p(scores), _p(argmax), _stream(stream))
+    _check("maxsim_fwd_varlen", st)
+    return scores, argmax
+
+
+def maxsim_fwd_i8(Q: torch.Tensor, q_scale: float, D: torch.Tensor, d_scale: float,
+                  q_mask: Optional[torch.Tensor] = None, d_mask: Optional[torch.Tensor] = None,
+                  want_argmax: bool = False, want_int: bool = True, want_float: bool = True,
+                  scores_i32: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                  argmax: Optional[torch.Tensor] = None, stream=None):
+    """INT8 forward with per-tensor scales. Returns (scores_i32, scores, argmax)."""
+    Nq, Lq, d = Q.shape
+    Nd, Ld, d2 = D.shape
+    if d2 != d:
+        raise ValueError("Q and D must share d")
+    _dev("Q", Q, torch.int8)
+    _dev("D", D, torch.int8)
+    _dev("q_mask", q_mask, torch.uint8)
+    _dev("d_mask", d_mask, torch.uint8)
+    dev = Q.device
+    if scores_i32 is None and want_int:
+        scores_i32 = torch.empty((Nq, Nd), dtype=torch.int32, device=dev)
+    if scores is None and want_float:
+        scores = torch.empty((Nq, Nd), dtype=torch.float32, device=dev)
+    if argmax is None and want_argmax:
+        argmax = torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=dev)
+    _dev("scores_i32", scores_i32, torch.int32)
+    _dev("scores", scores, torch.float32)
+    _dev("argmax", argmax, torch.int32)
+    st = lib().maxsim_fwd_i8(_p(Q), float(q_scale), _p(D), float(d_scale), Nq, Nd, Lq, Ld, d,
+                             _p(q_mask), _p(d_mask), _p(scores_i32), _p(scores), _p(argmax),
+                             _stream(stream))
+    _check("maxsim_fwd_i8", st)
+    return scores_i32, scores, argmax
+
+
+def maxsim_bwd(Q: torch.Tensor, D: torch.Tensor, argmax: torch.Tensor, grad_scores: torch.Tensor,
+               q_mask: Optional[torch.Tensor] = None, d_mask: Optional[torch.Tensor] = None,
+               dQ: Optional[torch.Tensor] = None, dD: Optional[torch.Tensor] = None,
+               csr_row_ptr: Optional[torch.Tensor] = None,
+               csr_col_idx: Optional[torch.Tensor] = None, stream=None):
+    """Backward through a saved argmax. Returns (dQ, dD, csr_row_ptr, csr_col_idx)."""
+    Nq, Lq, d = Q.shape
+    Nd, Ld, d2 = D.shape
+    if d2 != d or D.dtype != Q.dtype:
+        raise ValueError("Q and D must share d and dtype")
+    _dev("Q", Q)
+    _dev("D", D)
+    _dev("argmax", argmax, torch.int32)
+    _dev("grad_scores", grad_scores, torch.float32)
+    _dev("q_mask", q_mask, torch.uint8)
+    _dev("d_mask", d_mask, torch.uint8)
+    if tuple(argmax.shape) != (Nq, Nd, Lq) or tuple(grad_scores.shape) != (Nq, Nd):
+        raise ValueError("argmax must be [Nq,Nd,Lq] and grad_scores [Nq,Nd]")
+    dev = Q.device
+    if dQ is None:
+        dQ = torch.empty((Nq, Lq, d), dtype=torch.float32, device=dev)
+    if dD is None:
+        dD = torch.empty((Nd, Ld, d), dtype=torch.float32, device=dev)
+    if csr_row_ptr is None:
+        csr_row_ptr = torch.empty((Nd * Ld + 1,), dtype=torch.int32, device=dev)
+    if csr_col_idx is None:
+        csr_col_idx = torch.empty((max(1, Nq * Nd * Lq),), dtype=torch.int32, device=dev)
+    for n, t in (("dQ", dQ), ("dD", dD)):
+        _dev(n, t, torch.float32)
+    for n, t in (("csr_row_ptr", csr_row_ptr), ("csr_col_idx", csr_col_idx)):
+        _dev(n, t, torch.int32)
+    st = lib().maxsim_bwd(_dtype_code(Q), _p(Q), _p(D), Nq, Nd, Lq, Ld, d, _p(q_mask), _p(d_mask),
+                          _p(argmax), _p(grad_scores), _p(dQ), _p(dD), _p(csr_row_ptr),
+                          _p(csr_col_idx), _stream(stream))
+    _check("maxsim_bwd", st)
+    return dQ, dD, csr_row_ptr, csr_col_idx[:Nq * Nd * Lq]
+
+
+def maxsim_status_string(status: int) -> str:
+    return lib().maxsim_status_string(status).decode()
+
+
+def maxsim_abi_version() -> int:
+    return lib().maxsim_abi_version()

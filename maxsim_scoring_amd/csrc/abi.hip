@@ -1,0 +1,181 @@
+// The C ABI declared in include/maxsim.h: host-side validation (before
+// anything is enqueued), then one launcher per entry point.
+#include "../../include/maxsim.h"
+
+#include <climits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace maxsim;
+
+namespace {
+
+constexpr int64_t kI32Max = INT32_MAX;
+
+maxsim_status_t launch_status(hipError_t e) { return e == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH; }
+
+bool dtype_ok(maxsim_dtype_t t) { return t == MAXSIM_F16 || t == MAXSIM_BF16; }
+
+int elem_of(maxsim_dtype_t t) { return t == MAXSIM_F16 ? kF16 : kBF16; }
+
+// The product of non-negative sizes, or -1 when it exceeds int64.
+int64_t mul_sat(int64_t a, int64_t b)
+{
+    if (a == 0 || b == 0) return 0;
+    if (a > INT64_MAX / b) return -1;
+    return a * b;
+}
+
+}  // namespace
+
+extern "C" {
+
+maxsim_status_t maxsim_fwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
+                           int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
+                           const uint8_t* d_mask, float* scores, int32_t* argmax,
+                           maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
+    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || Nd == 0) return MAXSIM_OK;
+    if (!scores) return MAXSIM_ERR_NULL;
+    if ((Lq > 0 && !Q) || (Ld > 0 && !D)) return MAXSIM_ERR_NULL;
+    const int64_t pairs = mul_sat(Nq, Nd);
+    if (pairs < 0 || pairs > kI32Max) return MAXSIM_ERR_OVERFLOW;  // one workgroup per pair group
+    if (argmax) {
+        const int64_t n = mul_sat(pairs, Lq);
+        if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    DenseArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.q_mask = q_mask;
+    a.d_mask = d_mask;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.Lq = Lq;
+    a.Ld = Ld;
+    return launch_status(launch_fwd_dense(elem_of(dtype), a, argmax != nullptr, (hipStream_t)stream));
+}
+
+maxsim_status_t maxsim_fwd_varlen(maxsim_dtype_t dtype, const void* Q, const int32_t* cu_q,
+                                  int64_t Nq, int32_t max_lq, const void* D, const int32_t* cu_d,
+                                  int64_t Nd, int64_t d, float* scores, int32_t* argmax,
+                                  maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0) return MAXSIM_ERR_SHAPE;
+    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || Nd == 0) return MAXSIM_OK;
+    if (!cu_q || !cu_d || !scores || !Q || !D) return MAXSIM_ERR_NULL;
+    if (Nd > kI32Max - 1) return MAXSIM_ERR_OVERFLOW;
+    const int64_t pairs = mul_sat(Nq, Nd);
+    if (pairs < 0 || pairs > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (argmax) {
+        const int64_t n = mul_sat(pairs, max_lq);
+        if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    VarlenArgs a{};
+    a.Q = Q;
+    a.cu_q = cu_q;
+    a.D = D;
+    a.cu_d = cu_d;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.max_lq = max_lq;
+    return launch_status(launch_fwd_varlen(elem_of(dtype), a, (hipStream_t)stream));
+}
+
+maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, float d_scale,
+                              int64_t Nq, int64_t Nd, int64_t Lq, int64_t Ld, int64_t d,
+                              const uint8_t* q_mask, const uint8_t* d_mask, int32_t* scores_i32,
+                              float* scores, int32_t* argmax, maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
+    if (d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || Nd == 0) return MAXSIM_OK;
+    if (!scores_i32 && !scores) return MAXSIM_ERR_NULL;
+    if ((Lq > 0 && !Q) || (Ld > 0 && !D)) return MAXSIM_ERR_NULL;
+    // worst case |sum| = Lq * d * 127^2 must stay inside int32
+    const int64_t worst = mul_sat(mul_sat(Lq, d), 127 * 127);
+    if (worst < 0 || worst > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    const int64_t pairs = mul_sat(Nq, Nd);
+    if (pairs < 0 || pairs > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (argmax) {
+        const int64_t n = mul_sat(pairs, Lq);
+        if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    DenseArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.q_mask = q_mask;
+    a.d_mask = d_mask;
+    a.scores = scores;
+    a.scores_i32 = scores_i32;
+    a.argmax = argmax;
+    a.q_scale = (double)q_scale;
+    a.d_scale = (double)d_scale;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.Lq = Lq;
+    a.Ld = Ld;
+    return launch_status(launch_fwd_dense(kI8, a, argmax != nullptr, (hipStream_t)stream));
+}
+
+maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
+                           int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
+                           const uint8_t* d_mask, const int32_t* argmax, const float* grad_scores,
+                           float* dQ, float* dD, int32_t* csr_row_ptr, int32_t* csr_col_idx,
+                           maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
+    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    const int64_t nsrc = mul_sat(mul_sat(Nq, Nd), Lq);
+    const int64_t nrows = mul_sat(Nd, Ld);
+    if (nsrc < 0 || nsrc > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (nrows < 0 || nrows + 1 > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (mul_sat(Nq, Lq) > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (nsrc > 0 && Ld == 0) return MAXSIM_ERR_SHAPE;  // no destination for the sources
+    if (Nd > 0 && !csr_row_ptr) return MAXSIM_ERR_NULL;
+    if (nsrc > 0 && (!Q || !D || !argmax || !grad_scores || !csr_col_idx)) return MAXSIM_ERR_NULL;
+    if (Nq * Lq > 0 && !dQ) return MAXSIM_ERR_NULL;
+    if (nrows > 0 && !dD) return MAXSIM_ERR_NULL;
+    if (Nq * Lq == 0 && nrows == 0 && Nd == 0) return MAXSIM_OK;
+    BwdArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.q_mask = q_mask;
+    a.d_mask = d_mask;
+    a.argmax = argmax;
+    a.g = grad_scores;
+    a.dQ = dQ;
+    a.dD = dD;
+    a.row_ptr = csr_row_ptr;
+    a.col_idx = csr_col_idx;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.Lq = Lq;
+    a.Ld = Ld;
+    return launch_status(launch_bwd(elem_of(dtype), a, (hipStream_t)stream));
+}
+
+const char* maxsim_status_string(maxsim_status_t s)
+{
+    switch (s) {
+    case MAXSIM_OK: return "ok";
+    case MAXSIM_ERR_NULL: return "a required pointer is NULL";
+    case MAXSIM_ERR_SHAPE: return "negative or inconsistent sizes";
+    case MAXSIM_ERR_UNSUPPORTED: return "unsupported dtype or embedding width (d must be 128)";
+    case MAXSIM_ERR_OVERFLOW: return "sizes overflow the int32 index range or the int32 sum";
+    case MAXSIM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int maxsim_abi_version(void) { return MAXSIM_ABI_VERSION; }
+
+}  // extern "C"

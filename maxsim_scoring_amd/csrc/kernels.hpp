@@ -1,0 +1,56 @@
+// Argument blocks and launchers shared by the host ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace maxsim {
+
+struct DenseArgs {
+    const void* Q;
+    const void* D;
+    const uint8_t* q_mask;  // [Nq, Lq] or null
+    const uint8_t* d_mask;  // [Nd, Ld] or null
+    float* scores;          // [Nq, Nd] or null (int8 only)
+    int32_t* scores_i32;    // [Nq, Nd] or null (int8 only)
+    int32_t* argmax;        // [Nq, Nd, Lq] or null
+    double q_scale, d_scale;  // int8 only
+    int64_t Nq, Nd, Lq, Ld;
+    // filled by the launcher
+    int ntq;    // 32-token N-tiles per query
+    int qpw;    // whole queries per workgroup (single pass)
+    int npass;  // passes over a doc when one query has more N-tiles than a workgroup holds
+    int nqg;    // query groups
+};
+
+struct VarlenArgs {
+    const void* Q;
+    const int32_t* cu_q;
+    const void* D;
+    const int32_t* cu_d;
+    float* scores;    // [Nq, Nd]
+    int32_t* argmax;  // [Nq, Nd, max_lq] or null
+    int64_t Nq, Nd;
+    int32_t max_lq;
+    int32_t units;    // streaming units (waves) per query
+};
+
+struct BwdArgs {
+    const void* Q;
+    const void* D;
+    const uint8_t* q_mask;
+    const uint8_t* d_mask;
+    const int32_t* argmax;
+    const float* g;
+    float* dQ;
+    float* dD;
+    int32_t* row_ptr;
+    int32_t* col_idx;
+    int64_t Nq, Nd, Lq, Ld;
+};
+
+hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t stream);
+hipError_t launch_fwd_varlen(int elem, VarlenArgs a, hipStream_t stream);
+hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream);
+
+}  // namespace maxsim

@@ -1,0 +1,128 @@
+"""How GPU results are judged against the oracle -- TEST INFRASTRUCTURE ONLY.
+
+* float scores and gradients: |got - ref| <= 1e-3 + 1e-4 * |ref| element by
+  element;
+* integer outputs (int8 score sums, int8 argmax, CSR maps): bit-exact;
+* float argmax: several answers can be correct when two doc tokens are nearly
+  tied, because the GPU accumulates each dot product in fp32 and the oracle in
+  fp64. A GPU index t_g that differs from the oracle's t_o is accepted only if
+  t_g is a valid (unmasked) token and
+      v(t_o) - v(t_g) <= e(t_o) + e(t_g),
+  with v the exact (fp64) dot product and e(t) = gamma * sum_k |q_k x_tk|,
+  gamma = d*u / (1 - d*u), u = 2^-23, the textbook bound on an fp32 sum of d
+  exact products in any order. Every other mismatch fails.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ATOL = 1e-3
+RTOL = 1e-4
+U32 = 2.0 ** -23
+
+
+def gamma(d: int) -> float:
+    return d * U32 / (1.0 - d * U32)
+
+
+def close(got, ref, atol: float = ATOL, rtol: float = RTOL):
+    """Returns (ok, worst_excess, index_of_worst)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return True, 0.0, None
+    excess = np.abs(got - ref) - (atol + rtol * np.abs(ref))
+    k = int(np.argmax(excess))
+    worst = float(excess.reshape(-1)[k])
+    return bool(np.all(excess <= 0) and np.all(np.isfinite(got))), worst, np.unravel_index(k, got.shape)
+
+
+def argmax_float(got, ref, q_rows, d_rows, valid=None):
+    """Checks a float argmax with the near-tie rule.
+
+    got, ref : int arrays of identical shape, entries are doc-token indices
+    q_rows   : callable (entry index tuple) -> fp64 query row q (length d)
+    d_rows   : callable (entry index tuple, t) -> fp64 doc row x_t
+    valid    : callable (entry index tuple, t) -> bool, or None (all valid)
+    Returns (n_mismatch, n_accepted, list of failing entries).
+    """
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    mism = np.argwhere(got != ref)
+    bad = []
+    acc = 0
+    for e in mism:
+        e = tuple(int(x) for x in e)
+        tg, to = int(got[e]), int(ref[e])
+        if valid is not None and not valid(e, tg):
+            bad.append((e, tg, to, "masked or out-of-range token"))
+            continue
+        q = q_rows(e)
+        xo = d_rows(e, to)
+        xg = d_rows(e, tg)
+        if xg is None:
+            bad.append((e, tg, to, "out-of-range token"))
+            continue
+        vo, vg = float(q @ xo), float(q @ xg)
+        eo = gamma(q.size) * float(np.abs(q * xo).sum())
+        eg = gamma(q.size) * float(np.abs(q * xg).sum())
+        if vo - vg <= eo + eg:
+            acc += 1
+        else:
+            bad.append((e, tg, to, f"gap {vo - vg:.3e} > bound {eo + eg:.3e}"))
+    return len(mism), acc, bad
+
+
+def dense_argmax_float(got, ref, Q64, D64, d_mask=None, pairs=None):
+    """argmax_float for the cross-product layout. got/ref are [Nq', Nd', Lq]
+    over the query/doc index lists `pairs = (I, J)` (default: all)."""
+    I, J = pairs if pairs is not None else (np.arange(Q64.shape[0]), np.arange(D64.shape[0]))
+    Ld = D64.shape[1]
+    dm = None if d_mask is None else np.asarray(d_mask).astype(bool)
+
+    def qr(e):
+        return Q64[I[e[0]], e[2]]
+
+    def dr(e, t):
+        if t < 0 or t >= Ld:
+            return None
+        return D64[J[e[1]], t]
+
+    def ok(e, t):
+        if t < 0 or t >= Ld:
+            return False
+        if dm is None:
+            return True
+        j = J[e[1]]
+        if not dm[j].any():
+            return False  # a doc with no valid token must report 0 exactly
+        return bool(dm[j, t])
+
+    return argmax_float(got, ref, qr, dr, ok)
+
+
+def varlen_argmax_float(got, ref, Q64, cu_q, D64, cu_d, q_index, d_index):
+    """argmax_float for packed sequences; got/ref are [len(q_index), len(d_index), max_lq]."""
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_d = np.asarray(cu_d, dtype=np.int64)
+
+    def qr(e):
+        i = q_index[e[0]]
+        return Q64[cu_q[i] + e[2]]
+
+    def dr(e, t):
+        j = d_index[e[1]]
+        if t < 0 or t >= cu_d[j + 1] - cu_d[j]:
+            return None
+        return D64[cu_d[j] + t]
+
+    def ok(e, t):
+        i, j = q_index[e[0]], d_index[e[1]]
+        ld = cu_d[j + 1] - cu_d[j]
+        if e[2] >= cu_q[i + 1] - cu_q[i]:
+            return False  # rows past the query length must be 0 exactly
+        return 0 <= t < ld
+
+    return argmax_float(got, ref, qr, dr, ok)

@@ -1,0 +1,124 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every entry
+point include/maxsim.h declares, and rejects bad arguments on the host before
+touching a device (every call here returns from host-side validation)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "maxsim.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_OVERFLOW, ERR_LAUNCH = range(6)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:maxsim_status_t|const char\*|int)\s+(maxsim_\w+)\s*\(",
+                                 txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from maxsim_scoring_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from maxsim_scoring_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd",
+                          "maxsim_status_string", "maxsim_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    txt = open(HEADER).read()
+    ver = int(re.search(r"#define MAXSIM_ABI_VERSION (\d+)", txt).group(1))
+    assert L.maxsim_abi_version() == ver
+    for s in range(6):
+        assert L.maxsim_status_string(s)
+    assert L.maxsim_status_string(99) == b"unknown status"
+
+
+def fwd(L, dtype=0, Q=FAKE, D=FAKE, Nq=2, Nd=3, Lq=4, Ld=5, d=128, qm=None, dm=None, sc=FAKE,
+        am=None):
+    return L.maxsim_fwd(dtype, Q, D, Nq, Nd, Lq, Ld, d, qm, dm, sc, am, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, Nq=-1) == ERR_SHAPE
+    assert fwd(L, Ld=-5) == ERR_SHAPE
+    assert fwd(L, d=64) == ERR_UNSUPPORTED
+    assert fwd(L, dtype=7) == ERR_UNSUPPORTED
+    assert fwd(L, sc=None) == ERR_NULL
+    assert fwd(L, Q=None) == ERR_NULL
+    assert fwd(L, D=None) == ERR_NULL
+    assert fwd(L, Nq=0) == OK            # nothing to do, nothing enqueued
+    assert fwd(L, Nd=0, sc=None) == OK
+    assert fwd(L, Nq=1 << 16, Nd=1 << 15, Lq=2, am=FAKE) == ERR_OVERFLOW
+    assert fwd(L, Nq=1 << 20, Nd=1 << 12) == ERR_OVERFLOW
+
+
+def test_varlen_validation(L):
+    f = L.maxsim_fwd_varlen
+    assert f(0, FAKE, FAKE, 1, -1, FAKE, FAKE, 2, 128, FAKE, None, None) == ERR_SHAPE
+    assert f(0, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 96, FAKE, None, None) == ERR_UNSUPPORTED
+    assert f(1, FAKE, None, 1, 32, FAKE, FAKE, 2, 128, FAKE, None, None) == ERR_NULL
+    assert f(1, FAKE, FAKE, 1, 32, FAKE, None, 2, 128, FAKE, None, None) == ERR_NULL
+    assert f(1, FAKE, FAKE, 0, 32, FAKE, FAKE, 2, 128, None, None, None) == OK
+    assert f(0, FAKE, FAKE, 1 << 10, 1 << 12, FAKE, FAKE, 1 << 10, 128, FAKE, FAKE, None) == ERR_OVERFLOW
+
+
+def test_i8_validation(L):
+    f = L.maxsim_fwd_i8
+    args = dict(Q=FAKE, qs=1.0, D=FAKE, ds=1.0, Nq=1, Nd=2, Lq=8, Ld=8, d=128, qm=None, dm=None,
+                si=FAKE, sf=FAKE, am=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["Q"], a["qs"], a["D"], a["ds"], a["Nq"], a["Nd"], a["Lq"], a["Ld"], a["d"],
+                 a["qm"], a["dm"], a["si"], a["sf"], a["am"], None)
+
+    assert call(si=None, sf=None) == ERR_NULL
+    assert call(d=256) == ERR_UNSUPPORTED
+    assert call(Lq=-1) == ERR_SHAPE
+    # Lq*d*127^2 must stay below 2^31: 1041 rows * 128 * 16129 overflow, 1040 do not
+    assert call(Lq=1041) == ERR_OVERFLOW
+    assert call(Lq=1040, Q=None) == ERR_NULL
+    assert call(Nq=0) == OK
+
+
+def test_bwd_validation(L):
+    f = L.maxsim_bwd
+
+    def call(dtype=0, Nq=2, Nd=3, Lq=4, Ld=5, d=128, Q=FAKE, D=FAKE, am=FAKE, g=FAKE, dQ=FAKE,
+             dD=FAKE, rp=FAKE, ci=FAKE):
+        return f(dtype, Q, D, Nq, Nd, Lq, Ld, d, None, None, am, g, dQ, dD, rp, ci, None)
+
+    assert call(Nq=-2) == ERR_SHAPE
+    assert call(d=100) == ERR_UNSUPPORTED
+    assert call(Ld=0) == ERR_SHAPE            # sources with no destination
+    assert call(am=None) == ERR_NULL
+    assert call(rp=None) == ERR_NULL
+    assert call(ci=None) == ERR_NULL
+    assert call(dQ=None) == ERR_NULL
+    assert call(dD=None) == ERR_NULL
+    assert call(Nq=1 << 11, Nd=1 << 10, Lq=1 << 10) == ERR_OVERFLOW
+    assert call(Nd=1 << 16, Ld=1 << 15) == ERR_OVERFLOW
+    assert call(Nq=0, Nd=0, Lq=0, Ld=0, Q=None, D=None, am=None, g=None, dQ=None, dD=None,
+                rp=None, ci=None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import maxsim_scoring_amd as ms
+    Q = torch.zeros((1, 4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ms.maxsim_fwd(Q, Q)

@@ -1,0 +1,332 @@
+"""GPU parity: every entry point of the HIP library against the CPU oracle.
+
+All calls go through the C ABI (via the ctypes binding). Inputs come from the
+seeded generators; expected values come only from the oracle. Rules (see
+oracle/compare.py): float scores/gradients within 1e-3 + 1e-4*|ref|; int8
+sums, int8 argmax and CSR maps bit-exact; float argmax exact except for
+certified near-ties.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from maxsim_scoring_amd import synth
+from oracle import compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def ms():
+    import maxsim_scoring_amd as m
+    m.binding.lib()
+    assert torch.cuda.is_available()
+    return m
+
+
+def _g(t):
+    return None if t is None else t.to(DEV)
+
+
+def _assert_close(name, got, ref):
+    ok, worst, where = compare.close(got, ref)
+    assert ok, f"{name}: worst excess {worst:.3e} at {where}"
+
+
+def _assert_float_argmax(name, got, ref, w, pairs=None):
+    n, acc, bad = compare.dense_argmax_float(got, ref, w.Q.double().numpy(), w.D.double().numpy(),
+                                             None if w.d_mask is None else w.d_mask.numpy(), pairs)
+    assert not bad, f"{name}: {len(bad)} argmax mismatches outside the near-tie bound: {bad[:5]}"
+    return n, acc
+
+
+def _run_dense(ms, w, want_argmax=True):
+    s, a = ms.maxsim_fwd(_g(w.Q), _g(w.D), _g(w.q_mask), _g(w.d_mask), want_argmax=want_argmax)
+    torch.cuda.synchronize()
+    return s.cpu(), (None if a is None else a.cpu())
+
+
+# --------------------------------------------------------------------- dense
+
+DENSE_CASES = [
+    # (Nq, Nd, Lq, Ld, dtype, q_mask_p, d_mask_p, dead_docs, dead_queries, dup)
+    (4, 32, 32, 180, torch.float16, 0.0, 0.0, 0, 0, False),    # the tiny workload's shape
+    (3, 5, 45, 200, torch.bfloat16, 0.3, 0.3, 1, 1, False),    # ragged tiles, masks, dead rows
+    (9, 4, 32, 64, torch.float16, 0.0, 0.1, 0, 0, False),      # 8 queries per workgroup + 1
+    (2, 3, 300, 130, torch.bfloat16, 0.2, 0.0, 0, 0, False),   # long query: two passes
+    (2, 2, 1, 1, torch.float16, 0.0, 0.0, 0, 0, False),        # Lq = Ld = 1
+    (1, 3, 7, 70, torch.float16, 0.0, 0.0, 0, 0, True),        # duplicated doc tokens
+    (5, 7, 128, 96, torch.bfloat16, 0.5, 0.5, 2, 1, False),
+    (2, 2, 33, 65, torch.float16, 0.0, 0.0, 0, 0, False),      # one past a tile edge
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}_{str(c[4])[6:]}")
+def test_dense_small(ms, case, oracle_mod):
+    Nq, Nd, Lq, Ld, dt, qp, dp, dd, dq, dup = case
+    _say(f"dense {case}")
+    w = synth.random_dense(100 + Lq + Ld, Nq, Nd, Lq, Ld, dtype=dt, q_mask_p=qp, d_mask_p=dp,
+                           dead_docs=dd, dead_queries=dq, dup_tokens=dup)
+    s, a = _run_dense(ms, w)
+    rs, ra = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    _assert_close("scores", s.numpy(), rs)
+    _assert_float_argmax("argmax", a.numpy(), ra, w)
+    # no-argmax variant gives the same scores
+    s2, _ = _run_dense(ms, w, want_argmax=False)
+    _assert_close("scores (no argmax)", s2.numpy(), rs)
+
+
+def test_dense_exact_ties(ms, oracle_mod):
+    """Values k/8: every dot product is exact in fp32 too, so argmax must match
+    the oracle exactly, including lowest-index tie-breaking."""
+    _say("dense exact ties")
+    rng = np.random.default_rng(3)
+    Nq, Nd, Lq, Ld = 3, 4, 40, 150
+    Q = torch.from_numpy(rng.integers(-2, 3, size=(Nq, Lq, 128)) / 8.0).to(torch.float16)
+    D = torch.from_numpy(rng.integers(-2, 3, size=(Nd, Ld, 128)) / 8.0).to(torch.float16)
+    D[:, 100:140] = D[:, 10:50]
+    D[2] = D[2, 0]
+    dm = torch.from_numpy((rng.random((Nd, Ld)) > 0.1).astype(np.uint8))
+    w = synth.Dense("ties", Q, D, None, dm)
+    s, a = _run_dense(ms, w)
+    rs, ra = oracle_mod.fwd(Q, D, None, dm)
+    assert np.array_equal(s.numpy().astype(np.float64), rs)
+    assert np.array_equal(a.numpy(), ra)
+
+
+def test_dense_fp16_subnormals(ms, oracle_mod):
+    """fp16 subnormal inputs must not be flushed by the MFMA path."""
+    _say("dense fp16 subnormals")
+    rng = np.random.default_rng(4)
+    Q = torch.from_numpy(rng.standard_normal((2, 32, 128))).to(torch.float16)
+    sub = torch.from_numpy(rng.integers(1, 1024, size=(3, 64, 128)).astype(np.int16))
+    D = sub.view(torch.float16)  # positive subnormals (exponent field 0)
+    D = torch.where(torch.from_numpy(rng.random((3, 64, 128)) < 0.5), D, -D)
+    w = synth.Dense("subnormal", Q, D.contiguous())
+    s, a = _run_dense(ms, w)
+    rs, ra = oracle_mod.fwd(w.Q, w.D)
+    assert np.abs(rs).max() > 1e-3  # the inputs really carry signal
+    _assert_close("scores", s.numpy() * 1e3, rs * 1e3)  # tolerance scaled to the values' size
+    _assert_float_argmax("argmax", a.numpy(), ra, w)
+
+
+def test_dense_empty_and_degenerate(ms):
+    _say("dense empty sizes")
+    Q = torch.zeros((2, 0, 128), dtype=torch.float16, device=DEV)
+    D = torch.randn((3, 5, 128), device=DEV).half()
+    s, a = ms.maxsim_fwd(Q, D, want_argmax=True)
+    torch.cuda.synchronize()
+    assert torch.all(s == 0)
+    D0 = torch.zeros((3, 0, 128), dtype=torch.float16, device=DEV)
+    Q1 = torch.randn((2, 4, 128), device=DEV).half()
+    s, a = ms.maxsim_fwd(Q1, D0, want_argmax=True)
+    torch.cuda.synchronize()
+    assert torch.all(s == 0) and torch.all(a == 0)
+    s, a = ms.maxsim_fwd(Q1[:0], D, want_argmax=True)
+    assert s.numel() == 0
+
+
+def test_colpali_full_size_sampled(ms, oracle_mod):
+    """The ColPali cross-product (128x128 pairs, Lq=128, Ld=1024, bf16,
+    prefix masks) in the launch configuration the benchmark times; the oracle
+    scores a sample of 6 queries x 8 docs, argmax checked for those pairs."""
+    _say("colpali full size")
+    w = synth.colpali_bf16()
+    s, a = _run_dense(ms, w)
+    rng = np.random.default_rng(0)
+    I = np.sort(np.concatenate([[0, 127], rng.choice(np.arange(1, 127), 4, replace=False)]))
+    J = np.sort(np.concatenate([[0, 127], rng.choice(np.arange(1, 127), 6, replace=False)]))
+    rs, ra = oracle_mod.fwd(w.Q[I], w.D[J], w.q_mask[I], w.d_mask[J])
+    _assert_close("scores", s.numpy()[np.ix_(I, J)], rs)
+    n, acc = _assert_float_argmax("argmax", a.numpy()[np.ix_(I, J)], ra, w, pairs=(I, J))
+    print(f"argmax near-tie deviations: {n} of {ra.size}")
+    # determinism: a second run is bitwise identical
+    s2, a2 = _run_dense(ms, w)
+    assert torch.equal(s, s2) and torch.equal(a, a2)
+
+
+# --------------------------------------------------------------------- varlen
+
+def _run_varlen(ms, w, want_argmax):
+    s, a = ms.maxsim_fwd_varlen(_g(w.Q), _g(w.cu_q), w.max_lq, _g(w.D), _g(w.cu_d),
+                                want_argmax=want_argmax)
+    torch.cuda.synchronize()
+    return s.cpu(), (None if a is None else a.cpu())
+
+
+VARLEN_CASES = [
+    ([32], [50, 0, 1, 17, 300, 0, 0, 64, 16, 15]),          # empty docs, tile edges
+    ([5, 0, 32, 31], list(range(0, 120, 7))),               # several queries, an empty one
+    ([60, 17], [40] * 30 + [0] * 5),                        # 4 N-tiles, trailing empty docs
+    ([130], [33, 80, 1, 0, 200]),                           # multi-pass query
+    ([3], [0, 0, 0]),                                       # only empty docs
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"q{len(c[0])}_d{len(c[1])}")
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+def test_varlen_small(ms, oracle_mod, case, dtype):
+    ql, dl = case
+    _say(f"varlen {ql} {dl} {dtype}")
+    w = synth.random_varlen(200 + len(dl), ql, dl, dtype=dtype)
+    s, a = _run_varlen(ms, w, True)
+    rs, ra = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    _assert_close("scores", s.numpy(), rs)
+    Nq, Nd = len(ql), len(dl)
+    n, acc, bad = compare.varlen_argmax_float(a.numpy(), ra, w.Q.double().numpy(), w.cu_q.numpy(),
+                                              w.D.double().numpy(), w.cu_d.numpy(),
+                                              np.arange(Nq), np.arange(Nd))
+    assert not bad, bad[:5]
+    s2, _ = _run_varlen(ms, w, False)
+    _assert_close("scores (no argmax)", s2.numpy(), rs)
+
+
+def test_varlen_many_docs(ms, oracle_mod):
+    """Enough docs that many streaming units split the range."""
+    _say("varlen 20000 docs")
+    lens = synth.rerank_lengths(9, 20000, 1, 120)
+    w = synth.random_varlen(9, [32], lens)
+    s, _ = _run_varlen(ms, w, False)
+    rs, _ = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, want_argmax=False)
+    _assert_close("scores", s.numpy(), rs)
+    s2, _ = _run_varlen(ms, w, False)
+    assert torch.equal(s, s2)
+
+
+def _repack(w, docs):
+    cu = w.cu_d.numpy().astype(np.int64)
+    parts = [w.D[cu[j]:cu[j + 1]] for j in docs]
+    lens = np.array([cu[j + 1] - cu[j] for j in docs])
+    return torch.cat(parts), synth.cu_seqlens(lens)
+
+
+def test_rerank_full_size_sampled(ms, oracle_mod):
+    """One 32-token query against 100,000 packed docs of 50-300 tokens (about
+    17.5M tokens, 4.5 GB fp16) in the benchmark's launch configuration; the
+    oracle scores 1,200 docs including both ends of the range."""
+    _say("rerank varlen full size")
+    w = synth.rerank_varlen_fp16()
+    s, _ = _run_varlen(ms, w, False)
+    rng = np.random.default_rng(1)
+    docs = np.unique(np.concatenate([np.arange(300), np.arange(99700, 100000),
+                                     rng.choice(100000, 600, replace=False)]))
+    Dp, cu = _repack(w, docs)
+    rs, _ = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, Dp, cu, want_argmax=False)
+    _assert_close("scores", s.numpy()[:, docs], rs)
+    # argmax on a window of docs
+    s_a, a = _run_varlen(ms, w, True)
+    assert torch.equal(s_a, s)
+    win = np.arange(5000, 5200)
+    Dp, cu = _repack(w, win)
+    rs, ra = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, Dp, cu)
+    n, acc, bad = compare.varlen_argmax_float(a.numpy()[:, win], ra, w.Q.double().numpy(),
+                                              w.cu_q.numpy(), Dp.double().numpy(), cu.numpy(),
+                                              np.arange(1), np.arange(len(win)))
+    assert not bad, bad[:5]
+
+
+# --------------------------------------------------------------------- int8
+
+def _run_i8(ms, w, want_argmax):
+    si, sf, a = ms.maxsim_fwd_i8(_g(w.Q), w.q_scale, _g(w.D), w.d_scale, _g(w.q_mask),
+                                 _g(w.d_mask), want_argmax=want_argmax)
+    torch.cuda.synchronize()
+    return si.cpu(), sf.cpu(), (None if a is None else a.cpu())
+
+
+INT8_CASES = [
+    (2, 5, 9, 13, "ternary", 0.2, 0.2),
+    (3, 4, 100, 130, "quantised", 0.0, 0.3),
+    (1, 3, 1024, 70, "quantised", 0.1, 0.0),     # 32 N-tiles: one pass of 8 waves x 4
+    (1, 2, 1040, 40, "quantised", 0.0, 0.0),     # past one workgroup: two passes
+    (2, 3, 128, 64, "extreme", 0.0, 0.0),        # largest sums
+    (4, 3, 32, 200, "ternary", 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", INT8_CASES, ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}_{c[4]}")
+def test_int8_small(ms, oracle_mod, case):
+    Nq, Nd, Lq, Ld, kind, qp, dp = case
+    _say(f"int8 {case}")
+    w = synth.random_int8(300 + Lq, Nq, Nd, Lq, Ld, ternary=kind == "ternary",
+                          extreme=kind == "extreme", d_mask_p=dp, q_mask_p=qp)
+    si, sf, a = _run_i8(ms, w, True)
+    ri, rf, ra = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    assert np.array_equal(si.numpy().astype(np.int64), ri)
+    _assert_close("scores", sf.numpy(), rf)
+    assert np.array_equal(sf.numpy(), rf.astype(np.float32))  # same double rounding
+    assert np.array_equal(a.numpy(), ra)
+    si2, sf2, _ = _run_i8(ms, w, False)
+    assert torch.equal(si2, si) and torch.equal(sf2, sf)
+
+
+def test_int8_full_size_sampled(ms, oracle_mod):
+    """One 1024-token query against 10,000 docs of 1024 tokens, int8 with
+    per-tensor scales; the oracle scores 24 docs exactly."""
+    _say("int8 full size")
+    w = synth.int8_long_query()
+    si, sf, _ = _run_i8(ms, w, False)
+    rng = np.random.default_rng(2)
+    docs = np.sort(np.concatenate([[0, 9999], rng.choice(np.arange(1, 9999), 22, replace=False)]))
+    ri, rf, _ = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D[docs], w.d_scale, want_argmax=False)
+    assert np.array_equal(si.numpy()[:, docs].astype(np.int64), ri)
+    _assert_close("scores", sf.numpy()[:, docs], rf)
+
+
+# --------------------------------------------------------------------- backward
+
+def _run_bwd(ms, w, argmax, g):
+    out = ms.maxsim_bwd(_g(w.Q), _g(w.D), _g(argmax), _g(g), _g(w.q_mask), _g(w.d_mask))
+    torch.cuda.synchronize()
+    return [t.cpu() for t in out]
+
+
+def _check_bwd(ms, oracle_mod, w, argmax, g):
+    dQ, dD, rp, ci = _run_bwd(ms, w, argmax, g)
+    rdQ, rdD, rrp, rci = oracle_mod.bwd(w.Q, w.D, argmax, g, w.q_mask, w.d_mask)
+    assert np.array_equal(rp.numpy(), rrp), "row_ptr"
+    assert np.array_equal(ci.numpy(), rci), "col_idx"
+    _assert_close("dQ", dQ.numpy(), rdQ)
+    _assert_close("dD", dD.numpy(), rdD)
+    again = _run_bwd(ms, w, argmax, g)
+    assert all(torch.equal(x, y) for x, y in zip(again, (dQ, dD, rp, ci))), "not deterministic"
+
+
+BWD_CASES = [
+    (3, 4, 9, 14, torch.float16, 0.3, 0.2, 1, 0.0),
+    (5, 6, 70, 130, torch.bfloat16, 0.2, 0.1, 1, 0.0),
+    (4, 3, 64, 64, torch.bfloat16, 0.0, 0.0, 0, 0.7),   # hub token: 70% of sources in one row
+    (2, 2, 1, 5000, torch.float16, 0.0, 0.0, 0, 0.0),   # CSR bins in two rounds
+    (130, 2, 3, 10, torch.float16, 0.0, 0.0, 0, 0.0),   # many queries per doc
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}_hub{c[8]}")
+def test_bwd_small(ms, oracle_mod, case):
+    Nq, Nd, Lq, Ld, dt, qp, dp, dead, hub = case
+    _say(f"bwd {case}")
+    w = synth.random_dense(400 + Lq, Nq, Nd, Lq, Ld, dtype=dt, q_mask_p=qp, d_mask_p=dp,
+                           dead_docs=dead)
+    if hub > 0:
+        argmax = synth.draw_argmax(400 + Lq, Nq, Nd, Lq, Ld, None, hub_frac=hub)
+    else:
+        _, ra = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)  # the oracle's forward argmax
+        argmax = torch.from_numpy(ra)
+    g = synth.upstream_grad(400 + Lq, Nq, Nd)
+    _check_bwd(ms, oracle_mod, w, argmax, g)
+
+
+def test_bwd_full_size(ms, oracle_mod):
+    """Backward at the ColPali shapes (dQ [128,128,128], dD [128,1024,128]) with
+    an argmax drawn over each doc's valid prefix; every output compared."""
+    _say("bwd full size")
+    w = synth.colpali_bf16()
+    b = synth.colpali_backward(fwd=w)
+    _check_bwd(ms, oracle_mod, w, b.argmax, b.grad_scores)
