@@ -83,7 +83,9 @@ maxsim_status_t maxsim_fwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
  *   argmax  [Nq, Nd, max_lq] int32 or NULL: doc-relative index; rows s at or
  *           past the query's length, and every row of an empty doc, are 0.
  * Empty sequences contribute 0. Token offsets are 64-bit inside the kernels.
- * Errors: NULL, SHAPE (negative sizes, max_lq < 0), UNSUPPORTED (d, dtype),
+ * Q (or D) may be NULL only when its packed tensor has no rows.
+ * Errors: NULL (cu_q, cu_d or scores missing), SHAPE (negative sizes,
+ * max_lq < 0), UNSUPPORTED (d, dtype),
  * OVERFLOW when argmax is requested and Nq*Nd*max_lq >= 2^31.
  */
 maxsim_status_t maxsim_fwd_varlen(maxsim_dtype_t dtype, const void* Q, const int32_t* cu_q,

@@ -69,7 +69,9 @@ maxsim_status_t maxsim_fwd_varlen(maxsim_dtype_t dtype, const void* Q, const int
     if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0) return MAXSIM_ERR_SHAPE;
     if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
     if (Nq == 0 || Nd == 0) return MAXSIM_OK;
-    if (!cu_q || !cu_d || !scores || !Q || !D) return MAXSIM_ERR_NULL;
+    // Q or D may be NULL only when that packed tensor holds no tokens (an
+    // empty torch tensor has no storage); the kernels then never read it.
+    if (!cu_q || !cu_d || !scores) return MAXSIM_ERR_NULL;
     if (Nd > kI32Max - 1) return MAXSIM_ERR_OVERFLOW;
     const int64_t pairs = mul_sat(Nq, Nd);
     if (pairs < 0 || pairs > kI32Max) return MAXSIM_ERR_OVERFLOW;

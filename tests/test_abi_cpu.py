@@ -72,6 +72,7 @@ def test_varlen_validation(L):
     assert f(0, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 96, FAKE, None, None) == ERR_UNSUPPORTED
     assert f(1, FAKE, None, 1, 32, FAKE, FAKE, 2, 128, FAKE, None, None) == ERR_NULL
     assert f(1, FAKE, FAKE, 1, 32, FAKE, None, 2, 128, FAKE, None, None) == ERR_NULL
+    assert f(1, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 128, None, None, None) == ERR_NULL
     assert f(1, FAKE, FAKE, 0, 32, FAKE, FAKE, 2, 128, None, None, None) == OK
     assert f(0, FAKE, FAKE, 1 << 10, 1 << 12, FAKE, FAKE, 1 << 10, 128, FAKE, FAKE, None) == ERR_OVERFLOW
 
