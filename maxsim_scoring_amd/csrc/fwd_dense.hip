@@ -25,78 +25,6 @@ constexpr int kTileRows = 64;  // doc tokens per pipeline stage (2 MFMA M-tiles)
 constexpr int kStages = 3;
 constexpr int kMaxMaskTokens = 32768;  // d_mask bits kept in LDS per segment
 
-__device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
-
-// Barrier without the implicit vmcnt(0) of __syncthreads(): loads that are
-// still in flight for later pipeline stages keep flying across it. LDS writes
-// made before it are waited for (lgkmcnt(0)) so every wave sees them after.
-__device__ __forceinline__ void block_barrier()
-{
-    lds_fence();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    lds_fence();
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// LDS reads of direct-to-LDS data. They are issued from inline assembly on
-// purpose: the compiler cannot tell which ring stage an outstanding
-// direct-to-LDS load targets, so for a plain LDS load it would wait for every
-// load in flight (vmcnt(0)) and collapse the prefetch pipeline. The explicit
-// vmcnt wait + barrier at the top of each iteration already guarantees that
-// the stage being read has landed. Each helper waits for its own reads.
-__device__ __forceinline__ uint32_t lds_addr(const void* p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ void lds_read4(i32x4& a0, i32x4& a1, i32x4& a2, i32x4& a3,
-                                          uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3)
-{
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-        : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
-        : "memory");
-}
-
-__device__ __forceinline__ void lds_read8(i32x4 (&a)[8], const uint32_t (&p)[8])
-{
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %13\n\t"
-        "ds_read_b128 %6, %14\n\t"
-        "ds_read_b128 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
-          "=&v"(a[6]), "=&v"(a[7])
-        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
-        : "memory");
-}
-
-__device__ __forceinline__ uint64_t lds_read_u64_uniform(const uint64_t* p)
-{
-    uint64_t v;
-    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // Fold one 32x32 accumulator tile into the running (max, argmax) of each
 // N-tile. Lane rows are 8*(q/4) + 4*h + q%4; q ascends with the row, so a
 // strict '>' keeps the lowest index on ties. `lbits` bit r = row r + 4h valid.

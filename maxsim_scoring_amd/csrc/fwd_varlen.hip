@@ -10,13 +10,17 @@
 // Design: the reranking regime is bound by HBM reads of the packed D, so each
 // wave is a persistent streaming unit that owns a token-balanced, contiguous
 // range of whole docs and walks it as one flat stream of 16-token tiles,
-// regardless of doc boundaries. D rows go straight from HBM into the MFMA
-// A-operand registers (lane l holds token l % 16, 64 contiguous bytes per
-// instruction), with a register ring of kPrefetch tiles in flight. The query
-// (B operand) stays in VGPRs. Per tile each lane folds 4 doc rows into its
-// running max; a doc boundary inside a tile splits the fold with -inf masks,
-// and a finished doc is reduced across the 4 row groups and 16 query columns
-// in a fixed order and written once. No LDS, no barriers, no atomics.
+// regardless of doc boundaries. Each 4 KB tile is fetched with fully
+// coalesced, non-temporal direct-to-LDS loads (every instruction reads four
+// whole rows) into a per-wave ring of kStages tiles; the 16-byte chunks are
+// XOR-swizzled on the way in so that the MFMA A-operand reads back from LDS
+// (lane l takes token l % 16) are bank-conflict free. Loads that match the
+// MFMA layout directly (16 rows x 64 bytes per instruction) measured slower.
+// The query (B operand) stays in VGPRs. Per tile each lane folds 4 doc rows
+// into its running max; a doc boundary inside a tile splits the fold with
+// -inf masks, and a finished doc is reduced across the 4 row groups and 16
+// query columns in a fixed order and written once. The ring is private to the
+// wave, so there are no barriers, and there are no atomics.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,8 +28,22 @@ namespace maxsim {
 
 namespace {
 
-constexpr int kPrefetch = 4;   // tiles in flight per wave
+#ifndef MAXSIM_VARLEN_STAGES
+#define MAXSIM_VARLEN_STAGES 3
+#endif
+constexpr int kStages = MAXSIM_VARLEN_STAGES;  // 4 KB tiles in flight per wave
 constexpr int kUnitsPerBlock = 4;
+constexpr int kTileBytes = 16 * kD * 2;
+constexpr int kNonTemporal = 2;  // cache-policy bit of the load: streamed once
+
+// vmcnt(4 * n) for the number n of later tiles still in flight
+__device__ __forceinline__ void wait_tiles_behind(int n)
+{
+    if (n <= 0) wait_vmcnt<0>();
+    else if (n == 1) wait_vmcnt<4>();
+    else if (n == 2) wait_vmcnt<8>();
+    else wait_vmcnt<12>();
+}
 
 // Smallest j in [0, n] with cu[j] >= target, found by the whole wave with
 // 64 probes per round (cu is non-decreasing and cu[n] >= target).
@@ -54,6 +72,8 @@ __global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenA
 {
     constexpr int RB = kD * 2;   // bytes per token row
     constexpr int KS = kD / 32;  // 16x16x32: 4 K-steps
+    static_assert(KS == 4, "one lds_read4 per tile");
+    __shared__ __attribute__((aligned(16))) unsigned char ring_lds[kUnitsPerBlock][kStages][kTileBytes];
     const int lane = lane_id();
     const int col = lane & 15;   // query token within an N-tile / doc row within a tile
     const int g = lane >> 4;     // row group: this lane owns tile rows 4g .. 4g+3
@@ -104,9 +124,13 @@ __global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenA
         int cu_cache = a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd];
         auto cu_next = [&](int jj) -> int64_t {  // cu_d[jj + 1]
             int off = jj + 1 - cache_base;
-            if (off >= 64) {
+            if (off >= 64) {  // once per 64 docs
                 cache_base = jj + 1;
                 cu_cache = a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd];
+                // wait here, on the rare refill path, so that the compiler does
+                // not keep cu_cache "in flight" and wait for the whole tile ring
+                // at every doc boundary
+                wait_vmcnt<0>();
                 off = 0;
             }
             return (int64_t)__builtin_amdgcn_readlane(cu_cache, off);
@@ -215,32 +239,51 @@ __global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenA
             }
         }
 
-        // ---- register ring of prefetched tiles -------------------------------
-        i32x4 ring[kPrefetch][KS];
-        auto load_tile = [&](int64_t t, i32x4 (&dst)[KS]) {
-            int64_t row = u0 + t * 16 + col;
-            if (row >= u1) row = u1 - 1;  // rows past the range are never folded
-            const unsigned char* p = Dbase + row * RB + g * 16;
+        // ---- per-wave LDS ring of prefetched tiles ----------------------------
+        unsigned char* ring = &ring_lds[threadIdx.x >> 6][0][0];
+        auto issue_tile = [&](int64_t t, int stage) {
+            unsigned char* sb = ring + stage * kTileBytes;
 #pragma unroll
-            for (int k = 0; k < KS; ++k) dst[k] = *(const i32x4*)(p + k * 64);
+            for (int k = 0; k < 4; ++k) {  // instruction k fills rows 4k .. 4k+3
+                const int row = 4 * k + (lane >> 4);
+                const int lc = (lane & 15) ^ row;  // logical chunk stored at slot lane & 15
+                int64_t grow = u0 + t * 16 + row;
+                if (grow >= u1) grow = u1 - 1;  // rows past the range are never folded
+                __builtin_amdgcn_global_load_lds((const void*)(Dbase + grow * RB + lc * 16),
+                                                 LDS_PTR(sb + k * 1024), 16, 0, kNonTemporal);
+            }
         };
+        // A-operand read offsets: row = lane % 16, logical chunk 4k + g
+        uint32_t frag_off[KS];
 #pragma unroll
-        for (int q = 0; q < kPrefetch; ++q)
-            if (q < ntile) load_tile(q, ring[q]);
+        for (int k = 0; k < KS; ++k) frag_off[k] = col * RB + (((4 * k + g) ^ col) * 16);
+        const uint32_t ring_base = lds_addr(ring);
 
-        for (int64_t tb = 0; tb < ntile && !done; tb += kPrefetch) {
+        wait_vmcnt<0>();  // query fragments have landed before the pipeline starts
 #pragma unroll
-            for (int q = 0; q < kPrefetch; ++q) {
-                const int64_t t = tb + q;
-                if (t >= ntile || done) break;
+        for (int q = 0; q < kStages; ++q)
+            if (q < ntile) issue_tile(q, q);
+
+        int stage = 0;
+        for (int64_t t = 0; t < ntile && !done; ++t) {
+            {
+                const int64_t behind = ntile - 1 - t;
+                wait_tiles_behind(behind < kStages - 1 ? (int)behind : kStages - 1);
+            }
+            i32x4 af[KS];
+            const uint32_t sbase = ring_base + stage * kTileBytes;
+            lds_read4(af[0], af[1], af[2], af[3], sbase + frag_off[0], sbase + frag_off[1],
+                      sbase + frag_off[2], sbase + frag_off[3]);
+            if (t + kStages < ntile) issue_tile(t + kStages, stage);
+            stage = stage + 1 == kStages ? 0 : stage + 1;
+            {
                 f32x4 acc[NTQ];
 #pragma unroll
                 for (int n = 0; n < NTQ; ++n) {
                     acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int k = 0; k < KS; ++k) acc[n] = mfma16<E>(ring[q][k], qf[n][k], acc[n]);
+                    for (int k = 0; k < KS; ++k) acc[n] = mfma16<E>(af[k], qf[n][k], acc[n]);
                 }
-                if (t + kPrefetch < ntile) load_tile(t + kPrefetch, ring[q]);
 
                 const int64_t ts = u0 + t * 16;
                 int64_t lo = ts;
@@ -260,6 +303,7 @@ __global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenA
                 }
             }
         }
+        wait_vmcnt<0>();  // nothing of this unit's ring is still in flight
         // docs left with no tokens after the last tile (only when ntile == 0)
         while (!done) {
             finish_doc();
