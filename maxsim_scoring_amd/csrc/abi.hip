@@ -1,6 +1,6 @@
 // The C ABI declared in include/maxsim.h: host-side validation (before
 // anything is enqueued), then one launcher per entry point.
-#include "../../include/maxsim.h"
+#include "maxsim.h"
 
 #include <climits>
 

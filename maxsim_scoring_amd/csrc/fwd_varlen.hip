@@ -19,8 +19,9 @@
 // The query (B operand) stays in VGPRs. Per tile each lane folds 4 doc rows
 // into its running max; a doc boundary inside a tile splits the fold with
 // -inf masks, and a finished doc is reduced across the 4 row groups and 16
-// query columns in a fixed order and written once. The ring is private to the
-// wave, so there are no barriers, and there are no atomics.
+// query columns in a fixed order and written once. All cursor state is
+// wave-uniform (scalar registers). The ring is private to the wave, so there
+// are no barriers, and there are no atomics.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,7 +34,8 @@ namespace {
 #endif
 constexpr int kStages = MAXSIM_VARLEN_STAGES;  // 4 KB tiles in flight per wave
 constexpr int kUnitsPerBlock = 4;
-constexpr int kTileBytes = 16 * kD * 2;
+constexpr int kRowBytes = kD * 2;
+constexpr int kTileBytes = 16 * kRowBytes;
 constexpr int kNonTemporal = 2;  // cache-policy bit of the load: streamed once
 
 // vmcnt(4 * n) for the number n of later tiles still in flight
@@ -44,6 +46,8 @@ __device__ __forceinline__ void wait_tiles_behind(int n)
     else if (n == 2) wait_vmcnt<8>();
     else wait_vmcnt<12>();
 }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Smallest j in [0, n] with cu[j] >= target, found by the whole wave with
 // 64 probes per round (cu is non-decreasing and cu[n] >= target).
@@ -62,7 +66,39 @@ __device__ int wave_lower_bound(const int32_t* __restrict__ cu, int n, int64_t t
         lo = nlo < hi ? nlo : hi;
         hi = nhi < hi ? nhi : hi;
     }
-    return lo;
+    return uniform(lo);
+}
+
+// The doc boundary j whose offset cu[j] is nearest to `target` (ties to the
+// lower one). Units end where the next one starts, so every doc is owned once;
+// rounding to the nearest boundary halves the worst token imbalance compared
+// with always rounding up.
+__device__ int nearest_boundary(const int32_t* __restrict__ cu, int n, int64_t target)
+{
+    const int j1 = wave_lower_bound(cu, n, target);  // first boundary at or above
+    if (j1 == 0) return 0;
+    const int64_t above = (int64_t)cu[j1] - target;
+    const int64_t below = target - (int64_t)cu[j1 - 1];
+    return uniform(below <= above ? j1 - 1 : j1);
+}
+
+// Sum over the 16 lanes of each DPP row; every lane of the row receives the
+// same bits (each step adds a value and its mirror image, and fp addition is
+// commutative).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x)
+{
+    const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false);
+    return x + __builtin_bit_cast(float, o);
+}
+
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);  // row_half_mirror
+    v = dpp_add<0x140>(v);  // row_mirror
+    return v;
 }
 
 }  // namespace
@@ -70,13 +106,12 @@ __device__ int wave_lower_bound(const int32_t* __restrict__ cu, int n, int64_t t
 template <int E, bool ARGMAX, int NTQ>
 __global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenArgs a)
 {
-    constexpr int RB = kD * 2;   // bytes per token row
     constexpr int KS = kD / 32;  // 16x16x32: 4 K-steps
     static_assert(KS == 4, "one lds_read4 per tile");
     __shared__ __attribute__((aligned(16))) unsigned char ring_lds[kUnitsPerBlock][kStages][kTileBytes];
     const int lane = lane_id();
-    const int col = lane & 15;   // query token within an N-tile / doc row within a tile
-    const int g = lane >> 4;     // row group: this lane owns tile rows 4g .. 4g+3
+    const int col = lane & 15;  // query token within an N-tile / doc row within a tile
+    const int g = lane >> 4;    // row group: this lane owns tile rows 4g .. 4g+3
 
     const int unit = blockIdx.x * kUnitsPerBlock + (threadIdx.x >> 6);
     const int U = a.units;
@@ -84,199 +119,202 @@ __global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenA
 
     const int Nd = (int)a.Nd;
     const int64_t T = a.cu_d[Nd];
-    const int64_t tgt0 = (T * unit) / U;
-    const int64_t tgt1 = (T * (unit + 1)) / U;
-    const int jb = wave_lower_bound(a.cu_d, Nd, tgt0);
-    const int je = unit + 1 == U ? Nd : wave_lower_bound(a.cu_d, Nd, tgt1);
+    const int jb = unit == 0 ? 0 : nearest_boundary(a.cu_d, Nd, (T * unit) / U);
+    const int je = unit + 1 == U ? Nd : nearest_boundary(a.cu_d, Nd, (T * (unit + 1)) / U);
     if (jb >= je) return;
 
-  for (int64_t i = blockIdx.y; i < a.Nq; i += gridDim.y) {
-    const int64_t q0 = a.cu_q[i];
-    int64_t lq = (int64_t)a.cu_q[i + 1] - q0;
-    if (lq > a.max_lq) lq = a.max_lq;
-    if (lq < 0) lq = 0;
+    // token range of the unit; offsets below are relative to u0 and fit int32
     const int64_t u0 = a.cu_d[jb];
-    const int64_t u1 = a.cu_d[je];
-    const int64_t ntile = (u1 - u0 + 15) >> 4;
-    const unsigned char* Dbase = (const unsigned char*)a.D;
-    const int npass = lq == 0 ? 1 : (int)((lq + 16 * NTQ - 1) / (16 * NTQ));
+    const int span = uniform((int)((int64_t)a.cu_d[je] - u0));
+    const int ntile = (span + 15) >> 4;
+    const unsigned char* unit_ptr = (const unsigned char*)a.D + u0 * kRowBytes;
 
-    for (int pass = 0; pass < npass; ++pass) {
-        // ---- query fragments for this pass (B operand: col = token, k-quarter g)
-        i32x4 qf[NTQ][KS];
-        bool tok_ok[NTQ];
+    // per-lane byte offsets inside a tile for the 4 load instructions: slot
+    // (row 4k + lane/16, chunk lane%16) holds logical chunk (lane%16) ^ row
+    int load_row[4], load_off[4];
 #pragma unroll
-        for (int n = 0; n < NTQ; ++n) {
-            const int64_t s = (int64_t)pass * 16 * NTQ + n * 16 + col;
-            tok_ok[n] = s < lq;
-            const unsigned char* qrow = (const unsigned char*)a.Q + (q0 + (tok_ok[n] ? s : 0)) * RB;
+    for (int k = 0; k < 4; ++k) {
+        load_row[k] = 4 * k + g;
+        load_off[k] = load_row[k] * kRowBytes + ((col ^ load_row[k]) * 16);
+    }
+    unsigned char* ring = &ring_lds[threadIdx.x >> 6][0][0];
+    const uint32_t ring_base = lds_addr(ring);
+    // A-operand read offsets: row = lane % 16, logical chunk 4k + g
+    uint32_t frag_off[KS];
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                i32x4 v = {0, 0, 0, 0};
-                if (tok_ok[n]) v = *(const i32x4*)(qrow + (4 * k + g) * 16);
-                qf[n][k] = v;
+    for (int k = 0; k < KS; ++k) frag_off[k] = col * kRowBytes + (((4 * k + g) ^ col) * 16);
+
+    auto issue_tile = [&](int t, int stage) {
+        const unsigned char* tp = unit_ptr + (int64_t)t * kTileBytes;
+        unsigned char* sb = ring + stage * kTileBytes;
+        const int rows_left = span - t * 16;  // rows of this tile inside the unit
+        if (rows_left >= 16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                __builtin_amdgcn_global_load_lds((const void*)(tp + load_off[k]),
+                                                 LDS_PTR(sb + k * 1024), 16, 0, kNonTemporal);
+        } else {  // last tile: rows past the unit re-read its last row (never folded)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r = load_row[k] < rows_left ? load_row[k] : rows_left - 1;
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(tp + r * kRowBytes + ((col ^ load_row[k]) * 16)),
+                    LDS_PTR(sb + k * 1024), 16, 0, kNonTemporal);
             }
         }
+    };
 
-        // ---- doc cursor: cu_d values cached one per lane, read with readlane
-        int j = jb;
-        int cache_base = jb + 1;  // lane k holds cu_d[cache_base + k]
-        int cu_cache = a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd];
-        auto cu_next = [&](int jj) -> int64_t {  // cu_d[jj + 1]
-            int off = jj + 1 - cache_base;
-            if (off >= 64) {  // once per 64 docs
-                cache_base = jj + 1;
-                cu_cache = a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd];
-                // wait here, on the rare refill path, so that the compiler does
-                // not keep cu_cache "in flight" and wait for the whole tile ring
-                // at every doc boundary
-                wait_vmcnt<0>();
-                off = 0;
-            }
-            return (int64_t)__builtin_amdgcn_readlane(cu_cache, off);
-        };
-        int64_t doc_start = u0;
-        int64_t doc_end = cu_next(j);
+    for (int64_t i = blockIdx.y; i < a.Nq; i += gridDim.y) {
+        const int64_t q0 = a.cu_q[i];
+        int64_t lq64 = (int64_t)a.cu_q[i + 1] - q0;
+        if (lq64 > a.max_lq) lq64 = a.max_lq;
+        if (lq64 < 0) lq64 = 0;
+        const int lq = uniform((int)lq64);
+        const int npass = lq == 0 ? 1 : (lq + 16 * NTQ - 1) / (16 * NTQ);
+        float* score_row = a.scores + i * a.Nd;
+        int32_t* arg_row = ARGMAX ? a.argmax + i * a.Nd * (int64_t)a.max_lq : nullptr;
 
-        float m[NTQ];
-        int idx[NTQ];
-#pragma unroll
-        for (int n = 0; n < NTQ; ++n) {
-            m[n] = -__builtin_inff();
-            idx[n] = 0;
-        }
-
-        // finish doc j: merge the 4 row groups, mask, sum, write
-        auto finish_doc = [&]() {
-            float total = 0.f;
+        for (int pass = 0; pass < npass; ++pass) {
+            // ---- query fragments (B operand: col = token, k-quarter g) --------
+            i32x4 qf[NTQ][KS];
+            bool tok_ok[NTQ];
 #pragma unroll
             for (int n = 0; n < NTQ; ++n) {
-                float mv = m[n];
-                int iv = idx[n];
+                const int s = pass * 16 * NTQ + n * 16 + col;
+                tok_ok[n] = s < lq;
+                const unsigned char* qrow = (const unsigned char*)a.Q + (q0 + (tok_ok[n] ? s : 0)) * kRowBytes;
 #pragma unroll
-                for (int off = 16; off <= 32; off <<= 1) {
-                    const float om = shfl_xor_f(mv, off);
-                    const int oi = shfl_xor_i(iv, off);
-                    if constexpr (ARGMAX)
-                        argmax_merge(mv, iv, om, oi);
-                    else
-                        mv = mv > om ? mv : om;
+                for (int k = 0; k < KS; ++k) {
+                    i32x4 v = {0, 0, 0, 0};
+                    if (tok_ok[n]) v = *(const i32x4*)(qrow + (4 * k + g) * 16);
+                    qf[n][k] = v;
                 }
-                const bool fin = __builtin_isfinite(mv);
-                float c = (tok_ok[n] && fin) ? mv : 0.f;
+            }
+
+            // ---- doc cursor: cu_d cached one value per lane, read with readlane
+            int j = jb;
+            int cache_base = jb + 1;  // lane k holds cu_d[cache_base + k] - u0
+            int cu_cache = (int)((int64_t)a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd] - u0);
+            wait_vmcnt<0>();  // query fragments and the cache have landed
+            auto doc_end_of = [&](int jj) -> int {  // cu_d[jj + 1] - u0
+                int off = jj + 1 - cache_base;
+                if (off >= 64) {  // once per 64 docs
+                    cache_base = jj + 1;
+                    cu_cache = (int)((int64_t)a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd] - u0);
+                    wait_vmcnt<0>();  // keep the cache out of the tile ring's waits
+                    off = 0;
+                }
+                return uniform(__builtin_amdgcn_readlane(cu_cache, off));
+            };
+            int doc_start = 0;
+            int doc_end = doc_end_of(j);
+
+            float m[NTQ];
+            int idx[NTQ];
 #pragma unroll
-                for (int off = 8; off >= 1; off >>= 1) c += shfl_xor_f(c, off);
-                total += c;
-                if constexpr (ARGMAX) {
-                    if (g == 0 && tok_ok[n]) {
-                        const int64_t s = (int64_t)pass * 16 * NTQ + n * 16 + col;
-                        a.argmax[(i * a.Nd + j) * a.max_lq + s] = fin ? (int)(iv - doc_start) : 0;
-                    }
-                }
+            for (int n = 0; n < NTQ; ++n) {
                 m[n] = -__builtin_inff();
                 idx[n] = 0;
             }
-            if constexpr (ARGMAX) {
-                if (pass == 0) {  // rows past the query's length are 0
-                    for (int64_t s = lq + lane; s < a.max_lq; s += 64)
-                        a.argmax[(i * a.Nd + j) * a.max_lq + s] = 0;
-                }
-            }
-            if (lane == 0) {
-                float* out = a.scores + i * a.Nd + j;
-                *out = pass == 0 ? total : *out + total;
-            }
-        };
 
-        // fold rows [lo, hi) of the tile starting at token ts into the state
-        auto fold = [&](const f32x4 (&acc)[NTQ], int64_t ts, int64_t lo, int64_t hi) {
-            const int64_t rbase = ts + 4 * g;
-            if (lo <= ts && hi >= ts + 16) {
+            // finish doc j: merge the 4 row groups, drop padding lanes, sum, write
+            auto finish_doc = [&]() {
+                float total = 0.f;
 #pragma unroll
                 for (int n = 0; n < NTQ; ++n) {
+                    float mv = m[n];
+                    int iv = idx[n];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v = acc[n][r];
+                    for (int off = 16; off <= 32; off <<= 1) {
+                        const float om = shfl_xor_f(mv, off);
                         if constexpr (ARGMAX) {
-                            if (v > m[n]) {
-                                m[n] = v;
-                                idx[n] = (int)(rbase + r);
-                            }
+                            const int oi = shfl_xor_i(iv, off);
+                            argmax_merge(mv, iv, om, oi);
                         } else {
-                            m[n] = m[n] > v ? m[n] : v;
+                            mv = __builtin_fmaxf(mv, om);
+                        }
+                    }
+                    const bool fin = __builtin_isfinite(mv);
+                    total += row16_sum((tok_ok[n] && fin) ? mv : 0.f);
+                    if constexpr (ARGMAX) {
+                        if (g == 0 && tok_ok[n]) {
+                            const int s = pass * 16 * NTQ + n * 16 + col;
+                            arg_row[(int64_t)j * a.max_lq + s] = fin ? iv - doc_start : 0;
+                        }
+                    }
+                    m[n] = -__builtin_inff();
+                    idx[n] = 0;
+                }
+                if constexpr (ARGMAX) {
+                    if (pass == 0)  // rows past the query's length are 0
+                        for (int s = lq + lane; s < a.max_lq; s += 64) arg_row[(int64_t)j * a.max_lq + s] = 0;
+                }
+                if (lane == 0) score_row[j] = pass == 0 ? total : score_row[j] + total;
+            };
+
+            // fold tile rows [lo, hi) (tile-relative, uniform) into the state
+            auto fold = [&](const f32x4 (&acc)[NTQ], int tile0, int lo, int hi) {
+                if (lo == 0 && hi == 16) {
+#pragma unroll
+                    for (int n = 0; n < NTQ; ++n) {
+                        if constexpr (ARGMAX) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (acc[n][r] > m[n]) {
+                                    m[n] = acc[n][r];
+                                    idx[n] = tile0 + 4 * g + r;
+                                }
+                        } else {
+                            m[n] = __builtin_fmaxf(__builtin_fmaxf(m[n], acc[n][0]),
+                                                   __builtin_fmaxf(__builtin_fmaxf(acc[n][1], acc[n][2]), acc[n][3]));
+                        }
+                    }
+                } else {
+                    const uint32_t bits = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
+                    const uint32_t lb = bits >> (4 * g);
+#pragma unroll
+                    for (int n = 0; n < NTQ; ++n) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float v = ((lb >> r) & 1u) ? acc[n][r] : -__builtin_inff();
+                            if constexpr (ARGMAX) {
+                                if (v > m[n]) {
+                                    m[n] = v;
+                                    idx[n] = tile0 + 4 * g + r;
+                                }
+                            } else {
+                                m[n] = __builtin_fmaxf(m[n], v);
+                            }
                         }
                     }
                 }
-            } else {
-#pragma unroll
-                for (int n = 0; n < NTQ; ++n) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int64_t row = rbase + r;
-                        const float v = (row >= lo && row < hi) ? acc[n][r] : -__builtin_inff();
-                        if constexpr (ARGMAX) {
-                            if (v > m[n]) {
-                                m[n] = v;
-                                idx[n] = (int)row;
-                            }
-                        } else {
-                            m[n] = m[n] > v ? m[n] : v;
-                        }
-                    }
+            };
+
+            // leading empty docs
+            while (j < je && doc_end <= 0) {
+                finish_doc();
+                ++j;
+                if (j < je) {
+                    doc_start = doc_end;
+                    doc_end = doc_end_of(j);
                 }
             }
-        };
 
-        bool done = false;
-        // leading empty docs
-        while (!done && doc_end <= u0) {
-            finish_doc();
-            ++j;
-            if (j >= je) done = true;
-            else {
-                doc_start = doc_end;
-                doc_end = cu_next(j);
-            }
-        }
-
-        // ---- per-wave LDS ring of prefetched tiles ----------------------------
-        unsigned char* ring = &ring_lds[threadIdx.x >> 6][0][0];
-        auto issue_tile = [&](int64_t t, int stage) {
-            unsigned char* sb = ring + stage * kTileBytes;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {  // instruction k fills rows 4k .. 4k+3
-                const int row = 4 * k + (lane >> 4);
-                const int lc = (lane & 15) ^ row;  // logical chunk stored at slot lane & 15
-                int64_t grow = u0 + t * 16 + row;
-                if (grow >= u1) grow = u1 - 1;  // rows past the range are never folded
-                __builtin_amdgcn_global_load_lds((const void*)(Dbase + grow * RB + lc * 16),
-                                                 LDS_PTR(sb + k * 1024), 16, 0, kNonTemporal);
-            }
-        };
-        // A-operand read offsets: row = lane % 16, logical chunk 4k + g
-        uint32_t frag_off[KS];
-#pragma unroll
-        for (int k = 0; k < KS; ++k) frag_off[k] = col * RB + (((4 * k + g) ^ col) * 16);
-        const uint32_t ring_base = lds_addr(ring);
+            for (int q = 0; q < kStages; ++q)
+                if (q < ntile) issue_tile(q, q);
 
-        wait_vmcnt<0>();  // query fragments have landed before the pipeline starts
-#pragma unroll
-        for (int q = 0; q < kStages; ++q)
-            if (q < ntile) issue_tile(q, q);
+            int stage = 0;
+            for (int t = 0; t < ntile && j < je; ++t) {
+                const int behind = ntile - 1 - t;
+                wait_tiles_behind(behind < kStages - 1 ? behind : kStages - 1);
+                i32x4 af[KS];
+                const uint32_t sbase = ring_base + stage * kTileBytes;
+                lds_read4(af[0], af[1], af[2], af[3], sbase + frag_off[0], sbase + frag_off[1],
+                          sbase + frag_off[2], sbase + frag_off[3]);
+                if (t + kStages < ntile) issue_tile(t + kStages, stage);
+                stage = stage + 1 == kStages ? 0 : stage + 1;
 
-        int stage = 0;
-        for (int64_t t = 0; t < ntile && !done; ++t) {
-            {
-                const int64_t behind = ntile - 1 - t;
-                wait_tiles_behind(behind < kStages - 1 ? (int)behind : kStages - 1);
-            }
-            i32x4 af[KS];
-            const uint32_t sbase = ring_base + stage * kTileBytes;
-            lds_read4(af[0], af[1], af[2], af[3], sbase + frag_off[0], sbase + frag_off[1],
-                      sbase + frag_off[2], sbase + frag_off[3]);
-            if (t + kStages < ntile) issue_tile(t + kStages, stage);
-            stage = stage + 1 == kStages ? 0 : stage + 1;
-            {
                 f32x4 acc[NTQ];
 #pragma unroll
                 for (int n = 0; n < NTQ; ++n) {
@@ -285,37 +323,32 @@ __global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenA
                     for (int k = 0; k < KS; ++k) acc[n] = mfma16<E>(af[k], qf[n][k], acc[n]);
                 }
 
-                const int64_t ts = u0 + t * 16;
-                int64_t lo = ts;
+                const int tile0 = t * 16;
+                int lo = 0;
                 while (true) {
-                    const int64_t hi = doc_end < ts + 16 ? doc_end : ts + 16;
-                    if (hi > lo) fold(acc, ts, lo, hi);
-                    if (doc_end > ts + 16) break;
+                    const int hi = doc_end - tile0 < 16 ? doc_end - tile0 : 16;
+                    if (hi > lo) fold(acc, tile0, lo, hi);
+                    if (doc_end - tile0 > 16) break;  // the doc continues in the next tile
                     finish_doc();
                     ++j;
-                    if (j >= je) {
-                        done = true;
-                        break;
-                    }
-                    lo = doc_end;
+                    if (j >= je) break;
+                    lo = hi > lo ? hi : lo;
                     doc_start = doc_end;
-                    doc_end = cu_next(j);
+                    doc_end = doc_end_of(j);
                 }
             }
-        }
-        wait_vmcnt<0>();  // nothing of this unit's ring is still in flight
-        // docs left with no tokens after the last tile (only when ntile == 0)
-        while (!done) {
-            finish_doc();
-            ++j;
-            if (j >= je) done = true;
-            else {
-                doc_start = doc_end;
-                doc_end = cu_next(j);
+            // docs left with no tokens (only when the unit has no tiles)
+            while (j < je) {
+                finish_doc();
+                ++j;
+                if (j < je) {
+                    doc_start = doc_end;
+                    doc_end = doc_end_of(j);
+                }
             }
+            wait_vmcnt<0>();  // nothing of this pass is still in flight
         }
     }
-  }
 }
 
 template <int E, int NTQ>
