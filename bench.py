@@ -251,7 +251,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="",
                     help="run one workload: rerank|tiny|colpali|int8|backward|copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")

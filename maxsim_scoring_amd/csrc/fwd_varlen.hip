@@ -30,7 +30,7 @@ namespace maxsim {
 namespace {
 
 #ifndef MAXSIM_VARLEN_STAGES
-#define MAXSIM_VARLEN_STAGES 3
+#define MAXSIM_VARLEN_STAGES 2
 #endif
 constexpr int kStages = MAXSIM_VARLEN_STAGES;  // 4 KB tiles in flight per wave
 constexpr int kUnitsPerBlock = 4;
@@ -103,8 +103,15 @@ __device__ __forceinline__ float row16_sum(float v)
 
 }  // namespace
 
+// Three waves per SIMD (at most 168 VGPRs) with two ring stages measured
+// fastest (6.81 TB/s); two waves with four stages and four waves with two
+// stages were slower.
+#ifndef MAXSIM_VARLEN_WAVES_PER_EU
+#define MAXSIM_VARLEN_WAVES_PER_EU 3
+#endif
 template <int E, bool ARGMAX, int NTQ>
-__global__ __launch_bounds__(kUnitsPerBlock * 64) void fwd_varlen_kernel(VarlenArgs a)
+__global__ __launch_bounds__(kUnitsPerBlock * 64)
+__attribute__((amdgpu_waves_per_eu(MAXSIM_VARLEN_WAVES_PER_EU))) void fwd_varlen_kernel(VarlenArgs a)
 {
     constexpr int KS = kD / 32;  // 16x16x32: 4 K-steps
     static_assert(KS == 4, "one lds_read4 per tile");
