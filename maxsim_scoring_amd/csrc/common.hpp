@@ -147,6 +147,40 @@ __device__ __forceinline__ void block_barrier()
     lds_fence();
 }
 
+// One 16-byte-per-lane direct-to-LDS load: lane l reads base + voff[l] and
+// the wave's 1 KB lands at LDS byte address `lds` (+ 16 * lane). `base` and
+// `lds` must be wave-uniform. Written in assembly to use the scalar-base
+// addressing form (32-bit per-lane offsets) and to keep the compiler from
+// treating the load as an LDS write it must wait for before every later LDS
+// access; callers synchronise explicitly with wait_vmcnt. M0 is set here; no
+// compiler-generated code in these kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_lds16(const void* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+// the same with the non-temporal hint, for data that is streamed once
+__device__ __forceinline__ void dma_lds16_nt(const void* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -195,6 +229,84 @@ __device__ __forceinline__ void lds_read8(i32x4 (&a)[8], const uint32_t (&p)[8])
           "=&v"(a[6]), "=&v"(a[7])
         : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
         : "memory");
+}
+
+// The same reads without the wait, so that later work can overlap their
+// latency; lds_wait_regs() waits and ties the destination registers to the
+// wait so that no use of them can be scheduled before it.
+__device__ __forceinline__ void lds_read8_async(i32x4 (&a)[8], const uint32_t (&p)[8])
+{
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+          "=&v"(a[6]), "=&v"(a[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+        : "memory");
+}
+__device__ __forceinline__ void lds_read4_async(i32x4 (&a)[4], const uint32_t (&p)[4])
+{
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+}
+// As above with a compile-time byte offset added to every address (the
+// instruction's immediate offset field, so no address registers per offset).
+template <int OFF>
+__device__ __forceinline__ void lds_read8_async_off(i32x4 (&a)[8], const uint32_t (&p)[8])
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\t"
+        "ds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\t"
+        "ds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\t"
+        "ds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\t"
+        "ds_read_b128 %7, %15 offset:%16"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+          "=&v"(a[6]), "=&v"(a[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]),
+          "i"(OFF)
+        : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read4_async_off(i32x4 (&a)[4], const uint32_t (&p)[4])
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\t"
+        "ds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "i"(OFF)
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_wait_regs(i32x4 (&a)[8])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                   "+v"(a[6]), "+v"(a[7])
+                 :
+                 : "memory");
+}
+__device__ __forceinline__ void lds_wait_regs(i32x4 (&a)[4])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : : "memory");
 }
 
 __device__ __forceinline__ uint64_t lds_read_u64_uniform(const uint64_t* p)

@@ -7,13 +7,25 @@
 // finalise with finite(m) & q_active) and "Long-query chunking" (a query is
 // split into fixed chunks whose partial scores are summed in a fixed order).
 //
-// Work unit = one workgroup = (doc j, group of query N-tiles). The S tile is
-// computed transposed, S^T = D . Q^T: MFMA rows are doc tokens and columns are
-// query tokens, so every lane owns one query token and the max over doc
-// tokens stays inside the lane; only the two lane halves are merged, once per
-// doc. D is streamed HBM/L2 -> LDS with direct-to-LDS loads into a 3-stage
-// ring (prefetch distance 2), shared by every wave of the workgroup, so a doc
-// tile is read once per workgroup. Q stays in VGPRs for the whole doc.
+// Design. A workgroup of 8 waves is persistent over one block of query
+// N-tiles (32 query tokens each) and one contiguous range of docs. The query
+// block stays in VGPRs for the whole run (loaded once), and the docs of the
+// range stream through LDS as one flat sequence of 64-token tiles, crossing
+// doc boundaries without draining the pipeline: direct-to-LDS loads fill a
+// 3-stage ring two tiles ahead, and one barrier per tile hands a landed tile
+// to all 8 waves, so each doc tile is read once per workgroup. Workgroups
+// that share a doc range are placed on the same XCD, so the range is fetched
+// from HBM once per XCD and served from that XCD's L2 to the others.
+//
+// The S tile is computed transposed, S^T = D . Q^T: MFMA rows are doc tokens
+// and columns are query tokens, so every lane owns one query token and the
+// max over doc tokens stays inside the lane; the two lane halves are merged
+// once per doc. Per-tile validity of doc tokens comes from scalar loads of
+// d_mask; tiles with no valid token skip the MFMA work. Per-doc partial sums
+// of the N-tiles of a query meet in LDS and are added in slot order, so the
+// result does not depend on timing.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,63 +33,203 @@ namespace maxsim {
 
 namespace {
 
-constexpr int kTileRows = 64;  // doc tokens per pipeline stage (2 MFMA M-tiles)
+constexpr int kTileRows = 128;  // doc tokens per pipeline stage (4 MFMA M-tiles)
 constexpr int kStages = 3;
-constexpr int kMaxMaskTokens = 32768;  // d_mask bits kept in LDS per segment
+constexpr int kWaves = 8;
+constexpr int kMaskWords = 2048;  // 16 KB of LDS: d_mask bits of a doc range
 
-// Fold one 32x32 accumulator tile into the running (max, argmax) of each
-// N-tile. Lane rows are 8*(q/4) + 4*h + q%4; q ascends with the row, so a
-// strict '>' keeps the lowest index on ties. `lbits` bit r = row r + 4h valid.
-template <typename V, bool ARGMAX, int NTW, bool MASKED, typename Acc>
-__device__ __forceinline__ void update_rows(const Acc (&acc)[NTW], V (&m)[NTW], int (&idx)[NTW],
-                                            int base, uint32_t lbits)
+// 4-bit nonzero flags of the 4 bytes of x (byte b -> bit b)
+__device__ __forceinline__ uint32_t byte_flags(uint32_t x)
 {
+    x |= x >> 4;
+    x |= x >> 2;
+    x |= x >> 1;
+    x &= 0x01010101u;
+    return ((x * 0x01020408u) >> 24) & 0xFu;
+}
+
+// Validity bits of the 64 doc tokens starting at byte `p` of d_mask (bit r =
+// token r is valid), for `nb` (1..64) tokens that exist. Uses scalar loads of
+// the aligned dwords that hold those bytes only, so nothing past the last
+// valid byte's dword is read.
+__device__ __forceinline__ uint64_t mask_bits_scalar(const uint8_t* p, int nb)
+{
+    const uintptr_t a = (uintptr_t)p;
+    const int sh = (int)(a & 3u);
+    const __attribute__((address_space(4))) uint32_t* w =
+        (const __attribute__((address_space(4))) uint32_t*)(a - (uintptr_t)sh);
+    const int ndw = (sh + nb + 3) >> 2;  // dwords that hold a valid byte
+    uint64_t lo = 0, hi = 0;             // bits of bytes [a - sh, a - sh + 68)
+    if (nb == 64) {
+        // all 16 (+1 when unaligned) dwords hold a valid byte: one batch of loads
+        typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+        const u32x16 x = *(const __attribute__((address_space(4))) u32x16*)w;
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int r = 8 * (q >> 2) + (q & 3);
-            V v = acc[n][q];
-            if constexpr (MASKED) v = ((lbits >> r) & 1u) ? v : neg_inf<V>();
-            if constexpr (ARGMAX) {
-                if (v > m[n]) {
-                    m[n] = v;
-                    idx[n] = base + r;
-                }
-            } else {
-                m[n] = m[n] > v ? m[n] : v;
-            }
+        for (int k = 0; k < 16; ++k) lo |= (uint64_t)byte_flags(x[k]) << (4 * k);
+        if (sh) hi = byte_flags(w[16]);
+    } else {
+        for (int k = 0; k < ndw; ++k) {
+            const uint64_t f = byte_flags(w[k]);
+            if (k < 16) lo |= f << (4 * k);
+            else hi |= f;
         }
     }
+    uint64_t bits = sh ? ((lo >> sh) | (hi << (64 - sh))) : lo;
+    if (nb < 64) bits &= (1ull << nb) - 1ull;
+    return bits;
+}
+
+// Two 64-bit words at a uniform LDS address, read by every lane (broadcast)
+// and returned as scalars.
+__device__ __forceinline__ void lds_read_u64x2_uniform(uint32_t addr, uint64_t (&out)[2])
+{
+    i32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+    const uint32_t w0 = __builtin_amdgcn_readfirstlane(v[0]);
+    const uint32_t w1 = __builtin_amdgcn_readfirstlane(v[1]);
+    const uint32_t w2 = __builtin_amdgcn_readfirstlane(v[2]);
+    const uint32_t w3 = __builtin_amdgcn_readfirstlane(v[3]);
+    out[0] = ((uint64_t)w1 << 32) | w0;
+    out[1] = ((uint64_t)w3 << 32) | w2;
+}
+
+// LDS accesses made from inline assembly so that the compiler does not add
+// waits for the whole direct-to-LDS ring before them (see lds_read4).
+__device__ __forceinline__ void lds_store_b32(uint32_t addr, uint32_t v)
+{
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_load_b32(uint32_t addr)
+{
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+// Max without NaN handling: scores are finite or -inf here, and fmaxf would
+// make the compiler canonicalise every operand first (an extra op per value).
+template <typename V> __device__ __forceinline__ V vmax(V a, V b) { return a > b ? a : b; }
+template <> __device__ __forceinline__ float vmax<float>(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+template <typename V> __device__ __forceinline__ V vmax3(V a, V b, V c) { return vmax(vmax(a, b), c); }
+template <> __device__ __forceinline__ float vmax3<float>(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Running state of one N-tile for the lane's 16 rows of each M-tile.
+// Without argmax it is the running max only. With argmax the lane also keeps
+// the 16 values of the M-tile that last raised its max and that M-tile's row
+// base: a strict '>' across M-tiles (ascending t) keeps the earlier tile on
+// ties, and at the end of the doc the lowest row of the saved tile holding
+// the max is the argmax. This costs about 1.7 VALU ops per value instead of a
+// compare-and-select chain through every value.
+template <typename V, bool ARGMAX> struct RowState;
+template <typename V> struct RowState<V, false> {
+    V m;
+    __device__ __forceinline__ void reset() { m = neg_inf<V>(); }
+};
+template <typename V> struct RowState<V, true> {
+    V m;
+    int tbase;
+    V sv[16];
+    __device__ __forceinline__ void reset()
+    {
+        m = neg_inf<V>();
+        tbase = 0;
+    }
+};
+
+template <typename V, typename Acc, bool MASKED>
+__device__ __forceinline__ void masked_values(const Acc& acc, uint32_t lbits, V (&v)[16])
+{
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int r = 8 * (q >> 2) + (q & 3);  // lane row offset without the 4h term
+        v[q] = acc[q];
+        if constexpr (MASKED) v[q] = ((lbits >> r) & 1u) ? v[q] : neg_inf<V>();
+    }
+}
+
+template <typename V>
+__device__ __forceinline__ V max16(const V (&v)[16])
+{
+    const V a = vmax3(v[0], v[1], v[2]);
+    const V b = vmax3(v[3], v[4], v[5]);
+    const V c = vmax3(v[6], v[7], v[8]);
+    const V d = vmax3(v[9], v[10], v[11]);
+    const V e = vmax3(v[12], v[13], v[14]);
+    return vmax(vmax3(a, b, c), vmax3(d, e, v[15]));
+}
+
+// Fold one 32x32 accumulator tile (M-tile rows starting at `base`) into the
+// state of its N-tile. `lbits` bit r = lane row r (+4h) valid.
+template <typename V, bool ARGMAX, bool MASKED, typename Acc>
+__device__ __forceinline__ void fold_one(const Acc& acc, RowState<V, ARGMAX>& st, int base,
+                                         uint32_t lbits)
+{
+    V v[16];
+    masked_values<V, Acc, MASKED>(acc, lbits, v);
+    const V tm = max16(v);
+    if constexpr (ARGMAX) {
+        const bool upd = tm > st.m;
+        st.m = upd ? tm : st.m;
+        st.tbase = upd ? base : st.tbase;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) st.sv[q] = upd ? v[q] : st.sv[q];
+    } else {
+        st.m = vmax(st.m, tm);
+    }
+}
+
+// Lane-local argmax of the doc: lowest row of the saved tile equal to the max
+// (row offset without the 4h term), or 0 when nothing valid was seen.
+template <typename V>
+__device__ __forceinline__ int saved_argmax(const RowState<V, true>& st)
+{
+    int qs = 0;
+#pragma unroll
+    for (int q = 15; q >= 0; --q) qs = st.sv[q] == st.m ? q : qs;
+    return st.tbase + 8 * (qs >> 2) + (qs & 3);
 }
 
 }  // namespace
 
-template <int E, bool ARGMAX, int WAVES, int NTW>
-__global__ __launch_bounds__(WAVES * 64) void fwd_dense_kernel(DenseArgs a)
+// READAHEAD: read the next M-tile's A fragments while the current one
+// multiplies (32 more VGPRs for fp16/bf16; the argmax variants cannot afford
+// them within 256 VGPRs at two waves per SIMD and read synchronously).
+template <int E, bool ARGMAX, int NTW, bool READAHEAD>
+__global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 {
     using T = Traits<E>;
     using V = typename T::Scalar;
     using Acc = typename T::Acc;
     constexpr int RB = T::kRowBytes;
-    constexpr int NCH = RB / 16;                   // 16-byte chunks per row
+    constexpr int NCH = RB / 16;           // 16-byte chunks per row
     constexpr int KS = T::kKSteps;
-    constexpr int SLOTS = WAVES * NTW;             // N-tiles per workgroup
+    constexpr int SLOTS = kWaves * NTW;    // N-tiles per workgroup
     constexpr int STAGE_BYTES = kTileRows * RB;
     constexpr int CHUNKS = kTileRows * NCH;
-    constexpr int THREADS = WAVES * 64;
-    constexpr int LPS = CHUNKS / THREADS;          // direct-to-LDS loads per thread per stage
+    constexpr int THREADS = kWaves * 64;
+    constexpr int LPS = CHUNKS / THREADS;  // direct-to-LDS loads per thread per stage
     static_assert(CHUNKS % THREADS == 0, "stage must split evenly over the workgroup");
 
     __shared__ __attribute__((aligned(16))) unsigned char stage_buf[kStages * STAGE_BYTES];
-    __shared__ uint64_t mask_bits[kMaxMaskTokens / 64];
-    __shared__ V part[SLOTS];
+    __shared__ V part[2][SLOTS];
+    // d_mask of the whole doc range as bits, when it fits: 2 words per tile
+    __shared__ __attribute__((aligned(16))) uint64_t mask_lds[kMaskWords];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int h = lane >> 5;   // which K-half this lane feeds; which row-quad it owns
-    const int col = lane & 31; // MFMA column = query token within the N-tile
+    const int h = lane >> 5;    // which K-half this lane feeds; which row-quad it owns
+    const int col = lane & 31;  // MFMA column = query token within the N-tile
 
     // ---- work unit: XCD-aware order (workgroup b runs on XCD b % 8) --------
     const int nblk = gridDim.x;
@@ -85,227 +237,330 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_dense_kernel(DenseArgs a)
     const int xcd = b & 7, kth = b >> 3;
     const int full = nblk >> 3, rem = nblk & 7;
     const int unit = xcd * full + (xcd < rem ? xcd : rem) + kth;
-    const int64_t j = unit / a.nqg;
-    const int qg = unit % a.nqg;
+    const int qb = unit % a.nqb;
+    const int64_t r = unit / a.nqb;
+    const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
+    const int64_t d0 = r * Nd / a.nranges, d1 = (r + 1) * Nd / a.nranges;
+    if (d0 >= d1) return;  // uniform over the workgroup
 
-    const int64_t Lq = a.Lq, Ld = a.Ld, Nd = a.Nd;
-    const unsigned char* Dj = (const unsigned char*)a.D + j * Ld * RB;
-    const uint8_t* dmj = a.d_mask ? a.d_mask + j * Ld : nullptr;
+    const int ntd = Ld > 0 ? (int)((Ld + kTileRows - 1) / kTileRows) : 0;  // tiles per doc
+    const int64_t F = (d1 - d0) * ntd;                                     // tiles of the range
+    const uint32_t part_base = lds_addr(&part[0][0]);
 
-    V qsum = 0;  // running per-query sum across passes (multi-pass long queries)
+    // per-lane byte offsets: LDS slot p = (row p / NCH, chunk p % NCH) of a
+    // stage holds logical chunk swz(row, p % NCH) of that row
+    int dma_off[LPS], dma_row[LPS], dma_lc[LPS];
+#pragma unroll
+    for (int u = 0; u < LPS; ++u) {
+        const int p = (wave * LPS + u) * 64 + lane;
+        dma_row[u] = p / NCH;
+        dma_lc[u] = swz_chunk<RB>(dma_row[u], p % NCH);
+        dma_off[u] = dma_row[u] * RB + dma_lc[u] * 16;
+    }
+    // A-fragment offsets of M-tile 0 (row = lane % 32, logical chunk 2s + h);
+    // M-tile mt adds mt * 32 rows (the swizzle only depends on row % 16)
+    uint32_t frag_off[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) frag_off[s] = (uint32_t)(col * RB + swz_chunk<RB>(col, 2 * s + h) * 16);
+    const uint32_t ring_base = lds_addr(stage_buf);
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
+
+    // stage tile tt of doc `doc` into `stage`: uniform base pointer + 32-bit
+    // per-lane offsets (scalar-base addressing), no 64-bit per-lane math
+    auto issue = [&](int64_t doc, int tt, int stage) {
+        const int64_t t0 = (int64_t)tt * kTileRows;
+        const void* Dt = uniform_ptr((const unsigned char*)a.D + (doc * Ld + t0) * RB);
+        const int rows = Ld - t0 >= kTileRows ? kTileRows : (int)(Ld - t0);  // >= 1
+        const uint32_t lds0 = ring_base + (uint32_t)(stage * STAGE_BYTES + wave_u * LPS * 1024);
+        if (rows == kTileRows) {
+#pragma unroll
+            for (int u = 0; u < LPS; ++u) dma_lds16(Dt, (uint32_t)dma_off[u], lds0 + u * 1024);
+        } else {  // past the doc end: re-read its last row (masked out)
+#pragma unroll
+            for (int u = 0; u < LPS; ++u) {
+                const int row = dma_row[u] < rows ? dma_row[u] : rows - 1;
+                dma_lds16(Dt, (uint32_t)(row * RB + dma_lc[u] * 16), lds0 + u * 1024);
+            }
+        }
+    };
+
+    // ---- d_mask bits of the doc range into LDS (2 words per 128-token tile) --
+    const int wpd = 2 * ntd;  // mask words per doc
+    const bool mask_in_lds = a.d_mask && (d1 - d0) * (int64_t)wpd <= kMaskWords;
+    if (mask_in_lds) {
+        const int nwords = (int)((d1 - d0) * wpd);
+        for (int wd = wave; wd < nwords; wd += kWaves) {
+            const int64_t doc = d0 + wd / wpd;
+            const int64_t t = (int64_t)(wd % wpd) * 64 + lane;
+            const bool v = t < Ld && a.d_mask[doc * Ld + t] != 0;
+            const uint64_t bits = __ballot(v);
+            if (lane == 0) mask_lds[wd] = bits;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        block_barrier();
+    }
+    const uint32_t mask_base = lds_addr(mask_lds);
 
     for (int pass = 0; pass < a.npass; ++pass) {
         // ---- the N-tiles this wave owns in this pass ------------------------
-        int qi[NTW], nt_idx[NTW];
-        bool slot_ok[NTW];
+        int qi[NTW], ntl[NTW];
+        bool tok_ok[NTW];
+        bool keep_row[NTW];  // q_mask of this lane's query token
 #pragma unroll
         for (int n = 0; n < NTW; ++n) {
             const int slot = wave * NTW + n;
+            bool slot_ok;
             if (a.npass == 1) {
-                qi[n] = qg * a.qpw + slot / a.ntq;
-                nt_idx[n] = slot % a.ntq;
-                slot_ok[n] = slot < a.qpw * a.ntq && qi[n] < a.Nq;
+                qi[n] = qb * a.qpw + slot / a.ntq;
+                ntl[n] = slot % a.ntq;
+                slot_ok = slot < a.qpw * a.ntq && qi[n] < a.Nq;
             } else {
-                qi[n] = qg;
-                nt_idx[n] = pass * SLOTS + slot;
-                slot_ok[n] = nt_idx[n] < a.ntq;
+                qi[n] = qb;
+                ntl[n] = pass * SLOTS + slot;
+                slot_ok = ntl[n] < a.ntq;
             }
+            const int64_t s_tok = (int64_t)ntl[n] * 32 + col;
+            tok_ok[n] = slot_ok && s_tok < Lq;
+            keep_row[n] = tok_ok[n] && (!a.q_mask || a.q_mask[(int64_t)qi[n] * Lq + s_tok] != 0);
         }
 
-        // ---- Q fragments (B operand), kept in VGPRs for the whole doc -------
+        // ---- Q fragments (B operand), kept in VGPRs for the whole range -----
         i32x4 qf[NTW][KS];
 #pragma unroll
         for (int n = 0; n < NTW; ++n) {
-            const int64_t s_tok = (int64_t)nt_idx[n] * 32 + col;
-            const bool ok = slot_ok[n] && s_tok < Lq;
+            const int64_t s_tok = (int64_t)ntl[n] * 32 + col;
             const unsigned char* qrow =
-                (const unsigned char*)a.Q + ((int64_t)qi[n] * Lq + (ok ? s_tok : 0)) * RB;
+                (const unsigned char*)a.Q + ((int64_t)qi[n] * Lq + (tok_ok[n] ? s_tok : 0)) * RB;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 i32x4 v = {0, 0, 0, 0};
-                if (ok) v = *(const i32x4*)(qrow + (2 * s + h) * 16);
+                if (tok_ok[n]) v = *(const i32x4*)(qrow + (2 * s + h) * 16);
                 qf[n][s] = v;
             }
         }
+        wait_vmcnt<0>();  // Q and the q_mask bytes have landed before the pipeline
 
-        // Q must have landed before the pipeline starts: the compiler cannot
-        // count direct-to-LDS loads per stage and would otherwise wait for all
-        // of them inside the loop before the first use of qf.
-        wait_vmcnt<0>();
+        RowState<V, ARGMAX> st[NTW];
 
-        // ---- d_mask bits of this doc into LDS (first segment) ---------------
-        // Tokens are processed in segments of kMaxMaskTokens so the bitmask
-        // always fits LDS; typical docs have a single segment.
-        V m[NTW];
-        int idx[NTW];
+        // finish doc `doc` (ordinal `k` in the range): merge the lane halves,
+        // apply q_mask, write argmax, put per-N-tile sums into part[k & 1]
+        auto finish_doc = [&](int64_t doc, int64_t k) {
 #pragma unroll
-        for (int n = 0; n < NTW; ++n) {
-            m[n] = neg_inf<V>();
-            idx[n] = 0;
-        }
-
-        for (int64_t seg0 = 0; seg0 < Ld; seg0 += kMaxMaskTokens) {
-            const int64_t seg_len = Ld - seg0 < kMaxMaskTokens ? Ld - seg0 : kMaxMaskTokens;
-            if (dmj) {
-                block_barrier();  // previous users of mask_bits are done
-                const int nwords = (int)((seg_len + 63) >> 6);
-                for (int w = wave; w < nwords; w += WAVES) {
-                    const int64_t t = seg0 + (int64_t)w * 64 + lane;
-                    const bool v = t < Ld && dmj[t] != 0;
-                    const uint64_t bits = __ballot(v);
-                    if (lane == 0) mask_bits[w] = bits;
+            for (int n = 0; n < NTW; ++n) {
+                V mv = st[n].m;
+                int iv = 0;
+                if constexpr (ARGMAX) iv = saved_argmax(st[n]) + 4 * h;
+                const V om = __builtin_bit_cast(V, shfl_xor_i(__builtin_bit_cast(int, mv), 32));
+                if constexpr (ARGMAX) {
+                    const int oi = shfl_xor_i(iv, 32);
+                    argmax_merge(mv, iv, om, oi);
+                    if (!finite_score(mv)) iv = 0;
+                    if (h == 0 && tok_ok[n])
+                        a.argmax[((int64_t)qi[n] * Nd + doc) * Lq + (int64_t)ntl[n] * 32 + col] = iv;
+                } else {
+                    mv = mv > om ? mv : om;
                 }
-                __builtin_amdgcn_s_waitcnt(0);
-                block_barrier();
-            }
-            const int ntiles = (int)((seg_len + kTileRows - 1) / kTileRows);
-
-            // ---- direct-to-LDS staging of one 64-token tile ------------------
-            auto issue = [&](int tile, int stage) {
-                const int64_t t0 = seg0 + (int64_t)tile * kTileRows;
-                unsigned char* sb = stage_buf + stage * STAGE_BYTES;
+                V contrib = (keep_row[n] && finite_score(mv)) ? mv : (V)0;
+                // fixed-order butterfly over the 32 query tokens of the N-tile
 #pragma unroll
-                for (int u = 0; u < LPS; ++u) {
-                    const int p0 = (wave * LPS + u) * 64;  // first LDS chunk of this instruction
-                    const int p = p0 + lane;
-                    const int row = p / NCH;
-                    const int pc = p % NCH;
-                    const int lc = swz_chunk<RB>(row, pc);
-                    int64_t grow = t0 + row;
-                    if (grow >= Ld) grow = Ld - 1;  // clamped rows are masked out below
-                    const unsigned char* g = Dj + grow * RB + lc * 16;
-                    __builtin_amdgcn_global_load_lds((const void*)g, LDS_PTR(sb + p0 * 16), 16, 0, 0);
-                }
-            };
-
-            issue(0, 0);
-            if (ntiles > 1) issue(1, 1);
-
-            for (int it = 0; it < ntiles; ++it) {
-                if (it + 1 < ntiles) wait_vmcnt<LPS>();
-                else wait_vmcnt<0>();
-                block_barrier();
-                if (it + 2 < ntiles) issue(it + 2, (it + 2) % kStages);
-
-                // validity of the 64 rows of this tile
-                const int64_t t0 = seg0 + (int64_t)it * kTileRows;
-                const int64_t left = Ld - t0;
-                uint64_t vbits = left >= 64 ? ~0ull : ((1ull << left) - 1ull);
-                if (dmj) vbits &= lds_read_u64_uniform(&mask_bits[it]);
-                if (vbits == 0) continue;  // no valid token: nothing to reduce
-                const bool all_valid = vbits == ~0ull;
-                const unsigned char* sb = stage_buf + (it % kStages) * STAGE_BYTES;
-
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const uint32_t mbits = (uint32_t)(vbits >> (mt * 32));
-                    if (mbits == 0) continue;
-                    // A fragments: row = doc token (lane % 32), k-half = lane / 32
-                    i32x4 af[KS];
-                    const int row = mt * 32 + col;
-                    uint32_t ad[KS];
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        ad[s] = lds_addr(sb + row * RB + swz_chunk<RB>(row, 2 * s + h) * 16);
-                    if constexpr (KS == 8)
-                        lds_read8(af, ad);
+                for (int off = 16; off >= 1; off >>= 1) {
+                    if constexpr (E == kI8)
+                        contrib += shfl_xor_i(contrib, off);
                     else
-                        lds_read4(af[0], af[1], af[2], af[3], ad[0], ad[1], ad[2], ad[3]);
-                    Acc acc[NTW];
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) acc[n] = Acc{};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-#pragma unroll
-                        for (int n = 0; n < NTW; ++n) acc[n] = mfma32<E>(af[s], qf[n][s], acc[n]);
+                        contrib += shfl_xor_f(contrib, off);
+                }
+                if (lane == 0)
+                    lds_store_b32(part_base + (uint32_t)(((k & 1) * SLOTS + wave * NTW + n) * 4),
+                                  __builtin_bit_cast(uint32_t, contrib));
+            }
+        };
 
-                    // online max (+argmax) over this lane's 16 rows, ascending t;
-                    // masked rows become -inf before the max
-                    const int base = (int)(t0 + mt * 32);
-                    if (all_valid || mbits == 0xffffffffu) {
-                        update_rows<V, ARGMAX, NTW, false>(acc, m, idx, base, 0u);
-                    } else {
-                        update_rows<V, ARGMAX, NTW, true>(acc, m, idx, base, mbits >> (4 * h));
+        // add up part[k & 1] in slot order and write the scores of doc `doc`
+        auto write_scores = [&](int64_t doc, int64_t k) {
+            if (a.npass == 1) {
+                if (tid < a.qpw) {
+                    const int64_t i = (int64_t)qb * a.qpw + tid;
+                    if (i < a.Nq) {
+                        V sum = 0;
+                        for (int n = 0; n < a.ntq; ++n)
+                            sum += __builtin_bit_cast(V, lds_load_b32(
+                                part_base + (uint32_t)(((k & 1) * SLOTS + tid * a.ntq + n) * 4)));
+                        if constexpr (E == kI8) {
+                            if (a.scores_i32) a.scores_i32[i * Nd + doc] = sum;
+                            if (a.scores) a.scores[i * Nd + doc] = (float)(((double)sum * a.q_scale) * a.d_scale);
+                        } else {
+                            a.scores[i * Nd + doc] = sum;
+                        }
                     }
                 }
+            } else if (tid == 0) {
+                // one long query: this pass's N-tiles, in slot order, added to
+                // the running sum kept in the output (pass 0 starts it)
+                const int nslots = a.ntq - pass * SLOTS < SLOTS ? a.ntq - pass * SLOTS : SLOTS;
+                V sum = 0;
+                for (int n = 0; n < nslots; ++n)
+                    sum += __builtin_bit_cast(V, lds_load_b32(part_base + (uint32_t)(((k & 1) * SLOTS + n) * 4)));
+                const int64_t o = (int64_t)qb * Nd + doc;
+                const bool last = pass + 1 == a.npass;
+                if constexpr (E == kI8) {
+                    // the int32 running sum lives in scores_i32 when it exists,
+                    // else in the float output's bits until the last pass
+                    int32_t* run = a.scores_i32 ? a.scores_i32 : (int32_t*)a.scores;
+                    const V tot = (pass == 0 ? 0 : run[o]) + sum;
+                    if (a.scores_i32) a.scores_i32[o] = tot;
+                    if (last && a.scores) a.scores[o] = (float)(((double)tot * a.q_scale) * a.d_scale);
+                    else if (!a.scores_i32) run[o] = tot;
+                } else {
+                    a.scores[o] = (pass == 0 ? 0.f : a.scores[o]) + sum;
+                }
             }
-            // all waves must be done reading the ring before it is reused
-            block_barrier();
+        };
+
+        if (F == 0) {  // Ld == 0: every doc contributes 0 and keeps argmax 0
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) st[n].reset();
+            for (int64_t k = 0; k < d1 - d0; ++k) {
+                finish_doc(d0 + k, k);
+                block_barrier();
+                write_scores(d0 + k, k);
+                block_barrier();
+            }
+            continue;
         }
 
-        // ---- finalise: merge lane halves, q_mask, row sums --------------------
-#pragma unroll
-        for (int n = 0; n < NTW; ++n) {
-            V mv = m[n];
-            int iv = idx[n] + 4 * h;
-            if constexpr (ARGMAX) {
-                const V om = __builtin_bit_cast(V, shfl_xor_i(__builtin_bit_cast(int, mv), 32));
-                const int oi = shfl_xor_i(iv, 32);
-                argmax_merge(mv, iv, om, oi);
-                if (!finite_score(mv)) iv = 0;
+        // issue cursor (doc ordinal ik, tile it) runs two tiles ahead of the
+        // compute cursor (k, tt); both advance one tile per iteration
+        int64_t ik = 0;
+        int it = 0;
+        auto advance = [&](int64_t& kk, int& t) {
+            if (++t == ntd) {
+                t = 0;
+                ++kk;
+            }
+        };
+        issue(d0 + ik, it, 0);
+        advance(ik, it);
+        if (F > 1) {
+            issue(d0 + ik, it, 1);
+            advance(ik, it);
+        }
+
+        int stage = 0;
+        int64_t k = 0;  // doc ordinal in the range
+        int tt = 0;     // tile within the doc
+        for (int64_t f = 0; f < F; ++f, advance(k, tt)) {
+            const int64_t doc = d0 + k;
+            const int64_t t0 = (int64_t)tt * kTileRows;
+
+            // validity of the tile's rows; the scalar loads run before the
+            // wait below so that their latency hides behind it
+            uint64_t vb[2];
+            if (mask_in_lds) {
+                lds_read_u64x2_uniform(mask_base + (uint32_t)((k * wpd + 2 * tt) * 8), vb);
             } else {
-                const V om = __builtin_bit_cast(V, shfl_xor_i(__builtin_bit_cast(int, mv), 32));
-                mv = mv > om ? mv : om;
-            }
-            const int64_t s_tok = (int64_t)nt_idx[n] * 32 + col;
-            const bool tok_ok = slot_ok[n] && s_tok < Lq;
-            bool keep = tok_ok && finite_score(mv);
-            if (keep && a.q_mask) keep = a.q_mask[(int64_t)qi[n] * Lq + s_tok] != 0;
-            V contrib = keep ? mv : (V)0;
-            if constexpr (ARGMAX) {
-                if (h == 0 && tok_ok)
-                    a.argmax[((int64_t)qi[n] * Nd + j) * Lq + s_tok] = iv;
-            }
-            // fixed-order butterfly over the 32 query tokens of the N-tile
 #pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) {
-                if constexpr (E == kI8)
-                    contrib += shfl_xor_i(contrib, off);
-                else
-                    contrib += shfl_xor_f(contrib, off);
-            }
-            if (lane == 0) part[wave * NTW + n] = contrib;
-        }
-        block_barrier();
-        if (a.npass == 1) {
-            if (tid < a.qpw) {
-                const int64_t i = (int64_t)qg * a.qpw + tid;
-                if (i < a.Nq) {
-                    V sum = 0;
-                    for (int n = 0; n < a.ntq; ++n) sum += part[tid * a.ntq + n];
-                    if constexpr (E == kI8) {
-                        if (a.scores_i32) a.scores_i32[i * Nd + j] = sum;
-                        if (a.scores) a.scores[i * Nd + j] = (float)(((double)sum * a.q_scale) * a.d_scale);
-                    } else {
-                        a.scores[i * Nd + j] = sum;
-                    }
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int64_t left = Ld - t0 - 64 * hh;
+                    const int nb = left >= 64 ? 64 : (left > 0 ? (int)left : 0);
+                    if (nb == 0) vb[hh] = 0;
+                    else if (a.d_mask) vb[hh] = mask_bits_scalar(a.d_mask + doc * Ld + t0 + 64 * hh, nb);
+                    else vb[hh] = nb >= 64 ? ~0ull : ((1ull << nb) - 1ull);
                 }
             }
-        } else if (tid == 0) {
-            const int nslots = a.ntq - pass * SLOTS < SLOTS ? a.ntq - pass * SLOTS : SLOTS;
-            for (int n = 0; n < nslots; ++n) qsum += part[n];
+
+            if (f + 1 < F) wait_vmcnt<LPS>();
+            else wait_vmcnt<0>();
+            block_barrier();  // tile f landed for everyone; stage (f+2)%3 is free
+            if (f + 2 < F) {
+                issue(d0 + ik, it, stage == 0 ? 2 : stage - 1);
+                advance(ik, it);
+            }
+
+            if (tt == 0) {
+                if (k > 0) write_scores(doc - 1, k - 1);  // its part[] is complete
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) st[n].reset();
+            }
+
+            if ((vb[0] | vb[1]) != 0) {
+                const uint32_t sbase = ring_base + (uint32_t)(stage * STAGE_BYTES);
+                // A fragments: row = doc token (lane % 32), k-half = lane / 32;
+                // M-tile mt sits mt * 32 rows further (immediate offset)
+                uint32_t ad[KS];
+#pragma unroll
+                for (int s = 0; s < KS; ++s) ad[s] = sbase + frag_off[s];
+                auto read_async = [&](auto mtc, i32x4 (&af)[KS]) {
+                    constexpr int OFF = decltype(mtc)::value * 32 * RB;
+                    if constexpr (KS == 8) lds_read8_async_off<OFF>(af, ad);
+                    else lds_read4_async_off<OFF>(af, ad);
+                };
+                // one N-tile at a time: a single accumulator tile is live, and
+                // the fold of N-tile n overlaps the MFMAs of N-tile n+1
+                auto do_mtile = [&](int mt, const i32x4 (&af)[KS]) {
+                    const uint32_t mbits = (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
+                    if (mbits == 0) return;
+                    const int base = (int)(t0 + mt * 32);
+#pragma unroll
+                    for (int n = 0; n < NTW; ++n) {
+                        Acc acc = Acc{};
+#pragma unroll
+                        for (int s = 0; s < KS; ++s) acc = mfma32<E>(af[s], qf[n][s], acc);
+                        if (mbits == 0xffffffffu)
+                            fold_one<V, ARGMAX, false>(acc, st[n], base, 0u);
+                        else
+                            fold_one<V, ARGMAX, true>(acc, st[n], base, mbits >> (4 * h));
+                    }
+                };
+                using M0 = std::integral_constant<int, 0>;
+                using M1 = std::integral_constant<int, 1>;
+                using M2 = std::integral_constant<int, 2>;
+                using M3 = std::integral_constant<int, 3>;
+                if constexpr (READAHEAD) {
+                    i32x4 afA[KS], afB[KS];
+                    read_async(M0{}, afA);
+                    lds_wait_regs(afA);
+                    read_async(M1{}, afB);
+                    do_mtile(0, afA);
+                    lds_wait_regs(afB);
+                    read_async(M2{}, afA);
+                    do_mtile(1, afB);
+                    lds_wait_regs(afA);
+                    read_async(M3{}, afB);
+                    do_mtile(2, afA);
+                    lds_wait_regs(afB);
+                    do_mtile(3, afB);
+                } else {
+                    auto one = [&](auto mtc) {
+                        constexpr int mt = decltype(mtc)::value;
+                        if ((uint32_t)(vb[mt >> 1] >> (32 * (mt & 1))) == 0) return;
+                        i32x4 af[KS];
+                        read_async(mtc, af);
+                        lds_wait_regs(af);
+                        do_mtile(mt, af);
+                    };
+                    one(M0{});
+                    one(M1{});
+                    one(M2{});
+                    one(M3{});
+                }
+            }
+            if (tt == ntd - 1) finish_doc(doc, k);
+            stage = stage == 2 ? 0 : stage + 1;
         }
         block_barrier();
-    }
-
-    if (a.npass > 1 && tid == 0) {
-        const int64_t i = qg;
-        if constexpr (E == kI8) {
-            if (a.scores_i32) a.scores_i32[i * Nd + j] = qsum;
-            if (a.scores) a.scores[i * Nd + j] = (float)(((double)qsum * a.q_scale) * a.d_scale);
-        } else {
-            a.scores[i * Nd + j] = qsum;
-        }
+        write_scores(d1 - 1, d1 - 1 - d0);
+        block_barrier();  // part[] and the ring are free for the next pass
     }
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
-template <int E, int WAVES, int NTW>
-static hipError_t launch_dense_t(DenseArgs a, bool want_argmax, hipStream_t stream)
+template <int E, bool ARGMAX, int NTW, bool READAHEAD>
+static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
 {
-    constexpr int SLOTS = WAVES * NTW;
+    constexpr int SLOTS = kWaves * NTW;
     a.ntq = (int)((a.Lq + 31) / 32);
     if (a.ntq == 0) a.ntq = 1;
     if (a.ntq <= SLOTS) {
@@ -315,23 +570,40 @@ static hipError_t launch_dense_t(DenseArgs a, bool want_argmax, hipStream_t stre
         a.qpw = 1;
         a.npass = (a.ntq + SLOTS - 1) / SLOTS;
     }
-    a.nqg = (int)((a.Nq + a.qpw - 1) / a.qpw);
-    const int64_t units = (int64_t)a.nqg * a.Nd;
+    a.nqb = (int)((a.Nq + a.qpw - 1) / a.qpw);
+    static int ncu = 0;
+    if (ncu == 0) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (ncu <= 0) ncu = 256;
+    }
+    // doc ranges: enough workgroups to give every CU one, each range at least one doc
+    int64_t R = (ncu + a.nqb - 1) / a.nqb;
+    if (R > a.Nd) R = a.Nd;
+    if (R < 1) R = 1;
+    a.nranges = (int)R;
+    const int64_t units = (int64_t)a.nqb * R;
     if (units <= 0) return hipSuccess;
-    dim3 grid((unsigned)units), block(WAVES * 64);
-    if (want_argmax)
-        hipLaunchKernelGGL((fwd_dense_kernel<E, true, WAVES, NTW>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((fwd_dense_kernel<E, false, WAVES, NTW>), grid, block, 0, stream, a);
+    dim3 grid((unsigned)units), block(kWaves * 64);
+    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, READAHEAD>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t stream)
 {
     switch (elem) {
-    case kF16: return launch_dense_t<kF16, 4, 2>(a, want_argmax, stream);
-    case kBF16: return launch_dense_t<kBF16, 4, 2>(a, want_argmax, stream);
-    case kI8: return launch_dense_t<kI8, 8, 4>(a, want_argmax, stream);
+    case kF16:
+        return want_argmax ? launch_dense_t<kF16, true, 1, false>(a, stream)
+                           : launch_dense_t<kF16, false, 2, true>(a, stream);
+    case kBF16:
+        return want_argmax ? launch_dense_t<kBF16, true, 1, false>(a, stream)
+                           : launch_dense_t<kBF16, false, 2, true>(a, stream);
+    case kI8:
+        // a 1024-token int8 query fits one workgroup (8 waves x 4 N-tiles);
+        // with argmax the saved values only fit for 2 N-tiles per wave
+        return want_argmax ? launch_dense_t<kI8, true, 2, false>(a, stream)
+                           : launch_dense_t<kI8, false, 4, true>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -17,10 +17,11 @@ struct DenseArgs {
     double q_scale, d_scale;  // int8 only
     int64_t Nq, Nd, Lq, Ld;
     // filled by the launcher
-    int ntq;    // 32-token N-tiles per query
-    int qpw;    // whole queries per workgroup (single pass)
-    int npass;  // passes over a doc when one query has more N-tiles than a workgroup holds
-    int nqg;    // query groups
+    int ntq;      // 32-token N-tiles per query
+    int qpw;      // whole queries per workgroup (single pass)
+    int npass;    // passes over the docs when one query has more N-tiles than a workgroup holds
+    int nqb;      // query blocks
+    int nranges;  // doc ranges; workgroup = (query block, doc range)
 };
 
 struct VarlenArgs {
