@@ -20,8 +20,9 @@
  *   - All checks that need no device data run on the host BEFORE anything is
  *     enqueued; on failure the call returns a non-zero status and enqueues
  *     nothing. Device-data contents (mask bytes in {0,1}, monotone offsets,
- *     argmax in [0, Ld), int8 values != -128) are preconditions: breaking them
- *     gives unspecified values, never an out-of-bounds access.
+ *     argmax in [0, Ld), int8 values != -128, finite float inputs: no NaN or
+ *     Inf in Q, D or grad_scores) are preconditions: breaking them gives
+ *     unspecified values, never an out-of-bounds access.
  *   - Sizes of 0 are valid. Nq == 0 or Nd == 0 enqueues nothing.
  *   - Reductions run in a fixed order with no atomics: results are bitwise
  *     reproducible run to run.

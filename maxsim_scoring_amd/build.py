@@ -23,6 +23,10 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed fp32 VALU ops stay off in every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code: scores are finite or -inf, never NaN; with NaNs not honoured
+    # and IEEE mode off, a float max is a single v_max_f32/v_max3_f32 with no
+    # canonicalisation of its operands
+    "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
     "-I", os.path.join(ROOT, "include"),
 ]
 

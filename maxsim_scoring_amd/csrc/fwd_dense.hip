@@ -106,22 +106,14 @@ __device__ __forceinline__ uint32_t lds_load_b32(uint32_t addr)
     return v;
 }
 
-// Max without NaN handling: scores are finite or -inf here, and fmaxf would
-// make the compiler canonicalise every operand first (an extra op per value).
+// Max of scores that are finite or -inf. The kernels are built with IEEE mode
+// off and NaNs not honoured, so this is one v_max_f32 (three operands fold to
+// v_max3_f32) with no canonicalisation of the operands; being plain code, the
+// compiler also keeps the wait states between an MFMA and the first read of
+// its result, which it does not do for inline assembly.
 template <typename V> __device__ __forceinline__ V vmax(V a, V b) { return a > b ? a : b; }
-template <> __device__ __forceinline__ float vmax<float>(float a, float b)
-{
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
+template <> __device__ __forceinline__ float vmax<float>(float a, float b) { return __builtin_fmaxf(a, b); }
 template <typename V> __device__ __forceinline__ V vmax3(V a, V b, V c) { return vmax(vmax(a, b), c); }
-template <> __device__ __forceinline__ float vmax3<float>(float a, float b, float c)
-{
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
 
 // Running state of one N-tile for the lane's 16 rows of each M-tile.
 // Without argmax it is the running max only. With argmax the lane also keeps
@@ -496,17 +488,19 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     else lds_read4_async_off<OFF>(af, ad);
                 };
                 // one N-tile at a time: a single accumulator tile is live, and
-                // the fold of N-tile n overlaps the MFMAs of N-tile n+1
-                auto do_mtile = [&](int mt, const i32x4 (&af)[KS]) {
-                    const uint32_t mbits = (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
-                    if (mbits == 0) return;
+                // the fold of N-tile n overlaps the MFMAs of N-tile n+1.
+                // FULL: every row of the tile is valid (no mask work at all).
+                auto do_mtile = [&](auto fullc, int mt, const i32x4 (&af)[KS]) {
+                    constexpr bool FULL = decltype(fullc)::value;
+                    const uint32_t mbits = FULL ? 0xffffffffu : (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
+                    if (!FULL && mbits == 0) return;
                     const int base = (int)(t0 + mt * 32);
 #pragma unroll
                     for (int n = 0; n < NTW; ++n) {
                         Acc acc = Acc{};
 #pragma unroll
                         for (int s = 0; s < KS; ++s) acc = mfma32<E>(af[s], qf[n][s], acc);
-                        if (mbits == 0xffffffffu)
+                        if (FULL || mbits == 0xffffffffu)
                             fold_one<V, ARGMAX, false>(acc, st[n], base, 0u);
                         else
                             fold_one<V, ARGMAX, true>(acc, st[n], base, mbits >> (4 * h));
@@ -516,34 +510,41 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 using M1 = std::integral_constant<int, 1>;
                 using M2 = std::integral_constant<int, 2>;
                 using M3 = std::integral_constant<int, 3>;
-                if constexpr (READAHEAD) {
-                    i32x4 afA[KS], afB[KS];
-                    read_async(M0{}, afA);
-                    lds_wait_regs(afA);
-                    read_async(M1{}, afB);
-                    do_mtile(0, afA);
-                    lds_wait_regs(afB);
-                    read_async(M2{}, afA);
-                    do_mtile(1, afB);
-                    lds_wait_regs(afA);
-                    read_async(M3{}, afB);
-                    do_mtile(2, afA);
-                    lds_wait_regs(afB);
-                    do_mtile(3, afB);
-                } else {
-                    auto one = [&](auto mtc) {
-                        constexpr int mt = decltype(mtc)::value;
-                        if ((uint32_t)(vb[mt >> 1] >> (32 * (mt & 1))) == 0) return;
-                        i32x4 af[KS];
-                        read_async(mtc, af);
-                        lds_wait_regs(af);
-                        do_mtile(mt, af);
-                    };
-                    one(M0{});
-                    one(M1{});
-                    one(M2{});
-                    one(M3{});
-                }
+                auto run_tile = [&](auto fullc) {
+                    constexpr bool FULL = decltype(fullc)::value;
+                    if constexpr (READAHEAD) {
+                        i32x4 afA[KS], afB[KS];
+                        read_async(M0{}, afA);
+                        lds_wait_regs(afA);
+                        read_async(M1{}, afB);
+                        do_mtile(fullc, 0, afA);
+                        lds_wait_regs(afB);
+                        read_async(M2{}, afA);
+                        do_mtile(fullc, 1, afB);
+                        lds_wait_regs(afA);
+                        read_async(M3{}, afB);
+                        do_mtile(fullc, 2, afA);
+                        lds_wait_regs(afB);
+                        do_mtile(fullc, 3, afB);
+                    } else {
+                        auto one = [&](auto mtc) {
+                            constexpr int mt = decltype(mtc)::value;
+                            if (!FULL && (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1))) == 0) return;
+                            i32x4 af[KS];
+                            read_async(mtc, af);
+                            lds_wait_regs(af);
+                            do_mtile(fullc, mt, af);
+                        };
+                        one(M0{});
+                        one(M1{});
+                        one(M2{});
+                        one(M3{});
+                    }
+                };
+                if ((vb[0] & vb[1]) == ~0ull)
+                    run_tile(std::true_type{});
+                else
+                    run_tile(std::false_type{});
             }
             if (tt == ntd - 1) finish_doc(doc, k);
             stage = stage == 2 ? 0 : stage + 1;
@@ -601,8 +602,8 @@ hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t
                            : launch_dense_t<kBF16, false, 2, true>(a, stream);
     case kI8:
         // a 1024-token int8 query fits one workgroup (8 waves x 4 N-tiles);
-        // with argmax the saved values only fit for 2 N-tiles per wave
-        return want_argmax ? launch_dense_t<kI8, true, 2, false>(a, stream)
+        // with argmax the saved values only fit for 1 N-tile per wave
+        return want_argmax ? launch_dense_t<kI8, true, 1, false>(a, stream)
                            : launch_dense_t<kI8, false, 4, true>(a, stream);
     default: return hipErrorInvalidValue;
     }
