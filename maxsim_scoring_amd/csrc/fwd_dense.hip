@@ -10,7 +10,7 @@
 // Design. A workgroup of 8 waves is persistent over one block of query
 // N-tiles (32 query tokens each) and one contiguous range of docs. The query
 // block stays in VGPRs for the whole run (loaded once), and the docs of the
-// range stream through LDS as one flat sequence of 64-token tiles, crossing
+// range stream through LDS as one flat sequence of 128-token tiles, crossing
 // doc boundaries without draining the pipeline: direct-to-LDS loads fill a
 // 3-stage ring two tiles ahead, and one barrier per tile hands a landed tile
 // to all 8 waves, so each doc tile is read once per workgroup. Workgroups
@@ -20,10 +20,12 @@
 // The S tile is computed transposed, S^T = D . Q^T: MFMA rows are doc tokens
 // and columns are query tokens, so every lane owns one query token and the
 // max over doc tokens stays inside the lane; the two lane halves are merged
-// once per doc. Per-tile validity of doc tokens comes from scalar loads of
-// d_mask; tiles with no valid token skip the MFMA work. Per-doc partial sums
-// of the N-tiles of a query meet in LDS and are added in slot order, so the
-// result does not depend on timing.
+// once per doc. The d_mask of a range becomes 128 validity bits per tile,
+// built into LDS once (scalar loads per tile when it does not fit): tiles
+// whose rows are all valid take a path with no mask work, M-tiles with no
+// valid row skip their MFMAs. Per-doc partial sums of the N-tiles of a query
+// meet in LDS and are added in slot order, so the result does not depend on
+// timing.
 #include <type_traits>
 
 #include "common.hpp"
