@@ -14,6 +14,9 @@
  *     allocates no device memory and keeps no per-call state.
  *   - Every tensor is C-contiguous, row-major, with the embedding dimension d
  *     innermost. d must be 128 (other values return MAXSIM_ERR_UNSUPPORTED).
+ *   - Q, D, dQ and dD must be 16-byte aligned (any hipMalloc or torch
+ *     allocation is); every other array needs the alignment of its element
+ *     type. A misaligned pointer returns MAXSIM_ERR_UNSUPPORTED.
  *   - Calls are asynchronous on `stream` (NULL = the null stream). Outputs are
  *     valid after the stream is synchronised; inputs must stay unchanged until
  *     then. Outputs must not alias inputs or each other.
@@ -46,7 +49,7 @@ typedef enum {
     MAXSIM_OK = 0,
     MAXSIM_ERR_NULL = 1,        /* a required pointer is NULL */
     MAXSIM_ERR_SHAPE = 2,       /* a negative size or inconsistent sizes */
-    MAXSIM_ERR_UNSUPPORTED = 3, /* d != 128 or an unknown dtype */
+    MAXSIM_ERR_UNSUPPORTED = 3, /* d != 128, an unknown dtype, a misaligned pointer */
     MAXSIM_ERR_OVERFLOW = 4,    /* an index or an int32 sum could overflow */
     MAXSIM_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
 } maxsim_status_t;
@@ -123,11 +126,12 @@ maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, f
  *   dQ [Nq, Lq, d], dD [Nd, Ld, d] float32, fully overwritten
  *   csr_row_ptr [Nd*Ld + 1] int32, csr_col_idx [Nq*Nd*Lq] int32: outputs,
  *     the inverse map (row r = j*Ld + t lists the flat sources
- *     (i*Nd + j)*Lq + s that picked it, ascending). They are also the only
- *     scratch the backward needs.
+ *     (i*Nd + j)*Lq + s that picked it, ascending). The backward uses no
+ *     other memory: per-doc flags are kept in dD until dD is written.
  * Sums run in fp32 in a fixed order: dQ over j ascending, dD over the CSR row.
  * Errors: NULL, SHAPE (negative sizes; Ld == 0 with Nq*Nd*Lq > 0),
- * UNSUPPORTED, OVERFLOW when Nq*Nd*Lq >= 2^31 or Nd*Ld + 1 >= 2^31.
+ * UNSUPPORTED (also misaligned pointers), OVERFLOW when Nq*Nd*Lq >= 2^31 or
+ * Nd*Ld + 1 >= 2^31.
  */
 maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
                            int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,

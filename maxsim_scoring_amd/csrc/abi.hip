@@ -2,12 +2,27 @@
 // anything is enqueued), then one launcher per entry point.
 #include "maxsim.h"
 
+#include <atomic>
 #include <climits>
 
 #include "common.hpp"
 #include "kernels.hpp"
 
 using namespace maxsim;
+
+int maxsim::device_cu_count()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int n = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 namespace {
 
@@ -27,6 +42,10 @@ int64_t mul_sat(int64_t a, int64_t b)
     return a * b;
 }
 
+// Row tensors are read and written 16 bytes at a time; every other array
+// needs its natural alignment. NULL passes (it is checked separately).
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -41,6 +60,8 @@ maxsim_status_t maxsim_fwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
     if (Nq == 0 || Nd == 0) return MAXSIM_OK;
     if (!scores) return MAXSIM_ERR_NULL;
     if ((Lq > 0 && !Q) || (Ld > 0 && !D)) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(scores, 4) || !aligned(argmax, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
     const int64_t pairs = mul_sat(Nq, Nd);
     if (pairs < 0 || pairs > kI32Max) return MAXSIM_ERR_OVERFLOW;  // one workgroup per pair group
     if (argmax) {
@@ -72,6 +93,9 @@ maxsim_status_t maxsim_fwd_varlen(maxsim_dtype_t dtype, const void* Q, const int
     // Q or D may be NULL only when that packed tensor holds no tokens (an
     // empty torch tensor has no storage); the kernels then never read it.
     if (!cu_q || !cu_d || !scores) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(cu_q, 4) || !aligned(cu_d, 4) ||
+        !aligned(scores, 4) || !aligned(argmax, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
     if (Nd > kI32Max - 1) return MAXSIM_ERR_OVERFLOW;
     const int64_t pairs = mul_sat(Nq, Nd);
     if (pairs < 0 || pairs > kI32Max) return MAXSIM_ERR_OVERFLOW;
@@ -102,6 +126,9 @@ maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, f
     if (Nq == 0 || Nd == 0) return MAXSIM_OK;
     if (!scores_i32 && !scores) return MAXSIM_ERR_NULL;
     if ((Lq > 0 && !Q) || (Ld > 0 && !D)) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(scores_i32, 4) || !aligned(scores, 4) ||
+        !aligned(argmax, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
     // worst case |sum| = Lq * d * 127^2 must stay inside int32
     const int64_t worst = mul_sat(mul_sat(Lq, d), 127 * 127);
     if (worst < 0 || worst > kI32Max) return MAXSIM_ERR_OVERFLOW;
@@ -146,6 +173,10 @@ maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
     if (nsrc > 0 && (!Q || !D || !argmax || !grad_scores || !csr_col_idx)) return MAXSIM_ERR_NULL;
     if (Nq * Lq > 0 && !dQ) return MAXSIM_ERR_NULL;
     if (nrows > 0 && !dD) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(dQ, 16) || !aligned(dD, 16) ||
+        !aligned(argmax, 4) || !aligned(grad_scores, 4) || !aligned(csr_row_ptr, 4) ||
+        !aligned(csr_col_idx, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
     if (Nq * Lq == 0 && nrows == 0 && Nd == 0) return MAXSIM_OK;
     BwdArgs a{};
     a.Q = Q;

@@ -8,17 +8,24 @@
 // (the q_mask factor, grad_Q as a row-owned gather over docs).
 //
 // Launch sequence on one stream:
-//   live    one wave per doc: live(j) = any(d_mask[j,:]) parked in col_idx[0..Nd)
-//           (col_idx is caller-owned and is only filled by the CSR pass later);
-//   dq      one wave per query row (i,s): sum over j ascending of
-//           g[i,j] * live(j) * D[j, argmax[i,j,s]], times q_mask[i,s];
-//   csr     one workgroup per doc: the doc's Nq*Lq sources go into Ld bins.
-//           Every doc receives exactly Nq*Lq sources, so its CSR segment starts
-//           at j*Nq*Lq and no global scan is needed. Counting and the stable
-//           scatter use wave-level key matching (ballots over the key bits):
-//           a bin is only ever updated by one lane at a time, in source order;
-//   dd      one wave per destination row (j,t): walk the row's sources in CSR
-//           order, fp32 accumulation, one write.
+//   csr     one workgroup of 16 waves per doc. live(j) = any(d_mask[j,:]) is
+//           parked in dD[j, 0, 0] for the dq pass (dD is written last). Every
+//           doc receives exactly Nq*Lq sources, so its CSR segment starts at
+//           j*Nq*Lq and no global scan is needed. Each wave holds the
+//           destinations of a contiguous block of the doc's sources in
+//           registers, counts them into its own LDS histogram; the counts are
+//           scanned, and every wave scatters its block in source order (ranks
+//           inside a wave from ballots over the key bits), so each CSR row
+//           lists its sources ascending;
+//   dq      one 16-lane group per query row (i,s), 16 rows per workgroup: the
+//           argmax entries and weights of 64 docs at a time are staged in
+//           LDS, then each group gathers D[j, argmax[i,j,s]] for j ascending
+//           (16 bytes per lane, 8 loads in flight) and accumulates in fp32.
+//           All workgroups sweep j in the same order, so the D rows they
+//           gather are shared in L2;
+//   dd      one 16-lane group per destination row (j,t): the group walks the
+//           row's sources in CSR order, gathers Q rows (16 bytes per lane)
+//           and accumulates in fp32; every row is written once.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,37 +33,54 @@ namespace maxsim {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kCsrBins = 2048;  // destination bins handled per round of the CSR pass
+constexpr int kCsrWaves = 16;
+constexpr int kCsrThreads = kCsrWaves * 64;
+constexpr int kCsrChunk = 16384;  // sources of one doc held in registers per pass (16 per lane)
+constexpr int kCsrBins = 1024;    // destination bins handled per round
+constexpr int kGatherThreads = 256;
+constexpr int kGroups = kGatherThreads / 16;  // 16-lane groups per workgroup
+constexpr int kDqDocs = 64;                   // docs staged per round of the dq pass
+constexpr uint16_t kNoKey = 0xFFFF;
+#ifndef MAXSIM_DD_WAVES
+#define MAXSIM_DD_WAVES 8
+#endif
+#ifndef MAXSIM_DD_UNROLL
+#define MAXSIM_DD_UNROLL 2
+#endif
+constexpr int kDdUnroll = MAXSIM_DD_UNROLL;  // gathers in flight per lane
+constexpr int kDdThreads = 1024;
+constexpr int kWTab = 16384;  // per-(i,s) weights of one doc staged in LDS (64 KB)
 
-template <int E> __device__ __forceinline__ float2 load2(const void* base, int64_t elem_off);
-template <> __device__ __forceinline__ float2 load2<kF16>(const void* base, int64_t off)
+// 8 consecutive elements (16 bytes) widened to fp32
+template <int E> __device__ __forceinline__ void load8(const void* base, int64_t elem_off, float (&x)[8]);
+template <> __device__ __forceinline__ void load8<kF16>(const void* base, int64_t off, float (&x)[8])
 {
-    const _Float16* p = (const _Float16*)base + off;
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    h2 v = *(const h2*)p;
-    return make_float2((float)v[0], (float)v[1]);
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 v = *(const h8*)((const _Float16*)base + off);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (float)v[k];
 }
-template <> __device__ __forceinline__ float2 load2<kBF16>(const void* base, int64_t off)
+template <> __device__ __forceinline__ void load8<kBF16>(const void* base, int64_t off, float (&x)[8])
 {
-    const uint32_t u = *(const uint32_t*)((const __bf16*)base + off);
-    return make_float2(__builtin_bit_cast(float, u << 16), __builtin_bit_cast(float, u & 0xffff0000u));
+    const i32x4 v = *(const i32x4*)((const __bf16*)base + off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t u = (uint32_t)v[k];
+        x[2 * k] = __builtin_bit_cast(float, u << 16);
+        x[2 * k + 1] = __builtin_bit_cast(float, u & 0xffff0000u);
+    }
+}
+
+// gradient rows are written once and not read again here: streamed past the
+// caches so that the gathered rows stay in L2
+__device__ __forceinline__ void store8(float* p, const float (&a)[8])
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store((f4){a[0], a[1], a[2], a[3]}, (f4*)p);
+    __builtin_nontemporal_store((f4){a[4], a[5], a[6], a[7]}, (f4*)(p + 4));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
-
-// Lanes of the wave (among those with `active`) whose key equals this lane's.
-__device__ __forceinline__ uint64_t match_key(uint32_t key, bool active, int nbits)
-{
-    uint64_t peers = __ballot(active);
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = (key >> b) & 1u;
-        const uint64_t bb = __ballot(active && bit);
-        peers &= bit ? bb : ~bb;
-    }
-    return peers;
-}
 
 __device__ __forceinline__ void barrier_lds()
 {
@@ -66,248 +90,387 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("" ::: "memory");
 }
 
+// live(j): doc j has at least one valid token (always, without a d_mask,
+// when Ld > 0). Computed by one wave.
+__device__ __forceinline__ bool doc_live(const uint8_t* __restrict__ d_mask, int64_t j, int64_t Ld)
+{
+    if (!d_mask) return Ld > 0;
+    bool any = false;
+    for (int64_t t = lane_id(); t < Ld; t += 64) {
+        any = any || d_mask[j * Ld + t] != 0;
+        if (__ballot(any) != 0) break;
+    }
+    return __ballot(any) != 0;
+}
+
 }  // namespace
 
-// live(j) -> scratch[j] (1 or 0), one wave per doc
-__global__ __launch_bounds__(kThreads) void doc_live_kernel(const uint8_t* __restrict__ d_mask,
-                                                            int64_t Nd, int64_t Ld,
-                                                            int32_t* __restrict__ scratch)
-{
-    const int64_t j = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (j >= Nd) return;
-    const int lane = lane_id();
-    bool any = false;
-    for (int64_t t = lane; t < Ld && !any; t += 64) any = d_mask[j * Ld + t] != 0;
-    const bool live = __ballot(any) != 0;
-    if (lane == 0) scratch[j] = live ? 1 : 0;
-}
-
-// Eq. (2): one wave per query row r = i*Lq + s; lane l owns dims 2l, 2l+1.
-template <int E>
-__global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a, const int32_t* __restrict__ live)
-{
-    const int64_t r = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t Nq = a.Nq, Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
-    if (r >= Nq * Lq) return;
-    const int lane = lane_id();
-    const int64_t i = r / Lq, s = r % Lq;
-    float ax = 0.f, ay = 0.f;
-    const bool qkeep = a.q_mask ? a.q_mask[r] != 0 : true;
-    if (qkeep && Ld > 0) {
-        for (int64_t j0 = 0; j0 < Nd; j0 += 64) {
-            const int64_t jj = j0 + lane;
-            int t = 0;
-            float w = 0.f;
-            if (jj < Nd) {
-                t = a.argmax[(i * Nd + jj) * Lq + s];
-                t = t < 0 ? 0 : (t >= Ld ? (int)(Ld - 1) : t);  // precondition guard
-                w = a.g[i * Nd + jj];
-                if (live && live[jj] == 0) w = 0.f;
-            }
-            const int cnt = Nd - j0 < 64 ? (int)(Nd - j0) : 64;
-            int k = 0;
-            for (; k + 8 <= cnt; k += 8) {
-                float2 x[8];
-                float ww[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int tk = __builtin_amdgcn_readlane(t, k + u);
-                    ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k + u));
-                    x[u] = load2<E>(a.D, ((j0 + k + u) * Ld + tk) * kD + 2 * lane);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    ax = __builtin_fmaf(ww[u], x[u].x, ax);
-                    ay = __builtin_fmaf(ww[u], x[u].y, ay);
-                }
-            }
-            for (; k < cnt; ++k) {
-                const int tk = __builtin_amdgcn_readlane(t, k);
-                const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-                const float2 x = load2<E>(a.D, ((j0 + k) * Ld + tk) * kD + 2 * lane);
-                ax = __builtin_fmaf(wk, x.x, ax);
-                ay = __builtin_fmaf(wk, x.y, ay);
-            }
+// Doc-local sources k = i*Lq + s visited with a fixed stride: (i, s) is kept
+// incrementally so that no division runs per source. Every index here is
+// below Nq*Lq <= 2^31 - 1.
+struct SrcWalk {
+    uint32_t i, s, di, ds, Lq;
+    __device__ __forceinline__ void init(uint32_t k, uint32_t stride, uint32_t lq)
+    {
+        Lq = lq;
+        i = k / lq;
+        s = k - i * lq;
+        di = stride / lq;
+        ds = stride - di * lq;
+    }
+    __device__ __forceinline__ void next()
+    {
+        i += di;
+        s += ds;
+        if (s >= Lq) {
+            s -= Lq;
+            ++i;
         }
     }
-    *(float2*)(a.dQ + r * kD + 2 * lane) = make_float2(ax, ay);
+};
+
+// Lanes of the wave (among those with `active`) whose key equals this lane's,
+// from one ballot per key bit (keys < 2^10; bits that are 0 in every key
+// leave the result unchanged).
+__device__ __forceinline__ uint64_t match_key10(uint32_t key, bool active)
+{
+    uint64_t peers = __ballot(active);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+    }
+    return peers;
 }
 
-// Inverse map of doc j: row_ptr[j*Ld + t], col_idx[j*Nq*Lq ...] (stable).
-__global__ __launch_bounds__(kThreads) void csr_kernel(BwdArgs a)
+// Inverse map of doc j ("Flash-MaxSim" Sec. 4.2.2): row_ptr[j*Ld + t] and
+// the doc's segment col_idx[j*Nq*Lq, (j+1)*Nq*Lq), each row ascending.
+// Sources are taken in chunks of kCsrChunk; wave w owns the contiguous block
+// [w*kPerWave, (w+1)*kPerWave) of a chunk and holds its destinations in
+// registers (lane l, step m: source m*64 + l of the block). Bins are handled
+// in rounds of kCsrBins.
+__global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
 {
-    __shared__ int32_t hist[kWaves][kCsrBins];
-    __shared__ int32_t wsum[kWaves];
-    const int64_t j = blockIdx.x;
-    const int64_t Nq = a.Nq, Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
+    constexpr int kPerWave = kCsrChunk / kCsrWaves;  // 1024 sources of a chunk per wave
+    constexpr int kSteps = kPerWave / 64;             // 16 per lane
+    __shared__ uint32_t hist[kCsrWaves][kCsrBins];    // per-wave counts, then per-wave slots
+    __shared__ uint32_t run[kCsrBins];                // per-bin totals, then next free slot
+    __shared__ uint32_t wsum[kCsrWaves];
+    const uint32_t j = blockIdx.x;
+    const int64_t Nd = a.Nd, Ld = a.Ld;
+    const uint32_t Lq = (uint32_t)a.Lq, nd = (uint32_t)Nd;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int64_t per_doc = Nq * Lq;
-    const int64_t base = j * per_doc;
-    const int64_t i_lo = Nq * wave / kWaves, i_hi = Nq * (wave + 1) / kWaves;
-    int64_t carry = 0;
+    const uint32_t per_doc = (uint32_t)(a.Nq * a.Lq);
+    const int nchunks = (int)(((int64_t)per_doc + kCsrChunk - 1) / kCsrChunk);
 
+    // live(j) for the dq pass, parked in dD[j, 0, 0] (dD is written last)
+    if (wave == 0 && Ld > 0) {
+        const bool live = doc_live(a.d_mask, j, Ld);
+        if (lane == 0) a.dD[(int64_t)j * Ld * kD] = live ? 1.f : 0.f;
+    }
+
+    // destinations of this wave's block of chunk c, round-relative (kNoKey
+    // outside [t_lo, t_lo + nb))
+    uint32_t key[kSteps];
+    auto load_block = [&](int c, int64_t t_lo, int nb) {
+        const uint32_t k0 = (uint32_t)c * kCsrChunk + (uint32_t)wave * kPerWave;
+        SrcWalk w;
+        w.init(k0 + lane, 64, Lq);
+        int32_t tv[kSteps];
+#pragma unroll
+        for (int m = 0; m < kSteps; ++m, w.next()) {  // every load in flight before the first use
+            const bool ok = k0 + m * 64 + lane < per_doc;
+            const uint32_t src = ok ? (w.i * nd + j) * Lq + w.s : 0u;
+            tv[m] = ok ? __builtin_nontemporal_load(a.argmax + src) : -1;
+        }
+#pragma unroll
+        for (int m = 0; m < kSteps; ++m) {
+            key[m] = kNoKey;
+            if (k0 + m * 64 + lane < per_doc) {
+                int64_t t = tv[m];
+                t = t < 0 ? 0 : (t >= Ld ? Ld - 1 : t);  // precondition guard
+                if (t >= t_lo && t < t_lo + nb) key[m] = (uint32_t)(t - t_lo);
+            }
+        }
+    };
+    // per-wave histogram of the block (counts do not depend on order)
+    auto count_block = [&](int nb) {
+        for (int k = lane; k < nb; k += 64) hist[wave][k] = 0;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+        for (int m = 0; m < kSteps; ++m)
+            if (key[m] != kNoKey) atomicAdd(&hist[wave][key[m]], 1u);
+    };
+    int64_t carry = (int64_t)j * per_doc;  // first CSR slot of the current round
     for (int64_t t_lo = 0; t_lo < Ld; t_lo += kCsrBins) {
         const int nb = (int)(Ld - t_lo < kCsrBins ? Ld - t_lo : kCsrBins);
-        int nbits = 0;
-        while ((1 << nbits) < nb) ++nbits;
-        for (int k = tid; k < kWaves * kCsrBins; k += kThreads) (&hist[0][0])[k] = 0;
-        barrier_lds();
 
-        // pass 1: per-wave histogram of this bin range
-        for (int64_t i = i_lo; i < i_hi; ++i) {
-            const int32_t* arow = a.argmax + (i * Nd + j) * Lq;
-            for (int64_t s0 = 0; s0 < Lq; s0 += 64) {
-                const int64_t s = s0 + lane;
-                const int t = s < Lq ? arow[s] : -1;
-                const bool inr = s < Lq && t >= t_lo && t < t_lo + nb;
-                const uint32_t key = inr ? (uint32_t)(t - t_lo) : 0u;
-                const uint64_t peers = match_key(key, inr, nbits);
-                if (inr && (peers & lanemask_lt()) == 0) hist[wave][key] += __builtin_popcountll(peers);
+        // ---- totals per bin over every chunk --------------------------------
+        for (int k = tid; k < nb; k += kCsrThreads) run[k] = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            barrier_lds();
+            load_block(c, t_lo, nb);
+            count_block(nb);
+            barrier_lds();
+            for (int k = tid; k < nb; k += kCsrThreads) {
+                uint32_t tot = 0;
+                for (int w = 0; w < kCsrWaves; ++w) tot += hist[w][k];
+                run[k] += tot;
             }
         }
         barrier_lds();
 
-        // exclusive scan over bins of the per-bin totals; each thread owns a run of bins
-        const int per = (nb + kThreads - 1) / kThreads;
-        const int k0 = tid * per;
-        const int k1 = k0 + per < nb ? k0 + per : nb;
-        int run = 0;
-        for (int k = k0; k < k1; ++k)
-            for (int w = 0; w < kWaves; ++w) run += hist[w][k];
-        int incl = run;  // inclusive scan of `run` across the wave
+        // ---- exclusive scan of the totals -> row_ptr, first slot per bin ----
+        // (nb <= kCsrThreads: one bin per thread)
+        const uint32_t mine = tid < nb ? run[tid] : 0u;
+        uint32_t incl = mine;
         for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off, 64);
+            const uint32_t v = __shfl_up(incl, off, 64);
             if (lane >= off) incl += v;
         }
         if (lane == 63) wsum[wave] = incl;
         barrier_lds();
-        int wave_off = 0;
-        for (int w = 0; w < wave; ++w) wave_off += wsum[w];
-        int pos = (int)(base + carry) + wave_off + incl - run;  // first CSR slot of bin k0
-        for (int k = k0; k < k1; ++k) {
-            a.row_ptr[j * Ld + t_lo + k] = pos;
-            for (int w = 0; w < kWaves; ++w) {
-                const int c = hist[w][k];
-                hist[w][k] = pos;  // where wave w's sources of bin k start
-                pos += c;
-            }
+        uint32_t wave_off = 0, round_tot = 0;
+        for (int w = 0; w < kCsrWaves; ++w) {
+            if (w < wave) wave_off += wsum[w];
+            round_tot += wsum[w];
         }
-        int tot = 0;
-        for (int w = 0; w < kWaves; ++w) tot += wsum[w];
-        barrier_lds();
+        if (tid < nb) {
+            const int64_t first = carry + wave_off + incl - mine;
+            a.row_ptr[(int64_t)j * Ld + t_lo + tid] = (int32_t)first;
+            run[tid] = (uint32_t)first;
+        }
+        carry += round_tot;
 
-        // pass 2: stable scatter, same traversal order as pass 1
-        for (int64_t i = i_lo; i < i_hi; ++i) {
-            const int32_t* arow = a.argmax + (i * Nd + j) * Lq;
-            for (int64_t s0 = 0; s0 < Lq; s0 += 64) {
-                const int64_t s = s0 + lane;
-                const int t = s < Lq ? arow[s] : -1;
-                const bool inr = s < Lq && t >= t_lo && t < t_lo + nb;
-                const uint32_t key = inr ? (uint32_t)(t - t_lo) : 0u;
-                const uint64_t peers = match_key(key, inr, nbits);
-                if (inr) {
-                    const int slot = hist[wave][key] + __builtin_popcountll(peers & lanemask_lt());
-                    a.col_idx[slot] = (int32_t)((i * Nd + j) * Lq + s);
-                    if ((peers & lanemask_lt()) == 0) hist[wave][key] += __builtin_popcountll(peers);
+        // ---- stable scatter, chunk by chunk, in source order ----------------
+        for (int c = 0; c < nchunks; ++c) {
+            if (nchunks > 1) {  // the only chunk's block is still in registers
+                barrier_lds();
+                load_block(c, t_lo, nb);
+                count_block(nb);
+            }
+            barrier_lds();
+            // slots: bin k of wave w starts after the earlier waves' sources of bin k
+            for (int k = tid; k < nb; k += kCsrThreads) {
+                uint32_t pos = run[k];
+                for (int w = 0; w < kCsrWaves; ++w) {
+                    const uint32_t h = hist[w][k];
+                    hist[w][k] = pos;
+                    pos += h;
+                }
+                run[k] = pos;
+            }
+            barrier_lds();
+            const uint32_t k0 = (uint32_t)c * kCsrChunk + (uint32_t)wave * kPerWave;
+            SrcWalk w;
+            w.init(k0 + lane, 64, Lq > 0 ? Lq : 1u);
+#pragma unroll
+            for (int m = 0; m < kSteps; ++m, w.next()) {
+                const bool act = key[m] != kNoKey;
+                if (__ballot(act) == 0) continue;  // uniform
+                const uint64_t peers = match_key10(key[m], act);
+                if (act) {
+                    const uint64_t before = peers & lanemask_lt();
+                    const uint32_t slot = hist[wave][key[m]] + (uint32_t)__builtin_popcountll(before);
+                    a.col_idx[slot] = (int32_t)((w.i * nd + j) * Lq + w.s);
+                    if (before == 0) hist[wave][key[m]] += (uint32_t)__builtin_popcountll(peers);
                 }
             }
         }
-        carry += tot;
         barrier_lds();
     }
-    if (j == Nd - 1 && tid == 0) a.row_ptr[Nd * Ld] = (int32_t)(Nq * Nd * Lq);
+    if (j == Nd - 1 && tid == 0) a.row_ptr[Nd * Ld] = (int32_t)(a.Nq * Nd * a.Lq);
 }
 
-// Eq. (3): one wave per destination row (j,t), sources in CSR order.
+// Eq. (2): dQ[i,s] = q_mask[i,s] * sum_j g[i,j] live(j) D[j, argmax[i,j,s]].
+// Workgroup = query i and 16 rows s; group g owns row s0 + g, lane l16 owns
+// dims 8*l16 .. 8*l16+7.
 template <int E>
-__global__ __launch_bounds__(kThreads) void dd_kernel(BwdArgs a)
+__global__ __launch_bounds__(kGatherThreads) void dq_kernel(BwdArgs a)
 {
+    __shared__ int32_t am[kDqDocs][kGroups];  // argmax[i, j0 + jj, s0 + g]
+    __shared__ float wj[kDqDocs];             // g[i, j0 + jj] * live(j0 + jj)
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
-    const int64_t blocks_per_doc = (Ld + 63) / 64;
-    const int64_t j = blockIdx.x / blocks_per_doc;
-    const int64_t tb = (blockIdx.x % blocks_per_doc) * 64;
-    const int wave = threadIdx.x >> 6, lane = lane_id();
-    bool live = Ld > 0;
-    if (a.d_mask) {
-        bool any = false;
-        for (int64_t t = lane; t < Ld && !any; t += 64) any = a.d_mask[j * Ld + t] != 0;
-        live = __ballot(any) != 0;
+    const int64_t sblocks = (Lq + kGroups - 1) / kGroups;
+    const int64_t i = blockIdx.x / sblocks;
+    const int64_t s0 = (blockIdx.x % sblocks) * kGroups;
+    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+    const int64_t s = s0 + grp;
+    const bool row_ok = s < Lq;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t j0 = 0; j0 < Nd; j0 += kDqDocs) {
+        const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
+        barrier_lds();
+        for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
+            const int jj = e / kGroups, gg = e % kGroups;
+            int32_t t = 0;
+            if (jj < nj && s0 + gg < Lq) {
+                t = a.argmax[(i * Nd + j0 + jj) * Lq + s0 + gg];
+                t = t < 0 ? 0 : (t >= Ld ? (int32_t)(Ld - 1) : t);  // precondition guard
+            }
+            am[jj][gg] = t;
+        }
+        if (tid < nj) {
+            const int64_t jd = j0 + tid;
+            wj[tid] = a.g[i * Nd + jd] * a.dD[jd * Ld * kD];  // live(j) parked by the csr pass
+        }
+        barrier_lds();
+        if (!row_ok) continue;
+        const int64_t dbase = (j0 * Ld) * kD + 8 * l16;
+        int jj = 0;
+        for (; jj + 8 <= nj; jj += 8) {
+            float x[8][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                load8<E>(a.D, dbase + ((int64_t)(jj + u) * Ld + am[jj + u][grp]) * kD, x[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float w = wj[jj + u];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[u][k], acc[k]);
+            }
+        }
+        for (; jj < nj; ++jj) {
+            float x[8];
+            load8<E>(a.D, dbase + ((int64_t)jj * Ld + am[jj][grp]) * kD, x);
+            const float w = wj[jj];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
+        }
     }
-    for (int rr = 0; rr < 16; ++rr) {
-        const int64_t t = tb + wave * 16 + rr;
-        if (t >= Ld) break;
+    if (row_ok) {
+        const int64_t r = i * Lq + s;
+        if (a.q_mask && a.q_mask[r] == 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+        }
+        store8(a.dQ + r * kD + 8 * l16, acc);
+    }
+}
+
+// Eq. (3): dD[j,t] = sum over the CSR row of (j,t), in order, of
+// w(i,j,s) Q[i,s] with w = g[i,j] q_mask[i,s] live(j). Workgroup = doc j and
+// a block of its rows; group g owns rows t_begin + g + 64*k, lane l16 owns
+// dims 8*l16 .. 8*l16+7. TAB: the doc's weights w for every (i,s) are staged
+// in LDS first (Nq*Lq <= kWTab), so a source costs one CSR read and one
+// gather; otherwise w is read from g and q_mask per source.
+template <int E, bool TAB>
+__global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXSIM_DD_WAVES))) void dd_kernel(
+    BwdArgs a, int rows_per_block)
+{
+    __shared__ float wtab[TAB ? kWTab : 1];
+    const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
+    const int64_t blocks_per_doc = (Ld + rows_per_block - 1) / rows_per_block;
+    const int64_t j = blockIdx.x / blocks_per_doc;
+    const int64_t t_begin = (blockIdx.x % blocks_per_doc) * rows_per_block;
+    const int64_t t_end = t_begin + rows_per_block < Ld ? t_begin + rows_per_block : Ld;
+    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+    const int gbase = tid & 63 & ~15;  // first lane of the group within the wave
+    const bool live = doc_live(a.d_mask, j, Ld);
+    constexpr int kDdGroups = kDdThreads / 16;
+
+    if constexpr (TAB) {
+        const int64_t nqr = a.Nq * Lq;
+        if (live && nqr > 0) {
+            SrcWalk w;
+            w.init(tid, kDdThreads, Lq);
+            for (int64_t k = tid; k < nqr; k += kDdThreads, w.next()) {
+                const float gk = a.g[w.i * Nd + j];
+                wtab[k] = (a.q_mask && a.q_mask[k] == 0) ? 0.f : gk;
+            }
+        }
+        barrier_lds();
+    }
+
+    // a source index src = (i*Nd + j)*Lq + s of this doc gives
+    // src - j*Lq = i*(Nd*Lq) + s
+    const uint32_t ndlq = (uint32_t)(Nd * Lq), jlq = (uint32_t)(j * Lq);
+    const uint32_t nq = (uint32_t)a.Nq, lq = (uint32_t)Lq;
+    for (int64_t t = t_begin + grp; t < t_end; t += kDdGroups) {
         const int64_t row = j * Ld + t;
-        float ax = 0.f, ay = 0.f;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (live) {
             const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
-            for (int e = e0; e < e1; e += 64) {
-                const int cnt = e1 - e < 64 ? e1 - e : 64;
+            for (int e = e0; e < e1; e += 16) {
+                const int cnt = e1 - e < 16 ? e1 - e : 16;
                 int qrow = 0;
                 float w = 0.f;
-                if (lane < cnt) {
-                    const uint32_t src = (uint32_t)a.col_idx[e + lane];
-                    const uint32_t s = src % (uint32_t)Lq;
-                    const uint32_t i = (src / (uint32_t)Lq) / (uint32_t)Nd;
-                    qrow = (int)(i * (uint32_t)Lq + s);
-                    w = a.g[(int64_t)i * Nd + j];
-                    if (a.q_mask && a.q_mask[qrow] == 0) w = 0.f;
+                if (l16 < cnt) {
+                    const uint32_t x = (uint32_t)a.col_idx[e + l16] - jlq;
+                    uint32_t i = x / ndlq;
+                    uint32_t s = x - i * ndlq;
+                    // in range for any CSR content (guards the gathers)
+                    i = i < nq ? i : nq - 1;
+                    s = s < lq ? s : lq - 1;
+                    qrow = (int)(i * lq + s);
+                    if constexpr (TAB) {
+                        w = wtab[qrow];
+                    } else {
+                        w = a.g[(int64_t)i * Nd + j];
+                        if (a.q_mask && a.q_mask[qrow] == 0) w = 0.f;
+                    }
                 }
                 int k = 0;
-                for (; k + 8 <= cnt; k += 8) {
-                    float2 x[8];
-                    float ww[8];
+                for (; k + kDdUnroll <= cnt; k += kDdUnroll) {
+                    float xv[kDdUnroll][8];
+                    float ww[kDdUnroll];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int qr = __builtin_amdgcn_readlane(qrow, k + u);
-                        ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k + u));
-                        x[u] = load2<E>(a.Q, (int64_t)qr * kD + 2 * lane);
+                    for (int u = 0; u < kDdUnroll; ++u) {
+                        const int qr = __shfl(qrow, gbase + k + u, 64);
+                        ww[u] = __shfl(w, gbase + k + u, 64);
+                        load8<E>(a.Q, (int64_t)qr * kD + 8 * l16, xv[u]);
                     }
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        ax = __builtin_fmaf(ww[u], x[u].x, ax);
-                        ay = __builtin_fmaf(ww[u], x[u].y, ay);
-                    }
+                    for (int u = 0; u < kDdUnroll; ++u)
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(ww[u], xv[u][q], acc[q]);
                 }
                 for (; k < cnt; ++k) {
-                    const int qr = __builtin_amdgcn_readlane(qrow, k);
-                    const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-                    const float2 x = load2<E>(a.Q, (int64_t)qr * kD + 2 * lane);
-                    ax = __builtin_fmaf(wk, x.x, ax);
-                    ay = __builtin_fmaf(wk, x.y, ay);
+                    const int qr = __shfl(qrow, gbase + k, 64);
+                    const float wk = __shfl(w, gbase + k, 64);
+                    float xv[8];
+                    load8<E>(a.Q, (int64_t)qr * kD + 8 * l16, xv);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wk, xv[q], acc[q]);
                 }
             }
         }
-        *(float2*)(a.dD + row * kD + 2 * lane) = make_float2(ax, ay);
+        store8(a.dD + row * kD + 8 * l16, acc);
     }
 }
 
 template <int E>
 static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream)
 {
-    const int64_t nsrc = a.Nq * a.Nd * a.Lq;
     hipError_t err;
-    // live flags parked in col_idx[0..Nd) when there is a d_mask and col_idx can hold them
-    const int32_t* live = nullptr;
-    if (a.d_mask && nsrc >= a.Nd && a.Nd > 0) {
-        hipLaunchKernelGGL(doc_live_kernel, dim3((unsigned)((a.Nd + kWaves - 1) / kWaves)),
-                           dim3(kThreads), 0, stream, a.d_mask, a.Nd, a.Ld, a.col_idx);
+    if (a.Nd > 0) {  // CSR (and the parked live flags) first
+        hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.Nd), dim3(kCsrThreads), 0, stream, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        live = a.col_idx;
     }
     const int64_t qrows = a.Nq * a.Lq;
     if (qrows > 0) {
-        hipLaunchKernelGGL(dq_kernel<E>, dim3((unsigned)((qrows + kWaves - 1) / kWaves)),
-                           dim3(kThreads), 0, stream, a, live);
+        // (with no docs the kernel writes zeros)
+        const int64_t blocks = a.Nq * ((a.Lq + kGroups - 1) / kGroups);
+        hipLaunchKernelGGL(dq_kernel<E>, dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if (a.Nd > 0) {
-        hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.Nd), dim3(kThreads), 0, stream, a);
+    if (a.Nd > 0 && a.Ld > 0) {
+        // about two workgroups per CU, whole 64-row steps, within one doc
+        const int64_t rows = a.Nd * a.Ld;
+        int64_t rpb = (rows + 2 * (int64_t)device_cu_count() - 1) / (2 * (int64_t)device_cu_count());
+        rpb = (rpb + 63) / 64 * 64;
+        if (rpb > a.Ld) rpb = (a.Ld + 63) / 64 * 64;
+        if (rpb > 4096) rpb = 4096;
+        const int64_t blocks = a.Nd * ((a.Ld + rpb - 1) / rpb);
+        if (a.Nq * a.Lq <= kWTab)
+            hipLaunchKernelGGL((dd_kernel<E, true>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
+                               (int)rpb);
+        else
+            hipLaunchKernelGGL((dd_kernel<E, false>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
+                               (int)rpb);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if (a.Ld > 0) {
-            const int64_t blocks = a.Nd * ((a.Ld + 63) / 64);
-            hipLaunchKernelGGL(dd_kernel<E>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-        }
     }
     return hipSuccess;
 }

@@ -574,13 +574,7 @@ static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
         a.npass = (a.ntq + SLOTS - 1) / SLOTS;
     }
     a.nqb = (int)((a.Nq + a.qpw - 1) / a.qpw);
-    static int ncu = 0;
-    if (ncu == 0) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (ncu <= 0) ncu = 256;
-    }
+    const int ncu = device_cu_count();
     // doc ranges: enough workgroups to give every CU one, each range at least one doc
     int64_t R = (ncu + a.nqb - 1) / a.nqb;
     if (R > a.Nd) R = a.Nd;

@@ -22,6 +22,8 @@
 // query columns in a fixed order and written once. All cursor state is
 // wave-uniform (scalar registers). The ring is private to the wave, so there
 // are no barriers, and there are no atomics.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -363,17 +365,15 @@ static hipError_t launch_varlen_t(VarlenArgs a, hipStream_t stream)
 {
     const bool am = a.argmax != nullptr;
     auto kern = am ? fwd_varlen_kernel<E, true, NTQ> : fwd_varlen_kernel<E, false, NTQ>;
-    static int max_units_cache[2] = {0, 0};
-    int& max_units = max_units_cache[am ? 1 : 0];
-    if (max_units == 0) {
-        int dev = 0, ncu = 0, per_cu = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kUnitsPerBlock * 64, 0);
-        if (ncu <= 0) ncu = 256;
-        if (per_cu <= 0) per_cu = 1;
-        max_units = ncu * per_cu * kUnitsPerBlock;
+    static std::atomic<int> per_cu_cache[2];  // resident workgroups per CU, by argmax
+    int per_cu = per_cu_cache[am ? 1 : 0].load(std::memory_order_relaxed);
+    if (per_cu <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kUnitsPerBlock * 64, 0) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        per_cu_cache[am ? 1 : 0].store(per_cu, std::memory_order_relaxed);
     }
+    const int64_t max_units = (int64_t)device_cu_count() * per_cu * kUnitsPerBlock;
     int64_t units = a.Nd / 8;  // about 8+ docs per unit keeps the per-unit setup amortised
     if (units < 1) units = 1;
     if (units > max_units) units = max_units;

@@ -50,6 +50,9 @@ struct BwdArgs {
     int64_t Nq, Nd, Lq, Ld;
 };
 
+// Compute units of the current device (queried once per device, thread-safe).
+int device_cu_count();
+
 hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t stream);
 hipError_t launch_fwd_varlen(int elem, VarlenArgs a, hipStream_t stream);
 hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream);

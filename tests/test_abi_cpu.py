@@ -13,6 +13,8 @@ HEADER = os.path.join(ROOT, "include", "maxsim.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_OVERFLOW, ERR_LAUNCH = range(6)
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+MIS8 = ctypes.c_void_p(0x1008)  # 8- but not 16-byte aligned
+MIS2 = ctypes.c_void_p(0x1002)  # 2- but not 4-byte aligned
 
 
 def _declared():
@@ -64,6 +66,11 @@ def test_fwd_validation(L):
     assert fwd(L, Nd=0, sc=None) == OK
     assert fwd(L, Nq=1 << 16, Nd=1 << 15, Lq=2, am=FAKE) == ERR_OVERFLOW
     assert fwd(L, Nq=1 << 20, Nd=1 << 12) == ERR_OVERFLOW
+    # row tensors need 16-byte alignment, outputs their element alignment
+    assert fwd(L, Q=MIS8) == ERR_UNSUPPORTED
+    assert fwd(L, D=MIS8) == ERR_UNSUPPORTED
+    assert fwd(L, sc=MIS2) == ERR_UNSUPPORTED
+    assert fwd(L, am=MIS2) == ERR_UNSUPPORTED
 
 
 def test_varlen_validation(L):
@@ -75,6 +82,9 @@ def test_varlen_validation(L):
     assert f(1, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 128, None, None, None) == ERR_NULL
     assert f(1, FAKE, FAKE, 0, 32, FAKE, FAKE, 2, 128, None, None, None) == OK
     assert f(0, FAKE, FAKE, 1 << 10, 1 << 12, FAKE, FAKE, 1 << 10, 128, FAKE, FAKE, None) == ERR_OVERFLOW
+    assert f(0, MIS8, FAKE, 1, 32, FAKE, FAKE, 2, 128, FAKE, None, None) == ERR_UNSUPPORTED
+    assert f(0, FAKE, MIS2, 1, 32, FAKE, FAKE, 2, 128, FAKE, None, None) == ERR_UNSUPPORTED
+    assert f(0, FAKE, FAKE, 1, 32, MIS8, FAKE, 2, 128, FAKE, None, None) == ERR_UNSUPPORTED
 
 
 def test_i8_validation(L):
@@ -94,6 +104,8 @@ def test_i8_validation(L):
     assert call(Lq=1041) == ERR_OVERFLOW
     assert call(Lq=1040, Q=None) == ERR_NULL
     assert call(Nq=0) == OK
+    assert call(D=MIS8) == ERR_UNSUPPORTED
+    assert call(si=MIS2) == ERR_UNSUPPORTED
 
 
 def test_bwd_validation(L):
@@ -113,6 +125,10 @@ def test_bwd_validation(L):
     assert call(dD=None) == ERR_NULL
     assert call(Nq=1 << 11, Nd=1 << 10, Lq=1 << 10) == ERR_OVERFLOW
     assert call(Nd=1 << 16, Ld=1 << 15) == ERR_OVERFLOW
+    assert call(Q=MIS8) == ERR_UNSUPPORTED
+    assert call(dQ=MIS8) == ERR_UNSUPPORTED
+    assert call(dD=MIS8) == ERR_UNSUPPORTED
+    assert call(ci=MIS2) == ERR_UNSUPPORTED
     assert call(Nq=0, Nd=0, Lq=0, Ld=0, Q=None, D=None, am=None, g=None, dQ=None, dD=None,
                 rp=None, ci=None) == OK
 

@@ -305,6 +305,10 @@ BWD_CASES = [
     (4, 3, 64, 64, torch.bfloat16, 0.0, 0.0, 0, 0.7),   # hub token: 70% of sources in one row
     (2, 2, 1, 5000, torch.float16, 0.0, 0.0, 0, 0.0),   # CSR bins in two rounds
     (130, 2, 3, 10, torch.float16, 0.0, 0.0, 0, 0.0),   # many queries per doc
+    (130, 2, 128, 10, torch.float16, 0.2, 0.0, 0, 0.0),  # > 16384 sources per doc: two CSR chunks,
+                                                         # weights read per source
+    (6, 3, 40, 700, torch.bfloat16, 0.1, 0.2, 1, 0.0),   # a doc's bins split over workgroups
+    (1, 513, 2, 1030, torch.float16, 0.0, 0.0, 0, 0.0),  # one bin range per doc, two rounds
 ]
 
 
