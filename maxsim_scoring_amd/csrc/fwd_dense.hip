@@ -117,6 +117,16 @@ template <typename V> __device__ __forceinline__ V vmax(V a, V b) { return a > b
 template <> __device__ __forceinline__ float vmax<float>(float a, float b) { return __builtin_fmaxf(a, b); }
 template <typename V> __device__ __forceinline__ V vmax3(V a, V b, V c) { return vmax(vmax(a, b), c); }
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // Running state of one N-tile for the lane's 16 rows of each M-tile.
 // Without argmax it is the running max only. With argmax the lane also keeps
 // the 16 values of the M-tile that last raised its max and that M-tile's row
@@ -478,75 +488,64 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             }
 
             if ((vb[0] | vb[1]) != 0) {
-                const uint32_t sbase = ring_base + (uint32_t)(stage * STAGE_BYTES);
-                // A fragments: row = doc token (lane % 32), k-half = lane / 32;
-                // M-tile mt sits mt * 32 rows further (immediate offset)
-                uint32_t ad[KS];
+                // A fragments of M-tile mt: row = doc token 32 mt + lane % 32,
+                // 16-byte chunk 2s + lane / 32 of that row (swizzled). Plain
+                // LDS loads: the stage was published by the wait + barrier
+                // above, and the compiler does not see the ring's loads.
+                const unsigned char* sb = stage_buf + stage * STAGE_BYTES;
+                auto load_a = [&](int mt, i32x4 (&af)[KS]) {
 #pragma unroll
-                for (int s = 0; s < KS; ++s) ad[s] = sbase + frag_off[s];
-                auto read_async = [&](auto mtc, i32x4 (&af)[KS]) {
-                    constexpr int OFF = decltype(mtc)::value * 32 * RB;
-                    if constexpr (KS == 8) lds_read8_async_off<OFF>(af, ad);
-                    else lds_read4_async_off<OFF>(af, ad);
+                    for (int s = 0; s < KS; ++s) af[s] = *(const i32x4*)(sb + frag_off[s] + mt * 32 * RB);
                 };
-                // one N-tile at a time: a single accumulator tile is live, and
-                // the fold of N-tile n overlaps the MFMAs of N-tile n+1.
-                // FULL: every row of the tile is valid (no mask work at all).
-                auto do_mtile = [&](auto fullc, int mt, const i32x4 (&af)[KS]) {
-                    constexpr bool FULL = decltype(fullc)::value;
-                    const uint32_t mbits = FULL ? 0xffffffffu : (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
-                    if (!FULL && mbits == 0) return;
-                    const int base = (int)(t0 + mt * 32);
+                auto mma = [&](const i32x4 (&af)[KS], int n) {
+                    Acc acc = Acc{};
 #pragma unroll
-                    for (int n = 0; n < NTW; ++n) {
-                        Acc acc = Acc{};
+                    for (int s = 0; s < KS; ++s) acc = mfma32<E>(af[s], qf[n][s], acc);
+                    return acc;
+                };
+                if ((vb[0] & vb[1]) == ~0ull) {
+                    // every row valid: the (M-tile, N-tile) units in order,
+                    // software-pipelined: the MFMAs of unit u are issued before
+                    // the fold of unit u - 1, so the two execute together, and
+                    // the next M-tile's fragments are read during the first
+                    // unit of the current one
+                    constexpr int U = 4 * NTW;
+                    i32x4 afA[KS], afB[KS];
+                    Acc accs[2];
+                    load_a(0, afA);
+                    static_for<0, U>([&](auto uc) {
+                        constexpr int u = decltype(uc)::value;
+                        constexpr int mt = u / NTW, n = u % NTW;
+                        i32x4(&cur)[KS] = (mt & 1) ? afB : afA;
+                        i32x4(&nxt)[KS] = (mt & 1) ? afA : afB;
+                        if constexpr (n == 0 && mt + 1 < 4) load_a(mt + 1, nxt);
+                        accs[u & 1] = mma(cur, n);
+                        if constexpr (u > 0) {
+                            constexpr int pu = u - 1;
+                            fold_one<V, ARGMAX, false>(accs[pu & 1], st[pu % NTW], (int)(t0 + (pu / NTW) * 32), 0u);
+                        }
+                    });
+                    constexpr int lu = U - 1;
+                    fold_one<V, ARGMAX, false>(accs[lu & 1], st[lu % NTW], (int)(t0 + (lu / NTW) * 32), 0u);
+                } else {
+                    // partial tile: M-tiles with no valid row are skipped
+                    static_for<0, 4>([&](auto mc) {
+                        constexpr int mt = decltype(mc)::value;
+                        const uint32_t mbits = (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
+                        if (mbits == 0) return;
+                        i32x4 af[KS];
+                        load_a(mt, af);
+                        const int base = (int)(t0 + mt * 32);
 #pragma unroll
-                        for (int s = 0; s < KS; ++s) acc = mfma32<E>(af[s], qf[n][s], acc);
-                        if (FULL || mbits == 0xffffffffu)
-                            fold_one<V, ARGMAX, false>(acc, st[n], base, 0u);
-                        else
-                            fold_one<V, ARGMAX, true>(acc, st[n], base, mbits >> (4 * h));
-                    }
-                };
-                using M0 = std::integral_constant<int, 0>;
-                using M1 = std::integral_constant<int, 1>;
-                using M2 = std::integral_constant<int, 2>;
-                using M3 = std::integral_constant<int, 3>;
-                auto run_tile = [&](auto fullc) {
-                    constexpr bool FULL = decltype(fullc)::value;
-                    if constexpr (READAHEAD) {
-                        i32x4 afA[KS], afB[KS];
-                        read_async(M0{}, afA);
-                        lds_wait_regs(afA);
-                        read_async(M1{}, afB);
-                        do_mtile(fullc, 0, afA);
-                        lds_wait_regs(afB);
-                        read_async(M2{}, afA);
-                        do_mtile(fullc, 1, afB);
-                        lds_wait_regs(afA);
-                        read_async(M3{}, afB);
-                        do_mtile(fullc, 2, afA);
-                        lds_wait_regs(afB);
-                        do_mtile(fullc, 3, afB);
-                    } else {
-                        auto one = [&](auto mtc) {
-                            constexpr int mt = decltype(mtc)::value;
-                            if (!FULL && (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1))) == 0) return;
-                            i32x4 af[KS];
-                            read_async(mtc, af);
-                            lds_wait_regs(af);
-                            do_mtile(fullc, mt, af);
-                        };
-                        one(M0{});
-                        one(M1{});
-                        one(M2{});
-                        one(M3{});
-                    }
-                };
-                if ((vb[0] & vb[1]) == ~0ull)
-                    run_tile(std::true_type{});
-                else
-                    run_tile(std::false_type{});
+                        for (int n = 0; n < NTW; ++n) {
+                            const Acc acc = mma(af, n);
+                            if (mbits == 0xffffffffu)
+                                fold_one<V, ARGMAX, false>(acc, st[n], base, 0u);
+                            else
+                                fold_one<V, ARGMAX, true>(acc, st[n], base, mbits >> (4 * h));
+                        }
+                    });
+                }
             }
             if (tt == ntd - 1) finish_doc(doc, k);
             stage = stage == 2 ? 0 : stage + 1;
