@@ -35,6 +35,12 @@ namespace maxsim {
 
 namespace {
 
+#ifndef MAXSIM_DENSE_SGB
+#define MAXSIM_DENSE_SGB 0
+#endif
+#ifndef MAXSIM_DENSE_VPM
+#define MAXSIM_DENSE_VPM 4
+#endif
 constexpr int kTileRows = 128;  // doc tokens per pipeline stage (4 MFMA M-tiles)
 constexpr int kStages = 3;
 constexpr int kWaves = 8;
@@ -380,43 +386,51 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             }
         };
 
-        // add up part[k & 1] in slot order and write the scores of doc `doc`
+        // wave 0 adds up part[k & 1] and writes the scores of doc `doc`: the
+        // cnt partials of a query sit in a group of P lanes (P = cnt rounded
+        // up to a power of two) and are added by a fixed butterfly
         auto write_scores = [&](int64_t doc, int64_t k) {
+            if (wave != 0) return;
+            const int cnt = a.npass == 1 ? a.ntq : (a.ntq - pass * SLOTS < SLOTS ? a.ntq - pass * SLOTS : SLOTS);
+            const int nq = a.npass == 1 ? a.qpw : 1;  // queries of the workgroup
+            int P = 1;
+            while (P < cnt) P <<= 1;
+            const int q = lane / P, n = lane % P;
+            V v = 0;
+            if (q < nq && n < cnt)
+                v = __builtin_bit_cast(V, lds_load_b32(part_base + (uint32_t)(((k & 1) * SLOTS + q * cnt + n) * 4)));
+            for (int off = P >> 1; off >= 1; off >>= 1) {
+                if constexpr (E == kI8)
+                    v += shfl_xor_i(v, off);
+                else
+                    v += shfl_xor_f(v, off);
+            }
+            if (n != 0 || q >= nq) return;
             if (a.npass == 1) {
-                if (tid < a.qpw) {
-                    const int64_t i = (int64_t)qb * a.qpw + tid;
-                    if (i < a.Nq) {
-                        V sum = 0;
-                        for (int n = 0; n < a.ntq; ++n)
-                            sum += __builtin_bit_cast(V, lds_load_b32(
-                                part_base + (uint32_t)(((k & 1) * SLOTS + tid * a.ntq + n) * 4)));
-                        if constexpr (E == kI8) {
-                            if (a.scores_i32) a.scores_i32[i * Nd + doc] = sum;
-                            if (a.scores) a.scores[i * Nd + doc] = (float)(((double)sum * a.q_scale) * a.d_scale);
-                        } else {
-                            a.scores[i * Nd + doc] = sum;
-                        }
+                const int64_t i = (int64_t)qb * a.qpw + q;
+                if (i < a.Nq) {
+                    if constexpr (E == kI8) {
+                        if (a.scores_i32) a.scores_i32[i * Nd + doc] = v;
+                        if (a.scores) a.scores[i * Nd + doc] = (float)(((double)v * a.q_scale) * a.d_scale);
+                    } else {
+                        a.scores[i * Nd + doc] = v;
                     }
                 }
-            } else if (tid == 0) {
-                // one long query: this pass's N-tiles, in slot order, added to
-                // the running sum kept in the output (pass 0 starts it)
-                const int nslots = a.ntq - pass * SLOTS < SLOTS ? a.ntq - pass * SLOTS : SLOTS;
-                V sum = 0;
-                for (int n = 0; n < nslots; ++n)
-                    sum += __builtin_bit_cast(V, lds_load_b32(part_base + (uint32_t)(((k & 1) * SLOTS + n) * 4)));
+            } else {
+                // one long query: this pass's sum is added to the running sum
+                // kept in the output (pass 0 starts it)
                 const int64_t o = (int64_t)qb * Nd + doc;
                 const bool last = pass + 1 == a.npass;
                 if constexpr (E == kI8) {
                     // the int32 running sum lives in scores_i32 when it exists,
                     // else in the float output's bits until the last pass
                     int32_t* run = a.scores_i32 ? a.scores_i32 : (int32_t*)a.scores;
-                    const V tot = (pass == 0 ? 0 : run[o]) + sum;
+                    const V tot = (pass == 0 ? 0 : run[o]) + v;
                     if (a.scores_i32) a.scores_i32[o] = tot;
                     if (last && a.scores) a.scores[o] = (float)(((double)tot * a.q_scale) * a.d_scale);
                     else if (!a.scores_i32) run[o] = tot;
                 } else {
-                    a.scores[o] = (pass == 0 ? 0.f : a.scores[o]) + sum;
+                    a.scores[o] = (pass == 0 ? 0.f : a.scores[o]) + v;
                 }
             }
         };
@@ -527,6 +541,19 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     });
                     constexpr int lu = U - 1;
                     fold_one<V, ARGMAX, false>(accs[lu & 1], st[lu % NTW], (int)(t0 + (lu / NTW) * 32), 0u);
+#if MAXSIM_DENSE_SGB
+                    // issue order: each MFMA followed by a few VALU ops and
+                    // LDS reads, so that one wave keeps the matrix pipe busy
+                    // while its vector work and fragment reads go in between
+                    constexpr int NM = U * KS;
+                    static_for<0, NM>([&](auto ic) {
+                        constexpr int i = decltype(ic)::value;
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, MAXSIM_DENSE_VPM, 0);  // VALU
+                        if constexpr (i % (NM / (4 * KS) > 0 ? NM / (4 * KS) : 1) == 0)
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    });
+#endif
                 } else {
                     // partial tile: M-tiles with no valid row are skipped
                     static_for<0, 4>([&](auto mc) {
