@@ -35,12 +35,6 @@ namespace maxsim {
 
 namespace {
 
-#ifndef MAXSIM_DENSE_SGB
-#define MAXSIM_DENSE_SGB 0
-#endif
-#ifndef MAXSIM_DENSE_VPM
-#define MAXSIM_DENSE_VPM 4
-#endif
 constexpr int kTileRows = 128;  // doc tokens per pipeline stage (4 MFMA M-tiles)
 constexpr int kStages = 3;
 constexpr int kWaves = 8;
@@ -541,19 +535,6 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     });
                     constexpr int lu = U - 1;
                     fold_one<V, ARGMAX, false>(accs[lu & 1], st[lu % NTW], (int)(t0 + (lu / NTW) * 32), 0u);
-#if MAXSIM_DENSE_SGB
-                    // issue order: each MFMA followed by a few VALU ops and
-                    // LDS reads, so that one wave keeps the matrix pipe busy
-                    // while its vector work and fragment reads go in between
-                    constexpr int NM = U * KS;
-                    static_for<0, NM>([&](auto ic) {
-                        constexpr int i = decltype(ic)::value;
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, MAXSIM_DENSE_VPM, 0);  // VALU
-                        if constexpr (i % (NM / (4 * KS) > 0 ? NM / (4 * KS) : 1) == 0)
-                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                    });
-#endif
                 } else {
                     // partial tile: M-tiles with no valid row are skipped
                     static_for<0, 4>([&](auto mc) {
