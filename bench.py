@@ -211,7 +211,7 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
     return {"workload": "backward_colpali_bf16_128x128_lq128_ld1024", "ms": t,
             "pairs_per_s": 128 * 128 / (t * 1e-3), "compulsory_bytes": nbytes,
             "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
-            "kernels": ["doc_live_kernel", "dq_kernel", "csr_kernel", "dd_kernel"]}
+            "kernels": ["csr_kernel", "dq_kernel", "dd_kernel"]}
 
 
 def bench_copy(torch, ms, synth, wl, steps, warmup):
