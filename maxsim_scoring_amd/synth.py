@@ -98,6 +98,31 @@ def quantise_per_tensor(x: torch.Tensor) -> tuple[torch.Tensor, float]:
     return q, float(s)
 
 
+def quantise_per_token(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Symmetric int8 with one scale per row (token) of x [..., d]:
+    s = max|row|/127 (float32; 1 for an all-zero row),
+    q = clamp(round_half_even(row/s), -127, 127). Returns (q int8, s float32 [...])."""
+    xf = x.float().reshape(-1, x.shape[-1])
+    q = torch.empty(xf.shape, dtype=torch.int8)
+    s = torch.empty(xf.shape[0], dtype=torch.float32)
+    step = 1 << 16
+
+    def fill(c: int) -> None:
+        lo = c * step
+        hi = min(xf.shape[0], lo + step)
+        rows = xf[lo:hi].numpy()
+        amax = np.abs(rows).max(axis=1) if rows.shape[1] else np.zeros(rows.shape[0], np.float32)
+        sc = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+        v = np.rint(rows / sc[:, None])
+        q[lo:hi] = torch.from_numpy(np.clip(v, -127, 127).astype(np.int8))
+        s[lo:hi] = torch.from_numpy(sc)
+
+    n = (xf.shape[0] + step - 1) // step
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(n)))
+    return q.view(x.shape), s.view(x.shape[:-1])
+
+
 def prefix_mask(lengths: np.ndarray, width: int) -> torch.Tensor:
     """uint8 [len(lengths), width] with the first lengths[r] entries of row r set."""
     ar = np.arange(width)[None, :]
@@ -153,6 +178,22 @@ class Int8:
     want_argmax: bool = False
     seed: int = 0
     meta: dict = field(default_factory=dict)
+
+
+@dataclass
+class Int8Tok:
+    """INT8 cross-product workload with one scale per token, plus (optionally)
+    the float rows the int8 values were quantised from, for rescoring."""
+    name: str
+    Q: torch.Tensor
+    q_scale: torch.Tensor  # [Nq, Lq] float32
+    D: torch.Tensor
+    d_scale: torch.Tensor  # [Nd, Ld] float32
+    q_mask: Optional[torch.Tensor] = None
+    d_mask: Optional[torch.Tensor] = None
+    Qf: Optional[torch.Tensor] = None  # fp16/bf16 copies for the rescoring stage
+    Df: Optional[torch.Tensor] = None
+    seed: int = 0
 
 
 @dataclass
@@ -218,6 +259,22 @@ def int8_long_query(seed: int = 4, Nd: int = 10_000, Lq: int = 1024, Ld: int = 1
     D, ds = quantise_per_tensor(Df)
     del Df
     return Int8(f"int8_1x{Nd}_lq{Lq}_ld{Ld}", Q, qs, D, ds, None, None, False, seed)
+
+
+def two_stage_long_query(seed: int = 4, Nd: int = 10_000, Lq: int = 1024, Ld: int = 1024,
+                         float_dtype: torch.dtype = torch.float16) -> Int8Tok:
+    """The long-query INT8 corpus with per-token scales (the rows of
+    ``int8_long_query``), with fp16 copies of the same unit rows for the
+    rescoring stage of the INT8 -> FP16 top-K scan."""
+    Qf = unit_rows(seed, _S_Q, Lq, dtype=torch.float32).view(1, Lq, D_MODEL)
+    Q, qs = quantise_per_token(Qf)
+    Qh = Qf.to(float_dtype)
+    del Qf
+    Df = unit_rows(seed, _S_D, Nd * Ld, dtype=torch.float32).view(Nd, Ld, D_MODEL)
+    D, ds = quantise_per_token(Df)
+    Dh = Df.to(float_dtype)
+    del Df
+    return Int8Tok(f"int8tok_1x{Nd}_lq{Lq}_ld{Ld}", Q, qs, D, ds, None, None, Qh, Dh, seed)
 
 
 def colpali_backward(seed: int = 5, fwd: Optional[Dense] = None,
@@ -347,3 +404,44 @@ def hub_docs(dense: Dense) -> Dense:
 def upstream_grad(seed: int, Nq: int, Nd: int) -> torch.Tensor:
     return torch.from_numpy(np.random.default_rng([seed, _S_G]).standard_normal((Nq, Nd))
                             .astype(np.float32))
+
+
+def random_int8_tok(seed: int, Nq: int, Nd: int, Lq: int, Ld: int, q_mask_p: float = 0.0,
+                    d_mask_p: float = 0.0, dead_docs: int = 0, pow2_scales: bool = False,
+                    float_dtype: Optional[torch.dtype] = None) -> Int8Tok:
+    """Per-token quantised unit rows. ``pow2_scales`` replaces the scales by
+    powers of two in [2^-9, 2^-5] (every product is then exact in float64)."""
+    rng = np.random.default_rng([seed, _S_MISC])
+    Qf = unit_rows(seed, _S_Q, Nq * Lq, dtype=torch.float32).view(Nq, Lq, D_MODEL)
+    Df = unit_rows(seed, _S_D, Nd * Ld, dtype=torch.float32).view(Nd, Ld, D_MODEL)
+    Q, qs = quantise_per_token(Qf)
+    D, ds = quantise_per_token(Df)
+    if pow2_scales:
+        qs = torch.from_numpy(np.ldexp(1.0, rng.integers(-9, -4, size=(Nq, Lq))).astype(np.float32))
+        ds = torch.from_numpy(np.ldexp(1.0, rng.integers(-9, -4, size=(Nd, Ld))).astype(np.float32))
+    qm = dm = None
+    if q_mask_p > 0:
+        qm = torch.from_numpy((rng.random((Nq, Lq)) >= q_mask_p).astype(np.uint8))
+    if d_mask_p > 0 or dead_docs:
+        dm = torch.from_numpy((rng.random((Nd, Ld)) >= d_mask_p).astype(np.uint8))
+        for j in range(min(dead_docs, Nd)):
+            dm[Nd - 1 - j] = 0
+    Qh = Qf.to(float_dtype) if float_dtype is not None else None
+    Dh = Df.to(float_dtype) if float_dtype is not None else None
+    return Int8Tok(f"int8tok_{Nq}x{Nd}_lq{Lq}_ld{Ld}", Q, qs, D, ds, qm, dm, Qh, Dh, seed)
+
+
+def random_scores(seed: int, Nq: int, Nd: int, ties: bool = False) -> torch.Tensor:
+    """Scores [Nq, Nd] float32 for the top-k step; ``ties`` rounds them to a
+    coarse grid so that many values repeat."""
+    v = np.random.default_rng([seed, _S_MISC]).standard_normal((Nq, Nd)).astype(np.float32)
+    if ties:
+        v = np.round(v * 4.0).astype(np.float32) / np.float32(4.0)
+    return torch.from_numpy(v)
+
+
+def random_pairs(seed: int, Nq: int, Nd: int, P: int) -> tuple[torch.Tensor, torch.Tensor]:
+    """P (query, doc) index pairs, int32, drawn uniformly (repeats allowed)."""
+    rng = np.random.default_rng([seed, _S_ARG])
+    return (torch.from_numpy(rng.integers(0, Nq, size=P).astype(np.int32)),
+            torch.from_numpy(rng.integers(0, Nd, size=P).astype(np.int32)))

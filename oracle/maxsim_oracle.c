@@ -12,7 +12,10 @@
  *         Eq. (1) MaxSim; Sec. 4.1.1 online max with -inf masking;
  *         Sec. 4.2.1 Eqs. (2)-(3) closed-form gradients;
  *         Sec. 4.2.2 inverse-grid CSR (bincount, cumsum, stable argsort);
- *         Sec. 4.3.1 INT8 x INT8; Sec. 4.3.2 padding-free cu_seqlens.
+ *         Sec. 4.3.1 INT8 x INT8 (per-tensor and per-token scales);
+ *         Sec. 4.3.2 padding-free cu_seqlens.
+ *   [TMS] "TileMaxSim: IO-Aware GPU MaxSim Scoring ..." (arXiv 2606.26439v1):
+ *         Sec. 6.8 "End-to-End Retrieval Latency" (top-k after scoring).
  *   [LIK] "late-interaction-kernels design notes" (docs/design.md):
  *         "Problem" (masks), "Forward" pseudocode (strict '>' update,
  *         argmax starts at 0, finalise m <- finite(m) & q_active ? m : 0),
@@ -339,4 +342,156 @@ int oracle_bwd_f64(const double* Q, const double* D, int64_t Nq, int64_t Nd, int
     return 0;
 }
 
-int oracle_version(void) { return 1; }
+/* ------------------------------------------------------------------------ */
+/* INT8 x INT8 with one symmetric scale per token ("Flash-MaxSim" Sec.       */
+/* 4.3.1): the similarity of query row s and doc row t is the dot product of */
+/* the dequantised rows, q_scale[s] * d_scale[t] * <Q8[s], D8[t]>, taken     */
+/* through the same masked max and sum as Eq. (1).                           */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const int8_t *Q, *D;
+    const double *qs, *ds;
+    int64_t Nq, Nd, Lq, Ld, d;
+    const uint8_t *qm, *dm;
+    double* score;
+    int32_t* argmax;
+} i8tok_ctx;
+
+static void i8tok_item(void* p, int64_t k)
+{
+    i8tok_ctx* c = (i8tok_ctx*)p;
+    int64_t i = k / c->Nd, j = k % c->Nd;
+    const int8_t* Qi = c->Q + i * c->Lq * c->d;
+    const int8_t* Dj = c->D + j * c->Ld * c->d;
+    const double* qs = c->qs + i * c->Lq;
+    const double* ds = c->ds + j * c->Ld;
+    const uint8_t* qm = c->qm ? c->qm + i * c->Lq : NULL;
+    const uint8_t* dm = c->dm ? c->dm + j * c->Ld : NULL;
+    int32_t* arg = c->argmax ? c->argmax + k * c->Lq : NULL;
+    double acc = 0.0;
+    for (int64_t s = 0; s < c->Lq; ++s) {
+        const int8_t* q = Qi + s * c->d;
+        double best = -INFINITY;
+        int64_t at = 0;
+        for (int64_t t = 0; t < c->Ld; ++t) {
+            if (dm && !dm[t]) continue;
+            const int8_t* x = Dj + t * c->d;
+            int64_t dot = 0;
+            for (int64_t e = 0; e < c->d; ++e) dot += (int64_t)q[e] * (int64_t)x[e];
+            const double v = qs[s] * ds[t] * (double)dot;
+            if (v > best) {
+                best = v;
+                at = t;
+            }
+        }
+        if (arg) arg[s] = (int32_t)at;
+        if (isfinite(best) && (!qm || qm[s])) acc += best;
+    }
+    c->score[k] = acc;
+}
+
+/* Q int8 [Nq,Lq,d] with q_scale [Nq,Lq]; D int8 [Nd,Ld,d] with d_scale
+ * [Nd,Ld]; masks as in oracle_fwd_f64; score [Nq,Nd]; argmax or NULL. */
+int oracle_fwd_i8_tok(const int8_t* Q, const double* q_scale, const int8_t* D,
+                      const double* d_scale, int64_t Nq, int64_t Nd, int64_t Lq, int64_t Ld,
+                      int64_t d, const uint8_t* q_mask, const uint8_t* d_mask, double* score,
+                      int32_t* argmax, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return -1;
+    i8tok_ctx c = {Q, D, q_scale, d_scale, Nq, Nd, Lq, Ld, d, q_mask, d_mask, score, argmax};
+    parallel_for(Nq * Nd, nthreads, i8tok_item, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-k after scoring (the retrieval step that follows the scores in the    */
+/* TileMaxSim paper, Sec. 6.8 "End-to-End Retrieval Latency"): for each      */
+/* query the k largest scores in decreasing order; equal scores are taken in */
+/* increasing doc order. A full sort under that total order, then the first  */
+/* k entries.                                                                */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    double v;
+    int64_t j;
+} scored_t;
+
+static int scored_cmp(const void* a, const void* b)
+{
+    const scored_t* x = (const scored_t*)a;
+    const scored_t* y = (const scored_t*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+typedef struct {
+    const double* scores;
+    int64_t Nd, K;
+    int32_t* idx;
+    double* val;
+} topk_ctx;
+
+static void topk_item(void* p, int64_t i)
+{
+    topk_ctx* c = (topk_ctx*)p;
+    scored_t* a = (scored_t*)malloc(sizeof(scored_t) * (size_t)(c->Nd > 0 ? c->Nd : 1));
+    for (int64_t j = 0; j < c->Nd; ++j) {
+        a[j].v = c->scores[i * c->Nd + j];
+        a[j].j = j;
+    }
+    qsort(a, (size_t)c->Nd, sizeof(scored_t), scored_cmp);
+    for (int64_t r = 0; r < c->K; ++r) {
+        c->idx[i * c->K + r] = (int32_t)a[r].j;
+        c->val[i * c->K + r] = a[r].v;
+    }
+    free(a);
+}
+
+/* scores [Nq,Nd] (no NaN); idx [Nq,K] int32 and val [Nq,K]; 0 <= K <= Nd */
+int oracle_topk(const double* scores, int64_t Nq, int64_t Nd, int64_t K, int32_t* idx,
+                double* val, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || K < 0 || K > Nd) return -1;
+    for (int64_t e = 0; e < Nq * Nd; ++e)
+        if (isnan(scores[e])) return -2;
+    topk_ctx c = {scores, Nd, K, idx, val};
+    parallel_for(Nq, nthreads, topk_item, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scores of listed (query, doc) pairs: Eq. (1) for pair p between query     */
+/* pair_q[p] and doc pair_d[p] of the dense tensors (rescoring candidates).  */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const double *Q, *D;
+    int64_t Nq, Nd, Lq, Ld, d;
+    const uint8_t *qm, *dm;
+    const int32_t *pq, *pd;
+    double* scores;
+    int32_t* argmax;
+} pairs_ctx;
+
+static void pairs_item(void* p, int64_t k)
+{
+    pairs_ctx* c = (pairs_ctx*)p;
+    int64_t i = c->pq[k], j = c->pd[k];
+    c->scores[k] = pair_f64(c->Q + i * c->Lq * c->d, c->D + j * c->Ld * c->d, c->Lq, c->Ld, c->d,
+                            c->qm ? c->qm + i * c->Lq : NULL, c->dm ? c->dm + j * c->Ld : NULL,
+                            c->argmax ? c->argmax + k * c->Lq : NULL);
+}
+
+int oracle_fwd_pairs_f64(const double* Q, const double* D, int64_t Nq, int64_t Nd, int64_t Lq,
+                         int64_t Ld, int64_t d, const uint8_t* q_mask, const uint8_t* d_mask,
+                         const int32_t* pair_q, const int32_t* pair_d, int64_t P, double* scores,
+                         int32_t* argmax, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0 || P < 0) return -1;
+    for (int64_t k = 0; k < P; ++k)
+        if (pair_q[k] < 0 || pair_q[k] >= Nq || pair_d[k] < 0 || pair_d[k] >= Nd) return -2;
+    pairs_ctx c = {Q, D, Nq, Nd, Lq, Ld, d, q_mask, d_mask, pair_q, pair_d, scores, argmax};
+    parallel_for(P, nthreads, pairs_item, &c);
+    return 0;
+}
+
+int oracle_version(void) { return 2; }

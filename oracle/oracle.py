@@ -47,8 +47,14 @@ def _load():
                                       vp, i32]
         lib.oracle_bwd_f64.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                        vp, vp, i32]
+        lib.oracle_fwd_i8_tok.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
+                                          vp, i32]
+        lib.oracle_topk.argtypes = [vp, i64, i64, i64, vp, vp, i32]
+        lib.oracle_fwd_pairs_f64.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                                             i64, vp, vp, i32]
         for f in (lib.oracle_fwd_f64, lib.oracle_fwd_varlen_f64, lib.oracle_fwd_i8,
-                  lib.oracle_bwd_f64):
+                  lib.oracle_bwd_f64, lib.oracle_fwd_i8_tok, lib.oracle_topk,
+                  lib.oracle_fwd_pairs_f64):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -157,3 +163,54 @@ def bwd(Q, D, argmax, grad_scores, q_mask=None, d_mask=None, threads=None):
                                 _p(dQ), _p(dD), _p(rp), _p(ci), threads or default_threads())
     _check(rc, "bwd")
     return dQ, dD, rp, ci
+
+
+def fwd_i8_tok(Q, q_scale, D, d_scale, q_mask=None, d_mask=None, want_argmax=True, threads=None):
+    """INT8 forward with per-token scales q_scale [Nq,Lq], d_scale [Nd,Ld].
+    Returns (score float64 [Nq,Nd], argmax int32 [Nq,Nd,Lq] or None)."""
+    q = _arr(Q, np.int8)
+    dd = _arr(D, np.int8)
+    Nq, Lq, d = q.shape
+    Nd, Ld, _ = dd.shape
+    qs = _f64(q_scale).reshape(Nq, Lq)
+    ds = _f64(d_scale).reshape(Nd, Ld)
+    qm = _arr(q_mask, np.uint8)
+    dm = _arr(d_mask, np.uint8)
+    sf = np.zeros((Nq, Nd), np.float64)
+    arg = np.zeros((Nq, Nd, Lq), np.int32) if want_argmax else None
+    rc = _load().oracle_fwd_i8_tok(_p(q), _p(qs), _p(dd), _p(ds), Nq, Nd, Lq, Ld, d, _p(qm),
+                                   _p(dm), _p(sf), _p(arg), threads or default_threads())
+    _check(rc, "fwd_i8_tok")
+    return sf, arg
+
+
+def topk(scores, k, threads=None):
+    """Per-row top-k of scores [Nq,Nd]: (idx int32 [Nq,k], val float64 [Nq,k]),
+    values decreasing, equal values in increasing index order."""
+    v = _f64(scores)
+    Nq, Nd = v.shape
+    idx = np.zeros((Nq, k), np.int32)
+    val = np.zeros((Nq, k), np.float64)
+    rc = _load().oracle_topk(_p(v), Nq, Nd, k, _p(idx), _p(val), threads or default_threads())
+    _check(rc, "topk")
+    return idx, val
+
+
+def fwd_pairs(Q, D, pair_q, pair_d, q_mask=None, d_mask=None, want_argmax=True, threads=None):
+    """Scores of the listed (query, doc) pairs of dense Q [Nq,Lq,d], D [Nd,Ld,d].
+    Returns (scores float64 [P], argmax int32 [P,Lq] or None)."""
+    q = _f64(Q)
+    dd = _f64(D)
+    Nq, Lq, d = q.shape
+    Nd, Ld, _ = dd.shape
+    pq = _arr(pair_q, np.int32)
+    pd = _arr(pair_d, np.int32)
+    P = len(pq)
+    qm = _arr(q_mask, np.uint8)
+    dm = _arr(d_mask, np.uint8)
+    sc = np.zeros(P, np.float64)
+    arg = np.zeros((P, Lq), np.int32) if want_argmax else None
+    rc = _load().oracle_fwd_pairs_f64(_p(q), _p(dd), Nq, Nd, Lq, Ld, d, _p(qm), _p(dm), _p(pq),
+                                      _p(pd), P, _p(sc), _p(arg), threads or default_threads())
+    _check(rc, "fwd_pairs")
+    return sc, arg

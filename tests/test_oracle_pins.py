@@ -390,3 +390,86 @@ def test_size_examples():
     am = g["argmax"]
     b = wl.argmax_bytes(am["nq"], am["nd"], am["lq"])
     assert abs(b / 2**20 - am["approx_mb"]) <= am["rel_tol"] * am["approx_mb"]
+
+
+# ------------------------------------------- per-token INT8, top-k, pair lists
+
+def test_hand_example_int8_per_token(oracle_mod):
+    g = _gold("hand_example.json")
+    t = g["int8_per_token"]
+    Q = np.array(g["Q"], np.int8)
+    D = np.array(g["D"], np.int8)
+    dm = np.array(g["d_mask"], np.uint8)
+    s, a = oracle_mod.fwd_i8_tok(Q, np.array(t["q_scale"]), D, np.array(t["d_scale"]), None, dm)
+    assert np.array_equal(s, np.array(t["score"], np.float64))
+    assert np.array_equal(a, np.array(t["argmax"], np.int32))
+
+
+def test_int8_tok_uniform_scales_is_per_tensor(oracle_mod):
+    """One scale for every token reduces to the per-tensor form."""
+    w = synth.random_int8(31, 3, 4, 40, 70, d_mask_p=0.2, q_mask_p=0.2)
+    qs = np.full(w.Q.shape[:2], w.q_scale)
+    ds = np.full(w.D.shape[:2], w.d_scale)
+    s, a = oracle_mod.fwd_i8_tok(w.Q, qs, w.D, ds, w.q_mask, w.d_mask)
+    _, sf, ar = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    np.testing.assert_allclose(s, sf, rtol=1e-13, atol=1e-13)
+    assert np.array_equal(a, ar)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 9, 20), (1, 4, 33, 65), (3, 2, 1, 1)])
+def test_int8_tok_brute_force(oracle_mod, shape):
+    """Power-of-two scales make every product exact, so the brute force over
+    dequantised rows must agree exactly, argmax included."""
+    Nq, Nd, Lq, Ld = shape
+    w = synth.random_int8_tok(40 + Lq, Nq, Nd, Lq, Ld, q_mask_p=0.2, d_mask_p=0.2, dead_docs=1,
+                              pow2_scales=True)
+    s, a = oracle_mod.fwd_i8_tok(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    Qd = w.Q.double() * w.q_scale.double()[..., None]
+    Dd = w.D.double() * w.d_scale.double()[..., None]
+    sb, ab = bf.dense(Qd, Dd, w.q_mask, w.d_mask)
+    assert np.array_equal(s, sb)
+    assert np.array_equal(a, ab)
+
+
+def test_hand_example_topk(oracle_mod):
+    for c in _gold("hand_example.json")["topk"]["cases"]:
+        idx, val = oracle_mod.topk(np.array(c["scores"], np.float64), c["k"])
+        assert np.array_equal(idx, np.array(c["idx"], np.int32).reshape(idx.shape))
+        assert np.array_equal(val, np.array(c["val"], np.float64).reshape(val.shape))
+
+
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("k", [1, 7, 100, 300])
+def test_topk_matches_lexsort(oracle_mod, ties, k):
+    v = synth.random_scores(50 + k, 5, 300, ties=ties).numpy()
+    idx, val = oracle_mod.topk(v, k)
+    for i in range(v.shape[0]):
+        order = np.lexsort((np.arange(v.shape[1]), -v[i].astype(np.float64)))[:k]
+        assert np.array_equal(idx[i], order)
+        assert np.array_equal(val[i], v[i, order].astype(np.float64))
+        assert np.all(np.diff(val[i]) <= 0)
+
+
+def test_hand_example_pairs(oracle_mod):
+    g = _gold("hand_example.json")
+    t = g["pairs"]
+    Q = np.array(g["Q"], np.float64)
+    D = np.array(g["D"], np.float64)
+    dm = np.array(g["d_mask"], np.uint8)
+    s, a = oracle_mod.fwd_pairs(Q, D, np.array(t["pair_q"]), np.array(t["pair_d"]), None, dm)
+    assert np.array_equal(s, np.array(t["score"], np.float64))
+    assert np.array_equal(a, np.array(t["argmax"], np.int32))
+
+
+def test_pairs_brute_force(oracle_mod):
+    w = synth.random_dense(61, 4, 6, 20, 45, dtype=torch.bfloat16, q_mask_p=0.2, d_mask_p=0.2,
+                           dead_docs=1)
+    pq, pd = synth.random_pairs(61, 4, 6, 30)
+    s, a = oracle_mod.fwd_pairs(w.Q, w.D, pq, pd, w.q_mask, w.d_mask)
+    for p in range(30):
+        i, j = int(pq[p]), int(pd[p])
+        sb, ab = bf.dense(w.Q[i:i + 1], w.D[j:j + 1],
+                          None if w.q_mask is None else w.q_mask[i:i + 1],
+                          None if w.d_mask is None else w.d_mask[j:j + 1])
+        np.testing.assert_allclose(s[p], sb[0, 0], rtol=0, atol=1e-12)
+        assert np.array_equal(a[p], ab[0, 0])
