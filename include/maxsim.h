@@ -114,6 +114,59 @@ maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, f
                               float* scores, int32_t* argmax, maxsim_stream_t stream);
 
 /*
+ * INT8 x INT8 forward with one symmetric scale per token ("Flash-MaxSim"
+ * Sec. 4.3.1): the similarity of query row s and doc row t is
+ *     q_scale[i,s] * d_scale[j,t] * <Q[i,s], D[j,t]>
+ * (exact int32 dot product, then float), through the masked max and sum of
+ * maxsim_fwd.
+ *   Q int8 [Nq, Lq, d], q_scale [Nq, Lq] float32
+ *   D int8 [Nd, Ld, d], d_scale [Nd, Ld] float32
+ *   masks as in maxsim_fwd; scores [Nq, Nd] float32; argmax as in maxsim_fwd
+ *   or NULL
+ * Scales must be positive and finite (the query-token scale multiplies the
+ * max over doc tokens); values in [-127, 127]. Errors as maxsim_fwd.
+ */
+maxsim_status_t maxsim_fwd_i8_tok(const int8_t* Q, const float* q_scale, const int8_t* D,
+                                  const float* d_scale, int64_t Nq, int64_t Nd, int64_t Lq,
+                                  int64_t Ld, int64_t d, const uint8_t* q_mask,
+                                  const uint8_t* d_mask, float* scores, int32_t* argmax,
+                                  maxsim_stream_t stream);
+
+/*
+ * Scores of listed (query, doc) pairs, for rescoring candidates (the second
+ * stage of the INT8 -> FP16 top-K scan, "Flash-MaxSim" Sec. 4.1.4): pair p is
+ * Eq. (1) for query pair_q[p] of Q [Nq, Lq, d] against doc pair_d[p] of
+ * D [Nd, Ld, d], with the masks of maxsim_fwd.
+ *   pair_q, pair_d [P] int32 in [0, Nq) and [0, Nd) (a precondition: entries
+ *     outside are clamped, never read out of bounds); pairs may repeat
+ *   scores [P] float32; argmax [P, Lq] int32 or NULL
+ * Errors: SHAPE (negative sizes; P > 0 with Nq == 0 or Nd == 0), NULL,
+ * UNSUPPORTED (d, dtype, alignment), OVERFLOW (P*Lq >= 2^31 with argmax).
+ */
+maxsim_status_t maxsim_fwd_pairs(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
+                                 int64_t Nd, int64_t Lq, int64_t Ld, int64_t d,
+                                 const uint8_t* q_mask, const uint8_t* d_mask,
+                                 const int32_t* pair_q, const int32_t* pair_d, int64_t P,
+                                 float* scores, int32_t* argmax, maxsim_stream_t stream);
+
+/*
+ * Top-k after scoring (TileMaxSim paper, Sec. 6.8 "End-to-End Retrieval
+ * Latency"): for each row i of scores [Nq, Nd] float32 (no NaN), the K
+ * largest values in decreasing order; equal values are taken in increasing
+ * column order (-0 and +0 are equal).
+ *   ids  [Nq, Nd] int32 or NULL: idx reports ids[i, column] instead of the
+ *        column (e.g. the doc ids of a candidate list)
+ *   idx  [Nq, K] int32, val [Nq, K] float32 (the input values, bit for bit)
+ *   rows [Nq, K] int32 or NULL: the row index i of each entry (a pair list)
+ * 0 <= K <= Nd and K <= 1024. K == 0 or Nq == 0 enqueues nothing.
+ * Errors: SHAPE (negative sizes, K > Nd), UNSUPPORTED (K > 1024, alignment),
+ * NULL, OVERFLOW (Nq or Nd >= 2^31).
+ */
+maxsim_status_t maxsim_topk(const float* scores, int64_t Nq, int64_t Nd, int64_t K,
+                            const int32_t* ids, int32_t* idx, float* val, int32_t* rows,
+                            maxsim_stream_t stream);
+
+/*
  * Backward through a saved forward argmax ("Flash-MaxSim" Sec. 4.2.1
  * Eqs. (2)-(3), Sec. 4.2.2 inverse-grid CSR, Sec. 4.2.3 destination-owned
  * reduction; design notes "Backward"):

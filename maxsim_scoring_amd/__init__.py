@@ -7,7 +7,9 @@ seeded synthetic workloads and ``workload`` holds the byte/flop model.
 """
 
 from .binding import (MaxSimError, maxsim_abi_version, maxsim_bwd, maxsim_fwd, maxsim_fwd_i8,
-                      maxsim_fwd_varlen, maxsim_status_string)
+                      maxsim_fwd_i8_tok, maxsim_fwd_pairs, maxsim_fwd_varlen, maxsim_status_string,
+                      maxsim_topk, two_stage_topk)
 
-__all__ = ["MaxSimError", "maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd",
+__all__ = ["MaxSimError", "maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_fwd_i8_tok",
+           "maxsim_fwd_pairs", "maxsim_topk", "two_stage_topk", "maxsim_bwd",
            "maxsim_status_string", "maxsim_abi_version"]

@@ -49,7 +49,12 @@ def lib() -> ctypes.CDLL:
         L.maxsim_fwd_i8.argtypes = [vp, f32, vp, f32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.maxsim_bwd.argtypes = [ci, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp,
                                  vp, vp]
-        for f in (L.maxsim_fwd, L.maxsim_fwd_varlen, L.maxsim_fwd_i8, L.maxsim_bwd):
+        L.maxsim_fwd_i8_tok.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.maxsim_fwd_pairs.argtypes = [ci, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, vp,
+                                       vp, vp]
+        L.maxsim_topk.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        for f in (L.maxsim_fwd, L.maxsim_fwd_varlen, L.maxsim_fwd_i8, L.maxsim_bwd,
+                  L.maxsim_fwd_i8_tok, L.maxsim_fwd_pairs, L.maxsim_topk):
             f.restype = ci
         L.maxsim_status_string.argtypes = [ci]
         L.maxsim_status_string.restype = ctypes.c_char_p
@@ -223,3 +228,115 @@ def maxsim_status_string(status: int) -> str:
 
 def maxsim_abi_version() -> int:
     return lib().maxsim_abi_version()
+
+
+def maxsim_fwd_i8_tok(Q: torch.Tensor, q_scale: torch.Tensor, D: torch.Tensor,
+                      d_scale: torch.Tensor, q_mask: Optional[torch.Tensor] = None,
+                      d_mask: Optional[torch.Tensor] = None, want_argmax: bool = False,
+                      scores: Optional[torch.Tensor] = None,
+                      argmax: Optional[torch.Tensor] = None, stream=None):
+    """INT8 forward with per-token scales q_scale [Nq,Lq], d_scale [Nd,Ld]
+    (float32, positive). Returns (scores float32 [Nq,Nd], argmax or None)."""
+    Nq, Lq, d = Q.shape
+    Nd, Ld, d2 = D.shape
+    if d2 != d or Q.dtype != torch.int8 or D.dtype != torch.int8:
+        raise ValueError("Q and D must be int8 with the same d")
+    for n, t in (("Q", Q), ("D", D)):
+        _dev(n, t)
+    _dev("q_scale", q_scale, torch.float32)
+    _dev("d_scale", d_scale, torch.float32)
+    if tuple(q_scale.shape) != (Nq, Lq) or tuple(d_scale.shape) != (Nd, Ld):
+        raise ValueError("scales must be [Nq, Lq] and [Nd, Ld]")
+    _dev("q_mask", q_mask, torch.uint8)
+    _dev("d_mask", d_mask, torch.uint8)
+    if scores is None:
+        scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
+    if argmax is None and want_argmax:
+        argmax = torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=Q.device)
+    _dev("scores", scores, torch.float32)
+    _dev("argmax", argmax, torch.int32)
+    st = lib().maxsim_fwd_i8_tok(_p(Q), _p(q_scale), _p(D), _p(d_scale), Nq, Nd, Lq, Ld, d,
+                                 _p(q_mask), _p(d_mask), _p(scores), _p(argmax), _stream(stream))
+    _check("maxsim_fwd_i8_tok", st)
+    return scores, argmax
+
+
+def maxsim_fwd_pairs(Q: torch.Tensor, D: torch.Tensor, pair_q: torch.Tensor,
+                     pair_d: torch.Tensor, q_mask: Optional[torch.Tensor] = None,
+                     d_mask: Optional[torch.Tensor] = None, want_argmax: bool = False,
+                     scores: Optional[torch.Tensor] = None,
+                     argmax: Optional[torch.Tensor] = None, stream=None):
+    """Scores of the listed (query, doc) pairs of dense Q, D (fp16/bf16).
+    pair_q, pair_d int32 [P]. Returns (scores [P], argmax [P,Lq] or None)."""
+    Nq, Lq, d = Q.shape
+    Nd, Ld, d2 = D.shape
+    if d2 != d or D.dtype != Q.dtype:
+        raise ValueError("Q and D must share d and dtype")
+    for n, t in (("Q", Q), ("D", D)):
+        _dev(n, t)
+    _dev("pair_q", pair_q, torch.int32)
+    _dev("pair_d", pair_d, torch.int32)
+    P = pair_q.numel()
+    if pair_d.numel() != P:
+        raise ValueError("pair_q and pair_d must have the same length")
+    _dev("q_mask", q_mask, torch.uint8)
+    _dev("d_mask", d_mask, torch.uint8)
+    if scores is None:
+        scores = torch.empty((P,), dtype=torch.float32, device=Q.device)
+    if argmax is None and want_argmax:
+        argmax = torch.empty((P, Lq), dtype=torch.int32, device=Q.device)
+    _dev("scores", scores, torch.float32)
+    _dev("argmax", argmax, torch.int32)
+    st = lib().maxsim_fwd_pairs(_dtype_code(Q), _p(Q), _p(D), Nq, Nd, Lq, Ld, d, _p(q_mask),
+                                _p(d_mask), _p(pair_q), _p(pair_d), P, _p(scores), _p(argmax),
+                                _stream(stream))
+    _check("maxsim_fwd_pairs", st)
+    return scores, argmax
+
+
+def maxsim_topk(scores: torch.Tensor, k: int, ids: Optional[torch.Tensor] = None,
+                want_rows: bool = False, idx: Optional[torch.Tensor] = None,
+                val: Optional[torch.Tensor] = None, rows: Optional[torch.Tensor] = None,
+                stream=None):
+    """Per-row top-k of scores [Nq,Nd] float32: (idx int32 [Nq,k], val float32
+    [Nq,k], rows int32 [Nq,k] or None), values decreasing, equal values in
+    increasing column order. With ``ids`` [Nq,Nd] int32, idx reports
+    ids[row, column] instead of the column; ``rows`` holds each entry's row."""
+    if scores.dim() != 2:
+        raise ValueError("scores must be [Nq, Nd]")
+    _dev("scores", scores, torch.float32)
+    Nq, Nd = scores.shape
+    _dev("ids", ids, torch.int32)
+    if ids is not None and tuple(ids.shape) != (Nq, Nd):
+        raise ValueError("ids must have the shape of scores")
+    if idx is None:
+        idx = torch.empty((Nq, k), dtype=torch.int32, device=scores.device)
+    if val is None:
+        val = torch.empty((Nq, k), dtype=torch.float32, device=scores.device)
+    if rows is None and want_rows:
+        rows = torch.empty((Nq, k), dtype=torch.int32, device=scores.device)
+    _dev("idx", idx, torch.int32)
+    _dev("val", val, torch.float32)
+    _dev("rows", rows, torch.int32)
+    st = lib().maxsim_topk(_p(scores), Nq, Nd, k, _p(ids), _p(idx), _p(val), _p(rows),
+                           _stream(stream))
+    _check("maxsim_topk", st)
+    return idx, val, rows
+
+
+def two_stage_topk(Qi8: torch.Tensor, q_scale: torch.Tensor, Di8: torch.Tensor,
+                   d_scale: torch.Tensor, Qf: torch.Tensor, Df: torch.Tensor, k: int,
+                   candidates: int, q_mask: Optional[torch.Tensor] = None,
+                   d_mask: Optional[torch.Tensor] = None, stream=None):
+    """The INT8 -> FP16 top-K scan ("Flash-MaxSim" Sec. 4.1.4): per-token INT8
+    scores of every doc, the `candidates` best docs per query, exact fp16/bf16
+    scores of those (query, doc) pairs, and the top-k of the rescored
+    candidates. Four library calls. Returns (doc idx int32 [Nq,k], exact
+    scores float32 [Nq,k], int8-stage scores [Nq,Nd])."""
+    Nq = Qi8.shape[0]
+    s8, _ = maxsim_fwd_i8_tok(Qi8, q_scale, Di8, d_scale, q_mask, d_mask, stream=stream)
+    cand, _, cand_q = maxsim_topk(s8, candidates, want_rows=True, stream=stream)
+    exact, _ = maxsim_fwd_pairs(Qf, Df, cand_q.view(-1), cand.view(-1), q_mask, d_mask,
+                                stream=stream)
+    doc, val, _ = maxsim_topk(exact.view(Nq, candidates), k, ids=cand, stream=stream)
+    return doc, val, s8

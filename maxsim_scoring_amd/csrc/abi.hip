@@ -155,6 +155,103 @@ maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, f
     return launch_status(launch_fwd_dense(kI8, a, argmax != nullptr, (hipStream_t)stream));
 }
 
+maxsim_status_t maxsim_fwd_i8_tok(const int8_t* Q, const float* q_scale, const int8_t* D,
+                                  const float* d_scale, int64_t Nq, int64_t Nd, int64_t Lq,
+                                  int64_t Ld, int64_t d, const uint8_t* q_mask,
+                                  const uint8_t* d_mask, float* scores, int32_t* argmax,
+                                  maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
+    if (d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || Nd == 0) return MAXSIM_OK;
+    if (!scores) return MAXSIM_ERR_NULL;
+    if ((Lq > 0 && (!Q || !q_scale)) || (Ld > 0 && (!D || !d_scale))) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(q_scale, 4) || !aligned(d_scale, 4) ||
+        !aligned(scores, 4) || !aligned(argmax, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
+    const int64_t pairs = mul_sat(Nq, Nd);
+    if (pairs < 0 || pairs > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (argmax) {
+        const int64_t n = mul_sat(pairs, Lq);
+        if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    DenseArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.q_mask = q_mask;
+    a.d_mask = d_mask;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.q_scale_tok = q_scale;
+    a.d_scale_tok = d_scale;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.Lq = Lq;
+    a.Ld = Ld;
+    return launch_status(launch_fwd_dense(kI8, a, argmax != nullptr, (hipStream_t)stream));
+}
+
+maxsim_status_t maxsim_fwd_pairs(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
+                                 int64_t Nd, int64_t Lq, int64_t Ld, int64_t d,
+                                 const uint8_t* q_mask, const uint8_t* d_mask,
+                                 const int32_t* pair_q, const int32_t* pair_d, int64_t P,
+                                 float* scores, int32_t* argmax, maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0 || P < 0) return MAXSIM_ERR_SHAPE;
+    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (P == 0) return MAXSIM_OK;
+    if (Nq == 0 || Nd == 0) return MAXSIM_ERR_SHAPE;  // a pair needs a query and a doc
+    if (!scores || !pair_q || !pair_d) return MAXSIM_ERR_NULL;
+    if ((Lq > 0 && !Q) || (Ld > 0 && !D)) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(pair_q, 4) || !aligned(pair_d, 4) ||
+        !aligned(scores, 4) || !aligned(argmax, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
+    if (P > kI32Max) return MAXSIM_ERR_OVERFLOW;  // one workgroup per pair
+    if (argmax) {
+        const int64_t n = mul_sat(P, Lq);
+        if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    DenseArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.q_mask = q_mask;
+    a.d_mask = d_mask;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.pair_q = pair_q;
+    a.pair_d = pair_d;
+    a.npairs = P;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.Lq = Lq;
+    a.Ld = Ld;
+    return launch_status(launch_fwd_dense(elem_of(dtype), a, argmax != nullptr, (hipStream_t)stream));
+}
+
+maxsim_status_t maxsim_topk(const float* scores, int64_t Nq, int64_t Nd, int64_t K,
+                            const int32_t* ids, int32_t* idx, float* val, int32_t* rows,
+                            maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || K < 0 || K > Nd) return MAXSIM_ERR_SHAPE;
+    if (K > kTopkMaxK) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || K == 0) return MAXSIM_OK;
+    if (!scores || !idx || !val) return MAXSIM_ERR_NULL;
+    if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(val, 4) || !aligned(ids, 4) ||
+        !aligned(rows, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
+    if (Nd > kI32Max || Nq > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    TopkArgs a{};
+    a.scores = scores;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.K = (int)K;
+    a.ids = ids;
+    a.idx = idx;
+    a.val = val;
+    a.rows = rows;
+    return launch_status(launch_topk(a, (hipStream_t)stream));
+}
+
 maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
                            int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
                            const uint8_t* d_mask, const int32_t* argmax, const float* grad_scores,

@@ -171,6 +171,15 @@ __device__ __forceinline__ void dma_lds16_nt(const void* base, uint32_t voff, ui
                  : "s"(lds), "v"(voff), "s"(base)
                  : "memory", "m0");
 }
+// One 4-byte-per-lane direct-to-LDS load: lane l's dword lands at `lds` + 4 l
+// (active lanes only).
+__device__ __forceinline__ void dma_lds4(const void* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ const void* uniform_ptr(const void* p)

@@ -205,15 +205,18 @@ __device__ __forceinline__ int saved_argmax(const RowState<V, true>& st)
 
 }  // namespace
 
-// READAHEAD: read the next M-tile's A fragments while the current one
-// multiplies (32 more VGPRs for fp16/bf16; the argmax variants cannot afford
-// them within 256 VGPRs at two waves per SIMD and read synchronously).
-template <int E, bool ARGMAX, int NTW, bool READAHEAD>
+// TOK (int8 only): one scale per token. The doc-token scale multiplies each
+// integer dot product before the max (a float per score); the query-token
+// scale (positive) is applied to the max. The tile's doc scales are staged in
+// LDS with the tile.
+template <int E, bool ARGMAX, int NTW, bool TOK>
 __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 {
+    static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
     using T = Traits<E>;
-    using V = typename T::Scalar;
+    using V = std::conditional_t<TOK, float, typename T::Scalar>;  // value of the max
     using Acc = typename T::Acc;
+    typedef float F16v __attribute__((ext_vector_type(16)));
     constexpr int RB = T::kRowBytes;
     constexpr int NCH = RB / 16;           // 16-byte chunks per row
     constexpr int KS = T::kKSteps;
@@ -222,12 +225,15 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     constexpr int CHUNKS = kTileRows * NCH;
     constexpr int THREADS = kWaves * 64;
     constexpr int LPS = CHUNKS / THREADS;  // direct-to-LDS loads per thread per stage
+    constexpr int LPW = LPS + (TOK ? 1 : 0);  // direct-to-LDS loads per wave per stage
     static_assert(CHUNKS % THREADS == 0, "stage must split evenly over the workgroup");
 
     __shared__ __attribute__((aligned(16))) unsigned char stage_buf[kStages * STAGE_BYTES];
     __shared__ V part[2][SLOTS];
     // d_mask of the whole doc range as bits, when it fits: 2 words per tile
     __shared__ __attribute__((aligned(16))) uint64_t mask_lds[kMaskWords];
+    // doc-token scales of each stage's tile (TOK)
+    __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? kStages * kTileRows : 4];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -241,11 +247,26 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     const int xcd = b & 7, kth = b >> 3;
     const int full = nblk >> 3, rem = nblk & 7;
     const int unit = xcd * full + (xcd < rem ? xcd : rem) + kth;
-    const int qb = unit % a.nqb;
-    const int64_t r = unit / a.nqb;
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
-    const int64_t d0 = r * Nd / a.nranges, d1 = (r + 1) * Nd / a.nranges;
+    // work unit = (query block, doc range), or with a pair list, pair `unit`:
+    // query pair_q[unit] (one query per block) against the one doc pair_d[unit]
+    const bool pairs = a.pair_q != nullptr;
+    int qb;
+    int64_t d0, d1;
+    if (pairs) {
+        const int32_t pq = a.pair_q[unit], pd = a.pair_d[unit];
+        qb = pq < 0 ? 0 : (pq >= a.Nq ? (int)a.Nq - 1 : pq);  // precondition guard
+        d0 = pd < 0 ? 0 : (pd >= Nd ? Nd - 1 : pd);
+        d1 = d0 + 1;
+    } else {
+        qb = unit % a.nqb;
+        const int64_t r = unit / a.nqb;
+        d0 = r * Nd / a.nranges;
+        d1 = (r + 1) * Nd / a.nranges;
+    }
     if (d0 >= d1) return;  // uniform over the workgroup
+    // where the results of (query i, doc j) go
+    auto out_pair = [&](int64_t i, int64_t j) -> int64_t { return pairs ? (int64_t)unit : i * Nd + j; };
 
     const int ntd = Ld > 0 ? (int)((Ld + kTileRows - 1) / kTileRows) : 0;  // tiles per doc
     const int64_t F = (d1 - d0) * ntd;                                     // tiles of the range
@@ -267,6 +288,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 #pragma unroll
     for (int s = 0; s < KS; ++s) frag_off[s] = (uint32_t)(col * RB + swz_chunk<RB>(col, 2 * s + h) * 16);
     const uint32_t ring_base = lds_addr(stage_buf);
+    const uint32_t sc_base = lds_addr(sc_buf);
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
 
@@ -286,6 +308,13 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 const int row = dma_row[u] < rows ? dma_row[u] : rows - 1;
                 dma_lds16(Dt, (uint32_t)(row * RB + dma_lc[u] * 16), lds0 + u * 1024);
             }
+        }
+        if constexpr (TOK) {  // rows 16 w .. 16 w + 15 of the tile's doc scales
+            const void* St = uniform_ptr(a.d_scale_tok + doc * Ld + t0);
+            const int row = 16 * wave + lane < rows ? 16 * wave + lane : rows - 1;
+            if (lane < 16)
+                dma_lds4(St, (uint32_t)(row * 4),
+                         sc_base + (uint32_t)((stage * kTileRows + 16 * wave_u) * 4));
         }
     };
 
@@ -309,6 +338,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     for (int pass = 0; pass < a.npass; ++pass) {
         // ---- the N-tiles this wave owns in this pass ------------------------
         int qi[NTW], ntl[NTW];
+        float qsc[NTW];  // query-token scale (TOK)
         bool tok_ok[NTW];
         bool keep_row[NTW];  // q_mask of this lane's query token
 #pragma unroll
@@ -327,6 +357,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             const int64_t s_tok = (int64_t)ntl[n] * 32 + col;
             tok_ok[n] = slot_ok && s_tok < Lq;
             keep_row[n] = tok_ok[n] && (!a.q_mask || a.q_mask[(int64_t)qi[n] * Lq + s_tok] != 0);
+            if constexpr (TOK) qsc[n] = tok_ok[n] ? a.q_scale_tok[(int64_t)qi[n] * Lq + s_tok] : 0.f;
         }
 
         // ---- Q fragments (B operand), kept in VGPRs for the whole range -----
@@ -361,15 +392,16 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     argmax_merge(mv, iv, om, oi);
                     if (!finite_score(mv)) iv = 0;
                     if (h == 0 && tok_ok[n])
-                        a.argmax[((int64_t)qi[n] * Nd + doc) * Lq + (int64_t)ntl[n] * 32 + col] = iv;
+                        a.argmax[out_pair(qi[n], doc) * Lq + (int64_t)ntl[n] * 32 + col] = iv;
                 } else {
                     mv = mv > om ? mv : om;
                 }
+                if constexpr (TOK) mv = qsc[n] * mv;  // positive: keeps the max and -inf
                 V contrib = (keep_row[n] && finite_score(mv)) ? mv : (V)0;
                 // fixed-order butterfly over the 32 query tokens of the N-tile
 #pragma unroll
                 for (int off = 16; off >= 1; off >>= 1) {
-                    if constexpr (E == kI8)
+                    if constexpr (std::is_integral_v<V>)
                         contrib += shfl_xor_i(contrib, off);
                     else
                         contrib += shfl_xor_f(contrib, off);
@@ -394,7 +426,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             if (q < nq && n < cnt)
                 v = __builtin_bit_cast(V, lds_load_b32(part_base + (uint32_t)(((k & 1) * SLOTS + q * cnt + n) * 4)));
             for (int off = P >> 1; off >= 1; off >>= 1) {
-                if constexpr (E == kI8)
+                if constexpr (std::is_integral_v<V>)
                     v += shfl_xor_i(v, off);
                 else
                     v += shfl_xor_f(v, off);
@@ -403,19 +435,20 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             if (a.npass == 1) {
                 const int64_t i = (int64_t)qb * a.qpw + q;
                 if (i < a.Nq) {
-                    if constexpr (E == kI8) {
-                        if (a.scores_i32) a.scores_i32[i * Nd + doc] = v;
-                        if (a.scores) a.scores[i * Nd + doc] = (float)(((double)v * a.q_scale) * a.d_scale);
+                    const int64_t o = out_pair(i, doc);
+                    if constexpr (std::is_integral_v<V>) {
+                        if (a.scores_i32) a.scores_i32[o] = v;
+                        if (a.scores) a.scores[o] = (float)(((double)v * a.q_scale) * a.d_scale);
                     } else {
-                        a.scores[i * Nd + doc] = v;
+                        a.scores[o] = v;
                     }
                 }
             } else {
                 // one long query: this pass's sum is added to the running sum
                 // kept in the output (pass 0 starts it)
-                const int64_t o = (int64_t)qb * Nd + doc;
+                const int64_t o = out_pair(qb, doc);
                 const bool last = pass + 1 == a.npass;
-                if constexpr (E == kI8) {
+                if constexpr (std::is_integral_v<V>) {
                     // the int32 running sum lives in scores_i32 when it exists,
                     // else in the float output's bits until the last pass
                     int32_t* run = a.scores_i32 ? a.scores_i32 : (int32_t*)a.scores;
@@ -481,7 +514,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 }
             }
 
-            if (f + 1 < F) wait_vmcnt<LPS>();
+            if (f + 1 < F) wait_vmcnt<LPW>();
             else wait_vmcnt<0>();
             block_barrier();  // tile f landed for everyone; stage (f+2)%3 is free
             if (f + 2 < F) {
@@ -511,6 +544,35 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     for (int s = 0; s < KS; ++s) acc = mfma32<E>(af[s], qf[n][s], acc);
                     return acc;
                 };
+                // doc-token scales of the lane's 16 rows of M-tile mt (TOK)
+                const float* scs = sc_buf + stage * kTileRows;
+                auto load_sc = [&](int mt, float (&sc)[16]) {
+                    if constexpr (TOK) {
+                        typedef float f4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const f4 v = *(const f4*)(scs + mt * 32 + 8 * g + 4 * h);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) sc[4 * g + e] = v[e];
+                        }
+                    }
+                };
+                // fold one accumulator tile; TOK first turns the integer dot
+                // products into scaled floats
+                auto fold = [&](const Acc& acc, RowState<V, ARGMAX>& stn, int base, const float (&sc)[16],
+                                auto maskedc, uint32_t lbits) {
+                    constexpr bool MASKED = decltype(maskedc)::value;
+                    if constexpr (TOK) {
+                        F16v sv;
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) sv[q] = (float)acc[q] * sc[q];
+                        fold_one<V, ARGMAX, MASKED>(sv, stn, base, lbits);
+                    } else {
+                        fold_one<V, ARGMAX, MASKED>(acc, stn, base, lbits);
+                    }
+                };
+                using NoMask = std::false_type;
+                using Masked = std::true_type;
                 if ((vb[0] & vb[1]) == ~0ull) {
                     // every row valid: the (M-tile, N-tile) units in order,
                     // software-pipelined: the MFMAs of unit u are issued before
@@ -519,6 +581,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     // unit of the current one
                     constexpr int U = 4 * NTW;
                     i32x4 afA[KS], afB[KS];
+                    float scA[16], scB[16];
                     Acc accs[2];
                     load_a(0, afA);
                     static_for<0, U>([&](auto uc) {
@@ -527,14 +590,19 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                         i32x4(&cur)[KS] = (mt & 1) ? afB : afA;
                         i32x4(&nxt)[KS] = (mt & 1) ? afA : afB;
                         if constexpr (n == 0 && mt + 1 < 4) load_a(mt + 1, nxt);
+                        // the scales of M-tile mt are first needed by the fold
+                        // of its first unit, one step later; the other buffer
+                        // still serves the fold of M-tile mt - 1 in this step
+                        if constexpr (n == 0) load_sc(mt, (mt & 1) ? scB : scA);
                         accs[u & 1] = mma(cur, n);
                         if constexpr (u > 0) {
-                            constexpr int pu = u - 1;
-                            fold_one<V, ARGMAX, false>(accs[pu & 1], st[pu % NTW], (int)(t0 + (pu / NTW) * 32), 0u);
+                            constexpr int pu = u - 1, pmt = pu / NTW;
+                            fold(accs[pu & 1], st[pu % NTW], (int)(t0 + pmt * 32), (pmt & 1) ? scB : scA, NoMask{},
+                                 0u);
                         }
                     });
-                    constexpr int lu = U - 1;
-                    fold_one<V, ARGMAX, false>(accs[lu & 1], st[lu % NTW], (int)(t0 + (lu / NTW) * 32), 0u);
+                    constexpr int lu = U - 1, lmt = lu / NTW;
+                    fold(accs[lu & 1], st[lu % NTW], (int)(t0 + lmt * 32), (lmt & 1) ? scB : scA, NoMask{}, 0u);
                 } else {
                     // partial tile: M-tiles with no valid row are skipped
                     static_for<0, 4>([&](auto mc) {
@@ -542,15 +610,17 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                         const uint32_t mbits = (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
                         if (mbits == 0) return;
                         i32x4 af[KS];
+                        float sc[16];
                         load_a(mt, af);
+                        load_sc(mt, sc);
                         const int base = (int)(t0 + mt * 32);
 #pragma unroll
                         for (int n = 0; n < NTW; ++n) {
                             const Acc acc = mma(af, n);
                             if (mbits == 0xffffffffu)
-                                fold_one<V, ARGMAX, false>(acc, st[n], base, 0u);
+                                fold(acc, st[n], base, sc, NoMask{}, 0u);
                             else
-                                fold_one<V, ARGMAX, true>(acc, st[n], base, mbits >> (4 * h));
+                                fold(acc, st[n], base, sc, Masked{}, mbits >> (4 * h));
                         }
                     });
                 }
@@ -567,30 +637,36 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
-template <int E, bool ARGMAX, int NTW, bool READAHEAD>
+template <int E, bool ARGMAX, int NTW, bool TOK>
 static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
 {
     constexpr int SLOTS = kWaves * NTW;
     a.ntq = (int)((a.Lq + 31) / 32);
     if (a.ntq == 0) a.ntq = 1;
+    const bool pairs = a.pair_q != nullptr;
     if (a.ntq <= SLOTS) {
-        a.qpw = SLOTS / a.ntq;
+        a.qpw = pairs ? 1 : SLOTS / a.ntq;  // a pair is one query
         a.npass = 1;
     } else {
         a.qpw = 1;
         a.npass = (a.ntq + SLOTS - 1) / SLOTS;
     }
     a.nqb = (int)((a.Nq + a.qpw - 1) / a.qpw);
-    const int ncu = device_cu_count();
-    // doc ranges: enough workgroups to give every CU one, each range at least one doc
-    int64_t R = (ncu + a.nqb - 1) / a.nqb;
-    if (R > a.Nd) R = a.Nd;
-    if (R < 1) R = 1;
-    a.nranges = (int)R;
-    const int64_t units = (int64_t)a.nqb * R;
+    int64_t units;
+    if (pairs) {
+        units = a.npairs;
+    } else {
+        const int ncu = device_cu_count();
+        // doc ranges: enough workgroups to give every CU one, each range at least one doc
+        int64_t R = (ncu + a.nqb - 1) / a.nqb;
+        if (R > a.Nd) R = a.Nd;
+        if (R < 1) R = 1;
+        a.nranges = (int)R;
+        units = (int64_t)a.nqb * R;
+    }
     if (units <= 0) return hipSuccess;
     dim3 grid((unsigned)units), block(kWaves * 64);
-    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, READAHEAD>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, TOK>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
@@ -599,15 +675,18 @@ hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t
     switch (elem) {
     case kF16:
         return want_argmax ? launch_dense_t<kF16, true, 1, false>(a, stream)
-                           : launch_dense_t<kF16, false, 2, true>(a, stream);
+                           : launch_dense_t<kF16, false, 2, false>(a, stream);
     case kBF16:
         return want_argmax ? launch_dense_t<kBF16, true, 1, false>(a, stream)
-                           : launch_dense_t<kBF16, false, 2, true>(a, stream);
+                           : launch_dense_t<kBF16, false, 2, false>(a, stream);
     case kI8:
         // a 1024-token int8 query fits one workgroup (8 waves x 4 N-tiles);
         // with argmax the saved values only fit for 1 N-tile per wave
+        if (a.q_scale_tok)
+            return want_argmax ? launch_dense_t<kI8, true, 1, true>(a, stream)
+                               : launch_dense_t<kI8, false, 4, true>(a, stream);
         return want_argmax ? launch_dense_t<kI8, true, 1, false>(a, stream)
-                           : launch_dense_t<kI8, false, 4, true>(a, stream);
+                           : launch_dense_t<kI8, false, 4, false>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -11,10 +11,15 @@ struct DenseArgs {
     const void* D;
     const uint8_t* q_mask;  // [Nq, Lq] or null
     const uint8_t* d_mask;  // [Nd, Ld] or null
-    float* scores;          // [Nq, Nd] or null (int8 only)
-    int32_t* scores_i32;    // [Nq, Nd] or null (int8 only)
-    int32_t* argmax;        // [Nq, Nd, Lq] or null
+    float* scores;          // [Nq, Nd] ([npairs] with a pair list) or null (int8 only)
+    int32_t* scores_i32;    // [Nq, Nd] or null (int8 per-tensor only)
+    int32_t* argmax;        // [Nq, Nd, Lq] ([npairs, Lq] with a pair list) or null
     double q_scale, d_scale;  // int8 only
+    const float* q_scale_tok;  // [Nq, Lq] per-token scales (int8) or null
+    const float* d_scale_tok;  // [Nd, Ld]
+    const int32_t* pair_q;     // [npairs] pair list or null (score listed pairs only)
+    const int32_t* pair_d;
+    int64_t npairs;
     int64_t Nq, Nd, Lq, Ld;
     // filled by the launcher
     int ntq;      // 32-token N-tiles per query
@@ -50,11 +55,24 @@ struct BwdArgs {
     int64_t Nq, Nd, Lq, Ld;
 };
 
+struct TopkArgs {
+    const float* scores;  // [Nq, Nd]
+    int64_t Nq, Nd;
+    int K;
+    const int32_t* ids;  // [Nq, Nd] ids reported for each column, or null (the column)
+    int32_t* idx;        // [Nq, K]
+    float* val;          // [Nq, K]
+    int32_t* rows;       // [Nq, K] row index of each entry, or null
+};
+
+constexpr int kTopkMaxK = 1024;  // largest k of one top-k call
+
 // Compute units of the current device (queried once per device, thread-safe).
 int device_cu_count();
 
 hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t stream);
 hipError_t launch_fwd_varlen(int elem, VarlenArgs a, hipStream_t stream);
 hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream);
+hipError_t launch_topk(TopkArgs a, hipStream_t stream);
 
 }  // namespace maxsim

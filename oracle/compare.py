@@ -103,6 +103,35 @@ def dense_argmax_float(got, ref, Q64, D64, d_mask=None, pairs=None):
     return argmax_float(got, ref, qr, dr, ok)
 
 
+def pair_argmax_float(got, ref, Q64, D64, d_mask, pair_q, pair_d):
+    """argmax_float for a pair list; got/ref are [P, Lq] (pair p: query
+    pair_q[p] against doc pair_d[p])."""
+    Ld = D64.shape[1]
+    dm = None if d_mask is None else np.asarray(d_mask).astype(bool)
+    pq = np.asarray(pair_q)
+    pd = np.asarray(pair_d)
+
+    def qr(e):
+        return Q64[pq[e[0]], e[1]]
+
+    def dr(e, t):
+        if t < 0 or t >= Ld:
+            return None
+        return D64[pd[e[0]], t]
+
+    def ok(e, t):
+        if t < 0 or t >= Ld:
+            return False
+        if dm is None:
+            return True
+        j = pd[e[0]]
+        if not dm[j].any():
+            return False  # a doc with no valid token must report 0 exactly
+        return bool(dm[j, t])
+
+    return argmax_float(got, ref, qr, dr, ok)
+
+
 def varlen_argmax_float(got, ref, Q64, cu_q, D64, cu_d, q_index, d_index):
     """argmax_float for packed sequences; got/ref are [len(q_index), len(d_index), max_lq]."""
     cu_q = np.asarray(cu_q, dtype=np.int64)
@@ -126,3 +155,41 @@ def varlen_argmax_float(got, ref, Q64, cu_q, D64, cu_d, q_index, d_index):
         return 0 <= t < ld
 
     return argmax_float(got, ref, qr, dr, ok)
+
+
+U24 = 2.0 ** -24
+
+
+def int8_tok_argmax(got, ref, Q8, D8, d_scale, d_mask=None, pairs=None):
+    """Argmax check for per-token INT8 scores. The GPU ranks doc tokens by the
+    fp32 product fl(d_scale[t] * dot_t) of an exact integer dot product (one
+    rounding, relative error <= 2^-24); the oracle by the exact product (the
+    positive query scale does not change the order). A GPU index t_g != t_o
+    is accepted only if t_g is valid and
+        w(t_o) - w(t_g) <= 2^-24 * (|w(t_o)| + |w(t_g)|),  w(t) = d_scale[t] * dot_t.
+    got/ref are [Nq', Nd', Lq] over the query/doc lists `pairs = (I, J)`."""
+    Q8 = np.asarray(Q8, dtype=np.int64)
+    D8 = np.asarray(D8, dtype=np.int64)
+    ds = np.asarray(d_scale, dtype=np.float64)
+    dm = None if d_mask is None else np.asarray(d_mask)
+    I = np.arange(Q8.shape[0]) if pairs is None else np.asarray(pairs[0])
+    J = np.arange(D8.shape[0]) if pairs is None else np.asarray(pairs[1])
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    bad = []
+    acc = 0
+    mism = np.argwhere(got != ref)
+    for e in mism:
+        a, b, s = (int(x) for x in e)
+        i, j = int(I[a]), int(J[b])
+        tg, to = int(got[a, b, s]), int(ref[a, b, s])
+        if not (0 <= tg < D8.shape[1]) or (dm is not None and not dm[j, tg]):
+            bad.append(((a, b, s), tg, to, "masked or out-of-range token"))
+            continue
+        wo = ds[j, to] * float(Q8[i, s] @ D8[j, to])
+        wg = ds[j, tg] * float(Q8[i, s] @ D8[j, tg])
+        if wo - wg <= U24 * (abs(wo) + abs(wg)):
+            acc += 1
+        else:
+            bad.append(((a, b, s), tg, to, f"gap {wo - wg:.3e}"))
+    return len(mism), acc, bad

@@ -35,6 +35,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = _declared()
     assert set(names) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd",
+                          "maxsim_fwd_i8_tok", "maxsim_fwd_pairs", "maxsim_topk",
                           "maxsim_status_string", "maxsim_abi_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -131,6 +132,58 @@ def test_bwd_validation(L):
     assert call(ci=MIS2) == ERR_UNSUPPORTED
     assert call(Nq=0, Nd=0, Lq=0, Ld=0, Q=None, D=None, am=None, g=None, dQ=None, dD=None,
                 rp=None, ci=None) == OK
+
+
+def test_i8_tok_validation(L):
+    f = L.maxsim_fwd_i8_tok
+
+    def call(Q=FAKE, qs=FAKE, D=FAKE, ds=FAKE, Nq=2, Nd=3, Lq=4, Ld=5, d=128, sc=FAKE, am=None):
+        return f(Q, qs, D, ds, Nq, Nd, Lq, Ld, d, None, None, sc, am, None)
+
+    assert call(Lq=-1) == ERR_SHAPE
+    assert call(d=64) == ERR_UNSUPPORTED
+    assert call(sc=None) == ERR_NULL
+    assert call(qs=None) == ERR_NULL
+    assert call(ds=None) == ERR_NULL
+    assert call(D=MIS8) == ERR_UNSUPPORTED
+    assert call(qs=MIS2) == ERR_UNSUPPORTED
+    assert call(Nd=0, sc=None) == OK
+    assert call(Nq=1 << 16, Nd=1 << 15, Lq=2, am=FAKE) == ERR_OVERFLOW
+
+
+def test_pairs_validation(L):
+    f = L.maxsim_fwd_pairs
+
+    def call(dtype=0, Q=FAKE, D=FAKE, Nq=2, Nd=3, Lq=4, Ld=5, d=128, pq=FAKE, pd=FAKE, P=7,
+             sc=FAKE, am=None):
+        return f(dtype, Q, D, Nq, Nd, Lq, Ld, d, None, None, pq, pd, P, sc, am, None)
+
+    assert call(P=-1) == ERR_SHAPE
+    assert call(Nd=0) == ERR_SHAPE          # a pair needs a doc
+    assert call(P=0, Nd=0, pq=None) == OK   # nothing to score
+    assert call(dtype=5) == ERR_UNSUPPORTED
+    assert call(pq=None) == ERR_NULL
+    assert call(sc=None) == ERR_NULL
+    assert call(pd=MIS2) == ERR_UNSUPPORTED
+    assert call(Q=MIS8) == ERR_UNSUPPORTED
+    assert call(P=1 << 22, Lq=1 << 10, am=FAKE) == ERR_OVERFLOW
+
+
+def test_topk_validation(L):
+    f = L.maxsim_topk
+
+    def call(sc=FAKE, Nq=2, Nd=10, K=3, ids=None, idx=FAKE, val=FAKE, rows=None):
+        return f(sc, Nq, Nd, K, ids, idx, val, rows, None)
+
+    assert call(K=11) == ERR_SHAPE           # k > Nd
+    assert call(K=-1) == ERR_SHAPE
+    assert call(Nd=5000, K=1025) == ERR_UNSUPPORTED
+    assert call(K=0, idx=None, val=None) == OK
+    assert call(Nq=0) == OK
+    assert call(idx=None) == ERR_NULL
+    assert call(val=MIS2) == ERR_UNSUPPORTED
+    assert call(rows=MIS2) == ERR_UNSUPPORTED
+    assert call(Nq=1 << 31, Nd=1 << 31) == ERR_OVERFLOW
 
 
 def test_binding_refuses_cpu_tensors():

@@ -334,3 +334,126 @@ def test_bwd_full_size(ms, oracle_mod):
     w = synth.colpali_bf16()
     b = synth.colpali_backward(fwd=w)
     _check_bwd(ms, oracle_mod, w, b.argmax, b.grad_scores)
+
+
+# ------------------------------------------------ per-token INT8, top-k, pairs
+
+INT8_TOK_CASES = [
+    # (Nq, Nd, Lq, Ld, q_mask_p, d_mask_p, dead_docs)
+    (2, 5, 9, 13, 0.2, 0.2, 1),
+    (3, 4, 100, 130, 0.0, 0.3, 0),
+    (1, 3, 1024, 70, 0.1, 0.0, 0),     # 32 N-tiles: one pass of 8 waves x 4
+    (1, 2, 1100, 40, 0.0, 0.0, 0),     # past one workgroup: two passes (no int32 sum limit)
+    (4, 3, 32, 200, 0.0, 0.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", INT8_TOK_CASES, ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}")
+def test_int8_tok_small(ms, oracle_mod, case):
+    Nq, Nd, Lq, Ld, qp, dp, dead = case
+    _say(f"int8 per-token {case}")
+    w = synth.random_int8_tok(700 + Lq, Nq, Nd, Lq, Ld, q_mask_p=qp, d_mask_p=dp, dead_docs=dead)
+    s, a = ms.maxsim_fwd_i8_tok(_g(w.Q), _g(w.q_scale), _g(w.D), _g(w.d_scale), _g(w.q_mask),
+                                _g(w.d_mask), want_argmax=True)
+    s2, _ = ms.maxsim_fwd_i8_tok(_g(w.Q), _g(w.q_scale), _g(w.D), _g(w.d_scale), _g(w.q_mask),
+                                 _g(w.d_mask))
+    torch.cuda.synchronize()
+    rs, ra = oracle_mod.fwd_i8_tok(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    _assert_close("scores", s.cpu().numpy(), rs)
+    _assert_close("scores (no argmax)", s2.cpu().numpy(), rs)
+    n, acc, bad = compare.int8_tok_argmax(a.cpu().numpy(), ra, w.Q.numpy(), w.D.numpy(),
+                                          w.d_scale.numpy(),
+                                          None if w.d_mask is None else w.d_mask.numpy())
+    assert not bad, f"argmax mismatches outside the rounding bound: {bad[:5]}"
+
+
+def test_int8_tok_full_size_sampled(ms, oracle_mod):
+    """One 1024-token query against 10,000 docs of 1024 tokens with per-token
+    scales; the oracle scores 16 docs."""
+    _say("int8 per-token full size")
+    w = synth.two_stage_long_query()
+    s, _ = ms.maxsim_fwd_i8_tok(_g(w.Q), _g(w.q_scale), _g(w.D), _g(w.d_scale))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    docs = np.sort(np.concatenate([[0, 9999], rng.choice(np.arange(1, 9999), 14, replace=False)]))
+    rs, _ = oracle_mod.fwd_i8_tok(w.Q, w.q_scale, w.D[docs], w.d_scale[docs], want_argmax=False)
+    _assert_close("scores", s.cpu().numpy()[:, docs], rs)
+
+
+PAIR_CASES = [
+    # (Nq, Nd, Lq, Ld, dtype, P)
+    (3, 5, 40, 150, torch.bfloat16, 40),
+    (2, 7, 300, 130, torch.float16, 9),      # a query longer than one workgroup
+    (1, 4, 1024, 100, torch.bfloat16, 6),
+    (4, 3, 1, 1, torch.float16, 5),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}_p{c[5]}")
+def test_pairs(ms, oracle_mod, case):
+    Nq, Nd, Lq, Ld, dt, P = case
+    _say(f"pairs {case}")
+    w = synth.random_dense(800 + Lq, Nq, Nd, Lq, Ld, dtype=dt, q_mask_p=0.2, d_mask_p=0.2,
+                           dead_docs=1)
+    pq, pd = synth.random_pairs(800 + Lq, Nq, Nd, P)
+    s, a = ms.maxsim_fwd_pairs(_g(w.Q), _g(w.D), _g(pq), _g(pd), _g(w.q_mask), _g(w.d_mask),
+                               want_argmax=True)
+    torch.cuda.synchronize()
+    rs, ra = oracle_mod.fwd_pairs(w.Q, w.D, pq, pd, w.q_mask, w.d_mask)
+    _assert_close("scores", s.cpu().numpy(), rs)
+    n, acc, bad = compare.pair_argmax_float(a.cpu().numpy(), ra, w.Q.double().numpy(),
+                                            w.D.double().numpy(),
+                                            None if w.d_mask is None else w.d_mask.numpy(),
+                                            pq.numpy(), pd.numpy())
+    assert not bad, f"argmax mismatches outside the near-tie bound: {bad[:5]}"
+
+
+TOPK_CASES = [
+    # (Nq, Nd, k, ties)
+    (3, 1, 1, False),
+    (5, 300, 7, True),
+    (2, 5000, 100, False),
+    (4, 2048, 1024, True),      # the largest k
+    (1, 100000, 100, False),    # a reranking-size row
+    (6, 1000, 1000, False),     # k = Nd: a full sort
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=lambda c: f"{c[0]}x{c[1]}_k{c[2]}_ties{int(c[3])}")
+def test_topk(ms, oracle_mod, case):
+    Nq, Nd, k, ties = case
+    _say(f"topk {case}")
+    v = synth.random_scores(900 + k, Nq, Nd, ties=ties)
+    if Nd > 2:
+        v[0, 1] = -0.0   # -0 and +0 are equal and ordered by column
+        v[0, 2] = 0.0
+    idx, val, rows = ms.maxsim_topk(_g(v), k, want_rows=True)
+    ids = torch.arange(Nq * Nd, dtype=torch.int32).view(Nq, Nd) * 3 + 1
+    idx2, _, _ = ms.maxsim_topk(_g(v), k, ids=_g(ids))
+    torch.cuda.synchronize()
+    ri, rv = oracle_mod.topk(v, k)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    assert np.array_equal(val.cpu().numpy().view(np.int32), rv.astype(np.float32).view(np.int32))
+    assert np.array_equal(rows.cpu().numpy(), np.repeat(np.arange(Nq), k).reshape(Nq, k))
+    assert np.array_equal(idx2.cpu().numpy(), np.take_along_axis(ids.numpy(), ri.astype(np.int64), 1))
+
+
+def test_two_stage_scan(ms, oracle_mod):
+    """INT8 per-token scan of every doc, the best 12 docs as candidates, their
+    exact bf16 scores, the final top 5. With every doc a candidate the result
+    is the exact top 5; the oracle's gaps between consecutive scores of the top
+    6 are checked to be far above the fp32 rounding of these sums (about 1e-5)
+    before the order is compared."""
+    _say("two-stage scan")
+    Nq, Nd, Lq, Ld = 2, 12, 64, 150
+    w = synth.random_int8_tok(950, Nq, Nd, Lq, Ld, d_mask_p=0.1, float_dtype=torch.bfloat16)
+    doc, val, s8 = ms.two_stage_topk(_g(w.Q), _g(w.q_scale), _g(w.D), _g(w.d_scale), _g(w.Qf),
+                                     _g(w.Df), 5, Nd, None, _g(w.d_mask))
+    torch.cuda.synchronize()
+    rs, _ = oracle_mod.fwd(w.Qf, w.Df, None, w.d_mask, want_argmax=False)
+    ri, rv = oracle_mod.topk(rs, 6)
+    assert np.all(np.abs(np.diff(rv, axis=1)) > 1e-4), "seed gives near-ties; pick another"
+    assert np.array_equal(doc.cpu().numpy(), ri[:, :5])
+    _assert_close("scores", val.cpu().numpy(), rv[:, :5])
+    r8, _ = oracle_mod.fwd_i8_tok(w.Q, w.q_scale, w.D, w.d_scale, None, w.d_mask, want_argmax=False)
+    _assert_close("int8 stage scores", s8.cpu().numpy(), r8)
