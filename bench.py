@@ -214,6 +214,54 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
             "kernels": ["csr_kernel", "dq_kernel", "dd_kernel"]}
 
 
+def bench_two_stage(torch, ms, synth, wl, steps, warmup):
+    """The INT8 -> FP16 top-K scan on the long-query corpus (1 query of 1024
+    tokens, 10,000 docs of 1024 tokens): per-token INT8 scores of every doc,
+    100 candidates, their exact fp16 scores, the final top 10. Reports the
+    per-token INT8 scan alone (MFMA roofline) and the whole scan."""
+    w = synth.two_stage_long_query()
+    Q8, qs, D8, ds = (t.cuda() for t in (w.Q, w.q_scale, w.D, w.d_scale))
+    Qf, Df = w.Qf.cuda(), w.Df.cuda()
+    del w
+    s8 = torch.empty((1, 10_000), dtype=torch.float32, device="cuda")
+
+    def scan():
+        ms.maxsim_fwd_i8_tok(Q8, qs, D8, ds, scores=s8)
+
+    total, _ = time_steps(torch, scan, steps, warmup)
+    t_scan = total / steps
+    ops = 2 * 128 * 1024 * 1024 * 10_000
+
+    def pipeline():
+        ms.two_stage_topk(Q8, qs, D8, ds, Qf, Df, 10, 100)
+
+    total, _ = time_steps(torch, pipeline, steps, warmup)
+    t_all = total / steps
+    return {"workload": "int8tok_1x10000_lq1024_ld1024_top100_rescore_fp16_top10",
+            "ms": t_all, "docs_per_s": 10_000 / (t_all * 1e-3),
+            "int8_scan_ms": t_scan,
+            "roofline": roofline("mfma", ops / (t_scan * 1e-3) / 1e12, INT8_PEAK_TOPS, "TOP/s"),
+            "note": "roofline is the per-token INT8 scan kernel; ms is the whole four-call scan",
+            "kernel": "fwd_dense_kernel (per-token int8), topk_kernel, fwd_dense_kernel (pairs)"}
+
+
+def bench_topk(torch, ms, synth, wl, steps, warmup):
+    """Top-100 of one row of 100,000 scores (the reranking workload's output)."""
+    v = synth.random_scores(7, 1, 100_000).cuda()
+    idx = torch.empty((1, 100), dtype=torch.int32, device="cuda")
+    val = torch.empty((1, 100), dtype=torch.float32, device="cuda")
+
+    def step():
+        ms.maxsim_topk(v, 100, idx=idx, val=val)
+
+    total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
+    t = statistics.median(times)
+    nbytes = 100_000 * 4
+    return {"workload": "topk_1x100000_k100", "ms": t,
+            "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+            "note": "one workgroup per row: threshold from a leading sample, one filtering pass, select and sort in LDS", "kernel": "topk_kernel"}
+
+
 def bench_copy(torch, ms, synth, wl, steps, warmup):
     """A plain 1 GiB device-to-device copy: the reference kernel that the HBM
     byte counters are calibrated against (it must read and write 1 GiB)."""
@@ -269,7 +317,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="",
-                    help="run one workload: rerank|tiny|colpali|int8|backward|copy")
+                    help="run one workload: rerank|tiny|colpali|int8|backward|two_stage|topk|copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -286,9 +334,11 @@ def main() -> int:
         return 2
     ms.binding.lib()  # fails loudly without the built library
 
-    names = [args.only] if args.only else [HEADLINE, "tiny", "colpali", "int8", "backward"]
+    names = [args.only] if args.only else [HEADLINE, "tiny", "colpali", "int8", "backward",
+                                           "two_stage", "topk"]
     fns = {"rerank": bench_rerank, "tiny": bench_tiny, "colpali": bench_colpali,
-           "int8": bench_int8, "backward": bench_backward, "copy": bench_copy}
+           "int8": bench_int8, "backward": bench_backward, "two_stage": bench_two_stage,
+           "topk": bench_topk, "copy": bench_copy}
     per = {}
     head = None
     head_w = None

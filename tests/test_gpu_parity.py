@@ -416,6 +416,7 @@ TOPK_CASES = [
     (4, 2048, 1024, True),      # the largest k
     (1, 100000, 100, False),    # a reranking-size row
     (6, 1000, 1000, False),     # k = Nd: a full sort
+    (2, 20000, 50, True),       # row 1 constant: too many candidates, exact radix path
 ]
 
 
@@ -427,6 +428,8 @@ def test_topk(ms, oracle_mod, case):
     if Nd > 2:
         v[0, 1] = -0.0   # -0 and +0 are equal and ordered by column
         v[0, 2] = 0.0
+    if Nq > 1 and Nd >= 20000:
+        v[1, :] = 1.0    # every column ties
     idx, val, rows = ms.maxsim_topk(_g(v), k, want_rows=True)
     ids = torch.arange(Nq * Nd, dtype=torch.int32).view(Nq, Nd) * 3 + 1
     idx2, _, _ = ms.maxsim_topk(_g(v), k, ids=_g(ids))
