@@ -190,6 +190,13 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p)
     return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+__device__ __forceinline__ int64_t uniform_i64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {

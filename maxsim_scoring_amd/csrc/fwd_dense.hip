@@ -26,6 +26,14 @@
 // valid row skip their MFMAs. Per-doc partial sums of the N-tiles of a query
 // meet in LDS and are added in slot order, so the result does not depend on
 // timing.
+//
+// Argmax: a lane keeps its running max and the row base of the M-tile that
+// last raised it; when an M-tile raises it, the lane's 16 values of that
+// M-tile are stored to a per-lane LDS slot (an exec-masked store, so lanes
+// whose max did not change issue nothing). At the end of the doc the lowest
+// saved row holding the max is the argmax. Keeping the saved values in LDS
+// rather than selecting them into registers takes the 16 selects per value
+// tile off the VALU, which shares its issue port with the MFMAs.
 #include <type_traits>
 
 #include "common.hpp"
@@ -36,7 +44,6 @@ namespace maxsim {
 namespace {
 
 constexpr int kTileRows = 128;  // doc tokens per pipeline stage (4 MFMA M-tiles)
-constexpr int kStages = 3;
 constexpr int kWaves = 8;
 constexpr int kMaskWords = 2048;  // 16 KB of LDS: d_mask bits of a doc range
 
@@ -127,13 +134,12 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
-// Running state of one N-tile for the lane's 16 rows of each M-tile.
-// Without argmax it is the running max only. With argmax the lane also keeps
-// the 16 values of the M-tile that last raised its max and that M-tile's row
-// base: a strict '>' across M-tiles (ascending t) keeps the earlier tile on
-// ties, and at the end of the doc the lowest row of the saved tile holding
-// the max is the argmax. This costs about 1.7 VALU ops per value instead of a
-// compare-and-select chain through every value.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Running state of one N-tile for the lane's 16 rows of each M-tile: the
+// running max and, with argmax, the row base of the M-tile that last raised
+// it (a strict '>' across M-tiles in ascending t keeps the earlier one on
+// ties). That M-tile's 16 values sit in the lane's LDS slot.
 template <typename V, bool ARGMAX> struct RowState;
 template <typename V> struct RowState<V, false> {
     V m;
@@ -142,7 +148,6 @@ template <typename V> struct RowState<V, false> {
 template <typename V> struct RowState<V, true> {
     V m;
     int tbase;
-    V sv[16];
     __device__ __forceinline__ void reset()
     {
         m = neg_inf<V>();
@@ -173,10 +178,11 @@ __device__ __forceinline__ V max16(const V (&v)[16])
 }
 
 // Fold one 32x32 accumulator tile (M-tile rows starting at `base`) into the
-// state of its N-tile. `lbits` bit r = lane row r (+4h) valid.
+// state of its N-tile. `lbits` bit r = lane row r (+4h) valid. `save` is the
+// lane's LDS slot (4 chunks of 16 bytes, 64 lanes apart).
 template <typename V, bool ARGMAX, bool MASKED, typename Acc>
 __device__ __forceinline__ void fold_one(const Acc& acc, RowState<V, ARGMAX>& st, int base,
-                                         uint32_t lbits)
+                                         uint32_t lbits, u32x4* save)
 {
     V v[16];
     masked_values<V, Acc, MASKED>(acc, lbits, v);
@@ -185,21 +191,36 @@ __device__ __forceinline__ void fold_one(const Acc& acc, RowState<V, ARGMAX>& st
         const bool upd = tm > st.m;
         st.m = upd ? tm : st.m;
         st.tbase = upd ? base : st.tbase;
+        if (upd) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) st.sv[q] = upd ? v[q] : st.sv[q];
+            for (int c = 0; c < 4; ++c)
+                save[64 * c] = u32x4{__builtin_bit_cast(uint32_t, v[4 * c]), __builtin_bit_cast(uint32_t, v[4 * c + 1]),
+                                     __builtin_bit_cast(uint32_t, v[4 * c + 2]),
+                                     __builtin_bit_cast(uint32_t, v[4 * c + 3])};
+        }
     } else {
+        (void)save;
         st.m = vmax(st.m, tm);
     }
 }
 
-// Lane-local argmax of the doc: lowest row of the saved tile equal to the max
-// (row offset without the 4h term), or 0 when nothing valid was seen.
+// Lane-local argmax of the doc: lowest row of the saved M-tile equal to the
+// max (row offset without the 4h term); only meaningful when the max is
+// finite, i.e. when the slot was written for this doc.
 template <typename V>
-__device__ __forceinline__ int saved_argmax(const RowState<V, true>& st)
+__device__ __forceinline__ int saved_argmax(const RowState<V, true>& st, const u32x4* save)
 {
-    int qs = 0;
+    // the chunk is copied to a plain array before the compares: indexing the
+    // vector value directly inside the unrolled loop was compiled (ROCm 7.2)
+    // into a compare of element 0 only
+    int qs = 15;
 #pragma unroll
-    for (int q = 15; q >= 0; --q) qs = st.sv[q] == st.m ? q : qs;
+    for (int c = 3; c >= 0; --c) {
+        const u32x4 w = save[64 * c];
+        const uint32_t wv[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int e = 3; e >= 0; --e) qs = __builtin_bit_cast(V, wv[e]) == st.m ? 4 * c + e : qs;
+    }
     return st.tbase + 8 * (qs >> 2) + (qs & 3);
 }
 
@@ -209,7 +230,7 @@ __device__ __forceinline__ int saved_argmax(const RowState<V, true>& st)
 // integer dot product before the max (a float per score); the query-token
 // scale (positive) is applied to the max. The tile's doc scales are staged in
 // LDS with the tile.
-template <int E, bool ARGMAX, int NTW, bool TOK>
+template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES>
 __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 {
     static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
@@ -227,13 +248,16 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     constexpr int LPS = CHUNKS / THREADS;  // direct-to-LDS loads per thread per stage
     constexpr int LPW = LPS + (TOK ? 1 : 0);  // direct-to-LDS loads per wave per stage
     static_assert(CHUNKS % THREADS == 0, "stage must split evenly over the workgroup");
+    static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
-    __shared__ __attribute__((aligned(16))) unsigned char stage_buf[kStages * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char stage_buf[STAGES * STAGE_BYTES];
     __shared__ V part[2][SLOTS];
     // d_mask of the whole doc range as bits, when it fits: 2 words per tile
-    __shared__ __attribute__((aligned(16))) uint64_t mask_lds[kMaskWords];
+    __shared__ __attribute__((aligned(16))) uint16_t mask_lds[4 * kMaskWords];
     // doc-token scales of each stage's tile (TOK)
-    __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? kStages * kTileRows : 4];
+    __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? STAGES * kTileRows : 4];
+    // argmax: each lane's saved M-tile values, per (wave, N-tile): 4 chunks x 64 lanes
+    __shared__ __attribute__((aligned(16))) u32x4 save_buf[ARGMAX ? kWaves * NTW * 256 : 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -264,6 +288,11 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
         d0 = r * Nd / a.nranges;
         d1 = (r + 1) * Nd / a.nranges;
     }
+    // the range is uniform; the 64-bit division above runs on the vector unit,
+    // so move the results back to scalar registers, which keeps everything
+    // derived from them (cursors, tile pointers, mask words) scalar
+    d0 = uniform_i64(d0);
+    d1 = uniform_i64(d1);
     if (d0 >= d1) return;  // uniform over the workgroup
     // where the results of (query i, doc j) go
     auto out_pair = [&](int64_t i, int64_t j) -> int64_t { return pairs ? (int64_t)unit : i * Nd + j; };
@@ -274,13 +303,11 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 
     // per-lane byte offsets: LDS slot p = (row p / NCH, chunk p % NCH) of a
     // stage holds logical chunk swz(row, p % NCH) of that row
-    int dma_off[LPS], dma_row[LPS], dma_lc[LPS];
+    int dma_off[LPS];
 #pragma unroll
     for (int u = 0; u < LPS; ++u) {
         const int p = (wave * LPS + u) * 64 + lane;
-        dma_row[u] = p / NCH;
-        dma_lc[u] = swz_chunk<RB>(dma_row[u], p % NCH);
-        dma_off[u] = dma_row[u] * RB + dma_lc[u] * 16;
+        dma_off[u] = (p / NCH) * RB + swz_chunk<RB>(p / NCH, p % NCH) * 16;
     }
     // A-fragment offsets of M-tile 0 (row = lane % 32, logical chunk 2s + h);
     // M-tile mt adds mt * 32 rows (the swizzle only depends on row % 16)
@@ -299,15 +326,13 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
         const void* Dt = uniform_ptr((const unsigned char*)a.D + (doc * Ld + t0) * RB);
         const int rows = Ld - t0 >= kTileRows ? kTileRows : (int)(Ld - t0);  // >= 1
         const uint32_t lds0 = ring_base + (uint32_t)(stage * STAGE_BYTES + wave_u * LPS * 1024);
-        if (rows == kTileRows) {
+        // rows past the doc end read its last row's final chunk instead; they
+        // are never folded (their validity bits are 0)
+        const uint32_t lim = (uint32_t)(rows * RB - 16);
 #pragma unroll
-            for (int u = 0; u < LPS; ++u) dma_lds16(Dt, (uint32_t)dma_off[u], lds0 + u * 1024);
-        } else {  // past the doc end: re-read its last row (masked out)
-#pragma unroll
-            for (int u = 0; u < LPS; ++u) {
-                const int row = dma_row[u] < rows ? dma_row[u] : rows - 1;
-                dma_lds16(Dt, (uint32_t)(row * RB + dma_lc[u] * 16), lds0 + u * 1024);
-            }
+        for (int u = 0; u < LPS; ++u) {
+            const uint32_t o = (uint32_t)dma_off[u];
+            dma_lds16(Dt, o < lim ? o : lim, lds0 + u * 1024);
         }
         if constexpr (TOK) {  // rows 16 w .. 16 w + 15 of the tile's doc scales
             const void* St = uniform_ptr(a.d_scale_tok + doc * Ld + t0);
@@ -322,13 +347,26 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     const int wpd = 2 * ntd;  // mask words per doc
     const bool mask_in_lds = a.d_mask && (d1 - d0) * (int64_t)wpd <= kMaskWords;
     if (mask_in_lds) {
-        const int nwords = (int)((d1 - d0) * wpd);
-        for (int wd = wave; wd < nwords; wd += kWaves) {
-            const int64_t doc = d0 + wd / wpd;
-            const int64_t t = (int64_t)(wd % wpd) * 64 + lane;
-            const bool v = t < Ld && a.d_mask[doc * Ld + t] != 0;
-            const uint64_t bits = __ballot(v);
-            if (lane == 0) mask_lds[wd] = bits;
+        // each thread turns 16 consecutive mask bytes of one doc into 16 bits
+        // (a quarter of a mask word); all loads of a round are in flight together
+        const int spd = 4 * wpd;  // 16-token slots per doc
+        const int nslots = (int)((d1 - d0) * spd);
+        for (int sl = tid; sl < nslots; sl += THREADS) {
+            const int64_t doc = d0 + sl / spd;
+            const int64_t t = (int64_t)(sl % spd) * 16;
+            uint32_t bits = 0;
+            if (t < Ld) {
+                const uint8_t* p = a.d_mask + doc * Ld + t;
+                const int nb = Ld - t >= 16 ? 16 : (int)(Ld - t);
+                if (nb == 16 && ((uintptr_t)p & 15u) == 0) {
+                    const i32x4 v = *(const i32x4*)p;
+                    bits = byte_flags(v[0]) | (byte_flags(v[1]) << 4) | (byte_flags(v[2]) << 8) |
+                           (byte_flags(v[3]) << 12);
+                } else {
+                    for (int i = 0; i < nb; ++i) bits |= (p[i] != 0 ? 1u : 0u) << i;
+                }
+            }
+            mask_lds[sl] = (uint16_t)bits;
         }
         __builtin_amdgcn_s_waitcnt(0);
         block_barrier();
@@ -377,6 +415,8 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
         wait_vmcnt<0>();  // Q and the q_mask bytes have landed before the pipeline
 
         RowState<V, ARGMAX> st[NTW];
+        // this lane's LDS slot for the saved values of N-tile n
+        auto save_slot = [&](int n) -> u32x4* { return &save_buf[ARGMAX ? (wave * NTW + n) * 256 + lane : 0]; };
 
         // finish doc `doc` (ordinal `k` in the range): merge the lane halves,
         // apply q_mask, write argmax, put per-N-tile sums into part[k & 1]
@@ -385,7 +425,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             for (int n = 0; n < NTW; ++n) {
                 V mv = st[n].m;
                 int iv = 0;
-                if constexpr (ARGMAX) iv = saved_argmax(st[n]) + 4 * h;
+                if constexpr (ARGMAX) iv = saved_argmax(st[n], save_slot(n)) + 4 * h;
                 const V om = __builtin_bit_cast(V, shfl_xor_i(__builtin_bit_cast(int, mv), 32));
                 if constexpr (ARGMAX) {
                     const int oi = shfl_xor_i(iv, 32);
@@ -474,8 +514,8 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             continue;
         }
 
-        // issue cursor (doc ordinal ik, tile it) runs two tiles ahead of the
-        // compute cursor (k, tt); both advance one tile per iteration
+        // issue cursor (doc ordinal ik, tile it) runs STAGES - 1 tiles ahead
+        // of the compute cursor (k, tt); both advance one tile per iteration
         int64_t ik = 0;
         int it = 0;
         auto advance = [&](int64_t& kk, int& t) {
@@ -484,11 +524,12 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 ++kk;
             }
         };
-        issue(d0 + ik, it, 0);
-        advance(ik, it);
-        if (F > 1) {
-            issue(d0 + ik, it, 1);
-            advance(ik, it);
+#pragma unroll
+        for (int q = 0; q < STAGES - 1; ++q) {
+            if (q < F) {
+                issue(d0 + ik, it, q);
+                advance(ik, it);
+            }
         }
 
         int stage = 0;
@@ -514,11 +555,21 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 }
             }
 
-            if (f + 1 < F) wait_vmcnt<LPW>();
-            else wait_vmcnt<0>();
-            block_barrier();  // tile f landed for everyone; stage (f+2)%3 is free
-            if (f + 2 < F) {
-                issue(d0 + ik, it, stage == 0 ? 2 : stage - 1);
+            // tile f has landed once at most STAGES - 2 later tiles are in flight
+            const int64_t ahead = F - 1 - f;  // tiles issued after f (capped below)
+            if constexpr (STAGES >= 4) {
+                if (ahead >= 2) wait_vmcnt<2 * LPW>();
+                else if (ahead == 1) wait_vmcnt<LPW>();
+                else wait_vmcnt<0>();
+            } else if constexpr (STAGES == 3) {
+                if (ahead >= 1) wait_vmcnt<LPW>();
+                else wait_vmcnt<0>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            block_barrier();  // tile f landed for everyone; the stage of tile f - 1 is free
+            if (f + STAGES - 1 < F) {
+                issue(d0 + ik, it, stage == 0 ? STAGES - 1 : stage - 1);
                 advance(ik, it);
             }
 
@@ -538,10 +589,16 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 #pragma unroll
                     for (int s = 0; s < KS; ++s) af[s] = *(const i32x4*)(sb + frag_off[s] + mt * 32 * RB);
                 };
-                auto mma = [&](const i32x4 (&af)[KS], int n) {
-                    Acc acc = Acc{};
+                // the MFMAs of (M-tile in af, N-tile n); with next >= 0, each
+                // fragment is replaced by that of M-tile `next` as soon as its
+                // MFMA has been issued (a rolling prefetch of the next M-tile)
+                auto mma = [&](i32x4 (&af)[KS], int n, int next, const Acc& init) {
+                    Acc acc = init;
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) acc = mfma32<E>(af[s], qf[n][s], acc);
+                    for (int s = 0; s < KS; ++s) {
+                        acc = mfma32<E>(af[s], qf[n][s], acc);
+                        if (next >= 0) af[s] = *(const i32x4*)(sb + frag_off[s] + next * 32 * RB);
+                    }
                     return acc;
                 };
                 // doc-token scales of the lane's 16 rows of M-tile mt (TOK)
@@ -559,74 +616,80 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 };
                 // fold one accumulator tile; TOK first turns the integer dot
                 // products into scaled floats
-                auto fold = [&](const Acc& acc, RowState<V, ARGMAX>& stn, int base, const float (&sc)[16],
-                                auto maskedc, uint32_t lbits) {
+                auto fold = [&](const Acc& acc, int n, int base, int mt, auto maskedc, uint32_t lbits) {
                     constexpr bool MASKED = decltype(maskedc)::value;
                     if constexpr (TOK) {
+                        float sc[16];
+                        load_sc(mt, sc);
                         F16v sv;
 #pragma unroll
                         for (int q = 0; q < 16; ++q) sv[q] = (float)acc[q] * sc[q];
-                        fold_one<V, ARGMAX, MASKED>(sv, stn, base, lbits);
+                        fold_one<V, ARGMAX, MASKED>(sv, st[n], base, lbits, save_slot(n));
                     } else {
-                        fold_one<V, ARGMAX, MASKED>(acc, stn, base, lbits);
+                        fold_one<V, ARGMAX, MASKED>(acc, st[n], base, lbits, save_slot(n));
                     }
                 };
-                using NoMask = std::false_type;
-                using Masked = std::true_type;
-                if ((vb[0] & vb[1]) == ~0ull) {
-                    // every row valid: the (M-tile, N-tile) units in order,
-                    // software-pipelined: the MFMAs of unit u are issued before
-                    // the fold of unit u - 1, so the two execute together, and
-                    // the next M-tile's fragments are read during the first
-                    // unit of the current one
+                // validity bits of the 32 rows of M-tile mt
+                const uint32_t mb[4] = {(uint32_t)vb[0], (uint32_t)(vb[0] >> 32), (uint32_t)vb[1],
+                                        (uint32_t)(vb[1] >> 32)};
+                // The (M-tile, N-tile) units of the tile in order, software-
+                // pipelined: the MFMAs of unit u are issued before the fold of
+                // unit u - 1, so the two execute together, and the last unit of
+                // an M-tile reads the next M-tile's fragments behind its MFMAs.
+                // FULL (every row valid) has no mask work at all; otherwise
+                // M-tiles with no valid row skip their MFMAs and fold, and
+                // partly valid ones fold with -inf in their invalid rows.
+                auto run_tile = [&](auto fullc) {
+                    constexpr bool FULL = decltype(fullc)::value;
                     constexpr int U = 4 * NTW;
-                    i32x4 afA[KS], afB[KS];
-                    float scA[16], scB[16];
+                    i32x4 af[KS];
                     Acc accs[2];
-                    load_a(0, afA);
+                    load_a(0, af);
+                    // 16-bit inputs: the invalid rows of a partly valid M-tile
+                    // start their accumulation at -inf (the MFMA adds finite
+                    // products to it, so they stay -inf) and need no select in
+                    // the fold; int8 and per-token scales select in the fold
+                    constexpr bool BIAS = !TOK && E != kI8;
+                    Acc binit = Acc{};
+                    auto mask_bias = [&](int mt) {
+                        Acc b;
+                        const uint32_t lb = mb[mt] >> (4 * h);
+#pragma unroll
+                        for (int q = 0; q < 16; ++q)
+                            b[q] = ((lb >> (8 * (q >> 2) + (q & 3))) & 1u) ? 0.f : -__builtin_inff();
+                        return b;
+                    };
+                    auto fold_unit = [&](auto puc) {
+                        constexpr int pu = decltype(puc)::value, pmt = pu / NTW;
+                        const int base = (int)(t0 + pmt * 32);
+                        if constexpr (FULL) {
+                            fold(accs[pu & 1], pu % NTW, base, pmt, std::false_type{}, 0u);
+                        } else if constexpr (BIAS) {
+                            if (mb[pmt] != 0) fold(accs[pu & 1], pu % NTW, base, pmt, std::false_type{}, 0u);
+                        } else {
+                            if (mb[pmt] == 0xffffffffu)
+                                fold(accs[pu & 1], pu % NTW, base, pmt, std::false_type{}, 0u);
+                            else if (mb[pmt] != 0)
+                                fold(accs[pu & 1], pu % NTW, base, pmt, std::true_type{}, mb[pmt] >> (4 * h));
+                        }
+                    };
                     static_for<0, U>([&](auto uc) {
                         constexpr int u = decltype(uc)::value;
                         constexpr int mt = u / NTW, n = u % NTW;
-                        i32x4(&cur)[KS] = (mt & 1) ? afB : afA;
-                        i32x4(&nxt)[KS] = (mt & 1) ? afA : afB;
-                        if constexpr (n == 0 && mt + 1 < 4) load_a(mt + 1, nxt);
-                        // the scales of M-tile mt are first needed by the fold
-                        // of its first unit, one step later; the other buffer
-                        // still serves the fold of M-tile mt - 1 in this step
-                        if constexpr (n == 0) load_sc(mt, (mt & 1) ? scB : scA);
-                        accs[u & 1] = mma(cur, n);
-                        if constexpr (u > 0) {
-                            constexpr int pu = u - 1, pmt = pu / NTW;
-                            fold(accs[pu & 1], st[pu % NTW], (int)(t0 + pmt * 32), (pmt & 1) ? scB : scA, NoMask{},
-                                 0u);
-                        }
+                        constexpr int next = (n == NTW - 1 && mt + 1 < 4) ? mt + 1 : -1;
+                        if constexpr (!FULL && BIAS && n == 0)
+                            if (mb[mt] != 0) binit = mb[mt] == 0xffffffffu ? Acc{} : mask_bias(mt);
+                        if (FULL || mb[mt] != 0) accs[u & 1] = mma(af, n, next, (FULL || !BIAS) ? Acc{} : binit);
+                        else if constexpr (next >= 0) load_a(next, af);
+                        if constexpr (u > 0) fold_unit(std::integral_constant<int, u - 1>{});
                     });
-                    constexpr int lu = U - 1, lmt = lu / NTW;
-                    fold(accs[lu & 1], st[lu % NTW], (int)(t0 + lmt * 32), (lmt & 1) ? scB : scA, NoMask{}, 0u);
-                } else {
-                    // partial tile: M-tiles with no valid row are skipped
-                    static_for<0, 4>([&](auto mc) {
-                        constexpr int mt = decltype(mc)::value;
-                        const uint32_t mbits = (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
-                        if (mbits == 0) return;
-                        i32x4 af[KS];
-                        float sc[16];
-                        load_a(mt, af);
-                        load_sc(mt, sc);
-                        const int base = (int)(t0 + mt * 32);
-#pragma unroll
-                        for (int n = 0; n < NTW; ++n) {
-                            const Acc acc = mma(af, n);
-                            if (mbits == 0xffffffffu)
-                                fold(acc, st[n], base, sc, NoMask{}, 0u);
-                            else
-                                fold(acc, st[n], base, sc, Masked{}, mbits >> (4 * h));
-                        }
-                    });
-                }
+                    fold_unit(std::integral_constant<int, U - 1>{});
+                };
+                if ((vb[0] & vb[1]) == ~0ull) run_tile(std::true_type{});
+                else run_tile(std::false_type{});
             }
             if (tt == ntd - 1) finish_doc(doc, k);
-            stage = stage == 2 ? 0 : stage + 1;
+            stage = stage == STAGES - 1 ? 0 : stage + 1;
         }
         block_barrier();
         write_scores(d1 - 1, d1 - 1 - d0);
@@ -637,7 +700,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
-template <int E, bool ARGMAX, int NTW, bool TOK>
+template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES>
 static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
 {
     constexpr int SLOTS = kWaves * NTW;
@@ -666,27 +729,29 @@ static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
     }
     if (units <= 0) return hipSuccess;
     dim3 grid((unsigned)units), block(kWaves * 64);
-    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, TOK>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, TOK, STAGES>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
+// Variants: 16-bit inputs use 2 N-tiles per wave (64 query tokens), which
+// halves the LDS reads per MFMA against one; with argmax the ring has two
+// stages so that the saved-value slots (64 KB) fit beside it. A 1024-token
+// int8 query fits one workgroup (8 waves x 4 N-tiles), so D is read once.
 hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t stream)
 {
     switch (elem) {
     case kF16:
-        return want_argmax ? launch_dense_t<kF16, true, 1, false>(a, stream)
-                           : launch_dense_t<kF16, false, 2, false>(a, stream);
+        return want_argmax ? launch_dense_t<kF16, true, 2, false, 2>(a, stream)
+                           : launch_dense_t<kF16, false, 2, false, 3>(a, stream);
     case kBF16:
-        return want_argmax ? launch_dense_t<kBF16, true, 1, false>(a, stream)
-                           : launch_dense_t<kBF16, false, 2, false>(a, stream);
+        return want_argmax ? launch_dense_t<kBF16, true, 2, false, 2>(a, stream)
+                           : launch_dense_t<kBF16, false, 2, false, 3>(a, stream);
     case kI8:
-        // a 1024-token int8 query fits one workgroup (8 waves x 4 N-tiles);
-        // with argmax the saved values only fit for 1 N-tile per wave
         if (a.q_scale_tok)
-            return want_argmax ? launch_dense_t<kI8, true, 1, true>(a, stream)
-                               : launch_dense_t<kI8, false, 4, true>(a, stream);
-        return want_argmax ? launch_dense_t<kI8, true, 1, false>(a, stream)
-                           : launch_dense_t<kI8, false, 4, false>(a, stream);
+            return want_argmax ? launch_dense_t<kI8, true, 2, true, 3>(a, stream)
+                               : launch_dense_t<kI8, false, 4, true, 3>(a, stream);
+        return want_argmax ? launch_dense_t<kI8, true, 2, false, 3>(a, stream)
+                           : launch_dense_t<kI8, false, 4, false, 3>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
