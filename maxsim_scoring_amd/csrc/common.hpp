@@ -98,6 +98,36 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m)
 }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
+// Sum over the 16 lanes of each DPP row; every lane of the row receives the
+// same bits (each step adds a value and its mirror image, and addition is
+// commutative, so the order is fixed).
+template <int CTRL, typename V>
+__device__ __forceinline__ V dpp_add(V x)
+{
+    const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false);
+    return x + __builtin_bit_cast(V, o);
+}
+template <typename V>
+__device__ __forceinline__ V row16_sum(V v)
+{
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);  // row_half_mirror
+    v = dpp_add<0x140>(v);  // row_mirror
+    return v;
+}
+
+// Sum of lanes 0-31 (DPP row sums, then row 0 + row 1), the same in every
+// lane. (The permlane swap builtins are avoided here: with both operands the
+// same value, ROCm 7.2 compiled the two swap results as one.)
+template <typename V>
+__device__ __forceinline__ V lanes0_31_sum(V v)
+{
+    const uint32_t b = __builtin_bit_cast(uint32_t, row16_sum(v));
+    return __builtin_bit_cast(V, __builtin_amdgcn_readlane(b, 0)) +
+           __builtin_bit_cast(V, __builtin_amdgcn_readlane(b, 16));
+}
+
 // Max with lowest-index tie-break across two (value, index) candidates.
 template <typename V>
 __device__ __forceinline__ void argmax_merge(V& m, int& idx, V om, int oidx)

@@ -254,6 +254,9 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     __shared__ V part[2][SLOTS];
     // d_mask of the whole doc range as bits, when it fits: 2 words per tile
     __shared__ __attribute__((aligned(16))) uint16_t mask_lds[4 * kMaskWords];
+    // tiles streamed per doc of the range when its mask is in LDS: up to the
+    // last tile holding a valid token (at least one, so every doc is finished)
+    __shared__ uint16_t doc_tiles[kMaskWords / 2];
     // doc-token scales of each stage's tile (TOK)
     __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? STAGES * kTileRows : 4];
     // argmax: each lane's saved M-tile values, per (wave, N-tile): 4 chunks x 64 lanes
@@ -370,7 +373,28 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
         }
         __builtin_amdgcn_s_waitcnt(0);
         block_barrier();
+        // trailing tiles with no valid token (padding) are not streamed
+        for (int kk = tid; kk < (int)(d1 - d0); kk += THREADS) {
+            int n = 1;
+            for (int tt = ntd - 1; tt > 0; --tt) {
+                const uint16_t* w = &mask_lds[(kk * wpd + 2 * tt) * 4];
+                if ((w[0] | w[1] | w[2] | w[3] | w[4] | w[5] | w[6] | w[7]) != 0) {
+                    n = tt + 1;
+                    break;
+                }
+            }
+            doc_tiles[kk] = (uint16_t)n;
+        }
+        block_barrier();
     }
+    const uint32_t doc_tiles_base = lds_addr(doc_tiles);
+    // tiles streamed for doc ordinal kk (uniform)
+    auto tiles_of = [&](int64_t kk) -> int {
+        if (!mask_in_lds) return ntd;
+        uint32_t v;
+        asm volatile("ds_read_u16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(doc_tiles_base + (uint32_t)(kk * 2)) : "memory");
+        return __builtin_amdgcn_readfirstlane(v);
+    };
     const uint32_t mask_base = lds_addr(mask_lds);
 
     for (int pass = 0; pass < a.npass; ++pass) {
@@ -438,14 +462,8 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 }
                 if constexpr (TOK) mv = qsc[n] * mv;  // positive: keeps the max and -inf
                 V contrib = (keep_row[n] && finite_score(mv)) ? mv : (V)0;
-                // fixed-order butterfly over the 32 query tokens of the N-tile
-#pragma unroll
-                for (int off = 16; off >= 1; off >>= 1) {
-                    if constexpr (std::is_integral_v<V>)
-                        contrib += shfl_xor_i(contrib, off);
-                    else
-                        contrib += shfl_xor_f(contrib, off);
-                }
+                // fixed-order sum over the 32 query tokens of the N-tile
+                contrib = lanes0_31_sum(contrib);
                 if (lane == 0)
                     lds_store_b32(part_base + (uint32_t)(((k & 1) * SLOTS + wave * NTW + n) * 4),
                                   __builtin_bit_cast(uint32_t, contrib));
@@ -516,26 +534,31 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 
         // issue cursor (doc ordinal ik, tile it) runs STAGES - 1 tiles ahead
         // of the compute cursor (k, tt); both advance one tile per iteration
+        // over the streamed tiles of each doc
+        const int64_t nd = d1 - d0;
         int64_t ik = 0;
-        int it = 0;
-        auto advance = [&](int64_t& kk, int& t) {
-            if (++t == ntd) {
-                t = 0;
-                ++kk;
+        int it = 0, ik_tiles = tiles_of(0);
+        int64_t issued = 0;
+        auto advance_issue = [&]() {
+            if (++it == ik_tiles) {
+                it = 0;
+                if (++ik < nd) ik_tiles = tiles_of(ik);
             }
         };
 #pragma unroll
         for (int q = 0; q < STAGES - 1; ++q) {
-            if (q < F) {
+            if (ik < nd) {
                 issue(d0 + ik, it, q);
-                advance(ik, it);
+                advance_issue();
+                ++issued;
             }
         }
 
         int stage = 0;
         int64_t k = 0;  // doc ordinal in the range
         int tt = 0;     // tile within the doc
-        for (int64_t f = 0; f < F; ++f, advance(k, tt)) {
+        int k_tiles = tiles_of(0);
+        for (int64_t f = 0; k < nd; ++f) {
             const int64_t doc = d0 + k;
             const int64_t t0 = (int64_t)tt * kTileRows;
 
@@ -556,7 +579,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             }
 
             // tile f has landed once at most STAGES - 2 later tiles are in flight
-            const int64_t ahead = F - 1 - f;  // tiles issued after f (capped below)
+            const int64_t ahead = issued - 1 - f;  // tiles issued after f (capped below)
             if constexpr (STAGES >= 4) {
                 if (ahead >= 2) wait_vmcnt<2 * LPW>();
                 else if (ahead == 1) wait_vmcnt<LPW>();
@@ -568,9 +591,10 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 wait_vmcnt<0>();
             }
             block_barrier();  // tile f landed for everyone; the stage of tile f - 1 is free
-            if (f + STAGES - 1 < F) {
+            if (ik < nd) {
                 issue(d0 + ik, it, stage == 0 ? STAGES - 1 : stage - 1);
-                advance(ik, it);
+                advance_issue();
+                ++issued;
             }
 
             if (tt == 0) {
@@ -688,8 +712,12 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 if ((vb[0] & vb[1]) == ~0ull) run_tile(std::true_type{});
                 else run_tile(std::false_type{});
             }
-            if (tt == ntd - 1) finish_doc(doc, k);
+            if (tt == k_tiles - 1) finish_doc(doc, k);
             stage = stage == STAGES - 1 ? 0 : stage + 1;
+            if (++tt == k_tiles) {
+                tt = 0;
+                if (++k < nd) k_tiles = tiles_of(k);
+            }
         }
         block_barrier();
         write_scores(d1 - 1, d1 - 1 - d0);

@@ -84,25 +84,6 @@ __device__ int nearest_boundary(const int32_t* __restrict__ cu, int n, int64_t t
     return uniform(below <= above ? j1 - 1 : j1);
 }
 
-// Sum over the 16 lanes of each DPP row; every lane of the row receives the
-// same bits (each step adds a value and its mirror image, and fp addition is
-// commutative).
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x)
-{
-    const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false);
-    return x + __builtin_bit_cast(float, o);
-}
-
-__device__ __forceinline__ float row16_sum(float v)
-{
-    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
-    v = dpp_add<0x141>(v);  // row_half_mirror
-    v = dpp_add<0x140>(v);  // row_mirror
-    return v;
-}
-
 }  // namespace
 
 // Three waves per SIMD (at most 168 VGPRs) with two ring stages measured
