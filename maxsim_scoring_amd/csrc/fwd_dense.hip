@@ -43,7 +43,6 @@ namespace maxsim {
 
 namespace {
 
-constexpr int kTileRows = 128;  // doc tokens per pipeline stage (4 MFMA M-tiles)
 constexpr int kWaves = 8;
 constexpr int kMaskWords = 2048;  // 16 KB of LDS: d_mask bits of a doc range
 
@@ -88,18 +87,23 @@ __device__ __forceinline__ uint64_t mask_bits_scalar(const uint8_t* p, int nb)
     return bits;
 }
 
-// Two 64-bit words at a uniform LDS address, read by every lane (broadcast)
-// and returned as scalars.
-__device__ __forceinline__ void lds_read_u64x2_uniform(uint32_t addr, uint64_t (&out)[2])
+// N (2 or 4) 64-bit words at a uniform LDS address, read by every lane
+// (broadcast) and returned as scalars.
+template <int N>
+__device__ __forceinline__ void lds_read_u64_uniform(uint32_t addr, uint64_t (&out)[N])
 {
-    i32x4 v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
-    const uint32_t w0 = __builtin_amdgcn_readfirstlane(v[0]);
-    const uint32_t w1 = __builtin_amdgcn_readfirstlane(v[1]);
-    const uint32_t w2 = __builtin_amdgcn_readfirstlane(v[2]);
-    const uint32_t w3 = __builtin_amdgcn_readfirstlane(v[3]);
-    out[0] = ((uint64_t)w1 << 32) | w0;
-    out[1] = ((uint64_t)w3 << 32) | w2;
+    static_assert(N == 2 || N == 4, "one or two 16-byte reads");
+#pragma unroll
+    for (int r = 0; r < N / 2; ++r) {
+        i32x4 v;
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr + 16 * r) : "memory");
+        const uint32_t w0 = __builtin_amdgcn_readfirstlane(v[0]);
+        const uint32_t w1 = __builtin_amdgcn_readfirstlane(v[1]);
+        const uint32_t w2 = __builtin_amdgcn_readfirstlane(v[2]);
+        const uint32_t w3 = __builtin_amdgcn_readfirstlane(v[3]);
+        out[2 * r] = ((uint64_t)w1 << 32) | w0;
+        out[2 * r + 1] = ((uint64_t)w3 << 32) | w2;
+    }
 }
 
 // LDS accesses made from inline assembly so that the compiler does not add
@@ -230,7 +234,7 @@ __device__ __forceinline__ int saved_argmax(const RowState<V, true>& st, const u
 // integer dot product before the max (a float per score); the query-token
 // scale (positive) is applied to the max. The tile's doc scales are staged in
 // LDS with the tile.
-template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES>
+template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES, int TR>
 __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 {
     static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
@@ -242,8 +246,11 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     constexpr int NCH = RB / 16;           // 16-byte chunks per row
     constexpr int KS = T::kKSteps;
     constexpr int SLOTS = kWaves * NTW;    // N-tiles per workgroup
-    constexpr int STAGE_BYTES = kTileRows * RB;
-    constexpr int CHUNKS = kTileRows * NCH;
+    static_assert(TR == 128 || TR == 256, "doc tokens per pipeline stage");
+    constexpr int MT = TR / 32;            // MFMA M-tiles per stage
+    constexpr int WPT = TR / 64;           // d_mask words per stage
+    constexpr int STAGE_BYTES = TR * RB;
+    constexpr int CHUNKS = TR * NCH;
     constexpr int THREADS = kWaves * 64;
     constexpr int LPS = CHUNKS / THREADS;  // direct-to-LDS loads per thread per stage
     constexpr int LPW = LPS + (TOK ? 1 : 0);  // direct-to-LDS loads per wave per stage
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     // last tile holding a valid token (at least one, so every doc is finished)
     __shared__ uint16_t doc_tiles[kMaskWords / 2];
     // doc-token scales of each stage's tile (TOK)
-    __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? STAGES * kTileRows : 4];
+    __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? STAGES * TR : 4];
     // argmax: each lane's saved M-tile values, per (wave, N-tile): 4 chunks x 64 lanes
     __shared__ __attribute__((aligned(16))) u32x4 save_buf[ARGMAX ? kWaves * NTW * 256 : 1];
 
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     // where the results of (query i, doc j) go
     auto out_pair = [&](int64_t i, int64_t j) -> int64_t { return pairs ? (int64_t)unit : i * Nd + j; };
 
-    const int ntd = Ld > 0 ? (int)((Ld + kTileRows - 1) / kTileRows) : 0;  // tiles per doc
+    const int ntd = Ld > 0 ? (int)((Ld + TR - 1) / TR) : 0;  // tiles per doc
     const int64_t F = (d1 - d0) * ntd;                                     // tiles of the range
     const uint32_t part_base = lds_addr(&part[0][0]);
 
@@ -325,9 +332,9 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     // stage tile tt of doc `doc` into `stage`: uniform base pointer + 32-bit
     // per-lane offsets (scalar-base addressing), no 64-bit per-lane math
     auto issue = [&](int64_t doc, int tt, int stage) {
-        const int64_t t0 = (int64_t)tt * kTileRows;
+        const int64_t t0 = (int64_t)tt * TR;
         const void* Dt = uniform_ptr((const unsigned char*)a.D + (doc * Ld + t0) * RB);
-        const int rows = Ld - t0 >= kTileRows ? kTileRows : (int)(Ld - t0);  // >= 1
+        const int rows = Ld - t0 >= TR ? TR : (int)(Ld - t0);  // >= 1
         const uint32_t lds0 = ring_base + (uint32_t)(stage * STAGE_BYTES + wave_u * LPS * 1024);
         // rows past the doc end read its last row's final chunk instead; they
         // are never folded (their validity bits are 0)
@@ -337,17 +344,17 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             const uint32_t o = (uint32_t)dma_off[u];
             dma_lds16(Dt, o < lim ? o : lim, lds0 + u * 1024);
         }
-        if constexpr (TOK) {  // rows 16 w .. 16 w + 15 of the tile's doc scales
+        if constexpr (TOK) {  // rows RPW w .. RPW w + RPW - 1 of the tile's doc scales
+            constexpr int RPW = TR / kWaves;
             const void* St = uniform_ptr(a.d_scale_tok + doc * Ld + t0);
-            const int row = 16 * wave + lane < rows ? 16 * wave + lane : rows - 1;
-            if (lane < 16)
-                dma_lds4(St, (uint32_t)(row * 4),
-                         sc_base + (uint32_t)((stage * kTileRows + 16 * wave_u) * 4));
+            const int row = RPW * wave + lane < rows ? RPW * wave + lane : rows - 1;
+            if (lane < RPW)
+                dma_lds4(St, (uint32_t)(row * 4), sc_base + (uint32_t)((stage * TR + RPW * wave_u) * 4));
         }
     };
 
     // ---- d_mask bits of the doc range into LDS (2 words per 128-token tile) --
-    const int wpd = 2 * ntd;  // mask words per doc
+    const int wpd = WPT * ntd;  // mask words per doc
     const bool mask_in_lds = a.d_mask && (d1 - d0) * (int64_t)wpd <= kMaskWords;
     if (mask_in_lds) {
         // each thread turns 16 consecutive mask bytes of one doc into 16 bits
@@ -377,8 +384,10 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
         for (int kk = tid; kk < (int)(d1 - d0); kk += THREADS) {
             int n = 1;
             for (int tt = ntd - 1; tt > 0; --tt) {
-                const uint16_t* w = &mask_lds[(kk * wpd + 2 * tt) * 4];
-                if ((w[0] | w[1] | w[2] | w[3] | w[4] | w[5] | w[6] | w[7]) != 0) {
+                const uint16_t* w = &mask_lds[(kk * wpd + WPT * tt) * 4];
+                uint32_t any = 0;
+                for (int i = 0; i < 4 * WPT; ++i) any |= w[i];
+                if (any != 0) {
                     n = tt + 1;
                     break;
                 }
@@ -560,16 +569,16 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
         int k_tiles = tiles_of(0);
         for (int64_t f = 0; k < nd; ++f) {
             const int64_t doc = d0 + k;
-            const int64_t t0 = (int64_t)tt * kTileRows;
+            const int64_t t0 = (int64_t)tt * TR;
 
             // validity of the tile's rows; the scalar loads run before the
             // wait below so that their latency hides behind it
-            uint64_t vb[2];
+            uint64_t vb[WPT];
             if (mask_in_lds) {
-                lds_read_u64x2_uniform(mask_base + (uint32_t)((k * wpd + 2 * tt) * 8), vb);
+                lds_read_u64_uniform<WPT>(mask_base + (uint32_t)((k * wpd + WPT * tt) * 8), vb);
             } else {
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
+                for (int hh = 0; hh < WPT; ++hh) {
                     const int64_t left = Ld - t0 - 64 * hh;
                     const int nb = left >= 64 ? 64 : (left > 0 ? (int)left : 0);
                     if (nb == 0) vb[hh] = 0;
@@ -603,7 +612,13 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 for (int n = 0; n < NTW; ++n) st[n].reset();
             }
 
-            if ((vb[0] | vb[1]) != 0) {
+            uint64_t vany = 0, vall = ~0ull;
+#pragma unroll
+            for (int hh = 0; hh < WPT; ++hh) {
+                vany |= vb[hh];
+                vall &= vb[hh];
+            }
+            if (vany != 0) {
                 // A fragments of M-tile mt: row = doc token 32 mt + lane % 32,
                 // 16-byte chunk 2s + lane / 32 of that row (swizzled). Plain
                 // LDS loads: the stage was published by the wait + barrier
@@ -626,7 +641,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     return acc;
                 };
                 // doc-token scales of the lane's 16 rows of M-tile mt (TOK)
-                const float* scs = sc_buf + stage * kTileRows;
+                const float* scs = sc_buf + stage * TR;
                 auto load_sc = [&](int mt, float (&sc)[16]) {
                     if constexpr (TOK) {
                         typedef float f4 __attribute__((ext_vector_type(4)));
@@ -654,8 +669,9 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     }
                 };
                 // validity bits of the 32 rows of M-tile mt
-                const uint32_t mb[4] = {(uint32_t)vb[0], (uint32_t)(vb[0] >> 32), (uint32_t)vb[1],
-                                        (uint32_t)(vb[1] >> 32)};
+                uint32_t mb[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) mb[mt] = (uint32_t)(vb[mt >> 1] >> (32 * (mt & 1)));
                 // The (M-tile, N-tile) units of the tile in order, software-
                 // pipelined: the MFMAs of unit u are issued before the fold of
                 // unit u - 1, so the two execute together, and the last unit of
@@ -665,7 +681,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                 // partly valid ones fold with -inf in their invalid rows.
                 auto run_tile = [&](auto fullc) {
                     constexpr bool FULL = decltype(fullc)::value;
-                    constexpr int U = 4 * NTW;
+                    constexpr int U = MT * NTW;
                     i32x4 af[KS];
                     Acc accs[2];
                     load_a(0, af);
@@ -700,7 +716,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     static_for<0, U>([&](auto uc) {
                         constexpr int u = decltype(uc)::value;
                         constexpr int mt = u / NTW, n = u % NTW;
-                        constexpr int next = (n == NTW - 1 && mt + 1 < 4) ? mt + 1 : -1;
+                        constexpr int next = (n == NTW - 1 && mt + 1 < MT) ? mt + 1 : -1;
                         if constexpr (!FULL && BIAS && n == 0)
                             if (mb[mt] != 0) binit = mb[mt] == 0xffffffffu ? Acc{} : mask_bias(mt);
                         if (FULL || mb[mt] != 0) accs[u & 1] = mma(af, n, next, (FULL || !BIAS) ? Acc{} : binit);
@@ -709,7 +725,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
                     });
                     fold_unit(std::integral_constant<int, U - 1>{});
                 };
-                if ((vb[0] & vb[1]) == ~0ull) run_tile(std::true_type{});
+                if (vall == ~0ull) run_tile(std::true_type{});
                 else run_tile(std::false_type{});
             }
             if (tt == k_tiles - 1) finish_doc(doc, k);
@@ -728,7 +744,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
-template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES>
+template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES, int TR>
 static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
 {
     constexpr int SLOTS = kWaves * NTW;
@@ -757,29 +773,34 @@ static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
     }
     if (units <= 0) return hipSuccess;
     dim3 grid((unsigned)units), block(kWaves * 64);
-    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, TOK, STAGES>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, TOK, STAGES, TR>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 // Variants: 16-bit inputs use 2 N-tiles per wave (64 query tokens), which
-// halves the LDS reads per MFMA against one; with argmax the ring has two
-// stages so that the saved-value slots (64 KB) fit beside it. A 1024-token
-// int8 query fits one workgroup (8 waves x 4 N-tiles), so D is read once.
+// halves the LDS reads per MFMA against one. Without argmax a stage holds 256
+// doc tokens (8 M-tiles per barrier); with argmax the saved-value slots
+// (64 KB) leave room for two 128-token stages. A 1024-token int8 query fits
+// one workgroup (8 waves x 4 N-tiles), so D is read once.
+#ifndef MAXSIM_DENSE_TR
+#define MAXSIM_DENSE_TR 256
+#endif
 hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t stream)
 {
+    constexpr int TRN = MAXSIM_DENSE_TR;  // stage rows without argmax
     switch (elem) {
     case kF16:
-        return want_argmax ? launch_dense_t<kF16, true, 2, false, 2>(a, stream)
-                           : launch_dense_t<kF16, false, 2, false, 3>(a, stream);
+        return want_argmax ? launch_dense_t<kF16, true, 2, false, 2, 128>(a, stream)
+                           : launch_dense_t<kF16, false, 2, false, 2, TRN>(a, stream);
     case kBF16:
-        return want_argmax ? launch_dense_t<kBF16, true, 2, false, 2>(a, stream)
-                           : launch_dense_t<kBF16, false, 2, false, 3>(a, stream);
+        return want_argmax ? launch_dense_t<kBF16, true, 2, false, 2, 128>(a, stream)
+                           : launch_dense_t<kBF16, false, 2, false, 2, TRN>(a, stream);
     case kI8:
         if (a.q_scale_tok)
-            return want_argmax ? launch_dense_t<kI8, true, 2, true, 3>(a, stream)
-                               : launch_dense_t<kI8, false, 4, true, 3>(a, stream);
-        return want_argmax ? launch_dense_t<kI8, true, 2, false, 3>(a, stream)
-                           : launch_dense_t<kI8, false, 4, false, 3>(a, stream);
+            return want_argmax ? launch_dense_t<kI8, true, 2, true, 2, 128>(a, stream)
+                               : launch_dense_t<kI8, false, 4, true, 3, 128>(a, stream);
+        return want_argmax ? launch_dense_t<kI8, true, 2, false, 2, TRN>(a, stream)
+                           : launch_dense_t<kI8, false, 4, false, 2, TRN>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
