@@ -494,4 +494,151 @@ int oracle_fwd_pairs_f64(const double* Q, const double* D, int64_t Nq, int64_t N
     return 0;
 }
 
-int oracle_version(void) { return 2; }
+/* ------------------------------------------------------------------------ */
+/* Padding-free backward ([FM] Sec. 4.2.1 Eqs. (2)-(3) and Sec. 4.2.2 on the */
+/* packed layout of Sec. 4.3.2; [LIK] "Varlen / packed path"). Query i is    */
+/* packed rows [cu_q[i], cu_q[i+1]), doc j rows [cu_d[j], cu_d[j+1]). The    */
+/* argmax is the forward's [Nq, Nd, max_lq] doc-relative map. Sources are    */
+/* the real query rows (s < Lq_i) of every doc that has a token; an empty    */
+/* doc has no destination row and contributes nothing. The CSR has one row   */
+/* per packed doc token; a column index is the flat source index             */
+/* (i*Nd + j)*max_lq + s, rows list their sources ascending.                 */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const double *Q, *D, *g;
+    const int32_t *cu_q, *cu_d;
+    int64_t Nq, Nd, max_lq, d;
+    const int32_t* argmax;
+    const int32_t *row_ptr, *col_idx;
+    double *dQ, *dD;
+} vbwd_ctx;
+
+/* Eq. (2) for packed query row p: sum over live docs j ascending */
+static void vdq_item(void* p_, int64_t i)
+{
+    vbwd_ctx* c = (vbwd_ctx*)p_;
+    for (int64_t s = 0; s < (int64_t)c->cu_q[i + 1] - c->cu_q[i]; ++s) {
+        double* out = c->dQ + ((int64_t)c->cu_q[i] + s) * c->d;
+        for (int64_t k = 0; k < c->d; ++k) out[k] = 0.0;
+        for (int64_t j = 0; j < c->Nd; ++j) {
+            if (c->cu_d[j + 1] == c->cu_d[j]) continue; /* empty doc: no gradient */
+            double w = c->g[i * c->Nd + j];
+            int64_t t = c->argmax[(i * c->Nd + j) * c->max_lq + s];
+            const double* x = c->D + ((int64_t)c->cu_d[j] + t) * c->d;
+            for (int64_t k = 0; k < c->d; ++k) out[k] += w * x[k];
+        }
+    }
+}
+
+/* Eq. (3) for packed doc row r: the sources of CSR row r, in order */
+static void vdd_item(void* p_, int64_t r)
+{
+    vbwd_ctx* c = (vbwd_ctx*)p_;
+    double* out = c->dD + r * c->d;
+    for (int64_t k = 0; k < c->d; ++k) out[k] = 0.0;
+    for (int64_t e = c->row_ptr[r]; e < c->row_ptr[r + 1]; ++e) {
+        int64_t src = c->col_idx[e];
+        int64_t s = src % c->max_lq, ij = src / c->max_lq;
+        int64_t i = ij / c->Nd, j = ij % c->Nd;
+        double w = c->g[i * c->Nd + j];
+        const double* q = c->Q + ((int64_t)c->cu_q[i] + s) * c->d;
+        for (int64_t k = 0; k < c->d; ++k) out[k] += w * q[k];
+    }
+}
+
+int oracle_bwd_varlen_f64(const double* Q, const int32_t* cu_q, int64_t Nq, int64_t max_lq,
+                          const double* D, const int32_t* cu_d, int64_t Nd, int64_t d,
+                          const int32_t* argmax, const double* g, double* dQ, double* dD,
+                          int32_t* row_ptr, int32_t* col_idx, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0) return -1;
+    if ((Nq > 0 && cu_q[0] != 0) || (Nd > 0 && cu_d[0] != 0)) return -2;
+    for (int64_t i = 0; i < Nq; ++i) {
+        int64_t l = (int64_t)cu_q[i + 1] - cu_q[i];
+        if (l < 0 || l > max_lq) return -2;
+    }
+    for (int64_t j = 0; j < Nd; ++j)
+        if (cu_d[j + 1] < cu_d[j]) return -2;
+    int64_t nrows = Nd > 0 ? cu_d[Nd] : 0;
+    /* sources (i, j, s) in ascending flat index; destination row cu_d[j] + t */
+    int64_t* cnt = (int64_t*)calloc((size_t)(nrows + 1), sizeof(int64_t));
+    for (int64_t i = 0; i < Nq; ++i)
+        for (int64_t j = 0; j < Nd; ++j) {
+            int64_t ld = (int64_t)cu_d[j + 1] - cu_d[j];
+            if (ld == 0) continue;
+            for (int64_t s = 0; s < (int64_t)cu_q[i + 1] - cu_q[i]; ++s) {
+                int64_t t = argmax[(i * Nd + j) * max_lq + s];
+                if (t < 0 || t >= ld) {
+                    free(cnt);
+                    return -2;
+                }
+                cnt[cu_d[j] + t] += 1; /* histogram (bincount) */
+            }
+        }
+    int64_t run = 0; /* exclusive scan */
+    for (int64_t r = 0; r < nrows; ++r) {
+        row_ptr[r] = (int32_t)run;
+        run += cnt[r];
+    }
+    row_ptr[nrows] = (int32_t)run;
+    for (int64_t r = 0; r < nrows; ++r) cnt[r] = row_ptr[r];
+    for (int64_t i = 0; i < Nq; ++i) /* fill in ascending source order */
+        for (int64_t j = 0; j < Nd; ++j) {
+            if (cu_d[j + 1] == cu_d[j]) continue;
+            for (int64_t s = 0; s < (int64_t)cu_q[i + 1] - cu_q[i]; ++s) {
+                int64_t src = (i * Nd + j) * max_lq + s;
+                col_idx[cnt[cu_d[j] + argmax[src]]++] = (int32_t)src;
+            }
+        }
+    free(cnt);
+    vbwd_ctx c = {Q, D, g, cu_q, cu_d, Nq, Nd, max_lq, d, argmax, row_ptr, col_idx, dQ, dD};
+    parallel_for(Nq, nthreads, vdq_item, &c);
+    parallel_for(nrows, nthreads, vdd_item, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scores of listed (query, doc) pairs of packed batches ([LIK] "Varlen /    */
+/* packed path", the pair-list scorer): pair p is Eq. (1) for query pair_q[p]*/
+/* against doc pair_d[p]; argmax [P, max_lq] as the packed forward's.        */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const double *Q, *D;
+    const int32_t *cu_q, *cu_d, *pq, *pd;
+    int64_t max_lq, d;
+    double* scores;
+    int32_t* argmax;
+} vpairs_ctx;
+
+static void vpairs_item(void* p_, int64_t p)
+{
+    vpairs_ctx* c = (vpairs_ctx*)p_;
+    int64_t i = c->pq[p], j = c->pd[p];
+    int64_t q0 = c->cu_q[i], lq = (int64_t)c->cu_q[i + 1] - q0;
+    int64_t d0 = c->cu_d[j], ld = (int64_t)c->cu_d[j + 1] - d0;
+    int32_t* arg = c->argmax ? c->argmax + p * c->max_lq : NULL;
+    if (arg)
+        for (int64_t s = 0; s < c->max_lq; ++s) arg[s] = 0;
+    c->scores[p] = pair_f64(c->Q + q0 * c->d, c->D + d0 * c->d, lq, ld, c->d, NULL, NULL, arg);
+}
+
+int oracle_fwd_pairs_varlen_f64(const double* Q, const int32_t* cu_q, int64_t Nq, int64_t max_lq,
+                                const double* D, const int32_t* cu_d, int64_t Nd, int64_t d,
+                                const int32_t* pair_q, const int32_t* pair_d, int64_t P,
+                                double* scores, int32_t* argmax, int nthreads)
+{
+    if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0 || P < 0) return -1;
+    for (int64_t i = 0; i < Nq; ++i) {
+        int64_t l = (int64_t)cu_q[i + 1] - cu_q[i];
+        if (l < 0 || l > max_lq) return -2;
+    }
+    for (int64_t j = 0; j < Nd; ++j)
+        if (cu_d[j + 1] < cu_d[j]) return -2;
+    for (int64_t p = 0; p < P; ++p)
+        if (pair_q[p] < 0 || pair_q[p] >= Nq || pair_d[p] < 0 || pair_d[p] >= Nd) return -2;
+    vpairs_ctx c = {Q, D, cu_q, cu_d, pair_q, pair_d, max_lq, d, scores, argmax};
+    parallel_for(P, nthreads, vpairs_item, &c);
+    return 0;
+}
+
+int oracle_version(void) { return 3; }

@@ -52,9 +52,14 @@ def _load():
         lib.oracle_topk.argtypes = [vp, i64, i64, i64, vp, vp, i32]
         lib.oracle_fwd_pairs_f64.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
                                              i64, vp, vp, i32]
+        lib.oracle_bwd_varlen_f64.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp, vp,
+                                              vp, vp, vp, i32]
+        lib.oracle_fwd_pairs_varlen_f64.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp,
+                                                    i64, vp, vp, i32]
         for f in (lib.oracle_fwd_f64, lib.oracle_fwd_varlen_f64, lib.oracle_fwd_i8,
                   lib.oracle_bwd_f64, lib.oracle_fwd_i8_tok, lib.oracle_topk,
-                  lib.oracle_fwd_pairs_f64):
+                  lib.oracle_fwd_pairs_f64, lib.oracle_bwd_varlen_f64,
+                  lib.oracle_fwd_pairs_varlen_f64):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -214,3 +219,49 @@ def fwd_pairs(Q, D, pair_q, pair_d, q_mask=None, d_mask=None, want_argmax=True, 
                                       _p(pd), P, _p(sc), _p(arg), threads or default_threads())
     _check(rc, "fwd_pairs")
     return sc, arg
+
+
+def bwd_varlen(Q, cu_q, max_lq, D, cu_d, argmax, grad_scores, threads=None):
+    """Padding-free backward through the saved [Nq, Nd, max_lq] argmax.
+    Returns (dQ float64 [Tq,d], dD float64 [Td,d], row_ptr int32 [Td+1],
+    col_idx int32 [nnz]) with nnz = Tq * (number of docs with a token)."""
+    q = _f64(Q)
+    dd = _f64(D)
+    cq = _arr(cu_q, np.int32)
+    cd = _arr(cu_d, np.int32)
+    Nq, Nd = len(cq) - 1, len(cd) - 1
+    d = q.shape[1] if q.ndim == 2 else dd.shape[1]
+    Tq, Td = int(cq[-1]), int(cd[-1])
+    a = _arr(argmax, np.int32)
+    g = _f64(grad_scores)
+    live = int(np.count_nonzero(np.diff(cd.astype(np.int64)) > 0))
+    dQ = np.zeros((Tq, d), np.float64)
+    dD = np.zeros((Td, d), np.float64)
+    rp = np.zeros(Td + 1, np.int32)
+    ci = np.zeros(max(Tq * live, 1), np.int32)
+    rc = _load().oracle_bwd_varlen_f64(_p(q), _p(cq), Nq, max_lq, _p(dd), _p(cd), Nd, d, _p(a),
+                                       _p(g), _p(dQ), _p(dD), _p(rp), _p(ci),
+                                       threads or default_threads())
+    _check(rc, "bwd_varlen")
+    return dQ, dD, rp, ci[:Tq * live]
+
+
+def fwd_pairs_varlen(Q, cu_q, max_lq, D, cu_d, pair_q, pair_d, want_argmax=True, threads=None):
+    """Scores of listed (query, doc) pairs of packed batches. Returns
+    (scores float64 [P], argmax int32 [P, max_lq] or None)."""
+    q = _f64(Q)
+    dd = _f64(D)
+    cq = _arr(cu_q, np.int32)
+    cd = _arr(cu_d, np.int32)
+    Nq, Nd = len(cq) - 1, len(cd) - 1
+    d = q.shape[1] if q.ndim == 2 else dd.shape[1]
+    pq = _arr(pair_q, np.int32)
+    pd = _arr(pair_d, np.int32)
+    P = len(pq)
+    scores = np.zeros(P, np.float64)
+    arg = np.zeros((P, max_lq), np.int32) if want_argmax else None
+    rc = _load().oracle_fwd_pairs_varlen_f64(_p(q), _p(cq), Nq, max_lq, _p(dd), _p(cd), Nd, d,
+                                             _p(pq), _p(pd), P, _p(scores), _p(arg),
+                                             threads or default_threads())
+    _check(rc, "fwd_pairs_varlen")
+    return scores, arg

@@ -473,3 +473,107 @@ def test_pairs_brute_force(oracle_mod):
                           None if w.d_mask is None else w.d_mask[j:j + 1])
         np.testing.assert_allclose(s[p], sb[0, 0], rtol=0, atol=1e-12)
         assert np.array_equal(a[p], ab[0, 0])
+
+
+# ----------------------------------------------------- padding-free backward, pairs
+
+def _pad(w, lens_q, lens_d):
+    """The packed inputs of `w` laid out padded with prefix masks."""
+    Nq, Nd = len(lens_q), len(lens_d)
+    Lq, Ld = max(lens_q), max(max(lens_d), 1)
+    Qp = torch.zeros(Nq, Lq, 128, dtype=w.Q.dtype)
+    Dp = torch.zeros(Nd, Ld, 128, dtype=w.D.dtype)
+    cq, cd = w.cu_q.tolist(), w.cu_d.tolist()
+    for i in range(Nq):
+        Qp[i, :lens_q[i]] = w.Q[cq[i]:cq[i + 1]]
+    for j in range(Nd):
+        Dp[j, :lens_d[j]] = w.D[cd[j]:cd[j + 1]]
+    return Qp, Dp, synth.prefix_mask(np.array(lens_q), Lq), synth.prefix_mask(np.array(lens_d), Ld)
+
+
+def test_backward_padding_free_equals_padded(oracle_mod):
+    """The packed backward gives the padded backward's gradients on the real
+    rows, and its CSR is the padded CSR without the sources of padded query
+    rows and of empty docs, rows renumbered to packed doc tokens (Flash-MaxSim
+    Sec. 4.2.1-4.2.2 on the cu_seqlens layout of Sec. 4.3.2)."""
+    lens_q = [5, 12, 3]
+    lens_d = [7, 0, 19, 3, 1]
+    w = synth.random_varlen(47, lens_q, lens_d)
+    Nq, Nd, Lq = len(lens_q), len(lens_d), w.max_lq
+    g = synth.upstream_grad(47, Nq, Nd).double().numpy()
+    _, a = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    dQ, dD, rp, ci = oracle_mod.bwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, a, g)
+    Qp, Dp, qm, dm = _pad(w, lens_q, lens_d)
+    assert Qp.shape[1] == Lq
+    _, ap = oracle_mod.fwd(Qp, Dp, qm, dm)
+    dQp, dDp, rpp, cip = oracle_mod.bwd(Qp, Dp, ap, g, qm, dm)
+    cq, cd = w.cu_q.tolist(), w.cu_d.tolist()
+    for i in range(Nq):
+        assert np.array_equal(dQ[cq[i]:cq[i + 1]], dQp[i, :lens_q[i]])
+    for j in range(Nd):
+        assert np.array_equal(dD[cd[j]:cd[j + 1]], dDp[j, :lens_d[j]])
+    # the padded CSR restricted to real sources, in the same order
+    Ldp = Dp.shape[1]
+    rows = []
+    for j in range(Nd):
+        for t in range(lens_d[j]):
+            seg = cip[rpp[j * Ldp + t]:rpp[j * Ldp + t + 1]]
+            s = seg % Lq
+            i = seg // Lq // Nd
+            rows.append(seg[s < np.array(lens_q)[i]])
+    assert np.array_equal(rp, np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32))
+    assert np.array_equal(ci, np.concatenate(rows).astype(np.int32))
+    assert rp[-1] == sum(lens_q) * sum(1 for l in lens_d if l > 0)
+
+
+def test_backward_padding_free_euler_identity(oracle_mod):
+    lens_q = [4, 9]
+    lens_d = [6, 0, 11, 2]
+    w = synth.random_varlen(48, lens_q, lens_d)
+    g = synth.upstream_grad(48, 2, 4).double().numpy()
+    s, a = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    dQ, dD, _, _ = oracle_mod.bwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, a, g)
+    lhs = float((g * s).sum())
+    np.testing.assert_allclose(float((dQ * w.Q.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(float((dD * w.D.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_padding_free_finite_differences(oracle_mod):
+    """Central differences of sum(g * score) in fp64 on a tiny packed batch
+    whose top-2 gaps are far larger than the step."""
+    rng = np.random.default_rng(49)
+    cq = np.array([0, 2, 5], np.int32)
+    cd = np.array([0, 3, 3, 7], np.int32)
+    Q = _exact_grid(rng, (5, 3))
+    D = _exact_grid(rng, (7, 3)) * 3.0
+    g = rng.standard_normal((2, 3))
+    s, a = oracle_mod.fwd_varlen(Q, cq, 3, D, cd)
+    dQ, dD, _, _ = oracle_mod.bwd_varlen(Q, cq, 3, D, cd, a, g)
+    h = 1e-6
+
+    def f(Qx, Dx):
+        sc, ax = oracle_mod.fwd_varlen(Qx, cq, 3, Dx, cd)
+        assert np.array_equal(ax, a)  # the step does not move any argmax
+        return float((g * sc).sum())
+
+    for (X, grad) in ((Q, dQ), (D, dD)):
+        for idx in np.ndindex(X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            num = (f(Xp, D) - f(Xm, D)) / (2 * h) if X is Q else (f(Q, Xp) - f(Q, Xm)) / (2 * h)
+            assert abs(num - grad[idx]) < 1e-6
+
+
+def test_pairs_varlen_equals_cross_product(oracle_mod):
+    """Scores of listed packed pairs are the packed cross-product's entries
+    (brute force by materialising S), repeats and empty sequences included."""
+    lens_q = [5, 0, 9]
+    lens_d = [7, 0, 12, 3]
+    w = synth.random_varlen(50, lens_q, lens_d)
+    pq = np.array([0, 2, 2, 1, 0, 2], np.int32)
+    pd = np.array([3, 0, 2, 2, 1, 2], np.int32)
+    ps, pa = oracle_mod.fwd_pairs_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, pq, pd)
+    rs, ra = bf.varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    np.testing.assert_allclose(ps, rs[pq, pd], rtol=0, atol=1e-12)
+    assert np.array_equal(pa, ra[pq, pd])
