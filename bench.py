@@ -214,6 +214,59 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
             "kernels": ["csr_kernel", "dq_kernel", "dd_kernel"]}
 
 
+def bench_backward_varlen(torch, ms, synth, wl, steps, warmup):
+    """Padding-free backward at the ColPali training shapes without padding:
+    128 queries of 16-128 tokens and 128 docs of 768-1024 patches (the valid
+    prefixes of the cross-product workload), bf16, argmax from the GPU forward."""
+    import numpy as np
+    rng = np.random.default_rng(3)
+    ql, dl = rng.integers(16, 129, 128), rng.integers(768, 1025, 128)
+    w = synth.random_varlen(31, ql, dl, dtype=torch.bfloat16, max_lq=128)
+    Q, cu_q, D, cu_d = (t.cuda() for t in (w.Q, w.cu_q, w.D, w.cu_d))
+    _, argmax = ms.maxsim_fwd_varlen(Q, cu_q, 128, D, cu_d, want_argmax=True)
+    g = synth.upstream_grad(5, 128, 128).cuda()
+    Tq, Td = int(cu_q[-1]), int(cu_d[-1])
+    dQ = torch.empty((Tq, 128), dtype=torch.float32, device="cuda")
+    dD = torch.empty((Td, 128), dtype=torch.float32, device="cuda")
+    rp = torch.empty((Td + 1,), dtype=torch.int32, device="cuda")
+    ci = torch.empty((Tq * 128,), dtype=torch.int32, device="cuda")
+
+    def step():
+        ms.maxsim_bwd_varlen(Q, cu_q, 128, D, cu_d, argmax, g, dQ=dQ, dD=dD, csr_row_ptr=rp,
+                             csr_col_idx=ci)
+
+    total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
+    t = statistics.median(times)
+    nbytes = wl.bwd_varlen_compulsory_bytes(128, 128, 128, Tq, Td, 128, 128, 2)
+    return {"workload": f"backward_varlen_bf16_128x128_lq16-128_ld768-1024_packed_{Tq}x{Td}", "ms": t,
+            "pairs_per_s": 128 * 128 / (t * 1e-3), "compulsory_bytes": nbytes,
+            "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+            "kernels": ["vbwd_prep_kernel", "vbwd_csr_kernel", "vbwd_dq_kernel", "vbwd_dd_kernel"]}
+
+
+def bench_pairs_varlen(torch, ms, synth, wl, steps, warmup):
+    """Reranker scheduling on the packed corpus: 32 queries of 32 tokens, each
+    with 1,000 candidate docs drawn from the 100,000-passage corpus (50-300
+    tokens), scored as one list of 32,000 (query, doc) pairs."""
+    import numpy as np
+    lens = synth.rerank_lengths(2, 100_000)
+    w = synth.random_varlen(12, [32] * 32, lens)
+    pq, pd = synth.random_pairs(12, 32, 100_000, 32_000)
+    Q, cu_q, D, cu_d, pq_d, pd_d = (t.cuda() for t in (w.Q, w.cu_q, w.D, w.cu_d, pq, pd))
+    scores = torch.empty((32_000,), dtype=torch.float32, device="cuda")
+
+    def step():
+        ms.maxsim_fwd_pairs_varlen(Q, cu_q, 32, D, cu_d, pq_d, pd_d, scores=scores)
+
+    total, _ = time_steps(torch, step, steps, warmup)
+    t = total / steps
+    nbytes = wl.pairs_varlen_fwd_bytes(32 * 32, lens[pd.numpy()], 128, 2)
+    return {"workload": "pairs_varlen_fp16_32q_lq32_32000pairs_ld50-300", "ms": t,
+            "pairs_per_s": 32_000 / (t * 1e-3), "algorithmic_bytes": nbytes,
+            "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+            "kernel": "fwd_varlen_kernel (pair list)"}
+
+
 def bench_two_stage(torch, ms, synth, wl, steps, warmup):
     """The INT8 -> FP16 top-K scan on the long-query corpus (1 query of 1024
     tokens, 10,000 docs of 1024 tokens): per-token INT8 scores of every doc,
@@ -317,7 +370,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="",
-                    help="run one workload: rerank|tiny|colpali|int8|backward|two_stage|topk|copy")
+                    help="run one workload: rerank|tiny|colpali|int8|backward|backward_varlen|"
+                         "pairs_varlen|two_stage|topk|copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -335,9 +389,10 @@ def main() -> int:
     ms.binding.lib()  # fails loudly without the built library
 
     names = [args.only] if args.only else [HEADLINE, "tiny", "colpali", "int8", "backward",
-                                           "two_stage", "topk"]
+                                           "backward_varlen", "pairs_varlen", "two_stage", "topk"]
     fns = {"rerank": bench_rerank, "tiny": bench_tiny, "colpali": bench_colpali,
-           "int8": bench_int8, "backward": bench_backward, "two_stage": bench_two_stage,
+           "int8": bench_int8, "backward": bench_backward, "backward_varlen": bench_backward_varlen,
+           "pairs_varlen": bench_pairs_varlen, "two_stage": bench_two_stage,
            "topk": bench_topk, "copy": bench_copy}
     per = {}
     head = None

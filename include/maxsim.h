@@ -167,6 +167,57 @@ maxsim_status_t maxsim_topk(const float* scores, int64_t Nq, int64_t Nd, int64_t
                             maxsim_stream_t stream);
 
 /*
+ * Scores of listed (query, doc) pairs of packed batches (design notes
+ * "Varlen / packed path", the pair-list scorer for sparse pair lists):
+ * pair p is Eq. (1) for packed query pair_q[p] against packed doc pair_d[p],
+ * with the layout of maxsim_fwd_varlen.
+ *   pair_q, pair_d [P] int32 in [0, Nq) and [0, Nd) (a precondition: entries
+ *     outside are clamped, never read out of bounds); pairs may repeat
+ *   scores [P] float32; argmax [P, max_lq] int32 or NULL (doc-relative,
+ *     rows at or past the query's length 0)
+ * P == 0 enqueues nothing. Errors: SHAPE (negative sizes; P > 0 with Nq == 0
+ * or Nd == 0), NULL, UNSUPPORTED (d, dtype, alignment), OVERFLOW
+ * (P * max_lq >= 2^31 with argmax, or Nq, Nd, P >= 2^31 - 1).
+ */
+maxsim_status_t maxsim_fwd_pairs_varlen(maxsim_dtype_t dtype, const void* Q, const int32_t* cu_q,
+                                        int64_t Nq, int32_t max_lq, const void* D,
+                                        const int32_t* cu_d, int64_t Nd, int64_t d,
+                                        const int32_t* pair_q, const int32_t* pair_d, int64_t P,
+                                        float* scores, int32_t* argmax, maxsim_stream_t stream);
+
+/*
+ * Padding-free backward through the saved argmax of maxsim_fwd_varlen
+ * ("Flash-MaxSim" Sec. 4.2.1 Eqs. (2)-(3), Sec. 4.2.2 inverse-grid CSR,
+ * Sec. 4.2.3 destination-owned reduction, on the cu_seqlens layout of
+ * Sec. 4.3.2):
+ *   dQ[cu_q[i] + s] = sum_j live(j) g[i,j] D[cu_d[j] + argmax[i,j,s]]
+ *   dD[cu_d[j] + t] = sum over (i,s) with argmax[i,j,s] = t of g[i,j] Q[cu_q[i] + s]
+ * with live(j) = doc j has a token (an empty doc takes no gradient).
+ *   Q [total_q, d], D [total_d, d] packed, cu_q [Nq+1], cu_d [Nd+1] int32 as
+ *     in maxsim_fwd_varlen, with cu_q[Nq] == total_q, cu_d[Nd] == total_d and
+ *     every query length <= max_lq (preconditions)
+ *   argmax [Nq, Nd, max_lq] int32 doc-relative (in [0, L_j) for docs with a
+ *     token); grad_scores [Nq, Nd] float32
+ *   dQ [total_q, d], dD [total_d, d] float32, fully overwritten
+ *   csr_row_ptr [total_d + 1], csr_col_idx [total_q * Nd] int32: outputs.
+ *     Row r is packed doc token r; it lists the flat sources
+ *     (i*Nd + j)*max_lq + s that picked it, ascending. The sources are the
+ *     total_q query rows of every doc with a token, so the first
+ *     total_q * (docs with a token) entries of csr_col_idx are written.
+ *     dD's first element of each such doc holds scratch until dD is written.
+ * Sums run in fp32 in a fixed order: dQ over j ascending, dD over the CSR row.
+ * Errors: SHAPE (negative sizes; packed rows with Nq or Nd == 0; total_q > 0
+ * with max_lq == 0), NULL, UNSUPPORTED (d, dtype, alignment), OVERFLOW when
+ * Nq*Nd*max_lq or total_q*Nd >= 2^31 or total_d + 1 >= 2^31.
+ */
+maxsim_status_t maxsim_bwd_varlen(maxsim_dtype_t dtype, const void* Q, const int32_t* cu_q,
+                                  int64_t Nq, int64_t total_q, int32_t max_lq, const void* D,
+                                  const int32_t* cu_d, int64_t Nd, int64_t total_d, int64_t d,
+                                  const int32_t* argmax, const float* grad_scores, float* dQ,
+                                  float* dD, int32_t* csr_row_ptr, int32_t* csr_col_idx,
+                                  maxsim_stream_t stream);
+
+/*
  * Backward through a saved forward argmax ("Flash-MaxSim" Sec. 4.2.1
  * Eqs. (2)-(3), Sec. 4.2.2 inverse-grid CSR, Sec. 4.2.3 destination-owned
  * reduction; design notes "Backward"):

@@ -53,8 +53,13 @@ def lib() -> ctypes.CDLL:
         L.maxsim_fwd_pairs.argtypes = [ci, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, vp,
                                        vp, vp]
         L.maxsim_topk.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.maxsim_fwd_pairs_varlen.argtypes = [ci, vp, vp, i64, i32, vp, vp, i64, i64, vp, vp, i64,
+                                              vp, vp, vp]
+        L.maxsim_bwd_varlen.argtypes = [ci, vp, vp, i64, i64, i32, vp, vp, i64, i64, i64, vp, vp,
+                                        vp, vp, vp, vp, vp]
         for f in (L.maxsim_fwd, L.maxsim_fwd_varlen, L.maxsim_fwd_i8, L.maxsim_bwd,
-                  L.maxsim_fwd_i8_tok, L.maxsim_fwd_pairs, L.maxsim_topk):
+                  L.maxsim_fwd_i8_tok, L.maxsim_fwd_pairs, L.maxsim_topk,
+                  L.maxsim_fwd_pairs_varlen, L.maxsim_bwd_varlen):
             f.restype = ci
         L.maxsim_status_string.argtypes = [ci]
         L.maxsim_status_string.restype = ctypes.c_char_p
@@ -220,6 +225,76 @@ def maxsim_bwd(Q: torch.Tensor, D: torch.Tensor, argmax: torch.Tensor, grad_scor
                           _p(csr_col_idx), _stream(stream))
     _check("maxsim_bwd", st)
     return dQ, dD, csr_row_ptr, csr_col_idx[:Nq * Nd * Lq]
+
+
+def maxsim_fwd_pairs_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D: torch.Tensor,
+                            cu_d: torch.Tensor, pair_q: torch.Tensor, pair_d: torch.Tensor,
+                            want_argmax: bool = False, scores: Optional[torch.Tensor] = None,
+                            argmax: Optional[torch.Tensor] = None, stream=None):
+    """Scores of listed (query, doc) pairs of packed batches. Q [Tq,d], D [Td,d]
+    packed; pair_q, pair_d int32 [P]. Returns (scores [P], argmax [P,max_lq] or None)."""
+    if Q.dim() != 2 or D.dim() != 2 or Q.shape[1] != D.shape[1] or Q.dtype != D.dtype:
+        raise ValueError("Q and D must be packed [tokens, d] of one dtype")
+    d = Q.shape[1]
+    for n, t in (("Q", Q), ("D", D)):
+        _dev(n, t)
+    for n, t in (("cu_q", cu_q), ("cu_d", cu_d), ("pair_q", pair_q), ("pair_d", pair_d)):
+        _dev(n, t, torch.int32)
+    if pair_q.shape != pair_d.shape or pair_q.dim() != 1:
+        raise ValueError("pair_q and pair_d must be [P]")
+    Nq, Nd, P = cu_q.numel() - 1, cu_d.numel() - 1, pair_q.numel()
+    if scores is None:
+        scores = torch.empty((P,), dtype=torch.float32, device=Q.device)
+    if argmax is None and want_argmax:
+        argmax = torch.empty((P, max_lq), dtype=torch.int32, device=Q.device)
+    _dev("scores", scores, torch.float32)
+    _dev("argmax", argmax, torch.int32)
+    st = lib().maxsim_fwd_pairs_varlen(_dtype_code(Q), _p(Q), _p(cu_q), Nq, int(max_lq), _p(D),
+                                       _p(cu_d), Nd, d, _p(pair_q), _p(pair_d), P, _p(scores),
+                                       _p(argmax), _stream(stream))
+    _check("maxsim_fwd_pairs_varlen", st)
+    return scores, argmax
+
+
+def maxsim_bwd_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D: torch.Tensor,
+                      cu_d: torch.Tensor, argmax: torch.Tensor, grad_scores: torch.Tensor,
+                      dQ: Optional[torch.Tensor] = None, dD: Optional[torch.Tensor] = None,
+                      csr_row_ptr: Optional[torch.Tensor] = None,
+                      csr_col_idx: Optional[torch.Tensor] = None, stream=None):
+    """Padding-free backward through the saved [Nq,Nd,max_lq] argmax. Q [Tq,d],
+    D [Td,d] packed. Returns (dQ [Tq,d], dD [Td,d], csr_row_ptr [Td+1],
+    csr_col_idx [Tq*Nd]: the first Tq*(docs with a token) entries are the CSR)."""
+    if Q.dim() != 2 or D.dim() != 2 or Q.shape[1] != D.shape[1] or Q.dtype != D.dtype:
+        raise ValueError("Q and D must be packed [tokens, d] of one dtype")
+    Tq, d = Q.shape
+    Td = D.shape[0]
+    for n, t in (("Q", Q), ("D", D)):
+        _dev(n, t)
+    _dev("cu_q", cu_q, torch.int32)
+    _dev("cu_d", cu_d, torch.int32)
+    _dev("argmax", argmax, torch.int32)
+    _dev("grad_scores", grad_scores, torch.float32)
+    Nq, Nd = cu_q.numel() - 1, cu_d.numel() - 1
+    if tuple(argmax.shape) != (Nq, Nd, max_lq) or tuple(grad_scores.shape) != (Nq, Nd):
+        raise ValueError("argmax must be [Nq,Nd,max_lq] and grad_scores [Nq,Nd]")
+    dev = Q.device
+    if dQ is None:
+        dQ = torch.empty((Tq, d), dtype=torch.float32, device=dev)
+    if dD is None:
+        dD = torch.empty((Td, d), dtype=torch.float32, device=dev)
+    if csr_row_ptr is None:
+        csr_row_ptr = torch.empty((Td + 1,), dtype=torch.int32, device=dev)
+    if csr_col_idx is None:
+        csr_col_idx = torch.empty((max(1, Tq * Nd),), dtype=torch.int32, device=dev)
+    for n, t in (("dQ", dQ), ("dD", dD)):
+        _dev(n, t, torch.float32)
+    for n, t in (("csr_row_ptr", csr_row_ptr), ("csr_col_idx", csr_col_idx)):
+        _dev(n, t, torch.int32)
+    st = lib().maxsim_bwd_varlen(_dtype_code(Q), _p(Q), _p(cu_q), Nq, Tq, int(max_lq), _p(D),
+                                 _p(cu_d), Nd, Td, d, _p(argmax), _p(grad_scores), _p(dQ), _p(dD),
+                                 _p(csr_row_ptr), _p(csr_col_idx), _stream(stream))
+    _check("maxsim_bwd_varlen", st)
+    return dQ, dD, csr_row_ptr, csr_col_idx
 
 
 def maxsim_status_string(status: int) -> str:

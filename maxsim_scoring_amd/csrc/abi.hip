@@ -252,6 +252,85 @@ maxsim_status_t maxsim_topk(const float* scores, int64_t Nq, int64_t Nd, int64_t
     return launch_status(launch_topk(a, (hipStream_t)stream));
 }
 
+maxsim_status_t maxsim_fwd_pairs_varlen(maxsim_dtype_t dtype, const void* Q, const int32_t* cu_q,
+                                        int64_t Nq, int32_t max_lq, const void* D,
+                                        const int32_t* cu_d, int64_t Nd, int64_t d,
+                                        const int32_t* pair_q, const int32_t* pair_d, int64_t P,
+                                        float* scores, int32_t* argmax, maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0 || P < 0) return MAXSIM_ERR_SHAPE;
+    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (P == 0) return MAXSIM_OK;
+    if (Nq == 0 || Nd == 0) return MAXSIM_ERR_SHAPE;  // a pair needs a query and a doc
+    if (!cu_q || !cu_d || !pair_q || !pair_d || !scores) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(cu_q, 4) || !aligned(cu_d, 4) ||
+        !aligned(pair_q, 4) || !aligned(pair_d, 4) || !aligned(scores, 4) || !aligned(argmax, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq > kI32Max - 1 || Nd > kI32Max - 1 || P > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (argmax) {
+        const int64_t n = mul_sat(P, max_lq);
+        if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    VarlenArgs a{};
+    a.Q = Q;
+    a.cu_q = cu_q;
+    a.D = D;
+    a.cu_d = cu_d;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.max_lq = max_lq;
+    a.pair_q = pair_q;
+    a.pair_d = pair_d;
+    a.npairs = P;
+    return launch_status(launch_fwd_varlen(elem_of(dtype), a, (hipStream_t)stream));
+}
+
+maxsim_status_t maxsim_bwd_varlen(maxsim_dtype_t dtype, const void* Q, const int32_t* cu_q,
+                                  int64_t Nq, int64_t total_q, int32_t max_lq, const void* D,
+                                  const int32_t* cu_d, int64_t Nd, int64_t total_d, int64_t d,
+                                  const int32_t* argmax, const float* grad_scores, float* dQ,
+                                  float* dD, int32_t* csr_row_ptr, int32_t* csr_col_idx,
+                                  maxsim_stream_t stream)
+{
+    if (Nq < 0 || Nd < 0 || total_q < 0 || total_d < 0 || d < 0 || max_lq < 0) return MAXSIM_ERR_SHAPE;
+    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    // packed rows need a sequence to belong to, and a query row a max_lq slot
+    if ((Nq == 0 && total_q > 0) || (Nd == 0 && total_d > 0) || (total_q > 0 && max_lq == 0))
+        return MAXSIM_ERR_SHAPE;
+    const int64_t nsrc = mul_sat(mul_sat(Nq, Nd), max_lq);
+    const int64_t nnz = mul_sat(total_q, Nd);
+    if (nsrc < 0 || nsrc > kI32Max || nnz < 0 || nnz > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (total_d + 1 > kI32Max || Nq > kI32Max - 1 || Nd > kI32Max - 1) return MAXSIM_ERR_OVERFLOW;
+    if (!cu_q || !cu_d || !csr_row_ptr) return MAXSIM_ERR_NULL;
+    if (total_q > 0 && (!Q || !dQ)) return MAXSIM_ERR_NULL;
+    if (total_d > 0 && (!D || !dD || (total_q > 0 && !csr_col_idx))) return MAXSIM_ERR_NULL;
+    if (Nq * Nd > 0 && (!argmax || !grad_scores)) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(dQ, 16) || !aligned(dD, 16) ||
+        !aligned(cu_q, 4) || !aligned(cu_d, 4) || !aligned(argmax, 4) || !aligned(grad_scores, 4) ||
+        !aligned(csr_row_ptr, 4) || !aligned(csr_col_idx, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
+    VarBwdArgs a{};
+    a.Q = Q;
+    a.cu_q = cu_q;
+    a.D = D;
+    a.cu_d = cu_d;
+    a.argmax = argmax;
+    a.g = grad_scores;
+    a.dQ = dQ;
+    a.dD = dD;
+    a.row_ptr = csr_row_ptr;
+    a.col_idx = csr_col_idx;
+    a.Nq = Nq;
+    a.Nd = Nd;
+    a.Tq = total_q;
+    a.Td = total_d;
+    a.nnz_cap = nnz;
+    a.max_lq = max_lq;
+    return launch_status(launch_bwd_varlen(elem_of(dtype), a, (hipStream_t)stream));
+}
+
 maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
                            int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
                            const uint8_t* d_mask, const int32_t* argmax, const float* grad_scores,

@@ -484,4 +484,389 @@ hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream)
     }
 }
 
+// ===========================================================================
+// Padding-free backward ("Flash-MaxSim" Sec. 4.2.1-4.2.3 on the cu_seqlens
+// layout of Sec. 4.3.2; design notes "Varlen / packed path"). Query i is
+// packed rows [cu_q[i], cu_q[i+1]) and doc j rows [cu_d[j], cu_d[j+1]); the
+// argmax is the packed forward's [Nq, Nd, max_lq] doc-relative map. The
+// sources are the Tq packed query rows for every doc that has a token (an
+// empty doc has no destination and no gradient), so every such doc's CSR
+// segment holds Tq entries and starts at Tq * (docs with a token before it).
+//
+//   prep  one workgroup: that segment start for every doc with a token,
+//         parked in the first element of the doc's first dD row (dD is
+//         written last), and row_ptr[Td];
+//   csr   one workgroup per doc, as the padded kernel: destinations of a
+//         block of sources per wave in registers, per-wave LDS histograms,
+//         scan, stable scatter with ballot ranks. Source p (a packed query
+//         row) belongs to the query found by a search of cu_q once per lane,
+//         then by walking forward as p grows;
+//   dq    16 packed query rows per workgroup, a 16-lane group per row; the
+//         argmax entries, doc offsets and weights of 64 docs at a time are
+//         staged in LDS, then each group gathers its D rows in doc order;
+//   dd    a 16-lane group per packed doc row walks its CSR row in order and
+//         gathers Q rows; every row is written once.
+// No atomics on results; results are bitwise reproducible.
+// ===========================================================================
+
+namespace {
+
+// largest b in [0, n) with cu[b] <= p (cu non-decreasing, cu[0] = 0 <= p)
+__device__ __forceinline__ int seg_of(const int32_t* __restrict__ cu, int n, int64_t p)
+{
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= p) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+constexpr int kPrepThreads = 1024;
+
+}  // namespace
+
+__global__ __launch_bounds__(kPrepThreads) void vbwd_prep_kernel(VarBwdArgs a)
+{
+    __shared__ uint32_t part[kPrepThreads];
+    const int tid = threadIdx.x;
+    const int64_t Nd = a.Nd, Td = a.Td;
+    const int64_t chunk = (Nd + kPrepThreads - 1) / kPrepThreads;
+    const int64_t j0 = tid * chunk, j1 = j0 + chunk < Nd ? j0 + chunk : Nd;
+    uint32_t live = 0;
+    for (int64_t j = j0; j < j1; ++j) live += a.cu_d[j + 1] > a.cu_d[j] ? 1u : 0u;
+    part[tid] = live;
+    barrier_lds();
+    // exclusive scan of the per-thread counts (Hillis-Steele in LDS)
+    for (int off = 1; off < kPrepThreads; off <<= 1) {
+        const uint32_t v = tid >= off ? part[tid - off] : 0u;
+        barrier_lds();
+        part[tid] += v;
+        barrier_lds();
+    }
+    uint32_t before = part[tid] - live;
+    for (int64_t j = j0; j < j1; ++j) {
+        const int64_t r = a.cu_d[j];
+        if (a.cu_d[j + 1] > r) {
+            if (r >= 0 && r < Td) a.dD[r * kD] = __builtin_bit_cast(float, (uint32_t)((int64_t)before * a.Tq));
+            ++before;
+        }
+    }
+    if (tid == kPrepThreads - 1) a.row_ptr[Td] = (int32_t)((int64_t)part[tid] * a.Tq);
+}
+
+// CSR of doc j: row_ptr[cu_d[j] + t] and the doc's col_idx segment.
+__global__ __launch_bounds__(kCsrThreads) void vbwd_csr_kernel(VarBwdArgs a)
+{
+    constexpr int kPerWave = kCsrChunk / kCsrWaves;
+    constexpr int kSteps = kPerWave / 64;
+    __shared__ uint32_t hist[kCsrWaves][kCsrBins];
+    __shared__ uint32_t run[kCsrBins];
+    __shared__ uint32_t wsum[kCsrWaves];
+    const int64_t j = blockIdx.x;
+    const int64_t Nd = a.Nd, Tq = a.Tq, Nq = a.Nq;
+    const int64_t d0 = a.cu_d[j];
+    int64_t L = (int64_t)a.cu_d[j + 1] - d0;
+    if (d0 < 0 || d0 >= a.Td) return;  // empty doc (or broken offsets)
+    if (L > a.Td - d0) L = a.Td - d0;
+    if (L <= 0) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint32_t mlq = (uint32_t)a.max_lq, nd = (uint32_t)Nd;
+    const int nchunks = (int)((Tq + kCsrChunk - 1) / kCsrChunk);
+    const int nq = (int)Nq;
+
+    uint32_t key[kSteps];
+    uint32_t srcv[kSteps];  // flat source index of each held source
+    auto load_block = [&](int c, int64_t t_lo, int nb) {
+        const int64_t p0 = (int64_t)c * kCsrChunk + (int64_t)wave * kPerWave + lane;
+        int i = p0 < Tq ? seg_of(a.cu_q, nq + 1, p0) : 0;
+        i = i < nq ? i : nq - 1;  // precondition guard (cu_q[Nq] == Tq)
+        int32_t tv[kSteps];
+#pragma unroll
+        for (int m = 0; m < kSteps; ++m) {
+            const int64_t p = p0 + 64 * m;
+            srcv[m] = 0;
+            tv[m] = -1;
+            if (p < Tq) {
+                while (i + 1 < nq && (int64_t)a.cu_q[i + 1] <= p) ++i;
+                int64_t s = p - a.cu_q[i];
+                s = s < 0 ? 0 : (s >= mlq ? mlq - 1 : s);  // precondition guard
+                srcv[m] = ((uint32_t)i * nd + (uint32_t)j) * mlq + (uint32_t)s;
+                tv[m] = __builtin_nontemporal_load(a.argmax + srcv[m]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kSteps; ++m) {
+            key[m] = kNoKey;
+            if (p0 + 64 * m < Tq) {
+                int64_t t = tv[m];
+                t = t < 0 ? 0 : (t >= L ? L - 1 : t);  // precondition guard
+                if (t >= t_lo && t < t_lo + nb) key[m] = (uint32_t)(t - t_lo);
+            }
+        }
+    };
+    auto count_block = [&](int nb) {
+        for (int k = lane; k < nb; k += 64) hist[wave][k] = 0;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+        for (int m = 0; m < kSteps; ++m)
+            if (key[m] != kNoKey) atomicAdd(&hist[wave][key[m]], 1u);
+    };
+    int64_t carry = (int64_t)__builtin_bit_cast(uint32_t, a.dD[d0 * kD]);  // parked by prep
+    for (int64_t t_lo = 0; t_lo < L; t_lo += kCsrBins) {
+        const int nb = (int)(L - t_lo < kCsrBins ? L - t_lo : kCsrBins);
+        for (int k = tid; k < nb; k += kCsrThreads) run[k] = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            barrier_lds();
+            load_block(c, t_lo, nb);
+            count_block(nb);
+            barrier_lds();
+            for (int k = tid; k < nb; k += kCsrThreads) {
+                uint32_t tot = 0;
+                for (int w = 0; w < kCsrWaves; ++w) tot += hist[w][k];
+                run[k] += tot;
+            }
+        }
+        barrier_lds();
+        const uint32_t mine = tid < nb ? run[tid] : 0u;
+        uint32_t incl = mine;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        barrier_lds();
+        uint32_t wave_off = 0, round_tot = 0;
+        for (int w = 0; w < kCsrWaves; ++w) {
+            if (w < wave) wave_off += wsum[w];
+            round_tot += wsum[w];
+        }
+        if (tid < nb) {
+            const int64_t first = carry + wave_off + incl - mine;
+            a.row_ptr[d0 + t_lo + tid] = (int32_t)first;
+            run[tid] = (uint32_t)first;
+        }
+        carry += round_tot;
+        for (int c = 0; c < nchunks; ++c) {
+            if (nchunks > 1) {
+                barrier_lds();
+                load_block(c, t_lo, nb);
+                count_block(nb);
+            }
+            barrier_lds();
+            for (int k = tid; k < nb; k += kCsrThreads) {
+                uint32_t pos = run[k];
+                for (int w = 0; w < kCsrWaves; ++w) {
+                    const uint32_t h = hist[w][k];
+                    hist[w][k] = pos;
+                    pos += h;
+                }
+                run[k] = pos;
+            }
+            barrier_lds();
+#pragma unroll
+            for (int m = 0; m < kSteps; ++m) {
+                const bool act = key[m] != kNoKey;
+                if (__ballot(act) == 0) continue;
+                const uint64_t peers = match_key10(key[m], act);
+                if (act) {
+                    const uint64_t before = peers & lanemask_lt();
+                    const uint32_t slot = hist[wave][key[m]] + (uint32_t)__builtin_popcountll(before);
+                    a.col_idx[slot] = (int32_t)srcv[m];
+                    if (before == 0) hist[wave][key[m]] += (uint32_t)__builtin_popcountll(peers);
+                }
+            }
+        }
+        barrier_lds();
+    }
+}
+
+// Eq. (2) per packed query row p = cu_q[i] + s:
+// dQ[p] = sum over docs j with a token, ascending, of g[i,j] D[cu_d[j] + argmax[i,j,s]].
+template <int E>
+__global__ __launch_bounds__(kGatherThreads) void vbwd_dq_kernel(VarBwdArgs a)
+{
+    __shared__ int64_t dbase[kDqDocs];
+    __shared__ int32_t dlen[kDqDocs];
+    __shared__ int32_t am[kDqDocs][kGroups];
+    __shared__ float wq[kDqDocs][kGroups];
+    __shared__ int32_t qi[kGroups], qs[kGroups];
+    const int64_t Nd = a.Nd, Tq = a.Tq;
+    const int64_t p0 = (int64_t)blockIdx.x * kGroups;
+    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+    const int64_t p = p0 + grp;
+    const bool row_ok = p < Tq;
+    if (tid < kGroups) {
+        int i = 0, s = 0;
+        if (p0 + tid < Tq) {
+            i = seg_of(a.cu_q, (int)a.Nq + 1, p0 + tid);
+            i = i < (int)a.Nq ? i : (int)a.Nq - 1;  // precondition guard
+            int64_t sv = p0 + tid - a.cu_q[i];
+            s = (int)(sv < 0 ? 0 : (sv >= a.max_lq ? a.max_lq - 1 : sv));  // precondition guard
+        }
+        qi[tid] = i;
+        qs[tid] = s;
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // with no doc token at all there is no D row to gather (dQ = 0)
+    for (int64_t j0 = 0; j0 < (a.Td > 0 ? Nd : 0); j0 += kDqDocs) {
+        const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
+        barrier_lds();
+        if (tid < nj) {
+            const int64_t b = a.cu_d[j0 + tid];
+            int64_t l = (int64_t)a.cu_d[j0 + tid + 1] - b;
+            if (b < 0 || b >= a.Td) l = 0;
+            else if (l > a.Td - b) l = a.Td - b;
+            dbase[tid] = b;
+            dlen[tid] = (int32_t)(l < 0 ? 0 : l);
+        }
+        barrier_lds();
+        for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
+            const int jj = e / kGroups, gg = e % kGroups;
+            int32_t t = 0;
+            float w = 0.f;
+            if (jj < nj && p0 + gg < Tq && dlen[jj] > 0) {
+                const int64_t ij = (int64_t)qi[gg] * Nd + j0 + jj;
+                t = a.argmax[ij * a.max_lq + qs[gg]];
+                t = t < 0 ? 0 : (t >= dlen[jj] ? dlen[jj] - 1 : t);  // precondition guard
+                w = a.g[ij];
+            }
+            am[jj][gg] = t;
+            wq[jj][gg] = w;
+        }
+        barrier_lds();
+        if (!row_ok) continue;
+        int jj = 0;
+        for (; jj + 8 <= nj; jj += 8) {
+            float x[8][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t row = dlen[jj + u] > 0 ? dbase[jj + u] + am[jj + u][grp] : 0;
+                load8<E>(a.D, row * kD + 8 * l16, x[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float w = wq[jj + u][grp];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[u][k], acc[k]);
+            }
+        }
+        for (; jj < nj; ++jj) {
+            float x[8];
+            const int64_t row = dlen[jj] > 0 ? dbase[jj] + am[jj][grp] : 0;
+            load8<E>(a.D, row * kD + 8 * l16, x);
+            const float w = wq[jj][grp];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
+        }
+    }
+    if (row_ok) store8(a.dQ + p * kD + 8 * l16, acc);
+}
+
+// Eq. (3) per packed doc row r: the sources of CSR row r, in order, each
+// g[i,j] Q[cu_q[i] + s]. Workgroup = a block of rows; group g owns rows
+// r_begin + g + 64 k.
+template <int E>
+__global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXSIM_DD_WAVES))) void vbwd_dd_kernel(
+    VarBwdArgs a, int rows_per_block)
+{
+    constexpr int kDdGroups = kDdThreads / 16;
+    const int64_t Nd = a.Nd, Nq = a.Nq, Tq = a.Tq;
+    const int64_t r_begin = (int64_t)blockIdx.x * rows_per_block;
+    const int64_t r_end = r_begin + rows_per_block < a.Td ? r_begin + rows_per_block : a.Td;
+    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+    const int gbase = tid & 63 & ~15;
+    const uint32_t mlq = (uint32_t)a.max_lq, ndm = (uint32_t)(Nd * a.max_lq);
+    for (int64_t r = r_begin + grp; r < r_end; r += kDdGroups) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // a valid row lists at most Tq sources inside col_idx; the bounds
+        // also hold for any row_ptr content
+        int64_t e0 = a.row_ptr[r], e1 = a.row_ptr[r + 1];
+        e0 = e0 < 0 ? 0 : (e0 > a.nnz_cap ? a.nnz_cap : e0);
+        e1 = e1 < e0 ? e0 : (e1 > a.nnz_cap ? a.nnz_cap : e1);
+        e1 = e1 - e0 > Tq ? e0 + Tq : e1;
+        for (int64_t e = e0; e < e1; e += 16) {
+            const int cnt = (int)(e1 - e < 16 ? e1 - e : 16);
+            int64_t qrow = 0;
+            float w = 0.f;
+            if (l16 < cnt) {
+                const uint32_t x = (uint32_t)a.col_idx[e + l16];
+                uint32_t i = x / ndm;
+                const uint32_t rem = x - i * ndm;
+                uint32_t jd = rem / mlq;
+                const uint32_t s = rem - jd * mlq;
+                // in range for any CSR content (guards the gathers)
+                i = i < (uint32_t)Nq ? i : (uint32_t)Nq - 1;
+                jd = jd < (uint32_t)Nd ? jd : (uint32_t)Nd - 1;
+                qrow = (int64_t)a.cu_q[i] + s;
+                qrow = qrow < 0 ? 0 : (qrow < Tq ? qrow : Tq - 1);
+                w = a.g[(int64_t)i * Nd + jd];
+            }
+            int k = 0;
+            for (; k + kDdUnroll <= cnt; k += kDdUnroll) {
+                float xv[kDdUnroll][8];
+                float ww[kDdUnroll];
+#pragma unroll
+                for (int u = 0; u < kDdUnroll; ++u) {
+                    const int64_t qr = __shfl(qrow, gbase + k + u, 64);
+                    ww[u] = __shfl(w, gbase + k + u, 64);
+                    load8<E>(a.Q, qr * kD + 8 * l16, xv[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < kDdUnroll; ++u)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(ww[u], xv[u][q], acc[q]);
+            }
+            for (; k < cnt; ++k) {
+                const int64_t qr = __shfl(qrow, gbase + k, 64);
+                const float wk = __shfl(w, gbase + k, 64);
+                float xv[8];
+                load8<E>(a.Q, qr * kD + 8 * l16, xv);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wk, xv[q], acc[q]);
+            }
+        }
+        store8(a.dD + r * kD + 8 * l16, acc);
+    }
+}
+
+template <int E>
+static hipError_t launch_bwd_varlen_t(VarBwdArgs a, hipStream_t stream)
+{
+    hipError_t err;
+    // segment starts and row_ptr[Td] (always: row_ptr has Td + 1 entries),
+    // then the CSR (only docs with a token have rows)
+    hipLaunchKernelGGL(vbwd_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.Td > 0 && a.Nd > 0) {  // (with no query rows every row_ptr entry is 0)
+        hipLaunchKernelGGL(vbwd_csr_kernel, dim3((unsigned)a.Nd), dim3(kCsrThreads), 0, stream, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (a.Tq > 0) {
+        const int64_t blocks = (a.Tq + kGroups - 1) / kGroups;
+        hipLaunchKernelGGL(vbwd_dq_kernel<E>, dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (a.Td > 0) {
+        // about two workgroups per CU, whole 64-row steps
+        int64_t rpb = (a.Td + 2 * (int64_t)device_cu_count() - 1) / (2 * (int64_t)device_cu_count());
+        rpb = (rpb + 63) / 64 * 64;
+        if (rpb > 4096) rpb = 4096;
+        const int64_t blocks = (a.Td + rpb - 1) / rpb;
+        hipLaunchKernelGGL(vbwd_dd_kernel<E>, dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a, (int)rpb);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_bwd_varlen(int elem, VarBwdArgs a, hipStream_t stream)
+{
+    switch (elem) {
+    case kF16: return launch_bwd_varlen_t<kF16>(a, stream);
+    case kBF16: return launch_bwd_varlen_t<kBF16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace maxsim

@@ -107,10 +107,21 @@ __attribute__((amdgpu_waves_per_eu(MAXSIM_VARLEN_WAVES_PER_EU))) void fwd_varlen
     const int U = a.units;
     if (unit >= U) return;
 
+    // a unit is a range of whole docs scored against every query, or with a
+    // pair list the one listed (query, doc) pair `unit`
+    const bool pairs = a.pair_q != nullptr;
     const int Nd = (int)a.Nd;
-    const int64_t T = a.cu_d[Nd];
-    const int jb = unit == 0 ? 0 : nearest_boundary(a.cu_d, Nd, (T * unit) / U);
-    const int je = unit + 1 == U ? Nd : nearest_boundary(a.cu_d, Nd, (T * (unit + 1)) / U);
+    int jb, je, iq = 0;
+    if (pairs) {
+        const int32_t pq = a.pair_q[unit], pd = a.pair_d[unit];
+        iq = uniform(pq < 0 ? 0 : (pq >= a.Nq ? (int)a.Nq - 1 : pq));  // precondition guard
+        jb = uniform(pd < 0 ? 0 : (pd >= Nd ? Nd - 1 : pd));
+        je = jb + 1;
+    } else {
+        const int64_t T = a.cu_d[Nd];
+        jb = unit == 0 ? 0 : nearest_boundary(a.cu_d, Nd, (T * unit) / U);
+        je = unit + 1 == U ? Nd : nearest_boundary(a.cu_d, Nd, (T * (unit + 1)) / U);
+    }
     if (jb >= je) return;
 
     // token range of the unit; offsets below are relative to u0 and fit int32
@@ -154,15 +165,19 @@ __attribute__((amdgpu_waves_per_eu(MAXSIM_VARLEN_WAVES_PER_EU))) void fwd_varlen
         }
     };
 
-    for (int64_t i = blockIdx.y; i < a.Nq; i += gridDim.y) {
+    const int64_t i_begin = pairs ? iq : blockIdx.y, i_end = pairs ? iq + 1 : a.Nq;
+    const int64_t i_step = pairs ? 1 : gridDim.y;
+    for (int64_t i = i_begin; i < i_end; i += i_step) {
         const int64_t q0 = a.cu_q[i];
         int64_t lq64 = (int64_t)a.cu_q[i + 1] - q0;
         if (lq64 > a.max_lq) lq64 = a.max_lq;
         if (lq64 < 0) lq64 = 0;
         const int lq = uniform((int)lq64);
         const int npass = lq == 0 ? 1 : (lq + 16 * NTQ - 1) / (16 * NTQ);
-        float* score_row = a.scores + i * a.Nd;
-        int32_t* arg_row = ARGMAX ? a.argmax + i * a.Nd * (int64_t)a.max_lq : nullptr;
+        // outputs of doc j are at [j - j_out] of these rows
+        const int j_out = pairs ? jb : 0;
+        float* score_row = a.scores + (pairs ? (int64_t)unit : i * a.Nd);
+        int32_t* arg_row = ARGMAX ? a.argmax + (pairs ? (int64_t)unit : i * a.Nd) * (int64_t)a.max_lq : nullptr;
 
         for (int pass = 0; pass < npass; ++pass) {
             // ---- query fragments (B operand: col = token, k-quarter g) --------
@@ -229,7 +244,7 @@ __attribute__((amdgpu_waves_per_eu(MAXSIM_VARLEN_WAVES_PER_EU))) void fwd_varlen
                     if constexpr (ARGMAX) {
                         if (g == 0 && tok_ok[n]) {
                             const int s = pass * 16 * NTQ + n * 16 + col;
-                            arg_row[(int64_t)j * a.max_lq + s] = fin ? iv - doc_start : 0;
+                            arg_row[(int64_t)(j - j_out) * a.max_lq + s] = fin ? iv - doc_start : 0;
                         }
                     }
                     m[n] = -__builtin_inff();
@@ -237,9 +252,9 @@ __attribute__((amdgpu_waves_per_eu(MAXSIM_VARLEN_WAVES_PER_EU))) void fwd_varlen
                 }
                 if constexpr (ARGMAX) {
                     if (pass == 0)  // rows past the query's length are 0
-                        for (int s = lq + lane; s < a.max_lq; s += 64) arg_row[(int64_t)j * a.max_lq + s] = 0;
+                        for (int s = lq + lane; s < a.max_lq; s += 64) arg_row[(int64_t)(j - j_out) * a.max_lq + s] = 0;
                 }
-                if (lane == 0) score_row[j] = pass == 0 ? total : score_row[j] + total;
+                if (lane == 0) score_row[j - j_out] = pass == 0 ? total : score_row[j - j_out] + total;
             };
 
             // fold tile rows [lo, hi) (tile-relative, uniform) into the state
@@ -358,8 +373,12 @@ static hipError_t launch_varlen_t(VarlenArgs a, hipStream_t stream)
     int64_t units = a.Nd / 8;  // about 8+ docs per unit keeps the per-unit setup amortised
     if (units < 1) units = 1;
     if (units > max_units) units = max_units;
+    int64_t gy = a.Nq < 65535 ? a.Nq : 65535;
+    if (a.pair_q) {  // one unit per listed pair
+        units = a.npairs;
+        gy = 1;
+    }
     a.units = (int32_t)units;
-    const int64_t gy = a.Nq < 65535 ? a.Nq : 65535;
     dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock), (unsigned)gy);
     hipLaunchKernelGGL(kern, grid, dim3(kUnitsPerBlock * 64), 0, stream, a);
     return hipGetLastError();

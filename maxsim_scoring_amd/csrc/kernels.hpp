@@ -38,7 +38,10 @@ struct VarlenArgs {
     int32_t* argmax;  // [Nq, Nd, max_lq] or null
     int64_t Nq, Nd;
     int32_t max_lq;
-    int32_t units;    // streaming units (waves) per query
+    int32_t units;           // streaming units (waves) per query
+    const int32_t* pair_q;   // [npairs] pair list or null (score listed pairs only)
+    const int32_t* pair_d;
+    int64_t npairs;
 };
 
 struct BwdArgs {
@@ -53,6 +56,22 @@ struct BwdArgs {
     int32_t* row_ptr;
     int32_t* col_idx;
     int64_t Nq, Nd, Lq, Ld;
+};
+
+struct VarBwdArgs {
+    const void* Q;
+    const int32_t* cu_q;  // [Nq + 1]
+    const void* D;
+    const int32_t* cu_d;  // [Nd + 1]
+    const int32_t* argmax;  // [Nq, Nd, max_lq] doc-relative
+    const float* g;         // [Nq, Nd]
+    float* dQ;              // [Tq, d]
+    float* dD;              // [Td, d]
+    int32_t* row_ptr;       // [Td + 1]
+    int32_t* col_idx;       // [Tq * (docs with a token)]
+    int64_t Nq, Nd, Tq, Td;
+    int64_t nnz_cap;  // entries of col_idx (Tq * Nd)
+    int32_t max_lq;
 };
 
 struct TopkArgs {
@@ -74,5 +93,6 @@ hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t
 hipError_t launch_fwd_varlen(int elem, VarlenArgs a, hipStream_t stream);
 hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream);
 hipError_t launch_topk(TopkArgs a, hipStream_t stream);
+hipError_t launch_bwd_varlen(int elem, VarBwdArgs a, hipStream_t stream);
 
 }  // namespace maxsim

@@ -320,6 +320,25 @@ def draw_argmax(seed: int, Nq: int, Nd: int, Lq: int, Ld: int,
     return torch.from_numpy(a.astype(np.int32))
 
 
+def draw_argmax_varlen(seed: int, cu_q, cu_d, max_lq: int, hub_frac: float = 0.0) -> torch.Tensor:
+    """int32 [Nq,Nd,max_lq] doc-relative indices uniform over each packed doc's
+    tokens for the real rows of each query; rows past a query's length and
+    every row of an empty doc are 0 (the packed forward's layout). With
+    ``hub_frac`` > 0 that fraction of real entries points at token 0."""
+    cq = np.asarray(cu_q, dtype=np.int64)
+    cd = np.asarray(cu_d, dtype=np.int64)
+    lq, ld = np.diff(cq), np.diff(cd)
+    rng = np.random.default_rng([seed, _S_ARG])
+    Nq, Nd = len(lq), len(ld)
+    u = rng.random((Nq, Nd, max_lq))
+    a = np.floor(u * np.maximum(ld, 1)[None, :, None]).astype(np.int64)
+    a = np.minimum(a, np.maximum(ld, 1)[None, :, None] - 1)
+    if hub_frac > 0:
+        a[rng.random((Nq, Nd, max_lq)) < hub_frac] = 0
+    real = (np.arange(max_lq)[None, None, :] < lq[:, None, None]) & (ld[None, :, None] > 0)
+    return torch.from_numpy(np.where(real, a, 0).astype(np.int32))
+
+
 # --------------------------------------------------------------------------
 # Small and stress inputs for parity (not timed).
 # --------------------------------------------------------------------------

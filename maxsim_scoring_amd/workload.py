@@ -87,3 +87,23 @@ def bwd_compulsory_bytes(nq: int, nd: int, lq: int, ld: int, d: int, elem: int,
     b += nq * lq * d * 4 + nd * ld * d * 4
     b += 2 * ((nrows + 1) * 4 + nsrc * 4)
     return b
+
+
+def bwd_varlen_compulsory_bytes(nq: int, nd: int, max_lq: int, tq: int, td: int, live_docs: int,
+                                d: int, elem: int) -> int:
+    """Padding-free backward: argmax [Nq,Nd,max_lq], g, packed Q and D and both
+    offset arrays read once; dQ, dD fp32 written once; the CSR (row_ptr [Td+1],
+    col_idx of Tq per doc with a token) written once and read back once."""
+    nnz = tq * live_docs
+    b = nq * nd * max_lq * 4 + nq * nd * 4 + (tq + td) * d * elem + (nq + 1 + nd + 1) * 4
+    b += (tq + td) * d * 4
+    b += 2 * ((td + 1) * 4 + nnz * 4)
+    return b
+
+
+def pairs_varlen_fwd_bytes(q_rows: int, d_rows_per_pair, d: int, elem: int) -> int:
+    """Listed packed pairs: the queries read once (they are shared by many
+    pairs), each pair's doc rows read once (a doc listed twice is read twice),
+    both pair indices read, one score written per pair."""
+    n = len(d_rows_per_pair)
+    return (int(q_rows) + int(sum(d_rows_per_pair))) * d * elem + n * (4 + 4 + 4)

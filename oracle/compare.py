@@ -157,6 +157,32 @@ def varlen_argmax_float(got, ref, Q64, cu_q, D64, cu_d, q_index, d_index):
     return argmax_float(got, ref, qr, dr, ok)
 
 
+def pairs_varlen_argmax_float(got, ref, Q64, cu_q, D64, cu_d, pair_q, pair_d):
+    """argmax_float for a pair list over packed sequences; got/ref are
+    [P, max_lq] (pair p: packed query pair_q[p] against packed doc pair_d[p])."""
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_d = np.asarray(cu_d, dtype=np.int64)
+    pq = np.asarray(pair_q)
+    pd = np.asarray(pair_d)
+
+    def qr(e):
+        return Q64[cu_q[pq[e[0]]] + e[1]]
+
+    def dr(e, t):
+        j = pd[e[0]]
+        if t < 0 or t >= cu_d[j + 1] - cu_d[j]:
+            return None
+        return D64[cu_d[j] + t]
+
+    def ok(e, t):
+        i, j = pq[e[0]], pd[e[0]]
+        if e[1] >= cu_q[i + 1] - cu_q[i]:
+            return False  # rows past the query length must be 0 exactly
+        return 0 <= t < cu_d[j + 1] - cu_d[j]
+
+    return argmax_float(got, ref, qr, dr, ok)
+
+
 U24 = 2.0 ** -24
 
 

@@ -36,6 +36,7 @@ def test_exports_every_declared_symbol(L):
     names = _declared()
     assert set(names) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd",
                           "maxsim_fwd_i8_tok", "maxsim_fwd_pairs", "maxsim_topk",
+                          "maxsim_fwd_pairs_varlen", "maxsim_bwd_varlen",
                           "maxsim_status_string", "maxsim_abi_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -167,6 +168,49 @@ def test_pairs_validation(L):
     assert call(pd=MIS2) == ERR_UNSUPPORTED
     assert call(Q=MIS8) == ERR_UNSUPPORTED
     assert call(P=1 << 22, Lq=1 << 10, am=FAKE) == ERR_OVERFLOW
+
+
+def test_pairs_varlen_validation(L):
+    def f(dtype=0, Q=FAKE, cq=FAKE, Nq=2, mlq=8, D=FAKE, cd=FAKE, Nd=3, d=128, pq=FAKE, pd=FAKE,
+          P=4, sc=FAKE, am=None):
+        return L.maxsim_fwd_pairs_varlen(dtype, Q, cq, Nq, mlq, D, cd, Nd, d, pq, pd, P, sc, am,
+                                         None)
+    assert f(P=-1) == ERR_SHAPE
+    assert f(mlq=-1) == ERR_SHAPE
+    assert f(Nq=0) == ERR_SHAPE                # a pair needs a query
+    assert f(d=64) == ERR_UNSUPPORTED
+    assert f(dtype=3) == ERR_UNSUPPORTED
+    assert f(pq=None) == ERR_NULL
+    assert f(cd=None) == ERR_NULL
+    assert f(sc=None) == ERR_NULL
+    assert f(P=0, sc=None) == OK                # nothing to do, nothing enqueued
+    assert f(pd=MIS2) == ERR_UNSUPPORTED
+    assert f(Q=MIS8) == ERR_UNSUPPORTED
+    assert f(P=1 << 28, mlq=16, am=FAKE) == ERR_OVERFLOW
+
+
+def test_bwd_varlen_validation(L):
+    def f(dtype=1, Q=FAKE, cq=FAKE, Nq=2, Tq=40, mlq=32, D=FAKE, cd=FAKE, Nd=3, Td=500, d=128,
+          am=FAKE, g=FAKE, dQ=FAKE, dD=FAKE, rp=FAKE, ci=FAKE):
+        return L.maxsim_bwd_varlen(dtype, Q, cq, Nq, Tq, mlq, D, cd, Nd, Td, d, am, g, dQ, dD, rp,
+                                   ci, None)
+    assert f(Tq=-1) == ERR_SHAPE
+    assert f(Nd=-2) == ERR_SHAPE
+    assert f(Nq=0) == ERR_SHAPE                 # packed query rows without a query
+    assert f(Nd=0) == ERR_SHAPE                 # packed doc rows without a doc
+    assert f(mlq=0) == ERR_SHAPE                # query rows need a max_lq slot
+    assert f(d=256) == ERR_UNSUPPORTED
+    assert f(dtype=2) == ERR_UNSUPPORTED
+    assert f(cq=None) == ERR_NULL
+    assert f(rp=None) == ERR_NULL
+    assert f(ci=None) == ERR_NULL
+    assert f(dQ=None) == ERR_NULL
+    assert f(am=None) == ERR_NULL
+    assert f(Nq=1 << 16, Nd=1 << 10, mlq=32) == ERR_OVERFLOW   # flat source index
+    assert f(Tq=1 << 22, Nd=1 << 10, mlq=1 << 12) == ERR_OVERFLOW  # CSR entries
+    assert f(Td=1 << 31) == ERR_OVERFLOW
+    assert f(dD=MIS8) == ERR_UNSUPPORTED
+    assert f(rp=MIS2) == ERR_UNSUPPORTED
 
 
 def test_topk_validation(L):

@@ -460,3 +460,98 @@ def test_two_stage_scan(ms, oracle_mod):
     _assert_close("scores", val.cpu().numpy(), rv[:, :5])
     r8, _ = oracle_mod.fwd_i8_tok(w.Q, w.q_scale, w.D, w.d_scale, None, w.d_mask, want_argmax=False)
     _assert_close("int8 stage scores", s8.cpu().numpy(), r8)
+
+
+# ------------------------------------------- padding-free backward, packed pairs
+
+VARBWD_CASES = [
+    # (query lengths, doc lengths, dtype, hub fraction, argmax from the forward)
+    ([5, 12, 3], [7, 0, 19, 3, 1], torch.float16, 0.0, True),     # an empty doc
+    ([32] * 4, list(range(50, 300, 13)), torch.bfloat16, 0.0, True),
+    ([64] * 4, [64] * 3, torch.bfloat16, 0.7, False),             # hub token
+    ([2], [5000, 7], torch.float16, 0.0, False),                  # CSR bins in several rounds
+    ([128] * 130, [10, 0, 20], torch.float16, 0.0, False),        # > 16384 sources: two chunks
+    ([0, 3, 0], [4, 0, 4], torch.bfloat16, 0.0, True),            # empty queries
+    ([3], [0, 0], torch.float16, 0.0, True),                      # no doc token at all
+    ([0], [5, 3], torch.float16, 0.0, True),                      # no query row at all
+]
+
+
+def _run_bwd_varlen(ms, w, argmax, g):
+    out = ms.maxsim_bwd_varlen(_g(w.Q), _g(w.cu_q), w.max_lq, _g(w.D), _g(w.cu_d), _g(argmax), _g(g))
+    torch.cuda.synchronize()
+    return tuple(x.cpu() for x in out)
+
+
+@pytest.mark.parametrize("case", VARBWD_CASES, ids=lambda c: f"q{len(c[0])}_d{len(c[1])}_hub{c[3]}")
+def test_bwd_varlen(ms, oracle_mod, case):
+    ql, dl, dt, hub, from_fwd = case
+    _say(f"bwd varlen {case[0][:4]} {case[1][:6]} {dt} hub {hub}")
+    seed = 900 + len(ql) + len(dl)
+    w = synth.random_varlen(seed, ql, dl, dtype=dt, max_lq=max(max(ql), 1))
+    if from_fwd:
+        _, ra = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+        argmax = torch.from_numpy(ra)
+    else:
+        argmax = synth.draw_argmax_varlen(seed, w.cu_q, w.cu_d, w.max_lq, hub_frac=hub)
+    g = synth.upstream_grad(seed, len(ql), len(dl))
+    dQ, dD, rp, ci = _run_bwd_varlen(ms, w, argmax, g)
+    rdQ, rdD, rrp, rci = oracle_mod.bwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, argmax, g)
+    assert np.array_equal(rp.numpy(), rrp), "row_ptr"
+    assert np.array_equal(ci.numpy()[:len(rci)], rci), "col_idx"
+    _assert_close("dQ", dQ.numpy(), rdQ)
+    _assert_close("dD", dD.numpy(), rdD)
+    again = _run_bwd_varlen(ms, w, argmax, g)
+    n = len(rci)
+    assert all(torch.equal(x, y) for x, y in zip(again[:3], (dQ, dD, rp))), "not deterministic"
+    assert torch.equal(again[3][:n], ci[:n]), "not deterministic"
+
+
+def test_bwd_varlen_colpali_packed(ms, oracle_mod):
+    """The ColPali training shapes packed without padding: 128 queries of
+    16-128 tokens against 128 docs of 768-1024 patches (the masked prefixes
+    of the cross-product workload), argmax from the GPU forward; every output
+    compared."""
+    _say("bwd varlen colpali packed")
+    rng = np.random.default_rng(3)
+    ql = rng.integers(16, 129, 128)
+    dl = rng.integers(768, 1025, 128)
+    w = synth.random_varlen(31, ql, dl, dtype=torch.bfloat16, max_lq=128)
+    _, a = ms.maxsim_fwd_varlen(_g(w.Q), _g(w.cu_q), w.max_lq, _g(w.D), _g(w.cu_d), want_argmax=True)
+    argmax = a.cpu()
+    g = synth.upstream_grad(31, 128, 128)
+    dQ, dD, rp, ci = _run_bwd_varlen(ms, w, argmax, g)
+    rdQ, rdD, rrp, rci = oracle_mod.bwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, argmax, g)
+    assert np.array_equal(rp.numpy(), rrp), "row_ptr"
+    assert np.array_equal(ci.numpy()[:len(rci)], rci), "col_idx"
+    _assert_close("dQ", dQ.numpy(), rdQ)
+    _assert_close("dD", dD.numpy(), rdD)
+
+
+PAIRS_VARLEN_CASES = [
+    # (query lengths, doc lengths, dtype, P)
+    ([32, 5, 0, 17], [50, 0, 1, 300, 64, 16], torch.float16, 40),
+    ([130, 8], [33, 80, 0, 200], torch.bfloat16, 11),     # multi-pass query
+    ([32], synth.rerank_lengths(5, 3000, 50, 300).tolist(), torch.float16, 2000),
+]
+
+
+@pytest.mark.parametrize("case", PAIRS_VARLEN_CASES, ids=lambda c: f"q{len(c[0])}_d{len(c[1])}_p{c[3]}")
+def test_pairs_varlen(ms, oracle_mod, case):
+    ql, dl, dt, P = case
+    _say(f"pairs varlen q{len(ql)} d{len(dl)} P{P}")
+    w = synth.random_varlen(950 + P, ql, dl, dtype=dt)
+    pq, pd = synth.random_pairs(950 + P, len(ql), len(dl), P)
+    s, a = ms.maxsim_fwd_pairs_varlen(_g(w.Q), _g(w.cu_q), w.max_lq, _g(w.D), _g(w.cu_d), _g(pq),
+                                      _g(pd), want_argmax=True)
+    torch.cuda.synchronize()
+    rs, ra = oracle_mod.fwd_pairs_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, pq, pd)
+    _assert_close("scores", s.cpu().numpy(), rs)
+    n, acc, bad = compare.pairs_varlen_argmax_float(a.cpu().numpy(), ra, w.Q.double().numpy(),
+                                                    w.cu_q.numpy(), w.D.double().numpy(),
+                                                    w.cu_d.numpy(), pq.numpy(), pd.numpy())
+    assert not bad, f"argmax mismatches outside the near-tie bound: {bad[:5]}"
+    s2, _ = ms.maxsim_fwd_pairs_varlen(_g(w.Q), _g(w.cu_q), w.max_lq, _g(w.D), _g(w.cu_d), _g(pq),
+                                       _g(pd))
+    torch.cuda.synchronize()
+    _assert_close("scores (no argmax)", s2.cpu().numpy(), rs)
