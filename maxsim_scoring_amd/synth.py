@@ -464,3 +464,24 @@ def random_pairs(seed: int, Nq: int, Nd: int, P: int) -> tuple[torch.Tensor, tor
     rng = np.random.default_rng([seed, _S_ARG])
     return (torch.from_numpy(rng.integers(0, Nq, size=P).astype(np.int32)),
             torch.from_numpy(rng.integers(0, Nd, size=P).astype(np.int32)))
+
+
+# -------------------------------------------------------------------------- Chamfer
+
+_S_PTS = 8  # stream of point-cloud draws
+
+
+def point_clouds(seed: int, B: int, N: int, M: int) -> tuple[torch.Tensor, torch.Tensor]:
+    """Batches of 3-D point sets P [B,N,3] and Q [B,M,3], float32, coordinates
+    i.i.d. N(0,1) (a stand-in for shape-matching point clouds)."""
+    rng = np.random.default_rng([seed, _S_PTS])
+    P = rng.standard_normal((B, N, 3)).astype(np.float32)
+    Q = rng.standard_normal((B, M, 3)).astype(np.float32)
+    return torch.from_numpy(P), torch.from_numpy(Q)
+
+
+def chamfer_grads(seed: int, B: int, N: int, M: int) -> tuple[torch.Tensor, torch.Tensor]:
+    """Upstream gradients of the per-point distances, [B,N] and [B,M] float32."""
+    rng = np.random.default_rng([seed, _S_G])
+    return (torch.from_numpy(rng.standard_normal((B, N)).astype(np.float32)),
+            torch.from_numpy(rng.standard_normal((B, M)).astype(np.float32)))

@@ -641,4 +641,123 @@ int oracle_fwd_pairs_varlen_f64(const double* Q, const int32_t* cu_q, int64_t Nq
     return 0;
 }
 
-int oracle_version(void) { return 3; }
+/* ------------------------------------------------------------------------ */
+/* Chamfer distance ([FM] Sec. 4.2.4): batch b holds point sets P[b] (N x 3) */
+/* and Q[b] (M x 3). dist1[b,p] = min over q of ||p - q||^2 with idx1 the    */
+/* lowest q attaining it; dist2/idx2 the same from Q to P; loss[b] =         */
+/* (1/N) sum_p dist1 + (1/M) sum_q dist2. Squared distances are summed over  */
+/* the 3 coordinates in fp64 from the exact fp32 inputs.                     */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const double *A, *Bp;
+    int64_t na, nb;
+    double* dist;
+    int32_t* idx;
+} cham_ctx;
+
+/* item = (batch, source point): min over the batch's target points, ascending */
+static void cham_item(void* p_, int64_t k)
+{
+    cham_ctx* c = (cham_ctx*)p_;
+    int64_t b = k / c->na;
+    const double* a = c->A + k * 3;
+    const double* tgt = c->Bp + b * c->nb * 3;
+    double best = INFINITY;
+    int32_t arg = 0;
+    for (int64_t t = 0; t < c->nb; ++t) {
+        double dx = a[0] - tgt[t * 3], dy = a[1] - tgt[t * 3 + 1], dz = a[2] - tgt[t * 3 + 2];
+        double v = dx * dx + dy * dy + dz * dz;
+        if (v < best) { /* strict: the lowest index wins ties */
+            best = v;
+            arg = (int32_t)t;
+        }
+    }
+    c->dist[k] = best;
+    c->idx[k] = arg;
+}
+
+int oracle_chamfer_fwd(const double* P, const double* Q, int64_t B, int64_t N, int64_t M,
+                       double* dist1, int32_t* idx1, double* dist2, int32_t* idx2, double* loss,
+                       int nthreads)
+{
+    if (B < 0 || N < 0 || M < 0) return -1;
+    if (B > 0 && (N == 0 || M == 0)) return -2; /* a min over an empty set */
+    cham_ctx c1 = {P, Q, N, M, dist1, idx1};
+    parallel_for(B * N, nthreads, cham_item, &c1);
+    cham_ctx c2 = {Q, P, M, N, dist2, idx2};
+    parallel_for(B * M, nthreads, cham_item, &c2);
+    if (loss)
+        for (int64_t b = 0; b < B; ++b) {
+            double s1 = 0.0, s2 = 0.0;
+            for (int64_t p = 0; p < N; ++p) s1 += dist1[b * N + p];
+            for (int64_t q = 0; q < M; ++q) s2 += dist2[b * M + q];
+            loss[b] = s1 / (double)N + s2 / (double)M;
+        }
+    return 0;
+}
+
+/* Inverse map of one direction by counting sort: sources k = b*ns + s with  */
+/* destination row b*nr + idx[k]; rows list their sources ascending.         */
+static void seg_csr(const int32_t* idx, int64_t B, int64_t ns, int64_t nr, int32_t* row_ptr,
+                    int32_t* col_idx)
+{
+    int64_t nrows = B * nr, nsrc = B * ns;
+    int64_t* cnt = (int64_t*)calloc((size_t)(nrows + 1), sizeof(int64_t));
+    for (int64_t k = 0; k < nsrc; ++k) cnt[(k / ns) * nr + idx[k]] += 1;
+    int64_t run = 0;
+    for (int64_t r = 0; r < nrows; ++r) {
+        row_ptr[r] = (int32_t)run;
+        run += cnt[r];
+    }
+    row_ptr[nrows] = (int32_t)run;
+    for (int64_t r = 0; r < nrows; ++r) cnt[r] = row_ptr[r];
+    for (int64_t k = 0; k < nsrc; ++k) col_idx[cnt[(k / ns) * nr + idx[k]]++] = (int32_t)k;
+    free(cnt);
+}
+
+/* Gradient of sum g1*dist1 + sum g2*dist2 at the saved argmins:            */
+/*   dP[b,p] = 2 g1[b,p] (P[b,p] - Q[b,idx1]) + sum over CSR2 row (b,p) of  */
+/*             2 g2[b,q] (P[b,p] - Q[b,q])                                  */
+/*   dQ[b,q] = 2 g2[b,q] (Q[b,q] - P[b,idx2]) + sum over CSR1 row (b,q) of  */
+/*             2 g1[b,p] (Q[b,q] - P[b,p])                                  */
+int oracle_chamfer_bwd(const double* P, const double* Q, int64_t B, int64_t N, int64_t M,
+                       const int32_t* idx1, const int32_t* idx2, const double* g1,
+                       const double* g2, double* dP, double* dQ, int32_t* row_ptr1,
+                       int32_t* col_idx1, int32_t* row_ptr2, int32_t* col_idx2)
+{
+    if (B < 0 || N < 0 || M < 0) return -1;
+    if (B > 0 && (N == 0 || M == 0)) return -2;
+    for (int64_t k = 0; k < B * N; ++k)
+        if (idx1[k] < 0 || idx1[k] >= M) return -2;
+    for (int64_t k = 0; k < B * M; ++k)
+        if (idx2[k] < 0 || idx2[k] >= N) return -2;
+    seg_csr(idx1, B, N, M, row_ptr1, col_idx1);
+    seg_csr(idx2, B, M, N, row_ptr2, col_idx2);
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t p = 0; p < N; ++p) {
+            int64_t r = b * N + p;
+            const double* x = P + r * 3;
+            const double* y = Q + (b * M + idx1[r]) * 3;
+            for (int k = 0; k < 3; ++k) dP[r * 3 + k] = 2.0 * g1[r] * (x[k] - y[k]);
+            for (int64_t e = row_ptr2[r]; e < row_ptr2[r + 1]; ++e) {
+                int64_t q = col_idx2[e]; /* global index b*M + q */
+                const double* z = Q + q * 3;
+                for (int k = 0; k < 3; ++k) dP[r * 3 + k] += 2.0 * g2[q] * (x[k] - z[k]);
+            }
+        }
+        for (int64_t q = 0; q < M; ++q) {
+            int64_t r = b * M + q;
+            const double* x = Q + r * 3;
+            const double* y = P + (b * N + idx2[r]) * 3;
+            for (int k = 0; k < 3; ++k) dQ[r * 3 + k] = 2.0 * g2[r] * (x[k] - y[k]);
+            for (int64_t e = row_ptr1[r]; e < row_ptr1[r + 1]; ++e) {
+                int64_t p = col_idx1[e];
+                const double* z = P + p * 3;
+                for (int k = 0; k < 3; ++k) dQ[r * 3 + k] += 2.0 * g1[p] * (x[k] - z[k]);
+            }
+        }
+    }
+    return 0;
+}
+
+int oracle_version(void) { return 4; }

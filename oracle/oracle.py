@@ -56,6 +56,11 @@ def _load():
                                               vp, vp, vp, i32]
         lib.oracle_fwd_pairs_varlen_f64.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp,
                                                     i64, vp, vp, i32]
+        lib.oracle_chamfer_fwd.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32]
+        lib.oracle_chamfer_bwd.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, vp]
+        lib.oracle_chamfer_fwd.restype = ctypes.c_int
+        lib.oracle_chamfer_bwd.restype = ctypes.c_int
         for f in (lib.oracle_fwd_f64, lib.oracle_fwd_varlen_f64, lib.oracle_fwd_i8,
                   lib.oracle_bwd_f64, lib.oracle_fwd_i8_tok, lib.oracle_topk,
                   lib.oracle_fwd_pairs_f64, lib.oracle_bwd_varlen_f64,
@@ -265,3 +270,45 @@ def fwd_pairs_varlen(Q, cu_q, max_lq, D, cu_d, pair_q, pair_d, want_argmax=True,
                                              threads or default_threads())
     _check(rc, "fwd_pairs_varlen")
     return scores, arg
+
+
+def chamfer_fwd(P, Q, threads=None):
+    """Chamfer distance of point-set batches P [B,N,3], Q [B,M,3]. Returns
+    (dist1 [B,N], idx1 int32 [B,N], dist2 [B,M], idx2 int32 [B,M], loss [B])."""
+    p = _f64(P)
+    q = _f64(Q)
+    B, N, _ = p.shape
+    M = q.shape[1]
+    d1 = np.zeros((B, N))
+    i1 = np.zeros((B, N), np.int32)
+    d2 = np.zeros((B, M))
+    i2 = np.zeros((B, M), np.int32)
+    loss = np.zeros(B)
+    rc = _load().oracle_chamfer_fwd(_p(p), _p(q), B, N, M, _p(d1), _p(i1), _p(d2), _p(i2),
+                                    _p(loss), threads or default_threads())
+    _check(rc, "chamfer_fwd")
+    return d1, i1, d2, i2, loss
+
+
+def chamfer_bwd(P, Q, idx1, idx2, grad_dist1, grad_dist2):
+    """Gradients of sum(g1*dist1) + sum(g2*dist2) at the saved argmins.
+    Returns (dP [B,N,3], dQ [B,M,3], row_ptr1 [B*M+1], col_idx1 [B*N],
+    row_ptr2 [B*N+1], col_idx2 [B*M])."""
+    p = _f64(P)
+    q = _f64(Q)
+    B, N, _ = p.shape
+    M = q.shape[1]
+    i1 = _arr(idx1, np.int32)
+    i2 = _arr(idx2, np.int32)
+    g1 = _f64(grad_dist1)
+    g2 = _f64(grad_dist2)
+    dP = np.zeros((B, N, 3))
+    dQ = np.zeros((B, M, 3))
+    rp1 = np.zeros(B * M + 1, np.int32)
+    ci1 = np.zeros(max(B * N, 1), np.int32)
+    rp2 = np.zeros(B * N + 1, np.int32)
+    ci2 = np.zeros(max(B * M, 1), np.int32)
+    rc = _load().oracle_chamfer_bwd(_p(p), _p(q), B, N, M, _p(i1), _p(i2), _p(g1), _p(g2), _p(dP),
+                                    _p(dQ), _p(rp1), _p(ci1), _p(rp2), _p(ci2))
+    _check(rc, "chamfer_bwd")
+    return dP, dQ, rp1, ci1[:B * N], rp2, ci2[:B * M]

@@ -65,3 +65,16 @@ def varlen(Q, cu_q, max_lq, D, cu_d):
             scores[i, j] = S.max(axis=1).sum()
             arg[i, j, :len(qi)] = S.argmax(axis=1)
     return scores, arg
+
+
+def chamfer(P, Q):
+    """Chamfer distance by materialising the [B,N,M] squared-distance tensor
+    (the naive form of Flash-MaxSim Sec. 4.2.4); numpy argmin returns the
+    first minimum. Returns (dist1, idx1, dist2, idx2, loss)."""
+    p = _np(P, np.float64)
+    q = _np(Q, np.float64)
+    S = ((p[:, :, None, :] - q[:, None, :, :]) ** 2).sum(-1)  # [B,N,M]
+    d1, i1 = S.min(axis=2), S.argmin(axis=2)
+    d2, i2 = S.min(axis=1), S.argmin(axis=1)
+    loss = d1.mean(axis=1) + d2.mean(axis=1)
+    return d1, i1.astype(np.int32), d2, i2.astype(np.int32), loss

@@ -577,3 +577,97 @@ def test_pairs_varlen_equals_cross_product(oracle_mod):
     rs, ra = bf.varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
     np.testing.assert_allclose(ps, rs[pq, pd], rtol=0, atol=1e-12)
     assert np.array_equal(pa, ra[pq, pd])
+
+
+# ------------------------------------------------------------------ Chamfer distance
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 5, 7), (3, 40, 13), (1, 64, 64)])
+def test_chamfer_brute_force(oracle_mod, shape):
+    B, N, M = shape
+    P, Q = synth.point_clouds(71, B, N, M)
+    d1, i1, d2, i2, loss = oracle_mod.chamfer_fwd(P, Q)
+    r1, j1, r2, j2, rl = bf.chamfer(P, Q)
+    np.testing.assert_allclose(d1, r1, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(d2, r2, rtol=1e-13, atol=0)
+    assert np.array_equal(i1, j1) and np.array_equal(i2, j2)
+    np.testing.assert_allclose(loss, rl, rtol=1e-13, atol=0)
+
+
+def test_chamfer_closed_forms(oracle_mod):
+    rng = np.random.default_rng(72)
+    P = torch.from_numpy(rng.standard_normal((2, 20, 3)).astype(np.float32))
+    # a set against itself: distance 0, each point its own nearest neighbour
+    d1, i1, d2, i2, loss = oracle_mod.chamfer_fwd(P, P)
+    assert np.all(d1 == 0) and np.all(d2 == 0) and np.all(loss == 0)
+    assert np.array_equal(i1, np.tile(np.arange(20), (2, 1))) and np.array_equal(i1, i2)
+    # one point each: both terms are the squared distance
+    a = torch.tensor([[[1.0, 2.0, 3.0]]])
+    b = torch.tensor([[[0.5, -1.0, 4.0]]])
+    _, _, _, _, loss = oracle_mod.chamfer_fwd(a, b)
+    assert loss[0] == 2 * (0.25 + 9.0 + 1.0)
+    # exact ties go to the lowest index: two equidistant targets
+    a = torch.tensor([[[0.0, 0.0, 0.0]]])
+    b = torch.tensor([[[1.0, 0.0, 0.0], [0.0, -1.0, 0.0], [0.0, 0.0, 1.0]]])
+    d1, i1, d2, i2, _ = oracle_mod.chamfer_fwd(a, b)
+    assert i1[0, 0] == 0 and d1[0, 0] == 1.0 and np.all(i2 == 0)
+    # translating both sets together changes nothing (dyadic shift: exact)
+    P, Q = synth.point_clouds(73, 2, 15, 9)
+    s = oracle_mod.chamfer_fwd(P, Q)
+    t = oracle_mod.chamfer_fwd(P + 0.5, Q + 0.5)
+    for x, y in zip(s, t):
+        np.testing.assert_allclose(x, y, rtol=1e-6, atol=1e-6)
+
+
+def test_chamfer_backward_identities(oracle_mod):
+    """At fixed argmins sum(g1*dist1) + sum(g2*dist2) is translation invariant
+    (gradients sum to zero over all points) and homogeneous of degree 2
+    (<dP,P> + <dQ,Q> = 2 * sum(g*dist))."""
+    P, Q = synth.point_clouds(74, 3, 30, 17)
+    g1, g2 = synth.chamfer_grads(74, 3, 30, 17)
+    d1, i1, d2, i2, _ = oracle_mod.chamfer_fwd(P, Q)
+    dP, dQ, *_ = oracle_mod.chamfer_bwd(P, Q, i1, i2, g1, g2)
+    np.testing.assert_allclose(dP.sum(axis=1) + dQ.sum(axis=1), 0.0, atol=1e-10)
+    lhs = float((dP * P.double().numpy()).sum() + (dQ * Q.double().numpy()).sum())
+    rhs = 2 * float((g1.double().numpy() * d1).sum() + (g2.double().numpy() * d2).sum())
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12)
+
+
+def test_chamfer_backward_finite_differences(oracle_mod):
+    P, Q = synth.point_clouds(75, 2, 6, 5)
+    P, Q = P.double(), Q.double()
+    g1, g2 = synth.chamfer_grads(75, 2, 6, 5)
+    g1, g2 = g1.double().numpy(), g2.double().numpy()
+    d1, i1, d2, i2, _ = oracle_mod.chamfer_fwd(P, Q)
+    dP, dQ, *_ = oracle_mod.chamfer_bwd(P, Q, i1, i2, g1, g2)
+    h = 1e-6
+
+    def f(Pn, Qn):
+        e1, j1, e2, j2, _ = oracle_mod.chamfer_fwd(Pn, Qn)
+        assert np.array_equal(j1, i1) and np.array_equal(j2, i2)
+        return float((g1 * e1).sum() + (g2 * e2).sum())
+
+    Pn, Qn = P.numpy(), Q.numpy()
+    for X, G, is_p in ((Pn, dP, True), (Qn, dQ, False)):
+        for idx in np.ndindex(X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            if is_p:
+                num = (f(Xp, Qn) - f(Xm, Qn)) / (2 * h)
+            else:
+                num = (f(Pn, Xp) - f(Pn, Xm)) / (2 * h)
+            assert abs(num - G[idx]) < 1e-6
+
+
+def test_chamfer_csr_matches_stable_argsort(oracle_mod):
+    B, N, M = 3, 50, 8
+    P, Q = synth.point_clouds(76, B, N, M)
+    _, i1, _, i2, _ = oracle_mod.chamfer_fwd(P, Q)
+    g1, g2 = synth.chamfer_grads(76, B, N, M)
+    _, _, rp1, ci1, rp2, ci2 = oracle_mod.chamfer_bwd(P, Q, i1, i2, g1, g2)
+    for idx, ns, nr, rp, ci in ((i1, N, M, rp1, ci1), (i2, M, N, rp2, ci2)):
+        k = np.arange(B * ns)
+        dest = (k // ns) * nr + idx.reshape(-1)
+        cnt = np.bincount(dest, minlength=B * nr)
+        assert np.array_equal(rp, np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32))
+        assert np.array_equal(ci, np.argsort(dest, kind="stable").astype(np.int32))
