@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0
+FP32_PEAK_TFLOPS = 157.3
 METRIC = ("docs/sec + achieved HBM GB/s or MFMA TFLOP/s as % of MI355X peak, per config")
 HEADLINE = "rerank"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
@@ -267,6 +268,35 @@ def bench_pairs_varlen(torch, ms, synth, wl, steps, warmup):
             "kernel": "fwd_varlen_kernel (pair list)"}
 
 
+def bench_chamfer(torch, ms, synth, wl, steps, warmup):
+    """Chamfer distance between two 100,000-point clouds (N(0,1) coordinates,
+    fp32): the forward (both nearest-neighbour directions and the loss) and the
+    backward through the saved indices. ALU-bound: 8 fp32 operations per
+    (point, point) pair and direction (3 subtractions, 3 products, 2 adds)."""
+    P, Q = synth.point_clouds(782, 1, 100_000, 100_000)
+    P, Q = P.cuda(), Q.cuda()
+    g1, g2 = (t.cuda() for t in synth.chamfer_grads(782, 1, 100_000, 100_000))
+    out = {}
+
+    def fwd():
+        out["f"] = ms.maxsim_chamfer_fwd(P, Q)
+
+    total, _ = time_steps(torch, fwd, steps, warmup)
+    t_f = total / steps
+    _, i1, _, i2, _ = out["f"]
+
+    def bwd():
+        ms.maxsim_chamfer_bwd(P, Q, i1, i2, g1, g2)
+
+    total, _ = time_steps(torch, bwd, steps, warmup)
+    t_b = total / steps
+    flops = 8 * 2 * 100_000 * 100_000
+    return {"workload": "chamfer_fp32_1x100000x100000", "ms": t_f, "backward_ms": t_b,
+            "pairs_per_s": 2 * 100_000 * 100_000 / (t_f * 1e-3), "algorithmic_flops": flops,
+            "roofline": roofline("alu", flops / (t_f * 1e-3) / 1e12, FP32_PEAK_TFLOPS, "TFLOP/s"),
+            "kernels": ["chamfer_nn_kernel", "chamfer_loss_kernel", "cham_csr_kernel", "cham_grad_kernel"]}
+
+
 def bench_two_stage(torch, ms, synth, wl, steps, warmup):
     """The INT8 -> FP16 top-K scan on the long-query corpus (1 query of 1024
     tokens, 10,000 docs of 1024 tokens): per-token INT8 scores of every doc,
@@ -371,7 +401,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="",
                     help="run one workload: rerank|tiny|colpali|int8|backward|backward_varlen|"
-                         "pairs_varlen|two_stage|topk|copy")
+                         "pairs_varlen|two_stage|topk|chamfer|copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -389,11 +419,12 @@ def main() -> int:
     ms.binding.lib()  # fails loudly without the built library
 
     names = [args.only] if args.only else [HEADLINE, "tiny", "colpali", "int8", "backward",
-                                           "backward_varlen", "pairs_varlen", "two_stage", "topk"]
+                                           "backward_varlen", "pairs_varlen", "two_stage", "topk",
+                                           "chamfer"]
     fns = {"rerank": bench_rerank, "tiny": bench_tiny, "colpali": bench_colpali,
            "int8": bench_int8, "backward": bench_backward, "backward_varlen": bench_backward_varlen,
            "pairs_varlen": bench_pairs_varlen, "two_stage": bench_two_stage,
-           "topk": bench_topk, "copy": bench_copy}
+           "topk": bench_topk, "chamfer": bench_chamfer, "copy": bench_copy}
     per = {}
     head = None
     head_w = None

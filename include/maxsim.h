@@ -243,6 +243,50 @@ maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
                            float* dQ, float* dD, int32_t* csr_row_ptr, int32_t* csr_col_idx,
                            maxsim_stream_t stream);
 
+/*
+ * Chamfer distance between batches of 3-D point sets ("Flash-MaxSim"
+ * Sec. 4.2.4: the MaxSim pattern with a min of squared Euclidean distances in
+ * place of the max of inner products):
+ *   dist1[b,p] = min_q ||P[b,p] - Q[b,q]||^2, idx1[b,p] = the lowest q attaining it
+ *   dist2[b,q] = min_p ||Q[b,q] - P[b,p]||^2, idx2[b,q] likewise
+ *   loss[b]    = (1/N) sum_p dist1[b,p] + (1/M) sum_q dist2[b,q]
+ *   P [B, N, 3], Q [B, M, 3] float32 (finite); dist1, idx1 [B, N] float32 /
+ *   int32; dist2, idx2 [B, M]; loss [B] float32 or NULL.
+ * Distances are evaluated in fp32 from the coordinate differences; sums run in
+ * a fixed order. B == 0 enqueues nothing.
+ * Errors: SHAPE (negative sizes; N == 0 or M == 0 with B > 0), NULL,
+ * UNSUPPORTED (misaligned pointers), OVERFLOW (B*N or B*M >= 2^31).
+ */
+maxsim_status_t maxsim_chamfer_fwd(const float* P, const float* Q, int64_t B, int64_t N, int64_t M,
+                                   float* dist1, int32_t* idx1, float* dist2, int32_t* idx2,
+                                   float* loss, maxsim_stream_t stream);
+
+/*
+ * Chamfer backward through the saved nearest-neighbour indices ("Flash-MaxSim"
+ * Sec. 4.2.4 with the inverse-grid CSR of Sec. 4.2.2): the gradients of
+ * sum g1*dist1 + sum g2*dist2 at fixed idx1, idx2,
+ *   dP[b,p] = 2 g1[b,p] (P[b,p] - Q[b,idx1[b,p]])
+ *             + sum over q with idx2[b,q] = p of 2 g2[b,q] (P[b,p] - Q[b,q])
+ *   dQ[b,q] = 2 g2[b,q] (Q[b,q] - P[b,idx2[b,q]])
+ *             + sum over p with idx1[b,p] = q of 2 g1[b,p] (Q[b,q] - P[b,p])
+ * (the loss gradient is g1 = dloss/N, g2 = dloss/M).
+ *   idx1 [B,N] in [0,M), idx2 [B,M] in [0,N) int32 (a precondition: entries
+ *   outside are clamped, never read out of bounds); grad_dist1 [B,N],
+ *   grad_dist2 [B,M] float32; dP [B,N,3], dQ [B,M,3] float32, overwritten.
+ *   csr_row_ptr1 [B*M+1], csr_col_idx1 [B*N]: outputs, the inverse of idx1
+ *   (row b*M + q lists the flat indices b*N + p that chose it, ascending);
+ *   csr_row_ptr2 [B*N+1], csr_col_idx2 [B*M]: the inverse of idx2.
+ * Sums run in fp32 in a fixed order (the CSR row order); no atomics.
+ * B == 0 enqueues nothing. Errors as maxsim_chamfer_fwd, OVERFLOW also when
+ * B*N + 1 or B*M + 1 >= 2^31.
+ */
+maxsim_status_t maxsim_chamfer_bwd(const float* P, const float* Q, int64_t B, int64_t N, int64_t M,
+                                   const int32_t* idx1, const int32_t* idx2, const float* grad_dist1,
+                                   const float* grad_dist2, float* dP, float* dQ,
+                                   int32_t* csr_row_ptr1, int32_t* csr_col_idx1,
+                                   int32_t* csr_row_ptr2, int32_t* csr_col_idx2,
+                                   maxsim_stream_t stream);
+
 /* A static, human-readable name of a status. Never NULL. */
 const char* maxsim_status_string(maxsim_status_t s);
 

@@ -57,9 +57,13 @@ def lib() -> ctypes.CDLL:
                                               vp, vp, vp]
         L.maxsim_bwd_varlen.argtypes = [ci, vp, vp, i64, i64, i32, vp, vp, i64, i64, i64, vp, vp,
                                         vp, vp, vp, vp, vp]
+        L.maxsim_chamfer_fwd.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.maxsim_chamfer_bwd.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp]
         for f in (L.maxsim_fwd, L.maxsim_fwd_varlen, L.maxsim_fwd_i8, L.maxsim_bwd,
                   L.maxsim_fwd_i8_tok, L.maxsim_fwd_pairs, L.maxsim_topk,
-                  L.maxsim_fwd_pairs_varlen, L.maxsim_bwd_varlen):
+                  L.maxsim_fwd_pairs_varlen, L.maxsim_bwd_varlen, L.maxsim_chamfer_fwd,
+                  L.maxsim_chamfer_bwd):
             f.restype = ci
         L.maxsim_status_string.argtypes = [ci]
         L.maxsim_status_string.restype = ctypes.c_char_p
@@ -295,6 +299,57 @@ def maxsim_bwd_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D: torch
                                  _p(csr_row_ptr), _p(csr_col_idx), _stream(stream))
     _check("maxsim_bwd_varlen", st)
     return dQ, dD, csr_row_ptr, csr_col_idx
+
+
+def maxsim_chamfer_fwd(P: torch.Tensor, Q: torch.Tensor, want_loss: bool = True, stream=None):
+    """Chamfer distance of point-set batches P [B,N,3], Q [B,M,3] float32.
+    Returns (dist1 [B,N], idx1 [B,N], dist2 [B,M], idx2 [B,M], loss [B] or None)."""
+    if P.dim() != 3 or Q.dim() != 3 or P.shape[2] != 3 or Q.shape[2] != 3 or P.shape[0] != Q.shape[0]:
+        raise ValueError("P and Q must be [B,N,3] and [B,M,3]")
+    _dev("P", P, torch.float32)
+    _dev("Q", Q, torch.float32)
+    B, N, _ = P.shape
+    M = Q.shape[1]
+    dev = P.device
+    d1 = torch.empty((B, N), dtype=torch.float32, device=dev)
+    i1 = torch.empty((B, N), dtype=torch.int32, device=dev)
+    d2 = torch.empty((B, M), dtype=torch.float32, device=dev)
+    i2 = torch.empty((B, M), dtype=torch.int32, device=dev)
+    loss = torch.empty((B,), dtype=torch.float32, device=dev) if want_loss else None
+    st = lib().maxsim_chamfer_fwd(_p(P), _p(Q), B, N, M, _p(d1), _p(i1), _p(d2), _p(i2), _p(loss),
+                                  _stream(stream))
+    _check("maxsim_chamfer_fwd", st)
+    return d1, i1, d2, i2, loss
+
+
+def maxsim_chamfer_bwd(P: torch.Tensor, Q: torch.Tensor, idx1: torch.Tensor, idx2: torch.Tensor,
+                       grad_dist1: torch.Tensor, grad_dist2: torch.Tensor, stream=None):
+    """Chamfer backward through the saved indices. Returns (dP [B,N,3],
+    dQ [B,M,3], row_ptr1 [B*M+1], col_idx1 [B*N], row_ptr2 [B*N+1], col_idx2 [B*M])."""
+    B, N, _ = P.shape
+    M = Q.shape[1]
+    _dev("P", P, torch.float32)
+    _dev("Q", Q, torch.float32)
+    for n, t, shp in (("idx1", idx1, (B, N)), ("idx2", idx2, (B, M))):
+        _dev(n, t, torch.int32)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must be {list(shp)}")
+    for n, t, shp in (("grad_dist1", grad_dist1, (B, N)), ("grad_dist2", grad_dist2, (B, M))):
+        _dev(n, t, torch.float32)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must be {list(shp)}")
+    dev = P.device
+    dP = torch.empty((B, N, 3), dtype=torch.float32, device=dev)
+    dQ = torch.empty((B, M, 3), dtype=torch.float32, device=dev)
+    rp1 = torch.empty((B * M + 1,), dtype=torch.int32, device=dev)
+    ci1 = torch.empty((max(1, B * N),), dtype=torch.int32, device=dev)
+    rp2 = torch.empty((B * N + 1,), dtype=torch.int32, device=dev)
+    ci2 = torch.empty((max(1, B * M),), dtype=torch.int32, device=dev)
+    st = lib().maxsim_chamfer_bwd(_p(P), _p(Q), B, N, M, _p(idx1), _p(idx2), _p(grad_dist1),
+                                  _p(grad_dist2), _p(dP), _p(dQ), _p(rp1), _p(ci1), _p(rp2), _p(ci2),
+                                  _stream(stream))
+    _check("maxsim_chamfer_bwd", st)
+    return dP, dQ, rp1, ci1[:B * N], rp2, ci2[:B * M]
 
 
 def maxsim_status_string(status: int) -> str:

@@ -331,6 +331,72 @@ maxsim_status_t maxsim_bwd_varlen(maxsim_dtype_t dtype, const void* Q, const int
     return launch_status(launch_bwd_varlen(elem_of(dtype), a, (hipStream_t)stream));
 }
 
+maxsim_status_t maxsim_chamfer_fwd(const float* P, const float* Q, int64_t B, int64_t N, int64_t M,
+                                   float* dist1, int32_t* idx1, float* dist2, int32_t* idx2,
+                                   float* loss, maxsim_stream_t stream)
+{
+    if (B < 0 || N < 0 || M < 0) return MAXSIM_ERR_SHAPE;
+    if (B == 0) return MAXSIM_OK;
+    if (N == 0 || M == 0) return MAXSIM_ERR_SHAPE;  // a min over an empty set
+    const int64_t nP = mul_sat(B, N), nQ = mul_sat(B, M);
+    if (nP < 0 || nP > kI32Max || nQ < 0 || nQ > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (!P || !Q || !dist1 || !idx1 || !dist2 || !idx2) return MAXSIM_ERR_NULL;
+    if (!aligned(P, 4) || !aligned(Q, 4) || !aligned(dist1, 4) || !aligned(idx1, 4) ||
+        !aligned(dist2, 4) || !aligned(idx2, 4) || !aligned(loss, 4))
+        return MAXSIM_ERR_UNSUPPORTED;
+    ChamferArgs a{};
+    a.P = P;
+    a.Q = Q;
+    a.B = B;
+    a.N = N;
+    a.M = M;
+    a.dist1 = dist1;
+    a.idx1 = idx1;
+    a.dist2 = dist2;
+    a.idx2 = idx2;
+    a.loss = loss;
+    return launch_status(launch_chamfer_fwd(a, (hipStream_t)stream));
+}
+
+maxsim_status_t maxsim_chamfer_bwd(const float* P, const float* Q, int64_t B, int64_t N, int64_t M,
+                                   const int32_t* idx1, const int32_t* idx2, const float* grad_dist1,
+                                   const float* grad_dist2, float* dP, float* dQ,
+                                   int32_t* csr_row_ptr1, int32_t* csr_col_idx1,
+                                   int32_t* csr_row_ptr2, int32_t* csr_col_idx2,
+                                   maxsim_stream_t stream)
+{
+    if (B < 0 || N < 0 || M < 0) return MAXSIM_ERR_SHAPE;
+    if (B == 0) return MAXSIM_OK;
+    if (N == 0 || M == 0) return MAXSIM_ERR_SHAPE;
+    const int64_t nP = mul_sat(B, N), nQ = mul_sat(B, M);
+    if (nP < 0 || nP + 1 > kI32Max || nQ < 0 || nQ + 1 > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    if (!P || !Q || !idx1 || !idx2 || !grad_dist1 || !grad_dist2 || !dP || !dQ || !csr_row_ptr1 ||
+        !csr_col_idx1 || !csr_row_ptr2 || !csr_col_idx2)
+        return MAXSIM_ERR_NULL;
+    for (const void* p : {(const void*)P, (const void*)Q, (const void*)idx1, (const void*)idx2,
+                          (const void*)grad_dist1, (const void*)grad_dist2, (const void*)dP,
+                          (const void*)dQ, (const void*)csr_row_ptr1, (const void*)csr_col_idx1,
+                          (const void*)csr_row_ptr2, (const void*)csr_col_idx2})
+        if (!aligned(p, 4)) return MAXSIM_ERR_UNSUPPORTED;
+    ChamferArgs a{};
+    a.P = P;
+    a.Q = Q;
+    a.B = B;
+    a.N = N;
+    a.M = M;
+    a.idx1 = const_cast<int32_t*>(idx1);
+    a.idx2 = const_cast<int32_t*>(idx2);
+    a.g1 = grad_dist1;
+    a.g2 = grad_dist2;
+    a.dP = dP;
+    a.dQ = dQ;
+    a.row_ptr1 = csr_row_ptr1;
+    a.col_idx1 = csr_col_idx1;
+    a.row_ptr2 = csr_row_ptr2;
+    a.col_idx2 = csr_col_idx2;
+    return launch_status(launch_chamfer_bwd(a, (hipStream_t)stream));
+}
+
 maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
                            int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
                            const uint8_t* d_mask, const int32_t* argmax, const float* grad_scores,

@@ -144,52 +144,52 @@ __device__ __forceinline__ uint64_t match_key10(uint32_t key, bool active)
     return peers;
 }
 
-// Inverse map of doc j ("Flash-MaxSim" Sec. 4.2.2): row_ptr[j*Ld + t] and
-// the doc's segment col_idx[j*Nq*Lq, (j+1)*Nq*Lq), each row ascending.
-// Sources are taken in chunks of kCsrChunk; wave w owns the contiguous block
+// The inverse map of one segment ("Flash-MaxSim" Sec. 4.2.2): nsrc sources,
+// each with a destination in [0, L); row_ptr_seg[t] for t < L and the
+// segment's col_idx entries starting at `carry`, each row listing its sources
+// in ascending order. Run by a whole workgroup of kCsrWaves waves. Sources
+// are taken in chunks of kCsrChunk; wave w owns the contiguous block
 // [w*kPerWave, (w+1)*kPerWave) of a chunk and holds its destinations in
-// registers (lane l, step m: source m*64 + l of the block). Bins are handled
-// in rounds of kCsrBins.
-__global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
+// registers (lane l, step m: source m*64 + l of the block), counted into the
+// wave's own LDS histogram; the per-bin totals are scanned, and each wave
+// scatters its block in source order with ranks from ballots over the key
+// bits. Bins are handled in rounds of kCsrBins.
+// load(k0, tv, sv) fills, for this lane, the destination tv[m] (any value:
+// it is clamped into [0, L)) and the column-index value sv[m] of segment
+// source k0 + 64 m (only called with k0 + 64 m < nsrc checked per m inside).
+// Modes: kCsrFull builds the whole segment in one workgroup (bins in rounds);
+// a segment too large for one workgroup is split over workgroups that each own
+// one round [t_begin, t_begin + kCsrBins) of bins: kCsrCount writes that
+// round's per-bin counts into row_ptr_seg, a scan over the segment turns them
+// into row starts, and kCsrScatter then places the round's sources.
+enum CsrMode { kCsrFull = 0, kCsrCount = 1, kCsrScatter = 2 };
+
+template <int MODE = kCsrFull, typename Load>
+__device__ __forceinline__ void build_segment_csr(int64_t nsrc, int64_t L, int64_t carry,
+                                                  int32_t* __restrict__ row_ptr_seg,
+                                                  int32_t* __restrict__ col_idx, Load&& load,
+                                                  int64_t t_begin = 0)
 {
     constexpr int kPerWave = kCsrChunk / kCsrWaves;  // 1024 sources of a chunk per wave
     constexpr int kSteps = kPerWave / 64;             // 16 per lane
     __shared__ uint32_t hist[kCsrWaves][kCsrBins];    // per-wave counts, then per-wave slots
     __shared__ uint32_t run[kCsrBins];                // per-bin totals, then next free slot
     __shared__ uint32_t wsum[kCsrWaves];
-    const uint32_t j = blockIdx.x;
-    const int64_t Nd = a.Nd, Ld = a.Ld;
-    const uint32_t Lq = (uint32_t)a.Lq, nd = (uint32_t)Nd;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const uint32_t per_doc = (uint32_t)(a.Nq * a.Lq);
-    const int nchunks = (int)(((int64_t)per_doc + kCsrChunk - 1) / kCsrChunk);
+    const int nchunks = (int)((nsrc + kCsrChunk - 1) / kCsrChunk);
 
-    // live(j) for the dq pass, parked in dD[j, 0, 0] (dD is written last)
-    if (wave == 0 && Ld > 0) {
-        const bool live = doc_live(a.d_mask, j, Ld);
-        if (lane == 0) a.dD[(int64_t)j * Ld * kD] = live ? 1.f : 0.f;
-    }
-
-    // destinations of this wave's block of chunk c, round-relative (kNoKey
-    // outside [t_lo, t_lo + nb))
-    uint32_t key[kSteps];
+    uint32_t key[kSteps];  // destination relative to the round, kNoKey outside it
+    int32_t sv[kSteps];    // column-index value of each held source
     auto load_block = [&](int c, int64_t t_lo, int nb) {
-        const uint32_t k0 = (uint32_t)c * kCsrChunk + (uint32_t)wave * kPerWave;
-        SrcWalk w;
-        w.init(k0 + lane, 64, Lq);
+        const int64_t k0 = (int64_t)c * kCsrChunk + (int64_t)wave * kPerWave + lane;
         int32_t tv[kSteps];
-#pragma unroll
-        for (int m = 0; m < kSteps; ++m, w.next()) {  // every load in flight before the first use
-            const bool ok = k0 + m * 64 + lane < per_doc;
-            const uint32_t src = ok ? (w.i * nd + j) * Lq + w.s : 0u;
-            tv[m] = ok ? __builtin_nontemporal_load(a.argmax + src) : -1;
-        }
+        load(k0, tv, sv);  // every load in flight before the first use
 #pragma unroll
         for (int m = 0; m < kSteps; ++m) {
             key[m] = kNoKey;
-            if (k0 + m * 64 + lane < per_doc) {
+            if (k0 + 64 * m < nsrc) {
                 int64_t t = tv[m];
-                t = t < 0 ? 0 : (t >= Ld ? Ld - 1 : t);  // precondition guard
+                t = t < 0 ? 0 : (t >= L ? L - 1 : t);  // precondition guard
                 if (t >= t_lo && t < t_lo + nb) key[m] = (uint32_t)(t - t_lo);
             }
         }
@@ -202,46 +202,60 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
         for (int m = 0; m < kSteps; ++m)
             if (key[m] != kNoKey) atomicAdd(&hist[wave][key[m]], 1u);
     };
-    int64_t carry = (int64_t)j * per_doc;  // first CSR slot of the current round
-    for (int64_t t_lo = 0; t_lo < Ld; t_lo += kCsrBins) {
-        const int nb = (int)(Ld - t_lo < kCsrBins ? Ld - t_lo : kCsrBins);
+    const int64_t t_end = MODE == kCsrFull ? L : (t_begin + kCsrBins < L ? t_begin + kCsrBins : L);
+    for (int64_t t_lo = t_begin; t_lo < t_end; t_lo += kCsrBins) {
+        const int nb = (int)(L - t_lo < kCsrBins ? L - t_lo : kCsrBins);
 
-        // ---- totals per bin over every chunk --------------------------------
-        for (int k = tid; k < nb; k += kCsrThreads) run[k] = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            barrier_lds();
-            load_block(c, t_lo, nb);
-            count_block(nb);
-            barrier_lds();
-            for (int k = tid; k < nb; k += kCsrThreads) {
-                uint32_t tot = 0;
-                for (int w = 0; w < kCsrWaves; ++w) tot += hist[w][k];
-                run[k] += tot;
+        if constexpr (MODE == kCsrScatter) {
+            // row starts of this round, from the count pass and the scan
+            for (int k = tid; k < nb; k += kCsrThreads) run[k] = (uint32_t)row_ptr_seg[t_lo + k];
+            if (nchunks == 1) {  // the scatter below expects the block in registers
+                barrier_lds();
+                load_block(0, t_lo, nb);
+                count_block(nb);
             }
-        }
-        barrier_lds();
+        } else {
+            // ---- totals per bin over every chunk ----------------------------
+            for (int k = tid; k < nb; k += kCsrThreads) run[k] = 0;
+            for (int c = 0; c < nchunks; ++c) {
+                barrier_lds();
+                load_block(c, t_lo, nb);
+                count_block(nb);
+                barrier_lds();
+                for (int k = tid; k < nb; k += kCsrThreads) {
+                    uint32_t tot = 0;
+                    for (int w = 0; w < kCsrWaves; ++w) tot += hist[w][k];
+                    run[k] += tot;
+                }
+            }
+            barrier_lds();
+            if constexpr (MODE == kCsrCount) {
+                for (int k = tid; k < nb; k += kCsrThreads) row_ptr_seg[t_lo + k] = (int32_t)run[k];
+                return;
+            }
 
-        // ---- exclusive scan of the totals -> row_ptr, first slot per bin ----
-        // (nb <= kCsrThreads: one bin per thread)
-        const uint32_t mine = tid < nb ? run[tid] : 0u;
-        uint32_t incl = mine;
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
+            // ---- exclusive scan of the totals -> row_ptr, first slot per bin
+            // (nb <= kCsrThreads: one bin per thread)
+            const uint32_t mine = tid < nb ? run[tid] : 0u;
+            uint32_t incl = mine;
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t v = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += v;
+            }
+            if (lane == 63) wsum[wave] = incl;
+            barrier_lds();
+            uint32_t wave_off = 0, round_tot = 0;
+            for (int w = 0; w < kCsrWaves; ++w) {
+                if (w < wave) wave_off += wsum[w];
+                round_tot += wsum[w];
+            }
+            if (tid < nb) {
+                const int64_t first = carry + wave_off + incl - mine;
+                row_ptr_seg[t_lo + tid] = (int32_t)first;
+                run[tid] = (uint32_t)first;
+            }
+            carry += round_tot;
         }
-        if (lane == 63) wsum[wave] = incl;
-        barrier_lds();
-        uint32_t wave_off = 0, round_tot = 0;
-        for (int w = 0; w < kCsrWaves; ++w) {
-            if (w < wave) wave_off += wsum[w];
-            round_tot += wsum[w];
-        }
-        if (tid < nb) {
-            const int64_t first = carry + wave_off + incl - mine;
-            a.row_ptr[(int64_t)j * Ld + t_lo + tid] = (int32_t)first;
-            run[tid] = (uint32_t)first;
-        }
-        carry += round_tot;
 
         // ---- stable scatter, chunk by chunk, in source order ----------------
         for (int c = 0; c < nchunks; ++c) {
@@ -262,24 +276,52 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
                 run[k] = pos;
             }
             barrier_lds();
-            const uint32_t k0 = (uint32_t)c * kCsrChunk + (uint32_t)wave * kPerWave;
-            SrcWalk w;
-            w.init(k0 + lane, 64, Lq > 0 ? Lq : 1u);
 #pragma unroll
-            for (int m = 0; m < kSteps; ++m, w.next()) {
+            for (int m = 0; m < kSteps; ++m) {
                 const bool act = key[m] != kNoKey;
                 if (__ballot(act) == 0) continue;  // uniform
                 const uint64_t peers = match_key10(key[m], act);
                 if (act) {
                     const uint64_t before = peers & lanemask_lt();
                     const uint32_t slot = hist[wave][key[m]] + (uint32_t)__builtin_popcountll(before);
-                    a.col_idx[slot] = (int32_t)((w.i * nd + j) * Lq + w.s);
+                    col_idx[slot] = sv[m];
                     if (before == 0) hist[wave][key[m]] += (uint32_t)__builtin_popcountll(peers);
                 }
             }
         }
         barrier_lds();
     }
+}
+
+// Inverse map of doc j: row_ptr[j*Ld + t] and the doc's segment
+// col_idx[j*Nq*Lq, (j+1)*Nq*Lq). Every doc receives exactly Nq*Lq sources,
+// so no global scan is needed.
+__global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
+{
+    const uint32_t j = blockIdx.x;
+    const int64_t Nd = a.Nd, Ld = a.Ld;
+    const uint32_t Lq = (uint32_t)a.Lq, nd = (uint32_t)Nd;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint32_t per_doc = (uint32_t)(a.Nq * a.Lq);
+
+    // live(j) for the dq pass, parked in dD[j, 0, 0] (dD is written last)
+    if (wave == 0 && Ld > 0) {
+        const bool live = doc_live(a.d_mask, j, Ld);
+        if (lane == 0) a.dD[(int64_t)j * Ld * kD] = live ? 1.f : 0.f;
+    }
+    // doc-local source k = i*Lq + s is the flat source (i*Nd + j)*Lq + s
+    auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
+        SrcWalk w;
+        w.init((uint32_t)k0, 64, Lq > 0 ? Lq : 1u);
+#pragma unroll
+        for (int m = 0; m < 16; ++m, w.next()) {
+            const bool ok = k0 + 64 * m < per_doc;
+            const uint32_t src = ok ? (w.i * nd + j) * Lq + w.s : 0u;
+            sv[m] = (int32_t)src;
+            tv[m] = ok ? __builtin_nontemporal_load(a.argmax + src) : 0;
+        }
+    };
+    build_segment_csr(per_doc, Ld, (int64_t)j * per_doc, a.row_ptr + (int64_t)j * Ld, a.col_idx, load);
     if (j == Nd - 1 && tid == 0) a.row_ptr[Nd * Ld] = (int32_t)(a.Nq * Nd * a.Lq);
 }
 
@@ -556,130 +598,41 @@ __global__ __launch_bounds__(kPrepThreads) void vbwd_prep_kernel(VarBwdArgs a)
     if (tid == kPrepThreads - 1) a.row_ptr[Td] = (int32_t)((int64_t)part[tid] * a.Tq);
 }
 
-// CSR of doc j: row_ptr[cu_d[j] + t] and the doc's col_idx segment.
+// CSR of doc j: row_ptr[cu_d[j] + t] and the doc's col_idx segment, whose
+// start the prep pass parked in dD. Source p (a packed query row) belongs to
+// the query found by a search of cu_q once per lane, then by walking forward
+// as p grows.
 __global__ __launch_bounds__(kCsrThreads) void vbwd_csr_kernel(VarBwdArgs a)
 {
-    constexpr int kPerWave = kCsrChunk / kCsrWaves;
-    constexpr int kSteps = kPerWave / 64;
-    __shared__ uint32_t hist[kCsrWaves][kCsrBins];
-    __shared__ uint32_t run[kCsrBins];
-    __shared__ uint32_t wsum[kCsrWaves];
     const int64_t j = blockIdx.x;
-    const int64_t Nd = a.Nd, Tq = a.Tq, Nq = a.Nq;
+    const int64_t Nd = a.Nd, Tq = a.Tq;
     const int64_t d0 = a.cu_d[j];
     int64_t L = (int64_t)a.cu_d[j + 1] - d0;
     if (d0 < 0 || d0 >= a.Td) return;  // empty doc (or broken offsets)
     if (L > a.Td - d0) L = a.Td - d0;
     if (L <= 0) return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t mlq = (uint32_t)a.max_lq, nd = (uint32_t)Nd;
-    const int nchunks = (int)((Tq + kCsrChunk - 1) / kCsrChunk);
-    const int nq = (int)Nq;
-
-    uint32_t key[kSteps];
-    uint32_t srcv[kSteps];  // flat source index of each held source
-    auto load_block = [&](int c, int64_t t_lo, int nb) {
-        const int64_t p0 = (int64_t)c * kCsrChunk + (int64_t)wave * kPerWave + lane;
+    const int nq = (int)a.Nq;
+    auto load = [&](int64_t p0, int32_t (&tv)[16], int32_t (&sv)[16]) {
         int i = p0 < Tq ? seg_of(a.cu_q, nq + 1, p0) : 0;
         i = i < nq ? i : nq - 1;  // precondition guard (cu_q[Nq] == Tq)
-        int32_t tv[kSteps];
 #pragma unroll
-        for (int m = 0; m < kSteps; ++m) {
+        for (int m = 0; m < 16; ++m) {
             const int64_t p = p0 + 64 * m;
-            srcv[m] = 0;
-            tv[m] = -1;
+            sv[m] = 0;
+            tv[m] = 0;
             if (p < Tq) {
                 while (i + 1 < nq && (int64_t)a.cu_q[i + 1] <= p) ++i;
                 int64_t s = p - a.cu_q[i];
                 s = s < 0 ? 0 : (s >= mlq ? mlq - 1 : s);  // precondition guard
-                srcv[m] = ((uint32_t)i * nd + (uint32_t)j) * mlq + (uint32_t)s;
-                tv[m] = __builtin_nontemporal_load(a.argmax + srcv[m]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < kSteps; ++m) {
-            key[m] = kNoKey;
-            if (p0 + 64 * m < Tq) {
-                int64_t t = tv[m];
-                t = t < 0 ? 0 : (t >= L ? L - 1 : t);  // precondition guard
-                if (t >= t_lo && t < t_lo + nb) key[m] = (uint32_t)(t - t_lo);
+                const uint32_t src = ((uint32_t)i * nd + (uint32_t)j) * mlq + (uint32_t)s;
+                sv[m] = (int32_t)src;
+                tv[m] = __builtin_nontemporal_load(a.argmax + src);
             }
         }
     };
-    auto count_block = [&](int nb) {
-        for (int k = lane; k < nb; k += 64) hist[wave][k] = 0;
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-#pragma unroll
-        for (int m = 0; m < kSteps; ++m)
-            if (key[m] != kNoKey) atomicAdd(&hist[wave][key[m]], 1u);
-    };
-    int64_t carry = (int64_t)__builtin_bit_cast(uint32_t, a.dD[d0 * kD]);  // parked by prep
-    for (int64_t t_lo = 0; t_lo < L; t_lo += kCsrBins) {
-        const int nb = (int)(L - t_lo < kCsrBins ? L - t_lo : kCsrBins);
-        for (int k = tid; k < nb; k += kCsrThreads) run[k] = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            barrier_lds();
-            load_block(c, t_lo, nb);
-            count_block(nb);
-            barrier_lds();
-            for (int k = tid; k < nb; k += kCsrThreads) {
-                uint32_t tot = 0;
-                for (int w = 0; w < kCsrWaves; ++w) tot += hist[w][k];
-                run[k] += tot;
-            }
-        }
-        barrier_lds();
-        const uint32_t mine = tid < nb ? run[tid] : 0u;
-        uint32_t incl = mine;
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
-        }
-        if (lane == 63) wsum[wave] = incl;
-        barrier_lds();
-        uint32_t wave_off = 0, round_tot = 0;
-        for (int w = 0; w < kCsrWaves; ++w) {
-            if (w < wave) wave_off += wsum[w];
-            round_tot += wsum[w];
-        }
-        if (tid < nb) {
-            const int64_t first = carry + wave_off + incl - mine;
-            a.row_ptr[d0 + t_lo + tid] = (int32_t)first;
-            run[tid] = (uint32_t)first;
-        }
-        carry += round_tot;
-        for (int c = 0; c < nchunks; ++c) {
-            if (nchunks > 1) {
-                barrier_lds();
-                load_block(c, t_lo, nb);
-                count_block(nb);
-            }
-            barrier_lds();
-            for (int k = tid; k < nb; k += kCsrThreads) {
-                uint32_t pos = run[k];
-                for (int w = 0; w < kCsrWaves; ++w) {
-                    const uint32_t h = hist[w][k];
-                    hist[w][k] = pos;
-                    pos += h;
-                }
-                run[k] = pos;
-            }
-            barrier_lds();
-#pragma unroll
-            for (int m = 0; m < kSteps; ++m) {
-                const bool act = key[m] != kNoKey;
-                if (__ballot(act) == 0) continue;
-                const uint64_t peers = match_key10(key[m], act);
-                if (act) {
-                    const uint64_t before = peers & lanemask_lt();
-                    const uint32_t slot = hist[wave][key[m]] + (uint32_t)__builtin_popcountll(before);
-                    a.col_idx[slot] = (int32_t)srcv[m];
-                    if (before == 0) hist[wave][key[m]] += (uint32_t)__builtin_popcountll(peers);
-                }
-            }
-        }
-        barrier_lds();
-    }
+    const int64_t carry = (int64_t)__builtin_bit_cast(uint32_t, a.dD[d0 * kD]);  // parked by prep
+    build_segment_csr(Tq, L, carry, a.row_ptr + d0, a.col_idx, load);
 }
 
 // Eq. (2) per packed query row p = cu_q[i] + s:
@@ -867,6 +820,157 @@ hipError_t launch_bwd_varlen(int elem, VarBwdArgs a, hipStream_t stream)
     case kBF16: return launch_bwd_varlen_t<kBF16>(a, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+// ===========================================================================
+// Chamfer backward ("Flash-MaxSim" Sec. 4.2.4: the saved argmin, the
+// nearest-neighbour index, drives the same inverse-grid CSR). For the
+// weighted sum of distances with upstream gradients g1 [B,N], g2 [B,M]:
+//   dP[b,p] = 2 g1[b,p] (P[b,p] - Q[b,idx1]) + sum over CSR2 row (b,p) of
+//             2 g2[b,q] (P[b,p] - Q[b,q])
+//   dQ[b,q] = 2 g2[b,q] (Q[b,q] - P[b,idx2]) + sum over CSR1 row (b,q) of
+//             2 g1[b,p] (Q[b,q] - P[b,p])
+// CSR1 inverts idx1 (rows = Q points, sources = P points), CSR2 inverts idx2.
+// Each batch is a segment with a fixed number of sources, so segment b of
+// CSR1 starts at b*N (of CSR2 at b*M): no global scan. One workgroup builds
+// one segment; then one thread per point walks its CSR row in order and
+// writes its gradient once. No atomics; results are bitwise reproducible.
+// ===========================================================================
+
+// Segment g in [0, 2B): g < B is batch g of CSR1 (sources P, rows Q), else
+// batch g - B of CSR2. A segment's rows are split into rounds of kCsrBins,
+// one workgroup per (segment, round): a count pass, a scan per segment, a
+// scatter pass (every workgroup reads all of its segment's sources).
+struct ChamSeg {
+    int64_t b, ns, nr;
+    const int32_t* idx;
+    int32_t* row_ptr;
+    int32_t* col_idx;
+};
+
+__device__ __forceinline__ ChamSeg cham_seg(const ChamferArgs& a, int64_t g)
+{
+    const bool second = g >= a.B;
+    ChamSeg c;
+    c.b = second ? g - a.B : g;
+    c.ns = second ? a.M : a.N;
+    c.nr = second ? a.N : a.M;
+    c.idx = second ? a.idx2 : a.idx1;
+    c.row_ptr = second ? a.row_ptr2 : a.row_ptr1;
+    c.col_idx = second ? a.col_idx2 : a.col_idx1;
+    return c;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kCsrThreads) void cham_csr_kernel(ChamferArgs a, int rounds1, int rounds2)
+{
+    // workgroup -> (segment, round): CSR1 segments first, then CSR2
+    const int64_t w = blockIdx.x;
+    const int64_t n1 = a.B * rounds1;
+    const int64_t g = w < n1 ? w / rounds1 : a.B + (w - n1) / rounds2;
+    const int64_t r = w < n1 ? w % rounds1 : (w - n1) % rounds2;
+    const ChamSeg c = cham_seg(a, g);
+    auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int64_t k = k0 + 64 * m;
+            const int64_t src = c.b * c.ns + (k < c.ns ? k : 0);
+            sv[m] = (int32_t)src;
+            tv[m] = k < c.ns ? __builtin_nontemporal_load(c.idx + src) : 0;
+        }
+    };
+    build_segment_csr<MODE>(c.ns, c.nr, 0, c.row_ptr + c.b * c.nr, c.col_idx, load, r * (int64_t)kCsrBins);
+}
+
+// per segment: the counts in row_ptr become exclusive row starts (plus the
+// segment base b*ns); the last segment of each CSR also writes its end entry
+__global__ __launch_bounds__(1024) void cham_scan_kernel(ChamferArgs a)
+{
+    __shared__ uint32_t part[1024];
+    const ChamSeg c = cham_seg(a, blockIdx.x);
+    int32_t* rp = c.row_ptr + c.b * c.nr;
+    const int tid = threadIdx.x;
+    const int64_t chunk = (c.nr + 1023) / 1024;
+    const int64_t t0 = tid * chunk, t1 = t0 + chunk < c.nr ? t0 + chunk : c.nr;
+    uint32_t sum = 0;
+    for (int64_t t = t0; t < t1; ++t) sum += (uint32_t)rp[t];
+    part[tid] = sum;
+    barrier_lds();
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the chunk sums
+        const uint32_t v = tid >= off ? part[tid - off] : 0u;
+        barrier_lds();
+        part[tid] += v;
+        barrier_lds();
+    }
+    uint32_t run = (uint32_t)(c.b * c.ns) + part[tid] - sum;
+    for (int64_t t = t0; t < t1; ++t) {
+        const uint32_t cnt = (uint32_t)rp[t];
+        rp[t] = (int32_t)run;
+        run += cnt;
+    }
+    if (c.b == a.B - 1 && tid == 0) c.row_ptr[a.B * c.nr] = (int32_t)(a.B * c.ns);
+}
+
+// one thread per point; threads [0, B*N) produce dP, [B*N, B*N + B*M) dQ
+__global__ __launch_bounds__(256) void cham_grad_kernel(ChamferArgs a)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nP = a.B * a.N, nQ = a.B * a.M;
+    if (t >= nP + nQ) return;
+    const bool second = t >= nP;  // a point of Q
+    const int64_t r = second ? t - nP : t;
+    const int64_t nown = second ? a.M : a.N, nother = second ? a.N : a.M;
+    const float* X = second ? a.Q : a.P;      // the point's own set
+    const float* Y = second ? a.P : a.Q;      // the other set
+    const float* g_own = second ? a.g2 : a.g1;
+    const float* g_oth = second ? a.g1 : a.g2;
+    const int32_t* idx_own = second ? a.idx2 : a.idx1;
+    const int32_t* rp = second ? a.row_ptr1 : a.row_ptr2;  // rows over this set
+    const int32_t* ci = second ? a.col_idx1 : a.col_idx2;
+    const int64_t b = r / nown;
+    const float x0 = X[r * 3], x1 = X[r * 3 + 1], x2 = X[r * 3 + 2];
+    int64_t nn = idx_own[r];
+    nn = nn < 0 ? 0 : (nn >= nother ? nother - 1 : nn);  // precondition guard
+    const float* y = Y + (b * nother + nn) * 3;
+    const float w = 2.f * g_own[r];
+    float acc0 = w * (x0 - y[0]), acc1 = w * (x1 - y[1]), acc2 = w * (x2 - y[2]);
+    // sources of this row: points of the other set whose nearest neighbour is
+    // this point, ascending; bounded for any row_ptr content
+    const int64_t cap = a.B * nother;
+    int64_t e0 = rp[r], e1 = rp[r + 1];
+    e0 = e0 < 0 ? 0 : (e0 > cap ? cap : e0);
+    e1 = e1 < e0 ? e0 : (e1 > cap ? cap : e1);
+    e1 = e1 - e0 > nother ? e0 + nother : e1;
+    for (int64_t e = e0; e < e1; ++e) {
+        int64_t src = ci[e];
+        src = src < 0 ? 0 : (src >= cap ? cap - 1 : src);
+        const float* z = Y + src * 3;
+        const float v = 2.f * g_oth[src];
+        acc0 = __builtin_fmaf(v, x0 - z[0], acc0);
+        acc1 = __builtin_fmaf(v, x1 - z[1], acc1);
+        acc2 = __builtin_fmaf(v, x2 - z[2], acc2);
+    }
+    float* out = (second ? a.dQ : a.dP) + r * 3;
+    out[0] = acc0;
+    out[1] = acc1;
+    out[2] = acc2;
+}
+
+hipError_t launch_chamfer_bwd(ChamferArgs a, hipStream_t stream)
+{
+    if (a.B == 0) return hipSuccess;
+    hipError_t err;
+    const int r1 = (int)((a.M + kCsrBins - 1) / kCsrBins), r2 = (int)((a.N + kCsrBins - 1) / kCsrBins);
+    const unsigned wgs = (unsigned)(a.B * (r1 + r2));
+    hipLaunchKernelGGL(cham_csr_kernel<kCsrCount>, dim3(wgs), dim3(kCsrThreads), 0, stream, a, r1, r2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(cham_scan_kernel, dim3((unsigned)(2 * a.B)), dim3(1024), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(cham_csr_kernel<kCsrScatter>, dim3(wgs), dim3(kCsrThreads), 0, stream, a, r1, r2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t n = a.B * (a.N + a.M);
+    hipLaunchKernelGGL(cham_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace maxsim

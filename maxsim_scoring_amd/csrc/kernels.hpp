@@ -74,6 +74,26 @@ struct VarBwdArgs {
     int32_t max_lq;
 };
 
+struct ChamferArgs {
+    const float* P;  // [B, N, 3]
+    const float* Q;  // [B, M, 3]
+    int64_t B, N, M;
+    float* dist1;    // [B, N]
+    int32_t* idx1;
+    float* dist2;    // [B, M]
+    int32_t* idx2;
+    float* loss;     // [B] or null
+    // backward
+    const float* g1;  // [B, N]
+    const float* g2;  // [B, M]
+    float* dP;        // [B, N, 3]
+    float* dQ;        // [B, M, 3]
+    int32_t* row_ptr1;  // [B*M + 1]: rows = Q points, sources = P points
+    int32_t* col_idx1;  // [B*N]
+    int32_t* row_ptr2;  // [B*N + 1]: rows = P points, sources = Q points
+    int32_t* col_idx2;  // [B*M]
+};
+
 struct TopkArgs {
     const float* scores;  // [Nq, Nd]
     int64_t Nq, Nd;
@@ -94,5 +114,7 @@ hipError_t launch_fwd_varlen(int elem, VarlenArgs a, hipStream_t stream);
 hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream);
 hipError_t launch_topk(TopkArgs a, hipStream_t stream);
 hipError_t launch_bwd_varlen(int elem, VarBwdArgs a, hipStream_t stream);
+hipError_t launch_chamfer_fwd(ChamferArgs a, hipStream_t stream);
+hipError_t launch_chamfer_bwd(ChamferArgs a, hipStream_t stream);
 
 }  // namespace maxsim

@@ -219,3 +219,29 @@ def int8_tok_argmax(got, ref, Q8, D8, d_scale, d_mask=None, pairs=None):
         else:
             bad.append(((a, b, s), tg, to, f"gap {wo - wg:.3e}"))
     return len(mism), acc, bad
+
+
+def chamfer_argmin(got, ref, A64, T64):
+    """Nearest-neighbour indices of one Chamfer direction: got/ref [B, na]
+    index into the targets T64 [B, nt, 3] for the sources A64 [B, na, 3]. A
+    GPU index t_g differing from the oracle's t_o is accepted only if
+    dist(t_g) - dist(t_o) <= e(t_o) + e(t_g) with dist the exact squared
+    distance and e = gamma(5) * dist, the bound on an fp32 sum of three
+    squared fp32 differences (5 roundings per term, all terms >= 0).
+    Returns (n_mismatch, n_accepted, failing entries)."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    g5 = 5 * U32 / (1.0 - 5 * U32)
+    bad, acc = [], 0
+    for b, a in np.argwhere(got != ref):
+        tg, to = int(got[b, a]), int(ref[b, a])
+        if not 0 <= tg < T64.shape[1]:
+            bad.append(((int(b), int(a)), tg, to, "index out of range"))
+            continue
+        dg = float(((A64[b, a] - T64[b, tg]) ** 2).sum())
+        do = float(((A64[b, a] - T64[b, to]) ** 2).sum())
+        if dg - do <= g5 * (dg + do):
+            acc += 1
+        else:
+            bad.append(((int(b), int(a)), tg, to, f"gap {dg - do:.3e} > bound {g5 * (dg + do):.3e}"))
+    return int((got != ref).sum()), acc, bad

@@ -37,6 +37,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd",
                           "maxsim_fwd_i8_tok", "maxsim_fwd_pairs", "maxsim_topk",
                           "maxsim_fwd_pairs_varlen", "maxsim_bwd_varlen",
+                          "maxsim_chamfer_fwd", "maxsim_chamfer_bwd",
                           "maxsim_status_string", "maxsim_abi_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -211,6 +212,33 @@ def test_bwd_varlen_validation(L):
     assert f(Td=1 << 31) == ERR_OVERFLOW
     assert f(dD=MIS8) == ERR_UNSUPPORTED
     assert f(rp=MIS2) == ERR_UNSUPPORTED
+
+
+def test_chamfer_validation(L):
+    def fw(P=FAKE, Q=FAKE, B=2, N=100, M=50, d1=FAKE, i1=FAKE, d2=FAKE, i2=FAKE, loss=None):
+        return L.maxsim_chamfer_fwd(P, Q, B, N, M, d1, i1, d2, i2, loss, None)
+    assert fw(N=-1) == ERR_SHAPE
+    assert fw(M=0) == ERR_SHAPE                # a min over an empty set
+    assert fw(B=0, P=None) == OK               # nothing to do, nothing enqueued
+    assert fw(P=None) == ERR_NULL
+    assert fw(i2=None) == ERR_NULL
+    assert fw(d1=MIS2) == ERR_UNSUPPORTED
+    assert fw(B=1 << 20, N=1 << 12) == ERR_OVERFLOW
+
+    def bw(B=2, N=100, M=50, **kw):
+        args = dict(P=FAKE, Q=FAKE, i1=FAKE, i2=FAKE, g1=FAKE, g2=FAKE, dP=FAKE, dQ=FAKE,
+                    rp1=FAKE, ci1=FAKE, rp2=FAKE, ci2=FAKE)
+        args.update(kw)
+        return L.maxsim_chamfer_bwd(args["P"], args["Q"], B, N, M, args["i1"], args["i2"],
+                                    args["g1"], args["g2"], args["dP"], args["dQ"], args["rp1"],
+                                    args["ci1"], args["rp2"], args["ci2"], None)
+    assert bw(B=-1) == ERR_SHAPE
+    assert bw(N=0) == ERR_SHAPE
+    assert bw(B=0) == OK
+    assert bw(rp2=None) == ERR_NULL
+    assert bw(g1=None) == ERR_NULL
+    assert bw(ci1=MIS2) == ERR_UNSUPPORTED
+    assert bw(B=1 << 16, M=1 << 15) == ERR_OVERFLOW
 
 
 def test_topk_validation(L):

@@ -555,3 +555,88 @@ def test_pairs_varlen(ms, oracle_mod, case):
                                        _g(pd))
     torch.cuda.synchronize()
     _assert_close("scores (no argmax)", s2.cpu().numpy(), rs)
+
+
+# ------------------------------------------------------------------ Chamfer distance
+
+CHAMFER_CASES = [(1, 1, 1), (2, 5, 7), (3, 1000, 1500), (2, 3000, 2500), (1, 20000, 20000)]
+
+
+def _chamfer_gpu(ms, P, Q):
+    out = ms.maxsim_chamfer_fwd(_g(P), _g(Q))
+    torch.cuda.synchronize()
+    return tuple(x.cpu() for x in out)
+
+
+def _check_chamfer_fwd(oracle_mod, P, Q, got):
+    d1, i1, d2, i2, loss = got
+    r1, j1, r2, j2, rl = oracle_mod.chamfer_fwd(P, Q)
+    _assert_close("dist1", d1.numpy(), r1)
+    _assert_close("dist2", d2.numpy(), r2)
+    _assert_close("loss", loss.numpy(), rl)
+    P64, Q64 = P.double().numpy(), Q.double().numpy()
+    for name, g, r, A, T in (("idx1", i1, j1, P64, Q64), ("idx2", i2, j2, Q64, P64)):
+        n, acc, bad = compare.chamfer_argmin(g.numpy(), r, A, T)
+        assert not bad, f"{name}: {len(bad)} mismatches outside the near-tie bound: {bad[:5]}"
+
+
+@pytest.mark.parametrize("shape", CHAMFER_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
+def test_chamfer(ms, oracle_mod, shape):
+    B, N, M = shape
+    _say(f"chamfer {shape}")
+    P, Q = synth.point_clouds(700 + N, B, N, M)
+    got = _chamfer_gpu(ms, P, Q)
+    _check_chamfer_fwd(oracle_mod, P, Q, got)
+    # backward through the GPU's own indices
+    g1, g2 = synth.chamfer_grads(700 + N, B, N, M)
+    _, i1, _, i2, _ = got
+    out = ms.maxsim_chamfer_bwd(_g(P), _g(Q), _g(i1), _g(i2), _g(g1), _g(g2))
+    torch.cuda.synchronize()
+    dP, dQ, rp1, ci1, rp2, ci2 = (x.cpu() for x in out)
+    rdP, rdQ, rrp1, rci1, rrp2, rci2 = oracle_mod.chamfer_bwd(P, Q, i1, i2, g1, g2)
+    for name, x, y in (("row_ptr1", rp1, rrp1), ("col_idx1", ci1, rci1), ("row_ptr2", rp2, rrp2),
+                       ("col_idx2", ci2, rci2)):
+        assert np.array_equal(x.numpy(), y), name
+    _assert_close("dP", dP.numpy(), rdP)
+    _assert_close("dQ", dQ.numpy(), rdQ)
+    again = ms.maxsim_chamfer_bwd(_g(P), _g(Q), _g(i1), _g(i2), _g(g1), _g(g2))
+    torch.cuda.synchronize()
+    assert torch.equal(again[0].cpu(), dP) and torch.equal(again[1].cpu(), dQ), "not deterministic"
+
+
+def test_chamfer_exact_ties(ms, oracle_mod):
+    """Duplicated target points: every tie goes to the lowest index."""
+    _say("chamfer ties")
+    P, Q = synth.point_clouds(781, 2, 300, 100)
+    Q = torch.cat([Q, Q, Q[:, :50]], dim=1)  # each target appears two or three times
+    got = _chamfer_gpu(ms, P, Q)
+    _, i1, _, _, _ = got
+    assert int(i1.max()) < 100  # the first copy always wins
+    _check_chamfer_fwd(oracle_mod, P, Q, got)
+
+
+def test_chamfer_100k_points(ms, oracle_mod):
+    """Two 100,000-point clouds (the size the pages report the naive form
+    cannot hold): the forward on 2,000 sampled points of each set, the
+    backward (both CSRs and every gradient) in full."""
+    _say("chamfer 100k")
+    P, Q = synth.point_clouds(782, 1, 100_000, 100_000)
+    d1, i1, d2, i2, loss = _chamfer_gpu(ms, P, Q)
+    rng = np.random.default_rng(5)
+    for A, T, d, i in ((P, Q, d1, i1), (Q, P, d2, i2)):
+        rows = np.sort(rng.choice(100_000, 2000, replace=False))
+        rd, ri, _, _, _ = oracle_mod.chamfer_fwd(A[:, rows], T)
+        _assert_close("dist", d.numpy()[:, rows], rd)
+        n, acc, bad = compare.chamfer_argmin(i.numpy()[:, rows], ri, A[:, rows].double().numpy(),
+                                             T.double().numpy())
+        assert not bad, bad[:5]
+    g1, g2 = synth.chamfer_grads(782, 1, 100_000, 100_000)
+    out = ms.maxsim_chamfer_bwd(_g(P), _g(Q), _g(i1), _g(i2), _g(g1), _g(g2))
+    torch.cuda.synchronize()
+    dP, dQ, rp1, ci1, rp2, ci2 = (x.cpu() for x in out)
+    rdP, rdQ, rrp1, rci1, rrp2, rci2 = oracle_mod.chamfer_bwd(P, Q, i1, i2, g1, g2)
+    for name, x, y in (("row_ptr1", rp1, rrp1), ("col_idx1", ci1, rci1), ("row_ptr2", rp2, rrp2),
+                       ("col_idx2", ci2, rci2)):
+        assert np.array_equal(x.numpy(), y), name
+    _assert_close("dP", dP.numpy(), rdP)
+    _assert_close("dQ", dQ.numpy(), rdQ)
