@@ -44,7 +44,6 @@ namespace maxsim {
 namespace {
 
 constexpr int kWaves = 8;
-constexpr int kMaskWords = 2048;  // 16 KB of LDS: d_mask bits of a doc range
 
 // 4-bit nonzero flags of the 4 bytes of x (byte b -> bit b)
 __device__ __forceinline__ uint32_t byte_flags(uint32_t x)
@@ -234,8 +233,8 @@ __device__ __forceinline__ int saved_argmax(const RowState<V, true>& st, const u
 // integer dot product before the max (a float per score); the query-token
 // scale (positive) is applied to the max. The tile's doc scales are staged in
 // LDS with the tile.
-template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES, int TR>
-__global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
+template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES, int TR, int W = kWaves>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_dense_kernel(DenseArgs a)
 {
     static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
     using T = Traits<E>;
@@ -245,13 +244,14 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     constexpr int RB = T::kRowBytes;
     constexpr int NCH = RB / 16;           // 16-byte chunks per row
     constexpr int KS = T::kKSteps;
-    constexpr int SLOTS = kWaves * NTW;    // N-tiles per workgroup
+    constexpr int SLOTS = W * NTW;         // N-tiles per workgroup
     static_assert(TR == 128 || TR == 256, "doc tokens per pipeline stage");
     constexpr int MT = TR / 32;            // MFMA M-tiles per stage
     constexpr int WPT = TR / 64;           // d_mask words per stage
     constexpr int STAGE_BYTES = TR * RB;
     constexpr int CHUNKS = TR * NCH;
-    constexpr int THREADS = kWaves * 64;
+    constexpr int THREADS = W * 64;
+    constexpr int kMaskWords = W == 8 ? 2048 : 1024;  // d_mask words of a doc range in LDS
     constexpr int LPS = CHUNKS / THREADS;  // direct-to-LDS loads per thread per stage
     constexpr int LPW = LPS + (TOK ? 1 : 0);  // direct-to-LDS loads per wave per stage
     static_assert(CHUNKS % THREADS == 0, "stage must split evenly over the workgroup");
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
     // doc-token scales of each stage's tile (TOK)
     __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? STAGES * TR : 4];
     // argmax: each lane's saved M-tile values, per (wave, N-tile): 4 chunks x 64 lanes
-    __shared__ __attribute__((aligned(16))) u32x4 save_buf[ARGMAX ? kWaves * NTW * 256 : 1];
+    __shared__ __attribute__((aligned(16))) u32x4 save_buf[ARGMAX ? W * NTW * 256 : 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
             dma_lds16(Dt, o < lim ? o : lim, lds0 + u * 1024);
         }
         if constexpr (TOK) {  // rows RPW w .. RPW w + RPW - 1 of the tile's doc scales
-            constexpr int RPW = TR / kWaves;
+            constexpr int RPW = TR / W;
             const void* St = uniform_ptr(a.d_scale_tok + doc * Ld + t0);
             const int row = RPW * wave + lane < rows ? RPW * wave + lane : rows - 1;
             if (lane < RPW)
@@ -744,10 +744,10 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_dense_kernel(DenseArgs a)
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
-template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES, int TR>
+template <int E, bool ARGMAX, int NTW, bool TOK, int STAGES, int TR, int W = kWaves>
 static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
 {
-    constexpr int SLOTS = kWaves * NTW;
+    constexpr int SLOTS = W * NTW;
     a.ntq = (int)((a.Lq + 31) / 32);
     if (a.ntq == 0) a.ntq = 1;
     const bool pairs = a.pair_q != nullptr;
@@ -764,16 +764,18 @@ static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
         units = a.npairs;
     } else {
         const int ncu = device_cu_count();
-        // doc ranges: enough workgroups to give every CU one, each range at least one doc
-        int64_t R = (ncu + a.nqb - 1) / a.nqb;
+        // doc ranges: enough workgroups to give every CU one (two with 4-wave
+        // workgroups, which run two to a CU), each range at least one doc
+        const int64_t per_cu = W == 8 ? 1 : 2;
+        int64_t R = (per_cu * ncu + a.nqb - 1) / a.nqb;
         if (R > a.Nd) R = a.Nd;
         if (R < 1) R = 1;
         a.nranges = (int)R;
         units = (int64_t)a.nqb * R;
     }
     if (units <= 0) return hipSuccess;
-    dim3 grid((unsigned)units), block(kWaves * 64);
-    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, TOK, STAGES, TR>), grid, block, 0, stream, a);
+    dim3 grid((unsigned)units), block(W * 64);
+    hipLaunchKernelGGL((fwd_dense_kernel<E, ARGMAX, NTW, TOK, STAGES, TR, W>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
