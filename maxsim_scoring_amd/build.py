@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmaxsim_amd.so")
-SOURCES = ["abi.hip", "fwd_dense.hip", "fwd_varlen.hip", "bwd.hip", "topk.hip", "chamfer.hip"]
+SOURCES = ["abi.hip", "fwd_dense.hip", "fwd_varlen.hip", "fwd_dim.hip", "bwd.hip", "topk.hip", "chamfer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

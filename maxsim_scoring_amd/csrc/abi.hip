@@ -32,6 +32,11 @@ maxsim_status_t launch_status(hipError_t e) { return e == hipSuccess ? MAXSIM_OK
 
 bool dtype_ok(maxsim_dtype_t t) { return t == MAXSIM_F16 || t == MAXSIM_BF16; }
 
+// Embedding widths of the fp16/bf16 forwards: 128 has its own kernels, every
+// other width up to kMaxDim takes the general-width kernel.
+constexpr int64_t kMaxDim = 1024;
+bool width_ok(int64_t d) { return d >= 1 && d <= kMaxDim; }
+
 int elem_of(maxsim_dtype_t t) { return t == MAXSIM_F16 ? kF16 : kBF16; }
 
 // The product of non-negative sizes, or -1 when it exceeds int64.
@@ -56,7 +61,7 @@ maxsim_status_t maxsim_fwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
                            maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
-    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     if (Nq == 0 || Nd == 0) return MAXSIM_OK;
     if (!scores) return MAXSIM_ERR_NULL;
     if ((Lq > 0 && !Q) || (Ld > 0 && !D)) return MAXSIM_ERR_NULL;
@@ -67,6 +72,23 @@ maxsim_status_t maxsim_fwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
     if (argmax) {
         const int64_t n = mul_sat(pairs, Lq);
         if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    if (d != kD) {
+        const int64_t rows = mul_sat(Nd, Ld);
+        if (rows < 0 || rows > kI32Max || Lq > kI32Max) return MAXSIM_ERR_OVERFLOW;
+        DimArgs g{};
+        g.Q = Q;
+        g.D = D;
+        g.q_mask = q_mask;
+        g.d_mask = d_mask;
+        g.scores = scores;
+        g.argmax = argmax;
+        g.Nq = Nq;
+        g.Nd = Nd;
+        g.Lq = Lq;
+        g.Ld = Ld;
+        g.d = (int32_t)d;
+        return launch_status(launch_fwd_dim(elem_of(dtype), g, (hipStream_t)stream));
     }
     DenseArgs a{};
     a.Q = Q;
@@ -88,7 +110,7 @@ maxsim_status_t maxsim_fwd_varlen(maxsim_dtype_t dtype, const void* Q, const int
                                   maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0) return MAXSIM_ERR_SHAPE;
-    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     if (Nq == 0 || Nd == 0) return MAXSIM_OK;
     // Q or D may be NULL only when that packed tensor holds no tokens (an
     // empty torch tensor has no storage); the kernels then never read it.
@@ -102,6 +124,20 @@ maxsim_status_t maxsim_fwd_varlen(maxsim_dtype_t dtype, const void* Q, const int
     if (argmax) {
         const int64_t n = mul_sat(pairs, max_lq);
         if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    if (d != kD) {
+        DimArgs g{};
+        g.Q = Q;
+        g.cu_q = cu_q;
+        g.D = D;
+        g.cu_d = cu_d;
+        g.scores = scores;
+        g.argmax = argmax;
+        g.Nq = Nq;
+        g.Nd = Nd;
+        g.Lq = max_lq;
+        g.d = (int32_t)d;
+        return launch_status(launch_fwd_dim(elem_of(dtype), g, (hipStream_t)stream));
     }
     VarlenArgs a{};
     a.Q = Q;
@@ -198,7 +234,7 @@ maxsim_status_t maxsim_fwd_pairs(maxsim_dtype_t dtype, const void* Q, const void
                                  float* scores, int32_t* argmax, maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0 || P < 0) return MAXSIM_ERR_SHAPE;
-    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     if (P == 0) return MAXSIM_OK;
     if (Nq == 0 || Nd == 0) return MAXSIM_ERR_SHAPE;  // a pair needs a query and a doc
     if (!scores || !pair_q || !pair_d) return MAXSIM_ERR_NULL;
@@ -210,6 +246,26 @@ maxsim_status_t maxsim_fwd_pairs(maxsim_dtype_t dtype, const void* Q, const void
     if (argmax) {
         const int64_t n = mul_sat(P, Lq);
         if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    if (d != kD) {
+        const int64_t rows = mul_sat(Nd, Ld);
+        if (rows < 0 || rows > kI32Max || Lq > kI32Max) return MAXSIM_ERR_OVERFLOW;
+        DimArgs g{};
+        g.Q = Q;
+        g.D = D;
+        g.q_mask = q_mask;
+        g.d_mask = d_mask;
+        g.scores = scores;
+        g.argmax = argmax;
+        g.pair_q = pair_q;
+        g.pair_d = pair_d;
+        g.npairs = P;
+        g.Nq = Nq;
+        g.Nd = Nd;
+        g.Lq = Lq;
+        g.Ld = Ld;
+        g.d = (int32_t)d;
+        return launch_status(launch_fwd_dim(elem_of(dtype), g, (hipStream_t)stream));
     }
     DenseArgs a{};
     a.Q = Q;
@@ -259,7 +315,7 @@ maxsim_status_t maxsim_fwd_pairs_varlen(maxsim_dtype_t dtype, const void* Q, con
                                         float* scores, int32_t* argmax, maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || d < 0 || max_lq < 0 || P < 0) return MAXSIM_ERR_SHAPE;
-    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     if (P == 0) return MAXSIM_OK;
     if (Nq == 0 || Nd == 0) return MAXSIM_ERR_SHAPE;  // a pair needs a query and a doc
     if (!cu_q || !cu_d || !pair_q || !pair_d || !scores) return MAXSIM_ERR_NULL;
@@ -270,6 +326,23 @@ maxsim_status_t maxsim_fwd_pairs_varlen(maxsim_dtype_t dtype, const void* Q, con
     if (argmax) {
         const int64_t n = mul_sat(P, max_lq);
         if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    if (d != kD) {
+        DimArgs g{};
+        g.Q = Q;
+        g.cu_q = cu_q;
+        g.D = D;
+        g.cu_d = cu_d;
+        g.scores = scores;
+        g.argmax = argmax;
+        g.pair_q = pair_q;
+        g.pair_d = pair_d;
+        g.npairs = P;
+        g.Nq = Nq;
+        g.Nd = Nd;
+        g.Lq = max_lq;
+        g.d = (int32_t)d;
+        return launch_status(launch_fwd_dim(elem_of(dtype), g, (hipStream_t)stream));
     }
     VarlenArgs a{};
     a.Q = Q;

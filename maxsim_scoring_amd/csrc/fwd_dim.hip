@@ -1,0 +1,485 @@
+// MaxSim forward at any embedding width for gfx950: fp16/bf16 rows of d
+// elements (1 <= d <= 1024, any d other than 128, which has its own kernels),
+// uniform or cu_seqlens-packed, cross product or pair list, with masks and
+// optional argmax.
+//
+// TileMaxSim Sec. 3 (dimension tiling: a row wider than 128 is cut into
+// 128-wide chunks whose partial dot products are summed before the max) and
+// Sec. 6 "Embedding Dimension Scaling" with Table 9 (d from 64 to 768); the
+// TileMaxSim README notes on the embedding-dimension dispatch (a width up to
+// 128 is padded and the surplus lanes read as zero, which leaves every score
+// unchanged); "Flash-MaxSim" Sec. 4.1 and 4.1.1 (online max, -inf masking,
+// strict '>' argmax update) and Sec. 4.3.2 (cu_seqlens scoring over sum(L_d)
+// rows).
+//
+// Design. The streaming scheme of the 128-wide padding-free kernel,
+// generalised in the width. A row is cut into 256-byte chunks (128 elements,
+// the last chunk partial), so a 16-row tile of the doc stream becomes C chunk
+// tiles of 4 KB. Each wave is a persistent unit that owns a contiguous,
+// token-balanced range of whole docs and pulls its chunk tiles through a
+// private LDS ring with direct-to-LDS loads (16 bytes per lane, the pieces
+// XOR-swizzled by row so that the MFMA operand reads are conflict free). The
+// 16x16x32 MFMA consumes a chunk tile in up to four 64-byte K-steps and
+// accumulates the S tile over the C chunks; only after the last chunk is the
+// tile folded into the running max, so the dot products are those of the
+// whole row. Past the row end the query side holds zeros (K-steps wholly
+// past it are skipped) and the doc side re-reads a piece of the same row, so
+// no load leaves the row and the padded lanes add exact zeros.
+//
+// When the query block fits one chunk (d <= 128) its fragments stay in VGPRs
+// for the pass. Wider queries are staged once per pass into LDS, shared by the
+// four waves of a workgroup (all of which then run the same passes and
+// barriers), and read per chunk tile; with a pair list, where each wave has its
+// own query, a workgroup is a single wave. Rows whose byte length is not a
+// multiple of 16 cannot take 16-byte loads: their pieces are gathered from
+// 2-byte elements and written to LDS in the same layout (a slower path).
+//
+// Queries are the fastest grid axis, so the workgroups that are resident
+// together share doc ranges and the repeated reads of a range for different
+// queries are served from cache. Scores of a long query are the sum of its
+// 32-token passes, added in pass order.
+#include <atomic>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace maxsim {
+
+namespace {
+
+constexpr int kNT = 2;                         // 16-token query N-tiles per pass
+constexpr int kPassTokens = 16 * kNT;          // query tokens per pass
+constexpr int kChunkBytes = 256;               // bytes of a row per chunk tile
+constexpr int kCTileBytes = 16 * kChunkBytes;  // chunk tile: 16 rows x 256 bytes
+#ifndef MAXSIM_DIM_STAGES
+#define MAXSIM_DIM_STAGES 2
+#endif
+constexpr int kStages = MAXSIM_DIM_STAGES;  // chunk tiles in flight per wave (2..4)
+static_assert(kStages >= 2 && kStages <= 4, "vmcnt waits cover up to three later tiles");
+
+// vmcnt(4 n): the n most recently issued chunk tiles may still be in flight
+__device__ __forceinline__ void wait_ctiles_behind(int n)
+{
+    if (n <= 0) wait_vmcnt<0>();
+    else if (n == 1) wait_vmcnt<4>();
+    else if (n == 2) wait_vmcnt<8>();
+    else wait_vmcnt<12>();
+}
+
+// 16 bytes of a row starting at byte `off`; bytes at or past `rb` (the row's
+// length in bytes) read as zero. With 16-byte aligned rows (`al`) a piece is
+// either whole or past the end; otherwise it is gathered from 2-byte elements.
+__device__ __forceinline__ i32x4 load_piece(const unsigned char* row, int off, int rb, bool al)
+{
+    if (al) {
+        i32x4 v = {0, 0, 0, 0};
+        if (off < rb) v = *(const i32x4*)(row + off);
+        return v;
+    }
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < 16; b += 2)
+        if (off + b < rb) w[b >> 2] |= (uint32_t)(*(const uint16_t*)(row + off + b)) << (8 * (b & 3));
+    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+}
+
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, const i32x4& v)
+{
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// nonzero flags of the 4 bytes of x (byte b -> bit b)
+__device__ __forceinline__ uint32_t nz_bytes(uint32_t x)
+{
+    x |= x >> 4;
+    x |= x >> 2;
+    x |= x >> 1;
+    x &= 0x01010101u;
+    return ((x * 0x01020408u) >> 24) & 0xFu;
+}
+
+// Validity bits of the `nb` (1..16) doc tokens whose mask bytes start at the
+// wave-uniform address `p` (bit r = token r), from scalar loads of the aligned
+// dwords that hold those bytes only.
+__device__ __forceinline__ uint32_t mask_bits16(const uint8_t* p, int nb)
+{
+    const uintptr_t addr = (uintptr_t)uniform_ptr(p);
+    const int sh = (int)(addr & 3u);
+    const __attribute__((address_space(4))) uint32_t* w =
+        (const __attribute__((address_space(4))) uint32_t*)(addr - (uintptr_t)sh);
+    const int ndw = (sh + nb + 3) >> 2;  // 1 .. 5
+    uint32_t bits = 0;
+    for (int k = 0; k < ndw; ++k) bits |= nz_bytes(w[k]) << (4 * k);
+    bits >>= sh;
+    return bits & ((1u << nb) - 1u);
+}
+
+}  // namespace
+
+template <int E, bool ARGMAX, bool QREG, int W>
+__global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
+{
+    static_assert(E == kF16 || E == kBF16, "16-bit elements");
+    extern __shared__ __attribute__((aligned(16))) unsigned char dim_lds[];
+    const int lane = lane_id();
+    const int col = lane & 15;  // query token of an N-tile / doc row of a tile
+    const int g = lane >> 4;    // tile rows 4g .. 4g+3 and K-quarter g
+    const int wave = threadIdx.x >> 6;
+    const int C = uniform(a.nchunk);
+    const int RB = uniform(a.row_bytes);
+    const bool al = (RB & 15) == 0;
+    const int kt_last = (RB - (C - 1) * kChunkBytes + 63) >> 6;  // K-steps of the last chunk
+    unsigned char* qbuf = dim_lds;  // staged query block: [kNT][C] chunk tiles
+    const uint32_t q_base = lds_addr(qbuf);
+    const uint32_t ring_base =
+        (uint32_t)uniform((int)lds_addr(dim_lds + (QREG ? 0 : kNT * C * kCTileBytes) + wave * kStages * kCTileBytes));
+
+    // ---- the docs of this wave's unit -------------------------------------
+    const bool pairs = a.pair_q != nullptr;
+    const int64_t unit = (int64_t)(pairs ? blockIdx.x : blockIdx.y) * W + wave;
+    const int64_t U = pairs ? a.npairs : (int64_t)a.units;
+    const int Nd = (int)a.Nd;
+    int jb = 0, je = 0, iq = 0;
+    if (unit < U) {
+        if (pairs) {
+            const int32_t pq = a.pair_q[unit], pd = a.pair_d[unit];
+            iq = uniform(pq < 0 ? 0 : (pq >= a.Nq ? (int)a.Nq - 1 : pq));  // precondition guard
+            jb = uniform(pd < 0 ? 0 : (pd >= Nd ? Nd - 1 : pd));
+            je = jb + 1;
+        } else if (a.cu_d) {
+            const int64_t T = a.cu_d[Nd];
+            jb = unit == 0 ? 0 : nearest_boundary(a.cu_d, Nd, (T * unit) / U);
+            je = unit + 1 == U ? Nd : nearest_boundary(a.cu_d, Nd, (T * (unit + 1)) / U);
+        } else {
+            jb = uniform((int)(((int64_t)Nd * unit) / U));
+            je = uniform((int)(((int64_t)Nd * (unit + 1)) / U));
+        }
+    }
+    // a wave with no docs leaves now unless its workgroup shares a staged query
+    if ((QREG || W == 1) && jb >= je) return;
+
+    auto doc_off = [&](int j) -> int64_t { return a.cu_d ? (int64_t)a.cu_d[j] : (int64_t)j * a.Ld; };
+    const int64_t u0 = jb < je ? uniform_i64(doc_off(jb)) : 0;
+    const int span = jb < je ? uniform((int)(doc_off(je) - u0)) : 0;
+    const int ntile = (span + 15) >> 4;
+    const int nitem = ntile * C;
+    const unsigned char* unit_ptr = (const unsigned char*)a.D + u0 * RB;
+
+    // A-operand reads: row = lane % 16, logical piece 4k + g at slot (4k + g) ^ row
+    uint32_t frag_off[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) frag_off[k] = col * kChunkBytes + (((4 * k + g) ^ col) << 4);
+
+    const int64_t i_begin = pairs ? iq : blockIdx.x, i_end = pairs ? iq + 1 : a.Nq;
+    const int64_t i_step = pairs ? 1 : gridDim.x;
+    for (int64_t i = i_begin; i < i_end; i += i_step) {
+        const int64_t q0 = a.cu_q ? (int64_t)a.cu_q[i] : i * a.Lq;
+        int64_t lq64 = a.cu_q ? (int64_t)a.cu_q[i + 1] - q0 : a.Lq;
+        if (lq64 > a.Lq) lq64 = a.Lq;
+        if (lq64 < 0) lq64 = 0;
+        const int lq = uniform((int)lq64);
+        const int npass = lq == 0 ? 1 : (lq + kPassTokens - 1) / kPassTokens;
+        const int j_out = pairs ? jb : 0;  // outputs of doc j are at [j - j_out]
+        float* score_row = a.scores + (pairs ? unit : i * a.Nd);
+        int32_t* arg_row = ARGMAX ? a.argmax + (pairs ? unit : i * a.Nd) * a.Lq : nullptr;
+
+        for (int pass = 0; pass < npass; ++pass) {
+            // ---- query block: tokens pass*32 + n*16 + col ----------------------
+            bool tok_in[kNT], tok_ok[kNT];
+            i32x4 qf[kNT][4];
+#pragma unroll
+            for (int n = 0; n < kNT; ++n) {
+                const int s = pass * kPassTokens + n * 16 + col;
+                tok_in[n] = s < lq;
+                tok_ok[n] = tok_in[n] && (a.q_mask == nullptr || a.q_mask[i * a.Lq + s] != 0);
+                if constexpr (QREG) {
+                    const unsigned char* qrow = (const unsigned char*)a.Q + (q0 + (tok_in[n] ? s : 0)) * RB;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        i32x4 v = {0, 0, 0, 0};
+                        if (tok_in[n]) v = load_piece(qrow, (4 * k + g) << 4, RB, al);
+                        qf[n][k] = v;
+                    }
+                }
+            }
+            if constexpr (!QREG) {
+                block_barrier();  // every wave is done with the previous block
+                for (int it = threadIdx.x; it < kNT * C * 256; it += W * 64) {
+                    const int lp = it & 15, row = (it >> 4) & 15, nc = it >> 8;
+                    const int n = nc / C, c = nc - n * C;
+                    const int s = pass * kPassTokens + n * 16 + row;
+                    i32x4 v = {0, 0, 0, 0};
+                    if (s < lq) v = load_piece((const unsigned char*)a.Q + (q0 + s) * RB, c * kChunkBytes + (lp << 4), RB, al);
+                    *(i32x4*)(qbuf + nc * kCTileBytes + row * kChunkBytes + ((lp ^ row) << 4)) = v;
+                }
+                block_barrier();
+            }
+            if (jb >= je) continue;  // no docs: only here to share the staged query
+
+            // ---- doc cursor ------------------------------------------------------
+            int j = jb;
+            int cache_base = jb + 1;  // lane k holds cu_d[cache_base + k] - u0 (packed docs)
+            int cu_cache = 0;
+            if (a.cu_d) cu_cache = (int)((int64_t)a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd] - u0);
+            wait_vmcnt<0>();  // query fragments, masks and the cache have landed
+            auto doc_end_of = [&](int jj) -> int {  // offset of the end of doc jj in the unit
+                if (!a.cu_d) return uniform((int)((int64_t)(jj + 1) * a.Ld - u0));
+                int off = jj + 1 - cache_base;
+                if (off >= 64) {  // once per 64 docs
+                    cache_base = jj + 1;
+                    cu_cache = (int)((int64_t)a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd] - u0);
+                    wait_vmcnt<0>();
+                    off = 0;
+                }
+                return uniform(__builtin_amdgcn_readlane(cu_cache, off));
+            };
+            int doc_start = 0;
+            int doc_end = doc_end_of(j);
+
+            float m[kNT];
+            int idx[kNT];
+#pragma unroll
+            for (int n = 0; n < kNT; ++n) {
+                m[n] = -__builtin_inff();
+                idx[n] = 0;
+            }
+
+            // finish doc j: merge the 4 row groups, sum the valid query rows, write
+            auto finish_doc = [&]() {
+                float total = 0.f;
+#pragma unroll
+                for (int n = 0; n < kNT; ++n) {
+                    float mv = m[n];
+                    int iv = idx[n];
+#pragma unroll
+                    for (int off = 16; off <= 32; off <<= 1) {
+                        const float om = shfl_xor_f(mv, off);
+                        if constexpr (ARGMAX) {
+                            const int oi = shfl_xor_i(iv, off);
+                            argmax_merge(mv, iv, om, oi);
+                        } else {
+                            mv = __builtin_fmaxf(mv, om);
+                        }
+                    }
+                    const bool fin = __builtin_isfinite(mv);
+                    total += row16_sum((tok_ok[n] && fin) ? mv : 0.f);
+                    if constexpr (ARGMAX) {
+                        if (g == 0 && tok_in[n]) {
+                            const int s = pass * kPassTokens + n * 16 + col;
+                            arg_row[(int64_t)(j - j_out) * a.Lq + s] = fin ? iv - doc_start : 0;
+                        }
+                    }
+                    m[n] = -__builtin_inff();
+                    idx[n] = 0;
+                }
+                if constexpr (ARGMAX) {
+                    if (pass == 0)  // rows past the query's length are 0
+                        for (int s = lq + lane; s < a.Lq; s += 64) arg_row[(int64_t)(j - j_out) * a.Lq + s] = 0;
+                }
+                if (lane == 0) score_row[j - j_out] = pass == 0 ? total : score_row[j - j_out] + total;
+            };
+
+            // fold tile rows [lo, hi) that are valid in `vb` into the running state
+            auto fold = [&](const f32x4 (&acc)[kNT], int tile0, int lo, int hi, uint32_t vb) {
+                const uint32_t bits = ((1u << hi) - 1u) & ~((1u << lo) - 1u) & vb;
+                if (bits == 0xFFFFu) {
+#pragma unroll
+                    for (int n = 0; n < kNT; ++n) {
+                        if constexpr (ARGMAX) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (acc[n][r] > m[n]) {
+                                    m[n] = acc[n][r];
+                                    idx[n] = tile0 + 4 * g + r;
+                                }
+                        } else {
+                            m[n] = __builtin_fmaxf(__builtin_fmaxf(m[n], acc[n][0]),
+                                                   __builtin_fmaxf(__builtin_fmaxf(acc[n][1], acc[n][2]), acc[n][3]));
+                        }
+                    }
+                } else {
+                    const uint32_t lb = bits >> (4 * g);
+#pragma unroll
+                    for (int n = 0; n < kNT; ++n) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float v = ((lb >> r) & 1u) ? acc[n][r] : -__builtin_inff();
+                            if constexpr (ARGMAX) {
+                                if (v > m[n]) {
+                                    m[n] = v;
+                                    idx[n] = tile0 + 4 * g + r;
+                                }
+                            } else {
+                                m[n] = __builtin_fmaxf(m[n], v);
+                            }
+                        }
+                    }
+                }
+            };
+
+            // leading empty docs
+            while (j < je && doc_end <= 0) {
+                finish_doc();
+                ++j;
+                if (j < je) {
+                    doc_start = doc_end;
+                    doc_end = doc_end_of(j);
+                }
+            }
+
+            // ---- chunk-tile ring ---------------------------------------------------
+            int t_next = 0, c_next = 0, s_next = 0;  // next chunk tile to fetch, its stage
+            auto issue = [&]() {
+                const unsigned char* tp = (const unsigned char*)uniform_ptr(unit_ptr + (int64_t)t_next * 16 * RB);
+                const int rows_left = span - t_next * 16;  // rows past the unit re-read its last row
+                const uint32_t dst = (uint32_t)uniform((int)(ring_base + s_next * kCTileBytes));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int row = 4 * k + g;
+                    const int r = row < rows_left ? row : rows_left - 1;
+                    int off = c_next * kChunkBytes + ((col ^ row) << 4);
+                    if (al) {
+                        if (off >= RB) off = c_next * kChunkBytes;  // past the row end: a piece of the same row
+                        dma_lds16_nt(tp, (uint32_t)(r * RB + off), dst + k * 1024);
+                    } else {
+                        lds_write_b128(dst + k * 1024 + lane * 16, load_piece(tp + r * RB, off, RB, false));
+                    }
+                }
+                if (++c_next == C) {
+                    c_next = 0;
+                    ++t_next;
+                }
+                s_next = s_next + 1 == kStages ? 0 : s_next + 1;
+            };
+            for (int q = 0; q < kStages && q < nitem; ++q) issue();
+
+            int stage = 0;
+            for (int t = 0; t < ntile && j < je; ++t) {
+                uint32_t vb = 0xFFFFu;
+                if (a.d_mask) {
+                    const int nb = span - t * 16 < 16 ? span - t * 16 : 16;
+                    vb = mask_bits16(a.d_mask + u0 + t * 16, nb);
+                }
+                f32x4 acc[kNT];
+#pragma unroll
+                for (int n = 0; n < kNT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < C; ++c) {
+                    const int q = t * C + c;
+                    const int behind = nitem - 1 - q;
+                    wait_ctiles_behind(behind < kStages - 1 ? behind : kStages - 1);
+                    const uint32_t sbase = ring_base + stage * kCTileBytes;
+                    i32x4 af[4];
+                    lds_read4(af[0], af[1], af[2], af[3], sbase + frag_off[0], sbase + frag_off[1],
+                              sbase + frag_off[2], sbase + frag_off[3]);
+                    if constexpr (!QREG) {
+                        i32x4 qv[8];
+                        uint32_t qa[8];
+#pragma unroll
+                        for (int n = 0; n < kNT; ++n)
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) qa[n * 4 + k] = q_base + (n * C + c) * kCTileBytes + frag_off[k];
+                        lds_read8(qv, qa);
+#pragma unroll
+                        for (int n = 0; n < kNT; ++n)
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) qf[n][k] = qv[n * 4 + k];
+                    }
+                    if (q + kStages < nitem) issue();  // refill the stage just read
+                    stage = stage + 1 == kStages ? 0 : stage + 1;
+                    const int kt = c == C - 1 ? kt_last : 4;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (k < kt) {
+#pragma unroll
+                            for (int n = 0; n < kNT; ++n) acc[n] = mfma16<E>(af[k], qf[n][k], acc[n]);
+                        }
+                    }
+                }
+
+                const int tile0 = t * 16;
+                int lo = 0;
+                while (true) {
+                    const int hi = doc_end - tile0 < 16 ? doc_end - tile0 : 16;
+                    if (hi > lo) fold(acc, tile0, lo, hi, vb);
+                    if (doc_end - tile0 > 16) break;  // the doc continues in the next tile
+                    finish_doc();
+                    ++j;
+                    if (j >= je) break;
+                    lo = hi > lo ? hi : lo;
+                    doc_start = doc_end;
+                    doc_end = doc_end_of(j);
+                }
+            }
+            // docs left with no tokens (only when the unit has no tiles)
+            while (j < je) {
+                finish_doc();
+                ++j;
+                if (j < je) {
+                    doc_start = doc_end;
+                    doc_end = doc_end_of(j);
+                }
+            }
+            wait_vmcnt<0>();  // nothing of this pass is still in flight
+        }
+    }
+}
+
+namespace {
+
+template <int E, bool ARGMAX, bool QREG, int W>
+hipError_t launch_dim_t(DimArgs a, hipStream_t stream)
+{
+    auto kern = fwd_dim_kernel<E, ARGMAX, QREG, W>;
+    const size_t lds = (size_t)((QREG ? 0 : kNT * a.nchunk) + W * kStages) * kCTileBytes;
+    if (a.pair_q) {
+        a.units = 0;
+        const int64_t blocks = (a.npairs + W - 1) / W;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(W * 64), lds, stream, a);
+        return hipGetLastError();
+    }
+    // resident workgroups per CU, per chunk count (the LDS size depends on it)
+    static std::atomic<int> per_cu_cache[9];
+    const int key = a.nchunk < 9 ? a.nchunk : 8;
+    int per_cu = per_cu_cache[key].load(std::memory_order_relaxed);
+    if (per_cu <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, W * 64, lds) != hipSuccess || per_cu <= 0)
+            per_cu = 1;
+        per_cu_cache[key].store(per_cu, std::memory_order_relaxed);
+    }
+    // about one resident wave per unit over all queries, at most one unit per doc
+    const int64_t slots = (int64_t)device_cu_count() * per_cu * W;
+    int64_t units = (slots + a.Nq - 1) / a.Nq;
+    if (units > a.Nd) units = a.Nd;
+    if (units < 1) units = 1;
+    a.units = (int32_t)units;
+    const int64_t gq = a.Nq < 65535 ? a.Nq : 65535;
+    hipLaunchKernelGGL(kern, dim3((unsigned)gq, (unsigned)((units + W - 1) / W)), dim3(W * 64), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_dim_e(DimArgs a, hipStream_t stream)
+{
+    const bool am = a.argmax != nullptr;
+    if (a.nchunk == 1)
+        return am ? launch_dim_t<E, true, true, 4>(a, stream) : launch_dim_t<E, false, true, 4>(a, stream);
+    if (a.pair_q)
+        return am ? launch_dim_t<E, true, false, 1>(a, stream) : launch_dim_t<E, false, false, 1>(a, stream);
+    return am ? launch_dim_t<E, true, false, 4>(a, stream) : launch_dim_t<E, false, false, 4>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_dim(int elem, DimArgs a, hipStream_t stream)
+{
+    if (a.d < 1 || a.d > 1024) return hipErrorInvalidValue;
+    a.row_bytes = a.d * 2;
+    a.nchunk = (a.row_bytes + kChunkBytes - 1) / kChunkBytes;
+    switch (elem) {
+    case kF16: return launch_dim_e<kF16>(a, stream);
+    case kBF16: return launch_dim_e<kBF16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace maxsim

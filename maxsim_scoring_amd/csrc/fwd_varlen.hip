@@ -49,41 +49,6 @@ __device__ __forceinline__ void wait_tiles_behind(int n)
     else wait_vmcnt<12>();
 }
 
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Smallest j in [0, n] with cu[j] >= target, found by the whole wave with
-// 64 probes per round (cu is non-decreasing and cu[n] >= target).
-__device__ int wave_lower_bound(const int32_t* __restrict__ cu, int n, int64_t target)
-{
-    const int lane = lane_id();
-    int lo = 0, hi = n;  // the answer stays in [lo, hi]
-    while (lo < hi) {
-        const int step = (hi - lo + 63) / 64;
-        const int pos = lo + (lane + 1) * step - 1;
-        const bool pred = pos < hi ? ((int64_t)cu[pos] >= target) : true;
-        const uint64_t bal = __ballot(pred);
-        const int k = bal ? __builtin_ctzll(bal) : 64;  // first probe at or above target
-        const int nlo = lo + k * step;
-        const int nhi = lo + (k + 1) * step - 1;
-        lo = nlo < hi ? nlo : hi;
-        hi = nhi < hi ? nhi : hi;
-    }
-    return uniform(lo);
-}
-
-// The doc boundary j whose offset cu[j] is nearest to `target` (ties to the
-// lower one). Units end where the next one starts, so every doc is owned once;
-// rounding to the nearest boundary halves the worst token imbalance compared
-// with always rounding up.
-__device__ int nearest_boundary(const int32_t* __restrict__ cu, int n, int64_t target)
-{
-    const int j1 = wave_lower_bound(cu, n, target);  // first boundary at or above
-    if (j1 == 0) return 0;
-    const int64_t above = (int64_t)cu[j1] - target;
-    const int64_t below = target - (int64_t)cu[j1 - 1];
-    return uniform(below <= above ? j1 - 1 : j1);
-}
-
 }  // namespace
 
 // Three waves per SIMD (at most 168 VGPRs) with two ring stages measured

@@ -44,6 +44,31 @@ struct VarlenArgs {
     int64_t npairs;
 };
 
+// Forward at any embedding width d (rows of d elements, d * element size
+// bytes), for uniform or cu_seqlens-packed queries and docs, with or without a
+// pair list.
+struct DimArgs {
+    const void* Q;
+    const void* D;
+    const int32_t* cu_q;    // [Nq + 1] offsets, or null: query i is rows [i Lq, (i + 1) Lq)
+    const int32_t* cu_d;    // [Nd + 1] offsets, or null: doc j is rows [j Ld, (j + 1) Ld)
+    const uint8_t* q_mask;  // [Nq, Lq] or null (uniform queries only)
+    const uint8_t* d_mask;  // [Nd, Ld] or null (uniform docs only)
+    const int32_t* pair_q;  // [npairs] pair list or null (score listed pairs only)
+    const int32_t* pair_d;
+    int64_t npairs;
+    float* scores;    // [Nq, Nd] ([npairs] with a pair list)
+    int32_t* argmax;  // [Nq, Nd, Lq] ([npairs, Lq] with a pair list) or null
+    int64_t Nq, Nd;
+    int64_t Lq;  // uniform query length, or the max_lq bound of packed queries
+    int64_t Ld;  // uniform doc length (unused with cu_d)
+    int32_t d;
+    // filled by the launcher
+    int32_t row_bytes;  // d * element size
+    int32_t nchunk;     // 256-byte chunks per row
+    int32_t units;      // streaming units per query (or pairs)
+};
+
 struct BwdArgs {
     const void* Q;
     const void* D;
@@ -111,6 +136,7 @@ int device_cu_count();
 
 hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t stream);
 hipError_t launch_fwd_varlen(int elem, VarlenArgs a, hipStream_t stream);
+hipError_t launch_fwd_dim(int elem, DimArgs a, hipStream_t stream);
 hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream);
 hipError_t launch_topk(TopkArgs a, hipStream_t stream);
 hipError_t launch_bwd_varlen(int elem, VarBwdArgs a, hipStream_t stream);

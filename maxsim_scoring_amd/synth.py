@@ -6,7 +6,8 @@ INT8 workload. It holds no part of the scoring arithmetic. Both the HIP path and
 the CPU oracle are fed from here, so the two always see identical bytes.
 
 Recipe (the same for every workload):
-  * an embedding row is d = 128 i.i.d. standard normal float32 draws divided by
+  * an embedding row is d i.i.d. standard normal float32 draws (d = 128 unless a
+    workload names another width) divided by
     the row's l2 norm (computed in float32), then rounded to nearest-even into
     the workload dtype (fp16 via numpy, bf16 via torch's CPU cast);
   * rows are produced in chunks of ``CHUNK_ROWS``; chunk ``c`` of stream ``s``
@@ -18,8 +19,9 @@ Recipe (the same for every workload):
 The shapes and distributions follow the pages' workloads: ColBERT reranking
 (one 32-token query against passages of 50-300 tokens, packed without
 padding), ColPali in-batch contrastive scoring (128 queries of 128 tokens
-against 128 pages of 1024 patches with prefix masks), and long-query INT8
-scoring with per-tensor symmetric scales.
+against 128 pages of 1024 patches with prefix masks), long-query INT8
+scoring with per-tensor symmetric scales, and the embedding-width sweep (one
+32-token query against 10,000 docs of 128 tokens at widths 64 to 768).
 """
 
 from __future__ import annotations
@@ -250,6 +252,14 @@ def colpali_bf16(seed: int = 3, Nq: int = 128, Nd: int = 128, Lq: int = 128,
                  {"k": k, "m": m})
 
 
+def dim_scaling_fp16(d: int, seed: int = 6, Nd: int = 10_000, Lq: int = 32, Ld: int = 128) -> Dense:
+    """The embedding-width sweep: one 32-token query against Nd uniform docs
+    of 128 tokens, fp16, rows of width d, no masks."""
+    Q = unit_rows(seed, _S_Q, Lq, d).view(1, Lq, d)
+    D = unit_rows(seed, _S_D, Nd * Ld, d).view(Nd, Ld, d)
+    return Dense(f"dim_fp16_1x{Nd}_lq{Lq}_ld{Ld}_d{d}", Q, D, None, None, False, seed)
+
+
 def int8_long_query(seed: int = 4, Nd: int = 10_000, Lq: int = 1024, Ld: int = 1024) -> Int8:
     """One 1024-token query against Nd docs of 1024 tokens, int8 per-tensor."""
     Qf = unit_rows(seed, _S_Q, Lq, dtype=torch.float32).view(1, Lq, D_MODEL)
@@ -347,11 +357,11 @@ def random_dense(seed: int, Nq: int, Nd: int, Lq: int, Ld: int,
                  dtype: torch.dtype = torch.float16, q_mask_p: float = 0.0,
                  d_mask_p: float = 0.0, dup_tokens: bool = False,
                  dead_docs: int = 0, dead_queries: int = 0,
-                 want_argmax: bool = True) -> Dense:
+                 want_argmax: bool = True, d: int = D_MODEL) -> Dense:
     """Random masks (Bernoulli keep-probabilities 1-p), optionally duplicated
     doc tokens (exact ties), fully masked docs and fully masked queries."""
-    Q = unit_rows(seed, _S_Q, Nq * Lq, dtype=dtype).view(Nq, Lq, D_MODEL)
-    D = unit_rows(seed, _S_D, Nd * Ld, dtype=dtype).view(Nd, Ld, D_MODEL).clone()
+    Q = unit_rows(seed, _S_Q, Nq * Lq, d, dtype=dtype).view(Nq, Lq, d)
+    D = unit_rows(seed, _S_D, Nd * Ld, d, dtype=dtype).view(Nd, Ld, d).clone()
     rng = np.random.default_rng([seed, _S_MISC])
     if dup_tokens and Ld >= 2:
         for j in range(Nd):
@@ -369,13 +379,14 @@ def random_dense(seed: int, Nq: int, Nd: int, Lq: int, Ld: int,
 
 
 def random_varlen(seed: int, q_lengths, d_lengths, dtype: torch.dtype = torch.float16,
-                  max_lq: Optional[int] = None, want_argmax: bool = True) -> Varlen:
+                  max_lq: Optional[int] = None, want_argmax: bool = True,
+                  d: int = D_MODEL) -> Varlen:
     q_lengths = np.asarray(q_lengths, dtype=np.int64)
     d_lengths = np.asarray(d_lengths, dtype=np.int64)
     cu_q = cu_seqlens(q_lengths)
     cu_d = cu_seqlens(d_lengths)
-    Q = unit_rows(seed, _S_Q, int(cu_q[-1]), dtype=dtype)
-    D = unit_rows(seed, _S_D, int(cu_d[-1]), dtype=dtype)
+    Q = unit_rows(seed, _S_Q, int(cu_q[-1]), d, dtype=dtype)
+    D = unit_rows(seed, _S_D, int(cu_d[-1]), d, dtype=dtype)
     mlq = int(q_lengths.max()) if max_lq is None and len(q_lengths) else (max_lq or 0)
     return Varlen(f"varlen_{len(q_lengths)}x{len(d_lengths)}", Q, cu_q, mlq, D, cu_d,
                   want_argmax, seed)

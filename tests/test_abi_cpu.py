@@ -60,7 +60,9 @@ def fwd(L, dtype=0, Q=FAKE, D=FAKE, Nq=2, Nd=3, Lq=4, Ld=5, d=128, qm=None, dm=N
 def test_fwd_validation(L):
     assert fwd(L, Nq=-1) == ERR_SHAPE
     assert fwd(L, Ld=-5) == ERR_SHAPE
-    assert fwd(L, d=64) == ERR_UNSUPPORTED
+    assert fwd(L, d=0) == ERR_UNSUPPORTED         # widths 1 .. 1024
+    assert fwd(L, d=1025) == ERR_UNSUPPORTED
+    assert fwd(L, d=64, Nd=1 << 16, Ld=1 << 15) == ERR_OVERFLOW  # other widths: Nd*Ld < 2^31
     assert fwd(L, dtype=7) == ERR_UNSUPPORTED
     assert fwd(L, sc=None) == ERR_NULL
     assert fwd(L, Q=None) == ERR_NULL
@@ -79,7 +81,8 @@ def test_fwd_validation(L):
 def test_varlen_validation(L):
     f = L.maxsim_fwd_varlen
     assert f(0, FAKE, FAKE, 1, -1, FAKE, FAKE, 2, 128, FAKE, None, None) == ERR_SHAPE
-    assert f(0, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 96, FAKE, None, None) == ERR_UNSUPPORTED
+    assert f(0, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 0, FAKE, None, None) == ERR_UNSUPPORTED
+    assert f(0, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 2048, FAKE, None, None) == ERR_UNSUPPORTED
     assert f(1, FAKE, None, 1, 32, FAKE, FAKE, 2, 128, FAKE, None, None) == ERR_NULL
     assert f(1, FAKE, FAKE, 1, 32, FAKE, None, 2, 128, FAKE, None, None) == ERR_NULL
     assert f(1, FAKE, FAKE, 1, 32, FAKE, FAKE, 2, 128, None, None, None) == ERR_NULL
@@ -164,6 +167,8 @@ def test_pairs_validation(L):
     assert call(Nd=0) == ERR_SHAPE          # a pair needs a doc
     assert call(P=0, Nd=0, pq=None) == OK   # nothing to score
     assert call(dtype=5) == ERR_UNSUPPORTED
+    assert call(d=1100) == ERR_UNSUPPORTED
+    assert call(d=96, Nd=1 << 16, Ld=1 << 15) == ERR_OVERFLOW
     assert call(pq=None) == ERR_NULL
     assert call(sc=None) == ERR_NULL
     assert call(pd=MIS2) == ERR_UNSUPPORTED
@@ -179,7 +184,8 @@ def test_pairs_varlen_validation(L):
     assert f(P=-1) == ERR_SHAPE
     assert f(mlq=-1) == ERR_SHAPE
     assert f(Nq=0) == ERR_SHAPE                # a pair needs a query
-    assert f(d=64) == ERR_UNSUPPORTED
+    assert f(d=0) == ERR_UNSUPPORTED
+    assert f(d=1025) == ERR_UNSUPPORTED
     assert f(dtype=3) == ERR_UNSUPPORTED
     assert f(pq=None) == ERR_NULL
     assert f(cd=None) == ERR_NULL

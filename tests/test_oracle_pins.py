@@ -579,6 +579,59 @@ def test_pairs_varlen_equals_cross_product(oracle_mod):
     assert np.array_equal(pa, ra[pq, pd])
 
 
+# ------------------------------------------------------------------ embedding widths
+
+@pytest.mark.parametrize("d", [1, 8, 100, 200, 768])
+def test_brute_force_widths(oracle_mod, d):
+    """Any embedding width (TileMaxSim Sec. 6, Table 9 sweeps d from 64 to
+    768): cross product with masks and a dead doc, and packed sequences with
+    empty ones, against brute force."""
+    w = synth.random_dense(40 + d, 2, 3, 9, 21, dtype=torch.bfloat16, q_mask_p=0.2, d_mask_p=0.2,
+                           dead_docs=1, d=d)
+    s, a = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    sb, ab = bf.dense(w.Q, w.D, w.q_mask, w.d_mask)
+    np.testing.assert_allclose(s, sb, rtol=0, atol=1e-12)
+    assert np.array_equal(a, ab)
+    v = synth.random_varlen(41 + d, [3, 0, 17], [5, 0, 1, 40], d=d)
+    s, a = oracle_mod.fwd_varlen(v.Q, v.cu_q, v.max_lq, v.D, v.cu_d)
+    sb, ab = bf.varlen(v.Q, v.cu_q, v.max_lq, v.D, v.cu_d)
+    np.testing.assert_allclose(s, sb, rtol=0, atol=1e-12)
+    assert np.array_equal(a, ab)
+
+
+def test_zero_padded_width_is_identical(oracle_mod):
+    """Widening the rows with zero lanes changes no score and no argmax (the
+    TileMaxSim README's embedding-dimension dispatch: padded lanes read as
+    zero and add nothing)."""
+    rng = np.random.default_rng(61)
+    Q = rng.standard_normal((2, 11, 100))
+    D = rng.standard_normal((3, 30, 100))
+    dm = (rng.random((3, 30)) > 0.2).astype(np.uint8)
+    s, a = oracle_mod.fwd(Q, D, None, dm)
+    for width in (128, 256):
+        Qp = np.zeros((2, 11, width))
+        Dp = np.zeros((3, 30, width))
+        Qp[..., :100] = Q
+        Dp[..., :100] = D
+        sp, ap = oracle_mod.fwd(Qp, Dp, None, dm)
+        assert np.array_equal(s, sp) and np.array_equal(a, ap)
+
+
+def test_width_chunks_sum_to_full_dot(oracle_mod):
+    """Dimension tiling (TileMaxSim Sec. 3): cutting d = 300 into 128-wide
+    chunks and summing the chunks' partial similarity tiles before the max
+    gives the oracle's scores; taking the max per chunk first does not."""
+    rng = np.random.default_rng(62)
+    Q = rng.standard_normal((2, 7, 300))
+    D = rng.standard_normal((3, 19, 300))
+    s, _ = oracle_mod.fwd(Q, D)
+    S = sum(np.einsum("isk,jtk->ijst", Q[..., c:c + 128], D[..., c:c + 128]) for c in range(0, 300, 128))
+    np.testing.assert_allclose(s, S.max(axis=3).sum(axis=2), rtol=0, atol=1e-10)
+    wrong = sum(np.einsum("isk,jtk->ijst", Q[..., c:c + 128], D[..., c:c + 128]).max(axis=3).sum(axis=2)
+                for c in range(0, 300, 128))
+    assert np.abs(wrong - s).max() > 1e-3
+
+
 # ------------------------------------------------------------------ Chamfer distance
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (2, 5, 7), (3, 40, 13), (1, 64, 64)])
