@@ -193,6 +193,36 @@ def bench_int8(torch, ms, synth, wl, steps, warmup):
             "kernel": "fwd_dense_kernel"}
 
 
+DIM_SWEEP = (64, 96, 256, 384, 768)
+
+
+def bench_dim_sweep(torch, ms, synth, wl, steps, warmup):
+    """The embedding-width sweep: one 32-token fp16 query against 10,000 docs
+    of 128 tokens at each width, no masks, no argmax; every launch follows a
+    cache flush because the smaller widths' D fits in the last-level cache."""
+    rows = {}
+    for d in DIM_SWEEP:
+        w = synth.dim_scaling_fp16(d)
+        Q, D = w.Q.cuda(), w.D.cuda()
+        scores = torch.empty((1, 10_000), dtype=torch.float32, device="cuda")
+
+        def step():
+            ms.maxsim_fwd(Q, D, scores=scores)
+
+        total, times = time_steps(torch, step, min(steps, 10), min(warmup, 5), flush_bytes=512 << 20)
+        t = statistics.median(times)
+        nbytes = wl.dense_fwd_bytes(1, 10_000, 32, 128, d, 2, False, False, False)
+        rows[f"d{d}"] = {"workload": w.name, "ms": t, "docs_per_s": 10_000 / (t * 1e-3),
+                         "algorithmic_bytes": nbytes,
+                         "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+        del Q, D, w
+        torch.cuda.empty_cache()
+    best = max(rows.values(), key=lambda r: r["roofline"]["frac"])
+    return {"workload": "dim_sweep_fp16_1x10000_lq32_ld128", "ms": rows["d768"]["ms"],
+            "widths": rows, "roofline": rows["d768"]["roofline"], "best_width": best["workload"],
+            "kernel": "fwd_dim_kernel"}
+
+
 def bench_backward(torch, ms, synth, wl, steps, warmup):
     fw = synth.colpali_bf16()
     Q, D, qm, dm = (t.cuda() for t in (fw.Q, fw.D, fw.q_mask, fw.d_mask))
@@ -401,7 +431,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="",
                     help="run one workload: rerank|tiny|colpali|int8|backward|backward_varlen|"
-                         "pairs_varlen|two_stage|topk|chamfer|copy")
+                         "pairs_varlen|two_stage|topk|chamfer|dim_sweep|copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -420,11 +450,12 @@ def main() -> int:
 
     names = [args.only] if args.only else [HEADLINE, "tiny", "colpali", "int8", "backward",
                                            "backward_varlen", "pairs_varlen", "two_stage", "topk",
-                                           "chamfer"]
+                                           "chamfer", "dim_sweep"]
     fns = {"rerank": bench_rerank, "tiny": bench_tiny, "colpali": bench_colpali,
            "int8": bench_int8, "backward": bench_backward, "backward_varlen": bench_backward_varlen,
            "pairs_varlen": bench_pairs_varlen, "two_stage": bench_two_stage,
-           "topk": bench_topk, "chamfer": bench_chamfer, "copy": bench_copy}
+           "topk": bench_topk, "chamfer": bench_chamfer, "dim_sweep": bench_dim_sweep,
+           "copy": bench_copy}
     per = {}
     head = None
     head_w = None

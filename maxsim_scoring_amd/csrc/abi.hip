@@ -32,8 +32,9 @@ maxsim_status_t launch_status(hipError_t e) { return e == hipSuccess ? MAXSIM_OK
 
 bool dtype_ok(maxsim_dtype_t t) { return t == MAXSIM_F16 || t == MAXSIM_BF16; }
 
-// Embedding widths of the fp16/bf16 forwards: 128 has its own kernels, every
-// other width up to kMaxDim takes the general-width kernel.
+// Embedding widths of the fp16/bf16 entry points: 128 has its own forward
+// kernels, every other width up to kMaxDim takes the general-width forward;
+// the backward gathers handle any width in 128-wide chunks.
 constexpr int64_t kMaxDim = 1024;
 bool width_ok(int64_t d) { return d >= 1 && d <= kMaxDim; }
 
@@ -368,7 +369,7 @@ maxsim_status_t maxsim_bwd_varlen(maxsim_dtype_t dtype, const void* Q, const int
                                   maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || total_q < 0 || total_d < 0 || d < 0 || max_lq < 0) return MAXSIM_ERR_SHAPE;
-    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     // packed rows need a sequence to belong to, and a query row a max_lq slot
     if ((Nq == 0 && total_q > 0) || (Nd == 0 && total_d > 0) || (total_q > 0 && max_lq == 0))
         return MAXSIM_ERR_SHAPE;
@@ -401,6 +402,7 @@ maxsim_status_t maxsim_bwd_varlen(maxsim_dtype_t dtype, const void* Q, const int
     a.Td = total_d;
     a.nnz_cap = nnz;
     a.max_lq = max_lq;
+    a.d = (int32_t)d;
     return launch_status(launch_bwd_varlen(elem_of(dtype), a, (hipStream_t)stream));
 }
 
@@ -477,7 +479,7 @@ maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
                            maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
-    if (!dtype_ok(dtype) || d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     const int64_t nsrc = mul_sat(mul_sat(Nq, Nd), Lq);
     const int64_t nrows = mul_sat(Nd, Ld);
     if (nsrc < 0 || nsrc > kI32Max) return MAXSIM_ERR_OVERFLOW;
@@ -508,6 +510,7 @@ maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
     a.Nd = Nd;
     a.Lq = Lq;
     a.Ld = Ld;
+    a.d = (int32_t)d;
     return launch_status(launch_bwd(elem_of(dtype), a, (hipStream_t)stream));
 }
 

@@ -80,6 +80,52 @@ __device__ __forceinline__ void store8(float* p, const float (&a)[8])
     __builtin_nontemporal_store((f4){a[4], a[5], a[6], a[7]}, (f4*)(p + 4));
 }
 
+// One lane's share of a row at any width: elements [e0, e0 + n) of a row,
+// n in 0..8 (n < 8 only in the last 128-wide chunk of a row whose width is not
+// a multiple of 128). `vec`: all 8 wanted and 16-byte aligned, one load.
+template <int E> __device__ __forceinline__ float elem_f32(const void* base, int64_t off);
+template <> __device__ __forceinline__ float elem_f32<kF16>(const void* base, int64_t off)
+{
+    return (float)((const _Float16*)base)[off];
+}
+template <> __device__ __forceinline__ float elem_f32<kBF16>(const void* base, int64_t off)
+{
+    return __builtin_bit_cast(float, (uint32_t)((const uint16_t*)base)[off] << 16);
+}
+template <int E>
+__device__ __forceinline__ void loadn(const void* base, int64_t off, int n, bool vec, float (&x)[8])
+{
+    if (vec) {
+        load8<E>(base, off, x);
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = k < n ? elem_f32<E>(base, off + k) : 0.f;
+}
+__device__ __forceinline__ void storen(float* p, int n, bool vec, const float (&a)[8])
+{
+    if (vec) {
+        store8(p, a);
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        if (k < n) __builtin_nontemporal_store(a[k], p + k);
+}
+
+// Lane l16's elements of 128-wide chunk c of a row of width dw.
+struct LaneSpan {
+    int e0, n;
+    bool vec;
+    __device__ __forceinline__ LaneSpan(int c, int l16, int64_t dw, bool gen)
+    {
+        e0 = c * 128 + 8 * l16;
+        const int64_t left = dw - e0;
+        n = !gen ? 8 : (left <= 0 ? 0 : (left >= 8 ? 8 : (int)left));
+        vec = !gen || (n == 8 && (dw & 7) == 0);
+    }
+};
+
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
 __device__ __forceinline__ void barrier_lds()
@@ -307,7 +353,7 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
     // live(j) for the dq pass, parked in dD[j, 0, 0] (dD is written last)
     if (wave == 0 && Ld > 0) {
         const bool live = doc_live(a.d_mask, j, Ld);
-        if (lane == 0) a.dD[(int64_t)j * Ld * kD] = live ? 1.f : 0.f;
+        if (lane == 0) a.dD[(int64_t)j * Ld * a.d] = live ? 1.f : 0.f;
     }
     // doc-local source k = i*Lq + s is the flat source (i*Nd + j)*Lq + s
     auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
@@ -327,68 +373,74 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
 
 // Eq. (2): dQ[i,s] = q_mask[i,s] * sum_j g[i,j] live(j) D[j, argmax[i,j,s]].
 // Workgroup = query i and 16 rows s; group g owns row s0 + g, lane l16 owns
-// dims 8*l16 .. 8*l16+7.
-template <int E>
+// dims 8*l16 .. 8*l16+7 of each 128-wide chunk of the row (GEN: any width,
+// the chunks taken one after another).
+template <int E, bool GEN>
 __global__ __launch_bounds__(kGatherThreads) void dq_kernel(BwdArgs a)
 {
     __shared__ int32_t am[kDqDocs][kGroups];  // argmax[i, j0 + jj, s0 + g]
     __shared__ float wj[kDqDocs];             // g[i, j0 + jj] * live(j0 + jj)
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
+    const int64_t DW = GEN ? (int64_t)a.d : kD;
+    const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
     const int64_t sblocks = (Lq + kGroups - 1) / kGroups;
     const int64_t i = blockIdx.x / sblocks;
     const int64_t s0 = (blockIdx.x % sblocks) * kGroups;
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
     const int64_t s = s0 + grp;
     const bool row_ok = s < Lq;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t j0 = 0; j0 < Nd; j0 += kDqDocs) {
-        const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
-        barrier_lds();
-        for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
-            const int jj = e / kGroups, gg = e % kGroups;
-            int32_t t = 0;
-            if (jj < nj && s0 + gg < Lq) {
-                t = a.argmax[(i * Nd + j0 + jj) * Lq + s0 + gg];
-                t = t < 0 ? 0 : (t >= Ld ? (int32_t)(Ld - 1) : t);  // precondition guard
+    for (int c = 0; c < nchunk; ++c) {
+        const LaneSpan ls(c, l16, DW, GEN);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int64_t j0 = 0; j0 < Nd; j0 += kDqDocs) {
+            const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
+            barrier_lds();
+            for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
+                const int jj = e / kGroups, gg = e % kGroups;
+                int32_t t = 0;
+                if (jj < nj && s0 + gg < Lq) {
+                    t = a.argmax[(i * Nd + j0 + jj) * Lq + s0 + gg];
+                    t = t < 0 ? 0 : (t >= Ld ? (int32_t)(Ld - 1) : t);  // precondition guard
+                }
+                am[jj][gg] = t;
             }
-            am[jj][gg] = t;
-        }
-        if (tid < nj) {
-            const int64_t jd = j0 + tid;
-            wj[tid] = a.g[i * Nd + jd] * a.dD[jd * Ld * kD];  // live(j) parked by the csr pass
-        }
-        barrier_lds();
-        if (!row_ok) continue;
-        const int64_t dbase = (j0 * Ld) * kD + 8 * l16;
-        int jj = 0;
-        for (; jj + 8 <= nj; jj += 8) {
-            float x[8][8];
+            if (tid < nj) {
+                const int64_t jd = j0 + tid;
+                wj[tid] = a.g[i * Nd + jd] * a.dD[jd * Ld * DW];  // live(j) parked by the csr pass
+            }
+            barrier_lds();
+            if (!row_ok || ls.n == 0) continue;
+            const int64_t dbase = (j0 * Ld) * DW + ls.e0;
+            int jj = 0;
+            for (; jj + 8 <= nj; jj += 8) {
+                float x[8][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                load8<E>(a.D, dbase + ((int64_t)(jj + u) * Ld + am[jj + u][grp]) * kD, x[u]);
+                for (int u = 0; u < 8; ++u)
+                    loadn<E>(a.D, dbase + ((int64_t)(jj + u) * Ld + am[jj + u][grp]) * DW, ls.n, ls.vec, x[u]);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float w = wj[jj + u];
+                for (int u = 0; u < 8; ++u) {
+                    const float w = wj[jj + u];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[u][k], acc[k]);
+                    for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[u][k], acc[k]);
+                }
+            }
+            for (; jj < nj; ++jj) {
+                float x[8];
+                loadn<E>(a.D, dbase + ((int64_t)jj * Ld + am[jj][grp]) * DW, ls.n, ls.vec, x);
+                const float w = wj[jj];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
             }
         }
-        for (; jj < nj; ++jj) {
-            float x[8];
-            load8<E>(a.D, dbase + ((int64_t)jj * Ld + am[jj][grp]) * kD, x);
-            const float w = wj[jj];
+        if (row_ok && ls.n > 0) {
+            const int64_t r = i * Lq + s;
+            if (a.q_mask && a.q_mask[r] == 0) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
+                for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+            }
+            storen(a.dQ + r * DW + ls.e0, ls.n, ls.vec, acc);
         }
-    }
-    if (row_ok) {
-        const int64_t r = i * Lq + s;
-        if (a.q_mask && a.q_mask[r] == 0) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-        }
-        store8(a.dQ + r * kD + 8 * l16, acc);
     }
 }
 
@@ -398,12 +450,14 @@ __global__ __launch_bounds__(kGatherThreads) void dq_kernel(BwdArgs a)
 // dims 8*l16 .. 8*l16+7. TAB: the doc's weights w for every (i,s) are staged
 // in LDS first (Nq*Lq <= kWTab), so a source costs one CSR read and one
 // gather; otherwise w is read from g and q_mask per source.
-template <int E, bool TAB>
+template <int E, bool TAB, bool GEN>
 __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXSIM_DD_WAVES))) void dd_kernel(
     BwdArgs a, int rows_per_block)
 {
     __shared__ float wtab[TAB ? kWTab : 1];
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
+    const int64_t DW = GEN ? (int64_t)a.d : kD;
+    const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
     const int64_t blocks_per_doc = (Ld + rows_per_block - 1) / rows_per_block;
     const int64_t j = blockIdx.x / blocks_per_doc;
     const int64_t t_begin = (blockIdx.x % blocks_per_doc) * rows_per_block;
@@ -430,7 +484,9 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
     // src - j*Lq = i*(Nd*Lq) + s
     const uint32_t ndlq = (uint32_t)(Nd * Lq), jlq = (uint32_t)(j * Lq);
     const uint32_t nq = (uint32_t)a.Nq, lq = (uint32_t)Lq;
-    for (int64_t t = t_begin + grp; t < t_end; t += kDdGroups) {
+    for (int64_t t = t_begin + grp; t < t_end; t += kDdGroups)
+    for (int c = 0; c < nchunk; ++c) {
+        const LaneSpan ls(c, l16, DW, GEN);
         const int64_t row = j * Ld + t;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (live) {
@@ -462,7 +518,7 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                     for (int u = 0; u < kDdUnroll; ++u) {
                         const int qr = __shfl(qrow, gbase + k + u, 64);
                         ww[u] = __shfl(w, gbase + k + u, 64);
-                        load8<E>(a.Q, (int64_t)qr * kD + 8 * l16, xv[u]);
+                        loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv[u]);
                     }
 #pragma unroll
                     for (int u = 0; u < kDdUnroll; ++u)
@@ -473,17 +529,17 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                     const int qr = __shfl(qrow, gbase + k, 64);
                     const float wk = __shfl(w, gbase + k, 64);
                     float xv[8];
-                    load8<E>(a.Q, (int64_t)qr * kD + 8 * l16, xv);
+                    loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wk, xv[q], acc[q]);
                 }
             }
         }
-        store8(a.dD + row * kD + 8 * l16, acc);
+        if (ls.n > 0) storen(a.dD + row * DW + ls.e0, ls.n, ls.vec, acc);
     }
 }
 
-template <int E>
+template <int E, bool GEN>
 static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream)
 {
     hipError_t err;
@@ -495,7 +551,7 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream)
     if (qrows > 0) {
         // (with no docs the kernel writes zeros)
         const int64_t blocks = a.Nq * ((a.Lq + kGroups - 1) / kGroups);
-        hipLaunchKernelGGL(dq_kernel<E>, dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
+        hipLaunchKernelGGL((dq_kernel<E, GEN>), dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (a.Nd > 0 && a.Ld > 0) {
@@ -507,10 +563,10 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream)
         if (rpb > 4096) rpb = 4096;
         const int64_t blocks = a.Nd * ((a.Ld + rpb - 1) / rpb);
         if (a.Nq * a.Lq <= kWTab)
-            hipLaunchKernelGGL((dd_kernel<E, true>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
+            hipLaunchKernelGGL((dd_kernel<E, true, GEN>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
                                (int)rpb);
         else
-            hipLaunchKernelGGL((dd_kernel<E, false>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
+            hipLaunchKernelGGL((dd_kernel<E, false, GEN>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
                                (int)rpb);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -519,9 +575,10 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream)
 
 hipError_t launch_bwd(int elem, BwdArgs a, hipStream_t stream)
 {
+    const bool gen = a.d != kD;
     switch (elem) {
-    case kF16: return launch_bwd_t<kF16>(a, stream);
-    case kBF16: return launch_bwd_t<kBF16>(a, stream);
+    case kF16: return gen ? launch_bwd_t<kF16, true>(a, stream) : launch_bwd_t<kF16, false>(a, stream);
+    case kBF16: return gen ? launch_bwd_t<kBF16, true>(a, stream) : launch_bwd_t<kBF16, false>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -591,7 +648,7 @@ __global__ __launch_bounds__(kPrepThreads) void vbwd_prep_kernel(VarBwdArgs a)
     for (int64_t j = j0; j < j1; ++j) {
         const int64_t r = a.cu_d[j];
         if (a.cu_d[j + 1] > r) {
-            if (r >= 0 && r < Td) a.dD[r * kD] = __builtin_bit_cast(float, (uint32_t)((int64_t)before * a.Tq));
+            if (r >= 0 && r < Td) a.dD[r * a.d] = __builtin_bit_cast(float, (uint32_t)((int64_t)before * a.Tq));
             ++before;
         }
     }
@@ -631,13 +688,13 @@ __global__ __launch_bounds__(kCsrThreads) void vbwd_csr_kernel(VarBwdArgs a)
             }
         }
     };
-    const int64_t carry = (int64_t)__builtin_bit_cast(uint32_t, a.dD[d0 * kD]);  // parked by prep
+    const int64_t carry = (int64_t)__builtin_bit_cast(uint32_t, a.dD[d0 * a.d]);  // parked by prep
     build_segment_csr(Tq, L, carry, a.row_ptr + d0, a.col_idx, load);
 }
 
 // Eq. (2) per packed query row p = cu_q[i] + s:
 // dQ[p] = sum over docs j with a token, ascending, of g[i,j] D[cu_d[j] + argmax[i,j,s]].
-template <int E>
+template <int E, bool GEN>
 __global__ __launch_bounds__(kGatherThreads) void vbwd_dq_kernel(VarBwdArgs a)
 {
     __shared__ int64_t dbase[kDqDocs];
@@ -646,6 +703,8 @@ __global__ __launch_bounds__(kGatherThreads) void vbwd_dq_kernel(VarBwdArgs a)
     __shared__ float wq[kDqDocs][kGroups];
     __shared__ int32_t qi[kGroups], qs[kGroups];
     const int64_t Nd = a.Nd, Tq = a.Tq;
+    const int64_t DW = GEN ? (int64_t)a.d : kD;
+    const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
     const int64_t p0 = (int64_t)blockIdx.x * kGroups;
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
     const int64_t p = p0 + grp;
@@ -661,77 +720,84 @@ __global__ __launch_bounds__(kGatherThreads) void vbwd_dq_kernel(VarBwdArgs a)
         qi[tid] = i;
         qs[tid] = s;
     }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // with no doc token at all there is no D row to gather (dQ = 0)
-    for (int64_t j0 = 0; j0 < (a.Td > 0 ? Nd : 0); j0 += kDqDocs) {
-        const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
-        barrier_lds();
-        if (tid < nj) {
-            const int64_t b = a.cu_d[j0 + tid];
-            int64_t l = (int64_t)a.cu_d[j0 + tid + 1] - b;
-            if (b < 0 || b >= a.Td) l = 0;
-            else if (l > a.Td - b) l = a.Td - b;
-            dbase[tid] = b;
-            dlen[tid] = (int32_t)(l < 0 ? 0 : l);
-        }
-        barrier_lds();
-        for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
-            const int jj = e / kGroups, gg = e % kGroups;
-            int32_t t = 0;
-            float w = 0.f;
-            if (jj < nj && p0 + gg < Tq && dlen[jj] > 0) {
-                const int64_t ij = (int64_t)qi[gg] * Nd + j0 + jj;
-                t = a.argmax[ij * a.max_lq + qs[gg]];
-                t = t < 0 ? 0 : (t >= dlen[jj] ? dlen[jj] - 1 : t);  // precondition guard
-                w = a.g[ij];
+    for (int c = 0; c < nchunk; ++c) {
+        const LaneSpan ls(c, l16, DW, GEN);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // with no doc token at all there is no D row to gather (dQ = 0)
+        for (int64_t j0 = 0; j0 < (a.Td > 0 ? Nd : 0); j0 += kDqDocs) {
+            const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
+            barrier_lds();
+            if (tid < nj) {
+                const int64_t b = a.cu_d[j0 + tid];
+                int64_t l = (int64_t)a.cu_d[j0 + tid + 1] - b;
+                if (b < 0 || b >= a.Td) l = 0;
+                else if (l > a.Td - b) l = a.Td - b;
+                dbase[tid] = b;
+                dlen[tid] = (int32_t)(l < 0 ? 0 : l);
             }
-            am[jj][gg] = t;
-            wq[jj][gg] = w;
-        }
-        barrier_lds();
-        if (!row_ok) continue;
-        int jj = 0;
-        for (; jj + 8 <= nj; jj += 8) {
-            float x[8][8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t row = dlen[jj + u] > 0 ? dbase[jj + u] + am[jj + u][grp] : 0;
-                load8<E>(a.D, row * kD + 8 * l16, x[u]);
+            barrier_lds();
+            for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
+                const int jj = e / kGroups, gg = e % kGroups;
+                int32_t t = 0;
+                float w = 0.f;
+                if (jj < nj && p0 + gg < Tq && dlen[jj] > 0) {
+                    const int64_t ij = (int64_t)qi[gg] * Nd + j0 + jj;
+                    t = a.argmax[ij * a.max_lq + qs[gg]];
+                    t = t < 0 ? 0 : (t >= dlen[jj] ? dlen[jj] - 1 : t);  // precondition guard
+                    w = a.g[ij];
+                }
+                am[jj][gg] = t;
+                wq[jj][gg] = w;
             }
+            barrier_lds();
+            if (!row_ok || ls.n == 0) continue;
+            int jj = 0;
+            for (; jj + 8 <= nj; jj += 8) {
+                float x[8][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float w = wq[jj + u][grp];
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t row = dlen[jj + u] > 0 ? dbase[jj + u] + am[jj + u][grp] : 0;
+                    loadn<E>(a.D, row * DW + ls.e0, ls.n, ls.vec, x[u]);
+                }
 #pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[u][k], acc[k]);
+                for (int u = 0; u < 8; ++u) {
+                    const float w = wq[jj + u][grp];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[u][k], acc[k]);
+                }
+            }
+            for (; jj < nj; ++jj) {
+                float x[8];
+                const int64_t row = dlen[jj] > 0 ? dbase[jj] + am[jj][grp] : 0;
+                loadn<E>(a.D, row * DW + ls.e0, ls.n, ls.vec, x);
+                const float w = wq[jj][grp];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
             }
         }
-        for (; jj < nj; ++jj) {
-            float x[8];
-            const int64_t row = dlen[jj] > 0 ? dbase[jj] + am[jj][grp] : 0;
-            load8<E>(a.D, row * kD + 8 * l16, x);
-            const float w = wq[jj][grp];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
-        }
+        if (row_ok && ls.n > 0) storen(a.dQ + p * DW + ls.e0, ls.n, ls.vec, acc);
     }
-    if (row_ok) store8(a.dQ + p * kD + 8 * l16, acc);
 }
 
 // Eq. (3) per packed doc row r: the sources of CSR row r, in order, each
 // g[i,j] Q[cu_q[i] + s]. Workgroup = a block of rows; group g owns rows
 // r_begin + g + 64 k.
-template <int E>
+template <int E, bool GEN>
 __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXSIM_DD_WAVES))) void vbwd_dd_kernel(
     VarBwdArgs a, int rows_per_block)
 {
     constexpr int kDdGroups = kDdThreads / 16;
+    const int64_t DW = GEN ? (int64_t)a.d : kD;
+    const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
     const int64_t Nd = a.Nd, Nq = a.Nq, Tq = a.Tq;
     const int64_t r_begin = (int64_t)blockIdx.x * rows_per_block;
     const int64_t r_end = r_begin + rows_per_block < a.Td ? r_begin + rows_per_block : a.Td;
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
     const int gbase = tid & 63 & ~15;
     const uint32_t mlq = (uint32_t)a.max_lq, ndm = (uint32_t)(Nd * a.max_lq);
-    for (int64_t r = r_begin + grp; r < r_end; r += kDdGroups) {
+    for (int64_t r = r_begin + grp; r < r_end; r += kDdGroups)
+    for (int c = 0; c < nchunk; ++c) {
+        const LaneSpan ls(c, l16, DW, GEN);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         // a valid row lists at most Tq sources inside col_idx; the bounds
         // also hold for any row_ptr content
@@ -764,7 +830,7 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                 for (int u = 0; u < kDdUnroll; ++u) {
                     const int64_t qr = __shfl(qrow, gbase + k + u, 64);
                     ww[u] = __shfl(w, gbase + k + u, 64);
-                    load8<E>(a.Q, qr * kD + 8 * l16, xv[u]);
+                    loadn<E>(a.Q, qr * DW + ls.e0, ls.n, ls.vec, xv[u]);
                 }
 #pragma unroll
                 for (int u = 0; u < kDdUnroll; ++u)
@@ -775,16 +841,16 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                 const int64_t qr = __shfl(qrow, gbase + k, 64);
                 const float wk = __shfl(w, gbase + k, 64);
                 float xv[8];
-                load8<E>(a.Q, qr * kD + 8 * l16, xv);
+                loadn<E>(a.Q, qr * DW + ls.e0, ls.n, ls.vec, xv);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wk, xv[q], acc[q]);
             }
         }
-        store8(a.dD + r * kD + 8 * l16, acc);
+        if (ls.n > 0) storen(a.dD + r * DW + ls.e0, ls.n, ls.vec, acc);
     }
 }
 
-template <int E>
+template <int E, bool GEN>
 static hipError_t launch_bwd_varlen_t(VarBwdArgs a, hipStream_t stream)
 {
     hipError_t err;
@@ -798,7 +864,7 @@ static hipError_t launch_bwd_varlen_t(VarBwdArgs a, hipStream_t stream)
     }
     if (a.Tq > 0) {
         const int64_t blocks = (a.Tq + kGroups - 1) / kGroups;
-        hipLaunchKernelGGL(vbwd_dq_kernel<E>, dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
+        hipLaunchKernelGGL((vbwd_dq_kernel<E, GEN>), dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (a.Td > 0) {
@@ -807,7 +873,7 @@ static hipError_t launch_bwd_varlen_t(VarBwdArgs a, hipStream_t stream)
         rpb = (rpb + 63) / 64 * 64;
         if (rpb > 4096) rpb = 4096;
         const int64_t blocks = (a.Td + rpb - 1) / rpb;
-        hipLaunchKernelGGL(vbwd_dd_kernel<E>, dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a, (int)rpb);
+        hipLaunchKernelGGL((vbwd_dd_kernel<E, GEN>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a, (int)rpb);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
@@ -815,9 +881,10 @@ static hipError_t launch_bwd_varlen_t(VarBwdArgs a, hipStream_t stream)
 
 hipError_t launch_bwd_varlen(int elem, VarBwdArgs a, hipStream_t stream)
 {
+    const bool gen = a.d != kD;
     switch (elem) {
-    case kF16: return launch_bwd_varlen_t<kF16>(a, stream);
-    case kBF16: return launch_bwd_varlen_t<kBF16>(a, stream);
+    case kF16: return gen ? launch_bwd_varlen_t<kF16, true>(a, stream) : launch_bwd_varlen_t<kF16, false>(a, stream);
+    case kBF16: return gen ? launch_bwd_varlen_t<kBF16, true>(a, stream) : launch_bwd_varlen_t<kBF16, false>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -81,6 +81,7 @@ struct BwdArgs {
     int32_t* row_ptr;
     int32_t* col_idx;
     int64_t Nq, Nd, Lq, Ld;
+    int32_t d;  // embedding width (rows of d elements)
 };
 
 struct VarBwdArgs {
@@ -97,6 +98,7 @@ struct VarBwdArgs {
     int64_t Nq, Nd, Tq, Td;
     int64_t nnz_cap;  // entries of col_idx (Tq * Nd)
     int32_t max_lq;
+    int32_t d;  // embedding width (rows of d elements)
 };
 
 struct ChamferArgs {

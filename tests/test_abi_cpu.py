@@ -122,7 +122,8 @@ def test_bwd_validation(L):
         return f(dtype, Q, D, Nq, Nd, Lq, Ld, d, None, None, am, g, dQ, dD, rp, ci, None)
 
     assert call(Nq=-2) == ERR_SHAPE
-    assert call(d=100) == ERR_UNSUPPORTED
+    assert call(d=0) == ERR_UNSUPPORTED
+    assert call(d=1025) == ERR_UNSUPPORTED
     assert call(Ld=0) == ERR_SHAPE            # sources with no destination
     assert call(am=None) == ERR_NULL
     assert call(rp=None) == ERR_NULL
@@ -206,7 +207,8 @@ def test_bwd_varlen_validation(L):
     assert f(Nq=0) == ERR_SHAPE                 # packed query rows without a query
     assert f(Nd=0) == ERR_SHAPE                 # packed doc rows without a doc
     assert f(mlq=0) == ERR_SHAPE                # query rows need a max_lq slot
-    assert f(d=256) == ERR_UNSUPPORTED
+    assert f(d=0) == ERR_UNSUPPORTED
+    assert f(d=4096) == ERR_UNSUPPORTED
     assert f(dtype=2) == ERR_UNSUPPORTED
     assert f(cq=None) == ERR_NULL
     assert f(rp=None) == ERR_NULL

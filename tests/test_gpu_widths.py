@@ -1,13 +1,14 @@
-"""GPU parity of the forwards at embedding widths other than 128.
+"""GPU parity of the forwards and backwards at embedding widths other than 128.
 
-Every fp16/bf16 forward entry point accepts 1 <= d <= 1024; widths other than
-128 run the general-width kernel (TileMaxSim Sec. 3 dimension tiling, Sec. 6
+Every fp16/bf16 entry point accepts 1 <= d <= 1024; forwards at widths other
+than 128 run the general-width kernel (TileMaxSim Sec. 3 dimension tiling, Sec. 6
 Table 9 width sweep). The cases cover one-chunk widths whose query stays in
 registers (d <= 128), several chunks with a query staged in LDS (d > 128), a
 partial last chunk and K-step, rows whose byte length is not a multiple of 16
 (gathered element by element), masks, dead docs, empty sequences, multi-pass
-queries and pair lists. Expected values come only from the oracle; tolerances
-and the argmax rule are those of oracle/compare.py.
+queries and pair lists; the backwards gather rows in 128-wide chunks with a
+partial or unaligned tail. Expected values come only from the oracle;
+tolerances and the argmax rule are those of oracle/compare.py.
 """
 
 import numpy as np
@@ -192,3 +193,77 @@ def test_dim_sweep_full_size_sampled(ms, oracle_mod, d):
                                      rng.choice(10000, 200, replace=False)]))
     rs, _ = oracle_mod.fwd(w.Q, w.D[docs], want_argmax=False)
     _assert_close("scores", s.cpu().numpy()[:, docs], rs)
+
+
+BWD_CASES = [
+    # (Nq, Nd, Lq, Ld, dtype, d, mask_p, hub)
+    (3, 4, 9, 14, torch.float16, 64, 0.3, 0.0),
+    (5, 6, 70, 130, torch.bfloat16, 100, 0.2, 0.0),    # 200-byte rows: element gathers
+    (4, 3, 64, 64, torch.bfloat16, 300, 0.0, 0.7),     # three chunks, hub token
+    (2, 3, 33, 50, torch.float16, 768, 0.1, 0.0),
+    (2, 2, 5, 9, torch.float16, 1021, 0.0, 0.0),
+    (2, 2, 4, 6, torch.bfloat16, 3, 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES,
+                         ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}_{str(c[4])[6:]}_d{c[5]}")
+def test_bwd_widths(ms, oracle_mod, case):
+    Nq, Nd, Lq, Ld, dt, d, p, hub = case
+    _say(f"bwd width {case}")
+    w = synth.random_dense(1600 + d + Lq, Nq, Nd, Lq, Ld, dtype=dt, q_mask_p=p, d_mask_p=p,
+                           dead_docs=1 if p > 0 else 0, d=d)
+    if hub > 0:
+        argmax = synth.draw_argmax(1600 + d, Nq, Nd, Lq, Ld, None, hub_frac=hub)
+    else:
+        _, ra = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+        argmax = torch.from_numpy(ra)
+    g = synth.upstream_grad(1600 + d, Nq, Nd)
+
+    def run():
+        out = ms.maxsim_bwd(_g(w.Q), _g(w.D), _g(argmax), _g(g), _g(w.q_mask), _g(w.d_mask))
+        torch.cuda.synchronize()
+        return [t.cpu() for t in out]
+
+    dQ, dD, rp, ci = run()
+    rdQ, rdD, rrp, rci = oracle_mod.bwd(w.Q, w.D, argmax, g, w.q_mask, w.d_mask)
+    assert np.array_equal(rp.numpy(), rrp), "row_ptr"
+    assert np.array_equal(ci.numpy(), rci), "col_idx"
+    _assert_close("dQ", dQ.numpy(), rdQ)
+    _assert_close("dD", dD.numpy(), rdD)
+    again = run()
+    assert all(torch.equal(x, y) for x, y in zip(again, (dQ, dD, rp, ci))), "not deterministic"
+
+
+VARBWD_CASES = [
+    # (query lengths, doc lengths, dtype, d)
+    ([5, 12, 3], [7, 0, 19, 3, 1], torch.float16, 64),
+    ([32] * 4, list(range(50, 300, 13)), torch.bfloat16, 100),
+    ([0, 3, 40], [4, 0, 60], torch.bfloat16, 384),
+    ([7], [9, 2], torch.float16, 1000),
+]
+
+
+@pytest.mark.parametrize("case", VARBWD_CASES, ids=lambda c: f"q{len(c[0])}_d{len(c[1])}_w{c[3]}")
+def test_bwd_varlen_widths(ms, oracle_mod, case):
+    ql, dl, dt, d = case
+    _say(f"bwd varlen width {ql[:4]} {dl[:6]} d={d}")
+    seed = 1700 + d + len(dl)
+    w = synth.random_varlen(seed, ql, dl, dtype=dt, max_lq=max(max(ql), 1), d=d)
+    _, ra = oracle_mod.fwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d)
+    argmax = torch.from_numpy(ra)
+    g = synth.upstream_grad(seed, len(ql), len(dl))
+
+    def run():
+        out = ms.maxsim_bwd_varlen(_g(w.Q), _g(w.cu_q), w.max_lq, _g(w.D), _g(w.cu_d), _g(argmax), _g(g))
+        torch.cuda.synchronize()
+        return tuple(x.cpu() for x in out)
+
+    dQ, dD, rp, ci = run()
+    rdQ, rdD, rrp, rci = oracle_mod.bwd_varlen(w.Q, w.cu_q, w.max_lq, w.D, w.cu_d, argmax, g)
+    assert np.array_equal(rp.numpy(), rrp), "row_ptr"
+    assert np.array_equal(ci.numpy()[:len(rci)], rci), "col_idx"
+    _assert_close("dQ", dQ.numpy(), rdQ)
+    _assert_close("dD", dD.numpy(), rdD)
+    again = run()
+    assert all(torch.equal(x, y) for x, y in zip(again[:3], (dQ, dD, rp))), "not deterministic"

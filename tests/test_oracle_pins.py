@@ -632,6 +632,27 @@ def test_width_chunks_sum_to_full_dot(oracle_mod):
     assert np.abs(wrong - s).max() > 1e-3
 
 
+@pytest.mark.parametrize("d", [7, 300])
+def test_backward_euler_identity_widths(oracle_mod, d):
+    """The bilinear Euler identity of the backward (sum g*score = <dQ, Q> =
+    <dD, D> at a fixed argmax) at widths other than 128, padded and packed."""
+    w = synth.random_dense(52 + d, 3, 4, 10, 25, dtype=torch.bfloat16, q_mask_p=0.3, d_mask_p=0.2,
+                           dead_docs=1, d=d)
+    g = synth.upstream_grad(52 + d, 3, 4).double().numpy()
+    s, a = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    dQ, dD, _, _ = oracle_mod.bwd(w.Q, w.D, a, g, w.q_mask, w.d_mask)
+    lhs = float((g * s).sum())
+    np.testing.assert_allclose(float((dQ * w.Q.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(float((dD * w.D.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+    v = synth.random_varlen(53 + d, [4, 0, 9], [6, 0, 11, 2], d=d)
+    g = synth.upstream_grad(53 + d, 3, 4).double().numpy()
+    s, a = oracle_mod.fwd_varlen(v.Q, v.cu_q, v.max_lq, v.D, v.cu_d)
+    dQ, dD, _, _ = oracle_mod.bwd_varlen(v.Q, v.cu_q, v.max_lq, v.D, v.cu_d, a, g)
+    lhs = float((g * s).sum())
+    np.testing.assert_allclose(float((dQ * v.Q.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(float((dD * v.D.double().numpy()).sum()), lhs, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------ Chamfer distance
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (2, 5, 7), (3, 40, 13), (1, 64, 64)])
