@@ -32,9 +32,9 @@ maxsim_status_t launch_status(hipError_t e) { return e == hipSuccess ? MAXSIM_OK
 
 bool dtype_ok(maxsim_dtype_t t) { return t == MAXSIM_F16 || t == MAXSIM_BF16; }
 
-// Embedding widths of the fp16/bf16 entry points: 128 has its own forward
-// kernels, every other width up to kMaxDim takes the general-width forward;
-// the backward gathers handle any width in 128-wide chunks.
+// Embedding widths of the entry points: 128 has its own forward kernels,
+// every other width up to kMaxDim takes the general-width forward; the
+// backward gathers handle any width in 128-wide chunks.
 constexpr int64_t kMaxDim = 1024;
 bool width_ok(int64_t d) { return d >= 1 && d <= kMaxDim; }
 
@@ -159,7 +159,7 @@ maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, f
                               float* scores, int32_t* argmax, maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
-    if (d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     if (Nq == 0 || Nd == 0) return MAXSIM_OK;
     if (!scores_i32 && !scores) return MAXSIM_ERR_NULL;
     if ((Lq > 0 && !Q) || (Ld > 0 && !D)) return MAXSIM_ERR_NULL;
@@ -174,6 +174,26 @@ maxsim_status_t maxsim_fwd_i8(const int8_t* Q, float q_scale, const int8_t* D, f
     if (argmax) {
         const int64_t n = mul_sat(pairs, Lq);
         if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    if (d != kD) {
+        const int64_t rows = mul_sat(Nd, Ld);
+        if (rows < 0 || rows > kI32Max || Lq > kI32Max) return MAXSIM_ERR_OVERFLOW;
+        DimArgs g{};
+        g.Q = Q;
+        g.D = D;
+        g.q_mask = q_mask;
+        g.d_mask = d_mask;
+        g.scores = scores;
+        g.scores_i32 = scores_i32;
+        g.argmax = argmax;
+        g.q_scale = (double)q_scale;
+        g.d_scale = (double)d_scale;
+        g.Nq = Nq;
+        g.Nd = Nd;
+        g.Lq = Lq;
+        g.Ld = Ld;
+        g.d = (int32_t)d;
+        return launch_status(launch_fwd_dim(kI8, g, (hipStream_t)stream));
     }
     DenseArgs a{};
     a.Q = Q;
@@ -199,7 +219,7 @@ maxsim_status_t maxsim_fwd_i8_tok(const int8_t* Q, const float* q_scale, const i
                                   maxsim_stream_t stream)
 {
     if (Nq < 0 || Nd < 0 || Lq < 0 || Ld < 0 || d < 0) return MAXSIM_ERR_SHAPE;
-    if (d != kD) return MAXSIM_ERR_UNSUPPORTED;
+    if (!width_ok(d)) return MAXSIM_ERR_UNSUPPORTED;
     if (Nq == 0 || Nd == 0) return MAXSIM_OK;
     if (!scores) return MAXSIM_ERR_NULL;
     if ((Lq > 0 && (!Q || !q_scale)) || (Ld > 0 && (!D || !d_scale))) return MAXSIM_ERR_NULL;
@@ -211,6 +231,25 @@ maxsim_status_t maxsim_fwd_i8_tok(const int8_t* Q, const float* q_scale, const i
     if (argmax) {
         const int64_t n = mul_sat(pairs, Lq);
         if (n < 0 || n > kI32Max) return MAXSIM_ERR_OVERFLOW;
+    }
+    if (d != kD) {
+        const int64_t rows = mul_sat(Nd, Ld);
+        if (rows < 0 || rows > kI32Max || Lq > kI32Max) return MAXSIM_ERR_OVERFLOW;
+        DimArgs g{};
+        g.Q = Q;
+        g.D = D;
+        g.q_mask = q_mask;
+        g.d_mask = d_mask;
+        g.scores = scores;
+        g.argmax = argmax;
+        g.q_scale_tok = q_scale;
+        g.d_scale_tok = d_scale;
+        g.Nq = Nq;
+        g.Nd = Nd;
+        g.Lq = Lq;
+        g.Ld = Ld;
+        g.d = (int32_t)d;
+        return launch_status(launch_fwd_dim(kI8, g, (hipStream_t)stream));
     }
     DenseArgs a{};
     a.Q = Q;

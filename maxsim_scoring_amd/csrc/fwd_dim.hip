@@ -1,7 +1,7 @@
-// MaxSim forward at any embedding width for gfx950: fp16/bf16 rows of d
-// elements (1 <= d <= 1024, any d other than 128, which has its own kernels),
-// uniform or cu_seqlens-packed, cross product or pair list, with masks and
-// optional argmax.
+// MaxSim forward at any embedding width for gfx950: fp16/bf16 or int8 rows
+// of d elements (1 <= d <= 1024, any d other than 128, which has its own
+// kernels), uniform or cu_seqlens-packed, cross product or pair list, with
+// masks and optional argmax; int8 with per-tensor or per-token scales.
 //
 // TileMaxSim Sec. 3 (dimension tiling: a row wider than 128 is cut into
 // 128-wide chunks whose partial dot products are summed before the max) and
@@ -9,17 +9,19 @@
 // TileMaxSim README notes on the embedding-dimension dispatch (a width up to
 // 128 is padded and the surplus lanes read as zero, which leaves every score
 // unchanged); "Flash-MaxSim" Sec. 4.1 and 4.1.1 (online max, -inf masking,
-// strict '>' argmax update) and Sec. 4.3.2 (cu_seqlens scoring over sum(L_d)
-// rows).
+// strict '>' argmax update), Sec. 4.3.1 (INT8 x INT8 with the scales fused
+// into the epilogue; per-token doc scales inside the max) and Sec. 4.3.2
+// (cu_seqlens scoring over sum(L_d) rows).
 //
 // Design. The streaming scheme of the 128-wide padding-free kernel,
-// generalised in the width. A row is cut into 256-byte chunks (128 elements,
-// the last chunk partial), so a 16-row tile of the doc stream becomes C chunk
-// tiles of 4 KB. Each wave is a persistent unit that owns a contiguous,
+// generalised in the width. A row is cut into 256-byte chunks (128 fp16/bf16
+// or 256 int8 elements, the last chunk partial), so a 16-row tile of the doc
+// stream becomes C chunk tiles of 4 KB. Each wave is a persistent unit that owns a contiguous,
 // token-balanced range of whole docs and pulls its chunk tiles through a
 // private LDS ring with direct-to-LDS loads (16 bytes per lane, the pieces
 // XOR-swizzled by row so that the MFMA operand reads are conflict free). The
-// 16x16x32 MFMA consumes a chunk tile in up to four 64-byte K-steps and
+// 16x16x32 fp16/bf16 MFMA (16x16x64 for int8, exact int32 sums) consumes a
+// chunk tile in up to four 64-byte K-steps and
 // accumulates the S tile over the C chunks; only after the last chunk is the
 // tile folded into the running max, so the dot products are those of the
 // whole row. Past the row end the query side holds zeros (K-steps wholly
@@ -31,14 +33,19 @@
 // four waves of a workgroup (all of which then run the same passes and
 // barriers), and read per chunk tile; with a pair list, where each wave has its
 // own query, a workgroup is a single wave. Rows whose byte length is not a
-// multiple of 16 cannot take 16-byte loads: their pieces are gathered from
-// 2-byte elements and written to LDS in the same layout (a slower path).
+// multiple of 16 cannot take 16-byte loads: their pieces are gathered element
+// by element and written to LDS in the same layout (a slower path). With
+// per-token int8 scales, every chunk tile also brings its 16 doc-token scales
+// into the ring by a 4-byte direct-to-LDS load; they turn the tile's integer
+// dot products into floats before the max, and the query-token scale
+// (positive) multiplies the max.
 //
 // Queries are the fastest grid axis, so the workgroups that are resident
 // together share doc ranges and the repeated reads of a range for different
 // queries are served from cache. Scores of a long query are the sum of its
 // 32-token passes, added in pass order.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -57,18 +64,42 @@ constexpr int kCTileBytes = 16 * kChunkBytes;  // chunk tile: 16 rows x 256 byte
 constexpr int kStages = MAXSIM_DIM_STAGES;  // chunk tiles in flight per wave (2..4)
 static_assert(kStages >= 2 && kStages <= 4, "vmcnt waits cover up to three later tiles");
 
-// vmcnt(4 n): the n most recently issued chunk tiles may still be in flight
+// vmcnt(LPI n): the n most recently issued chunk tiles (LPI loads each) may
+// still be in flight
+template <int LPI>
 __device__ __forceinline__ void wait_ctiles_behind(int n)
 {
     if (n <= 0) wait_vmcnt<0>();
-    else if (n == 1) wait_vmcnt<4>();
-    else if (n == 2) wait_vmcnt<8>();
-    else wait_vmcnt<12>();
+    else if (n == 1) wait_vmcnt<LPI>();
+    else if (n == 2) wait_vmcnt<2 * LPI>();
+    else wait_vmcnt<3 * LPI>();
+}
+
+// Element traits: a K-step is 64 bytes of a row for every type.
+template <int E> struct DimT;
+template <> struct DimT<kF16> {
+    static constexpr int kES = 2;
+    typedef f32x4 Acc;
+};
+template <> struct DimT<kBF16> {
+    static constexpr int kES = 2;
+    typedef f32x4 Acc;
+};
+template <> struct DimT<kI8> {
+    static constexpr int kES = 1;
+    typedef i32x4 Acc;
+};
+template <int E>
+__device__ __forceinline__ typename DimT<E>::Acc mma(const i32x4& a, const i32x4& b, const typename DimT<E>::Acc& c)
+{
+    if constexpr (E == kI8) return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+    else return mfma16<E>(a, b, c);
 }
 
 // 16 bytes of a row starting at byte `off`; bytes at or past `rb` (the row's
 // length in bytes) read as zero. With 16-byte aligned rows (`al`) a piece is
-// either whole or past the end; otherwise it is gathered from 2-byte elements.
+// either whole or past the end; otherwise it is gathered from ES-byte elements.
+template <int ES>
 __device__ __forceinline__ i32x4 load_piece(const unsigned char* row, int off, int rb, bool al)
 {
     if (al) {
@@ -78,11 +109,17 @@ __device__ __forceinline__ i32x4 load_piece(const unsigned char* row, int off, i
     }
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int b = 0; b < 16; b += 2)
-        if (off + b < rb) w[b >> 2] |= (uint32_t)(*(const uint16_t*)(row + off + b)) << (8 * (b & 3));
+    for (int b = 0; b < 16; b += ES) {
+        if (off + b < rb) {
+            const uint32_t e = ES == 2 ? (uint32_t)(*(const uint16_t*)(row + off + b)) : (uint32_t)row[off + b];
+            w[b >> 2] |= e << (8 * (b & 3));
+        }
+    }
     return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
 }
 
+// LDS store into the direct-to-LDS ring, in assembly so that the compiler adds
+// no wait for the ring's loads in flight
 __device__ __forceinline__ void lds_write_b128(uint32_t addr, const i32x4& v)
 {
     asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
@@ -116,10 +153,15 @@ __device__ __forceinline__ uint32_t mask_bits16(const uint8_t* p, int nb)
 
 }  // namespace
 
-template <int E, bool ARGMAX, bool QREG, int W>
+template <int E, bool ARGMAX, bool QREG, int W, bool TOK>
 __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 {
-    static_assert(E == kF16 || E == kBF16, "16-bit elements");
+    static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
+    using Acc = typename DimT<E>::Acc;
+    using V = std::conditional_t<E == kI8 && !TOK, int, float>;  // value of the max
+    constexpr int ES = DimT<E>::kES;
+    constexpr int LPI = TOK ? 5 : 4;  // loads per chunk tile: 4 row loads (+ the doc-token scales)
+    constexpr int kStageBytes = kCTileBytes + (TOK ? 256 : 0);
     extern __shared__ __attribute__((aligned(16))) unsigned char dim_lds[];
     const int lane = lane_id();
     const int col = lane & 15;  // query token of an N-tile / doc row of a tile
@@ -131,8 +173,8 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
     const int kt_last = (RB - (C - 1) * kChunkBytes + 63) >> 6;  // K-steps of the last chunk
     unsigned char* qbuf = dim_lds;  // staged query block: [kNT][C] chunk tiles
     const uint32_t q_base = lds_addr(qbuf);
-    const uint32_t ring_base =
-        (uint32_t)uniform((int)lds_addr(dim_lds + (QREG ? 0 : kNT * C * kCTileBytes) + wave * kStages * kCTileBytes));
+    unsigned char* ring = dim_lds + (QREG ? 0 : kNT * C * kCTileBytes) + wave * kStages * kStageBytes;
+    const uint32_t ring_base = (uint32_t)uniform((int)lds_addr(ring));
 
     // ---- the docs of this wave's unit -------------------------------------
     const bool pairs = a.pair_q != nullptr;
@@ -180,24 +222,27 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
         const int lq = uniform((int)lq64);
         const int npass = lq == 0 ? 1 : (lq + kPassTokens - 1) / kPassTokens;
         const int j_out = pairs ? jb : 0;  // outputs of doc j are at [j - j_out]
-        float* score_row = a.scores + (pairs ? unit : i * a.Nd);
-        int32_t* arg_row = ARGMAX ? a.argmax + (pairs ? unit : i * a.Nd) * a.Lq : nullptr;
+        const int64_t out_row = pairs ? unit : i * a.Nd;
+        int32_t* arg_row = ARGMAX ? a.argmax + out_row * a.Lq : nullptr;
 
         for (int pass = 0; pass < npass; ++pass) {
             // ---- query block: tokens pass*32 + n*16 + col ----------------------
             bool tok_in[kNT], tok_ok[kNT];
+            float qsc[kNT];  // query-token scales (TOK)
             i32x4 qf[kNT][4];
 #pragma unroll
             for (int n = 0; n < kNT; ++n) {
                 const int s = pass * kPassTokens + n * 16 + col;
                 tok_in[n] = s < lq;
                 tok_ok[n] = tok_in[n] && (a.q_mask == nullptr || a.q_mask[i * a.Lq + s] != 0);
+                qsc[n] = 0.f;
+                if constexpr (TOK) qsc[n] = tok_in[n] ? a.q_scale_tok[q0 + s] : 0.f;
                 if constexpr (QREG) {
                     const unsigned char* qrow = (const unsigned char*)a.Q + (q0 + (tok_in[n] ? s : 0)) * RB;
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         i32x4 v = {0, 0, 0, 0};
-                        if (tok_in[n]) v = load_piece(qrow, (4 * k + g) << 4, RB, al);
+                        if (tok_in[n]) v = load_piece<ES>(qrow, (4 * k + g) << 4, RB, al);
                         qf[n][k] = v;
                     }
                 }
@@ -209,7 +254,8 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                     const int n = nc / C, c = nc - n * C;
                     const int s = pass * kPassTokens + n * 16 + row;
                     i32x4 v = {0, 0, 0, 0};
-                    if (s < lq) v = load_piece((const unsigned char*)a.Q + (q0 + s) * RB, c * kChunkBytes + (lp << 4), RB, al);
+                    if (s < lq)
+                        v = load_piece<ES>((const unsigned char*)a.Q + (q0 + s) * RB, c * kChunkBytes + (lp << 4), RB, al);
                     *(i32x4*)(qbuf + nc * kCTileBytes + row * kChunkBytes + ((lp ^ row) << 4)) = v;
                 }
                 block_barrier();
@@ -221,7 +267,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
             int cache_base = jb + 1;  // lane k holds cu_d[cache_base + k] - u0 (packed docs)
             int cu_cache = 0;
             if (a.cu_d) cu_cache = (int)((int64_t)a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd] - u0);
-            wait_vmcnt<0>();  // query fragments, masks and the cache have landed
+            wait_vmcnt<0>();  // query fragments, scales, masks and the cache have landed
             auto doc_end_of = [&](int jj) -> int {  // offset of the end of doc jj in the unit
                 if (!a.cu_d) return uniform((int)((int64_t)(jj + 1) * a.Ld - u0));
                 int off = jj + 1 - cache_base;
@@ -236,83 +282,90 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
             int doc_start = 0;
             int doc_end = doc_end_of(j);
 
-            float m[kNT];
+            V m[kNT];
             int idx[kNT];
 #pragma unroll
             for (int n = 0; n < kNT; ++n) {
-                m[n] = -__builtin_inff();
+                m[n] = neg_inf<V>();
                 idx[n] = 0;
             }
 
             // finish doc j: merge the 4 row groups, sum the valid query rows, write
             auto finish_doc = [&]() {
-                float total = 0.f;
+                V total = 0;
 #pragma unroll
                 for (int n = 0; n < kNT; ++n) {
-                    float mv = m[n];
+                    V mv = m[n];
                     int iv = idx[n];
 #pragma unroll
                     for (int off = 16; off <= 32; off <<= 1) {
-                        const float om = shfl_xor_f(mv, off);
+                        const V om = __builtin_bit_cast(V, shfl_xor_i(__builtin_bit_cast(int, mv), off));
                         if constexpr (ARGMAX) {
                             const int oi = shfl_xor_i(iv, off);
                             argmax_merge(mv, iv, om, oi);
                         } else {
-                            mv = __builtin_fmaxf(mv, om);
+                            mv = om > mv ? om : mv;
                         }
                     }
-                    const bool fin = __builtin_isfinite(mv);
-                    total += row16_sum((tok_ok[n] && fin) ? mv : 0.f);
+                    const bool fin = finite_score(mv);
+                    if constexpr (TOK) mv = fin ? qsc[n] * mv : mv;  // positive: keeps the max
+                    total += row16_sum((tok_ok[n] && fin) ? mv : (V)0);
                     if constexpr (ARGMAX) {
                         if (g == 0 && tok_in[n]) {
                             const int s = pass * kPassTokens + n * 16 + col;
                             arg_row[(int64_t)(j - j_out) * a.Lq + s] = fin ? iv - doc_start : 0;
                         }
                     }
-                    m[n] = -__builtin_inff();
+                    m[n] = neg_inf<V>();
                     idx[n] = 0;
                 }
                 if constexpr (ARGMAX) {
                     if (pass == 0)  // rows past the query's length are 0
                         for (int s = lq + lane; s < a.Lq; s += 64) arg_row[(int64_t)(j - j_out) * a.Lq + s] = 0;
                 }
-                if (lane == 0) score_row[j - j_out] = pass == 0 ? total : score_row[j - j_out] + total;
+                if (lane == 0) {
+                    const int64_t o = out_row + (j - j_out);
+                    if constexpr (std::is_integral_v<V>) {
+                        // the int32 running sum lives in scores_i32 when it exists,
+                        // else in the bits of scores until the last pass
+                        int32_t* run = a.scores_i32 ? a.scores_i32 : (int32_t*)a.scores;
+                        const int32_t tot = pass == 0 ? total : run[o] + total;
+                        if (a.scores_i32) a.scores_i32[o] = tot;
+                        if (pass + 1 == npass && a.scores) a.scores[o] = (float)(((double)tot * a.q_scale) * a.d_scale);
+                        else if (!a.scores_i32) run[o] = tot;
+                    } else {
+                        a.scores[o] = pass == 0 ? total : a.scores[o] + total;
+                    }
+                }
             };
 
             // fold tile rows [lo, hi) that are valid in `vb` into the running state
-            auto fold = [&](const f32x4 (&acc)[kNT], int tile0, int lo, int hi, uint32_t vb) {
+            // (TOK: the integer dot products scaled by the rows' doc-token scales)
+            auto fold = [&](const Acc (&acc)[kNT], const float (&sc)[4], int tile0, int lo, int hi, uint32_t vb) {
                 const uint32_t bits = ((1u << hi) - 1u) & ~((1u << lo) - 1u) & vb;
-                if (bits == 0xFFFFu) {
+                const uint32_t lb = bits >> (4 * g);
+                const bool full = bits == 0xFFFFu;
 #pragma unroll
-                    for (int n = 0; n < kNT; ++n) {
-                        if constexpr (ARGMAX) {
+                for (int n = 0; n < kNT; ++n) {
+                    V v[4];
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (acc[n][r] > m[n]) {
-                                    m[n] = acc[n][r];
-                                    idx[n] = tile0 + 4 * g + r;
-                                }
-                        } else {
-                            m[n] = __builtin_fmaxf(__builtin_fmaxf(m[n], acc[n][0]),
-                                                   __builtin_fmaxf(__builtin_fmaxf(acc[n][1], acc[n][2]), acc[n][3]));
-                        }
+                    for (int r = 0; r < 4; ++r) {
+                        if constexpr (TOK) v[r] = (float)acc[n][r] * sc[r];
+                        else v[r] = acc[n][r];
+                        if (!full) v[r] = ((lb >> r) & 1u) ? v[r] : neg_inf<V>();
                     }
-                } else {
-                    const uint32_t lb = bits >> (4 * g);
+                    if constexpr (ARGMAX) {
 #pragma unroll
-                    for (int n = 0; n < kNT; ++n) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float v = ((lb >> r) & 1u) ? acc[n][r] : -__builtin_inff();
-                            if constexpr (ARGMAX) {
-                                if (v > m[n]) {
-                                    m[n] = v;
-                                    idx[n] = tile0 + 4 * g + r;
-                                }
-                            } else {
-                                m[n] = __builtin_fmaxf(m[n], v);
+                        for (int r = 0; r < 4; ++r)
+                            if (v[r] > m[n]) {
+                                m[n] = v[r];
+                                idx[n] = tile0 + 4 * g + r;
                             }
-                        }
+                    } else {
+                        const V a01 = v[0] > v[1] ? v[0] : v[1];
+                        const V a23 = v[2] > v[3] ? v[2] : v[3];
+                        const V a03 = a01 > a23 ? a01 : a23;
+                        m[n] = a03 > m[n] ? a03 : m[n];
                     }
                 }
             };
@@ -332,7 +385,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
             auto issue = [&]() {
                 const unsigned char* tp = (const unsigned char*)uniform_ptr(unit_ptr + (int64_t)t_next * 16 * RB);
                 const int rows_left = span - t_next * 16;  // rows past the unit re-read its last row
-                const uint32_t dst = (uint32_t)uniform((int)(ring_base + s_next * kCTileBytes));
+                const uint32_t dst = (uint32_t)uniform((int)(ring_base + s_next * kStageBytes));
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int row = 4 * k + g;
@@ -342,8 +395,13 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                         if (off >= RB) off = c_next * kChunkBytes;  // past the row end: a piece of the same row
                         dma_lds16_nt(tp, (uint32_t)(r * RB + off), dst + k * 1024);
                     } else {
-                        lds_write_b128(dst + k * 1024 + lane * 16, load_piece(tp + r * RB, off, RB, false));
+                        lds_write_b128(dst + k * 1024 + lane * 16, load_piece<ES>(tp + r * RB, off, RB, false));
                     }
+                }
+                if constexpr (TOK) {  // lane l: the scale of tile row l % 16, at dst + 4 KB + 4 l
+                    const float* sp = (const float*)uniform_ptr(a.d_scale_tok + u0 + (int64_t)t_next * 16);
+                    const int r = col < rows_left ? col : rows_left - 1;
+                    dma_lds4(sp, (uint32_t)(r * 4), dst + kCTileBytes);
                 }
                 if (++c_next == C) {
                     c_next = 0;
@@ -360,17 +418,32 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                     const int nb = span - t * 16 < 16 ? span - t * 16 : 16;
                     vb = mask_bits16(a.d_mask + u0 + t * 16, nb);
                 }
-                f32x4 acc[kNT];
+                Acc acc[kNT];
 #pragma unroll
-                for (int n = 0; n < kNT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int n = 0; n < kNT; ++n) acc[n] = Acc{0, 0, 0, 0};
+                float sc[4] = {1.f, 1.f, 1.f, 1.f};  // doc-token scales of rows 4g .. 4g+3 (TOK)
                 for (int c = 0; c < C; ++c) {
                     const int q = t * C + c;
                     const int behind = nitem - 1 - q;
-                    wait_ctiles_behind(behind < kStages - 1 ? behind : kStages - 1);
-                    const uint32_t sbase = ring_base + stage * kCTileBytes;
+                    wait_ctiles_behind<LPI>(behind < kStages - 1 ? behind : kStages - 1);
+                    const uint32_t sbase = ring_base + stage * kStageBytes;
                     i32x4 af[4];
                     lds_read4(af[0], af[1], af[2], af[3], sbase + frag_off[0], sbase + frag_off[1],
                               sbase + frag_off[2], sbase + frag_off[3]);
+                    if constexpr (TOK) {
+                        if (c == C - 1) {  // before the stage is refilled
+                            // a plain LDS load (the ring's direct-to-LDS writes are
+                            // inline assembly, so the compiler adds no wait for
+                            // them): taking the four values out of an assembly
+                            // ds_read_b128 that is skipped on other paths gave
+                            // the first value for all four with this compiler
+                            const f32x4 sv = *(const f32x4*)(ring + stage * kStageBytes + kCTileBytes + 16 * g);
+                            sc[0] = sv.x;
+                            sc[1] = sv.y;
+                            sc[2] = sv.z;
+                            sc[3] = sv.w;
+                        }
+                    }
                     if constexpr (!QREG) {
                         i32x4 qv[8];
                         uint32_t qa[8];
@@ -391,7 +464,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                     for (int k = 0; k < 4; ++k) {
                         if (k < kt) {
 #pragma unroll
-                            for (int n = 0; n < kNT; ++n) acc[n] = mfma16<E>(af[k], qf[n][k], acc[n]);
+                            for (int n = 0; n < kNT; ++n) acc[n] = mma<E>(af[k], qf[n][k], acc[n]);
                         }
                     }
                 }
@@ -400,7 +473,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                 int lo = 0;
                 while (true) {
                     const int hi = doc_end - tile0 < 16 ? doc_end - tile0 : 16;
-                    if (hi > lo) fold(acc, tile0, lo, hi, vb);
+                    if (hi > lo) fold(acc, sc, tile0, lo, hi, vb);
                     if (doc_end - tile0 > 16) break;  // the doc continues in the next tile
                     finish_doc();
                     ++j;
@@ -426,11 +499,12 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 
 namespace {
 
-template <int E, bool ARGMAX, bool QREG, int W>
+template <int E, bool ARGMAX, bool QREG, int W, bool TOK>
 hipError_t launch_dim_t(DimArgs a, hipStream_t stream)
 {
-    auto kern = fwd_dim_kernel<E, ARGMAX, QREG, W>;
-    const size_t lds = (size_t)((QREG ? 0 : kNT * a.nchunk) + W * kStages) * kCTileBytes;
+    auto kern = fwd_dim_kernel<E, ARGMAX, QREG, W, TOK>;
+    constexpr int kStageBytes = kCTileBytes + (TOK ? 256 : 0);
+    const size_t lds = (size_t)(QREG ? 0 : kNT * a.nchunk) * kCTileBytes + (size_t)W * kStages * kStageBytes;
     if (a.pair_q) {
         a.units = 0;
         const int64_t blocks = (a.npairs + W - 1) / W;
@@ -457,15 +531,18 @@ hipError_t launch_dim_t(DimArgs a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int E>
+template <int E, bool TOK>
 hipError_t launch_dim_e(DimArgs a, hipStream_t stream)
 {
     const bool am = a.argmax != nullptr;
     if (a.nchunk == 1)
-        return am ? launch_dim_t<E, true, true, 4>(a, stream) : launch_dim_t<E, false, true, 4>(a, stream);
-    if (a.pair_q)
-        return am ? launch_dim_t<E, true, false, 1>(a, stream) : launch_dim_t<E, false, false, 1>(a, stream);
-    return am ? launch_dim_t<E, true, false, 4>(a, stream) : launch_dim_t<E, false, false, 4>(a, stream);
+        return am ? launch_dim_t<E, true, true, 4, TOK>(a, stream) : launch_dim_t<E, false, true, 4, TOK>(a, stream);
+    if constexpr (E != kI8) {  // pair lists (16-bit types only): one wave per workgroup
+        if (a.pair_q)
+            return am ? launch_dim_t<E, true, false, 1, TOK>(a, stream)
+                      : launch_dim_t<E, false, false, 1, TOK>(a, stream);
+    }
+    return am ? launch_dim_t<E, true, false, 4, TOK>(a, stream) : launch_dim_t<E, false, false, 4, TOK>(a, stream);
 }
 
 }  // namespace
@@ -473,11 +550,14 @@ hipError_t launch_dim_e(DimArgs a, hipStream_t stream)
 hipError_t launch_fwd_dim(int elem, DimArgs a, hipStream_t stream)
 {
     if (a.d < 1 || a.d > 1024) return hipErrorInvalidValue;
-    a.row_bytes = a.d * 2;
+    a.row_bytes = elem == kI8 ? a.d : a.d * 2;
     a.nchunk = (a.row_bytes + kChunkBytes - 1) / kChunkBytes;
     switch (elem) {
-    case kF16: return launch_dim_e<kF16>(a, stream);
-    case kBF16: return launch_dim_e<kBF16>(a, stream);
+    case kF16: return launch_dim_e<kF16, false>(a, stream);
+    case kBF16: return launch_dim_e<kBF16, false>(a, stream);
+    case kI8:
+        if (a.pair_q) return hipErrorInvalidValue;
+        return a.q_scale_tok ? launch_dim_e<kI8, true>(a, stream) : launch_dim_e<kI8, false>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

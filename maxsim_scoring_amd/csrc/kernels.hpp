@@ -57,8 +57,12 @@ struct DimArgs {
     const int32_t* pair_q;  // [npairs] pair list or null (score listed pairs only)
     const int32_t* pair_d;
     int64_t npairs;
-    float* scores;    // [Nq, Nd] ([npairs] with a pair list)
+    float* scores;    // [Nq, Nd] ([npairs] with a pair list); int8: or null
     int32_t* argmax;  // [Nq, Nd, Lq] ([npairs, Lq] with a pair list) or null
+    int32_t* scores_i32;        // int8 per-tensor: [Nq, Nd] exact sums or null
+    double q_scale, d_scale;    // int8 per-tensor scales
+    const float* q_scale_tok;   // int8 per-token scales: [rows of Q] or null
+    const float* d_scale_tok;   // [rows of D]
     int64_t Nq, Nd;
     int64_t Lq;  // uniform query length, or the max_lq bound of packed queries
     int64_t Ld;  // uniform doc length (unused with cu_d)

@@ -394,22 +394,22 @@ def random_varlen(seed: int, q_lengths, d_lengths, dtype: torch.dtype = torch.fl
 
 def random_int8(seed: int, Nq: int, Nd: int, Lq: int, Ld: int, ternary: bool = False,
                 extreme: bool = False, d_mask_p: float = 0.0, q_mask_p: float = 0.0,
-                want_argmax: bool = True) -> Int8:
+                want_argmax: bool = True, d: int = D_MODEL) -> Int8:
     """Quantised unit rows; ``ternary`` draws values in {-1,0,1} (many exact
     ties); ``extreme`` fills everything with +-127 (largest int32 sums)."""
     rng = np.random.default_rng([seed, _S_MISC])
     if ternary or extreme:
         if extreme:
-            Q = torch.full((Nq, Lq, D_MODEL), 127, dtype=torch.int8)
-            D = torch.from_numpy(np.where(rng.random((Nd, Ld, D_MODEL)) < 0.9, 127, -127)
+            Q = torch.full((Nq, Lq, d), 127, dtype=torch.int8)
+            D = torch.from_numpy(np.where(rng.random((Nd, Ld, d)) < 0.9, 127, -127)
                                  .astype(np.int8))
         else:
-            Q = torch.from_numpy(rng.integers(-1, 2, size=(Nq, Lq, D_MODEL)).astype(np.int8))
-            D = torch.from_numpy(rng.integers(-1, 2, size=(Nd, Ld, D_MODEL)).astype(np.int8))
+            Q = torch.from_numpy(rng.integers(-1, 2, size=(Nq, Lq, d)).astype(np.int8))
+            D = torch.from_numpy(rng.integers(-1, 2, size=(Nd, Ld, d)).astype(np.int8))
         qs, ds = 0.0078125, 0.015625
     else:
-        Qf = unit_rows(seed, _S_Q, Nq * Lq, dtype=torch.float32).view(Nq, Lq, D_MODEL)
-        Df = unit_rows(seed, _S_D, Nd * Ld, dtype=torch.float32).view(Nd, Ld, D_MODEL)
+        Qf = unit_rows(seed, _S_Q, Nq * Lq, d, dtype=torch.float32).view(Nq, Lq, d)
+        Df = unit_rows(seed, _S_D, Nd * Ld, d, dtype=torch.float32).view(Nd, Ld, d)
         Q, qs = quantise_per_tensor(Qf)
         D, ds = quantise_per_tensor(Df)
     qm = dm = None
@@ -438,12 +438,12 @@ def upstream_grad(seed: int, Nq: int, Nd: int) -> torch.Tensor:
 
 def random_int8_tok(seed: int, Nq: int, Nd: int, Lq: int, Ld: int, q_mask_p: float = 0.0,
                     d_mask_p: float = 0.0, dead_docs: int = 0, pow2_scales: bool = False,
-                    float_dtype: Optional[torch.dtype] = None) -> Int8Tok:
+                    float_dtype: Optional[torch.dtype] = None, d: int = D_MODEL) -> Int8Tok:
     """Per-token quantised unit rows. ``pow2_scales`` replaces the scales by
     powers of two in [2^-9, 2^-5] (every product is then exact in float64)."""
     rng = np.random.default_rng([seed, _S_MISC])
-    Qf = unit_rows(seed, _S_Q, Nq * Lq, dtype=torch.float32).view(Nq, Lq, D_MODEL)
-    Df = unit_rows(seed, _S_D, Nd * Ld, dtype=torch.float32).view(Nd, Ld, D_MODEL)
+    Qf = unit_rows(seed, _S_Q, Nq * Lq, d, dtype=torch.float32).view(Nq, Lq, d)
+    Df = unit_rows(seed, _S_D, Nd * Ld, d, dtype=torch.float32).view(Nd, Ld, d)
     Q, qs = quantise_per_token(Qf)
     D, ds = quantise_per_token(Df)
     if pow2_scales:

@@ -104,7 +104,8 @@ def test_i8_validation(L):
                  a["qm"], a["dm"], a["si"], a["sf"], a["am"], None)
 
     assert call(si=None, sf=None) == ERR_NULL
-    assert call(d=256) == ERR_UNSUPPORTED
+    assert call(d=0) == ERR_UNSUPPORTED
+    assert call(d=1025) == ERR_UNSUPPORTED
     assert call(Lq=-1) == ERR_SHAPE
     # Lq*d*127^2 must stay below 2^31: 1041 rows * 128 * 16129 overflow, 1040 do not
     assert call(Lq=1041) == ERR_OVERFLOW
@@ -147,7 +148,8 @@ def test_i8_tok_validation(L):
         return f(Q, qs, D, ds, Nq, Nd, Lq, Ld, d, None, None, sc, am, None)
 
     assert call(Lq=-1) == ERR_SHAPE
-    assert call(d=64) == ERR_UNSUPPORTED
+    assert call(d=0) == ERR_UNSUPPORTED
+    assert call(d=2000) == ERR_UNSUPPORTED
     assert call(sc=None) == ERR_NULL
     assert call(qs=None) == ERR_NULL
     assert call(ds=None) == ERR_NULL

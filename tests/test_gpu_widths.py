@@ -7,8 +7,10 @@ registers (d <= 128), several chunks with a query staged in LDS (d > 128), a
 partial last chunk and K-step, rows whose byte length is not a multiple of 16
 (gathered element by element), masks, dead docs, empty sequences, multi-pass
 queries and pair lists; the backwards gather rows in 128-wide chunks with a
-partial or unaligned tail. Expected values come only from the oracle;
-tolerances and the argmax rule are those of oracle/compare.py.
+partial or unaligned tail; int8 rows (per-tensor scales: exact int32 sums and
+argmax; per-token scales: float compare inside the max) take the same kernel.
+Expected values come only from the oracle; tolerances and the argmax rule are
+those of oracle/compare.py.
 """
 
 import numpy as np
@@ -267,3 +269,61 @@ def test_bwd_varlen_widths(ms, oracle_mod, case):
     _assert_close("dD", dD.numpy(), rdD)
     again = run()
     assert all(torch.equal(x, y) for x, y in zip(again[:3], (dQ, dD, rp))), "not deterministic"
+
+
+INT8_CASES = [
+    # (Nq, Nd, Lq, Ld, kind, d, q_mask_p, d_mask_p)
+    (2, 5, 9, 13, "ternary", 64, 0.2, 0.2),
+    (3, 4, 100, 130, "quantised", 100, 0.0, 0.3),    # 100-byte rows: byte gathers
+    (2, 3, 128, 64, "extreme", 300, 0.0, 0.0),       # largest sums, two chunks
+    (1, 3, 64, 70, "quantised", 1000, 0.1, 0.0),     # four chunks, partial K-step
+    (2, 3, 40, 50, "ternary", 256, 0.0, 0.1),        # exactly one chunk
+    (1, 2, 100, 40, "quantised", 48, 0.0, 0.0),      # four passes
+    (2, 2, 3, 5, "ternary", 7, 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", INT8_CASES, ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}_{c[4]}_d{c[5]}")
+def test_int8_widths(ms, oracle_mod, case):
+    Nq, Nd, Lq, Ld, kind, d, qp, dp = case
+    _say(f"int8 width {case}")
+    w = synth.random_int8(1800 + d + Lq, Nq, Nd, Lq, Ld, ternary=kind == "ternary",
+                          extreme=kind == "extreme", d_mask_p=dp, q_mask_p=qp, d=d)
+
+    def run(want_argmax, both=True):
+        si = torch.empty((Nq, Nd), dtype=torch.int32, device=DEV) if both else None
+        out = ms.maxsim_fwd_i8(_g(w.Q), w.q_scale, _g(w.D), w.d_scale, _g(w.q_mask), _g(w.d_mask),
+                               want_argmax=want_argmax, scores_i32=si)
+        torch.cuda.synchronize()
+        return [None if t is None else t.cpu() for t in out]
+
+    si, sf, a = run(True)
+    ri, rf, ra = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    assert np.array_equal(si.numpy().astype(np.int64), ri)
+    assert np.array_equal(sf.numpy(), rf.astype(np.float32))  # same double rounding
+    assert np.array_equal(a.numpy(), ra)
+    si2, sf2, _ = run(False)
+    assert torch.equal(si2, si) and torch.equal(sf2, sf)
+    # float scores alone: the running int32 sum is kept in the float output's bits
+    _, sf3, _ = ms.maxsim_fwd_i8(_g(w.Q), w.q_scale, _g(w.D), w.d_scale, _g(w.q_mask), _g(w.d_mask),
+                                 want_int=False)
+    torch.cuda.synchronize()
+    assert torch.equal(sf3.cpu(), sf)
+
+
+@pytest.mark.parametrize("d", [64, 100, 384])
+def test_int8_tok_widths(ms, oracle_mod, d):
+    _say(f"int8 per-token width d={d}")
+    Nq, Nd, Lq, Ld = 3, 5, 70, 90
+    w = synth.random_int8_tok(1900 + d, Nq, Nd, Lq, Ld, q_mask_p=0.2, d_mask_p=0.2, dead_docs=1, d=d)
+    s, a = ms.maxsim_fwd_i8_tok(_g(w.Q), _g(w.q_scale), _g(w.D), _g(w.d_scale), _g(w.q_mask),
+                                _g(w.d_mask), want_argmax=True)
+    s2, _ = ms.maxsim_fwd_i8_tok(_g(w.Q), _g(w.q_scale), _g(w.D), _g(w.d_scale), _g(w.q_mask),
+                                 _g(w.d_mask))
+    torch.cuda.synchronize()
+    rs, ra = oracle_mod.fwd_i8_tok(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    _assert_close("scores", s.cpu().numpy(), rs)
+    _assert_close("scores (no argmax)", s2.cpu().numpy(), rs)
+    n, acc, bad = compare.int8_tok_argmax(a.cpu().numpy(), ra, w.Q.numpy(), w.D.numpy(),
+                                          w.d_scale.numpy(), w.d_mask.numpy())
+    assert not bad, f"argmax mismatches outside the rounding bound: {bad[:5]}"

@@ -632,6 +632,24 @@ def test_width_chunks_sum_to_full_dot(oracle_mod):
     assert np.abs(wrong - s).max() > 1e-3
 
 
+@pytest.mark.parametrize("d", [5, 100, 300])
+def test_brute_force_int8_widths(oracle_mod, d):
+    """INT8 sums and argmax at widths other than 128 against integer brute
+    force; per-token scales against the float brute force of the scaled dots."""
+    w = synth.random_int8(32 + d, 2, 4, 9, 13, ternary=True, d_mask_p=0.2, q_mask_p=0.2, d=d)
+    si, sf, a = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    sb, ab = bf.dense(w.Q, w.D, w.q_mask, w.d_mask, exact_int=True)
+    assert np.array_equal(si, sb)
+    assert np.array_equal(a, ab)
+    t = synth.random_int8_tok(33 + d, 2, 3, 7, 11, pow2_scales=True, d=d)
+    s, a = oracle_mod.fwd_i8_tok(t.Q, t.q_scale, t.D, t.d_scale)
+    Qs = t.Q.double() * t.q_scale.double()[..., None]
+    Ds = t.D.double() * t.d_scale.double()[..., None]
+    sb, ab = bf.dense(Qs, Ds)
+    np.testing.assert_allclose(s, sb, rtol=0, atol=1e-12)
+    assert np.array_equal(a, ab)
+
+
 @pytest.mark.parametrize("d", [7, 300])
 def test_backward_euler_identity_widths(oracle_mod, d):
     """The bilinear Euler identity of the backward (sum g*score = <dQ, Q> =
