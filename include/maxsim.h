@@ -13,7 +13,13 @@
  *   - Array arguments are DEVICE pointers owned by the caller. The library
  *     allocates no device memory and keeps no per-call state.
  *   - Every tensor is C-contiguous, row-major, with the embedding dimension d
- *     innermost. d must be 128 (other values return MAXSIM_ERR_UNSUPPORTED).
+ *     innermost. Any width 1 <= d <= 1024 is accepted (TileMaxSim Sec. 3
+ *     "dimension tiling" and Sec. 6 Table 9, widths 64 to 768); other values
+ *     return MAXSIM_ERR_UNSUPPORTED. d = 128 runs the kernels tuned for it;
+ *     every other width runs a kernel that walks rows in 256-byte chunks
+ *     (rows whose byte length is not a multiple of 16 are read element by
+ *     element, more slowly). Those other widths also need Nd*Ld < 2^31 for
+ *     uniform docs (OVERFLOW otherwise).
  *   - Q, D, dQ and dD must be 16-byte aligned (any hipMalloc or torch
  *     allocation is); every other array needs the alignment of its element
  *     type. A misaligned pointer returns MAXSIM_ERR_UNSUPPORTED.
@@ -49,7 +55,7 @@ typedef enum {
     MAXSIM_OK = 0,
     MAXSIM_ERR_NULL = 1,        /* a required pointer is NULL */
     MAXSIM_ERR_SHAPE = 2,       /* a negative size or inconsistent sizes */
-    MAXSIM_ERR_UNSUPPORTED = 3, /* d != 128, an unknown dtype, a misaligned pointer */
+    MAXSIM_ERR_UNSUPPORTED = 3, /* d outside 1..1024, an unknown dtype, a misaligned pointer */
     MAXSIM_ERR_OVERFLOW = 4,    /* an index or an int32 sum could overflow */
     MAXSIM_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
 } maxsim_status_t;
@@ -68,8 +74,8 @@ typedef enum { MAXSIM_F16 = 0, MAXSIM_BF16 = 1 } maxsim_dtype_t;
  *            valid token.
  * Products are exact in fp32 and accumulated in fp32. Errors: NULL for a
  * missing Q, D or scores (when the output is non-empty); SHAPE for negative
- * sizes; UNSUPPORTED for d != 128 or a bad dtype; OVERFLOW when argmax is
- * requested and Nq*Nd*Lq >= 2^31.
+ * sizes; UNSUPPORTED for d outside 1..1024 or a bad dtype; OVERFLOW when
+ * argmax is requested and Nq*Nd*Lq >= 2^31.
  */
 maxsim_status_t maxsim_fwd(maxsim_dtype_t dtype, const void* Q, const void* D, int64_t Nq,
                            int64_t Nd, int64_t Lq, int64_t Ld, int64_t d, const uint8_t* q_mask,
