@@ -37,8 +37,6 @@ constexpr int kCsrWaves = 16;
 constexpr int kCsrThreads = kCsrWaves * 64;
 constexpr int kCsrChunk = 16384;  // sources of one doc held in registers per pass (16 per lane)
 constexpr int kCsrBins = 1024;    // destination bins handled per round
-constexpr int kGatherThreads = 256;
-constexpr int kGroups = kGatherThreads / 16;  // 16-lane groups per workgroup
 constexpr int kDqDocs = 64;                   // docs staged per round of the dq pass
 constexpr uint16_t kNoKey = 0xFFFF;
 #ifndef MAXSIM_DD_WAVES
@@ -210,17 +208,24 @@ __device__ __forceinline__ uint64_t match_key10(uint32_t key, bool active)
 // into row starts, and kCsrScatter then places the round's sources.
 enum CsrMode { kCsrFull = 0, kCsrCount = 1, kCsrScatter = 2 };
 
+// LDS of one CSR-building workgroup
+struct CsrLds {
+    uint32_t hist[kCsrWaves][kCsrBins];  // per-wave counts, then per-wave slots
+    uint32_t run[kCsrBins];              // per-bin totals, then next free slot
+    uint32_t wsum[kCsrWaves];
+};
+
 template <int MODE = kCsrFull, typename Load>
-__device__ __forceinline__ void build_segment_csr(int64_t nsrc, int64_t L, int64_t carry,
+__device__ __forceinline__ void build_segment_csr(CsrLds& sm, int64_t nsrc, int64_t L, int64_t carry,
                                                   int32_t* __restrict__ row_ptr_seg,
                                                   int32_t* __restrict__ col_idx, Load&& load,
                                                   int64_t t_begin = 0)
 {
     constexpr int kPerWave = kCsrChunk / kCsrWaves;  // 1024 sources of a chunk per wave
     constexpr int kSteps = kPerWave / 64;             // 16 per lane
-    __shared__ uint32_t hist[kCsrWaves][kCsrBins];    // per-wave counts, then per-wave slots
-    __shared__ uint32_t run[kCsrBins];                // per-bin totals, then next free slot
-    __shared__ uint32_t wsum[kCsrWaves];
+    auto& hist = sm.hist;
+    auto& run = sm.run;
+    auto& wsum = sm.wsum;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nchunks = (int)((nsrc + kCsrChunk - 1) / kCsrChunk);
 
@@ -342,19 +347,11 @@ __device__ __forceinline__ void build_segment_csr(int64_t nsrc, int64_t L, int64
 // Inverse map of doc j: row_ptr[j*Ld + t] and the doc's segment
 // col_idx[j*Nq*Lq, (j+1)*Nq*Lq). Every doc receives exactly Nq*Lq sources,
 // so no global scan is needed.
-__global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
+__device__ __forceinline__ void csr_doc(const BwdArgs& a, CsrLds& sm, uint32_t j)
 {
-    const uint32_t j = blockIdx.x;
     const int64_t Nd = a.Nd, Ld = a.Ld;
     const uint32_t Lq = (uint32_t)a.Lq, nd = (uint32_t)Nd;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t per_doc = (uint32_t)(a.Nq * a.Lq);
-
-    // live(j) for the dq pass, parked in dD[j, 0, 0] (dD is written last)
-    if (wave == 0 && Ld > 0) {
-        const bool live = doc_live(a.d_mask, j, Ld);
-        if (lane == 0) a.dD[(int64_t)j * Ld * a.d] = live ? 1.f : 0.f;
-    }
     // doc-local source k = i*Lq + s is the flat source (i*Nd + j)*Lq + s
     auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
         SrcWalk w;
@@ -367,26 +364,33 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(BwdArgs a)
             tv[m] = ok ? __builtin_nontemporal_load(a.argmax + src) : 0;
         }
     };
-    build_segment_csr(per_doc, Ld, (int64_t)j * per_doc, a.row_ptr + (int64_t)j * Ld, a.col_idx, load);
-    if (j == Nd - 1 && tid == 0) a.row_ptr[Nd * Ld] = (int32_t)(a.Nq * Nd * a.Lq);
+    build_segment_csr(sm, per_doc, Ld, (int64_t)j * per_doc, a.row_ptr + (int64_t)j * Ld, a.col_idx, load);
+    if (j == Nd - 1 && threadIdx.x == 0) a.row_ptr[Nd * Ld] = (int32_t)(a.Nq * Nd * a.Lq);
 }
 
+// LDS of a dq workgroup with G row groups
+template <int G> struct DqLds {
+    int32_t am[kDqDocs][G];  // argmax[i, j0 + jj, s0 + g]
+    float wj[kDqDocs];       // g[i, j0 + jj] * live(j0 + jj)
+};
+
 // Eq. (2): dQ[i,s] = q_mask[i,s] * sum_j g[i,j] live(j) D[j, argmax[i,j,s]].
-// Workgroup = query i and 16 rows s; group g owns row s0 + g, lane l16 owns
-// dims 8*l16 .. 8*l16+7 of each 128-wide chunk of the row (GEN: any width,
-// the chunks taken one after another).
-template <int E, bool GEN>
-__global__ __launch_bounds__(kGatherThreads) void dq_kernel(BwdArgs a)
+// Workgroup `blk` = query i and G rows s; group g owns row s0 + g, lane l16
+// owns dims 8*l16 .. 8*l16+7 of each 128-wide chunk of the row (GEN: any
+// width, the chunks taken one after another). live(j) = any(d_mask[j,:]) is
+// found by the workgroup's waves while it stages the doc's weight (one early-
+// exit scan of the mask row per doc).
+template <int E, bool GEN, int G>
+__device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t blk)
 {
-    __shared__ int32_t am[kDqDocs][kGroups];  // argmax[i, j0 + jj, s0 + g]
-    __shared__ float wj[kDqDocs];             // g[i, j0 + jj] * live(j0 + jj)
+    constexpr int kThreads = 16 * G, kWavesB = kThreads / 64;
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
     const int64_t DW = GEN ? (int64_t)a.d : kD;
     const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
-    const int64_t sblocks = (Lq + kGroups - 1) / kGroups;
-    const int64_t i = blockIdx.x / sblocks;
-    const int64_t s0 = (blockIdx.x % sblocks) * kGroups;
-    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+    const int64_t sblocks = (Lq + G - 1) / G;
+    const int64_t i = blk / sblocks;
+    const int64_t s0 = (blk % sblocks) * G;
+    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15, wave = tid >> 6;
     const int64_t s = s0 + grp;
     const bool row_ok = s < Lq;
 
@@ -396,18 +400,18 @@ __global__ __launch_bounds__(kGatherThreads) void dq_kernel(BwdArgs a)
         for (int64_t j0 = 0; j0 < Nd; j0 += kDqDocs) {
             const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
             barrier_lds();
-            for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
-                const int jj = e / kGroups, gg = e % kGroups;
+            for (int e = tid; e < kDqDocs * G; e += kThreads) {
+                const int jj = e / G, gg = e % G;
                 int32_t t = 0;
                 if (jj < nj && s0 + gg < Lq) {
                     t = a.argmax[(i * Nd + j0 + jj) * Lq + s0 + gg];
                     t = t < 0 ? 0 : (t >= Ld ? (int32_t)(Ld - 1) : t);  // precondition guard
                 }
-                am[jj][gg] = t;
+                sm.am[jj][gg] = t;
             }
-            if (tid < nj) {
-                const int64_t jd = j0 + tid;
-                wj[tid] = a.g[i * Nd + jd] * a.dD[jd * Ld * DW];  // live(j) parked by the csr pass
+            for (int jj = wave; jj < nj; jj += kWavesB) {
+                const bool live = doc_live(a.d_mask, j0 + jj, Ld);
+                if ((tid & 63) == 0) sm.wj[jj] = a.g[i * Nd + j0 + jj] * (live ? 1.f : 0.f);
             }
             barrier_lds();
             if (!row_ok || ls.n == 0) continue;
@@ -417,18 +421,18 @@ __global__ __launch_bounds__(kGatherThreads) void dq_kernel(BwdArgs a)
                 float x[8][8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    loadn<E>(a.D, dbase + ((int64_t)(jj + u) * Ld + am[jj + u][grp]) * DW, ls.n, ls.vec, x[u]);
+                    loadn<E>(a.D, dbase + ((int64_t)(jj + u) * Ld + sm.am[jj + u][grp]) * DW, ls.n, ls.vec, x[u]);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const float w = wj[jj + u];
+                    const float w = sm.wj[jj + u];
 #pragma unroll
                     for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[u][k], acc[k]);
                 }
             }
             for (; jj < nj; ++jj) {
                 float x[8];
-                loadn<E>(a.D, dbase + ((int64_t)jj * Ld + am[jj][grp]) * DW, ls.n, ls.vec, x);
-                const float w = wj[jj];
+                loadn<E>(a.D, dbase + ((int64_t)jj * Ld + sm.am[jj][grp]) * DW, ls.n, ls.vec, x);
+                const float w = sm.wj[jj];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
             }
@@ -442,6 +446,21 @@ __global__ __launch_bounds__(kGatherThreads) void dq_kernel(BwdArgs a)
             storen(a.dQ + r * DW + ls.e0, ls.n, ls.vec, acc);
         }
     }
+}
+
+// The CSR and the dQ gathers in one launch (neither needs the other):
+// workgroups [0, Nd) build doc blockIdx's CSR, the rest are dq workgroups of
+// 64 query rows, which fill the CUs the Nd CSR workgroups leave idle. The two
+// kinds share one LDS allocation.
+template <int E, bool GEN>
+__global__ __launch_bounds__(kCsrThreads) void csr_dq_kernel(BwdArgs a, int64_t csr_blocks)
+{
+    __shared__ union {
+        CsrLds csr;
+        DqLds<kCsrThreads / 16> dq;
+    } sm;
+    if ((int64_t)blockIdx.x < csr_blocks) csr_doc(a, sm.csr, blockIdx.x);
+    else dq_block<E, GEN, kCsrThreads / 16>(a, sm.dq, (int64_t)blockIdx.x - csr_blocks);
 }
 
 // Eq. (3): dD[j,t] = sum over the CSR row of (j,t), in order, of
@@ -543,15 +562,13 @@ template <int E, bool GEN>
 static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream)
 {
     hipError_t err;
-    if (a.Nd > 0) {  // CSR (and the parked live flags) first
-        hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.Nd), dim3(kCsrThreads), 0, stream, a);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-    const int64_t qrows = a.Nq * a.Lq;
-    if (qrows > 0) {
-        // (with no docs the kernel writes zeros)
-        const int64_t blocks = a.Nq * ((a.Lq + kGroups - 1) / kGroups);
-        hipLaunchKernelGGL((dq_kernel<E, GEN>), dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
+    // CSR of every doc and dQ (zeros when there are no docs) in one launch
+    constexpr int64_t kDqRows = kCsrThreads / 16;
+    const int64_t csr_blocks = a.Nd;
+    const int64_t dq_blocks = a.Nq * a.Lq > 0 ? a.Nq * ((a.Lq + kDqRows - 1) / kDqRows) : 0;
+    if (csr_blocks + dq_blocks > 0) {
+        hipLaunchKernelGGL((csr_dq_kernel<E, GEN>), dim3((unsigned)(csr_blocks + dq_blocks)), dim3(kCsrThreads), 0,
+                           stream, a, csr_blocks);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (a.Nd > 0 && a.Ld > 0) {
@@ -659,9 +676,8 @@ __global__ __launch_bounds__(kPrepThreads) void vbwd_prep_kernel(VarBwdArgs a)
 // start the prep pass parked in dD. Source p (a packed query row) belongs to
 // the query found by a search of cu_q once per lane, then by walking forward
 // as p grows.
-__global__ __launch_bounds__(kCsrThreads) void vbwd_csr_kernel(VarBwdArgs a)
+__device__ __forceinline__ void vbwd_csr_doc(const VarBwdArgs& a, CsrLds& sm, int64_t j)
 {
-    const int64_t j = blockIdx.x;
     const int64_t Nd = a.Nd, Tq = a.Tq;
     const int64_t d0 = a.cu_d[j];
     int64_t L = (int64_t)a.cu_d[j + 1] - d0;
@@ -689,27 +705,37 @@ __global__ __launch_bounds__(kCsrThreads) void vbwd_csr_kernel(VarBwdArgs a)
         }
     };
     const int64_t carry = (int64_t)__builtin_bit_cast(uint32_t, a.dD[d0 * a.d]);  // parked by prep
-    build_segment_csr(Tq, L, carry, a.row_ptr + d0, a.col_idx, load);
+    build_segment_csr(sm, Tq, L, carry, a.row_ptr + d0, a.col_idx, load);
 }
 
 // Eq. (2) per packed query row p = cu_q[i] + s:
 // dQ[p] = sum over docs j with a token, ascending, of g[i,j] D[cu_d[j] + argmax[i,j,s]].
-template <int E, bool GEN>
-__global__ __launch_bounds__(kGatherThreads) void vbwd_dq_kernel(VarBwdArgs a)
+template <int G> struct VdqLds {
+    int64_t dbase[kDqDocs];
+    int32_t dlen[kDqDocs];
+    int32_t am[kDqDocs][G];
+    float wq[kDqDocs][G];
+    int32_t qi[G], qs[G];
+};
+
+template <int E, bool GEN, int G>
+__device__ __forceinline__ void vbwd_dq_block(const VarBwdArgs& a, VdqLds<G>& sm, int64_t blk)
 {
-    __shared__ int64_t dbase[kDqDocs];
-    __shared__ int32_t dlen[kDqDocs];
-    __shared__ int32_t am[kDqDocs][kGroups];
-    __shared__ float wq[kDqDocs][kGroups];
-    __shared__ int32_t qi[kGroups], qs[kGroups];
+    constexpr int kThreads = 16 * G;
+    auto& dbase = sm.dbase;
+    auto& dlen = sm.dlen;
+    auto& am = sm.am;
+    auto& wq = sm.wq;
+    auto& qi = sm.qi;
+    auto& qs = sm.qs;
     const int64_t Nd = a.Nd, Tq = a.Tq;
     const int64_t DW = GEN ? (int64_t)a.d : kD;
     const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
-    const int64_t p0 = (int64_t)blockIdx.x * kGroups;
+    const int64_t p0 = blk * G;
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
     const int64_t p = p0 + grp;
     const bool row_ok = p < Tq;
-    if (tid < kGroups) {
+    if (tid < G) {
         int i = 0, s = 0;
         if (p0 + tid < Tq) {
             i = seg_of(a.cu_q, (int)a.Nq + 1, p0 + tid);
@@ -736,8 +762,8 @@ __global__ __launch_bounds__(kGatherThreads) void vbwd_dq_kernel(VarBwdArgs a)
                 dlen[tid] = (int32_t)(l < 0 ? 0 : l);
             }
             barrier_lds();
-            for (int e = tid; e < kDqDocs * kGroups; e += kGatherThreads) {
-                const int jj = e / kGroups, gg = e % kGroups;
+            for (int e = tid; e < kDqDocs * G; e += kThreads) {
+                const int jj = e / G, gg = e % G;
                 int32_t t = 0;
                 float w = 0.f;
                 if (jj < nj && p0 + gg < Tq && dlen[jj] > 0) {
@@ -777,6 +803,20 @@ __global__ __launch_bounds__(kGatherThreads) void vbwd_dq_kernel(VarBwdArgs a)
         }
         if (row_ok && ls.n > 0) storen(a.dQ + p * DW + ls.e0, ls.n, ls.vec, acc);
     }
+}
+
+// The packed CSR and the packed dQ gathers in one launch: workgroups
+// [0, Nd) build doc blockIdx's CSR (its segment start parked by the prep
+// pass), the rest are dq workgroups of 64 packed query rows.
+template <int E, bool GEN>
+__global__ __launch_bounds__(kCsrThreads) void vbwd_csr_dq_kernel(VarBwdArgs a, int64_t csr_blocks)
+{
+    __shared__ union {
+        CsrLds csr;
+        VdqLds<kCsrThreads / 16> dq;
+    } sm;
+    if ((int64_t)blockIdx.x < csr_blocks) vbwd_csr_doc(a, sm.csr, blockIdx.x);
+    else vbwd_dq_block<E, GEN, kCsrThreads / 16>(a, sm.dq, (int64_t)blockIdx.x - csr_blocks);
 }
 
 // Eq. (3) per packed doc row r: the sources of CSR row r, in order, each
@@ -858,13 +898,14 @@ static hipError_t launch_bwd_varlen_t(VarBwdArgs a, hipStream_t stream)
     // then the CSR (only docs with a token have rows)
     hipLaunchKernelGGL(vbwd_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.Td > 0 && a.Nd > 0) {  // (with no query rows every row_ptr entry is 0)
-        hipLaunchKernelGGL(vbwd_csr_kernel, dim3((unsigned)a.Nd), dim3(kCsrThreads), 0, stream, a);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-    if (a.Tq > 0) {
-        const int64_t blocks = (a.Tq + kGroups - 1) / kGroups;
-        hipLaunchKernelGGL((vbwd_dq_kernel<E, GEN>), dim3((unsigned)blocks), dim3(kGatherThreads), 0, stream, a);
+    // the CSR (only docs with a token have rows; with no query rows every
+    // row_ptr entry is 0) and dQ in one launch
+    constexpr int64_t kDqRows = kCsrThreads / 16;
+    const int64_t csr_blocks = a.Td > 0 ? a.Nd : 0;
+    const int64_t dq_blocks = (a.Tq + kDqRows - 1) / kDqRows;
+    if (csr_blocks + dq_blocks > 0) {
+        hipLaunchKernelGGL((vbwd_csr_dq_kernel<E, GEN>), dim3((unsigned)(csr_blocks + dq_blocks)), dim3(kCsrThreads),
+                           0, stream, a, csr_blocks);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (a.Td > 0) {
@@ -946,7 +987,8 @@ __global__ __launch_bounds__(kCsrThreads) void cham_csr_kernel(ChamferArgs a, in
             tv[m] = k < c.ns ? __builtin_nontemporal_load(c.idx + src) : 0;
         }
     };
-    build_segment_csr<MODE>(c.ns, c.nr, 0, c.row_ptr + c.b * c.nr, c.col_idx, load, r * (int64_t)kCsrBins);
+    __shared__ CsrLds sm;
+    build_segment_csr<MODE>(sm, c.ns, c.nr, 0, c.row_ptr + c.b * c.nr, c.col_idx, load, r * (int64_t)kCsrBins);
 }
 
 // per segment: the counts in row_ptr become exclusive row starts (plus the

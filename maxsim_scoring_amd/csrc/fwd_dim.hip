@@ -520,7 +520,9 @@ hipError_t launch_dim_t(DimArgs a, hipStream_t stream)
             per_cu = 1;
         per_cu_cache[key].store(per_cu, std::memory_order_relaxed);
     }
-    // about one resident wave per unit over all queries, at most one unit per doc
+    // about one resident wave per unit over all queries, at most one unit per
+    // doc (more, shorter units measured slower here: a unit's setup, and for
+    // a staged query its LDS copy, is paid per unit)
     const int64_t slots = (int64_t)device_cu_count() * per_cu * W;
     int64_t units = (slots + a.Nq - 1) / a.Nq;
     if (units > a.Nd) units = a.Nd;
