@@ -153,10 +153,16 @@ __device__ __forceinline__ uint32_t mask_bits16(const uint8_t* p, int nb)
 
 }  // namespace
 
-template <int E, bool ARGMAX, bool QREG, int W, bool TOK>
+template <int E, bool ARGMAX, bool QREG, int W, bool TOK, int MT>
 __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 {
     static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
+    // MT = 2: rows of at most 128 bytes, so a 4 KB stage holds 32 rows of 128
+    // bytes (two MFMA M-tiles) instead of 16 rows of 256
+    static_assert(MT == 1 || (MT == 2 && QREG), "two M-tiles per stage only for one-chunk rows");
+    constexpr int R = 16 * MT;             // rows per chunk tile
+    constexpr int CB = kChunkBytes / MT;   // bytes of a row in a stage
+    constexpr int KMAX = CB / 64;          // K-steps a stage row holds
     using Acc = typename DimT<E>::Acc;
     using V = std::conditional_t<E == kI8 && !TOK, int, float>;  // value of the max
     constexpr int ES = DimT<E>::kES;
@@ -203,14 +209,23 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
     auto doc_off = [&](int j) -> int64_t { return a.cu_d ? (int64_t)a.cu_d[j] : (int64_t)j * a.Ld; };
     const int64_t u0 = jb < je ? uniform_i64(doc_off(jb)) : 0;
     const int span = jb < je ? uniform((int)(doc_off(je) - u0)) : 0;
-    const int ntile = (span + 15) >> 4;
+    const int ntile = (span + R - 1) / R;
     const int nitem = ntile * C;
     const unsigned char* unit_ptr = (const unsigned char*)a.D + u0 * RB;
 
-    // A-operand reads: row = lane % 16, logical piece 4k + g at slot (4k + g) ^ row
-    uint32_t frag_off[4];
+    // A-operand reads of M-tile m: row r = 16 m + lane % 16, logical piece
+    // 4k + g; 256-byte rows keep piece p at slot p ^ (r % 16), 128-byte rows
+    // at slot p ^ ((r / 2) % 8), so the 16 rows a read touches fall in
+    // distinct banks either way
+    uint32_t frag_off[MT][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) frag_off[k] = col * kChunkBytes + (((4 * k + g) ^ col) << 4);
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 16 * m + col;
+            frag_off[m][k] = MT == 1 ? (uint32_t)(col * kChunkBytes + (((4 * k + g) ^ col) << 4))
+                                     : (uint32_t)(r * CB + (((4 * k + g) ^ ((r >> 1) & 7)) << 4));
+        }
 
     const int64_t i_begin = pairs ? iq : blockIdx.x, i_end = pairs ? iq + 1 : a.Nq;
     const int64_t i_step = pairs ? 1 : gridDim.x;
@@ -383,14 +398,16 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
             // ---- chunk-tile ring ---------------------------------------------------
             int t_next = 0, c_next = 0, s_next = 0;  // next chunk tile to fetch, its stage
             auto issue = [&]() {
-                const unsigned char* tp = (const unsigned char*)uniform_ptr(unit_ptr + (int64_t)t_next * 16 * RB);
-                const int rows_left = span - t_next * 16;  // rows past the unit re-read its last row
+                const unsigned char* tp = (const unsigned char*)uniform_ptr(unit_ptr + (int64_t)t_next * R * RB);
+                const int rows_left = span - t_next * R;  // rows past the unit re-read its last row
                 const uint32_t dst = (uint32_t)uniform((int)(ring_base + s_next * kStageBytes));
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const int row = 4 * k + g;
+                    // lane's 16-byte slot of instruction k: row and logical piece (see frag_off)
+                    const int row = MT == 1 ? 4 * k + g : 8 * k + (lane >> 3);
+                    const int lp = MT == 1 ? col ^ row : (lane & 7) ^ ((row >> 1) & 7);
                     const int r = row < rows_left ? row : rows_left - 1;
-                    int off = c_next * kChunkBytes + ((col ^ row) << 4);
+                    int off = c_next * kChunkBytes + (lp << 4);
                     if (al) {
                         if (off >= RB) off = c_next * kChunkBytes;  // past the row end: a piece of the same row
                         dma_lds16_nt(tp, (uint32_t)(r * RB + off), dst + k * 1024);
@@ -398,9 +415,10 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                         lds_write_b128(dst + k * 1024 + lane * 16, load_piece<ES>(tp + r * RB, off, RB, false));
                     }
                 }
-                if constexpr (TOK) {  // lane l: the scale of tile row l % 16, at dst + 4 KB + 4 l
-                    const float* sp = (const float*)uniform_ptr(a.d_scale_tok + u0 + (int64_t)t_next * 16);
-                    const int r = col < rows_left ? col : rows_left - 1;
+                if constexpr (TOK) {  // lane l: the scale of tile row l % R, at dst + 4 KB + 4 l
+                    const float* sp = (const float*)uniform_ptr(a.d_scale_tok + u0 + (int64_t)t_next * R);
+                    const int rl = lane & (R - 1);
+                    const int r = rl < rows_left ? rl : rows_left - 1;
                     dma_lds4(sp, (uint32_t)(r * 4), dst + kCTileBytes);
                 }
                 if (++c_next == C) {
@@ -413,23 +431,26 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 
             int stage = 0;
             for (int t = 0; t < ntile && j < je; ++t) {
-                uint32_t vb = 0xFFFFu;
-                if (a.d_mask) {
-                    const int nb = span - t * 16 < 16 ? span - t * 16 : 16;
-                    vb = mask_bits16(a.d_mask + u0 + t * 16, nb);
-                }
-                Acc acc[kNT];
+                Acc acc[MT][kNT];
 #pragma unroll
-                for (int n = 0; n < kNT; ++n) acc[n] = Acc{0, 0, 0, 0};
-                float sc[4] = {1.f, 1.f, 1.f, 1.f};  // doc-token scales of rows 4g .. 4g+3 (TOK)
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int n = 0; n < kNT; ++n) acc[m][n] = Acc{0, 0, 0, 0};
+                float sc[MT][4];  // doc-token scales of rows 16m + 4g .. +3 (TOK)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) sc[m][0] = sc[m][1] = sc[m][2] = sc[m][3] = 1.f;
                 for (int c = 0; c < C; ++c) {
                     const int q = t * C + c;
                     const int behind = nitem - 1 - q;
                     wait_ctiles_behind<LPI>(behind < kStages - 1 ? behind : kStages - 1);
                     const uint32_t sbase = ring_base + stage * kStageBytes;
-                    i32x4 af[4];
-                    lds_read4(af[0], af[1], af[2], af[3], sbase + frag_off[0], sbase + frag_off[1],
-                              sbase + frag_off[2], sbase + frag_off[3]);
+                    i32x4 af[MT][4];
+                    if constexpr (MT == 1)
+                        lds_read4(af[0][0], af[0][1], af[0][2], af[0][3], sbase + frag_off[0][0], sbase + frag_off[0][1],
+                                  sbase + frag_off[0][2], sbase + frag_off[0][3]);
+                    else  // 128-byte rows hold two K-steps
+                        lds_read4(af[0][0], af[0][1], af[1][0], af[1][1], sbase + frag_off[0][0], sbase + frag_off[0][1],
+                                  sbase + frag_off[1][0], sbase + frag_off[1][1]);
                     if constexpr (TOK) {
                         if (c == C - 1) {  // before the stage is refilled
                             // a plain LDS load (the ring's direct-to-LDS writes are
@@ -437,11 +458,14 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                             // them): taking the four values out of an assembly
                             // ds_read_b128 that is skipped on other paths gave
                             // the first value for all four with this compiler
-                            const f32x4 sv = *(const f32x4*)(ring + stage * kStageBytes + kCTileBytes + 16 * g);
-                            sc[0] = sv.x;
-                            sc[1] = sv.y;
-                            sc[2] = sv.z;
-                            sc[3] = sv.w;
+#pragma unroll
+                            for (int m = 0; m < MT; ++m) {
+                                const f32x4 sv = *(const f32x4*)(ring + stage * kStageBytes + kCTileBytes + 64 * m + 16 * g);
+                                sc[m][0] = sv.x;
+                                sc[m][1] = sv.y;
+                                sc[m][2] = sv.z;
+                                sc[m][3] = sv.w;
+                            }
                         }
                     }
                     if constexpr (!QREG) {
@@ -450,7 +474,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 #pragma unroll
                         for (int n = 0; n < kNT; ++n)
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) qa[n * 4 + k] = q_base + (n * C + c) * kCTileBytes + frag_off[k];
+                            for (int k = 0; k < 4; ++k) qa[n * 4 + k] = q_base + (n * C + c) * kCTileBytes + frag_off[0][k];
                         lds_read8(qv, qa);
 #pragma unroll
                         for (int n = 0; n < kNT; ++n)
@@ -461,26 +485,37 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                     stage = stage + 1 == kStages ? 0 : stage + 1;
                     const int kt = c == C - 1 ? kt_last : 4;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
+                    for (int k = 0; k < KMAX; ++k) {
                         if (k < kt) {
 #pragma unroll
-                            for (int n = 0; n < kNT; ++n) acc[n] = mma<E>(af[k], qf[n][k], acc[n]);
+                            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                                for (int n = 0; n < kNT; ++n) acc[m][n] = mma<E>(af[m][k], qf[n][k], acc[m][n]);
                         }
                     }
                 }
 
-                const int tile0 = t * 16;
-                int lo = 0;
-                while (true) {
-                    const int hi = doc_end - tile0 < 16 ? doc_end - tile0 : 16;
-                    if (hi > lo) fold(acc, sc, tile0, lo, hi, vb);
-                    if (doc_end - tile0 > 16) break;  // the doc continues in the next tile
-                    finish_doc();
-                    ++j;
-                    if (j >= je) break;
-                    lo = hi > lo ? hi : lo;
-                    doc_start = doc_end;
-                    doc_end = doc_end_of(j);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const int tile0 = t * R + 16 * m;
+                    if (j >= je || tile0 >= span) break;
+                    uint32_t vb = 0xFFFFu;
+                    if (a.d_mask) {
+                        const int nb = span - tile0 < 16 ? span - tile0 : 16;
+                        vb = mask_bits16(a.d_mask + u0 + tile0, nb);
+                    }
+                    int lo = 0;
+                    while (true) {
+                        const int hi = doc_end - tile0 < 16 ? doc_end - tile0 : 16;
+                        if (hi > lo) fold(acc[m], sc[m], tile0, lo, hi, vb);
+                        if (doc_end - tile0 > 16) break;  // the doc continues in the next tile
+                        finish_doc();
+                        ++j;
+                        if (j >= je) break;
+                        lo = hi > lo ? hi : lo;
+                        doc_start = doc_end;
+                        doc_end = doc_end_of(j);
+                    }
                 }
             }
             // docs left with no tokens (only when the unit has no tiles)
@@ -499,10 +534,10 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 
 namespace {
 
-template <int E, bool ARGMAX, bool QREG, int W, bool TOK>
+template <int E, bool ARGMAX, bool QREG, int W, bool TOK, int MT = 1>
 hipError_t launch_dim_t(DimArgs a, hipStream_t stream)
 {
-    auto kern = fwd_dim_kernel<E, ARGMAX, QREG, W, TOK>;
+    auto kern = fwd_dim_kernel<E, ARGMAX, QREG, W, TOK, MT>;
     constexpr int kStageBytes = kCTileBytes + (TOK ? 256 : 0);
     const size_t lds = (size_t)(QREG ? 0 : kNT * a.nchunk) * kCTileBytes + (size_t)W * kStages * kStageBytes;
     if (a.pair_q) {
@@ -513,7 +548,7 @@ hipError_t launch_dim_t(DimArgs a, hipStream_t stream)
     }
     // resident workgroups per CU, per chunk count (the LDS size depends on it)
     static std::atomic<int> per_cu_cache[9];
-    const int key = a.nchunk < 9 ? a.nchunk : 8;
+    const int key = a.nchunk < 9 ? a.nchunk : 8;  // (one instance per MT: a kernel has one MT)
     int per_cu = per_cu_cache[key].load(std::memory_order_relaxed);
     if (per_cu <= 0) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, W * 64, lds) != hipSuccess || per_cu <= 0)
@@ -537,6 +572,8 @@ template <int E, bool TOK>
 hipError_t launch_dim_e(DimArgs a, hipStream_t stream)
 {
     const bool am = a.argmax != nullptr;
+    if (a.row_bytes <= kChunkBytes / 2)  // two 16-row M-tiles of 128-byte rows per stage
+        return am ? launch_dim_t<E, true, true, 4, TOK, 2>(a, stream) : launch_dim_t<E, false, true, 4, TOK, 2>(a, stream);
     if (a.nchunk == 1)
         return am ? launch_dim_t<E, true, true, 4, TOK>(a, stream) : launch_dim_t<E, false, true, 4, TOK>(a, stream);
     if constexpr (E != kI8) {  // pair lists (16-bit types only): one wave per workgroup

@@ -181,7 +181,23 @@ def test_pairs_varlen_widths(ms, oracle_mod, d):
     assert not bad, f"argmax mismatches outside the near-tie bound: {bad[:5]}"
 
 
-@pytest.mark.parametrize("d", [64, 256, 768])
+@pytest.mark.parametrize("d", [64, 200])
+def test_dense_widths_many_queries(ms, oracle_mod, d):
+    """More queries than the grid's query axis holds (65,535): workgroups loop
+    over queries, with the staged-query barriers when d > 128."""
+    _say(f"dense width many queries d={d}")
+    Nq, Nd, Lq, Ld = 70_000, 3, 2, 7
+    w = synth.random_dense(2000 + d, Nq, Nd, Lq, Ld, dtype=torch.float16, d_mask_p=0.2, d=d)
+    s, a = ms.maxsim_fwd(_g(w.Q), _g(w.D), None, _g(w.d_mask), want_argmax=True)
+    torch.cuda.synchronize()
+    rs, ra = oracle_mod.fwd(w.Q, w.D, None, w.d_mask)
+    _assert_close("scores", s.cpu().numpy(), rs)
+    n, acc, bad = compare.dense_argmax_float(a.cpu().numpy(), ra, w.Q.double().numpy(),
+                                             w.D.double().numpy(), w.d_mask.numpy())
+    assert not bad, f"argmax mismatches outside the near-tie bound: {bad[:5]}"
+
+
+@pytest.mark.parametrize("d", [64, 100, 256, 768])
 def test_dim_sweep_full_size_sampled(ms, oracle_mod, d):
     """The width sweep at full size (one 32-token query against 10,000 docs of
     128 tokens, fp16) in the benchmark's launch configuration; the oracle
