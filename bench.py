@@ -193,7 +193,7 @@ def bench_int8(torch, ms, synth, wl, steps, warmup):
             "kernel": "fwd_dense_kernel"}
 
 
-DIM_SWEEP = (64, 96, 256, 384, 768)
+DIM_SWEEP = (64, 96, 128, 256, 384, 768)
 
 
 def bench_dim_sweep(torch, ms, synth, wl, steps, warmup):
