@@ -154,7 +154,7 @@ __device__ __forceinline__ uint32_t mask_bits16(const uint8_t* p, int nb)
 }  // namespace
 
 template <int E, bool ARGMAX, bool QREG, int W, bool TOK, int MT>
-__global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(QREG && !ARGMAX && !TOK ? 3 : 1))) void fwd_dim_kernel(DimArgs a)
 {
     static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
     // MT = 2: rows of at most 128 bytes, so a 4 KB stage holds 32 rows of 128
@@ -181,10 +181,20 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
     const uint32_t q_base = lds_addr(qbuf);
     unsigned char* ring = dim_lds + (QREG ? 0 : kNT * C * kCTileBytes) + wave * kStages * kStageBytes;
     const uint32_t ring_base = (uint32_t)uniform((int)lds_addr(ring));
+    // hand-over slot of wave w, written once its ring is idle at the end of a
+    // pass: the continued doc and the per-lane partial state
+    auto slot_of = [&](int w) { return dim_lds + (QREG ? 0 : kNT * C * kCTileBytes) + w * kStages * kStageBytes; };
+    static_assert(16 + kNT * 64 * 8 <= kCTileBytes, "a hand-over slot fits one ring stage");
 
-    // ---- the docs of this wave's unit -------------------------------------
+    // ---- the docs of this unit ----------------------------------------------
+    // With a pair list a unit is one wave's pair. Otherwise a unit is the
+    // workgroup's doc range, whose tiles are split evenly among its waves
+    // (`split`): a doc belongs to the wave holding its first row, and the
+    // waves that hold later rows of it hand their partial maxima over through
+    // LDS at the end of the pass.
     const bool pairs = a.pair_q != nullptr;
-    const int64_t unit = (int64_t)(pairs ? blockIdx.x : blockIdx.y) * W + wave;
+    const bool split = !pairs;
+    const int64_t unit = pairs ? (int64_t)blockIdx.x * W + wave : (int64_t)blockIdx.y;
     const int64_t U = pairs ? a.npairs : (int64_t)a.units;
     const int Nd = (int)a.Nd;
     int jb = 0, je = 0, iq = 0;
@@ -203,15 +213,39 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
             je = uniform((int)(((int64_t)Nd * (unit + 1)) / U));
         }
     }
-    // a wave with no docs leaves now unless its workgroup shares a staged query
+    // a unit with no docs leaves now unless its workgroup shares a staged query
+    // (in split mode every wave of the workgroup has the same range)
     if ((QREG || W == 1) && jb >= je) return;
 
     auto doc_off = [&](int j) -> int64_t { return a.cu_d ? (int64_t)a.cu_d[j] : (int64_t)j * a.Ld; };
     const int64_t u0 = jb < je ? uniform_i64(doc_off(jb)) : 0;
     const int span = jb < je ? uniform((int)(doc_off(je) - u0)) : 0;
     const int ntile = (span + R - 1) / R;
-    const int nitem = ntile * C;
     const unsigned char* unit_ptr = (const unsigned char*)a.D + u0 * RB;
+
+    // this wave's tiles [t_begin, t_end), rows [r_lo, r_hi), and owned docs
+    // [j_own, j_lim): those whose first row is in the rows (the last wave also
+    // owns the empty docs at the end of the range); j_own - 1 continues into
+    // the rows when it starts before r_lo and ends after it
+    int t_begin = 0, t_end = ntile, r_lo = 0, r_hi = span, j_own = jb, j_lim = je;
+    bool has_cont = false;
+    if (split && jb < je) {
+        t_begin = (int)(((int64_t)ntile * wave) / W);
+        t_end = (int)(((int64_t)ntile * (wave + 1)) / W);
+        r_lo = t_begin * R;
+        r_hi = wave == W - 1 ? span : t_end * R;
+        // first doc of [jb, je] whose start is at or after row x of the range
+        auto first_from = [&](int x) -> int {
+            if (a.cu_d) return jb + wave_lower_bound(a.cu_d + jb, je - jb, u0 + x);
+            if (a.Ld <= 0) return x > 0 ? je : jb;
+            const int64_t k = jb + ((int64_t)x + a.Ld - 1) / a.Ld;
+            return uniform((int)(k < je ? k : je));
+        };
+        j_own = first_from(r_lo);
+        j_lim = wave == W - 1 ? je : first_from(r_hi);
+        has_cont = j_own > jb && doc_off(j_own) - u0 > r_lo;
+    }
+    const int nitem = (t_end - t_begin) * C;
 
     // A-operand reads of M-tile m: row r = 16 m + lane % 16, logical piece
     // 4k + g; 256-byte rows keep piece p at slot p ^ (r % 16), 128-byte rows
@@ -278,8 +312,9 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
             if (jb >= je) continue;  // no docs: only here to share the staged query
 
             // ---- doc cursor ------------------------------------------------------
-            int j = jb;
-            int cache_base = jb + 1;  // lane k holds cu_d[cache_base + k] - u0 (packed docs)
+            bool cont = has_cont;  // folding the doc continued from the previous wave
+            int j = cont ? j_own - 1 : j_own;
+            int cache_base = j + 1;  // lane k holds cu_d[cache_base + k] - u0 (packed docs)
             int cu_cache = 0;
             if (a.cu_d) cu_cache = (int)((int64_t)a.cu_d[cache_base + lane <= Nd ? cache_base + lane : Nd] - u0);
             wait_vmcnt<0>();  // query fragments, scales, masks and the cache have landed
@@ -294,8 +329,8 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                 }
                 return uniform(__builtin_amdgcn_readlane(cu_cache, off));
             };
-            int doc_start = 0;
-            int doc_end = doc_end_of(j);
+            int doc_start = j < je ? uniform((int)(doc_off(j) - u0)) : span;
+            int doc_end = j < je ? doc_end_of(j) : span;
 
             V m[kNT];
             int idx[kNT];
@@ -385,18 +420,42 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                 }
             };
 
+            // the partial state of the continued doc, kept until the hand-over
+            V mc[kNT];
+            int ic[kNT];
+#pragma unroll
+            for (int n = 0; n < kNT; ++n) {
+                mc[n] = neg_inf<V>();
+                ic[n] = 0;
+            }
+            auto store_cont = [&]() {
+#pragma unroll
+                for (int n = 0; n < kNT; ++n) {
+                    mc[n] = m[n];
+                    ic[n] = idx[n];
+                    m[n] = neg_inf<V>();
+                    idx[n] = 0;
+                }
+                cont = false;
+            };
+            // a doc that ends: finished here, or handed over when continued
+            auto end_doc = [&]() {
+                if (cont) store_cont();
+                else finish_doc();
+            };
+
             // leading empty docs
-            while (j < je && doc_end <= 0) {
+            while (j < j_lim && doc_end <= r_lo) {
                 finish_doc();
                 ++j;
-                if (j < je) {
+                if (j < j_lim) {
                     doc_start = doc_end;
                     doc_end = doc_end_of(j);
                 }
             }
 
             // ---- chunk-tile ring ---------------------------------------------------
-            int t_next = 0, c_next = 0, s_next = 0;  // next chunk tile to fetch, its stage
+            int t_next = t_begin, c_next = 0, s_next = 0;  // next chunk tile to fetch, its stage
             auto issue = [&]() {
                 const unsigned char* tp = (const unsigned char*)uniform_ptr(unit_ptr + (int64_t)t_next * R * RB);
                 const int rows_left = span - t_next * R;  // rows past the unit re-read its last row
@@ -430,7 +489,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
             for (int q = 0; q < kStages && q < nitem; ++q) issue();
 
             int stage = 0;
-            for (int t = 0; t < ntile && j < je; ++t) {
+            for (int t = t_begin; t < t_end && j < j_lim; ++t) {
                 Acc acc[MT][kNT];
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
@@ -440,7 +499,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 #pragma unroll
                 for (int m = 0; m < MT; ++m) sc[m][0] = sc[m][1] = sc[m][2] = sc[m][3] = 1.f;
                 for (int c = 0; c < C; ++c) {
-                    const int q = t * C + c;
+                    const int q = (t - t_begin) * C + c;
                     const int behind = nitem - 1 - q;
                     wait_ctiles_behind<LPI>(behind < kStages - 1 ? behind : kStages - 1);
                     const uint32_t sbase = ring_base + stage * kStageBytes;
@@ -498,7 +557,7 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const int tile0 = t * R + 16 * m;
-                    if (j >= je || tile0 >= span) break;
+                    if (j >= j_lim || tile0 >= span) break;
                     uint32_t vb = 0xFFFFu;
                     if (a.d_mask) {
                         const int nb = span - tile0 < 16 ? span - tile0 : 16;
@@ -509,25 +568,66 @@ __global__ __launch_bounds__(W * 64) void fwd_dim_kernel(DimArgs a)
                         const int hi = doc_end - tile0 < 16 ? doc_end - tile0 : 16;
                         if (hi > lo) fold(acc[m], sc[m], tile0, lo, hi, vb);
                         if (doc_end - tile0 > 16) break;  // the doc continues in the next tile
-                        finish_doc();
+                        end_doc();
                         ++j;
-                        if (j >= je) break;
+                        if (j >= j_lim) break;
                         lo = hi > lo ? hi : lo;
                         doc_start = doc_end;
                         doc_end = doc_end_of(j);
                     }
                 }
             }
-            // docs left with no tokens (only when the unit has no tiles)
-            while (j < je) {
+            // a doc continued through all of this wave's rows (or into an empty
+            // range) is handed over whole
+            if (cont) {
+                store_cont();
+                ++j;
+                if (j < j_lim) {
+                    doc_start = doc_end;
+                    doc_end = doc_end_of(j);
+                }
+            }
+            // the last rows' open doc: finished by this wave after the hand-over
+            const bool open = split && wave < W - 1 && j < j_lim;
+            // docs left with no tokens (the empty docs at the end of the range)
+            while (!open && j < j_lim) {
                 finish_doc();
                 ++j;
-                if (j < je) {
+                if (j < j_lim) {
                     doc_start = doc_end;
                     doc_end = doc_end_of(j);
                 }
             }
             wait_vmcnt<0>();  // nothing of this pass is still in flight
+            if (split) {
+                {
+                    unsigned char* sl = slot_of(wave);
+                    if (lane == 0) *(int*)sl = has_cont ? j_own - 1 : -1;
+#pragma unroll
+                    for (int n = 0; n < kNT; ++n) {
+                        ((V*)(sl + 16))[n * 64 + lane] = mc[n];
+                        ((int*)(sl + 16 + kNT * 64 * 4))[n * 64 + lane] = ic[n];
+                    }
+                }
+                block_barrier();  // every wave's hand-over is in LDS
+                if (open) {
+                    // merge the later waves' partial maxima of doc j, in wave
+                    // (= row) order, so equal maxima keep the lowest row
+                    for (int w2 = wave + 1; w2 < W; ++w2) {
+                        const unsigned char* sl = slot_of(w2);
+                        if (uniform(*(const int*)sl) != j) break;
+#pragma unroll
+                        for (int n = 0; n < kNT; ++n) {
+                            const V om = ((const V*)(sl + 16))[n * 64 + lane];
+                            const int oi = ((const int*)(sl + 16 + kNT * 64 * 4))[n * 64 + lane];
+                            if constexpr (ARGMAX) argmax_merge(m[n], idx[n], om, oi);
+                            else m[n] = om > m[n] ? om : m[n];
+                        }
+                    }
+                    finish_doc();
+                }
+                block_barrier();  // the slots (ring stages) are free for the next pass
+            }
         }
     }
 }
@@ -555,16 +655,17 @@ hipError_t launch_dim_t(DimArgs a, hipStream_t stream)
             per_cu = 1;
         per_cu_cache[key].store(per_cu, std::memory_order_relaxed);
     }
-    // about one resident wave per unit over all queries, at most one unit per
-    // doc (more, shorter units measured slower here: a unit's setup, and for
-    // a staged query its LDS copy, is paid per unit)
-    const int64_t slots = (int64_t)device_cu_count() * per_cu * W;
-    int64_t units = (slots + a.Nq - 1) / a.Nq;
+    // a unit is a workgroup's doc range: about one resident workgroup per unit
+    // over all queries, at most one unit per doc (more, shorter units measured
+    // slower here: a unit's setup, and for a staged query its LDS copy, is
+    // paid per unit)
+    const int64_t wg_slots = (int64_t)device_cu_count() * per_cu;
+    int64_t units = (wg_slots + a.Nq - 1) / a.Nq;
     if (units > a.Nd) units = a.Nd;
     if (units < 1) units = 1;
     a.units = (int32_t)units;
     const int64_t gq = a.Nq < 65535 ? a.Nq : 65535;
-    hipLaunchKernelGGL(kern, dim3((unsigned)gq, (unsigned)((units + W - 1) / W)), dim3(W * 64), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)gq, (unsigned)units), dim3(W * 64), lds, stream, a);
     return hipGetLastError();
 }
 
