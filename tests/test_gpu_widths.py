@@ -84,6 +84,28 @@ def test_dense_widths(ms, oracle_mod, case):
     _assert_close("scores (no argmax)", s2.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("d", [64, 300])
+def test_split_docs_across_waves(ms, oracle_mod, d):
+    """A workgroup's rows are split among its waves: long docs continue across
+    several waves (their partial maxima handed over to the owner), empty docs
+    sit on wave boundaries, and duplicated rows put exact ties on both sides of
+    a boundary (the lowest row must win)."""
+    _say(f"split docs across waves d={d}")
+    rng = np.random.default_rng(90 + d)
+    lens = [0, 0, 1000, 0, 3, 0, 37, 0, 700, 16, 0]
+    w = synth.random_varlen(2100 + d, [32, 20], lens, dtype=torch.float16, d=d)
+    Dk = (torch.from_numpy(rng.integers(-2, 3, size=(int(w.cu_d[-1]), d)) / 8.0)).to(torch.float16)
+    Qk = (torch.from_numpy(rng.integers(-2, 3, size=(int(w.cu_q[-1]), d)) / 8.0)).to(torch.float16)
+    c = w.cu_d.numpy()
+    Dk[c[2] + 600:c[2] + 700] = Dk[c[2] + 10:c[2] + 110]  # ties far apart in the long doc
+    Dk[c[8] + 500:c[8] + 560] = Dk[c[8]:c[8] + 60]
+    s, a = ms.maxsim_fwd_varlen(_g(Qk), _g(w.cu_q), w.max_lq, _g(Dk), _g(w.cu_d), want_argmax=True)
+    torch.cuda.synchronize()
+    rs, ra = oracle_mod.fwd_varlen(Qk, w.cu_q, w.max_lq, Dk, w.cu_d)
+    assert np.array_equal(s.cpu().numpy().astype(np.float64), rs)  # k/8 values: exact in fp32
+    assert np.array_equal(a.cpu().numpy(), ra)
+
+
 @pytest.mark.parametrize("d", [64, 100, 300])
 def test_dense_widths_exact_ties(ms, oracle_mod, d):
     """Values k/8 make every dot product exact in fp32, so scores and argmax
