@@ -1,7 +1,8 @@
 // MaxSim forward at any embedding width for gfx950: fp16/bf16 or int8 rows
-// of d elements (1 <= d <= 1024, any d other than 128, which has its own
-// kernels), uniform or cu_seqlens-packed, cross product or pair list, with
-// masks and optional argmax; int8 with per-tensor or per-token scales.
+// of d elements (1 <= d <= 1024), uniform or cu_seqlens-packed, cross product
+// or pair list, with masks and optional argmax; int8 with per-tensor or
+// per-token scales. It serves every width other than 128 (which has its own
+// kernels) and, at 128 too, cross-product calls with one or two short queries.
 //
 // TileMaxSim Sec. 3 (dimension tiling: a row wider than 128 is cut into
 // 128-wide chunks whose partial dot products are summed before the max) and
@@ -16,29 +17,33 @@
 // Design. The streaming scheme of the 128-wide padding-free kernel,
 // generalised in the width. A row is cut into 256-byte chunks (128 fp16/bf16
 // or 256 int8 elements, the last chunk partial), so a 16-row tile of the doc
-// stream becomes C chunk tiles of 4 KB. Each wave is a persistent unit that owns a contiguous,
-// token-balanced range of whole docs and pulls its chunk tiles through a
-// private LDS ring with direct-to-LDS loads (16 bytes per lane, the pieces
-// XOR-swizzled by row so that the MFMA operand reads are conflict free). The
-// 16x16x32 fp16/bf16 MFMA (16x16x64 for int8, exact int32 sums) consumes a
-// chunk tile in up to four 64-byte K-steps and
-// accumulates the S tile over the C chunks; only after the last chunk is the
-// tile folded into the running max, so the dot products are those of the
-// whole row. Past the row end the query side holds zeros (K-steps wholly
-// past it are skipped) and the doc side re-reads a piece of the same row, so
-// no load leaves the row and the padded lanes add exact zeros.
+// stream becomes C chunk tiles of 4 KB (rows of at most 128 bytes instead
+// fill a 4 KB stage with 32 rows). A workgroup of 4 waves owns a contiguous,
+// token-balanced range of whole docs and splits the range's tiles evenly
+// among its waves; each wave pulls its chunk tiles through a private LDS ring
+// with direct-to-LDS loads (16 bytes per lane, the pieces XOR-swizzled by row
+// so that the MFMA operand reads are conflict free). The 16x16x32 fp16/bf16
+// MFMA (16x16x64 for int8, exact int32 sums) consumes a chunk tile in up to
+// four 64-byte K-steps and accumulates the S tile over the C chunks; only
+// after the last chunk is the tile folded into the running max, so the dot
+// products are those of the whole row. Past the row end the query side holds
+// zeros (K-steps wholly past it are skipped) and the doc side re-reads a
+// piece of the same row, so no load leaves the row and the padded lanes add
+// exact zeros. A doc whose rows run on into the next wave's share is finished
+// by the wave that holds its first row, after the later waves hand their
+// partial maxima over through LDS.
 //
 // When the query block fits one chunk (d <= 128) its fragments stay in VGPRs
 // for the pass. Wider queries are staged once per pass into LDS, shared by the
-// four waves of a workgroup (all of which then run the same passes and
-// barriers), and read per chunk tile; with a pair list, where each wave has its
-// own query, a workgroup is a single wave. Rows whose byte length is not a
-// multiple of 16 cannot take 16-byte loads: their pieces are gathered element
-// by element and written to LDS in the same layout (a slower path). With
-// per-token int8 scales, every chunk tile also brings its 16 doc-token scales
-// into the ring by a 4-byte direct-to-LDS load; they turn the tile's integer
-// dot products into floats before the max, and the query-token scale
-// (positive) multiplies the max.
+// workgroup's waves, and read per chunk tile; with a pair list, where each
+// wave has its own query, a unit is one wave's pair (and a workgroup a single
+// wave when the query is staged). Rows whose byte length is not a multiple of
+// 16 cannot take 16-byte loads: their pieces are gathered element by element
+// and written to LDS in the same layout (a slower path). With per-token int8
+// scales, every chunk tile also brings its doc-token scales into the ring by a
+// 4-byte direct-to-LDS load; they turn the tile's integer dot products into
+// floats before the max, and the query-token scale (positive) multiplies the
+// max.
 //
 // Queries are the fastest grid axis, so the workgroups that are resident
 // together share doc ranges and the repeated reads of a range for different
@@ -153,8 +158,12 @@ __device__ __forceinline__ uint32_t mask_bits16(const uint8_t* p, int nb)
 
 }  // namespace
 
+// Three waves per SIMD for the plain register-query kernels (they fit in 168
+// VGPRs without spilling; two per SIMD measured slower); the argmax and
+// per-token instances keep the compiler's choice, which does not spill.
 template <int E, bool ARGMAX, bool QREG, int W, bool TOK, int MT>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(QREG && !ARGMAX && !TOK ? 3 : 1))) void fwd_dim_kernel(DimArgs a)
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(QREG && !ARGMAX && !TOK ? 3 : 1)))
+void fwd_dim_kernel(DimArgs a)
 {
     static_assert(!TOK || E == kI8, "per-token scales are an int8 mode");
     // MT = 2: rows of at most 128 bytes, so a 4 KB stage holds 32 rows of 128
