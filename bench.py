@@ -92,6 +92,12 @@ def time_steps(torch, fn, steps: int, warmup: int, flush_bytes: int = 0):
     return sum(times), times
 
 
+def spread(times) -> dict:
+    """Minimum and 90th percentile of per-launch times (ms), beside the median."""
+    ts = sorted(times)
+    return {"ms_min": round(ts[0], 5), "ms_p90": round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)], 5)}
+
+
 def roofline(bound: str, achieved: float, peak: float, unit: str, traffic=None) -> dict:
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -148,7 +154,7 @@ def bench_tiny(torch, ms, synth, wl, steps, warmup):
     total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
     t = statistics.median(times)
     nbytes = wl.dense_fwd_bytes(4, 32, 32, 180, 128, 2, False, False, True)
-    return {"workload": w.name, "ms": t, "pairs_per_s": 128 / (t * 1e-3),
+    return {"workload": w.name, "ms": t, **spread(times), "pairs_per_s": 128 / (t * 1e-3),
             "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
             "note": "launch-bound: 1.5 MB of operands", "kernel": "fwd_dense_kernel"}
 
@@ -166,7 +172,7 @@ def bench_colpali(torch, ms, synth, wl, steps, warmup):
     t = statistics.median(times)
     valid = int(w.d_mask.sum())
     flops = wl.dense_fwd_flops(128, 128, 128, valid)
-    return {"workload": w.name, "ms": t, "pairs_per_s": 128 * 128 / (t * 1e-3),
+    return {"workload": w.name, "ms": t, **spread(times), "pairs_per_s": 128 * 128 / (t * 1e-3),
             "algorithmic_flops": flops, "dense_flops": 2 * 128 * 128 * 128 * 128 * 1024,
             "roofline": roofline("mfma", flops / (t * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s",
                                  load_traffic("fwd_dense_kernel", w.name)),
@@ -212,7 +218,7 @@ def bench_dim_sweep(torch, ms, synth, wl, steps, warmup):
         total, times = time_steps(torch, step, min(steps, 10), min(warmup, 5), flush_bytes=512 << 20)
         t = statistics.median(times)
         nbytes = wl.dense_fwd_bytes(1, 10_000, 32, 128, d, 2, False, False, False)
-        rows[f"d{d}"] = {"workload": w.name, "ms": t, "docs_per_s": 10_000 / (t * 1e-3),
+        rows[f"d{d}"] = {"workload": w.name, "ms": t, **spread(times), "docs_per_s": 10_000 / (t * 1e-3),
                          "algorithmic_bytes": nbytes,
                          "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
         del Q, D, w
@@ -239,7 +245,7 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
     total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
     t = statistics.median(times)
     nbytes = wl.bwd_compulsory_bytes(128, 128, 128, 1024, 128, 2, True, True)
-    return {"workload": "backward_colpali_bf16_128x128_lq128_ld1024", "ms": t,
+    return {"workload": "backward_colpali_bf16_128x128_lq128_ld1024", "ms": t, **spread(times),
             "pairs_per_s": 128 * 128 / (t * 1e-3), "compulsory_bytes": nbytes,
             "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
             "kernels": ["csr_kernel", "dq_kernel", "dd_kernel"]}
@@ -269,7 +275,7 @@ def bench_backward_varlen(torch, ms, synth, wl, steps, warmup):
     total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
     t = statistics.median(times)
     nbytes = wl.bwd_varlen_compulsory_bytes(128, 128, 128, Tq, Td, 128, 128, 2)
-    return {"workload": f"backward_varlen_bf16_128x128_lq16-128_ld768-1024_packed_{Tq}x{Td}", "ms": t,
+    return {"workload": f"backward_varlen_bf16_128x128_lq16-128_ld768-1024_packed_{Tq}x{Td}", "ms": t, **spread(times),
             "pairs_per_s": 128 * 128 / (t * 1e-3), "compulsory_bytes": nbytes,
             "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
             "kernels": ["vbwd_prep_kernel", "vbwd_csr_kernel", "vbwd_dq_kernel", "vbwd_dd_kernel"]}
@@ -370,7 +376,7 @@ def bench_topk(torch, ms, synth, wl, steps, warmup):
     total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
     t = statistics.median(times)
     nbytes = 100_000 * 4
-    return {"workload": "topk_1x100000_k100", "ms": t,
+    return {"workload": "topk_1x100000_k100", "ms": t, **spread(times),
             "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
             "note": "one workgroup per row: threshold from a leading sample, one filtering pass, select and sort in LDS", "kernel": "topk_kernel"}
 

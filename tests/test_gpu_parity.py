@@ -640,3 +640,34 @@ def test_chamfer_100k_points(ms, oracle_mod):
         assert np.array_equal(x.numpy(), y), name
     _assert_close("dP", dP.numpy(), rdP)
     _assert_close("dQ", dQ.numpy(), rdQ)
+
+
+# ------------------------------------------------------------------ streams
+
+def test_concurrent_streams(ms, oracle_mod):
+    """Calls on two streams at once (the ABI allows it; the library's shared
+    state is per-process launch caches): each stream's results equal the
+    oracle's and the single-stream results, bit for bit."""
+    _say("two streams at once")
+    w1 = synth.random_varlen(61, [32], synth.rerank_lengths(61, 4000, 50, 300).tolist())
+    w2 = synth.random_dense(62, 3, 40, 64, 200, dtype=torch.bfloat16, q_mask_p=0.2, d_mask_p=0.2, d=96)
+    a1 = [_g(t) for t in (w1.Q, w1.cu_q, w1.D, w1.cu_d)]
+    a2 = [_g(t) for t in (w2.Q, w2.D, w2.q_mask, w2.d_mask)]
+    ref1, _ = ms.maxsim_fwd_varlen(a1[0], a1[1], w1.max_lq, a1[2], a1[3])
+    ref2, ref2a = ms.maxsim_fwd(*a2, want_argmax=True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            o1, _ = ms.maxsim_fwd_varlen(a1[0], a1[1], w1.max_lq, a1[2], a1[3], stream=s1)
+        with torch.cuda.stream(s2):
+            o2, o2a = ms.maxsim_fwd(*a2, want_argmax=True, stream=s2)
+        outs.append((o1, o2, o2a))
+    torch.cuda.synchronize()
+    for o1, o2, o2a in outs:
+        assert torch.equal(o1, ref1) and torch.equal(o2, ref2) and torch.equal(o2a, ref2a)
+    rs1, _ = oracle_mod.fwd_varlen(w1.Q, w1.cu_q, w1.max_lq, w1.D, w1.cu_d, want_argmax=False)
+    rs2, _ = oracle_mod.fwd(w2.Q, w2.D, w2.q_mask, w2.d_mask, want_argmax=False)
+    _assert_close("stream 1 scores", ref1.cpu().numpy(), rs1)
+    _assert_close("stream 2 scores", ref2.cpu().numpy(), rs2)
