@@ -397,6 +397,31 @@ def bench_copy(torch, ms, synth, wl, steps, warmup):
             "roofline": roofline("hbm", 2 * n / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
 
 
+def bench_vendor_gemm(torch, ms, synth, wl, steps, warmup):
+    """Not a path of this library: the vendor's own GEMMs (torch.mm and
+    torch._int_mm, served by the ROCm BLAS libraries) on square 8192 x 8192 x
+    8192 bf16 and int8 operands, timed the same way. Their fraction of the
+    nominal dense MFMA peaks shows what a plain, well-tuned contraction reaches
+    on this part under its clock and power limits, a yardstick for the
+    fused forward kernels' fractions."""
+    n = 8192
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+    ai = torch.randint(-127, 128, (n, n), device="cuda", dtype=torch.int8, generator=gen)
+    bi = torch.randint(-127, 128, (n, n), device="cuda", dtype=torch.int8, generator=gen)
+    ops = 2 * n ** 3
+    out = {}
+    for name, fn, peak, unit in (("bf16", lambda: torch.mm(a, b), BF16_PEAK_TFLOPS, "TFLOP/s"),
+                                 ("int8", lambda: torch._int_mm(ai, bi), INT8_PEAK_TOPS, "TOP/s")):
+        k = min(steps, 20)
+        total, _ = time_steps(torch, fn, k, min(warmup, 5))
+        t = total / k
+        out[name] = {"shape": f"{n}x{n}x{n}", "ms": t,
+                     "roofline": roofline("mfma", ops / (t * 1e-3) / 1e12, peak, unit)}
+    return {"workload": "vendor_gemm_8192", **out}
+
+
 def cpu_baseline(w, target_s: float = 12.0) -> dict:
     """The oracle, as it stands, on the headline workload: a 300-doc run sizes
     the sample for about `target_s` seconds of work, taken as the first n docs
@@ -437,7 +462,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="",
                     help="run one workload: rerank|tiny|colpali|int8|backward|backward_varlen|"
-                         "pairs_varlen|two_stage|topk|chamfer|dim_sweep|copy")
+                         "pairs_varlen|two_stage|topk|chamfer|dim_sweep|copy|vendor_gemm")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -461,7 +486,7 @@ def main() -> int:
            "int8": bench_int8, "backward": bench_backward, "backward_varlen": bench_backward_varlen,
            "pairs_varlen": bench_pairs_varlen, "two_stage": bench_two_stage,
            "topk": bench_topk, "chamfer": bench_chamfer, "dim_sweep": bench_dim_sweep,
-           "copy": bench_copy}
+           "copy": bench_copy, "vendor_gemm": bench_vendor_gemm}
     per = {}
     head = None
     head_w = None
