@@ -225,23 +225,32 @@ def chamfer_argmin(got, ref, A64, T64):
     """Nearest-neighbour indices of one Chamfer direction: got/ref [B, na]
     index into the targets T64 [B, nt, 3] for the sources A64 [B, na, 3]. A
     GPU index t_g differing from the oracle's t_o is accepted only if
-    dist(t_g) - dist(t_o) <= e(t_o) + e(t_g) with dist the exact squared
-    distance and e = gamma(5) * dist, the bound on an fp32 sum of three
-    squared fp32 differences (5 roundings per term, all terms >= 0).
-    Returns (n_mismatch, n_accepted, failing entries)."""
+    dist(t_g) - dist(t_o) <= e(t_o) + e(t_g), with dist the exact squared
+    distance and e(t) = gamma(10) * (|s|^2 + |t|^2 + 2 sum_k |s_k t_k|): the
+    bound on an fp32 evaluation of the expanded form |s|^2 + |t|^2 - 2<s,t>
+    (the norms' own roundings, a 4-term dot product with any summation order,
+    and the final addition), which also covers the direct form from the
+    coordinate differences. Returns (n_mismatch, n_accepted, failing entries)."""
     got = np.asarray(got)
     ref = np.asarray(ref)
-    g5 = 5 * U32 / (1.0 - 5 * U32)
+    g10 = 10 * U32 / (1.0 - 10 * U32)
     bad, acc = [], 0
     for b, a in np.argwhere(got != ref):
         tg, to = int(got[b, a]), int(ref[b, a])
         if not 0 <= tg < T64.shape[1]:
             bad.append(((int(b), int(a)), tg, to, "index out of range"))
             continue
-        dg = float(((A64[b, a] - T64[b, tg]) ** 2).sum())
-        do = float(((A64[b, a] - T64[b, to]) ** 2).sum())
-        if dg - do <= g5 * (dg + do):
+        s = A64[b, a]
+
+        def dist_and_bound(t):
+            tt = T64[b, t]
+            return (float(((s - tt) ** 2).sum()),
+                    g10 * float((s * s).sum() + (tt * tt).sum() + 2.0 * np.abs(s * tt).sum()))
+
+        dg, eg = dist_and_bound(tg)
+        do, eo = dist_and_bound(to)
+        if dg - do <= eg + eo:
             acc += 1
         else:
-            bad.append(((int(b), int(a)), tg, to, f"gap {dg - do:.3e} > bound {g5 * (dg + do):.3e}"))
+            bad.append(((int(b), int(a)), tg, to, f"gap {dg - do:.3e} > bound {eg + eo:.3e}"))
     return int((got != ref).sum()), acc, bad

@@ -763,3 +763,20 @@ def test_chamfer_csr_matches_stable_argsort(oracle_mod):
         cnt = np.bincount(dest, minlength=B * nr)
         assert np.array_equal(rp, np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32))
         assert np.array_equal(ci, np.argsort(dest, kind="stable").astype(np.int32))
+
+
+def test_chamfer_argmin_comparator():
+    """The near-tie rule for Chamfer indices accepts a swap only inside the
+    fp32 evaluation bound: two targets whose exact squared distances differ by
+    far less than the bound may swap, a clearly farther target may not, and an
+    index out of range never passes."""
+    from oracle import compare
+    s = np.array([[[0.5, -0.25, 1.0]]])                     # one source
+    T = np.array([[[0.5, -0.25, 1.0 + 1e-3],                # dist 1e-6
+                   [0.5, -0.25 + 1e-3 * (1 + 1e-9), 1.0],   # dist 1e-6 (1 + 2e-9): a near tie
+                   [0.6, -0.25, 1.0]]])                     # dist 1e-2: clearly farther
+    ref = np.array([[0]])
+    assert compare.chamfer_argmin(np.array([[1]]), ref, s, T)[2] == []
+    assert len(compare.chamfer_argmin(np.array([[2]]), ref, s, T)[2]) == 1
+    assert len(compare.chamfer_argmin(np.array([[3]]), ref, s, T)[2]) == 1
+    assert compare.chamfer_argmin(ref, ref, s, T)[:2] == (0, 0)
