@@ -1001,8 +1001,17 @@ __global__ __launch_bounds__(1024) void cham_scan_kernel(ChamferArgs a)
     const int tid = threadIdx.x;
     const int64_t chunk = (c.nr + 1023) / 1024;
     const int64_t t0 = tid * chunk, t1 = t0 + chunk < c.nr ? t0 + chunk : c.nr;
+    // 16 loads in flight per step (integer sums: the grouping does not matter)
     uint32_t sum = 0;
-    for (int64_t t = t0; t < t1; ++t) sum += (uint32_t)rp[t];
+    int64_t t = t0;
+    for (; t + 16 <= t1; t += 16) {
+        uint32_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = (uint32_t)rp[t + k];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sum += v[k];
+    }
+    for (; t < t1; ++t) sum += (uint32_t)rp[t];
     part[tid] = sum;
     barrier_lds();
     for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the chunk sums
@@ -1012,7 +1021,17 @@ __global__ __launch_bounds__(1024) void cham_scan_kernel(ChamferArgs a)
         barrier_lds();
     }
     uint32_t run = (uint32_t)(c.b * c.ns) + part[tid] - sum;
-    for (int64_t t = t0; t < t1; ++t) {
+    for (t = t0; t + 16 <= t1; t += 16) {
+        uint32_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = (uint32_t)rp[t + k];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            rp[t + k] = (int32_t)run;
+            run += v[k];
+        }
+    }
+    for (; t < t1; ++t) {
         const uint32_t cnt = (uint32_t)rp[t];
         rp[t] = (int32_t)run;
         run += cnt;

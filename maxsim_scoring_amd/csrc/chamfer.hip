@@ -35,7 +35,6 @@ namespace maxsim {
 
 namespace {
 
-constexpr int kChThreads = 256;  // threads of the loss workgroup
 constexpr int kChTileT = 256;    // target points per LDS tile
 constexpr int kChMaxBlocks = 5;  // 16-point source blocks a wave holds at once
 typedef float f4v __attribute__((ext_vector_type(4)));
@@ -256,22 +255,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void ch
     }
 }
 
-// loss[b] = (1/N) sum_p dist1[b,p] + (1/M) sum_q dist2[b,q]: each thread sums
-// a strided slice in order, then a fixed tree over the workgroup.
-__global__ __launch_bounds__(kChThreads) void chamfer_loss_kernel(const float* __restrict__ dist1,
-                                                                  const float* __restrict__ dist2,
-                                                                  int64_t N, int64_t M, float* __restrict__ loss)
+// loss[b] = (1/N) sum_p dist1[b,p] + (1/M) sum_q dist2[b,q] in a fixed order:
+// thread t keeps kLossUnroll partial sums, partial j over the elements
+// t + kLossThreads*(kLossUnroll*k + j) for k ascending (so kLossUnroll loads
+// are in flight), adds them in j order, then a fixed tree over the workgroup.
+constexpr int kLossThreads = 1024, kLossUnroll = 16;
+__device__ __forceinline__ float cham_sum(const float* __restrict__ x, int64_t n, int tid)
 {
-    __shared__ float red[2][kChThreads];
+    float part[kLossUnroll];
+#pragma unroll
+    for (int j = 0; j < kLossUnroll; ++j) part[j] = 0.f;
+    for (int64_t p = tid; p < n; p += (int64_t)kLossThreads * kLossUnroll) {
+#pragma unroll
+        for (int j = 0; j < kLossUnroll; ++j) {
+            const int64_t q = p + (int64_t)j * kLossThreads;
+            if (q < n) part[j] += x[q];
+        }
+    }
+    float s = part[0];
+#pragma unroll
+    for (int j = 1; j < kLossUnroll; ++j) s += part[j];
+    return s;
+}
+__global__ __launch_bounds__(kLossThreads) void chamfer_loss_kernel(const float* __restrict__ dist1,
+                                                                    const float* __restrict__ dist2,
+                                                                    int64_t N, int64_t M, float* __restrict__ loss)
+{
+    __shared__ float red[2][kLossThreads];
     const int64_t b = blockIdx.x;
     const int tid = threadIdx.x;
-    float s1 = 0.f, s2 = 0.f;
-    for (int64_t p = tid; p < N; p += kChThreads) s1 += dist1[b * N + p];
-    for (int64_t q = tid; q < M; q += kChThreads) s2 += dist2[b * M + q];
-    red[0][tid] = s1;
-    red[1][tid] = s2;
+    red[0][tid] = cham_sum(dist1 + b * N, N, tid);
+    red[1][tid] = cham_sum(dist2 + b * M, M, tid);
     cham_barrier();
-    for (int off = kChThreads / 2; off > 0; off >>= 1) {
+    for (int off = kLossThreads / 2; off > 0; off >>= 1) {
         if (tid < off) {
             red[0][tid] += red[0][tid + off];
             red[1][tid] += red[1][tid + off];
@@ -303,7 +319,7 @@ hipError_t launch_chamfer_fwd(ChamferArgs a, hipStream_t stream)
     hipLaunchKernelGGL(chamfer_nn_kernel, dim3((unsigned)waves), dim3(64), 0, stream, a, nblocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.loss) {
-        hipLaunchKernelGGL(chamfer_loss_kernel, dim3((unsigned)a.B), dim3(kChThreads), 0, stream, a.dist1,
+        hipLaunchKernelGGL(chamfer_loss_kernel, dim3((unsigned)a.B), dim3(kLossThreads), 0, stream, a.dist1,
                            a.dist2, a.N, a.M, a.loss);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
