@@ -559,7 +559,11 @@ def test_pairs_varlen(ms, oracle_mod, case):
 
 # ------------------------------------------------------------------ Chamfer distance
 
-CHAMFER_CASES = [(1, 1, 1), (2, 5, 7), (3, 1000, 1500), (2, 3000, 2500), (1, 20000, 20000)]
+# the last two give the forward more 16-point source blocks than resident
+# waves: runs of several blocks per wave that cross (batch, direction)
+# segment ends, and (256 batches) more blocks than the waves can hold at once
+CHAMFER_CASES = [(1, 1, 1), (2, 5, 7), (3, 1000, 1500), (2, 3000, 2500), (1, 20000, 20000),
+                 (64, 1024, 1000), (256, 600, 520)]
 
 
 def _chamfer_gpu(ms, P, Q):
