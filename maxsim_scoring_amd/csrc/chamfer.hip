@@ -266,11 +266,16 @@ __device__ __forceinline__ float cham_sum(const float* __restrict__ x, int64_t n
 #pragma unroll
     for (int j = 0; j < kLossUnroll; ++j) part[j] = 0.f;
     for (int64_t p = tid; p < n; p += (int64_t)kLossThreads * kLossUnroll) {
+        // every load is issued (clamped in range) before any is used
+        float v[kLossUnroll];
 #pragma unroll
         for (int j = 0; j < kLossUnroll; ++j) {
             const int64_t q = p + (int64_t)j * kLossThreads;
-            if (q < n) part[j] += x[q];
+            v[j] = x[q < n ? q : n - 1];
         }
+#pragma unroll
+        for (int j = 0; j < kLossUnroll; ++j)
+            if (p + (int64_t)j * kLossThreads < n) part[j] += v[j];
     }
     float s = part[0];
 #pragma unroll
