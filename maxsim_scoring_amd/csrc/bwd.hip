@@ -135,12 +135,13 @@ __device__ __forceinline__ void barrier_lds()
 }
 
 // live(j): doc j has at least one valid token (always, without a d_mask,
-// when Ld > 0). Computed by one wave.
-__device__ __forceinline__ bool doc_live(const uint8_t* __restrict__ d_mask, int64_t j, int64_t Ld)
+// when Ld > 0); with t0 > 0, among tokens t0 and later. Computed by one wave.
+__device__ __forceinline__ bool doc_live(const uint8_t* __restrict__ d_mask, int64_t j, int64_t Ld,
+                                         int64_t t0 = 0)
 {
     if (!d_mask) return Ld > 0;
     bool any = false;
-    for (int64_t t = lane_id(); t < Ld; t += 64) {
+    for (int64_t t = t0 + lane_id(); t < Ld; t += 64) {
         any = any || d_mask[j * Ld + t] != 0;
         if (__ballot(any) != 0) break;
     }
@@ -400,18 +401,48 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
         for (int64_t j0 = 0; j0 < Nd; j0 += kDqDocs) {
             const int nj = (int)(Nd - j0 < kDqDocs ? Nd - j0 : kDqDocs);
             barrier_lds();
-            for (int e = tid; e < kDqDocs * G; e += kThreads) {
-                const int jj = e / G, gg = e % G;
+            // the argmax entries and weights of the batch, every load issued
+            // before any is used (out-of-range slots read entry 0)
+            constexpr int kPer = kDqDocs * G / kThreads;
+            constexpr int kPerW = (kDqDocs + kWavesB - 1) / kWavesB;
+            const int lane = tid & 63;
+            int32_t tv[kPer];
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int e = tid + u * kThreads, jj = e / G, gg = e % G;
+                const bool ok = jj < nj && s0 + gg < Lq;
+                tv[u] = a.argmax[ok ? (i * Nd + j0 + jj) * Lq + s0 + gg : 0];
+            }
+            float gv[kPerW];
+            uint8_t m0[kPerW];
+#pragma unroll
+            for (int u = 0; u < kPerW; ++u) {
+                const int jj = wave + u * kWavesB;
+                const int64_t j = j0 + (jj < nj ? jj : 0);
+                gv[u] = a.g[i * Nd + j];
+                m0[u] = a.d_mask ? a.d_mask[j * Ld + (lane < Ld ? lane : 0)] : (uint8_t)1;
+            }
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int e = tid + u * kThreads, jj = e / G, gg = e % G;
                 int32_t t = 0;
                 if (jj < nj && s0 + gg < Lq) {
-                    t = a.argmax[(i * Nd + j0 + jj) * Lq + s0 + gg];
+                    t = tv[u];
                     t = t < 0 ? 0 : (t >= Ld ? (int32_t)(Ld - 1) : t);  // precondition guard
                 }
                 sm.am[jj][gg] = t;
             }
-            for (int jj = wave; jj < nj; jj += kWavesB) {
-                const bool live = doc_live(a.d_mask, j0 + jj, Ld);
-                if ((tid & 63) == 0) sm.wj[jj] = a.g[i * Nd + j0 + jj] * (live ? 1.f : 0.f);
+#pragma unroll
+            for (int u = 0; u < kPerW; ++u) {
+                const int jj = wave + u * kWavesB;  // uniform over the wave
+                if (jj < nj) {
+                    bool live = Ld > 0;
+                    if (a.d_mask) {
+                        live = __ballot(lane < Ld && m0[u] != 0) != 0;  // the first 64 tokens
+                        if (!live && Ld > 64) live = doc_live(a.d_mask, j0 + jj, Ld, 64);
+                    }
+                    if (lane == 0) sm.wj[jj] = gv[u] * (live ? 1.f : 0.f);
+                }
             }
             barrier_lds();
             if (!row_ok || ls.n == 0) continue;
@@ -489,11 +520,24 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
     if constexpr (TAB) {
         const int64_t nqr = a.Nq * Lq;
         if (live && nqr > 0) {
+            // kWTab / kDdThreads entries per thread, every load issued
+            // before any is used (indices past the end read entry 0)
+            constexpr int kW = kWTab / kDdThreads;
             SrcWalk w;
             w.init(tid, kDdThreads, Lq);
-            for (int64_t k = tid; k < nqr; k += kDdThreads, w.next()) {
-                const float gk = a.g[w.i * Nd + j];
-                wtab[k] = (a.q_mask && a.q_mask[k] == 0) ? 0.f : gk;
+            float gk[kW];
+            uint8_t qm[kW];
+#pragma unroll
+            for (int u = 0; u < kW; ++u, w.next()) {
+                const int64_t k = tid + (int64_t)u * kDdThreads;
+                const bool ok = k < nqr;
+                gk[u] = a.g[(ok ? (int64_t)w.i : 0) * Nd + j];
+                qm[u] = a.q_mask ? a.q_mask[ok ? k : 0] : (uint8_t)1;
+            }
+#pragma unroll
+            for (int u = 0; u < kW; ++u) {
+                const int64_t k = tid + (int64_t)u * kDdThreads;
+                if (k < nqr) wtab[k] = qm[u] == 0 ? 0.f : gk[u];
             }
         }
         barrier_lds();
@@ -762,15 +806,28 @@ __device__ __forceinline__ void vbwd_dq_block(const VarBwdArgs& a, VdqLds<G>& sm
                 dlen[tid] = (int32_t)(l < 0 ? 0 : l);
             }
             barrier_lds();
-            for (int e = tid; e < kDqDocs * G; e += kThreads) {
-                const int jj = e / G, gg = e % G;
+            // every load of the batch issued before any is used
+            // (out-of-range slots read entry 0)
+            constexpr int kPer = kDqDocs * G / kThreads;
+            int32_t tv[kPer];
+            float wv[kPer];
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int e = tid + u * kThreads, jj = e / G, gg = e % G;
+                const bool ok = jj < nj && p0 + gg < Tq && dlen[jj] > 0;
+                const int64_t ij = ok ? (int64_t)qi[gg] * Nd + j0 + jj : 0;
+                tv[u] = a.argmax[ok ? ij * a.max_lq + qs[gg] : 0];
+                wv[u] = a.g[ij];
+            }
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int e = tid + u * kThreads, jj = e / G, gg = e % G;
                 int32_t t = 0;
                 float w = 0.f;
                 if (jj < nj && p0 + gg < Tq && dlen[jj] > 0) {
-                    const int64_t ij = (int64_t)qi[gg] * Nd + j0 + jj;
-                    t = a.argmax[ij * a.max_lq + qs[gg]];
+                    t = tv[u];
                     t = t < 0 ? 0 : (t >= dlen[jj] ? dlen[jj] - 1 : t);  // precondition guard
-                    w = a.g[ij];
+                    w = wv[u];
                 }
                 am[jj][gg] = t;
                 wq[jj][gg] = w;
