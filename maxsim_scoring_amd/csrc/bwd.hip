@@ -8,24 +8,27 @@
 // (the q_mask factor, grad_Q as a row-owned gather over docs).
 //
 // Launch sequence on one stream:
-//   csr     one workgroup of 16 waves per doc. live(j) = any(d_mask[j,:]) is
-//           parked in dD[j, 0, 0] for the dq pass (dD is written last). Every
-//           doc receives exactly Nq*Lq sources, so its CSR segment starts at
-//           j*Nq*Lq and no global scan is needed. Each wave holds the
-//           destinations of a contiguous block of the doc's sources in
-//           registers, counts them into its own LDS histogram; the counts are
-//           scanned, and every wave scatters its block in source order (ranks
-//           inside a wave from ballots over the key bits), so each CSR row
-//           lists its sources ascending;
-//   dq      one 16-lane group per query row (i,s), 16 rows per workgroup: the
-//           argmax entries and weights of 64 docs at a time are staged in
-//           LDS, then each group gathers D[j, argmax[i,j,s]] for j ascending
-//           (16 bytes per lane, 8 loads in flight) and accumulates in fp32.
-//           All workgroups sweep j in the same order, so the D rows they
-//           gather are shared in L2;
+//   csr+dq  one launch of 16-wave workgroups. The first Nd build the CSR of
+//           one doc each: every doc receives exactly Nq*Lq sources, so its
+//           CSR segment starts at j*Nq*Lq and no global scan is needed. Each
+//           wave holds the destinations of a contiguous block of the doc's
+//           sources in registers and counts them into its own LDS histogram;
+//           the counts are scanned, and every wave scatters its block in
+//           source order (ranks inside a wave from ballots over the key
+//           bits), so each CSR row lists its sources ascending. The other
+//           workgroups compute dQ, which needs no CSR: one 16-lane group per
+//           query row (i,s), 64 rows per workgroup; the argmax entries and
+//           weights g[i,j] live(j) of 64 docs at a time are staged in LDS
+//           (live(j) = any(d_mask[j,:]) found by the workgroup itself), then
+//           each group gathers D[j, argmax[i,j,s]] for j ascending (16 bytes
+//           per lane, 8 loads in flight) and accumulates in fp32. All
+//           workgroups sweep j in the same order, so the D rows they gather
+//           are shared in L2;
 //   dd      one 16-lane group per destination row (j,t): the group walks the
 //           row's sources in CSR order, gathers Q rows (16 bytes per lane)
 //           and accumulates in fp32; every row is written once.
+// The padding-free backward (vbwd_*) and the Chamfer backward (cham_*) below
+// follow the same pattern.
 #include "common.hpp"
 #include "kernels.hpp"
 
