@@ -631,13 +631,19 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 // the MFMAs of (M-tile in af, N-tile n); with next >= 0, each
                 // fragment is replaced by that of M-tile `next` as soon as its
                 // MFMA has been issued (a rolling prefetch of the next M-tile)
+                // The wave issues its MFMA chain at raised priority, so that
+                // the SIMD's other wave (folding or reading LDS) yields the
+                // issue slots while the chain is being fed (2-4 % at C3). Not
+                // with per-token scales, whose VALU-heavy fold it slows down.
                 auto mma = [&](i32x4 (&af)[KS], int n, int next, const Acc& init) {
                     Acc acc = init;
+                    if constexpr (!TOK) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                     for (int s = 0; s < KS; ++s) {
                         acc = mfma32<E>(af[s], qf[n][s], acc);
                         if (next >= 0) af[s] = *(const i32x4*)(sb + frag_off[s] + next * 32 * RB);
                     }
+                    if constexpr (!TOK) __builtin_amdgcn_s_setprio(0);
                     return acc;
                 };
                 // doc-token scales of the lane's 16 rows of M-tile mt (TOK)
