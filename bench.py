@@ -404,8 +404,8 @@ def bench_yardstick(torch, ms, synth, wl, steps, warmup):
     reported for the fused kernels. The vendor's GEMMs (torch.mm and
     torch._int_mm, served by the ROCm BLAS libraries) on square 8192^3 bf16
     and int8 operands, against the nominal dense MFMA peaks; and torch's
-    integer sum over a buffer of the headline's size (4.48 GB), a streaming
-    read, against the HBM peak."""
+    integer sum over buffers of the headline's size (4.48 GB) and of the
+    width sweep's corpus sizes, streaming reads, against the HBM peak."""
     n = 8192
     gen = torch.Generator(device="cuda").manual_seed(0)
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
@@ -427,6 +427,17 @@ def bench_yardstick(torch, ms, synth, wl, steps, warmup):
     t = total / k
     out["read_sum_4.48GB"] = {"ms": t, "bytes": nbytes,
                              "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    del x
+    # the same read at the width sweep's corpus sizes (10,000 docs x 128
+    # tokens x d x 2 bytes), each launch after a cache flush like the sweep's
+    for d in DIM_SWEEP:
+        nb = 10_000 * 128 * d * 2
+        x = torch.ones(nb // 8, dtype=torch.int64, device="cuda")
+        _, times = time_steps(torch, lambda: x.sum(), min(steps, 10), min(warmup, 5), flush_bytes=512 << 20)
+        t = statistics.median(times)
+        out[f"read_sum_d{d}"] = {"ms": t, "bytes": nb,
+                                 "roofline": roofline("hbm", nb / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+        del x
     return {"workload": "vendor_yardstick", **out}
 
 
