@@ -405,7 +405,8 @@ def bench_yardstick(torch, ms, synth, wl, steps, warmup):
     torch._int_mm, served by the ROCm BLAS libraries) on square 8192^3 bf16
     and int8 operands, against the nominal dense MFMA peaks; and torch's
     integer sum over buffers of the headline's size (4.48 GB) and of the
-    width sweep's corpus sizes, streaming reads, against the HBM peak."""
+    width sweep's corpus sizes, streaming reads, against the HBM peak; and
+    torch's row gather at the backward's gather volume."""
     n = 8192
     gen = torch.Generator(device="cuda").manual_seed(0)
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
@@ -438,6 +439,16 @@ def bench_yardstick(torch, ms, synth, wl, steps, warmup):
         out[f"read_sum_d{d}"] = {"ms": t, "bytes": nb,
                                  "roofline": roofline("hbm", nb / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
         del x
+    # random row gathers of the backward's volume: 2,097,152 rows of 256 bytes
+    # (bf16, d = 128) picked from a 32 MiB matrix, torch's index_select (it
+    # also writes the 537 MB it gathers)
+    src = torch.ones((128 * 1024, 128), dtype=torch.bfloat16, device="cuda")
+    idx = torch.randint(0, 128 * 1024, (128 * 128 * 128,), device="cuda", generator=gen)
+    _, times = time_steps(torch, lambda: torch.index_select(src, 0, idx), min(steps, 10), min(warmup, 5),
+                          flush_bytes=512 << 20)
+    t = statistics.median(times)
+    nb = idx.numel() * 256
+    out["gather_rows_537MB"] = {"ms": t, "bytes_gathered": nb, "gathered_GBps": round(nb / (t * 1e-3) / 1e9, 1)}
     return {"workload": "vendor_yardstick", **out}
 
 
