@@ -10,13 +10,15 @@
 // 2 <s, t>), where the bracket is one v_mfma_f32_16x16x4_f32 per 16 x 16 tile
 // with the targets (tx, ty, tz, ||t||^2) as rows of A and the sources
 // (-2 sx, -2 sy, -2 sz, 1) as columns of B (K = 4, fp32 in and out). A lane
-// owns one source column and 4 target rows of each tile; it keeps the running
-// min of its rows with a strict '<' and, only when that min drops (rare after
-// the first tiles), finds the lowest row holding it, so the first minimum in
-// ascending target order wins. The 4 row groups of a column are merged at the
-// end by (value, index). ||s||^2 is added once at the end (adding the same
-// value to every candidate keeps their order); the result is clamped at 0,
-// since the expanded form can round a zero distance slightly negative.
+// owns one source column and 4 target rows of each tile. Tiles go in pairs of
+// 16-target blocks; the lane folds its 8 values of a pair into its running
+// min and records, with a strict '<', the pair that last lowered it, so the
+// earliest pair keeps a tie. At the end it re-evaluates its 8 rows of that
+// pair and takes the lowest index with the smallest value. The 4 row groups
+// of a column are then merged by (value, index). ||s||^2 is added once at the
+// end (adding the same value to every candidate keeps their order); the
+// result is clamped at 0, since the expanded form can round a zero distance
+// slightly negative.
 //
 // Every wave is its own workgroup and streams its own copy of the target set
 // through LDS in 256-point tiles (coalesced loads, prepared as
