@@ -245,10 +245,16 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
     total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
     t = statistics.median(times)
     nbytes = wl.bwd_compulsory_bytes(128, 128, 128, 1024, 128, 2, True, True)
+    # the row gathers the two passes make beyond the compulsory bytes (served
+    # from L2 and the last-level cache): one 256-byte D row per (i, j, s) for
+    # dQ and one Q row per CSR entry for dD
+    gathered = 2 * 128 * 128 * 128 * 128 * 2
     return {"workload": "backward_colpali_bf16_128x128_lq128_ld1024", "ms": t, **spread(times),
             "pairs_per_s": 128 * 128 / (t * 1e-3), "compulsory_bytes": nbytes,
+            "gathered_bytes": gathered,
+            "gathered_GBps": round(gathered / (t * 1e-3) / 1e9, 1),
             "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
-            "kernels": ["csr_kernel", "dq_kernel", "dd_kernel"]}
+            "kernels": ["csr_dq_kernel", "dd_kernel"]}
 
 
 def bench_backward_varlen(torch, ms, synth, wl, steps, warmup):
@@ -275,10 +281,13 @@ def bench_backward_varlen(torch, ms, synth, wl, steps, warmup):
     total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
     t = statistics.median(times)
     nbytes = wl.bwd_varlen_compulsory_bytes(128, 128, 128, Tq, Td, 128, 128, 2)
+    gathered = 2 * Tq * 128 * 128 * 2  # a D row per (query row, doc) for dQ, a Q row per CSR entry for dD
     return {"workload": f"backward_varlen_bf16_128x128_lq16-128_ld768-1024_packed_{Tq}x{Td}", "ms": t, **spread(times),
             "pairs_per_s": 128 * 128 / (t * 1e-3), "compulsory_bytes": nbytes,
+            "gathered_bytes": gathered,
+            "gathered_GBps": round(gathered / (t * 1e-3) / 1e9, 1),
             "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
-            "kernels": ["vbwd_prep_kernel", "vbwd_csr_kernel", "vbwd_dq_kernel", "vbwd_dd_kernel"]}
+            "kernels": ["vbwd_prep_kernel", "vbwd_csr_dq_kernel", "vbwd_dd_kernel"]}
 
 
 def bench_pairs_varlen(torch, ms, synth, wl, steps, warmup):
