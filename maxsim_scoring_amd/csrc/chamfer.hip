@@ -18,7 +18,8 @@
 // of a column are then merged by (value, index). ||s||^2 is added once at the
 // end (adding the same value to every candidate keeps their order); the
 // result is clamped at 0, since the expanded form can round a zero distance
-// slightly negative.
+// slightly negative. All coordinates are first taken relative to the target
+// set's first point, so that rounding scales with the sets' extent.
 //
 // Every wave is its own workgroup and streams its own copy of the target set
 // through LDS in 256-point tiles (coalesced loads, prepared as
@@ -72,7 +73,7 @@ __device__ __forceinline__ void cham_load_raw(const float* __restrict__ T, int64
 // Raw coordinates -> tile entries (x, y, z, ||t||^2); points past the set's
 // end get ||t||^2 = +inf, so their distance is +inf and never wins.
 __device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (&r)[12], int64_t nt, int64_t t0,
-                                             int lane)
+                                             int lane, float cx, float cy, float cz)
 {
 #pragma unroll
     for (int m = 0; m < 12; ++m) sm.raw[64 * m + lane] = r[m];
@@ -82,7 +83,7 @@ __device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int p = lane + 64 * u;  // point of the tile
-        const float x = sm.raw[3 * p], y = sm.raw[3 * p + 1], z = sm.raw[3 * p + 2];
+        const float x = sm.raw[3 * p] - cx, y = sm.raw[3 * p + 1] - cy, z = sm.raw[3 * p + 2] - cz;
         const float n2 = t0 + p < nt ? __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x)) : __builtin_inff();
         sm.tile[buf][p] = f4v{x, y, z, n2};
     }
@@ -101,6 +102,11 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
     const int lane = threadIdx.x;
     const int col = lane & 15, rg = lane >> 4;  // source column, target row group (= K index of A, B)
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // both sets are taken relative to the target set's first point: the
+    // distances do not change, and the expanded form's rounding then scales
+    // with the sets' extent rather than their distance from the origin
+    const float cx = T[0], cy = T[1], cz = T[2];
+    const float crg = rg == 0 ? cx : (rg == 1 ? cy : cz);  // this lane's K component
 
     // this lane's source point of each block (clamped copies past the end)
     float bop[KN], best[KN];
@@ -109,7 +115,7 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
     for (int u = 0; u < KN; ++u) {
         int64_t sp = (k0 + u) * 16 + col;
         sp = sp < na ? sp : na - 1;
-        bop[u] = rg < 3 ? -2.f * A[sp * 3 + rg] : 1.f;
+        bop[u] = rg < 3 ? -2.f * (A[sp * 3 + (rg < 3 ? rg : 0)] - crg) : 1.f;
         best[u] = __builtin_inff();
         bstep[u] = 0;
     }
@@ -117,7 +123,7 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
     const int64_t ntiles = (nt + kChTileT - 1) / kChTileT;
     float raw[12];
     cham_load_raw(T, nt, 0, lane, raw);
-    cham_prepare(sm, 0, raw, nt, 0, lane);
+    cham_prepare(sm, 0, raw, nt, 0, lane, cx, cy, cz);
     for (int64_t it = 0; it < ntiles; ++it) {
         const int64_t t0 = it * kChTileT;
         const int buf = (int)(it & 1);
@@ -174,7 +180,7 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
         } else {
             for (int tb = 0; tb < tbs; ++tb) block(tf[tb * 64], step0 + tb);
         }
-        if (it + 1 < ntiles) cham_prepare(sm, buf ^ 1, raw, nt, t0 + kChTileT, lane);
+        if (it + 1 < ntiles) cham_prepare(sm, buf ^ 1, raw, nt, t0 + kChTileT, lane, cx, cy, cz);
     }
 
     // the row of the recorded step: among this lane's rows of the step's
@@ -190,7 +196,7 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
         int64_t sp = (k0 + u) * 16 + col;
         const bool own = sp < na;
         sp = own ? sp : na - 1;
-        const float sx = A[sp * 3], sy = A[sp * 3 + 1], sz = A[sp * 3 + 2];
+        const float sx = A[sp * 3] - cx, sy = A[sp * 3 + 1] - cy, sz = A[sp * 3 + 2] - cz;
         const int64_t tbase = (int64_t)bstep[u] * 16 + 4 * rg;
         int i = (int)(tbase < nt ? tbase : nt - 1);
         float rv = __builtin_inff();
@@ -198,7 +204,7 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
         for (int r = 0; r < 8; ++r) {
             const int64_t t = tbase + (r < 4 ? r : 12 + r);
             if (t < nt) {
-                const float tx = T[t * 3], ty = T[t * 3 + 1], tz = T[t * 3 + 2];
+                const float tx = T[t * 3] - cx, ty = T[t * 3 + 1] - cy, tz = T[t * 3 + 2] - cz;
                 const float n2 = __builtin_fmaf(tz, tz, __builtin_fmaf(ty, ty, tx * tx));
                 const float v =
                     __builtin_fmaf(-2.f * sz, tz, __builtin_fmaf(-2.f * sy, ty, __builtin_fmaf(-2.f * sx, tx, n2)));

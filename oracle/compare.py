@@ -226,11 +226,14 @@ def chamfer_argmin(got, ref, A64, T64):
     index into the targets T64 [B, nt, 3] for the sources A64 [B, na, 3]. A
     GPU index t_g differing from the oracle's t_o is accepted only if
     dist(t_g) - dist(t_o) <= e(t_o) + e(t_g), with dist the exact squared
-    distance and e(t) = gamma(10) * (|s|^2 + |t|^2 + 2 sum_k |s_k t_k|): the
-    bound on an fp32 evaluation of the expanded form |s|^2 + |t|^2 - 2<s,t>
-    (the norms' own roundings, a 4-term dot product with any summation order,
-    and the final addition), which also covers the direct form from the
-    coordinate differences. Returns (n_mismatch, n_accepted, failing entries)."""
+    distance and e(t) the bound on an fp32 evaluation of the expanded form
+    |s'|^2 + |t'|^2 - 2<s',t'> of coordinates taken relative to the batch's
+    first target point c (s' = s - c, t' = t - c, each coordinate rounded
+    once): gamma(10) * (|s'|^2 + |t'|^2 + 2 sum_k |s'_k t'_k|) for the norms'
+    roundings, a 4-term dot product in any summation order and the final
+    addition, plus 4u sum_k (|s'_k| + |t'_k|) |s_k - t_k| for the rounded
+    differences. It also covers the direct form from coordinate differences.
+    Returns (n_mismatch, n_accepted, failing entries)."""
     got = np.asarray(got)
     ref = np.asarray(ref)
     g10 = 10 * U32 / (1.0 - 10 * U32)
@@ -241,11 +244,14 @@ def chamfer_argmin(got, ref, A64, T64):
             bad.append(((int(b), int(a)), tg, to, "index out of range"))
             continue
         s = A64[b, a]
+        c = T64[b, 0]
 
         def dist_and_bound(t):
             tt = T64[b, t]
-            return (float(((s - tt) ** 2).sum()),
-                    g10 * float((s * s).sum() + (tt * tt).sum() + 2.0 * np.abs(s * tt).sum()))
+            sc, tc = s - c, tt - c
+            e = g10 * float((sc * sc).sum() + (tc * tc).sum() + 2.0 * np.abs(sc * tc).sum())
+            e += 4 * U32 * float(((np.abs(sc) + np.abs(tc)) * np.abs(s - tt)).sum())
+            return float(((s - tt) ** 2).sum()), e
 
         dg, eg = dist_and_bound(tg)
         do, eo = dist_and_bound(to)

@@ -619,6 +619,19 @@ def test_chamfer_exact_ties(ms, oracle_mod):
     _check_chamfer_fwd(oracle_mod, P, Q, got)
 
 
+def test_chamfer_offset_clouds(ms, oracle_mod):
+    """Point clouds far from the origin (unit spread around (100, -50, 200)):
+    distances and indices still meet the tolerance and the near-tie bound,
+    which the expanded form's rounding would not at this offset without
+    taking the coordinates relative to a point of the set."""
+    _say("chamfer offset clouds")
+    P, Q = synth.point_clouds(783, 2, 3000, 2500)
+    off = torch.tensor([100.0, -50.0, 200.0])
+    P, Q = P + off, Q + off
+    got = _chamfer_gpu(ms, P, Q)
+    _check_chamfer_fwd(oracle_mod, P, Q, got)
+
+
 def test_chamfer_100k_points(ms, oracle_mod):
     """Two 100,000-point clouds (the size the pages report the naive form
     cannot hold): the forward on 2,000 sampled points of each set, the
