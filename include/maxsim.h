@@ -259,9 +259,11 @@ maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
  *   P [B, N, 3], Q [B, M, 3] float32 (finite); dist1, idx1 [B, N] float32 /
  *   int32; dist2, idx2 [B, M]; loss [B] float32 or NULL.
  * Distances are evaluated in fp32 in the expanded form ||p||^2 + ||q||^2 -
- * 2<p,q> (the inner products on the matrix cores) and clamped at 0; an index
- * may differ from an exact evaluation's only among candidates within that
- * form's rounding bound. Sums run in a fixed order. B == 0 enqueues nothing.
+ * 2<p,q> (the inner products on the matrix cores) of coordinates taken
+ * relative to the batch's first point of the other set, and clamped at 0; an
+ * index may differ from an exact evaluation's only among candidates within
+ * that form's rounding bound. Sums run in a fixed order. B == 0 enqueues
+ * nothing.
  * Errors: SHAPE (negative sizes; N == 0 or M == 0 with B > 0), NULL,
  * UNSUPPORTED (misaligned pointers), OVERFLOW (B*N or B*M >= 2^31).
  */
