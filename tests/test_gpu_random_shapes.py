@@ -1,7 +1,8 @@
 """GPU parity on a seeded sweep of irregular shapes: the dense forward (with
 masks, dead rows and widths other than 128), its backward through the
-oracle's argmax, and the packed forward with empty and ragged sequences, each
-against the CPU oracle under the same rules as tests/test_gpu_parity.py.
+oracle's argmax, the packed forward with empty and ragged sequences, and the
+int8 forwards (per-tensor and per-token scales), each against the CPU oracle
+under the same rules as tests/test_gpu_parity.py.
 The shapes are drawn once from a fixed seed, so every run checks the same
 cases; they sit off the tile sizes the kernels use (16, 32, 64, 128, 256)."""
 
@@ -80,3 +81,46 @@ def test_random_varlen_fwd(ms, oracle_mod, case):
                                               w.D.double().numpy(), w.cu_d.numpy(),
                                               np.arange(len(c["ql"])), np.arange(len(c["dl"])))
     assert not bad, bad[:5]
+
+
+def _int8_case(k):
+    return dict(seed=980 + k, Nq=int(_rng.integers(1, 5)), Nd=int(_rng.integers(1, 20)),
+                Lq=int(_rng.integers(1, 300)), Ld=int(_rng.integers(1, 300)),
+                d=int((128, 128, 64, 192, 256)[int(_rng.integers(0, 5))]),
+                q_mask_p=float(_rng.choice([0.0, 0.3])), d_mask_p=float(_rng.choice([0.0, 0.3])),
+                ternary=bool(_rng.random() < 0.3))
+
+
+INT8 = [_int8_case(k) for k in range(8)]
+
+
+def _int8_id(c):
+    return f"{c['Nq']}x{c['Nd']}_lq{c['Lq']}_ld{c['Ld']}_d{c['d']}" + ("_ternary" if c["ternary"] else "")
+
+
+@pytest.mark.parametrize("case", INT8, ids=_int8_id)
+def test_random_int8_fwd(ms, oracle_mod, case):
+    """Per-tensor scales: exact int32 sums and argmax, the same fp32 scores;
+    per-token scales on the same shapes: scores within tolerance, argmax
+    within the scale-product rounding bound."""
+    c = case
+    _say(f"random int8 {_int8_id(c)}")
+    w = synth.random_int8(c["seed"], c["Nq"], c["Nd"], c["Lq"], c["Ld"], ternary=c["ternary"],
+                          q_mask_p=c["q_mask_p"], d_mask_p=c["d_mask_p"], d=c["d"])
+    si, sf, a = ms.maxsim_fwd_i8(_g(w.Q), w.q_scale, _g(w.D), w.d_scale, _g(w.q_mask), _g(w.d_mask),
+                                 want_argmax=True)
+    torch.cuda.synchronize()
+    ri, rf, ra = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D, w.d_scale, w.q_mask, w.d_mask)
+    assert np.array_equal(si.cpu().numpy().astype(np.int64), ri)
+    assert np.array_equal(sf.cpu().numpy(), rf.astype(np.float32))
+    assert np.array_equal(a.cpu().numpy(), ra)
+    t = synth.random_int8_tok(c["seed"], c["Nq"], c["Nd"], c["Lq"], c["Ld"], q_mask_p=c["q_mask_p"],
+                              d_mask_p=c["d_mask_p"], d=c["d"])
+    s, a = ms.maxsim_fwd_i8_tok(_g(t.Q), _g(t.q_scale), _g(t.D), _g(t.d_scale), _g(t.q_mask),
+                                _g(t.d_mask), want_argmax=True)
+    torch.cuda.synchronize()
+    rs, ra = oracle_mod.fwd_i8_tok(t.Q, t.q_scale, t.D, t.d_scale, t.q_mask, t.d_mask)
+    _assert_close("scores (per-token)", s.cpu().numpy(), rs)
+    n, acc, bad = compare.int8_tok_argmax(a.cpu().numpy(), ra, t.Q.numpy(), t.D.numpy(), t.d_scale.numpy(),
+                                          None if t.d_mask is None else t.d_mask.numpy())
+    assert not bad, f"argmax mismatches outside the rounding bound: {bad[:5]}"
