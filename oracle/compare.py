@@ -11,6 +11,9 @@
   with v the exact (fp64) dot product and e(t) = gamma * sum_k |q_k x_tk|,
   gamma = d*u / (1 - d*u), u = 2^-23, the textbook bound on an fp32 sum of d
   exact products in any order. Every other mismatch fails.
+* Chamfer distances, indices and gradients (chamfer_*): bounds derived from an
+  fp32 evaluation of the direct form sum_k (s_k - t_k)^2 and of the gradient
+  sums, independent of how the GPU searches.
 """
 
 from __future__ import annotations
@@ -222,41 +225,103 @@ def int8_tok_argmax(got, ref, Q8, D8, d_scale, d_mask=None, pairs=None):
 
 
 def chamfer_argmin(got, ref, A64, T64):
-    """Nearest-neighbour indices of one Chamfer direction: got/ref [B, na]
-    index into the targets T64 [B, nt, 3] for the sources A64 [B, na, 3]. A
-    GPU index t_g differing from the oracle's t_o is accepted only if
-    dist(t_g) - dist(t_o) <= e(t_o) + e(t_g), with dist the exact squared
-    distance and e(t) the bound on an fp32 evaluation of the expanded form
-    |s'|^2 + |t'|^2 - 2<s',t'> of coordinates taken relative to the batch's
-    first target point c (s' = s - c, t' = t - c, each coordinate rounded
-    once): gamma(10) * (|s'|^2 + |t'|^2 + 2 sum_k |s'_k t'_k|) for the norms'
-    roundings, a 4-term dot product in any summation order and the final
-    addition, plus 4u sum_k (|s'_k| + |t'_k|) |s_k - t_k| for the rounded
-    differences. It also covers the direct form from coordinate differences.
-    Returns (n_mismatch, n_accepted, failing entries)."""
+    """Nearest-neighbour indices of one Chamfer direction ("Flash-MaxSim"
+    Sec. 4.2.4 defines the distance as the squared Euclidean distance and
+    nothing about how it is evaluated): got/ref [B, na] index into the
+    targets T64 [B, nt, 3] for the sources A64 [B, na, 3]. A GPU index t_g
+    differing from the oracle's t_o is accepted only if
+        dist(t_g) - dist(t_o) <= gamma(5) * (dist(t_g) + dist(t_o)),
+    with dist the exact squared distance: an fp32 evaluation of the direct form
+    sum_k (s_k - t_k)^2 (one rounding per difference, per square and per
+    addition, in any order; every term >= 0) has relative error at most
+    gamma(5), so either index could be its argmin. The bound does not depend on
+    how the GPU searches. Returns (n_mismatch, n_accepted, failing entries)."""
     got = np.asarray(got)
     ref = np.asarray(ref)
-    g10 = 10 * U32 / (1.0 - 10 * U32)
+    g5 = gamma(5)
     bad, acc = [], 0
     for b, a in np.argwhere(got != ref):
         tg, to = int(got[b, a]), int(ref[b, a])
         if not 0 <= tg < T64.shape[1]:
             bad.append(((int(b), int(a)), tg, to, "index out of range"))
             continue
-        s = A64[b, a]
-        c = T64[b, 0]
-
-        def dist_and_bound(t):
-            tt = T64[b, t]
-            sc, tc = s - c, tt - c
-            e = g10 * float((sc * sc).sum() + (tc * tc).sum() + 2.0 * np.abs(sc * tc).sum())
-            e += 4 * U32 * float(((np.abs(sc) + np.abs(tc)) * np.abs(s - tt)).sum())
-            return float(((s - tt) ** 2).sum()), e
-
-        dg, eg = dist_and_bound(tg)
-        do, eo = dist_and_bound(to)
-        if dg - do <= eg + eo:
+        dg = float(((A64[b, a] - T64[b, tg]) ** 2).sum())
+        do = float(((A64[b, a] - T64[b, to]) ** 2).sum())
+        if dg - do <= g5 * (dg + do):
             acc += 1
         else:
-            bad.append(((int(b), int(a)), tg, to, f"gap {dg - do:.3e} > bound {eg + eo:.3e}"))
+            bad.append(((int(b), int(a)), tg, to, f"gap {dg - do:.3e} > bound {g5 * (dg + do):.3e}"))
     return int((got != ref).sum()), acc, bad
+
+
+def chamfer_dist(got, ref):
+    """Nearest-neighbour distances of one Chamfer direction, element by
+    element: |got - ref| <= 3.01 * gamma(5) * ref. If the GPU's index obeys
+    chamfer_argmin and its distance is a direct-form fp32 evaluation at that
+    index (relative error <= gamma(5)), then got lies in
+    [(1 - gamma(5)) ref, (1 + gamma(5))^2 / (1 - gamma(5)) ref]. No absolute
+    term: a zero distance (coincident points) must come out exactly 0.
+    Returns (ok, worst excess, index of the worst)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return True, 0.0, None
+    excess = np.abs(got - ref) - 3.01 * gamma(5) * np.abs(ref)
+    k = int(np.argmax(excess))
+    return (bool(np.all(excess <= 0) and np.all(np.isfinite(got))), float(excess.reshape(-1)[k]),
+            np.unravel_index(k, got.shape))
+
+
+def chamfer_dist_at_index(got_dist, got_idx, A64, T64):
+    """The distance written for each source is a direct-form fp32 evaluation
+    at the index written next to it: |got - exact(idx)| <= gamma(5) * exact(idx).
+    Returns (ok, worst excess)."""
+    got_idx = np.asarray(got_idx, dtype=np.int64)
+    b = np.arange(A64.shape[0])[:, None]
+    ex = ((A64 - T64[b, got_idx]) ** 2).sum(-1)
+    excess = np.abs(np.asarray(got_dist, dtype=np.float64) - ex) - gamma(5) * ex
+    return bool(np.all(excess <= 0)), float(excess.max()) if excess.size else 0.0
+
+
+def chamfer_loss_tol(depth: int) -> float:
+    """Relative tolerance of a Chamfer loss (1/N) sum dist1 + (1/M) sum dist2:
+    each distance within 3.01 gamma(5) (chamfer_dist), an fp32 sum of positive
+    terms whose rounding depth (the additions any one term passes through) is
+    at most `depth`, the rounding of N (or M) to fp32, one division and one
+    addition."""
+    return 3.01 * gamma(5) + gamma(depth + 3) + gamma(5) * gamma(depth + 3)
+
+
+def chamfer_grad_bounds(A64, T64, idx_a, idx_t, g_a, g_t):
+    """Per point and coordinate of the gradient with respect to the sources A
+    (dA[b,p] = 2 g_a[b,p] (A[b,p] - T[b,idx_a[b,p]]) + sum over the targets q
+    with idx_t[b,q] = p of 2 g_t[b,q] (A[b,p] - T[b,q])): the sum of the
+    terms' magnitudes S and their number n. An fp32 sum of those terms, each
+    formed with two roundings (the difference and the product by g; the factor
+    2 is exact), in any order, is within gamma(n + 2) * S of the exact sum."""
+    B, na, _ = A64.shape
+    nt = T64.shape[1]
+    b_a = np.broadcast_to(np.arange(B)[:, None], (B, na))
+    b_t = np.broadcast_to(np.arange(B)[:, None], (B, nt))
+    S = 2 * np.abs(g_a)[..., None] * np.abs(A64 - T64[b_a, idx_a])
+    terms = 2 * np.abs(g_t)[..., None] * np.abs(T64 - A64[b_t, idx_t])
+    np.add.at(S, (b_t.reshape(-1), np.asarray(idx_t).reshape(-1)), terms.reshape(-1, 3))
+    n = np.ones((B, na), np.int64)
+    np.add.at(n, (b_t.reshape(-1), np.asarray(idx_t).reshape(-1)), 1)
+    return S, n
+
+
+def chamfer_grad(got, ref, S, n):
+    """|got - ref| <= gamma(n + 2) * S element by element (chamfer_grad_bounds).
+    Returns (ok, worst excess, index of the worst)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    nn = np.asarray(n, dtype=np.float64)[..., None] + 2
+    tol = nn * U32 / (1.0 - nn * U32) * S
+    excess = np.abs(got - ref) - tol
+    if got.size == 0:
+        return True, 0.0, None
+    k = int(np.argmax(excess))
+    return (bool(np.all(excess <= 0) and np.all(np.isfinite(got))), float(excess.reshape(-1)[k]),
+            np.unravel_index(k, got.shape))
