@@ -767,16 +767,104 @@ def test_chamfer_csr_matches_stable_argsort(oracle_mod):
 
 def test_chamfer_argmin_comparator():
     """The near-tie rule for Chamfer indices accepts a swap only inside the
-    fp32 evaluation bound: two targets whose exact squared distances differ by
-    far less than the bound may swap, a clearly farther target may not, and an
-    index out of range never passes."""
+    direct form's fp32 rounding bound: two targets whose exact squared
+    distances differ by far less than the bound may swap, a clearly farther
+    target may not, and an index out of range never passes."""
     from oracle import compare
     s = np.array([[[0.5, -0.25, 1.0]]])                     # one source
     T = np.array([[[0.5, -0.25, 1.0 + 1e-3],                # dist 1e-6
                    [0.5, -0.25 + 1e-3 * (1 + 1e-9), 1.0],   # dist 1e-6 (1 + 2e-9): a near tie
+                   [0.5, -0.25 + 1e-3 * (1 + 1e-5), 1.0],   # dist 1e-6 (1 + 2e-5): outside the bound
                    [0.6, -0.25, 1.0]]])                     # dist 1e-2: clearly farther
     ref = np.array([[0]])
     assert compare.chamfer_argmin(np.array([[1]]), ref, s, T)[2] == []
     assert len(compare.chamfer_argmin(np.array([[2]]), ref, s, T)[2]) == 1
     assert len(compare.chamfer_argmin(np.array([[3]]), ref, s, T)[2]) == 1
+    assert len(compare.chamfer_argmin(np.array([[4]]), ref, s, T)[2]) == 1
     assert compare.chamfer_argmin(ref, ref, s, T)[:2] == (0, 0)
+
+
+def _fp32_direct_nn(A, T):
+    """Nearest neighbours with every operation in fp32, direct form, in the
+    order (dx*dx + dy*dy) + dz*dz: the evaluation the comparator's bounds are
+    derived for (any order or fusion is covered)."""
+    A32, T32 = A.astype(np.float32), T.astype(np.float32)
+    diff = A32[:, :, None, :] - T32[:, None, :, :]
+    sq = diff * diff
+    v = (sq[..., 0] + sq[..., 1]) + sq[..., 2]
+    idx = np.argmin(v, axis=2)
+    return np.take_along_axis(v, idx[..., None], 2)[..., 0], idx
+
+
+def test_chamfer_comparator_accepts_fp32_direct_form(oracle_mod):
+    """An fp32 direct-form evaluation passes every Chamfer rule against the
+    fp64 oracle, on clouds with near ties (targets duplicated with one-ulp
+    moves) and far from the origin; a 1 % distance error, a loss 1 % off and
+    a gradient 1 % off fail."""
+    from oracle import compare
+    rng = np.random.default_rng(785)
+    P = (rng.standard_normal((2, 300, 3)) * 0.3 + [40.0, -7.0, 3.0]).astype(np.float32)
+    base = (rng.standard_normal((2, 200, 3)) * 0.3 + [40.0, -7.0, 3.0]).astype(np.float32)
+    nudged = np.nextafter(base, np.float32(np.inf))
+    Q = np.concatenate([base, nudged], axis=1)
+    d1, i1, d2, i2, loss = oracle_mod.chamfer_fwd(P, Q)
+    P64, Q64 = P.astype(np.float64), Q.astype(np.float64)
+    for A, T, rd, ri in ((P64, Q64, d1, i1), (Q64, P64, d2, i2)):
+        gd, gi = _fp32_direct_nn(A, T)
+        assert compare.chamfer_argmin(gi, ri, A, T)[2] == []
+        assert compare.chamfer_dist(gd, rd)[0]
+        assert compare.chamfer_dist_at_index(gd, gi, A, T)[0]
+        assert not compare.chamfer_dist(gd * 1.01, rd)[0]
+        assert not compare.chamfer_dist_at_index(gd * 1.01, gi, A, T)[0]
+    # exact coincidence must come out exactly 0
+    assert not compare.chamfer_dist(np.array([[1e-30]]), np.array([[0.0]]))[0]
+    # loss: the fp32 sum of fp32 distances meets the tolerance, 1 % off does not
+    gd1, _ = _fp32_direct_nn(P64, Q64)
+    gd2, _ = _fp32_direct_nn(Q64, P64)
+    l32 = gd1.sum(1, dtype=np.float32) / np.float32(300) + gd2.sum(1, dtype=np.float32) / np.float32(400)
+    tol = compare.chamfer_loss_tol(400)  # a sequential fp32 sum of up to 400 terms
+    assert np.all(np.abs(l32 - loss) <= tol * loss)
+    assert not np.all(np.abs(1.01 * l32 - loss) <= tol * loss)
+    # gradients: fp32 terms summed in fp32 pass; a 1 % error fails
+    g1 = rng.standard_normal((2, 300))
+    g2 = rng.standard_normal((2, 400))
+    dP, dQ, *_ = oracle_mod.chamfer_bwd(P, Q, i1, i2, g1, g2)
+    S, n = compare.chamfer_grad_bounds(P64, Q64, i1, i2, g1, g2)
+    assert compare.chamfer_grad(dP, dP, S, n)[0]
+    P32, Q32, g132, g232 = P, Q, g1.astype(np.float32), g2.astype(np.float32)
+    b = np.arange(2)[:, None]
+    dP32 = np.float32(2) * g132[..., None] * (P32 - Q32[b, i1])
+    for bb in range(2):
+        for q in range(400):
+            p = i2[bb, q]
+            dP32[bb, p] += np.float32(2) * g232[bb, q] * (P32[bb, p] - Q32[bb, q])
+    g1r = g132.astype(np.float64)
+    g2r = g232.astype(np.float64)
+    dPr, _, *_ = oracle_mod.chamfer_bwd(P, Q, i1, i2, g1r, g2r)
+    S, n = compare.chamfer_grad_bounds(P64, Q64, i1, i2, g1r, g2r)
+    assert compare.chamfer_grad(dP32, dPr, S, n)[0]
+    assert not compare.chamfer_grad(dP32 * 1.01, dPr, S, n)[0]
+
+
+@pytest.mark.slow
+def test_int8_long_query_expectation_is_the_oracles(oracle_mod):
+    """The stored expectation of the long-query INT8 workload
+    (tests/golden/make_int8_long_query.py) still describes the generated
+    inputs, and its first argmax block, scores and fp32 scores of those docs
+    are the oracle's."""
+    import hashlib
+    import json
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "int8_long_query_expected.json")
+    with open(path) as f:
+        exp = json.load(f)
+    w = synth.int8_long_query()
+    assert hashlib.sha256(w.D.numpy().tobytes()).hexdigest() == exp["inputs_sha256"]["D"]
+    assert hashlib.sha256(w.Q.numpy().tobytes()).hexdigest() == exp["inputs_sha256"]["Q"]
+    blk = exp["argmax_block"]
+    si, sf, a = oracle_mod.fwd_i8(w.Q, w.q_scale, w.D[:blk], w.d_scale, want_argmax=True)
+    assert list(si[0]) == exp["scores_i32"][:blk]
+    rf = np.frombuffer(bytes.fromhex(exp["scores_f32_hex"]), dtype="<f4")
+    assert np.array_equal(sf[0].astype(np.float32), rf[:blk])
+    d = hashlib.sha256(np.ascontiguousarray(a, dtype="<i4")[0].tobytes()).hexdigest()[:16]
+    assert d == exp["argmax_block_digests"][0]
