@@ -31,10 +31,14 @@
  *     nothing. Device-data contents (mask bytes in {0,1}, monotone offsets,
  *     argmax in [0, Ld), int8 values != -128, finite float inputs: no NaN or
  *     Inf in Q, D or grad_scores) are preconditions: breaking them gives
- *     unspecified values, never an out-of-bounds access.
+ *     unspecified values, never an out-of-bounds access, with one exception:
+ *     the packed forwards (maxsim_fwd_varlen, maxsim_fwd_pairs_varlen) take
+ *     no packed row counts, so they read the rows cu_q and cu_d name, and
+ *     offsets past the packed tensors read out of bounds.
  *   - Sizes of 0 are valid. Nq == 0 or Nd == 0 enqueues nothing.
- *   - Reductions run in a fixed order with no atomics: results are bitwise
- *     reproducible run to run.
+ *   - Reductions run in a fixed order and no result is written by an atomic
+ *     (the CSR and top-k builders count with LDS integer histograms only):
+ *     results are bitwise reproducible run to run.
  *   - Ties among equal maxima go to the lowest doc-token index.
  */
 #ifndef MAXSIM_H
@@ -258,12 +262,16 @@ maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
  *   loss[b]    = (1/N) sum_p dist1[b,p] + (1/M) sum_q dist2[b,q]
  *   P [B, N, 3], Q [B, M, 3] float32 (finite); dist1, idx1 [B, N] float32 /
  *   int32; dist2, idx2 [B, M]; loss [B] float32 or NULL.
- * Distances are evaluated in fp32 in the expanded form ||p||^2 + ||q||^2 -
- * 2<p,q> (the inner products on the matrix cores) of coordinates taken
- * relative to the batch's first point of the other set, and clamped at 0; an
- * index may differ from an exact evaluation's only among candidates within
- * that form's rounding bound. Sums run in a fixed order. B == 0 enqueues
- * nothing.
+ * Each distance is the fp32 direct form (dx*dx + dy*dy) + dz*dz of the
+ * raw coordinates at the index written beside it, and that index is one an
+ * fp32 direct-form evaluation could pick: its exact squared distance exceeds
+ * the exact minimum by at most gamma_5 (u = 2^-23) times their sum, ties
+ * going to the lowest index. (The search itself runs on the matrix cores in
+ * the expanded form; every candidate inside that form's rounding bound of
+ * the minimum is re-evaluated in the direct form, and a source with too many
+ * such candidates is decided by a direct-form scan of its whole target set.)
+ * The loss sums each set's distances in a fixed order whose rounding depth
+ * is at most ceil(n / 16384) + 25 additions. B == 0 enqueues nothing.
  * Errors: SHAPE (negative sizes; N == 0 or M == 0 with B > 0), NULL,
  * UNSUPPORTED (misaligned pointers), OVERFLOW (B*N or B*M >= 2^31).
  */

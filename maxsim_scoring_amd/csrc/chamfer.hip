@@ -4,22 +4,32 @@
 // min instead of the materialised [N, M] distance matrix; then the per-batch
 // loss (1/N) sum dist1 + (1/M) sum dist2 in a fixed order.
 //
-// Design: the pages obtain Chamfer from MaxSim by putting a squared distance
-// where the inner product was, so the distance tile is formed the same way,
-// as a contraction on the matrix cores: ||s - t||^2 = ||s||^2 + (||t||^2 -
-// 2 <s, t>), where the bracket is one v_mfma_f32_16x16x4_f32 per 16 x 16 tile
-// with the targets (tx, ty, tz, ||t||^2) as rows of A and the sources
-// (-2 sx, -2 sy, -2 sz, 1) as columns of B (K = 4, fp32 in and out). A lane
-// owns one source column and 4 target rows of each tile. Tiles go in pairs of
-// 16-target blocks; the lane folds its 8 values of a pair into its running
-// min and records, with a strict '<', the pair that last lowered it, so the
-// earliest pair keeps a tie. At the end it re-evaluates its 8 rows of that
-// pair and takes the lowest index with the smallest value. The 4 row groups
-// of a column are then merged by (value, index). ||s||^2 is added once at the
-// end (adding the same value to every candidate keeps their order); the
-// result is clamped at 0, since the expanded form can round a zero distance
-// slightly negative. All coordinates are first taken relative to the target
-// set's first point, so that rounding scales with the sets' extent.
+// Design: the search for the nearest point runs on the matrix cores. The pages
+// obtain Chamfer from MaxSim by putting a squared distance where the inner
+// product was, so the distance tile is formed as a contraction: ||s - t||^2 =
+// ||s||^2 + (||t||^2 - 2 <s, t>), where the bracket is one
+// v_mfma_f32_16x16x4_f32 per 16 x 16 tile with the targets (tx, ty, tz,
+// ||t||^2) as rows of A and the sources (-2 sx, -2 sy, -2 sz, 1) as columns of
+// B (K = 4, fp32 in and out). Coordinates are first taken relative to the
+// mean of the target set's first 64 points, so the rounding scales with the
+// sets' extent rather than their offset from the origin.
+//
+// The expanded form cancels: its rounding error is of the order of u |s'|^2,
+// far above that of the direct form sum_k (s_k - t_k)^2 when the nearest
+// distance is small. So the matrix-core pass only finds candidates, and the
+// answer is decided in the direct form: a lane owns one source column and 4
+// target rows of each tile, and per 256-target tile it folds its 64 values
+// into the tile's min. Two slots keep the tiles whose min lies within the
+// expanded form's rounding bound tau(b) of the running min b (the best tile
+// and one more); a third tile inside the window while both slots are still
+// inside it marks the source as overflowed. At the end every kept tile whose
+// min is within tau of the source's overall min (over the 4 lanes of the
+// column) is re-evaluated row by row in the direct form from the raw fp32
+// coordinates, and the smallest direct value wins, lowest index on ties. The
+// exact nearest point is always among the re-evaluated rows, so the returned
+// index is one a direct-form fp32 evaluation could return, and the distance
+// written is that evaluation. An overflowed source is written with index -1,
+// and chamfer_fix_kernel then scans its whole target set in the direct form.
 //
 // Every wave is its own workgroup and streams its own copy of the target set
 // through LDS in 256-point tiles (coalesced loads, prepared as
@@ -91,9 +101,23 @@ __device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (
 
 }  // namespace
 
+// Near-tie window of the matrix-core pass. For a source s' (coordinates
+// relative to the centring point) whose running min of the bracket
+// ||t'||^2 - 2 <s', t'> is b, a target t can still be the exact nearest point
+// only if its bracket is at most thr(b) = b + 2^-18 (18 |s'|^2 + 12 b). This
+// holds for any rounding with unit u <= 2^-23 of: the centring differences,
+// ||t'||^2 (two fused steps), and a 4-term fp32 dot product with any order of
+// its products and sums. For such a t the error of the bracket is at most
+// gamma_12 ((|s'| + |t'|)^2 + |s - t|^2) with |t'| <= |s'| + |s - t|, and the
+// window is twice that bound for both the true and the found minimum, written
+// with b + |s'|^2 in place of the distance.
+constexpr float kTauK = 1.0f + 12.0f * 0x1p-18f;
+constexpr float kTau0 = 18.0f * 0x1p-18f;
+
 // KN source blocks of one (batch, direction) segment against its whole
 // target set: A [na, 3] holds the sources, blocks k0 .. k0+KN-1; T [nt, 3]
-// the targets. Writes dist[sp] and idx[sp] for the blocks' points.
+// the targets. Writes dist[sp] and idx[sp] for the blocks' points, or
+// idx[sp] = -1 when the source's near-tie candidates overflowed.
 template <int KN>
 __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict__ A, int64_t na,
                                            const float* __restrict__ T, int64_t nt, int64_t k0,
@@ -102,22 +126,48 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
     const int lane = threadIdx.x;
     const int col = lane & 15, rg = lane >> 4;  // source column, target row group (= K index of A, B)
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    // both sets are taken relative to the target set's first point: the
-    // distances do not change, and the expanded form's rounding then scales
-    // with the sets' extent rather than their distance from the origin
-    const float cx = T[0], cy = T[1], cz = T[2];
-    const float crg = rg == 0 ? cx : (rg == 1 ? cy : cz);  // this lane's K component
+    // centring point: the mean of the target set's first (up to) 64 points.
+    // The butterfly sum gives every lane the same bits; the distances do not
+    // depend on it, only the expanded form's rounding does.
+    float cx, cy, cz;
+    {
+        const int m = (int)(nt < 64 ? nt : 64);
+        float x = 0.f, y = 0.f, z = 0.f;
+        if (lane < m) {
+            x = T[lane * 3];
+            y = T[lane * 3 + 1];
+            z = T[lane * 3 + 2];
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            x += __shfl_xor(x, o, 64);
+            y += __shfl_xor(y, o, 64);
+            z += __shfl_xor(z, o, 64);
+        }
+        const float inv = 1.0f / (float)m;
+        cx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x * inv)));
+        cy = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(y * inv)));
+        cz = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(z * inv)));
+    }
 
-    // this lane's source point of each block (clamped copies past the end)
-    float bop[KN], best[KN];
-    int bstep[KN];  // the 16-target block where best was last lowered
+    // per source of each block (clamped copies past the end): the B operand,
+    // the window constant, the running min and its tile, the second kept tile
+    float bop[KN], tau0[KN], best[KN], v1[KN];
+    int s0[KN], s1[KN];
+    bool ovf[KN];
 #pragma unroll
     for (int u = 0; u < KN; ++u) {
         int64_t sp = (k0 + u) * 16 + col;
         sp = sp < na ? sp : na - 1;
-        bop[u] = rg < 3 ? -2.f * (A[sp * 3 + (rg < 3 ? rg : 0)] - crg) : 1.f;
+        const float sx = A[sp * 3] - cx, sy = A[sp * 3 + 1] - cy, sz = A[sp * 3 + 2] - cz;
+        const float comp = rg == 0 ? sx : (rg == 1 ? sy : sz);
+        bop[u] = rg < 3 ? -2.f * comp : 1.f;
+        tau0[u] = kTau0 * __builtin_fmaf(sz, sz, __builtin_fmaf(sy, sy, sx * sx));
         best[u] = __builtin_inff();
-        bstep[u] = 0;
+        v1[u] = __builtin_inff();
+        s0[u] = 0;
+        s1[u] = 0;
+        ovf[u] = false;
     }
 
     const int64_t ntiles = (nt + kChTileT - 1) / kChTileT;
@@ -132,103 +182,210 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
         const int64_t left = nt - t0;
         const int tbs = __builtin_amdgcn_readfirstlane(left >= kChTileT ? kChTileT / 16 : (int)((left + 15) / 16));
         const float* tf = (const float*)&sm.tile[buf][0] + col * 4 + rg;  // A[row col][k rg] of block 0
-        const int step0 = (int)(t0 / 16);
-        // one 16-target block (or two): KN MFMAs per block sharing the A
-        // operand, then the running min of this lane's 4 rows per block and
-        // the first block of the step that last lowered it (strict '<': the
-        // earliest step keeps a tie)
-        auto block = [&](float aop, int step) {
-            f32x4 d[KN];
-#pragma unroll
-            for (int u = 0; u < KN; ++u) d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop[u], zero, 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < KN; ++u) {
-                const float m = __builtin_fminf(
-                    __builtin_fminf(__builtin_fminf(__builtin_fminf(d[u][0], d[u][1]), d[u][2]), d[u][3]), best[u]);
-                bstep[u] = m < best[u] ? step : bstep[u];
-                best[u] = m;
-            }
-        };
-        auto block2 = [&](float a0, float a1, int step) {
-            f32x4 d[KN], e[KN];
-            // MFMAs issued at raised priority (the SIMD's other waves yield
-            // the issue slots to the MFMA stream; about 6 % here)
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int u = 0; u < KN; ++u) d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bop[u], zero, 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < KN; ++u) e[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bop[u], zero, 0, 0, 0);
-            __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-            for (int u = 0; u < KN; ++u) {
-                const float x = __builtin_fminf(__builtin_fminf(d[u][0], d[u][1]), d[u][2]);
-                const float y = __builtin_fminf(__builtin_fminf(d[u][3], e[u][0]), e[u][1]);
-                const float z = __builtin_fminf(__builtin_fminf(e[u][2], e[u][3]), best[u]);
-                const float m = __builtin_fminf(__builtin_fminf(x, y), z);
-                bstep[u] = m < best[u] ? step : bstep[u];
-                best[u] = m;
-            }
-        };
+        // mp: this tile's min of the lane's rows, per source
+        float mp[KN];
         if (tbs == kChTileT / 16) {
             // a full tile: every block's operand is read up front, and the
-            // blocks go in pairs (one min update per pair)
+            // blocks go in pairs, the MFMAs issued at raised priority (the
+            // SIMD's other waves yield the issue slots to the MFMA stream)
             float av[kChTileT / 16];
 #pragma unroll
             for (int tb = 0; tb < kChTileT / 16; ++tb) av[tb] = tf[tb * 64];
 #pragma unroll
-            for (int tb = 0; tb < kChTileT / 16; tb += 2) block2(av[tb], av[tb + 1], step0 + tb);
+            for (int tb = 0; tb < kChTileT / 16; tb += 2) {
+                f32x4 d[KN], e[KN];
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int u = 0; u < KN; ++u) d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[tb], bop[u], zero, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < KN; ++u) e[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[tb + 1], bop[u], zero, 0, 0, 0);
+                __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+                for (int u = 0; u < KN; ++u) {
+                    const float x = __builtin_fminf(__builtin_fminf(d[u][0], d[u][1]), d[u][2]);
+                    const float y = __builtin_fminf(__builtin_fminf(d[u][3], e[u][0]), e[u][1]);
+                    if (tb == 0) {
+                        mp[u] = __builtin_fminf(__builtin_fminf(__builtin_fminf(e[u][2], e[u][3]), x), y);
+                    } else {
+                        const float z = __builtin_fminf(__builtin_fminf(e[u][2], e[u][3]), mp[u]);
+                        mp[u] = __builtin_fminf(__builtin_fminf(x, y), z);
+                    }
+                }
+            }
         } else {
-            for (int tb = 0; tb < tbs; ++tb) block(tf[tb * 64], step0 + tb);
+#pragma unroll
+            for (int u = 0; u < KN; ++u) mp[u] = __builtin_inff();
+            for (int tb = 0; tb < tbs; ++tb) {
+                const float aop = tf[tb * 64];
+#pragma unroll
+                for (int u = 0; u < KN; ++u) {
+                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop[u], zero, 0, 0, 0);
+                    mp[u] = __builtin_fminf(__builtin_fminf(__builtin_fminf(d[0], d[1]), __builtin_fminf(d[2], d[3])),
+                                            mp[u]);
+                }
+            }
+        }
+        // the two kept tiles: a tile inside the window of the running min is
+        // kept; a lower tile becomes the best and the old best the second; a
+        // third tile inside the window while the second is still inside it
+        // overflows. Equal mins keep the earlier tile as the best.
+        const int step = (int)it;
+#pragma unroll
+        for (int u = 0; u < KN; ++u) {
+            const float thr_old = __builtin_fmaf(best[u], kTauK, tau0[u]);
+            const bool near = mp[u] <= thr_old;
+            const bool lower = mp[u] < best[u];
+            const float bn = __builtin_fminf(best[u], mp[u]);
+            const float thr_new = __builtin_fmaf(bn, kTauK, tau0[u]);
+            ovf[u] = ovf[u] | (near & (v1[u] <= thr_new));  // bitwise: no branches
+            v1[u] = near ? __builtin_fmaxf(best[u], mp[u]) : v1[u];
+            s1[u] = near ? (lower ? s0[u] : step) : s1[u];
+            s0[u] = lower ? step : s0[u];
+            best[u] = bn;
         }
         if (it + 1 < ntiles) cham_prepare(sm, buf ^ 1, raw, nt, t0 + kChTileT, lane, cx, cy, cz);
     }
 
-    // the row of the recorded step: among this lane's rows of the step's
-    // first block and the block after it (8 targets), the lowest index whose
-    // value, evaluated again in the same form on the VALU, is smallest. A row
-    // of the later block can only tie the recorded min (a smaller value would
-    // have been recorded as a later step), and since the MFMA's own rounding
-    // is not reproduced, a row inside a near tie may be taken, within the
-    // evaluation bound. Then the 4 row groups of each column are merged by
-    // (value, index) and written
+    // the answer in the direct form: the kept tiles inside the window of the
+    // source's overall min are re-evaluated on this lane's rows from the raw
+    // coordinates; the smallest value wins, the lowest index on ties, then
+    // the 4 row groups of the column are merged the same way
 #pragma unroll
     for (int u = 0; u < KN; ++u) {
         int64_t sp = (k0 + u) * 16 + col;
         const bool own = sp < na;
         sp = own ? sp : na - 1;
-        const float sx = A[sp * 3] - cx, sy = A[sp * 3 + 1] - cy, sz = A[sp * 3 + 2] - cz;
-        const int64_t tbase = (int64_t)bstep[u] * 16 + 4 * rg;
-        int i = (int)(tbase < nt ? tbase : nt - 1);
-        float rv = __builtin_inff();
+        const float px = A[sp * 3], py = A[sp * 3 + 1], pz = A[sp * 3 + 2];
+        float bs = best[u];
+        bs = __builtin_fminf(bs, __shfl_xor(bs, 16, 64));
+        bs = __builtin_fminf(bs, __shfl_xor(bs, 32, 64));
+        const float thr = __builtin_fmaf(bs, kTauK, tau0[u]);
+        int lost = (ovf[u] & (best[u] <= thr)) ? 1 : 0;
+        lost |= __shfl_xor(lost, 16, 64);
+        lost |= __shfl_xor(lost, 32, 64);
+        float dv = __builtin_inff();
+        int di = 0x7fffffff;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t t = tbase + (r < 4 ? r : 12 + r);
-            if (t < nt) {
-                const float tx = T[t * 3] - cx, ty = T[t * 3 + 1] - cy, tz = T[t * 3 + 2] - cz;
-                const float n2 = __builtin_fmaf(tz, tz, __builtin_fmaf(ty, ty, tx * tx));
-                const float v =
-                    __builtin_fmaf(-2.f * sz, tz, __builtin_fmaf(-2.f * sy, ty, __builtin_fmaf(-2.f * sx, tx, n2)));
-                if (v < rv) {
-                    rv = v;
-                    i = (int)t;
+        for (int slot = 0; slot < 2; ++slot) {
+            const bool keep = slot == 0 ? best[u] <= thr : v1[u] <= thr;
+            if (keep) {
+                const int64_t tb = (int64_t)(slot == 0 ? s0[u] : s1[u]) * kChTileT + 4 * rg;
+#pragma unroll 2
+                for (int k = 0; k < kChTileT / 16; ++k) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t t = tb + 16 * k + r;
+                        if (t < nt) {
+                            const float dx = px - T[t * 3], dy = py - T[t * 3 + 1], dz = pz - T[t * 3 + 2];
+                            const float v = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+                            if (v < dv || (v == dv && (int)t < di)) {
+                                dv = v;
+                                di = (int)t;
+                            }
+                        }
+                    }
                 }
             }
         }
-        float v = best[u];
 #pragma unroll
         for (int x = 16; x <= 32; x <<= 1) {
-            const float ov = __shfl_xor(v, x, 64);
-            const int oi = __shfl_xor(i, x, 64);
-            if (ov < v || (ov == v && oi < i)) {
-                v = ov;
-                i = oi;
+            const float ov = __shfl_xor(dv, x, 64);
+            const int oi = __shfl_xor(di, x, 64);
+            if (ov < dv || (ov == dv && oi < di)) {
+                dv = ov;
+                di = oi;
             }
         }
         if (rg == 0 && own) {
-            const float dd = __builtin_fmaf(sz, sz, __builtin_fmaf(sy, sy, sx * sx)) + v;
-            dist[sp] = dd > 0.f ? dd : 0.f;
-            idx[sp] = i;
+            if (lost) {
+                idx[sp] = -1;
+            } else {
+                dist[sp] = dv;
+                idx[sp] = di;
+            }
         }
+    }
+}
+
+// Sources whose near-tie candidates overflowed (index -1): the whole target
+// set in the direct form, the smallest value and the lowest index among equal
+// ones. A workgroup checks kFixThreads consecutive sources of the list
+// [dist1 | dist2] and treats each overflowed one with all its threads.
+constexpr int kFixThreads = 256;
+__global__ __launch_bounds__(kFixThreads) void chamfer_fix_kernel(ChamferArgs a)
+{
+    __shared__ int flag[kFixThreads];
+    __shared__ float wv[kFixThreads / 64];
+    __shared__ int wi[kFixThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t n1 = a.B * a.N, ntot = n1 + a.B * a.M;
+    const int64_t g0 = (int64_t)blockIdx.x * kFixThreads;
+    {
+        const int64_t g = g0 + tid;
+        int f = 0;
+        if (g < ntot) f = (g < n1 ? a.idx1[g] : a.idx2[g - n1]) < 0;
+        flag[tid] = f;
+    }
+    cham_barrier();
+    for (int f = 0; f < kFixThreads; ++f) {
+        if (!flag[f]) continue;  // the same for every thread
+        const int64_t gs = g0 + f;
+        const bool second = gs >= n1;
+        const int64_t gl = second ? gs - n1 : gs;
+        const int64_t na = second ? a.M : a.N, nt = second ? a.N : a.M;
+        const int64_t b = gl / na;
+        const float* S = (second ? a.Q : a.P) + gl * 3;
+        const float* T = (second ? a.P : a.Q) + b * nt * 3;
+        const float px = S[0], py = S[1], pz = S[2];
+        float dv = __builtin_inff();
+        int di = 0x7fffffff;
+        // ascending targets per thread with a strict '<': the lowest index of
+        // a tie stays; four loads in flight
+        for (int64_t t = tid; t < nt; t += 4 * kFixThreads) {
+            float x[4], y[4], z[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int64_t q = t + (int64_t)j * kFixThreads;
+                q = q < nt ? q : nt - 1;
+                x[j] = T[q * 3];
+                y[j] = T[q * 3 + 1];
+                z[j] = T[q * 3 + 2];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t q = t + (int64_t)j * kFixThreads;
+                const float dx = px - x[j], dy = py - y[j], dz = pz - z[j];
+                const float v = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+                if (q < nt && v < dv) {
+                    dv = v;
+                    di = (int)q;
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(dv, o, 64);
+            const int oi = __shfl_xor(di, o, 64);
+            if (ov < dv || (ov == dv && oi < di)) {
+                dv = ov;
+                di = oi;
+            }
+        }
+        if (lane == 0) {
+            wv[w] = dv;
+            wi[w] = di;
+        }
+        cham_barrier();
+        if (tid == 0) {
+            for (int k = 1; k < kFixThreads / 64; ++k)
+                if (wv[k] < dv || (wv[k] == dv && wi[k] < di)) {
+                    dv = wv[k];
+                    di = wi[k];
+                }
+            (second ? a.dist2 : a.dist1)[gl] = dv;
+            (second ? a.idx2 : a.idx1)[gl] = di;
+        }
+        cham_barrier();
     }
 }
 
@@ -334,6 +491,10 @@ hipError_t launch_chamfer_fwd(ChamferArgs a, hipStream_t stream)
     if (waves > nblocks) waves = nblocks;
     if (waves > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(chamfer_nn_kernel, dim3((unsigned)waves), dim3(64), 0, stream, a, nblocks);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t nsrc = a.B * (a.N + a.M);
+    hipLaunchKernelGGL(chamfer_fix_kernel, dim3((unsigned)((nsrc + kFixThreads - 1) / kFixThreads)),
+                       dim3(kFixThreads), 0, stream, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.loss) {
         hipLaunchKernelGGL(chamfer_loss_kernel, dim3((unsigned)a.B), dim3(kLossThreads), 0, stream, a.dist1,
