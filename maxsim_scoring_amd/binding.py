@@ -88,6 +88,30 @@ def _dev(name: str, t: Optional[torch.Tensor], dtype=None) -> None:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _out(name: str, t: Optional[torch.Tensor], dtype, shape) -> None:
+    """An output the caller passed in: on the GPU, contiguous, of `dtype` and
+    exactly the documented `shape` (the kernels write every element of it)."""
+    if t is None:
+        return
+    _dev(name, t, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
+def _out_flat(name: str, t: torch.Tensor, dtype, n: int) -> None:
+    """A flat output of n elements; with n == 0 a placeholder of at most one
+    element is accepted (the default allocation keeps one)."""
+    _dev(name, t, dtype)
+    if t.dim() != 1 or (t.numel() != n if n > 0 else t.numel() > 1):
+        raise ValueError(f"{name} must have shape [{n}], got {list(t.shape)}")
+
+
+def _mask(name: str, t: Optional[torch.Tensor], shape) -> None:
+    _dev(name, t, torch.uint8)
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -118,18 +142,14 @@ def maxsim_fwd(Q: torch.Tensor, D: torch.Tensor, q_mask: Optional[torch.Tensor] 
         raise ValueError("Q and D must share d and dtype")
     _dev("Q", Q)
     _dev("D", D)
-    _dev("q_mask", q_mask, torch.uint8)
-    _dev("d_mask", d_mask, torch.uint8)
-    if q_mask is not None and tuple(q_mask.shape) != (Nq, Lq):
-        raise ValueError("q_mask must be [Nq, Lq]")
-    if d_mask is not None and tuple(d_mask.shape) != (Nd, Ld):
-        raise ValueError("d_mask must be [Nd, Ld]")
+    _mask("q_mask", q_mask, (Nq, Lq))
+    _mask("d_mask", d_mask, (Nd, Ld))
     if scores is None:
         scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
     if argmax is None and want_argmax:
         argmax = torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=Q.device)
-    _dev("scores", scores, torch.float32)
-    _dev("argmax", argmax, torch.int32)
+    _out("scores", scores, torch.float32, (Nq, Nd))
+    _out("argmax", argmax, torch.int32, (Nq, Nd, Lq))
     st = lib().maxsim_fwd(_dtype_code(Q), _p(Q), _p(D), Nq, Nd, Lq, Ld, d, _p(q_mask), _p(d_mask),
                           _p(scores), _p(argmax), _stream(stream))
     _check("maxsim_fwd", st)
@@ -149,13 +169,15 @@ def maxsim_fwd_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D: torch
         _dev(n, t)
     _dev("cu_q", cu_q, torch.int32)
     _dev("cu_d", cu_d, torch.int32)
+    if cu_q.dim() != 1 or cu_d.dim() != 1:
+        raise ValueError("cu_q and cu_d must be [N+1]")
     Nq, Nd = cu_q.numel() - 1, cu_d.numel() - 1
     if scores is None:
         scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
     if argmax is None and want_argmax:
         argmax = torch.empty((Nq, Nd, max_lq), dtype=torch.int32, device=Q.device)
-    _dev("scores", scores, torch.float32)
-    _dev("argmax", argmax, torch.int32)
+    _out("scores", scores, torch.float32, (Nq, Nd))
+    _out("argmax", argmax, torch.int32, (Nq, Nd, max_lq))
     st = lib().maxsim_fwd_varlen(_dtype_code(Q), _p(Q), _p(cu_q), Nq, int(max_lq), _p(D),
                                  _p(cu_d), Nd, d, _p(scores), _p(argmax), _stream(stream))
     _check("maxsim_fwd_varlen", st)
@@ -174,8 +196,8 @@ def maxsim_fwd_i8(Q: torch.Tensor, q_scale: float, D: torch.Tensor, d_scale: flo
         raise ValueError("Q and D must share d")
     _dev("Q", Q, torch.int8)
     _dev("D", D, torch.int8)
-    _dev("q_mask", q_mask, torch.uint8)
-    _dev("d_mask", d_mask, torch.uint8)
+    _mask("q_mask", q_mask, (Nq, Lq))
+    _mask("d_mask", d_mask, (Nd, Ld))
     dev = Q.device
     if scores_i32 is None and want_int:
         scores_i32 = torch.empty((Nq, Nd), dtype=torch.int32, device=dev)
@@ -183,9 +205,9 @@ def maxsim_fwd_i8(Q: torch.Tensor, q_scale: float, D: torch.Tensor, d_scale: flo
         scores = torch.empty((Nq, Nd), dtype=torch.float32, device=dev)
     if argmax is None and want_argmax:
         argmax = torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=dev)
-    _dev("scores_i32", scores_i32, torch.int32)
-    _dev("scores", scores, torch.float32)
-    _dev("argmax", argmax, torch.int32)
+    _out("scores_i32", scores_i32, torch.int32, (Nq, Nd))
+    _out("scores", scores, torch.float32, (Nq, Nd))
+    _out("argmax", argmax, torch.int32, (Nq, Nd, Lq))
     st = lib().maxsim_fwd_i8(_p(Q), float(q_scale), _p(D), float(d_scale), Nq, Nd, Lq, Ld, d,
                              _p(q_mask), _p(d_mask), _p(scores_i32), _p(scores), _p(argmax),
                              _stream(stream))
@@ -207,8 +229,8 @@ def maxsim_bwd(Q: torch.Tensor, D: torch.Tensor, argmax: torch.Tensor, grad_scor
     _dev("D", D)
     _dev("argmax", argmax, torch.int32)
     _dev("grad_scores", grad_scores, torch.float32)
-    _dev("q_mask", q_mask, torch.uint8)
-    _dev("d_mask", d_mask, torch.uint8)
+    _mask("q_mask", q_mask, (Nq, Lq))
+    _mask("d_mask", d_mask, (Nd, Ld))
     if tuple(argmax.shape) != (Nq, Nd, Lq) or tuple(grad_scores.shape) != (Nq, Nd):
         raise ValueError("argmax must be [Nq,Nd,Lq] and grad_scores [Nq,Nd]")
     dev = Q.device
@@ -220,10 +242,10 @@ def maxsim_bwd(Q: torch.Tensor, D: torch.Tensor, argmax: torch.Tensor, grad_scor
         csr_row_ptr = torch.empty((Nd * Ld + 1,), dtype=torch.int32, device=dev)
     if csr_col_idx is None:
         csr_col_idx = torch.empty((max(1, Nq * Nd * Lq),), dtype=torch.int32, device=dev)
-    for n, t in (("dQ", dQ), ("dD", dD)):
-        _dev(n, t, torch.float32)
-    for n, t in (("csr_row_ptr", csr_row_ptr), ("csr_col_idx", csr_col_idx)):
-        _dev(n, t, torch.int32)
+    _out("dQ", dQ, torch.float32, (Nq, Lq, d))
+    _out("dD", dD, torch.float32, (Nd, Ld, d))
+    _out("csr_row_ptr", csr_row_ptr, torch.int32, (Nd * Ld + 1,))
+    _out_flat("csr_col_idx", csr_col_idx, torch.int32, Nq * Nd * Lq)
     st = lib().maxsim_bwd(_dtype_code(Q), _p(Q), _p(D), Nq, Nd, Lq, Ld, d, _p(q_mask), _p(d_mask),
                           _p(argmax), _p(grad_scores), _p(dQ), _p(dD), _p(csr_row_ptr),
                           _p(csr_col_idx), _stream(stream))
@@ -251,8 +273,8 @@ def maxsim_fwd_pairs_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D:
         scores = torch.empty((P,), dtype=torch.float32, device=Q.device)
     if argmax is None and want_argmax:
         argmax = torch.empty((P, max_lq), dtype=torch.int32, device=Q.device)
-    _dev("scores", scores, torch.float32)
-    _dev("argmax", argmax, torch.int32)
+    _out("scores", scores, torch.float32, (P,))
+    _out("argmax", argmax, torch.int32, (P, max_lq))
     st = lib().maxsim_fwd_pairs_varlen(_dtype_code(Q), _p(Q), _p(cu_q), Nq, int(max_lq), _p(D),
                                        _p(cu_d), Nd, d, _p(pair_q), _p(pair_d), P, _p(scores),
                                        _p(argmax), _stream(stream))
@@ -290,10 +312,10 @@ def maxsim_bwd_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D: torch
         csr_row_ptr = torch.empty((Td + 1,), dtype=torch.int32, device=dev)
     if csr_col_idx is None:
         csr_col_idx = torch.empty((max(1, Tq * Nd),), dtype=torch.int32, device=dev)
-    for n, t in (("dQ", dQ), ("dD", dD)):
-        _dev(n, t, torch.float32)
-    for n, t in (("csr_row_ptr", csr_row_ptr), ("csr_col_idx", csr_col_idx)):
-        _dev(n, t, torch.int32)
+    _out("dQ", dQ, torch.float32, (Tq, d))
+    _out("dD", dD, torch.float32, (Td, d))
+    _out("csr_row_ptr", csr_row_ptr, torch.int32, (Td + 1,))
+    _out_flat("csr_col_idx", csr_col_idx, torch.int32, Tq * Nd)
     st = lib().maxsim_bwd_varlen(_dtype_code(Q), _p(Q), _p(cu_q), Nq, Tq, int(max_lq), _p(D),
                                  _p(cu_d), Nd, Td, d, _p(argmax), _p(grad_scores), _p(dQ), _p(dD),
                                  _p(csr_row_ptr), _p(csr_col_idx), _stream(stream))
@@ -377,14 +399,14 @@ def maxsim_fwd_i8_tok(Q: torch.Tensor, q_scale: torch.Tensor, D: torch.Tensor,
     _dev("d_scale", d_scale, torch.float32)
     if tuple(q_scale.shape) != (Nq, Lq) or tuple(d_scale.shape) != (Nd, Ld):
         raise ValueError("scales must be [Nq, Lq] and [Nd, Ld]")
-    _dev("q_mask", q_mask, torch.uint8)
-    _dev("d_mask", d_mask, torch.uint8)
+    _mask("q_mask", q_mask, (Nq, Lq))
+    _mask("d_mask", d_mask, (Nd, Ld))
     if scores is None:
         scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
     if argmax is None and want_argmax:
         argmax = torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=Q.device)
-    _dev("scores", scores, torch.float32)
-    _dev("argmax", argmax, torch.int32)
+    _out("scores", scores, torch.float32, (Nq, Nd))
+    _out("argmax", argmax, torch.int32, (Nq, Nd, Lq))
     st = lib().maxsim_fwd_i8_tok(_p(Q), _p(q_scale), _p(D), _p(d_scale), Nq, Nd, Lq, Ld, d,
                                  _p(q_mask), _p(d_mask), _p(scores), _p(argmax), _stream(stream))
     _check("maxsim_fwd_i8_tok", st)
@@ -409,14 +431,14 @@ def maxsim_fwd_pairs(Q: torch.Tensor, D: torch.Tensor, pair_q: torch.Tensor,
     P = pair_q.numel()
     if pair_d.numel() != P:
         raise ValueError("pair_q and pair_d must have the same length")
-    _dev("q_mask", q_mask, torch.uint8)
-    _dev("d_mask", d_mask, torch.uint8)
+    _mask("q_mask", q_mask, (Nq, Lq))
+    _mask("d_mask", d_mask, (Nd, Ld))
     if scores is None:
         scores = torch.empty((P,), dtype=torch.float32, device=Q.device)
     if argmax is None and want_argmax:
         argmax = torch.empty((P, Lq), dtype=torch.int32, device=Q.device)
-    _dev("scores", scores, torch.float32)
-    _dev("argmax", argmax, torch.int32)
+    _out("scores", scores, torch.float32, (P,))
+    _out("argmax", argmax, torch.int32, (P, Lq))
     st = lib().maxsim_fwd_pairs(_dtype_code(Q), _p(Q), _p(D), Nq, Nd, Lq, Ld, d, _p(q_mask),
                                 _p(d_mask), _p(pair_q), _p(pair_d), P, _p(scores), _p(argmax),
                                 _stream(stream))
@@ -445,9 +467,9 @@ def maxsim_topk(scores: torch.Tensor, k: int, ids: Optional[torch.Tensor] = None
         val = torch.empty((Nq, k), dtype=torch.float32, device=scores.device)
     if rows is None and want_rows:
         rows = torch.empty((Nq, k), dtype=torch.int32, device=scores.device)
-    _dev("idx", idx, torch.int32)
-    _dev("val", val, torch.float32)
-    _dev("rows", rows, torch.int32)
+    _out("idx", idx, torch.int32, (Nq, k))
+    _out("val", val, torch.float32, (Nq, k))
+    _out("rows", rows, torch.int32, (Nq, k))
     st = lib().maxsim_topk(_p(scores), Nq, Nd, k, _p(ids), _p(idx), _p(val), _p(rows),
                            _stream(stream))
     _check("maxsim_topk", st)

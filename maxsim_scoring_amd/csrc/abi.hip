@@ -566,7 +566,7 @@ const char* maxsim_status_string(maxsim_status_t s)
     case MAXSIM_OK: return "ok";
     case MAXSIM_ERR_NULL: return "a required pointer is NULL";
     case MAXSIM_ERR_SHAPE: return "negative or inconsistent sizes";
-    case MAXSIM_ERR_UNSUPPORTED: return "unsupported dtype or embedding width (d must be 128)";
+    case MAXSIM_ERR_UNSUPPORTED: return "unsupported: d outside 1..1024, an unknown dtype, or a misaligned pointer";
     case MAXSIM_ERR_OVERFLOW: return "sizes overflow the int32 index range or the int32 sum";
     case MAXSIM_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";

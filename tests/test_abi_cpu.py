@@ -274,3 +274,81 @@ def test_binding_refuses_cpu_tensors():
     Q = torch.zeros((1, 4, 128), dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU tensor"):
         ms.maxsim_fwd(Q, Q)
+
+
+class _FakeGpuTensor:
+    """Stands in for a contiguous GPU tensor on a machine without a GPU: the
+    binding's layout checks read only these attributes, and every case below
+    fails a check before the library is called."""
+
+    def __init__(self, shape, dtype):
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.is_cuda = True
+        self.device = "cuda:0"
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return len(self.shape)
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+
+def test_binding_rejects_outputs_and_masks_of_the_wrong_shape():
+    """Every output a caller passes in must have exactly the documented shape,
+    and every mask must be [N, L]: an undersized buffer would let the kernels
+    write past it."""
+    import torch
+    from maxsim_scoring_amd import binding as b
+
+    def T(*shape, dtype=torch.float32):
+        return _FakeGpuTensor(shape, dtype)
+
+    bf, i32, u8, i8 = torch.bfloat16, torch.int32, torch.uint8, torch.int8
+    Q, D = T(2, 4, 128, dtype=bf), T(3, 5, 128, dtype=bf)
+    am, g = T(2, 3, 4, dtype=i32), T(2, 3)
+    cases = [
+        lambda: b.maxsim_fwd(Q, D, scores=T(2, 2)),
+        lambda: b.maxsim_fwd(Q, D, scores=T(2, 3), argmax=T(2, 3, 3, dtype=i32)),
+        lambda: b.maxsim_fwd(Q, D, q_mask=T(2, 5, dtype=u8), scores=T(2, 3)),
+        lambda: b.maxsim_bwd(Q, D, am, g, dQ=T(2, 4, 127), dD=T(3, 5, 128), csr_row_ptr=T(16, dtype=i32),
+                             csr_col_idx=T(24, dtype=i32)),
+        lambda: b.maxsim_bwd(Q, D, am, g, dQ=T(2, 4, 128), dD=T(3, 4, 128), csr_row_ptr=T(16, dtype=i32),
+                             csr_col_idx=T(24, dtype=i32)),
+        lambda: b.maxsim_bwd(Q, D, am, g, dQ=T(2, 4, 128), dD=T(3, 5, 128), csr_row_ptr=T(15, dtype=i32),
+                             csr_col_idx=T(24, dtype=i32)),
+        lambda: b.maxsim_bwd(Q, D, am, g, dQ=T(2, 4, 128), dD=T(3, 5, 128), csr_row_ptr=T(16, dtype=i32),
+                             csr_col_idx=T(23, dtype=i32)),
+        lambda: b.maxsim_bwd(Q, D, am, g, q_mask=T(2, 3, dtype=u8), dQ=T(2, 4, 128), dD=T(3, 5, 128),
+                             csr_row_ptr=T(16, dtype=i32), csr_col_idx=T(24, dtype=i32)),
+        lambda: b.maxsim_bwd(Q, D, am, g, d_mask=T(3, 6, dtype=u8), dQ=T(2, 4, 128), dD=T(3, 5, 128),
+                             csr_row_ptr=T(16, dtype=i32), csr_col_idx=T(24, dtype=i32)),
+        lambda: b.maxsim_fwd_i8(T(2, 4, 128, dtype=i8), 1.0, T(3, 5, 128, dtype=i8), 1.0,
+                                q_mask=T(4, 2, dtype=u8), scores_i32=T(2, 3, dtype=i32), scores=T(2, 3)),
+        lambda: b.maxsim_fwd_i8(T(2, 4, 128, dtype=i8), 1.0, T(3, 5, 128, dtype=i8), 1.0,
+                                scores_i32=T(1, 3, dtype=i32), scores=T(2, 3)),
+        lambda: b.maxsim_fwd_i8_tok(T(2, 4, 128, dtype=i8), T(2, 4), T(3, 5, 128, dtype=i8), T(3, 5),
+                                    d_mask=T(3, 4, dtype=u8), scores=T(2, 3)),
+        lambda: b.maxsim_fwd_varlen(T(8, 128, dtype=bf), T(3, dtype=i32), 4, T(9, 128, dtype=bf),
+                                    T(4, dtype=i32), scores=T(2, 2)),
+        lambda: b.maxsim_fwd_varlen(T(8, 128, dtype=bf), T(3, dtype=i32), 4, T(9, 128, dtype=bf),
+                                    T(4, dtype=i32), scores=T(2, 3), argmax=T(2, 3, 3, dtype=i32)),
+        lambda: b.maxsim_bwd_varlen(T(8, 128, dtype=bf), T(3, dtype=i32), 4, T(9, 128, dtype=bf),
+                                    T(4, dtype=i32), T(2, 3, 4, dtype=i32), T(2, 3), dQ=T(8, 128),
+                                    dD=T(8, 128), csr_row_ptr=T(10, dtype=i32), csr_col_idx=T(24, dtype=i32)),
+        lambda: b.maxsim_fwd_pairs(Q, D, T(6, dtype=i32), T(6, dtype=i32), scores=T(5)),
+        lambda: b.maxsim_fwd_pairs_varlen(T(8, 128, dtype=bf), T(3, dtype=i32), 4, T(9, 128, dtype=bf),
+                                          T(4, dtype=i32), T(6, dtype=i32), T(6, dtype=i32), scores=T(6),
+                                          argmax=T(6, 3, dtype=i32)),
+        lambda: b.maxsim_topk(T(2, 50), 10, idx=T(2, 9, dtype=i32), val=T(2, 10)),
+        lambda: b.maxsim_topk(T(2, 50), 10, idx=T(2, 10, dtype=i32), val=T(2, 10), rows=T(10, dtype=i32)),
+    ]
+    for k, call in enumerate(cases):
+        with pytest.raises(ValueError):
+            call()
