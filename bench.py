@@ -8,10 +8,18 @@ resident in HBM. The other workloads of the pages (tiny cross-product,
 ColPali cross-product, INT8 long query, backward at ColPali shapes) are timed
 in the same run and reported under "per_config".
 
+Each workload runs in a child process of its own (a kernel fault poisons only
+that process's context); the parent never touches the GPU. Every timing
+starts after the W warm-up launches and, beyond them, at least --min-warmup-s
+seconds of launches, so the part's clocks have settled before the timed
+region.
+
 The oracle (the plain CPU implementation) is timed on a bounded sample of the
-headline workload on this host's cores and reported as "cpu_baseline".
+headline workload on this host's cores and reported as "cpu_baseline"; the
+tiny, ColPali, INT8 and backward workloads report their own oracle samples.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+       python bench.py --child NAME ...   (one workload in this process)
 """
 
 from __future__ import annotations
@@ -21,6 +29,7 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -59,15 +68,34 @@ def kernel_source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+MIN_WARMUP_S = 1.0  # set from --min-warmup-s
+WARMUP_LOG = []      # (launches, seconds) of each warm-up in this process
+
+
+def warm_up(torch, fn, warmup: int) -> None:
+    """W launches, then more until at least MIN_WARMUP_S seconds of launches
+    have run (the clocks ramp up under load), all outside any timed region."""
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(warmup):
+        fn()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        for _ in range(16):
+            fn()
+        n += 16
+        torch.cuda.synchronize()
+    WARMUP_LOG.append((n, round(time.perf_counter() - t0, 3)))
+
+
 def time_steps(torch, fn, steps: int, warmup: int, flush_bytes: int = 0):
     """Times `fn` (one launch per call) with HIP events on torch's current
     stream, which is the stream the library launches on. Without a flush the
     K launches run back to back between one pair of events; with a flush, a
     buffer larger than the 256 MiB last-level cache is rewritten before every
     launch, outside the events, and each launch is timed by its own pair."""
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(torch, fn, warmup)
     if not flush_bytes:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -90,6 +118,19 @@ def time_steps(torch, fn, steps: int, warmup: int, flush_bytes: int = 0):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     return sum(times), times
+
+
+def per_launch(torch, fn, steps: int):
+    """Each of `steps` back-to-back launches timed by its own event pair (for
+    the spread; the value comes from the back-to-back total)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
 def spread(times) -> dict:
@@ -130,10 +171,12 @@ def bench_rerank(torch, ms, synth, wl, steps, warmup):
 
     total_ms, _ = time_steps(torch, step, steps, warmup)
     ms_per = total_ms / steps
+    launches = per_launch(torch, step, steps)
     nbytes = wl.varlen_fwd_bytes(32, 1, T, 100_000, 128, 2)
     gbs = nbytes / (ms_per * 1e-3) / 1e9
     out = {
         "workload": w.name, "ms": ms_per, "docs_per_s": 100_000 / (ms_per * 1e-3),
+        "per_launch_ms": {"median": round(statistics.median(launches), 5), **spread(launches)},
         "algorithmic_bytes": nbytes, "tokens": T,
         "roofline": roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s",
                              load_traffic("fwd_varlen_kernel", w.name)),
@@ -142,8 +185,12 @@ def bench_rerank(torch, ms, synth, wl, steps, warmup):
     return out, w
 
 
+KEEP = {}  # inputs a workload leaves for its oracle sample (child process only)
+
+
 def bench_tiny(torch, ms, synth, wl, steps, warmup):
     w = synth.tiny_fp16()
+    KEEP["tiny"] = w
     Q, D = w.Q.cuda(), w.D.cuda()
     scores = torch.empty((4, 32), dtype=torch.float32, device="cuda")
     argmax = torch.empty((4, 32, 32), dtype=torch.int32, device="cuda")
@@ -161,6 +208,7 @@ def bench_tiny(torch, ms, synth, wl, steps, warmup):
 
 def bench_colpali(torch, ms, synth, wl, steps, warmup):
     w = synth.colpali_bf16()
+    KEEP["colpali"] = w
     Q, D, qm, dm = (t.cuda() for t in (w.Q, w.D, w.q_mask, w.d_mask))
     scores = torch.empty((128, 128), dtype=torch.float32, device="cuda")
     argmax = torch.empty((128, 128, 128), dtype=torch.int32, device="cuda")
@@ -181,6 +229,7 @@ def bench_colpali(torch, ms, synth, wl, steps, warmup):
 
 def bench_int8(torch, ms, synth, wl, steps, warmup):
     w = synth.int8_long_query()
+    KEEP["int8"] = w
     Q, D = w.Q.cuda(), w.D.cuda()
     si = torch.empty((1, 10_000), dtype=torch.int32, device="cuda")
     sf = torch.empty((1, 10_000), dtype=torch.float32, device="cuda")
@@ -234,6 +283,7 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
     Q, D, qm, dm = (t.cuda() for t in (fw.Q, fw.D, fw.q_mask, fw.d_mask))
     _, argmax = ms.maxsim_fwd(Q, D, qm, dm, want_argmax=True)  # the saved forward argmax
     g = synth.upstream_grad(5, 128, 128).cuda()
+    KEEP["backward"] = (fw, argmax.cpu(), g.cpu())
     dQ = torch.empty((128, 128, 128), dtype=torch.float32, device="cuda")
     dD = torch.empty((128, 1024, 128), dtype=torch.float32, device="cuda")
     rp = torch.empty((128 * 1024 + 1,), dtype=torch.int32, device="cuda")
@@ -461,6 +511,28 @@ def bench_yardstick(torch, ms, synth, wl, steps, warmup):
     return {"workload": "vendor_yardstick", **out}
 
 
+def host_info() -> dict:
+    """The host the oracle runs on: CPU model, logical CPUs, oracle threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    from oracle import oracle
+    return {"cpu_model": model, "nproc": os.cpu_count(), "oracle_threads": oracle.default_threads()}
+
+
+def _timed(fn, reps=1):
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(w, target_s: float = 12.0) -> dict:
     """The oracle, as it stands, on the headline workload: a 300-doc run sizes
     the sample for about `target_s` seconds of work, taken as the first n docs
@@ -492,24 +564,76 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
                       f"fp64 on {threads} threads, {t:.2f} s"}
 
 
+def cpu_baseline_tiny(w, target_s: float = 2.0) -> dict:
+    from oracle import oracle
+    th = oracle.default_threads()
+    run = lambda: oracle.fwd(w.Q, w.D, threads=th)  # noqa: E731
+    reps = max(1, int(target_s / max(_timed(run), 1e-4)))
+    t = _timed(run, reps)
+    return {"value": round(128 * reps / t, 3), "unit": "pairs/s", "cores": th, "kind": "oracle",
+            "sample": f"the whole 4 x 32 workload with argmax x {reps} passes, fp64 on {th} threads, {t:.2f} s"}
+
+
+def cpu_baseline_colpali(w, target_s: float = 6.0) -> dict:
+    from oracle import oracle
+    th = oracle.default_threads()
+
+    def run(nq):
+        return _timed(lambda: oracle.fwd(w.Q[:nq], w.D, w.q_mask[:nq], w.d_mask, threads=th))
+
+    t2 = run(2)
+    nq = int(min(128, max(2, 2 * target_s / max(t2, 1e-3))))
+    t = run(nq)
+    return {"value": round(nq * 128 / t, 3), "unit": "pairs/s", "cores": th, "kind": "oracle",
+            "sample": f"the first {nq} of the 128 queries against all 128 docs, masks and argmax, "
+                      f"fp64 on {th} threads, {t:.2f} s"}
+
+
+def cpu_baseline_int8(w, target_s: float = 6.0) -> dict:
+    from oracle import oracle
+    th = oracle.default_threads()
+
+    def run(nd):
+        return _timed(lambda: oracle.fwd_i8(w.Q, w.q_scale, w.D[:nd], w.d_scale, want_argmax=False,
+                                            threads=th))
+
+    t20 = run(20)
+    nd = int(min(10_000, max(20, 20 * target_s / max(t20, 1e-3))))
+    t = run(nd)
+    return {"value": round(nd / t, 3), "unit": "docs/s", "cores": th, "kind": "oracle",
+            "sample": f"the first {nd} of the 10,000 docs, 1024-token query, int64 on {th} threads, {t:.2f} s"}
+
+
+def cpu_baseline_backward(keep, target_s: float = 6.0) -> dict:
+    from oracle import oracle
+    th = oracle.default_threads()
+    fw, argmax, g = keep
+    run = lambda: oracle.bwd(fw.Q, fw.D, argmax, g, fw.q_mask, fw.d_mask, threads=th)  # noqa: E731
+    reps = max(1, int(round(target_s / max(_timed(run), 1e-3))))
+    t = _timed(run, reps)
+    return {"value": round(128 * 128 * reps / t, 3), "unit": "pairs/s", "cores": th, "kind": "oracle",
+            "sample": f"the whole backward (CSR, dQ, dD) through the GPU forward's argmax x {reps} passes, "
+                      f"fp64 on {th} threads, {t:.2f} s"}
+
+
+CPU_SAMPLES = {"tiny": cpu_baseline_tiny, "colpali": cpu_baseline_colpali,
+               "int8": cpu_baseline_int8, "backward": cpu_baseline_backward}
+
+FNS = {"rerank": bench_rerank, "tiny": bench_tiny, "colpali": bench_colpali,
+       "int8": bench_int8, "backward": bench_backward, "backward_varlen": bench_backward_varlen,
+       "pairs_varlen": bench_pairs_varlen, "two_stage": bench_two_stage,
+       "topk": bench_topk, "chamfer": bench_chamfer, "dim_sweep": bench_dim_sweep,
+       "copy": bench_copy, "yardstick": bench_yardstick}
+DEFAULT = [HEADLINE, "tiny", "colpali", "int8", "backward", "backward_varlen", "pairs_varlen",
+           "two_stage", "topk", "chamfer", "dim_sweep"]
+MARK = "@@bench-result "
+
+
 # ------------------------------------------------------------------ main
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="",
-                    help="run one workload: rerank|tiny|colpali|int8|backward|backward_varlen|"
-                         "pairs_varlen|two_stage|topk|chamfer|dim_sweep|copy|yardstick")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(docs shard across GPUs with no exchange but a final gather of scores).",
-              file=sys.stderr)
-        return 2
-
+def run_child(args) -> int:
+    """One workload in this process: its timing, then (with --cpu) its oracle
+    sample; prints one marked JSON line."""
     import torch
     import maxsim_scoring_amd as ms
     from maxsim_scoring_amd import synth, workload as wl
@@ -517,55 +641,107 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     ms.binding.lib()  # fails loudly without the built library
+    name = args.child
+    _log(f"workload {name}: generating inputs and timing {args.steps} steps")
+    r = FNS[name](torch, ms, synth, wl, args.steps, args.warmup)
+    w = None
+    if name == HEADLINE:
+        r, w = r
+    r["warmup_runs"] = [{"launches": n, "s": s} for n, s in WARMUP_LOG]
+    cpu = None
+    if args.cpu:
+        torch.cuda.synchronize()
+        if name == HEADLINE:
+            _log("oracle CPU baseline on a bounded sample")
+            cpu = cpu_baseline(w)
+        elif name in CPU_SAMPLES:
+            _log(f"workload {name}: oracle sample")
+            cpu = CPU_SAMPLES[name](KEEP[name])
+    print(MARK + json.dumps({"name": name, "result": r, "cpu": cpu}), flush=True)
+    return 0
 
-    names = [args.only] if args.only else [HEADLINE, "tiny", "colpali", "int8", "backward",
-                                           "backward_varlen", "pairs_varlen", "two_stage", "topk",
-                                           "chamfer", "dim_sweep"]
-    fns = {"rerank": bench_rerank, "tiny": bench_tiny, "colpali": bench_colpali,
-           "int8": bench_int8, "backward": bench_backward, "backward_varlen": bench_backward_varlen,
-           "pairs_varlen": bench_pairs_varlen, "two_stage": bench_two_stage,
-           "topk": bench_topk, "chamfer": bench_chamfer, "dim_sweep": bench_dim_sweep,
-           "copy": bench_copy, "yardstick": bench_yardstick}
-    per = {}
-    head = None
-    head_w = None
+
+def run_in_child(name: str, args, cpu: bool) -> dict:
+    cmd = [sys.executable, "-u", os.path.abspath(__file__), "--child", name, "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--min-warmup-s", str(args.min_warmup_s)]
+    if cpu:
+        cmd.append("--cpu")
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    lines = [l for l in p.stdout.splitlines() if l.startswith(MARK)]
+    if p.returncode != 0 or not lines:
+        return {"error": f"child process exited with status {p.returncode}"}
+    return json.loads(lines[-1][len(MARK):])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-warmup-s", type=float, default=1.0,
+                    help="minimum seconds of untimed launches before each timed region")
+    ap.add_argument("--only", default="",
+                    help="run one workload: " + "|".join(FNS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
+    ap.add_argument("--child", default="", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu", action="store_true", help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(docs shard across GPUs with no exchange but a final gather of scores).",
+              file=sys.stderr)
+        return 2
+    global MIN_WARMUP_S
+    MIN_WARMUP_S = max(0.0, args.min_warmup_s)
+    if args.child:
+        return run_child(args)
+
+    # the parent: runs every workload in a child process and never touches the GPU
+    names = [args.only] if args.only else DEFAULT
+    per, head = {}, None
     for n in names:
-        _log(f"workload {n}: generating inputs and timing {args.steps} steps")
-        r = fns[n](torch, ms, synth, wl, args.steps, args.warmup)
+        _log(f"workload {n}: child process")
+        r = run_in_child(n, args, cpu=not args.no_cpu)
         if n == HEADLINE:
-            head, head_w = r
-        else:
+            if "error" in r:
+                print(f"bench.py: the headline workload failed ({r['error']})", file=sys.stderr)
+                return 1
+            head = r
+        elif "error" in r:
             per[n] = r
-        torch.cuda.empty_cache()
+        else:
+            per[n] = dict(r["result"], **({"cpu_baseline": r["cpu"]} if r["cpu"] else {}))
         _log(f"workload {n}: done")
 
     if head is None:  # a single non-headline workload was asked for
         n, r = next(iter(per.items()))
-        print(json.dumps({"metric": METRIC, "workload": r["workload"], "result": r}), flush=True)
+        print(json.dumps({"metric": METRIC, "workload": r.get("workload", n), "result": r}), flush=True)
         return 0
 
-    cpu = None
-    if not args.no_cpu:
-        _log("oracle CPU baseline on a bounded sample")
-        cpu = cpu_baseline(head_w)
+    h = head["result"]
+    cpu = head["cpu"]
+    if cpu is not None:
+        cpu = dict(cpu, host=host_info())
     line = {
         "metric": METRIC,
-        "value": round(head["docs_per_s"], 1),
+        "value": round(h["docs_per_s"], 1),
         "unit": "docs/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["ms"], 4),
+        "warmup_min_s": MIN_WARMUP_S,
+        "ms_per_step": round(h["ms"], 4),
+        "per_launch_ms": h["per_launch_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": head["workload"], "queries": 1, "query_tokens": 32,
-                   "docs": 100_000, "doc_tokens": "U{50..300}", "packed_tokens": head["tokens"],
+        "config": {"workload": h["workload"], "queries": 1, "query_tokens": 32,
+                   "docs": 100_000, "doc_tokens": "U{50..300}", "packed_tokens": h["tokens"],
                    "d": 128, "seed": 2},
-        "roofline": head["roofline"],
-        "kernel": head["kernel"],
+        "roofline": h["roofline"],
+        "kernel": h["kernel"],
         "cpu_baseline": cpu,
         "per_config": per,
     }
