@@ -661,6 +661,31 @@ def run_child(args) -> int:
     return 0
 
 
+def under_profiler() -> bool:
+    """True when a GPU profiler's library is preloaded: it may initialise the
+    GPU in this process before main(), and a process whose GPU is initialised
+    must not start other programs, so the workloads then run in this process."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+
+
+def run_in_process(name: str, args, cpu: bool) -> dict:
+    """The child's work in this process (used under a profiler)."""
+    import io
+    import contextlib
+    args.child, args.cpu = name, cpu
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        rc = run_child(args)
+    WARMUP_LOG.clear()
+    KEEP.clear()
+    import torch
+    torch.cuda.empty_cache()
+    lines = [l for l in buf.getvalue().splitlines() if l.startswith(MARK)]
+    if rc != 0 or not lines:
+        return {"error": f"workload returned status {rc}"}
+    return json.loads(lines[-1][len(MARK):])
+
+
 def run_in_child(name: str, args, cpu: bool) -> dict:
     cmd = [sys.executable, "-u", os.path.abspath(__file__), "--child", name, "--steps", str(args.steps),
            "--warmup", str(args.warmup), "--min-warmup-s", str(args.min_warmup_s)]
@@ -696,12 +721,14 @@ def main() -> int:
     if args.child:
         return run_child(args)
 
-    # the parent: runs every workload in a child process and never touches the GPU
+    # the parent: runs every workload in a child process and never touches the
+    # GPU (under a profiler, in this process instead)
     names = [args.only] if args.only else DEFAULT
     per, head = {}, None
+    inproc = under_profiler()
     for n in names:
-        _log(f"workload {n}: child process")
-        r = run_in_child(n, args, cpu=not args.no_cpu)
+        _log(f"workload {n}: {'in this process (profiler)' if inproc else 'child process'}")
+        r = (run_in_process if inproc else run_in_child)(n, args, cpu=not args.no_cpu)
         if n == HEADLINE:
             if "error" in r:
                 print(f"bench.py: the headline workload failed ({r['error']})", file=sys.stderr)
@@ -730,6 +757,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_min_s": MIN_WARMUP_S,
+        "warmup_launches": h["warmup_runs"][0]["launches"] if h.get("warmup_runs") else None,
         "ms_per_step": round(h["ms"], 4),
         "per_launch_ms": h["per_launch_ms"],
         "higher_is_better": True,

@@ -114,6 +114,11 @@ __device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (
 constexpr float kTauK = 1.0f + 12.0f * 0x1p-18f;
 constexpr float kTau0 = 18.0f * 0x1p-18f;
 
+// 4 consecutive points (12 floats), read with one 48-byte copy
+struct __attribute__((aligned(4))) ChRows4 {
+    float v[12];
+};
+
 // KN source blocks of one (batch, direction) segment against its whole
 // target set: A [na, 3] holds the sources, blocks k0 .. k0+KN-1; T [nt, 3]
 // the targets. Writes dist[sp] and idx[sp] for the blocks' points, or
@@ -265,23 +270,57 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
         lost |= __shfl_xor(lost, 32, 64);
         float dv = __builtin_inff();
         int di = 0x7fffffff;
+        // The column's tasks are the kept tiles of its 4 lanes: bit 2j + slot
+        // is set when lane j keeps that slot (j = the lane's row group). Each
+        // task's 64 rows (rows 4j .. 4j+3 of the tile's 16 blocks) are split
+        // over the column's 4 lanes, lane rg taking blocks 4rg .. 4rg+3, so a
+        // wave makes one pass of 16 rows per task of its busiest column.
+        const int mine = ((best[u] <= thr) ? 1 : 0) | ((v1[u] <= thr) ? 2 : 0);
+        int mask = mine << (2 * rg);
+        mask |= __shfl_xor(mask, 16, 64);
+        mask |= __shfl_xor(mask, 32, 64);
+        int tile[8];
 #pragma unroll
-        for (int slot = 0; slot < 2; ++slot) {
-            const bool keep = slot == 0 ? best[u] <= thr : v1[u] <= thr;
-            if (keep) {
-                const int64_t tb = (int64_t)(slot == 0 ? s0[u] : s1[u]) * kChTileT + 4 * rg;
-#pragma unroll 2
-                for (int k = 0; k < kChTileT / 16; ++k) {
+        for (int j = 0; j < 4; ++j) {
+            tile[2 * j] = __shfl(s0[u], col + 16 * j, 64);
+            tile[2 * j + 1] = __shfl(s1[u], col + 16 * j, 64);
+        }
+        while (__any(mask != 0)) {
+            if (mask != 0) {
+                const int q = __builtin_ctz(mask);
+                mask &= mask - 1;
+                int tq = tile[0];
+#pragma unroll
+                for (int k = 1; k < 8; ++k) tq = q == k ? tile[k] : tq;
+                const int64_t tb = (int64_t)tq * kChTileT + 4 * (q >> 1) + 64 * rg;
+                ChRows4 x[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int64_t t = tb + 16 * k;
+                    if (t + 3 < nt) __builtin_memcpy(&x[k], T + t * 3, sizeof(ChRows4));
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int64_t t = tb + 16 * k;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int64_t t = tb + 16 * k + r;
-                        if (t < nt) {
-                            const float dx = px - T[t * 3], dy = py - T[t * 3 + 1], dz = pz - T[t * 3 + 2];
-                            const float v = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
-                            if (v < dv || (v == dv && (int)t < di)) {
-                                dv = v;
-                                di = (int)t;
-                            }
+                        float tx, ty, tz;
+                        if (t + 3 < nt) {
+                            tx = x[k].v[3 * r];
+                            ty = x[k].v[3 * r + 1];
+                            tz = x[k].v[3 * r + 2];
+                        } else if (t + r < nt) {
+                            tx = T[(t + r) * 3];
+                            ty = T[(t + r) * 3 + 1];
+                            tz = T[(t + r) * 3 + 2];
+                        } else {
+                            continue;
+                        }
+                        const float dx = px - tx, dy = py - ty, dz = pz - tz;
+                        const float v = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+                        if (v < dv || (v == dv && (int)(t + r) < di)) {
+                            dv = v;
+                            di = (int)(t + r);
                         }
                     }
                 }
@@ -310,82 +349,132 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
 // Sources whose near-tie candidates overflowed (index -1): the whole target
 // set in the direct form, the smallest value and the lowest index among equal
 // ones. A workgroup checks kFixThreads consecutive sources of the list
-// [dist1 | dist2] and treats each overflowed one with all its threads.
-constexpr int kFixThreads = 256;
+// [dist1 | dist2], lists the overflowed ones in order, and takes them in
+// groups of up to kFixGroup that share a target set (one batch and
+// direction): one pass over the set serves the whole group. Wave w takes
+// every 16th run of kFixRun points, reads the run's coordinates with
+// consecutive-dword loads (each instruction 256 contiguous bytes) into its own
+// LDS stage, and its lanes evaluate the run's points in ascending order.
+constexpr int kFixThreads = 1024, kFixRun = 512, kFixGroup = 8;
 __global__ __launch_bounds__(kFixThreads) void chamfer_fix_kernel(ChamferArgs a)
 {
-    __shared__ int flag[kFixThreads];
-    __shared__ float wv[kFixThreads / 64];
-    __shared__ int wi[kFixThreads / 64];
+    constexpr int kWavesFix = kFixThreads / 64;
+    __shared__ int list[kFixThreads];
+    __shared__ int wcount[kWavesFix];
+    __shared__ float stage[kWavesFix][kFixRun * 3];
+    __shared__ float wv[kFixGroup][kWavesFix];
+    __shared__ int wi[kFixGroup][kWavesFix];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t n1 = a.B * a.N, ntot = n1 + a.B * a.M;
     const int64_t g0 = (int64_t)blockIdx.x * kFixThreads;
-    {
-        const int64_t g = g0 + tid;
-        int f = 0;
-        if (g < ntot) f = (g < n1 ? a.idx1[g] : a.idx2[g - n1]) < 0;
-        flag[tid] = f;
-    }
+    // the overflowed sources of this workgroup, in order
+    const int64_t g = g0 + tid;
+    bool flagged = false;
+    if (g < ntot) flagged = (g < n1 ? a.idx1[g] : a.idx2[g - n1]) < 0;
+    const uint64_t bal = __ballot(flagged);
+    if (lane == 0) wcount[w] = __builtin_popcountll(bal);
     cham_barrier();
-    for (int f = 0; f < kFixThreads; ++f) {
-        if (!flag[f]) continue;  // the same for every thread
-        const int64_t gs = g0 + f;
-        const bool second = gs >= n1;
-        const int64_t gl = second ? gs - n1 : gs;
+    int nlist = 0, off = 0;
+    for (int k = 0; k < kWavesFix; ++k) {
+        off += k < w ? wcount[k] : 0;
+        nlist += wcount[k];
+    }
+    if (flagged) list[off + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = tid;
+    cham_barrier();
+    float* st = &stage[w][0];
+    for (int i0 = 0; i0 < nlist;) {
+        // a group: consecutive listed sources of one (batch, direction)
+        const int64_t gf = g0 + list[i0];
+        const bool second = gf >= n1;
         const int64_t na = second ? a.M : a.N, nt = second ? a.N : a.M;
-        const int64_t b = gl / na;
-        const float* S = (second ? a.Q : a.P) + gl * 3;
-        const float* T = (second ? a.P : a.Q) + b * nt * 3;
-        const float px = S[0], py = S[1], pz = S[2];
-        float dv = __builtin_inff();
-        int di = 0x7fffffff;
-        // ascending targets per thread with a strict '<': the lowest index of
-        // a tie stays; four loads in flight
-        for (int64_t t = tid; t < nt; t += 4 * kFixThreads) {
-            float x[4], y[4], z[4];
+        const int64_t seg = (second ? gf - n1 : gf) / na;
+        int ng = 1;
+        while (ng < kFixGroup && i0 + ng < nlist) {
+            const int64_t gn = g0 + list[i0 + ng];
+            if ((gn >= n1) != second || ((second ? gn - n1 : gn) / na) != seg) break;
+            ++ng;
+        }
+        const float* T = (second ? a.P : a.Q) + seg * nt * 3;
+        float px[kFixGroup], py[kFixGroup], pz[kFixGroup], dv[kFixGroup];
+        int di[kFixGroup];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int64_t q = t + (int64_t)j * kFixThreads;
-                q = q < nt ? q : nt - 1;
-                x[j] = T[q * 3];
-                y[j] = T[q * 3 + 1];
-                z[j] = T[q * 3 + 2];
+        for (int k = 0; k < kFixGroup; ++k) {
+            const int64_t gk = g0 + list[i0 + (k < ng ? k : 0)];
+            const float* S = (second ? a.Q + (gk - n1) * 3 : a.P + gk * 3);
+            px[k] = S[0];
+            py[k] = S[1];
+            pz[k] = S[2];
+            dv[k] = __builtin_inff();
+            di[k] = 0x7fffffff;
+        }
+        // ascending targets per lane with a strict '<': the lowest index of a
+        // tie stays
+        for (int64_t p0 = (int64_t)w * kFixRun; p0 < nt; p0 += (int64_t)kWavesFix * kFixRun) {
+            const int64_t lim = nt * 3;
+            float v[kFixRun * 3 / 64];
+#pragma unroll
+            for (int m = 0; m < kFixRun * 3 / 64; ++m) {
+                const int64_t f = p0 * 3 + 64 * m + lane;
+                v[m] = f < lim ? T[f] : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t q = t + (int64_t)j * kFixThreads;
-                const float dx = px - x[j], dy = py - y[j], dz = pz - z[j];
-                const float v = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
-                if (q < nt && v < dv) {
-                    dv = v;
-                    di = (int)q;
+            for (int m = 0; m < kFixRun * 3 / 64; ++m) st[64 * m + lane] = v[m];
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to its reads
+#pragma unroll 2
+            for (int kk = 0; kk < kFixRun / 64; ++kk) {
+                const int pl = 64 * kk + lane;  // odd word stride between lanes: no bank conflicts
+                const float tx = st[3 * pl], ty = st[3 * pl + 1], tz = st[3 * pl + 2];
+                const bool in = p0 + pl < nt;
+#pragma unroll
+                for (int k = 0; k < kFixGroup; ++k) {
+                    if (k < ng) {  // the same for every thread
+                        const float dx = px[k] - tx, dy = py[k] - ty, dz = pz[k] - tz;
+                        const float d = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+                        if (in && d < dv[k]) {
+                            dv[k] = d;
+                            di[k] = (int)(p0 + pl);
+                        }
+                    }
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the stage is refilled
         }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(dv, o, 64);
-            const int oi = __shfl_xor(di, o, 64);
-            if (ov < dv || (ov == dv && oi < di)) {
-                dv = ov;
-                di = oi;
+        for (int k = 0; k < kFixGroup; ++k) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const float ov = __shfl_xor(dv[k], o, 64);
+                const int oi = __shfl_xor(di[k], o, 64);
+                if (ov < dv[k] || (ov == dv[k] && oi < di[k])) {
+                    dv[k] = ov;
+                    di[k] = oi;
+                }
+            }
+            if (lane == 0) {
+                wv[k][w] = dv[k];
+                wi[k][w] = di[k];
             }
         }
-        if (lane == 0) {
-            wv[w] = dv;
-            wi[w] = di;
-        }
         cham_barrier();
-        if (tid == 0) {
-            for (int k = 1; k < kFixThreads / 64; ++k)
-                if (wv[k] < dv || (wv[k] == dv && wi[k] < di)) {
-                    dv = wv[k];
-                    di = wi[k];
+        if (tid < ng) {
+            float bv = wv[tid][0];
+            int bi = wi[tid][0];
+            for (int k = 1; k < kWavesFix; ++k)
+                if (wv[tid][k] < bv || (wv[tid][k] == bv && wi[tid][k] < bi)) {
+                    bv = wv[tid][k];
+                    bi = wi[tid][k];
                 }
-            (second ? a.dist2 : a.dist1)[gl] = dv;
-            (second ? a.idx2 : a.idx1)[gl] = di;
+            const int64_t gk = g0 + list[i0 + tid];
+            if (second) {
+                a.dist2[gk - n1] = bv;
+                a.idx2[gk - n1] = bi;
+            } else {
+                a.dist1[gk] = bv;
+                a.idx1[gk] = bi;
+            }
         }
         cham_barrier();
+        i0 += ng;
     }
 }
 
