@@ -735,6 +735,31 @@ def test_chamfer_many_near_ties(ms, oracle_mod):
     _check_chamfer_fwd(oracle_mod, P, Q, got)
 
 
+def test_chamfer_near_ties_many_batches(ms, oracle_mod):
+    """Overflowed sources of several batches and both directions inside one
+    fix workgroup (its 1,024 sources span many batch segments): 12 batches of
+    40 sources, each source at the centre of a ring of 10 targets whose radii
+    differ by a few ulps, spread over the batch's 3,000 random targets."""
+    _say("chamfer ring near-ties, many batches")
+    rng = np.random.default_rng(786)
+    B, ns, nfar, nring = 12, 40, 3000, 10
+    P = rng.standard_normal((B, ns, 3)).astype(np.float32)
+    Q = []
+    for b in range(B):
+        ring = []
+        for k in range(nring):
+            v = rng.standard_normal((ns, 3))
+            v /= np.linalg.norm(v, axis=1, keepdims=True)
+            ring.append((P[b] + 0.05 * (1 + k * 2.0 ** -22) * v).astype(np.float32))
+        far = (3.0 * rng.standard_normal((nfar, 3))).astype(np.float32)
+        parts = [far[:700]] + ring[:5] + [far[700:1900]] + ring[5:] + [far[1900:]]
+        Q.append(np.concatenate(parts))
+    P = torch.from_numpy(P)
+    Q = torch.from_numpy(np.stack(Q))
+    got = _chamfer_gpu(ms, P, Q)
+    _check_chamfer_fwd(oracle_mod, P, Q, got)
+
+
 # ------------------------------------------------------------------ streams
 
 def test_concurrent_streams(ms, oracle_mod):
