@@ -294,7 +294,8 @@ maxsim_status_t maxsim_chamfer_fwd(const float* P, const float* Q, int64_t B, in
  *   csr_row_ptr1 [B*M+1], csr_col_idx1 [B*N]: outputs, the inverse of idx1
  *   (row b*M + q lists the flat indices b*N + p that chose it, ascending);
  *   csr_row_ptr2 [B*N+1], csr_col_idx2 [B*M]: the inverse of idx2.
- * Sums run in fp32 in a fixed order (the CSR row order); no atomics.
+ * Sums run in fp32 in a fixed order (the CSR row order); no atomics. dP and
+ * dQ hold intermediates of the CSR build until the gradients are written.
  * B == 0 enqueues nothing. Errors as maxsim_chamfer_fwd, OVERFLOW also when
  * B*N + 1 or B*M + 1 >= 2^31.
  */

@@ -323,7 +323,10 @@ def maxsim_bwd_varlen(Q: torch.Tensor, cu_q: torch.Tensor, max_lq: int, D: torch
     return dQ, dD, csr_row_ptr, csr_col_idx
 
 
-def maxsim_chamfer_fwd(P: torch.Tensor, Q: torch.Tensor, want_loss: bool = True, stream=None):
+def maxsim_chamfer_fwd(P: torch.Tensor, Q: torch.Tensor, want_loss: bool = True,
+                       dist1: Optional[torch.Tensor] = None, idx1: Optional[torch.Tensor] = None,
+                       dist2: Optional[torch.Tensor] = None, idx2: Optional[torch.Tensor] = None,
+                       loss: Optional[torch.Tensor] = None, stream=None):
     """Chamfer distance of point-set batches P [B,N,3], Q [B,M,3] float32.
     Returns (dist1 [B,N], idx1 [B,N], dist2 [B,M], idx2 [B,M], loss [B] or None)."""
     if P.dim() != 3 or Q.dim() != 3 or P.shape[2] != 3 or Q.shape[2] != 3 or P.shape[0] != Q.shape[0]:
@@ -333,19 +336,34 @@ def maxsim_chamfer_fwd(P: torch.Tensor, Q: torch.Tensor, want_loss: bool = True,
     B, N, _ = P.shape
     M = Q.shape[1]
     dev = P.device
-    d1 = torch.empty((B, N), dtype=torch.float32, device=dev)
-    i1 = torch.empty((B, N), dtype=torch.int32, device=dev)
-    d2 = torch.empty((B, M), dtype=torch.float32, device=dev)
-    i2 = torch.empty((B, M), dtype=torch.int32, device=dev)
-    loss = torch.empty((B,), dtype=torch.float32, device=dev) if want_loss else None
-    st = lib().maxsim_chamfer_fwd(_p(P), _p(Q), B, N, M, _p(d1), _p(i1), _p(d2), _p(i2), _p(loss),
-                                  _stream(stream))
+    if dist1 is None:
+        dist1 = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if idx1 is None:
+        idx1 = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if dist2 is None:
+        dist2 = torch.empty((B, M), dtype=torch.float32, device=dev)
+    if idx2 is None:
+        idx2 = torch.empty((B, M), dtype=torch.int32, device=dev)
+    if loss is None and want_loss:
+        loss = torch.empty((B,), dtype=torch.float32, device=dev)
+    _out("dist1", dist1, torch.float32, (B, N))
+    _out("idx1", idx1, torch.int32, (B, N))
+    _out("dist2", dist2, torch.float32, (B, M))
+    _out("idx2", idx2, torch.int32, (B, M))
+    _out("loss", loss, torch.float32, (B,))
+    st = lib().maxsim_chamfer_fwd(_p(P), _p(Q), B, N, M, _p(dist1), _p(idx1), _p(dist2), _p(idx2),
+                                  _p(loss), _stream(stream))
     _check("maxsim_chamfer_fwd", st)
-    return d1, i1, d2, i2, loss
+    return dist1, idx1, dist2, idx2, loss
 
 
 def maxsim_chamfer_bwd(P: torch.Tensor, Q: torch.Tensor, idx1: torch.Tensor, idx2: torch.Tensor,
-                       grad_dist1: torch.Tensor, grad_dist2: torch.Tensor, stream=None):
+                       grad_dist1: torch.Tensor, grad_dist2: torch.Tensor,
+                       dP: Optional[torch.Tensor] = None, dQ: Optional[torch.Tensor] = None,
+                       csr_row_ptr1: Optional[torch.Tensor] = None,
+                       csr_col_idx1: Optional[torch.Tensor] = None,
+                       csr_row_ptr2: Optional[torch.Tensor] = None,
+                       csr_col_idx2: Optional[torch.Tensor] = None, stream=None):
     """Chamfer backward through the saved indices. Returns (dP [B,N,3],
     dQ [B,M,3], row_ptr1 [B*M+1], col_idx1 [B*N], row_ptr2 [B*N+1], col_idx2 [B*M])."""
     B, N, _ = P.shape
@@ -361,17 +379,29 @@ def maxsim_chamfer_bwd(P: torch.Tensor, Q: torch.Tensor, idx1: torch.Tensor, idx
         if tuple(t.shape) != shp:
             raise ValueError(f"{n} must be {list(shp)}")
     dev = P.device
-    dP = torch.empty((B, N, 3), dtype=torch.float32, device=dev)
-    dQ = torch.empty((B, M, 3), dtype=torch.float32, device=dev)
-    rp1 = torch.empty((B * M + 1,), dtype=torch.int32, device=dev)
-    ci1 = torch.empty((max(1, B * N),), dtype=torch.int32, device=dev)
-    rp2 = torch.empty((B * N + 1,), dtype=torch.int32, device=dev)
-    ci2 = torch.empty((max(1, B * M),), dtype=torch.int32, device=dev)
+    if dP is None:
+        dP = torch.empty((B, N, 3), dtype=torch.float32, device=dev)
+    if dQ is None:
+        dQ = torch.empty((B, M, 3), dtype=torch.float32, device=dev)
+    if csr_row_ptr1 is None:
+        csr_row_ptr1 = torch.empty((B * M + 1,), dtype=torch.int32, device=dev)
+    if csr_col_idx1 is None:
+        csr_col_idx1 = torch.empty((max(1, B * N),), dtype=torch.int32, device=dev)
+    if csr_row_ptr2 is None:
+        csr_row_ptr2 = torch.empty((B * N + 1,), dtype=torch.int32, device=dev)
+    if csr_col_idx2 is None:
+        csr_col_idx2 = torch.empty((max(1, B * M),), dtype=torch.int32, device=dev)
+    _out("dP", dP, torch.float32, (B, N, 3))
+    _out("dQ", dQ, torch.float32, (B, M, 3))
+    _out("csr_row_ptr1", csr_row_ptr1, torch.int32, (B * M + 1,))
+    _out_flat("csr_col_idx1", csr_col_idx1, torch.int32, B * N)
+    _out("csr_row_ptr2", csr_row_ptr2, torch.int32, (B * N + 1,))
+    _out_flat("csr_col_idx2", csr_col_idx2, torch.int32, B * M)
     st = lib().maxsim_chamfer_bwd(_p(P), _p(Q), B, N, M, _p(idx1), _p(idx2), _p(grad_dist1),
-                                  _p(grad_dist2), _p(dP), _p(dQ), _p(rp1), _p(ci1), _p(rp2), _p(ci2),
-                                  _stream(stream))
+                                  _p(grad_dist2), _p(dP), _p(dQ), _p(csr_row_ptr1), _p(csr_col_idx1),
+                                  _p(csr_row_ptr2), _p(csr_col_idx2), _stream(stream))
     _check("maxsim_chamfer_bwd", st)
-    return dP, dQ, rp1, ci1[:B * N], rp2, ci2[:B * M]
+    return dP, dQ, csr_row_ptr1, csr_col_idx1[:B * N], csr_row_ptr2, csr_col_idx2[:B * M]
 
 
 def maxsim_status_string(status: int) -> str:

@@ -1051,6 +1051,146 @@ __global__ __launch_bounds__(kCsrThreads) void cham_csr_kernel(ChamferArgs a, in
     build_segment_csr<MODE>(sm, c.ns, c.nr, 0, c.row_ptr + c.b * c.nr, c.col_idx, load, r * (int64_t)kCsrBins);
 }
 
+// The two CSRs in two steps, when the scratch fits (see the launcher):
+// 1. a stable partition of each segment's sources by bucket of kCsrBins rows
+//    (destination / 1024), over chunks of kCsrChunk sources: per chunk the
+//    bucket counts (cham_part_kernel<kCsrCount>), per segment the scan that
+//    turns them into each chunk's first slot per bucket and the bucket starts
+//    (cham_part_scan_kernel), per chunk the stable scatter of the local
+//    source indices in bucket order (cham_part_kernel<kCsrScatter>);
+// 2. cham_bucket_kernel, one workgroup per (segment, bucket): the CSR rows of
+//    the bucket from the bucket's own sources, in source order.
+// Scratch of a segment with ns sources, nchunk chunks and R buckets, in its
+// share of dP (the first CSR's sources are P points) or dQ (second CSR) as
+// ints, which the gradient kernel writes last: the partition [0, ns), the
+// bucket starts [ns, ns + R], the chunk counts, then slots,
+// [ns + R + 1, ns + R + 1 + nchunk * R) chunk-major. Every round of the
+// three-pass build below reads the whole segment; here each source is read
+// three times in all.
+struct ChamPart {
+    int32_t* part;   // [ns] local source indices in bucket order
+    int32_t* start;  // [R + 1] bucket starts
+    int32_t* cnt;    // [nchunk][R] counts, then first slots
+    int64_t R, nchunk;
+};
+__device__ __forceinline__ ChamPart cham_part(const ChamferArgs& a, const ChamSeg& c, bool second)
+{
+    ChamPart p;
+    p.part = (int32_t*)(second ? a.dQ : a.dP) + c.b * c.ns * 3;
+    p.R = (c.nr + kCsrBins - 1) / kCsrBins;
+    p.nchunk = (c.ns + kCsrChunk - 1) / kCsrChunk;
+    p.start = p.part + c.ns;
+    p.cnt = p.start + p.R + 1;
+    return p;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kCsrThreads) void cham_part_kernel(ChamferArgs a, int nch1, int nch2)
+{
+    // workgroup -> (segment, chunk): CSR1 segments first, then CSR2
+    const int64_t w = blockIdx.x;
+    const int64_t n1 = a.B * nch1;
+    const int64_t g = w < n1 ? w / nch1 : a.B + (w - n1) / nch2;
+    const int64_t ch = w < n1 ? w % nch1 : (w - n1) % nch2;
+    const bool second = g >= a.B;
+    const ChamSeg c = cham_seg(a, g);
+    const ChamPart p = cham_part(a, c, second);
+    const int64_t k_lo = ch * kCsrChunk;
+    const int64_t n = c.ns - k_lo < kCsrChunk ? c.ns - k_lo : kCsrChunk;
+    const int32_t last = (int32_t)(c.nr - 1);
+    const int32_t* idx = c.idx + c.b * c.ns + k_lo;
+    auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int64_t k = k0 + 64 * m;
+            const bool ok = k < n;
+            sv[m] = (int32_t)(ok ? k_lo + k : 0);
+            int32_t t = ok ? __builtin_nontemporal_load(idx + k) : 0;
+            t = t < 0 ? 0 : (t > last ? last : t);  // precondition guard
+            tv[m] = t / kCsrBins;
+        }
+    };
+    __shared__ CsrLds sm;
+    build_segment_csr<MODE>(sm, n, p.R, 0, p.cnt + ch * p.R, p.part, load);
+}
+
+// per segment: bucket totals over the chunks, their exclusive scan (the
+// bucket starts), and each chunk's first slot per bucket in place of its count
+__global__ __launch_bounds__(kCsrBins) void cham_part_scan_kernel(ChamferArgs a)
+{
+    __shared__ uint32_t wsum[kCsrBins / 64];
+    const int64_t g = blockIdx.x;
+    const bool second = g >= a.B;
+    const ChamSeg c = cham_seg(a, g);
+    const ChamPart p = cham_part(a, c, second);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t tot = 0;
+    if (tid < p.R)
+        for (int64_t ch = 0; ch < p.nchunk; ++ch) tot += (uint32_t)p.cnt[ch * p.R + tid];
+    uint32_t incl = tot;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    barrier_lds();
+    uint32_t base = 0;
+    for (int k = 0; k < wave; ++k) base += wsum[k];
+    if (tid < p.R) {
+        uint32_t run = base + incl - tot;
+        p.start[tid] = (int32_t)run;
+        for (int64_t ch = 0; ch < p.nchunk; ++ch) {
+            const uint32_t v = (uint32_t)p.cnt[ch * p.R + tid];
+            p.cnt[ch * p.R + tid] = (int32_t)run;
+            run += v;
+        }
+    }
+    if (tid == 0) p.start[p.R] = (int32_t)c.ns;
+}
+
+__global__ __launch_bounds__(kCsrThreads) void cham_bucket_kernel(ChamferArgs a, int R1, int R2)
+{
+    // workgroup -> (segment, bucket): CSR1 segments first, then CSR2
+    const int64_t w = blockIdx.x;
+    const int64_t n1 = a.B * R1;
+    const int64_t g = w < n1 ? w / R1 : a.B + (w - n1) / R2;
+    const int64_t r = w < n1 ? w % R1 : (w - n1) % R2;
+    const bool second = g >= a.B;
+    const ChamSeg c = cham_seg(a, g);
+    const ChamPart p = cham_part(a, c, second);
+    const int64_t R = second ? R2 : R1;
+    const int32_t* part = p.part;
+    // the bucket's sources, bounded for any scratch content
+    int64_t k_beg = p.start[r], k_end = p.start[r + 1];
+    k_beg = k_beg < 0 ? 0 : (k_beg > c.ns ? c.ns : k_beg);
+    k_end = k_end < k_beg ? k_beg : (k_end > c.ns ? c.ns : k_end);
+    const int64_t cnt = k_end - k_beg;
+    const int64_t t0 = r * kCsrBins;
+    const int64_t L = c.nr - t0 < kCsrBins ? c.nr - t0 : kCsrBins;
+    const int32_t last = (int32_t)(c.nr - 1);
+    const int64_t sbase = c.b * c.ns;
+    auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
+        int64_t loc[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int64_t k = k0 + 64 * m;
+            int64_t v = k < cnt ? part[k_beg + k] : 0;
+            loc[m] = v < 0 ? 0 : (v >= c.ns ? c.ns - 1 : v);
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int64_t k = k0 + 64 * m;
+            sv[m] = (int32_t)(sbase + loc[m]);
+            int32_t t = k < cnt ? c.idx[sbase + loc[m]] : 0;
+            t = t < 0 ? 0 : (t > last ? last : t);
+            tv[m] = (int32_t)(t - t0);  // in [0, L) for a bucket's own sources
+        }
+    };
+    __shared__ CsrLds sm;
+    build_segment_csr<kCsrFull>(sm, cnt, L, sbase + k_beg, c.row_ptr + c.b * c.nr + t0, c.col_idx, load);
+    if (c.b == a.B - 1 && r == R - 1 && threadIdx.x == 0) c.row_ptr[a.B * c.nr] = (int32_t)(a.B * c.ns);
+}
+
 // per segment: the counts in row_ptr become exclusive row starts (plus the
 // segment base b*ns); the last segment of each CSR also writes its end entry
 __global__ __launch_bounds__(1024) void cham_scan_kernel(ChamferArgs a)
@@ -1150,12 +1290,28 @@ hipError_t launch_chamfer_bwd(ChamferArgs a, hipStream_t stream)
     hipError_t err;
     const int r1 = (int)((a.M + kCsrBins - 1) / kCsrBins), r2 = (int)((a.N + kCsrBins - 1) / kCsrBins);
     const unsigned wgs = (unsigned)(a.B * (r1 + r2));
-    hipLaunchKernelGGL(cham_csr_kernel<kCsrCount>, dim3(wgs), dim3(kCsrThreads), 0, stream, a, r1, r2);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(cham_scan_kernel, dim3((unsigned)(2 * a.B)), dim3(1024), 0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(cham_csr_kernel<kCsrScatter>, dim3(wgs), dim3(kCsrThreads), 0, stream, a, r1, r2);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // the two-step build keeps ns + R + 1 + nchunk * R ints in a segment's
+    // 3 * ns floats of dP (or dQ), and its partition passes handle up to
+    // kCsrBins buckets (segments of at most about 1 M rows)
+    const int64_t c1 = (a.N + kCsrChunk - 1) / kCsrChunk, c2 = (a.M + kCsrChunk - 1) / kCsrChunk;
+    if (r1 <= kCsrBins && r2 <= kCsrBins && r1 + 1 + c1 * r1 <= 2 * a.N && r2 + 1 + c2 * r2 <= 2 * a.M) {
+        const unsigned pw = (unsigned)(a.B * (c1 + c2));
+        hipLaunchKernelGGL(cham_part_kernel<kCsrCount>, dim3(pw), dim3(kCsrThreads), 0, stream, a, (int)c1, (int)c2);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(cham_part_scan_kernel, dim3((unsigned)(2 * a.B)), dim3(kCsrBins), 0, stream, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(cham_part_kernel<kCsrScatter>, dim3(pw), dim3(kCsrThreads), 0, stream, a, (int)c1, (int)c2);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(cham_bucket_kernel, dim3(wgs), dim3(kCsrThreads), 0, stream, a, r1, r2);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else {
+        hipLaunchKernelGGL(cham_csr_kernel<kCsrCount>, dim3(wgs), dim3(kCsrThreads), 0, stream, a, r1, r2);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(cham_scan_kernel, dim3((unsigned)(2 * a.B)), dim3(1024), 0, stream, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(cham_csr_kernel<kCsrScatter>, dim3(wgs), dim3(kCsrThreads), 0, stream, a, r1, r2);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     const int64_t n = a.B * (a.N + a.M);
     hipLaunchKernelGGL(cham_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
