@@ -278,6 +278,37 @@ def bench_dim_sweep(torch, ms, synth, wl, steps, warmup):
             "kernel": "fwd_dim_kernel"}
 
 
+BATCHES = (1_000, 10_000, 100_000, 200_000)
+
+
+def bench_batch_sweep(torch, ms, synth, wl, steps, warmup):
+    """Batch scaling ([TMS] Sec. 6, Table 8): one 32-token fp16 query against
+    B docs of 128 tokens (d = 128, no masks), B = 1,000 ... 200,000, the first
+    B docs of one 200,000-doc corpus. Launches whose D fits the 256 MiB
+    last-level cache (B <= 10,000) are timed one by one after a cache flush,
+    the others back to back. Not in the default run."""
+    w = synth.dim_scaling_fp16(128, seed=8, Nd=max(BATCHES))
+    Q, Dall = w.Q.cuda(), w.D.cuda()
+    del w
+    rows = {}
+    for B in BATCHES:
+        D = Dall[:B]
+        scores = torch.empty((1, B), dtype=torch.float32, device="cuda")
+
+        def step():
+            ms.maxsim_fwd(Q, D, scores=scores)
+
+        flush = 512 << 20 if B * 128 * 256 < (256 << 20) else 0
+        total, times = time_steps(torch, step, steps, warmup, flush_bytes=flush)
+        t = statistics.median(times) if flush else total / steps
+        nbytes = wl.dense_fwd_bytes(1, B, 32, 128, 128, 2, False, False, False)
+        rows[f"B{B}"] = {"docs": B, "ms": t, **(spread(times) if flush else {}),
+                         "docs_per_s": B / (t * 1e-3), "algorithmic_bytes": nbytes,
+                         "roofline": roofline("hbm", nbytes / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    return {"workload": "batch_sweep_fp16_1xB_lq32_ld128", "ms": rows["B200000"]["ms"], "batches": rows,
+            "roofline": rows["B200000"]["roofline"], "kernel": "fwd_dim_kernel (one short query)"}
+
+
 def bench_backward(torch, ms, synth, wl, steps, warmup):
     fw = synth.colpali_bf16()
     Q, D, qm, dm = (t.cuda() for t in (fw.Q, fw.D, fw.q_mask, fw.d_mask))
@@ -633,7 +664,7 @@ FNS = {"rerank": bench_rerank, "tiny": bench_tiny, "colpali": bench_colpali,
        "int8": bench_int8, "backward": bench_backward, "backward_varlen": bench_backward_varlen,
        "pairs_varlen": bench_pairs_varlen, "two_stage": bench_two_stage,
        "topk": bench_topk, "chamfer": bench_chamfer, "dim_sweep": bench_dim_sweep,
-       "copy": bench_copy, "yardstick": bench_yardstick}
+       "copy": bench_copy, "yardstick": bench_yardstick, "batch_sweep": bench_batch_sweep}
 DEFAULT = [HEADLINE, "tiny", "colpali", "int8", "backward", "backward_varlen", "pairs_varlen",
            "two_stage", "topk", "chamfer", "dim_sweep"]
 MARK = "@@bench-result "
