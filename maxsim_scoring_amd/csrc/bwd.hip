@@ -32,6 +32,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace maxsim {
 
 namespace {
@@ -348,16 +350,124 @@ __device__ __forceinline__ void build_segment_csr(CsrLds& sm, int64_t nsrc, int6
     }
 }
 
-// Inverse map of doc j: row_ptr[j*Ld + t] and the doc's segment
-// col_idx[j*Nq*Lq, (j+1)*Nq*Lq). Every doc receives exactly Nq*Lq sources,
-// so no global scan is needed.
-__device__ __forceinline__ void csr_doc(const BwdArgs& a, CsrLds& sm, uint32_t j)
+// LDS of a workgroup that builds a small segment's map in one pass
+struct CsrSmallLds {
+    uint32_t hist[kCsrWaves][kCsrBins];  // per-wave counts, then per-wave slots
+    uint32_t wsum[kCsrWaves];
+    uint64_t grp[kCsrWaves][64];         // per wave: lanes holding equal keys, by representative lane
+    uint8_t owner[kCsrWaves][kCsrBins];  // per wave: representative lane of each key of a step
+    int32_t stage[kCsrChunk];            // the segment's col_idx entries, in place
+};
+
+// The inverse map of a segment small enough for one pass (the same map as
+// build_segment_csr): nsrc <= kCsrChunk sources, one register block per
+// wave, and L <= kCsrBins rows. Equal destinations within a step of a wave
+// are found through LDS instead of ballots over the key bits: every lane
+// writes its lane number into owner[key], so each group of equal keys reads
+// back one member as its representative, and an atomic OR of the lanes' bits
+// into grp[representative] gives each lane the set of its group (OR is order
+// free, so the set does not depend on which member won the write). A lane's
+// rank is the number of group members below it, and the lowest member adds
+// the group's size to the wave's histogram. The sources are then placed in
+// source order into `stage` (LDS) and copied out in one contiguous run.
+template <typename Load>
+__device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, int64_t L, int64_t carry,
+                                                int32_t* __restrict__ row_ptr_seg,
+                                                int32_t* __restrict__ col_idx, Load&& load)
 {
-    const int64_t Nd = a.Nd, Ld = a.Ld;
-    const uint32_t Lq = (uint32_t)a.Lq, nd = (uint32_t)Nd;
-    const uint32_t per_doc = (uint32_t)(a.Nq * a.Lq);
-    // doc-local source k = i*Lq + s is the flat source (i*Nd + j)*Lq + s
-    auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
+    constexpr int kPerWave = kCsrChunk / kCsrWaves;
+    constexpr int kSteps = kPerWave / 64;
+    const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t k0 = (int64_t)wave * kPerWave + lane;
+    int32_t tv[kSteps], sv[kSteps];
+    load(k0, tv, sv);  // every load in flight before the first use
+    for (int k = lane; k < L; k += 64) sm.hist[wave][k] = 0;
+    sm.grp[wave][lane] = 0;
+    uint32_t key[kSteps];
+#pragma unroll
+    for (int m = 0; m < kSteps; ++m) {
+        key[m] = kNoKey;
+        if (k0 + 64 * m < nsrc) {
+            int64_t t = tv[m];
+            t = t < 0 ? 0 : (t >= L ? L - 1 : t);  // precondition guard
+            key[m] = (uint32_t)t;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the zeroing lands before the counts
+    // a wave's LDS operations complete in issue order, so each read below
+    // sees the writes issued before it
+    // key[m] gains the lane's rank among the step's equal keys (bits 16-23)
+    // and, in the lowest of them, the group's size (bits 24-31). The owner
+    // and group reads are volatile: they must return what the other lanes
+    // wrote, not what this lane stored a moment before.
+    const uint64_t me = 1ull << lane;
+    typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
+    typedef __attribute__((address_space(3))) volatile uint64_t lds_u64;
+    lds_u8* owner = (lds_u8*)sm.owner[wave];
+    lds_u64* grp = (lds_u64*)sm.grp[wave];
+#pragma unroll
+    for (int m = 0; m < kSteps; ++m) {
+        const bool act = key[m] != kNoKey;
+        if (__ballot(act) == 0) continue;  // uniform
+        if (act) owner[key[m]] = (uint8_t)lane;
+        const uint32_t rep = act ? owner[key[m]] : 0u;
+        if (act) atomicOr(&sm.grp[wave][rep], me);
+        const uint64_t peers = act ? grp[rep] : 0ull;
+        const uint32_t rank = (uint32_t)__builtin_popcountll(peers & (me - 1ull));
+        const uint32_t n = (uint32_t)__builtin_popcountll(peers);
+        const bool lead = act && rank == 0;
+        if (lead) {
+            atomicAdd(&sm.hist[wave][key[m]], n);  // one lane per key
+            grp[rep] = 0;                          // free for the next step
+        }
+        key[m] |= (rank << 16) | (lead ? n << 24 : 0u);  // 0 for an inactive lane
+    }
+    barrier_lds();
+
+    // exclusive scan of the per-row totals (one row per thread)
+    uint32_t mine = 0;
+    if (tid < L)
+        for (int w = 0; w < kCsrWaves; ++w) mine += sm.hist[w][tid];
+    uint32_t incl = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) sm.wsum[wave] = incl;
+    barrier_lds();
+    uint32_t wave_off = 0;
+    for (int w = 0; w < wave; ++w) wave_off += sm.wsum[w];
+    if (tid < L) {
+        const uint32_t first = wave_off + incl - mine;
+        row_ptr_seg[tid] = (int32_t)(carry + first);
+        // slots: row k of wave w starts after the earlier waves' sources of row k
+        uint32_t pos = first;
+        for (int w = 0; w < kCsrWaves; ++w) {
+            const uint32_t h = sm.hist[w][tid];
+            sm.hist[w][tid] = pos;
+            pos += h;
+        }
+    }
+    barrier_lds();
+#pragma unroll
+    for (int m = 0; m < kSteps; ++m) {
+        if (key[m] != kNoKey) {
+            const uint32_t t = key[m] & 0xFFFFu, rank = (key[m] >> 16) & 0xFFu;
+            sm.stage[sm.hist[wave][t] + rank] = sv[m];
+            if (rank == 0) sm.hist[wave][t] += key[m] >> 24;
+        }
+    }
+    barrier_lds();
+    for (int64_t e = tid; e < nsrc; e += kCsrThreads) col_idx[carry + e] = sm.stage[e];
+}
+
+// Sources of doc j for the CSR builders: doc-local source k = i*Lq + s is
+// the flat source (i*Nd + j)*Lq + s.
+struct DocSources {
+    const int32_t* argmax;
+    uint32_t Lq, nd, j, per_doc;
+    __device__ __forceinline__ void operator()(int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) const
+    {
         SrcWalk w;
         w.init((uint32_t)k0, 64, Lq > 0 ? Lq : 1u);
 #pragma unroll
@@ -365,11 +475,28 @@ __device__ __forceinline__ void csr_doc(const BwdArgs& a, CsrLds& sm, uint32_t j
             const bool ok = k0 + 64 * m < per_doc;
             const uint32_t src = ok ? (w.i * nd + j) * Lq + w.s : 0u;
             sv[m] = (int32_t)src;
-            tv[m] = ok ? __builtin_nontemporal_load(a.argmax + src) : 0;
+            tv[m] = ok ? __builtin_nontemporal_load(argmax + src) : 0;
         }
-    };
-    build_segment_csr(sm, per_doc, Ld, (int64_t)j * per_doc, a.row_ptr + (int64_t)j * Ld, a.col_idx, load);
-    if (j == Nd - 1 && threadIdx.x == 0) a.row_ptr[Nd * Ld] = (int32_t)(a.Nq * Nd * a.Lq);
+    }
+};
+
+// Inverse map of doc j: row_ptr[j*Ld + t] and the doc's segment
+// col_idx[j*Nq*Lq, (j+1)*Nq*Lq). Every doc receives exactly Nq*Lq sources,
+// so no global scan is needed.
+__device__ __forceinline__ void csr_doc(const BwdArgs& a, CsrLds& sm, uint32_t j)
+{
+    const uint32_t per_doc = (uint32_t)(a.Nq * a.Lq);
+    const DocSources load{a.argmax, (uint32_t)a.Lq, (uint32_t)a.Nd, j, per_doc};
+    build_segment_csr(sm, per_doc, a.Ld, (int64_t)j * per_doc, a.row_ptr + (int64_t)j * a.Ld, a.col_idx, load);
+}
+
+// The same map for a doc small enough for the one-pass builder
+// (Nq*Lq <= kCsrChunk, Ld <= kCsrBins).
+__device__ __forceinline__ void csr_doc_small(const BwdArgs& a, CsrSmallLds& sm, uint32_t j)
+{
+    const uint32_t per_doc = (uint32_t)(a.Nq * a.Lq);
+    const DocSources load{a.argmax, (uint32_t)a.Lq, (uint32_t)a.Nd, j, per_doc};
+    build_csr_small(sm, per_doc, a.Ld, (int64_t)j * per_doc, a.row_ptr + (int64_t)j * a.Ld, a.col_idx, load);
 }
 
 // LDS of a dq workgroup with G row groups
@@ -489,12 +616,27 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
 template <int E, bool GEN>
 __global__ __launch_bounds__(kCsrThreads) void csr_dq_kernel(BwdArgs a, int64_t csr_blocks)
 {
+    // the general-width instances keep the ballot builder only: with their
+    // wider dq state the larger LDS block made their registers spill
     __shared__ union {
         CsrLds csr;
+        typename std::conditional<GEN, CsrLds, CsrSmallLds>::type small;
         DqLds<kCsrThreads / 16> dq;
     } sm;
-    if ((int64_t)blockIdx.x < csr_blocks) csr_doc(a, sm.csr, blockIdx.x);
-    else dq_block<E, GEN, kCsrThreads / 16>(a, sm.dq, (int64_t)blockIdx.x - csr_blocks);
+    const int64_t b = blockIdx.x;
+    if (b < csr_blocks) {
+        bool done = false;
+        if constexpr (!GEN) {
+            if (a.Nq * a.Lq <= kCsrChunk && a.Ld <= kCsrBins) {
+                csr_doc_small(a, sm.small, (uint32_t)b);
+                done = true;
+            }
+        }
+        if (!done) csr_doc(a, sm.csr, (uint32_t)b);
+        if (b == a.Nd - 1 && threadIdx.x == 0) a.row_ptr[a.Nd * a.Ld] = (int32_t)(a.Nq * a.Nd * a.Lq);
+    } else {
+        dq_block<E, GEN, kCsrThreads / 16>(a, sm.dq, b - csr_blocks);
+    }
 }
 
 // Eq. (3): dD[j,t] = sum over the CSR row of (j,t), in order, of

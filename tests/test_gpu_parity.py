@@ -335,6 +335,8 @@ BWD_CASES = [
                                                          # weights read per source
     (6, 3, 40, 700, torch.bfloat16, 0.1, 0.2, 1, 0.0),   # a doc's bins split over workgroups
     (1, 513, 2, 1030, torch.float16, 0.0, 0.0, 0, 0.0),  # one bin range per doc, two rounds
+    (3, 2, 5, 1, torch.float16, 0.0, 0.0, 0, 0.0),       # one row per doc: a row range with no rows
+    (64, 3, 256, 96, torch.bfloat16, 0.1, 0.1, 1, 0.0),  # exactly 16384 sources per doc
 ]
 
 
