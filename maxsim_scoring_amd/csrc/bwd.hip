@@ -617,7 +617,8 @@ template <int E, bool GEN>
 __global__ __launch_bounds__(kCsrThreads) void csr_dq_kernel(BwdArgs a, int64_t csr_blocks)
 {
     // the general-width instances keep the ballot builder only: with their
-    // wider dq state the larger LDS block made their registers spill
+    // wider dq state the one-pass builder's larger LDS block made their
+    // registers spill
     __shared__ union {
         CsrLds csr;
         typename std::conditional<GEN, CsrLds, CsrSmallLds>::type small;
@@ -865,7 +866,10 @@ __global__ __launch_bounds__(kPrepThreads) void vbwd_prep_kernel(VarBwdArgs a)
 // start the prep pass parked in dD. Source p (a packed query row) belongs to
 // the query found by a search of cu_q once per lane, then by walking forward
 // as p grows.
-__device__ __forceinline__ void vbwd_csr_doc(const VarBwdArgs& a, CsrLds& sm, int64_t j)
+// SMALL: a doc with at most kCsrBins rows is built by the one-pass builder
+// when the segment has at most kCsrChunk sources.
+template <bool SMALL, typename SmallLds>
+__device__ __forceinline__ void vbwd_csr_doc(const VarBwdArgs& a, CsrLds& sm, SmallLds& small, int64_t j)
 {
     const int64_t Nd = a.Nd, Tq = a.Tq;
     const int64_t d0 = a.cu_d[j];
@@ -894,6 +898,12 @@ __device__ __forceinline__ void vbwd_csr_doc(const VarBwdArgs& a, CsrLds& sm, in
         }
     };
     const int64_t carry = (int64_t)__builtin_bit_cast(uint32_t, a.dD[d0 * a.d]);  // parked by prep
+    if constexpr (SMALL) {
+        if (Tq <= kCsrChunk && L <= kCsrBins) {
+            build_csr_small(small, Tq, L, carry, a.row_ptr + d0, a.col_idx, load);
+            return;
+        }
+    }
     build_segment_csr(sm, Tq, L, carry, a.row_ptr + d0, a.col_idx, load);
 }
 
@@ -1013,11 +1023,13 @@ __device__ __forceinline__ void vbwd_dq_block(const VarBwdArgs& a, VdqLds<G>& sm
 template <int E, bool GEN>
 __global__ __launch_bounds__(kCsrThreads) void vbwd_csr_dq_kernel(VarBwdArgs a, int64_t csr_blocks)
 {
+    // one-pass CSR builder for the 128-wide instances only, as in csr_dq_kernel
     __shared__ union {
         CsrLds csr;
+        typename std::conditional<GEN, CsrLds, CsrSmallLds>::type small;
         VdqLds<kCsrThreads / 16> dq;
     } sm;
-    if ((int64_t)blockIdx.x < csr_blocks) vbwd_csr_doc(a, sm.csr, blockIdx.x);
+    if ((int64_t)blockIdx.x < csr_blocks) vbwd_csr_doc<!GEN>(a, sm.csr, sm.small, blockIdx.x);
     else vbwd_dq_block<E, GEN, kCsrThreads / 16>(a, sm.dq, (int64_t)blockIdx.x - csr_blocks);
 }
 
