@@ -89,6 +89,28 @@ def warm_up(torch, fn, warmup: int) -> None:
     WARMUP_LOG.append((n, round(time.perf_counter() - t0, 3)))
 
 
+FLUSH_BYTES = 512 << 20
+FLUSH_PREWRITES = 32
+_FLUSH = []  # the process's cache-flush buffer, once written
+
+
+def flush_buffer(torch):
+    """The process's 512 MiB cache-flush buffer (twice the last-level cache).
+    It is allocated once and written FLUSH_PREWRITES times before any timed
+    region: while a freshly allocated buffer of this size had been written
+    only a few times, the kernels launched between its writes ran slower (the
+    ColPali kernel took 427-478 us per launch in the kernel trace, against
+    398 us for the same launches once the buffer had been written about 20
+    times), which would charge a one-time cost of the process to the kernel."""
+    if not _FLUSH:
+        buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        for _ in range(FLUSH_PREWRITES):
+            buf.fill_(1.0)
+        torch.cuda.synchronize()
+        _FLUSH.append(buf)
+    return _FLUSH[0]
+
+
 def time_steps(torch, fn, steps: int, warmup: int, flush_bytes: int = 0):
     """Times `fn` (one launch per call) with HIP events on torch's current
     stream, which is the stream the library launches on. Without a flush the
@@ -106,7 +128,8 @@ def time_steps(torch, fn, steps: int, warmup: int, flush_bytes: int = 0):
         torch.cuda.synchronize()
         total = e0.elapsed_time(e1)
         return total, [total / steps]
-    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    assert flush_bytes == FLUSH_BYTES
+    scratch = flush_buffer(torch)
     times = []
     for _ in range(steps):
         scratch.fill_(1.0)
@@ -198,7 +221,7 @@ def bench_tiny(torch, ms, synth, wl, steps, warmup):
     def step():
         ms.maxsim_fwd(Q, D, scores=scores, argmax=argmax)
 
-    total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
+    total, times = time_steps(torch, step, steps, warmup, flush_bytes=FLUSH_BYTES)
     t = statistics.median(times)
     nbytes = wl.dense_fwd_bytes(4, 32, 32, 180, 128, 2, False, False, True)
     return {"workload": w.name, "ms": t, **spread(times), "pairs_per_s": 128 / (t * 1e-3),
@@ -216,7 +239,7 @@ def bench_colpali(torch, ms, synth, wl, steps, warmup):
     def step():
         ms.maxsim_fwd(Q, D, qm, dm, scores=scores, argmax=argmax)
 
-    total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
+    total, times = time_steps(torch, step, steps, warmup, flush_bytes=FLUSH_BYTES)
     t = statistics.median(times)
     valid = int(w.d_mask.sum())
     flops = wl.dense_fwd_flops(128, 128, 128, valid)
@@ -264,7 +287,7 @@ def bench_dim_sweep(torch, ms, synth, wl, steps, warmup):
         def step():
             ms.maxsim_fwd(Q, D, scores=scores)
 
-        total, times = time_steps(torch, step, min(steps, 10), min(warmup, 5), flush_bytes=512 << 20)
+        total, times = time_steps(torch, step, min(steps, 10), min(warmup, 5), flush_bytes=FLUSH_BYTES)
         t = statistics.median(times)
         nbytes = wl.dense_fwd_bytes(1, 10_000, 32, 128, d, 2, False, False, False)
         rows[f"d{d}"] = {"workload": w.name, "ms": t, **spread(times), "docs_per_s": 10_000 / (t * 1e-3),
@@ -298,7 +321,7 @@ def bench_batch_sweep(torch, ms, synth, wl, steps, warmup):
         def step():
             ms.maxsim_fwd(Q, D, scores=scores)
 
-        flush = 512 << 20 if B * 128 * 256 < (256 << 20) else 0
+        flush = FLUSH_BYTES if B * 128 * 256 < (256 << 20) else 0
         total, times = time_steps(torch, step, steps, warmup, flush_bytes=flush)
         t = statistics.median(times) if flush else total / steps
         nbytes = wl.dense_fwd_bytes(1, B, 32, 128, 128, 2, False, False, False)
@@ -323,7 +346,7 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
     def step():
         ms.maxsim_bwd(Q, D, argmax, g, qm, dm, dQ=dQ, dD=dD, csr_row_ptr=rp, csr_col_idx=ci)
 
-    total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
+    total, times = time_steps(torch, step, steps, warmup, flush_bytes=FLUSH_BYTES)
     t = statistics.median(times)
     nbytes = wl.bwd_compulsory_bytes(128, 128, 128, 1024, 128, 2, True, True)
     # the row gathers the two passes make beyond the compulsory bytes (served
@@ -359,7 +382,7 @@ def bench_backward_varlen(torch, ms, synth, wl, steps, warmup):
         ms.maxsim_bwd_varlen(Q, cu_q, 128, D, cu_d, argmax, g, dQ=dQ, dD=dD, csr_row_ptr=rp,
                              csr_col_idx=ci)
 
-    total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
+    total, times = time_steps(torch, step, steps, warmup, flush_bytes=FLUSH_BYTES)
     t = statistics.median(times)
     nbytes = wl.bwd_varlen_compulsory_bytes(128, 128, 128, Tq, Td, 128, 128, 2)
     gathered = 2 * Tq * 128 * 128 * 2  # a D row per (query row, doc) for dQ, a Q row per CSR entry for dD
@@ -474,7 +497,7 @@ def bench_topk(torch, ms, synth, wl, steps, warmup):
     def step():
         ms.maxsim_topk(v, 100, idx=idx, val=val)
 
-    total, times = time_steps(torch, step, steps, warmup, flush_bytes=512 << 20)
+    total, times = time_steps(torch, step, steps, warmup, flush_bytes=FLUSH_BYTES)
     t = statistics.median(times)
     nbytes = 100_000 * 4
     return {"workload": "topk_1x100000_k100", "ms": t, **spread(times),
@@ -534,7 +557,7 @@ def bench_yardstick(torch, ms, synth, wl, steps, warmup):
     for d in DIM_SWEEP:
         nb = 10_000 * 128 * d * 2
         x = torch.ones(nb // 8, dtype=torch.int64, device="cuda")
-        _, times = time_steps(torch, lambda: x.sum(), min(steps, 10), min(warmup, 5), flush_bytes=512 << 20)
+        _, times = time_steps(torch, lambda: x.sum(), min(steps, 10), min(warmup, 5), flush_bytes=FLUSH_BYTES)
         t = statistics.median(times)
         out[f"read_sum_d{d}"] = {"ms": t, "bytes": nb,
                                  "roofline": roofline("hbm", nb / (t * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
@@ -545,7 +568,7 @@ def bench_yardstick(torch, ms, synth, wl, steps, warmup):
     src = torch.ones((128 * 1024, 128), dtype=torch.bfloat16, device="cuda")
     idx = torch.randint(0, 128 * 1024, (128 * 128 * 128,), device="cuda", generator=gen)
     _, times = time_steps(torch, lambda: torch.index_select(src, 0, idx), min(steps, 10), min(warmup, 5),
-                          flush_bytes=512 << 20)
+                          flush_bytes=FLUSH_BYTES)
     t = statistics.median(times)
     nb = idx.numel() * 256
     out["gather_rows_537MB"] = {"ms": t, "bytes_gathered": nb, "gathered_GBps": round(nb / (t * 1e-3) / 1e9, 1)}
@@ -682,6 +705,7 @@ def run_child(args) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     ms.binding.lib()  # fails loudly without the built library
+    flush_buffer(torch)  # written before the workload's warm-up and timing
     name = args.child
     _log(f"workload {name}: generating inputs and timing {args.steps} steps")
     r = FNS[name](torch, ms, synth, wl, args.steps, args.warmup)
