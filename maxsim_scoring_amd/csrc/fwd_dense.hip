@@ -633,7 +633,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 // MFMA has been issued (a rolling prefetch of the next M-tile)
                 // The wave issues its MFMA chain at raised priority, so that
                 // the SIMD's other wave (folding or reading LDS) yields the
-                // issue slots while the chain is being fed (2-4 % at C3). Not
+                // issue slots while the chain is being fed (2 % on the 128 x 128 bf16
+                // ColPali pairs, 3 % on the 1024-token int8 query). Not
                 // with per-token scales, whose VALU-heavy fold it slows down.
                 auto mma = [&](i32x4 (&af)[KS], int n, int next, const Acc& init) {
                     Acc acc = init;
