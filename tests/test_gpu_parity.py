@@ -337,6 +337,8 @@ BWD_CASES = [
     (1, 513, 2, 1030, torch.float16, 0.0, 0.0, 0, 0.0),  # one bin range per doc, two rounds
     (3, 2, 5, 1, torch.float16, 0.0, 0.0, 0, 0.0),       # one row per doc: a row range with no rows
     (64, 3, 256, 96, torch.bfloat16, 0.1, 0.1, 1, 0.0),  # exactly 16384 sources per doc
+    (8, 3, 100, 300, torch.float16, 0.0, 0.0, 0, 1.0),   # every source of a doc in one row:
+                                                         # groups of 64 equal keys per step
 ]
 
 
@@ -515,6 +517,8 @@ VARBWD_CASES = [
     ([0, 3, 0], [4, 0, 4], torch.bfloat16, 0.0, True),            # empty queries
     ([3], [0, 0], torch.float16, 0.0, True),                      # no doc token at all
     ([0], [5, 3], torch.float16, 0.0, True),                      # no query row at all
+    ([128] * 128, [100, 1024, 1], torch.bfloat16, 1.0, False),    # 16384 rows, docs of up to 1024
+                                                                   # rows, every source in one row
 ]
 
 
