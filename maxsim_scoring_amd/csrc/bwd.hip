@@ -1323,13 +1323,15 @@ __global__ __launch_bounds__(kCsrThreads) void cham_bucket_kernel(ChamferArgs a,
     const int64_t L = c.nr - t0 < kCsrBins ? c.nr - t0 : kCsrBins;
     const int32_t last = (int32_t)(c.nr - 1);
     const int64_t sbase = c.b * c.ns;
+    // local source indices are below ns < 2^31 (the entry point bounds B*N and B*M)
+    const int32_t ns_last = (int32_t)(c.ns - 1);
     auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
-        int64_t loc[16];
+        int32_t loc[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int64_t k = k0 + 64 * m;
-            int64_t v = k < cnt ? part[k_beg + k] : 0;
-            loc[m] = v < 0 ? 0 : (v >= c.ns ? c.ns - 1 : v);
+            const int32_t v = k < cnt ? part[k_beg + k] : 0;
+            loc[m] = v < 0 ? 0 : (v > ns_last ? ns_last : v);
         }
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
@@ -1340,8 +1342,14 @@ __global__ __launch_bounds__(kCsrThreads) void cham_bucket_kernel(ChamferArgs a,
             tv[m] = (int32_t)(t - t0);  // in [0, L) for a bucket's own sources
         }
     };
-    __shared__ CsrLds sm;
-    build_segment_csr<kCsrFull>(sm, cnt, L, sbase + k_beg, c.row_ptr + c.b * c.nr + t0, c.col_idx, load);
+    __shared__ union {
+        CsrLds csr;
+        CsrSmallLds small;
+    } sm;
+    if (cnt <= kCsrChunk)  // one pass (L <= kCsrBins always)
+        build_csr_small(sm.small, cnt, L, sbase + k_beg, c.row_ptr + c.b * c.nr + t0, c.col_idx, load);
+    else
+        build_segment_csr<kCsrFull>(sm.csr, cnt, L, sbase + k_beg, c.row_ptr + c.b * c.nr + t0, c.col_idx, load);
     if (c.b == a.B - 1 && r == R - 1 && threadIdx.x == 0) c.row_ptr[a.B * c.nr] = (int32_t)(a.B * c.ns);
 }
 
