@@ -42,6 +42,8 @@ constexpr int kCsrWaves = 16;
 constexpr int kCsrThreads = kCsrWaves * 64;
 constexpr int kCsrChunk = 16384;  // sources of one doc held in registers per pass (16 per lane)
 constexpr int kCsrBins = 1024;    // destination bins handled per round
+constexpr int kPartSteps = 4;     // sources per lane in a chunk of the Chamfer partition
+constexpr int kPartChunk = kCsrWaves * 64 * kPartSteps;  // 4,096 sources per partition chunk
 constexpr int kDqDocs = 64;                   // docs staged per round of the dq pass
 constexpr uint16_t kNoKey = 0xFFFF;
 #ifndef MAXSIM_DD_WAVES
@@ -359,31 +361,32 @@ struct CsrSmallLds {
     int32_t stage[kCsrChunk];            // the segment's col_idx entries, in place
 };
 
-// The inverse map of a segment small enough for one pass (the same map as
-// build_segment_csr): nsrc <= kCsrChunk sources, one register block per
-// wave, and L <= kCsrBins rows. Equal destinations within a step of a wave
-// are found through LDS instead of ballots over the key bits: every lane
-// writes its lane number into owner[key], so each group of equal keys reads
-// back one member as its representative, and an atomic OR of the lanes' bits
-// into grp[representative] gives each lane the set of its group (OR is order
+// One pass over a block of at most kCsrWaves * 64 * STEPS sources (STEPS per
+// lane, one register block per wave) with destinations in [0, L), L <= kCsrBins: loads them, ranks each
+// source among the equal destinations of its wave's step, and counts them
+// into the waves' LDS histograms. Equal destinations within a step are found
+// through LDS instead of ballots over the key bits: every lane writes its
+// lane number into owner[key], so each group of equal keys reads back one
+// member as its representative, and an atomic OR of the lanes' bits into
+// grp[representative] gives each lane the set of its group (OR is order
 // free, so the set does not depend on which member won the write). A lane's
 // rank is the number of group members below it, and the lowest member adds
-// the group's size to the wave's histogram. The sources are then placed in
-// source order into `stage` (LDS) and copied out in one contiguous run.
-template <typename Load>
-__device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, int64_t L, int64_t carry,
-                                                int32_t* __restrict__ row_ptr_seg,
-                                                int32_t* __restrict__ col_idx, Load&& load)
+// the group's size to the wave's histogram, so a row that receives many
+// sources costs no more than any other. On return (after a barrier)
+// key[m] = destination | rank << 16 | (group size << 24 in the lowest
+// member), or kNoKey past the block's end, and sv[m] is the source's value.
+template <int STEPS, typename Load>
+__device__ __forceinline__ void rank_block(CsrSmallLds& sm, int64_t nsrc, int64_t L, Load&& load,
+                                           uint32_t (&key)[STEPS], int32_t (&sv)[STEPS])
 {
-    constexpr int kPerWave = kCsrChunk / kCsrWaves;
-    constexpr int kSteps = kPerWave / 64;
+    constexpr int kSteps = STEPS;
+    constexpr int kPerWave = 64 * STEPS;
     const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t k0 = (int64_t)wave * kPerWave + lane;
-    int32_t tv[kSteps], sv[kSteps];
+    int32_t tv[kSteps];
     load(k0, tv, sv);  // every load in flight before the first use
     for (int k = lane; k < L; k += 64) sm.hist[wave][k] = 0;
     sm.grp[wave][lane] = 0;
-    uint32_t key[kSteps];
 #pragma unroll
     for (int m = 0; m < kSteps; ++m) {
         key[m] = kNoKey;
@@ -395,11 +398,9 @@ __device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, i
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // the zeroing lands before the counts
     // a wave's LDS operations complete in issue order, so each read below
-    // sees the writes issued before it
-    // key[m] gains the lane's rank among the step's equal keys (bits 16-23)
-    // and, in the lowest of them, the group's size (bits 24-31). The owner
-    // and group reads are volatile: they must return what the other lanes
-    // wrote, not what this lane stored a moment before.
+    // sees the writes issued before it; the owner and group reads are
+    // volatile: they must return what the other lanes wrote, not what this
+    // lane stored a moment before
     const uint64_t me = 1ull << lane;
     typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
     typedef __attribute__((address_space(3))) volatile uint64_t lds_u64;
@@ -423,8 +424,15 @@ __device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, i
         key[m] |= (rank << 16) | (lead ? n << 24 : 0u);  // 0 for an inactive lane
     }
     barrier_lds();
+}
 
-    // exclusive scan of the per-row totals (one row per thread)
+// Exclusive scan of the block's per-row totals (one row per thread, rows
+// [0, L)), then per-wave first slots in sm.hist: row r of wave w starts after
+// the earlier rows and the earlier waves' sources of row r. Returns this
+// thread's row's first slot and total (0 past L); the slots are block-local.
+__device__ __forceinline__ void block_slots(CsrSmallLds& sm, int64_t L, uint32_t& first, uint32_t& total)
+{
+    const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
     uint32_t mine = 0;
     if (tid < L)
         for (int w = 0; w < kCsrWaves; ++w) mine += sm.hist[w][tid];
@@ -437,10 +445,9 @@ __device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, i
     barrier_lds();
     uint32_t wave_off = 0;
     for (int w = 0; w < wave; ++w) wave_off += sm.wsum[w];
+    first = wave_off + incl - mine;
+    total = mine;
     if (tid < L) {
-        const uint32_t first = wave_off + incl - mine;
-        row_ptr_seg[tid] = (int32_t)(carry + first);
-        // slots: row k of wave w starts after the earlier waves' sources of row k
         uint32_t pos = first;
         for (int w = 0; w < kCsrWaves; ++w) {
             const uint32_t h = sm.hist[w][tid];
@@ -449,8 +456,16 @@ __device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, i
         }
     }
     barrier_lds();
+}
+
+// Each ranked source into sm.stage at its block-local slot, in source order
+// within every row.
+template <int STEPS>
+__device__ __forceinline__ void stage_block(CsrSmallLds& sm, const uint32_t (&key)[STEPS], const int32_t (&sv)[STEPS])
+{
+    const int wave = (int)threadIdx.x >> 6;
 #pragma unroll
-    for (int m = 0; m < kSteps; ++m) {
+    for (int m = 0; m < STEPS; ++m) {
         if (key[m] != kNoKey) {
             const uint32_t t = key[m] & 0xFFFFu, rank = (key[m] >> 16) & 0xFFu;
             sm.stage[sm.hist[wave][t] + rank] = sv[m];
@@ -458,7 +473,67 @@ __device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, i
         }
     }
     barrier_lds();
+}
+
+// The inverse map of a segment small enough for one pass (the same map as
+// build_segment_csr): nsrc <= kCsrChunk sources and L <= kCsrBins rows. The
+// sources are ranked (rank_block), the row totals scanned into row_ptr, the
+// sources placed in source order into `stage` (LDS), and the segment written
+// out in one contiguous run.
+template <typename Load>
+__device__ __forceinline__ void build_csr_small(CsrSmallLds& sm, int64_t nsrc, int64_t L, int64_t carry,
+                                                int32_t* __restrict__ row_ptr_seg,
+                                                int32_t* __restrict__ col_idx, Load&& load)
+{
+    constexpr int kSteps = kCsrChunk / kCsrWaves / 64;
+    const int tid = (int)threadIdx.x;
+    uint32_t key[kSteps];
+    int32_t sv[kSteps];
+    rank_block<kSteps>(sm, nsrc, L, load, key, sv);
+    uint32_t first, total;
+    block_slots(sm, L, first, total);
+    if (tid < L) row_ptr_seg[tid] = (int32_t)(carry + first);
+    stage_block<kSteps>(sm, key, sv);
     for (int64_t e = tid; e < nsrc; e += kCsrThreads) col_idx[carry + e] = sm.stage[e];
+}
+
+// One chunk of a stable partition by row in one pass: the chunk's sources
+// (nsrc <= kCsrWaves * 64 * STEPS) with rows in [0, L), L <= kCsrBins. COUNT writes the
+// chunk's per-row counts to row_arr[r]; otherwise row_arr[r] holds the
+// absolute first slot of the chunk's run in row r (from the scan over the
+// chunks), and each source goes to out at its run's slot in source order,
+// every run written contiguously. Slots are kept below out_len for any
+// row_arr content.
+template <bool COUNT, int STEPS, typename Load>
+__device__ __forceinline__ void place_small(CsrSmallLds& sm, int64_t nsrc, int64_t L, int32_t* __restrict__ row_arr,
+                                            int32_t* __restrict__ out, int64_t out_len, Load&& load)
+{
+    const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    uint32_t key[STEPS];
+    int32_t sv[STEPS];
+    rank_block<STEPS>(sm, nsrc, L, load, key, sv);
+    uint32_t first, total;
+    block_slots(sm, L, first, total);
+    if constexpr (COUNT) {
+        if (tid < L) row_arr[tid] = (int32_t)total;
+        return;
+    }
+    // the rows' block-local starts and sizes, in the owner area (free now)
+    uint32_t* rstart = (uint32_t*)&sm.owner[0][0];
+    uint32_t* rsize = rstart + kCsrBins;
+    if (tid < L) {
+        rstart[tid] = first;
+        rsize[tid] = total;
+    }
+    stage_block<STEPS>(sm, key, sv);  // ends with a barrier
+    for (int64_t r = wave; r < L; r += kCsrWaves) {
+        const uint32_t n = rsize[r], s0 = rstart[r];
+        const int64_t d0 = row_arr[r];
+        for (uint32_t i = lane; i < n; i += 64) {
+            const int64_t d = d0 + i;
+            if (d >= 0 && d < out_len) out[d] = sm.stage[s0 + i];
+        }
+    }
 }
 
 // Sources of doc j for the CSR builders: doc-local source k = i*Lq + s is
@@ -1207,13 +1282,16 @@ __global__ __launch_bounds__(kCsrThreads) void cham_csr_kernel(ChamferArgs a, in
 
 // The two CSRs in two steps, when the scratch fits (see the launcher):
 // 1. a stable partition of each segment's sources by bucket of kCsrBins rows
-//    (destination / 1024), over chunks of kCsrChunk sources: per chunk the
+//    (destination / 1024), over chunks of kPartChunk sources: per chunk the
 //    bucket counts (cham_part_kernel<kCsrCount>), per segment the scan that
 //    turns them into each chunk's first slot per bucket and the bucket starts
 //    (cham_part_scan_kernel), per chunk the stable scatter of the local
-//    source indices in bucket order (cham_part_kernel<kCsrScatter>);
+//    source indices in bucket order (cham_part_kernel<kCsrScatter>), each
+//    chunk pass ranked through LDS in one pass (place_small) and the scatter
+//    written run by run;
 // 2. cham_bucket_kernel, one workgroup per (segment, bucket): the CSR rows of
-//    the bucket from the bucket's own sources, in source order.
+//    the bucket from the bucket's own sources, in source order (one pass when
+//    the bucket has at most kCsrChunk sources).
 // Scratch of a segment with ns sources, nchunk chunks and R buckets, in its
 // share of dP (the first CSR's sources are P points) or dQ (second CSR) as
 // ints, which the gradient kernel writes last: the partition [0, ns), the
@@ -1232,7 +1310,7 @@ __device__ __forceinline__ ChamPart cham_part(const ChamferArgs& a, const ChamSe
     ChamPart p;
     p.part = (int32_t*)(second ? a.dQ : a.dP) + c.b * c.ns * 3;
     p.R = (c.nr + kCsrBins - 1) / kCsrBins;
-    p.nchunk = (c.ns + kCsrChunk - 1) / kCsrChunk;
+    p.nchunk = (c.ns + kPartChunk - 1) / kPartChunk;
     p.start = p.part + c.ns;
     p.cnt = p.start + p.R + 1;
     return p;
@@ -1249,13 +1327,13 @@ __global__ __launch_bounds__(kCsrThreads) void cham_part_kernel(ChamferArgs a, i
     const bool second = g >= a.B;
     const ChamSeg c = cham_seg(a, g);
     const ChamPart p = cham_part(a, c, second);
-    const int64_t k_lo = ch * kCsrChunk;
-    const int64_t n = c.ns - k_lo < kCsrChunk ? c.ns - k_lo : kCsrChunk;
+    const int64_t k_lo = ch * kPartChunk;
+    const int64_t n = c.ns - k_lo < kPartChunk ? c.ns - k_lo : kPartChunk;
     const int32_t last = (int32_t)(c.nr - 1);
     const int32_t* idx = c.idx + c.b * c.ns + k_lo;
-    auto load = [&](int64_t k0, int32_t (&tv)[16], int32_t (&sv)[16]) {
+    auto load = [&](int64_t k0, int32_t (&tv)[kPartSteps], int32_t (&sv)[kPartSteps]) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
+        for (int m = 0; m < kPartSteps; ++m) {
             const int64_t k = k0 + 64 * m;
             const bool ok = k < n;
             sv[m] = (int32_t)(ok ? k_lo + k : 0);
@@ -1264,8 +1342,10 @@ __global__ __launch_bounds__(kCsrThreads) void cham_part_kernel(ChamferArgs a, i
             tv[m] = t / kCsrBins;
         }
     };
-    __shared__ CsrLds sm;
-    build_segment_csr<MODE>(sm, n, p.R, 0, p.cnt + ch * p.R, p.part, load);
+    // one pass per chunk of kPartChunk sources (this path runs only with
+    // R <= kCsrBins buckets); short chunks give the few segments many workgroups
+    __shared__ CsrSmallLds sm;
+    place_small<MODE == kCsrCount, kPartSteps>(sm, n, p.R, p.cnt + ch * p.R, p.part, c.ns, load);
 }
 
 // per segment: bucket totals over the chunks, their exclusive scan (the
@@ -1278,9 +1358,17 @@ __global__ __launch_bounds__(kCsrBins) void cham_part_scan_kernel(ChamferArgs a)
     const ChamSeg c = cham_seg(a, g);
     const ChamPart p = cham_part(a, c, second);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the chunk counts of this bucket, 8 loads in flight at a time
+    constexpr int kB = 8;
     uint32_t tot = 0;
     if (tid < p.R)
-        for (int64_t ch = 0; ch < p.nchunk; ++ch) tot += (uint32_t)p.cnt[ch * p.R + tid];
+        for (int64_t c0 = 0; c0 < p.nchunk; c0 += kB) {
+            uint32_t v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[u] = c0 + u < p.nchunk ? (uint32_t)p.cnt[(c0 + u) * p.R + tid] : 0u;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) tot += v[u];
+        }
     uint32_t incl = tot;
     for (int off = 1; off < 64; off <<= 1) {
         const uint32_t v = __shfl_up(incl, off, 64);
@@ -1293,10 +1381,16 @@ __global__ __launch_bounds__(kCsrBins) void cham_part_scan_kernel(ChamferArgs a)
     if (tid < p.R) {
         uint32_t run = base + incl - tot;
         p.start[tid] = (int32_t)run;
-        for (int64_t ch = 0; ch < p.nchunk; ++ch) {
-            const uint32_t v = (uint32_t)p.cnt[ch * p.R + tid];
-            p.cnt[ch * p.R + tid] = (int32_t)run;
-            run += v;
+        for (int64_t c0 = 0; c0 < p.nchunk; c0 += kB) {
+            uint32_t v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[u] = c0 + u < p.nchunk ? (uint32_t)p.cnt[(c0 + u) * p.R + tid] : 0u;
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (c0 + u < p.nchunk) {
+                    p.cnt[(c0 + u) * p.R + tid] = (int32_t)run;
+                    run += v[u];
+                }
         }
     }
     if (tid == 0) p.start[p.R] = (int32_t)c.ns;
@@ -1455,7 +1549,7 @@ hipError_t launch_chamfer_bwd(ChamferArgs a, hipStream_t stream)
     // the two-step build keeps ns + R + 1 + nchunk * R ints in a segment's
     // 3 * ns floats of dP (or dQ), and its partition passes handle up to
     // kCsrBins buckets (segments of at most about 1 M rows)
-    const int64_t c1 = (a.N + kCsrChunk - 1) / kCsrChunk, c2 = (a.M + kCsrChunk - 1) / kCsrChunk;
+    const int64_t c1 = (a.N + kPartChunk - 1) / kPartChunk, c2 = (a.M + kPartChunk - 1) / kPartChunk;
     if (r1 <= kCsrBins && r2 <= kCsrBins && r1 + 1 + c1 * r1 <= 2 * a.N && r2 + 1 + c2 * r2 <= 2 * a.M) {
         const unsigned pw = (unsigned)(a.B * (c1 + c2));
         hipLaunchKernelGGL(cham_part_kernel<kCsrCount>, dim3(pw), dim3(kCsrThreads), 0, stream, a, (int)c1, (int)c2);
