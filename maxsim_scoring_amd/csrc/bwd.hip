@@ -13,9 +13,12 @@
 //           CSR segment starts at j*Nq*Lq and no global scan is needed. Each
 //           wave holds the destinations of a contiguous block of the doc's
 //           sources in registers and counts them into its own LDS histogram;
-//           the counts are scanned, and every wave scatters its block in
-//           source order (ranks inside a wave from ballots over the key
-//           bits), so each CSR row lists its sources ascending. The other
+//           the counts are scanned, and every wave places its block in
+//           source order (ranks inside a wave from equal destinations found
+//           through LDS, or for docs too large for one pass from ballots
+//           over the key bits), so each CSR row lists its sources
+//           ascending; a one-pass doc is staged in LDS and written out
+//           contiguously. The other
 //           workgroups compute dQ, which needs no CSR: one 16-lane group per
 //           query row (i,s), 64 rows per workgroup; the argmax entries and
 //           weights g[i,j] live(j) of 64 docs at a time are staged in LDS
