@@ -37,8 +37,10 @@
  *     offsets past the packed tensors read out of bounds.
  *   - Sizes of 0 are valid. Nq == 0 or Nd == 0 enqueues nothing.
  *   - Reductions run in a fixed order and no result is written by an atomic
- *     (the CSR and top-k builders count with LDS integer histograms only):
- *     results are bitwise reproducible run to run.
+ *     (the CSR and top-k builders use integer atomics on LDS only, for
+ *     counts and for the sets of lanes holding equal keys, whose outcome
+ *     does not depend on their order): results are bitwise reproducible run
+ *     to run.
  *   - Ties among equal maxima go to the lowest doc-token index.
  */
 #ifndef MAXSIM_H
@@ -294,7 +296,8 @@ maxsim_status_t maxsim_chamfer_fwd(const float* P, const float* Q, int64_t B, in
  *   csr_row_ptr1 [B*M+1], csr_col_idx1 [B*N]: outputs, the inverse of idx1
  *   (row b*M + q lists the flat indices b*N + p that chose it, ascending);
  *   csr_row_ptr2 [B*N+1], csr_col_idx2 [B*M]: the inverse of idx2.
- * Sums run in fp32 in a fixed order (the CSR row order); no atomics. dP and
+ * Sums run in fp32 in a fixed order (the CSR row order); no atomics on
+ * results (the CSR builds count in LDS as in maxsim_bwd). dP and
  * dQ hold intermediates of the CSR build until the gradients are written.
  * B == 0 enqueues nothing. Errors as maxsim_chamfer_fwd, OVERFLOW also when
  * B*N + 1 or B*M + 1 >= 2^31.
