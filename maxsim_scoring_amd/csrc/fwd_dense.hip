@@ -27,13 +27,14 @@
 // meet in LDS and are added in slot order, so the result does not depend on
 // timing.
 //
-// Argmax: a lane keeps its running max and the row base of the M-tile that
-// last raised it; when an M-tile raises it, the lane's 16 values of that
-// M-tile are stored to a per-lane LDS slot (an exec-masked store, so lanes
-// whose max did not change issue nothing). At the end of the doc the lowest
-// saved row holding the max is the argmax. Keeping the saved values in LDS
-// rather than selecting them into registers takes the 16 selects per value
-// tile off the VALU, which shares its issue port with the MFMAs.
+// Argmax: a lane keeps its running max and the base row of the values it
+// last saved; when an M-tile raises the max, the half of the lane's 16 values
+// of that M-tile that holds the first occurrence of the new max is stored to
+// a per-lane LDS slot (an exec-masked store, so lanes whose max did not
+// change issue nothing). At the end of the doc the lowest saved row holding
+// the max is the argmax. Keeping the saved values in LDS rather than
+// selecting them into registers takes the 16 selects per value tile off the
+// VALU, which shares its issue port with the MFMAs.
 #include <type_traits>
 
 #include "common.hpp"
@@ -140,9 +141,9 @@ __device__ __forceinline__ void static_for(F&& f)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Running state of one N-tile for the lane's 16 rows of each M-tile: the
-// running max and, with argmax, the row base of the M-tile that last raised
-// it (a strict '>' across M-tiles in ascending t keeps the earlier one on
-// ties). That M-tile's 16 values sit in the lane's LDS slot.
+// running max and, with argmax, the base row of the values saved when an
+// M-tile last raised it (a strict '>' across M-tiles in ascending t keeps the
+// earlier one on ties). Those values sit in the lane's LDS slot.
 template <typename V, bool ARGMAX> struct RowState;
 template <typename V> struct RowState<V, false> {
     V m;
@@ -180,34 +181,71 @@ __device__ __forceinline__ V max16(const V (&v)[16])
     return vmax(vmax3(a, b, c), vmax3(d, e, v[15]));
 }
 
+// 16-byte chunks of a raised M-tile that a lane saves: the half of its 16
+// values (in the lane's row order) that holds the first occurrence of the
+// tile max. Against saving all 16 values this costs a compare and 8 selects
+// per raise and halves the LDS stores and the slot memory, which ran the
+// 128 x 128 bf16 ColPali pairs 2 % faster.
+constexpr int kSaveChunks = 2;
+static_assert(kSaveChunks == 1 || kSaveChunks == 2 || kSaveChunks == 4, "saved chunks per raise");
+
+// max of v[B .. B+N-1], N in {4, 8, 16}
+template <int B, int N, typename V>
+__device__ __forceinline__ V max_run(const V (&v)[16])
+{
+    if constexpr (N == 4) return vmax(vmax3(v[B], v[B + 1], v[B + 2]), v[B + 3]);
+    else if constexpr (N == 8) return vmax3(vmax3(v[B], v[B + 1], v[B + 2]), vmax3(v[B + 3], v[B + 4], v[B + 5]), vmax(v[B + 6], v[B + 7]));
+    else return max16(v);
+}
+
 // Fold one 32x32 accumulator tile (M-tile rows starting at `base`) into the
 // state of its N-tile. `lbits` bit r = lane row r (+4h) valid. `save` is the
-// lane's LDS slot (4 chunks of 16 bytes, 64 lanes apart).
+// lane's LDS slot (kSaveChunks chunks of 16 bytes, 64 lanes apart). On a
+// raise the lane keeps only the group of values that holds the first
+// occurrence of the new max, and folds the group's row offset into tbase.
 template <typename V, bool ARGMAX, bool MASKED, typename Acc>
 __device__ __forceinline__ void fold_one(const Acc& acc, RowState<V, ARGMAX>& st, int base,
                                          uint32_t lbits, u32x4* save)
 {
     V v[16];
     masked_values<V, Acc, MASKED>(acc, lbits, v);
-    const V tm = max16(v);
     if constexpr (ARGMAX) {
+        constexpr int SV = 4 * kSaveChunks;  // values per group
+        constexpr int NG = 16 / SV;          // groups
+        V g[NG];
+        static_for<0, NG>([&](auto k) { g[k] = max_run<decltype(k)::value * SV, SV>(v); });
+        V tm = g[0];
+#pragma unroll
+        for (int k = 1; k < NG; ++k) tm = vmax(tm, g[k]);
         const bool upd = tm > st.m;
         st.m = upd ? tm : st.m;
-        st.tbase = upd ? base : st.tbase;
         if (upd) {
+            // first group whose max is the tile max; its first chunk is
+            // chunk k * kSaveChunks, i.e. rows 8 * k * kSaveChunks (+4h) on
+            int sel = NG - 1;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                save[64 * c] = u32x4{__builtin_bit_cast(uint32_t, v[4 * c]), __builtin_bit_cast(uint32_t, v[4 * c + 1]),
-                                     __builtin_bit_cast(uint32_t, v[4 * c + 2]),
-                                     __builtin_bit_cast(uint32_t, v[4 * c + 3])};
+            for (int k = NG - 2; k >= 0; --k) sel = g[k] == tm ? k : sel;
+            st.tbase = base + 8 * kSaveChunks * sel;
+#pragma unroll
+            for (int c = 0; c < kSaveChunks; ++c) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    V x = v[(NG - 1) * SV + 4 * c + e];
+#pragma unroll
+                    for (int k = NG - 2; k >= 0; --k) x = g[k] == tm ? v[k * SV + 4 * c + e] : x;
+                    w[e] = __builtin_bit_cast(uint32_t, x);
+                }
+                save[64 * c] = u32x4{w[0], w[1], w[2], w[3]};
+            }
         }
     } else {
         (void)save;
-        st.m = vmax(st.m, tm);
+        st.m = vmax(st.m, max16(v));
     }
 }
 
-// Lane-local argmax of the doc: lowest row of the saved M-tile equal to the
+// Lane-local argmax of the doc: lowest row of the saved group equal to the
 // max (row offset without the 4h term); only meaningful when the max is
 // finite, i.e. when the slot was written for this doc.
 template <typename V>
@@ -216,9 +254,9 @@ __device__ __forceinline__ int saved_argmax(const RowState<V, true>& st, const u
     // the chunk is copied to a plain array before the compares: indexing the
     // vector value directly inside the unrolled loop was compiled (ROCm 7.2)
     // into a compare of element 0 only
-    int qs = 15;
+    int qs = 4 * kSaveChunks - 1;
 #pragma unroll
-    for (int c = 3; c >= 0; --c) {
+    for (int c = kSaveChunks - 1; c >= 0; --c) {
         const u32x4 w = save[64 * c];
         const uint32_t wv[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
@@ -266,8 +304,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ uint16_t doc_tiles[kMaskWords / 2];
     // doc-token scales of each stage's tile (TOK)
     __shared__ __attribute__((aligned(16))) float sc_buf[TOK ? STAGES * TR : 4];
-    // argmax: each lane's saved M-tile values, per (wave, N-tile): 4 chunks x 64 lanes
-    __shared__ __attribute__((aligned(16))) u32x4 save_buf[ARGMAX ? W * NTW * 256 : 1];
+    // argmax: each lane's saved values, per (wave, N-tile): kSaveChunks chunks x 64 lanes
+    __shared__ __attribute__((aligned(16))) u32x4 save_buf[ARGMAX ? W * NTW * 64 * kSaveChunks : 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -311,14 +349,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int64_t F = (d1 - d0) * ntd;                                     // tiles of the range
     const uint32_t part_base = lds_addr(&part[0][0]);
 
-    // per-lane byte offsets: LDS slot p = (row p / NCH, chunk p % NCH) of a
-    // stage holds logical chunk swz(row, p % NCH) of that row
-    int dma_off[LPS];
-#pragma unroll
-    for (int u = 0; u < LPS; ++u) {
-        const int p = (wave * LPS + u) * 64 + lane;
-        dma_off[u] = (p / NCH) * RB + swz_chunk<RB>(p / NCH, p % NCH) * 16;
-    }
     // A-fragment offsets of M-tile 0 (row = lane % 32, logical chunk 2s + h);
     // M-tile mt adds mt * 32 rows (the swizzle only depends on row % 16)
     uint32_t frag_off[KS];
@@ -328,6 +358,19 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint32_t sc_base = lds_addr(sc_buf);
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
+    // per-lane byte offset of direct-to-LDS load u: LDS slot p = (row p / NCH,
+    // chunk p % NCH) of a stage holds logical chunk swz(row, p % NCH) of that
+    // row. Load u covers rows 64 u / NCH further on, and with the lane's row
+    // bits below those (row % 16 < 4 for 256-byte rows, and row % 8 for
+    // 128-byte rows, whose swizzle also takes bit 3 of the row) the swizzle
+    // of load u is that of load 0 with fixed chunk bits flipped: offset u =
+    // (offset 0 ^ dma_flip(u)) + 1024 u.
+    static_assert(64 * LPS * W == CHUNKS && (RB == 256 || (RB == 128 && LPS % 2 == 0)), "load layout");
+    auto dma_flip = [](int u) -> uint32_t { return RB == 256 ? 64u * (uint32_t)(u & 3) : 16u * (uint32_t)(u & 1); };
+    const uint32_t dma_off0 = [&] {
+        const uint32_t p = (uint32_t)(wave * LPS) * 64 + (uint32_t)lane;
+        return (p / NCH) * RB + (uint32_t)swz_chunk<RB>((int)(p / NCH), (int)(p % NCH)) * 16;
+    }();
 
     // stage tile tt of doc `doc` into `stage`: uniform base pointer + 32-bit
     // per-lane offsets (scalar-base addressing), no 64-bit per-lane math
@@ -339,9 +382,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         // rows past the doc end read its last row's final chunk instead; they
         // are never folded (their validity bits are 0)
         const uint32_t lim = (uint32_t)(rows * RB - 16);
+        // offsets 1 .. LPS - 1 are derived at each issue from a copy of
+        // offset 0 that the compiler cannot hoist (it depends on the stage),
+        // so that they do not hold LPS registers across the tile loop
+        uint32_t o0 = dma_off0;
+        asm("" : "+v"(o0) : "s"(stage));
 #pragma unroll
         for (int u = 0; u < LPS; ++u) {
-            const uint32_t o = (uint32_t)dma_off[u];
+            const uint32_t o = (o0 ^ dma_flip(u)) + 1024u * (uint32_t)u;
             dma_lds16(Dt, o < lim ? o : lim, lds0 + u * 1024);
         }
         if constexpr (TOK) {  // rows RPW w .. RPW w + RPW - 1 of the tile's doc scales
@@ -449,7 +497,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 
         RowState<V, ARGMAX> st[NTW];
         // this lane's LDS slot for the saved values of N-tile n
-        auto save_slot = [&](int n) -> u32x4* { return &save_buf[ARGMAX ? (wave * NTW + n) * 256 + lane : 0]; };
+        auto save_slot = [&](int n) -> u32x4* { return &save_buf[ARGMAX ? (wave * NTW + n) * 64 * kSaveChunks + lane : 0]; };
 
         // finish doc `doc` (ordinal `k` in the range): merge the lane halves,
         // apply q_mask, write argmax, put per-N-tile sums into part[k & 1]
