@@ -28,9 +28,9 @@
 // timing.
 //
 // Argmax: a lane keeps its running max and the base row of the values it
-// last saved; when an M-tile raises the max, the half of the lane's 16 values
-// of that M-tile that holds the first occurrence of the new max is stored to
-// a per-lane LDS slot (an exec-masked store, so lanes whose max did not
+// last saved; when an M-tile raises the max, the quarter of the lane's 16
+// values of that M-tile (4 rows) that holds the first occurrence of the new
+// max is stored to a per-lane LDS slot (an exec-masked store, so lanes whose max did not
 // change issue nothing). At the end of the doc the lowest saved row holding
 // the max is the argmax. Keeping the saved values in LDS rather than
 // selecting them into registers takes the 16 selects per value tile off the
@@ -139,6 +139,19 @@ __device__ __forceinline__ void static_for(F&& f)
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Scheduling groups for the region that holds the MFMA chain of one unit and
+// the max fold of the previous one: one MFMA, then up to two VALU
+// instructions of the fold, then one LDS read (the next M-tile's fragment),
+// repeated, so that the fold issues in the shadow of the chain instead of
+// after it.
+__device__ __forceinline__ void interleave_fold_with_chain()
+{
+    static_for<0, 8>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    });
+}
 
 // Running state of one N-tile for the lane's 16 rows of each M-tile: the
 // running max and, with argmax, the base row of the values saved when an
@@ -181,12 +194,13 @@ __device__ __forceinline__ V max16(const V (&v)[16])
     return vmax(vmax3(a, b, c), vmax3(d, e, v[15]));
 }
 
-// 16-byte chunks of a raised M-tile that a lane saves: the half of its 16
-// values (in the lane's row order) that holds the first occurrence of the
-// tile max. Against saving all 16 values this costs a compare and 8 selects
-// per raise and halves the LDS stores and the slot memory, which ran the
-// 128 x 128 bf16 ColPali pairs 2 % faster.
-constexpr int kSaveChunks = 2;
+// 16-byte chunks of a raised M-tile that a lane saves: the quarter of its
+// 16 values (in the lane's row order) that holds the first occurrence of the
+// tile max. Against saving all 16 values this costs three compares and 12
+// selects per raise and cuts the LDS stores and the slot memory to a quarter,
+// which ran the 128 x 128 bf16 ColPali pairs about 4 % faster (half the values:
+// about 2 %).
+constexpr int kSaveChunks = 1;
 static_assert(kSaveChunks == 1 || kSaveChunks == 2 || kSaveChunks == 4, "saved chunks per raise");
 
 // max of v[B .. B+N-1], N in {4, 8, 16}
@@ -203,7 +217,10 @@ __device__ __forceinline__ V max_run(const V (&v)[16])
 // lane's LDS slot (kSaveChunks chunks of 16 bytes, 64 lanes apart). On a
 // raise the lane keeps only the group of values that holds the first
 // occurrence of the new max, and folds the group's row offset into tbase.
-template <typename V, bool ARGMAX, bool MASKED, typename Acc>
+// CHAINED: the fold follows an MFMA chain issued at raised priority in the
+// same region; its max and compare are interleaved with that chain, and the
+// priority drops once they are issued.
+template <typename V, bool ARGMAX, bool MASKED, typename Acc, bool CHAINED = false>
 __device__ __forceinline__ void fold_one(const Acc& acc, RowState<V, ARGMAX>& st, int base,
                                          uint32_t lbits, u32x4* save)
 {
@@ -219,6 +236,10 @@ __device__ __forceinline__ void fold_one(const Acc& acc, RowState<V, ARGMAX>& st
         for (int k = 1; k < NG; ++k) tm = vmax(tm, g[k]);
         const bool upd = tm > st.m;
         st.m = upd ? tm : st.m;
+        if constexpr (CHAINED) {
+            interleave_fold_with_chain();
+            __builtin_amdgcn_s_setprio(0);
+        }
         if (upd) {
             // first group whose max is the tile max; its first chunk is
             // chunk k * kSaveChunks, i.e. rows 8 * k * kSaveChunks (+4h) on
@@ -242,6 +263,10 @@ __device__ __forceinline__ void fold_one(const Acc& acc, RowState<V, ARGMAX>& st
     } else {
         (void)save;
         st.m = vmax(st.m, max16(v));
+        if constexpr (CHAINED) {
+            interleave_fold_with_chain();
+            __builtin_amdgcn_s_setprio(0);
+        }
     }
 }
 
@@ -682,8 +707,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 // The wave issues its MFMA chain at raised priority, so that
                 // the SIMD's other wave (folding or reading LDS) yields the
                 // issue slots while the chain is being fed (2 % on the 128 x 128 bf16
-                // ColPali pairs, 3 % on the 1024-token int8 query). Not
-                // with per-token scales, whose VALU-heavy fold it slows down.
+                // ColPali pairs, 3 % on the 1024-token int8 query). The fold
+                // that follows in program order (of the previous unit) is
+                // interleaved with the chain and drops the priority when its
+                // max is issued (fold_one, CHAINED). Not with per-token
+                // scales, whose VALU-heavy fold it slows down.
                 auto mma = [&](i32x4 (&af)[KS], int n, int next, const Acc& init) {
                     Acc acc = init;
                     if constexpr (!TOK) __builtin_amdgcn_s_setprio(1);
@@ -692,7 +720,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                         acc = mfma32<E>(af[s], qf[n][s], acc);
                         if (next >= 0) af[s] = *(const i32x4*)(sb + frag_off[s] + next * 32 * RB);
                     }
-                    if constexpr (!TOK) __builtin_amdgcn_s_setprio(0);
                     return acc;
                 };
                 // doc-token scales of the lane's 16 rows of M-tile mt (TOK)
@@ -720,7 +747,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                         for (int q = 0; q < 16; ++q) sv[q] = (float)acc[q] * sc[q];
                         fold_one<V, ARGMAX, MASKED>(sv, st[n], base, lbits, save_slot(n));
                     } else {
-                        fold_one<V, ARGMAX, MASKED>(acc, st[n], base, lbits, save_slot(n));
+                        fold_one<V, ARGMAX, MASKED, Acc, true>(acc, st[n], base, lbits, save_slot(n));
                     }
                 };
                 // validity bits of the 32 rows of M-tile mt
@@ -782,6 +809,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 };
                 if (vall == ~0ull) run_tile(std::true_type{});
                 else run_tile(std::false_type{});
+                // a chain whose fold was skipped (no valid row) left it raised
+                if constexpr (!TOK) __builtin_amdgcn_s_setprio(0);
             }
             if (tt == k_tiles - 1) finish_doc(doc, k);
             stage = stage == STAGES - 1 ? 0 : stage + 1;
