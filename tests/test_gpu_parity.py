@@ -90,16 +90,28 @@ def test_dense_small(ms, case, oracle_mod):
     _assert_close("scores (no argmax)", s2.numpy(), rs)
 
 
-def test_dense_exact_ties(ms, oracle_mod):
+EXACT_TIE_CASES = [
+    # (Nq, Nd, Lq, Ld, dtype, largest |k|, seed)
+    (3, 4, 40, 150, torch.float16, 2, 3),
+    (3, 4, 40, 150, torch.bfloat16, 2, 3),
+    (2, 3, 64, 300, torch.bfloat16, 1, 5),    # ternary: the max recurs in many rows
+    (4, 2, 100, 520, torch.float16, 1, 6),    # several 128-token tiles per doc
+]
+
+
+@pytest.mark.parametrize("case", EXACT_TIE_CASES, ids=lambda c: f"{c[0]}x{c[1]}_lq{c[2]}_ld{c[3]}_{str(c[4])[6:]}_k{c[5]}")
+def test_dense_exact_ties(ms, oracle_mod, case):
     """Values k/8: every dot product is exact in fp32 too, so argmax must match
-    the oracle exactly, including lowest-index tie-breaking."""
-    _say("dense exact ties")
-    rng = np.random.default_rng(3)
-    Nq, Nd, Lq, Ld = 3, 4, 40, 150
-    Q = torch.from_numpy(rng.integers(-2, 3, size=(Nq, Lq, 128)) / 8.0).to(torch.float16)
-    D = torch.from_numpy(rng.integers(-2, 3, size=(Nd, Ld, 128)) / 8.0).to(torch.float16)
+    the oracle exactly, including lowest-index tie-breaking: within a lane's
+    rows of one 32-row block, across blocks and tiles, and across the two
+    lane halves."""
+    Nq, Nd, Lq, Ld, dt, kmax, seed = case
+    _say(f"dense exact ties {case}")
+    rng = np.random.default_rng(seed)
+    Q = torch.from_numpy(rng.integers(-kmax, kmax + 1, size=(Nq, Lq, 128)) / 8.0).to(dt)
+    D = torch.from_numpy(rng.integers(-kmax, kmax + 1, size=(Nd, Ld, 128)) / 8.0).to(dt)
     D[:, 100:140] = D[:, 10:50]
-    D[2] = D[2, 0]
+    D[Nd - 2] = D[Nd - 2, 0]
     dm = torch.from_numpy((rng.random((Nd, Ld)) > 0.1).astype(np.uint8))
     w = synth.Dense("ties", Q, D, None, dm)
     s, a = _run_dense(ms, w)
@@ -249,6 +261,7 @@ INT8_CASES = [
     (1, 2, 1040, 40, "quantised", 0.0, 0.0),     # past one workgroup: two passes
     (2, 3, 128, 64, "extreme", 0.0, 0.0),        # largest sums
     (4, 3, 32, 200, "ternary", 0.0, 0.0),
+    (2, 3, 64, 600, "ternary", 0.0, 0.1),        # argmax ties across 256-token tiles
 ]
 
 
