@@ -602,6 +602,8 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15, wave = tid >> 6;
     const int64_t s = s0 + grp;
     const bool row_ok = s < Lq;
+    // a masked row's gradient is 0 (written below); its gathers are skipped
+    const bool row_live = row_ok && !(a.q_mask && a.q_mask[i * Lq + s] == 0);
 
     for (int c = 0; c < nchunk; ++c) {
         const LaneSpan ls(c, l16, DW, GEN);
@@ -653,7 +655,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
                 }
             }
             barrier_lds();
-            if (!row_ok || ls.n == 0) continue;
+            if (!row_live || ls.n == 0) continue;
             const int64_t dbase = (j0 * Ld) * DW + ls.e0;
             int jj = 0;
             for (; jj + 8 <= nj; jj += 8) {
@@ -676,14 +678,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
                 for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);
             }
         }
-        if (row_ok && ls.n > 0) {
-            const int64_t r = i * Lq + s;
-            if (a.q_mask && a.q_mask[r] == 0) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-            }
-            storen(a.dQ + r * DW + ls.e0, ls.n, ls.vec, acc);
-        }
+        if (row_ok && ls.n > 0) storen(a.dQ + (i * Lq + s) * DW + ls.e0, ls.n, ls.vec, acc);
     }
 }
 
@@ -797,14 +792,22 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                         if (a.q_mask && a.q_mask[qrow] == 0) w = 0.f;
                     }
                 }
+                // only the sources with a nonzero weight are gathered, in
+                // CSR order (a zero-weight term adds an exact zero, the
+                // inputs being finite): gm lists the group's lanes that hold
+                // one
+                uint32_t gm = (uint32_t)(__ballot(l16 < cnt && w != 0.f) >> gbase) & 0xffffu;
+                const int nz = __builtin_popcount(gm);
                 int k = 0;
-                for (; k + kDdUnroll <= cnt; k += kDdUnroll) {
+                for (; k + kDdUnroll <= nz; k += kDdUnroll) {
                     float xv[kDdUnroll][8];
                     float ww[kDdUnroll];
 #pragma unroll
                     for (int u = 0; u < kDdUnroll; ++u) {
-                        const int qr = __shfl(qrow, gbase + k + u, 64);
-                        ww[u] = __shfl(w, gbase + k + u, 64);
+                        const int src = gbase + __builtin_ctz(gm);
+                        gm &= gm - 1;
+                        const int qr = __shfl(qrow, src, 64);
+                        ww[u] = __shfl(w, src, 64);
                         loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv[u]);
                     }
 #pragma unroll
@@ -812,9 +815,11 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
 #pragma unroll
                         for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(ww[u], xv[u][q], acc[q]);
                 }
-                for (; k < cnt; ++k) {
-                    const int qr = __shfl(qrow, gbase + k, 64);
-                    const float wk = __shfl(w, gbase + k, 64);
+                for (; k < nz; ++k) {
+                    const int src = gbase + __builtin_ctz(gm);
+                    gm &= gm - 1;
+                    const int qr = __shfl(qrow, src, 64);
+                    const float wk = __shfl(w, src, 64);
                     float xv[8];
                     loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv);
 #pragma unroll
