@@ -718,11 +718,15 @@ __global__ __launch_bounds__(kCsrThreads) void csr_dq_kernel(BwdArgs a, int64_t 
 // a block of its rows; group g owns rows t_begin + g + 64*k, lane l16 owns
 // dims 8*l16 .. 8*l16+7. TAB: the doc's weights w for every (i,s) are staged
 // in LDS first (Nq*Lq <= kWTab), so a source costs one CSR read and one
-// gather; otherwise w is read from g and q_mask per source.
-template <int E, bool TAB, bool GEN>
+// gather; otherwise w is read from g and q_mask per source. O32 (d = 128 and
+// Q under 4 GiB): a source is handed from its decoding lane to its group as
+// the 32-bit byte offset of its Q row, and each lane adds its own 16 bytes,
+// so a gather needs no 64-bit address arithmetic.
+template <int E, bool TAB, bool GEN, bool O32>
 __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXSIM_DD_WAVES))) void dd_kernel(
     BwdArgs a, int rows_per_block)
 {
+    static_assert(!(O32 && GEN), "32-bit offsets only for 128-wide rows");
     __shared__ float wtab[TAB ? kWTab : 1];
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
     const int64_t DW = GEN ? (int64_t)a.d : kD;
@@ -770,7 +774,13 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
     for (int c = 0; c < nchunk; ++c) {
         const LaneSpan ls(c, l16, DW, GEN);
         const int64_t row = j * Ld + t;
+        const uint32_t e0b = (uint32_t)ls.e0 * (uint32_t)sizeof(uint16_t);  // this lane's bytes of a row (O32)
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // the source handed to the group: Q row index, or its byte offset (O32)
+        auto gather = [&](int qr, float (&xv)[8]) {
+            if constexpr (O32) load8<E>((const unsigned char*)a.Q + ((uint32_t)qr + e0b), 0, xv);
+            else loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv);
+        };
         if (live) {
             const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
             for (int e = e0; e < e1; e += 16) {
@@ -796,6 +806,7 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                 // CSR order (a zero-weight term adds an exact zero, the
                 // inputs being finite): gm lists the group's lanes that hold
                 // one
+                if constexpr (O32) qrow = (int)((uint32_t)qrow * (uint32_t)(kD * sizeof(uint16_t)));
                 uint32_t gm = (uint32_t)(__ballot(l16 < cnt && w != 0.f) >> gbase) & 0xffffu;
                 const int nz = __builtin_popcount(gm);
                 int k = 0;
@@ -808,7 +819,7 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                         gm &= gm - 1;
                         const int qr = __shfl(qrow, src, 64);
                         ww[u] = __shfl(w, src, 64);
-                        loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv[u]);
+                        gather(qr, xv[u]);
                     }
 #pragma unroll
                     for (int u = 0; u < kDdUnroll; ++u)
@@ -821,7 +832,7 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                     const int qr = __shfl(qrow, src, 64);
                     const float wk = __shfl(w, src, 64);
                     float xv[8];
-                    loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv);
+                    gather(qr, xv);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wk, xv[q], acc[q]);
                 }
@@ -852,12 +863,17 @@ static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream)
         if (rpb > a.Ld) rpb = (a.Ld + 63) / 64 * 64;
         if (rpb > 4096) rpb = 4096;
         const int64_t blocks = a.Nd * ((a.Ld + rpb - 1) / rpb);
-        if (a.Nq * a.Lq <= kWTab)
-            hipLaunchKernelGGL((dd_kernel<E, true, GEN>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
-                               (int)rpb);
-        else
-            hipLaunchKernelGGL((dd_kernel<E, false, GEN>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
-                               (int)rpb);
+        // Q rows addressed by 32-bit byte offsets when Q is under 4 GiB
+        constexpr bool kO32 = !GEN;
+        const bool o32 = kO32 && a.Nq * a.Lq <= (int64_t)(0xFFFFFFFFu / (kD * sizeof(uint16_t)));
+        const dim3 grid((unsigned)blocks), block(kDdThreads);
+        if (a.Nq * a.Lq <= kWTab) {
+            if (o32) hipLaunchKernelGGL((dd_kernel<E, true, GEN, kO32>), grid, block, 0, stream, a, (int)rpb);
+            else hipLaunchKernelGGL((dd_kernel<E, true, GEN, false>), grid, block, 0, stream, a, (int)rpb);
+        } else {
+            if (o32) hipLaunchKernelGGL((dd_kernel<E, false, GEN, kO32>), grid, block, 0, stream, a, (int)rpb);
+            else hipLaunchKernelGGL((dd_kernel<E, false, GEN, false>), grid, block, 0, stream, a, (int)rpb);
+        }
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
