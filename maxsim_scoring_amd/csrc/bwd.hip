@@ -596,9 +596,11 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
     const int64_t DW = GEN ? (int64_t)a.d : kD;
     const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
-    const int64_t sblocks = (Lq + G - 1) / G;
-    const int64_t i = blk / sblocks;
-    const int64_t s0 = (blk % sblocks) * G;
+    // blocks go query-minor: the first G rows of every query come first, so
+    // that the row blocks most likely to be unmasked (masks usually cut a
+    // query's tail) start before the lighter ones
+    const int64_t i = blk % a.Nq;
+    const int64_t s0 = (blk / a.Nq) * G;
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15, wave = tid >> 6;
     const int64_t s = s0 + grp;
     const bool row_ok = s < Lq;
