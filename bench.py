@@ -350,9 +350,11 @@ def bench_backward(torch, ms, synth, wl, steps, warmup):
     t = statistics.median(times)
     nbytes = wl.bwd_compulsory_bytes(128, 128, 128, 1024, 128, 2, True, True)
     # the row gathers the two passes make beyond the compulsory bytes (served
-    # from L2 and the last-level cache): one 256-byte D row per (i, j, s) for
-    # dQ and one Q row per CSR entry for dD
-    gathered = 2 * 128 * 128 * 128 * 128 * 2
+    # from L2 and the last-level cache): one 256-byte D row per doc and
+    # unmasked query row for dQ, and one Q row per CSR entry of nonzero weight
+    # g[i,j] q_mask[i,s] live(j) for dD (every g here is nonzero and every doc
+    # live, so both count the unmasked query rows times the docs)
+    gathered = 2 * int(fw.q_mask.sum()) * 128 * 128 * 2
     return {"workload": "backward_colpali_bf16_128x128_lq128_ld1024", "ms": t, **spread(times),
             "pairs_per_s": 128 * 128 / (t * 1e-3), "compulsory_bytes": nbytes,
             "gathered_bytes": gathered,
