@@ -606,6 +606,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
     const bool row_ok = s < Lq;
     // a masked row's gradient is 0 (written below); its gathers are skipped
     const bool row_live = row_ok && !(a.q_mask && a.q_mask[i * Lq + s] == 0);
+    const bool o32 = !GEN && (uint64_t)kDqDocs * (uint64_t)Ld * (kD * sizeof(uint16_t)) <= 0xFFFFFFFFull;
 
     for (int c = 0; c < nchunk; ++c) {
         const LaneSpan ls(c, l16, DW, GEN);
@@ -659,12 +660,21 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
             barrier_lds();
             if (!row_live || ls.n == 0) continue;
             const int64_t dbase = (j0 * Ld) * DW + ls.e0;
+            // d = 128 and a batch's docs under 4 GiB: a gather is the batch's
+            // uniform base plus a 32-bit byte offset
+            const unsigned char* batch = (const unsigned char*)a.D + (size_t)(j0 * Ld) * (kD * sizeof(uint16_t));
+            const uint32_t lane_b = (uint32_t)ls.e0 * (uint32_t)sizeof(uint16_t);
+            auto gather = [&](int jr, int t, float (&x)[8]) {
+                if (!GEN && o32)
+                    load8<E>(batch + (((uint32_t)jr * (uint32_t)Ld + (uint32_t)t) * (uint32_t)(kD * sizeof(uint16_t)) + lane_b), 0, x);
+                else
+                    loadn<E>(a.D, dbase + ((int64_t)jr * Ld + t) * DW, ls.n, ls.vec, x);
+            };
             int jj = 0;
             for (; jj + 8 <= nj; jj += 8) {
                 float x[8][8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    loadn<E>(a.D, dbase + ((int64_t)(jj + u) * Ld + sm.am[jj + u][grp]) * DW, ls.n, ls.vec, x[u]);
+                for (int u = 0; u < 8; ++u) gather(jj + u, sm.am[jj + u][grp], x[u]);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const float w = sm.wj[jj + u];
@@ -674,7 +684,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
             }
             for (; jj < nj; ++jj) {
                 float x[8];
-                loadn<E>(a.D, dbase + ((int64_t)jj * Ld + sm.am[jj][grp]) * DW, ls.n, ls.vec, x);
+                gather(jj, sm.am[jj][grp], x);
                 const float w = sm.wj[jj];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, x[k], acc[k]);

@@ -352,6 +352,9 @@ BWD_CASES = [
     (64, 3, 256, 96, torch.bfloat16, 0.1, 0.1, 1, 0.0),  # exactly 16384 sources per doc
     (8, 3, 100, 300, torch.float16, 0.0, 0.0, 0, 1.0),   # every source of a doc in one row:
                                                          # groups of 64 equal keys per step
+    (4, 130, 40, 60, torch.bfloat16, 0.3, 0.2, 2, 0.0),  # dQ over three rounds of staged docs
+    (3, 200, 64, 33, torch.float16, 0.0, 0.3, 1, 0.0),   # rounds of 64 + 64 + 64 + 8 docs
+    (40, 128, 80, 20, torch.float16, 0.2, 0.0, 0, 0.0),  # more query rows than doc rows
 ]
 
 
