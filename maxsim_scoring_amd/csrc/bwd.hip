@@ -24,12 +24,13 @@
 //           weights g[i,j] live(j) of 64 docs at a time are staged in LDS
 //           (live(j) = any(d_mask[j,:]) found by the workgroup itself), then
 //           each group gathers D[j, argmax[i,j,s]] for j ascending (16 bytes
-//           per lane, 8 loads in flight) and accumulates in fp32. All
-//           workgroups sweep j in the same order, so the D rows they gather
-//           are shared in L2;
+//           per lane, 8 loads in flight) and accumulates in fp32; a row with
+//           q_mask 0 gathers nothing. All workgroups sweep j in the same
+//           order, so the D rows they gather are shared in L2;
 //   dd      one 16-lane group per destination row (j,t): the group walks the
-//           row's sources in CSR order, gathers Q rows (16 bytes per lane)
-//           and accumulates in fp32; every row is written once.
+//           row's sources in CSR order, gathers the Q rows (16 bytes per
+//           lane) of those with a nonzero weight and accumulates in fp32;
+//           every row is written once.
 // The padding-free backward (vbwd_*) and the Chamfer backward (cham_*) below
 // follow the same pattern.
 #include "common.hpp"
