@@ -1147,11 +1147,13 @@ __global__ __launch_bounds__(kCsrThreads) void vbwd_csr_dq_kernel(VarBwdArgs a, 
 
 // Eq. (3) per packed doc row r: the sources of CSR row r, in order, each
 // g[i,j] Q[cu_q[i] + s]. Workgroup = a block of rows; group g owns rows
-// r_begin + g + 64 k.
-template <int E, bool GEN>
+// r_begin + g + 64 k. O32 (d = 128, packed Q under 4 GiB): a source is
+// handed to its group as the 32-bit byte offset of its Q row.
+template <int E, bool GEN, bool O32>
 __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXSIM_DD_WAVES))) void vbwd_dd_kernel(
     VarBwdArgs a, int rows_per_block)
 {
+    static_assert(!(O32 && GEN), "32-bit offsets only for 128-wide rows");
     constexpr int kDdGroups = kDdThreads / 16;
     const int64_t DW = GEN ? (int64_t)a.d : kD;
     const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
@@ -1164,6 +1166,7 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
     for (int64_t r = r_begin + grp; r < r_end; r += kDdGroups)
     for (int c = 0; c < nchunk; ++c) {
         const LaneSpan ls(c, l16, DW, GEN);
+        const uint32_t e0b = (uint32_t)ls.e0 * (uint32_t)sizeof(uint16_t);  // this lane's bytes of a row (O32)
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         // a valid row lists at most Tq sources inside col_idx; the bounds
         // also hold for any row_ptr content
@@ -1188,15 +1191,23 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                 qrow = qrow < 0 ? 0 : (qrow < Tq ? qrow : Tq - 1);
                 w = a.g[(int64_t)i * Nd + jd];
             }
+            // what the group broadcasts per source: the Q row, or (O32) its
+            // 32-bit byte offset
+            using Src = typename std::conditional<O32, uint32_t, int64_t>::type;
+            const Src hand = O32 ? (Src)((uint64_t)qrow * (kD * sizeof(uint16_t))) : (Src)qrow;
+            auto gather = [&](Src qr, float (&xv)[8]) {
+                if constexpr (O32) load8<E>((const unsigned char*)a.Q + ((uint32_t)qr + e0b), 0, xv);
+                else loadn<E>(a.Q, (int64_t)qr * DW + ls.e0, ls.n, ls.vec, xv);
+            };
             int k = 0;
             for (; k + kDdUnroll <= cnt; k += kDdUnroll) {
                 float xv[kDdUnroll][8];
                 float ww[kDdUnroll];
 #pragma unroll
                 for (int u = 0; u < kDdUnroll; ++u) {
-                    const int64_t qr = __shfl(qrow, gbase + k + u, 64);
+                    const Src qr = __shfl(hand, gbase + k + u, 64);
                     ww[u] = __shfl(w, gbase + k + u, 64);
-                    loadn<E>(a.Q, qr * DW + ls.e0, ls.n, ls.vec, xv[u]);
+                    gather(qr, xv[u]);
                 }
 #pragma unroll
                 for (int u = 0; u < kDdUnroll; ++u)
@@ -1204,10 +1215,10 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                     for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(ww[u], xv[u][q], acc[q]);
             }
             for (; k < cnt; ++k) {
-                const int64_t qr = __shfl(qrow, gbase + k, 64);
+                const Src qr = __shfl(hand, gbase + k, 64);
                 const float wk = __shfl(w, gbase + k, 64);
                 float xv[8];
-                loadn<E>(a.Q, qr * DW + ls.e0, ls.n, ls.vec, xv);
+                gather(qr, xv);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wk, xv[q], acc[q]);
             }
@@ -1240,7 +1251,14 @@ static hipError_t launch_bwd_varlen_t(VarBwdArgs a, hipStream_t stream)
         rpb = (rpb + 63) / 64 * 64;
         if (rpb > 4096) rpb = 4096;
         const int64_t blocks = (a.Td + rpb - 1) / rpb;
-        hipLaunchKernelGGL((vbwd_dd_kernel<E, GEN>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a, (int)rpb);
+        // Q rows addressed by 32-bit byte offsets when packed Q is under 4 GiB
+        const bool o32 = !GEN && a.Tq <= (int64_t)(0xFFFFFFFFu / (kD * sizeof(uint16_t)));
+        if (o32)
+            hipLaunchKernelGGL((vbwd_dd_kernel<E, GEN, !GEN>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
+                               (int)rpb);
+        else
+            hipLaunchKernelGGL((vbwd_dd_kernel<E, GEN, false>), dim3((unsigned)blocks), dim3(kDdThreads), 0, stream, a,
+                               (int)rpb);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
