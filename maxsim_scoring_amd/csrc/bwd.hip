@@ -741,6 +741,12 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
 {
     static_assert(!(O32 && GEN), "32-bit offsets only for 128-wide rows");
     __shared__ float wtab[TAB ? kWTab : 1];
+    // per 16-lane group: the current batch's sources of nonzero weight, in order
+    struct SrcEntry {
+        int q;    // Q row, or (O32) its byte offset
+        float w;
+    };
+    __shared__ SrcEntry srcq[kDdThreads / 16][16];
     const int64_t Nd = a.Nd, Lq = a.Lq, Ld = a.Ld;
     const int64_t DW = GEN ? (int64_t)a.d : kD;
     const int nchunk = GEN ? (int)((DW + 127) / 128) : 1;
@@ -817,22 +823,24 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                 }
                 // only the sources with a nonzero weight are gathered, in
                 // CSR order (a zero-weight term adds an exact zero, the
-                // inputs being finite): gm lists the group's lanes that hold
-                // one
+                // inputs being finite): each such lane puts its source at its
+                // rank among them into the group's LDS list, which the group
+                // then reads in order (a lane's own slot is the only one it
+                // writes; LDS operations of a wave are in order)
                 if constexpr (O32) qrow = (int)((uint32_t)qrow * (uint32_t)(kD * sizeof(uint16_t)));
-                uint32_t gm = (uint32_t)(__ballot(l16 < cnt && w != 0.f) >> gbase) & 0xffffu;
+                const bool keep = l16 < cnt && w != 0.f;
+                const uint32_t gm = (uint32_t)(__ballot(keep) >> gbase) & 0xffffu;
                 const int nz = __builtin_popcount(gm);
+                if (keep) srcq[grp][__builtin_popcount(gm & ((1u << l16) - 1u))] = SrcEntry{qrow, w};
                 int k = 0;
                 for (; k + kDdUnroll <= nz; k += kDdUnroll) {
                     float xv[kDdUnroll][8];
                     float ww[kDdUnroll];
 #pragma unroll
                     for (int u = 0; u < kDdUnroll; ++u) {
-                        const int src = gbase + __builtin_ctz(gm);
-                        gm &= gm - 1;
-                        const int qr = __shfl(qrow, src, 64);
-                        ww[u] = __shfl(w, src, 64);
-                        gather(qr, xv[u]);
+                        const SrcEntry se = srcq[grp][k + u];
+                        ww[u] = se.w;
+                        gather(se.q, xv[u]);
                     }
 #pragma unroll
                     for (int u = 0; u < kDdUnroll; ++u)
@@ -840,14 +848,11 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                         for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(ww[u], xv[u][q], acc[q]);
                 }
                 for (; k < nz; ++k) {
-                    const int src = gbase + __builtin_ctz(gm);
-                    gm &= gm - 1;
-                    const int qr = __shfl(qrow, src, 64);
-                    const float wk = __shfl(w, src, 64);
+                    const SrcEntry se = srcq[grp][k];
                     float xv[8];
-                    gather(qr, xv);
+                    gather(se.q, xv);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wk, xv[q], acc[q]);
+                    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(se.w, xv[q], acc[q]);
                 }
             }
         }
