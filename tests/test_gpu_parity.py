@@ -373,6 +373,28 @@ def test_bwd_small(ms, oracle_mod, case):
     _check_bwd(ms, oracle_mod, w, argmax, g)
 
 
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+def test_bwd_zero_weights(ms, oracle_mod, dt):
+    """Upstream gradients that are zero for most (query, doc) pairs, with
+    masked query tokens and a dead doc: every term of zero weight is skipped
+    by the gathers, which must leave dQ and dD as the oracle's (rows whose
+    terms are all zero come out exactly 0)."""
+    _say(f"bwd zero weights {dt}")
+    Nq, Nd, Lq, Ld = 6, 5, 48, 90
+    w = synth.random_dense(470, Nq, Nd, Lq, Ld, dtype=dt, q_mask_p=0.4, d_mask_p=0.2, dead_docs=1)
+    _, ra = oracle_mod.fwd(w.Q, w.D, w.q_mask, w.d_mask)
+    g = synth.upstream_grad(470, Nq, Nd)
+    keep = torch.from_numpy(np.random.default_rng(471).random((Nq, Nd)) < 0.3)
+    g = torch.where(keep, g, torch.zeros_like(g))
+    g[0] = 0.0  # a query with no gradient at all
+    _check_bwd(ms, oracle_mod, w, torch.from_numpy(ra), g)
+    dQ, dD, _, _ = _run_bwd(ms, w, torch.from_numpy(ra), g)
+    assert torch.all(dQ[0] == 0), "a query whose gradients are all zero"
+    rdQ, rdD, _, _ = oracle_mod.bwd(w.Q, w.D, torch.from_numpy(ra), g, w.q_mask, w.d_mask)
+    zero_rows = np.all(rdD == 0, axis=-1)  # destinations with no term of nonzero weight
+    assert zero_rows.any() and torch.all(dD[torch.from_numpy(zero_rows)] == 0)
+
+
 def test_bwd_full_size(ms, oracle_mod):
     """Backward at the ColPali shapes (dQ [128,128,128], dD [128,1024,128]) as
     the benchmark times it: through the argmax saved by the GPU forward (its
