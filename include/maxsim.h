@@ -269,9 +269,10 @@ maxsim_status_t maxsim_bwd(maxsim_dtype_t dtype, const void* Q, const void* D, i
  * fp32 direct-form evaluation could pick: its exact squared distance exceeds
  * the exact minimum by at most gamma_5 (u = 2^-23) times their sum, ties
  * going to the lowest index. (The search itself runs on the matrix cores in
- * the expanded form; every candidate inside that form's rounding bound of
- * the minimum is re-evaluated in the direct form, and a source with too many
- * such candidates is decided by a direct-form scan of its whole target set.)
+ * the expanded form with bf16 hi/lo parts of the coordinates; every
+ * candidate inside that form's rounding bound of the minimum is re-evaluated
+ * in the direct form, and a source with too many such candidates is decided
+ * by a direct-form scan of its whole target set.)
  * The loss sums each set's distances in a fixed order whose rounding depth
  * is at most ceil(n / 16384) + 25 additions. B == 0 enqueues nothing.
  * Errors: SHAPE (negative sizes; N == 0 or M == 0 with B > 0), NULL,

@@ -31,8 +31,8 @@ FLAGS = [
 ]
 
 
-# Per-source additions. The Chamfer kernel's K = 4 fp32 MFMAs feed VALU min
-# updates directly, so their results go to ordinary VGPRs instead of the
+# Per-source additions. The Chamfer kernel's MFMA results feed VALU min
+# updates directly, so they go to ordinary VGPRs instead of the
 # accumulation registers (no copy back per MFMA); the other kernels keep the
 # compiler's default register form.
 EXTRA = {"chamfer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -7,38 +7,43 @@
 // Design: the search for the nearest point runs on the matrix cores. The pages
 // obtain Chamfer from MaxSim by putting a squared distance where the inner
 // product was, so the distance tile is formed as a contraction: ||s - t||^2 =
-// ||s||^2 + (||t||^2 - 2 <s, t>), where the bracket is one
-// v_mfma_f32_16x16x4_f32 per 16 x 16 tile with the targets (tx, ty, tz,
-// ||t||^2) as rows of A and the sources (-2 sx, -2 sy, -2 sz, 1) as columns of
-// B (K = 4, fp32 in and out). Coordinates are first taken relative to the
-// mean of the target set's first 64 points, so the rounding scales with the
-// sets' extent rather than their offset from the origin.
+// ||s||^2 + (||t||^2 - 2 <s, t>). Coordinates are first taken relative to the
+// mean of the target set's first 64 points (so the rounding scales with the
+// sets' extent rather than their offset from the origin), and each of the
+// target's x, y, z, ||t||^2 and the source's -2x, -2y, -2z is split into two
+// bf16 parts, hi = bf16(v) and lo = bf16(v - hi). One
+// v_mfma_f32_32x32x16_bf16 then gives the bracket of a 32 x 32 tile (targets
+// as rows of A, sources as columns of B) from the hi x hi, lo x hi and
+// hi x lo products of the coordinates and the two parts of ||t||^2, 11 of its
+// 16 K slots: four times the values per matrix-core cycle of an fp32
+// 16x16x4 MFMA, with a rounding bound of order 2^-14 |s'|^2 (the dropped
+// lo x lo products and the parts' own rounding) instead of 2^-21 |s'|^2.
 //
-// The expanded form cancels: its rounding error is of the order of u |s'|^2,
-// far above that of the direct form sum_k (s_k - t_k)^2 when the nearest
-// distance is small. So the matrix-core pass only finds candidates, and the
-// answer is decided in the direct form: a lane owns one source column and 4
-// target rows of each tile, and per 256-target tile it folds its 64 values
-// into the tile's min. Two slots keep the tiles whose min lies within the
-// expanded form's rounding bound tau(b) of the running min b (the best tile
-// and one more); a third tile inside the window while both slots are still
-// inside it marks the source as overflowed. At the end every kept tile whose
-// min is within tau of the source's overall min (over the 4 lanes of the
-// column) is re-evaluated row by row in the direct form from the raw fp32
-// coordinates, and the smallest direct value wins, lowest index on ties. The
-// exact nearest point is always among the re-evaluated rows, so the returned
-// index is one a direct-form fp32 evaluation could return, and the distance
-// written is that evaluation. An overflowed source is written with index -1,
-// and chamfer_fix_kernel then scans its whole target set in the direct form.
+// That search form cancels: its rounding error is far above that of the
+// direct form sum_k (s_k - t_k)^2 when the nearest distance is small. So the
+// matrix-core pass only finds candidates, and the answer is decided in the
+// direct form: a lane owns one source column and 16 target rows of each
+// 32-row block (rows 8 g + 4 h + r, h = lane / 32), and per 256-target tile
+// it folds its 128 values into the tile's min. Three slots keep the tiles
+// whose min lies within the search form's rounding window thr(b) of the
+// running min b (the best tile and two more); a fourth tile inside the window
+// while the oldest kept one is still inside it marks the source as
+// overflowed. At the end every kept tile whose min is within the window of
+// the source's overall min (over the column's 2 lanes) is re-evaluated row by
+// row in the direct form from the raw fp32 coordinates, and the smallest
+// direct value wins, lowest index on ties. The exact nearest point is always
+// among the re-evaluated rows, so the returned index is one a direct-form
+// fp32 evaluation could return, and the distance written is that evaluation.
+// An overflowed source is written with index -1, and chamfer_fix_kernel then
+// scans its whole target set in the direct form.
 //
 // Every wave is its own workgroup and streams its own copy of the target set
-// through LDS in 256-point tiles (coalesced loads, prepared as
-// (x, y, z, ||t||^2), double-buffered), so no barriers are needed. The
-// sources of all batches and both directions form one list of 16-point
-// blocks; wave w takes a contiguous run of blocks (the runs differ by at most
-// one block), cut where a (batch, direction) segment ends, and holds up to
-// kChMaxBlocks blocks in registers, so every target tile feeds that many
-// MFMAs per LDS read.
+// through LDS in 256-point tiles (coalesced loads, prepared as two planes of
+// bf16 A rows), so no barriers are needed. The sources of all batches and
+// both directions form one list of 32-point blocks; wave w takes a contiguous
+// run of blocks (the runs differ by at most one block), cut where a (batch,
+// direction) segment ends, and holds up to kChMaxBlocks blocks in registers,
+// so every A row read from LDS feeds that many MFMAs.
 #include <atomic>
 
 #include "common.hpp"
@@ -48,9 +53,21 @@ namespace maxsim {
 
 namespace {
 
-constexpr int kChTileT = 256;    // target points per LDS tile
-constexpr int kChMaxBlocks = 5;  // 16-point source blocks a wave holds at once
-typedef float f4v __attribute__((ext_vector_type(4)));
+#ifndef MAXSIM_CH_TILE
+#define MAXSIM_CH_TILE 256
+#endif
+#ifndef MAXSIM_CH_BLOCKS
+#define MAXSIM_CH_BLOCKS 4
+#endif
+#ifndef MAXSIM_CH_WAVES
+#define MAXSIM_CH_WAVES 2
+#endif
+constexpr int kChTileT = MAXSIM_CH_TILE;      // target points per LDS tile
+constexpr int kChBlk = 32;                    // source points per block (one MFMA column block)
+constexpr int kChMaxBlocks = MAXSIM_CH_BLOCKS;  // source blocks a wave holds at once
+constexpr int kChRB = kChTileT / 32;          // 32-row blocks per tile
+constexpr int kChRaw = kChTileT * 3 / 64;     // raw coordinates per lane per tile
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void cham_barrier()
 {
@@ -60,64 +77,87 @@ __device__ __forceinline__ void cham_barrier()
     asm volatile("" ::: "memory");
 }
 
-// LDS of one wave: two prepared tiles and the raw coordinates being prepared
+// bits of (__bf16)x | (__bf16)y << 16, both rounded to nearest even
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y)
+{
+    const bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
+
+// LDS of one wave: the prepared tile as two planes of 16-byte rows (plane h
+// holds the 8 bf16 of K-half h of every target's A row), and the raw
+// coordinates being prepared. A wave reads all of a tile's rows into
+// registers before it prepares the next tile into the same planes (the
+// wave's LDS operations complete in order), so one tile buffer suffices.
 struct ChamLds {
-    f4v tile[2][kChTileT];
+    i32x4 tile[2][kChTileT];
     float raw[kChTileT * 3];
 };
 
-// Coordinates [t0*3, t0*3 + 768) of a target set with nt points, one float
+// Coordinates [t0*3, t0*3 + 3*kChTileT) of a target set with nt points, one float
 // per (lane, m) at 64*m + lane: every load instruction reads 256 contiguous
 // bytes. Past the set's end the value is 0.
 __device__ __forceinline__ void cham_load_raw(const float* __restrict__ T, int64_t nt, int64_t t0, int lane,
-                                              float (&r)[12])
+                                              float (&r)[kChRaw])
 {
     const int64_t lim = nt * 3, base = t0 * 3;
 #pragma unroll
-    for (int m = 0; m < 12; ++m) {
+    for (int m = 0; m < kChRaw; ++m) {
         const int64_t f = base + 64 * m + lane;
         r[m] = f < lim ? T[f] : 0.f;
     }
 }
 
-// Raw coordinates -> tile entries (x, y, z, ||t||^2); points past the set's
-// end get ||t||^2 = +inf, so their distance is +inf and never wins.
-__device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (&r)[12], int64_t nt, int64_t t0,
+// Raw coordinates -> A rows. With t' = t - c (fp32) and n = |t'|^2 (fp32),
+// each of tx', ty', tz', n is split into bf16 parts hi = bf16(v) and
+// lo = bf16(v - hi) (v - hi is exact in fp32), and the row holds
+//   K 0..7  (plane 0): hx hy hz lx ly lz hx hy
+//   K 8..15 (plane 1): hz nh nl 0 0 0 0 0
+// against the source columns' -2 hi / -2 lo parts (cham_piece), so one
+// bf16 MFMA gives nh + nl - 2 (<th, sh> + <tl, sh> + <th, sl>). Points past
+// the set's end get hi = lo = 0 and nh = +inf: their value is +inf.
+__device__ __forceinline__ void cham_prepare(ChamLds& sm, const float (&r)[kChRaw], int64_t nt, int64_t t0,
                                              int lane, float cx, float cy, float cz)
 {
 #pragma unroll
-    for (int m = 0; m < 12; ++m) sm.raw[64 * m + lane] = r[m];
+    for (int m = 0; m < kChRaw; ++m) sm.raw[64 * m + lane] = r[m];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to its reads
-    // lane l prepares points l, l+64, l+128, l+192 (odd word stride between
-    // lanes: no LDS bank conflicts)
+    // lane l prepares points l, l+64, ... (odd word stride between lanes: no
+    // LDS bank conflicts)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kChTileT / 64; ++u) {
         const int p = lane + 64 * u;  // point of the tile
+        const bool in = t0 + p < nt;
         const float x = sm.raw[3 * p] - cx, y = sm.raw[3 * p + 1] - cy, z = sm.raw[3 * p + 2] - cz;
-        const float n2 = t0 + p < nt ? __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x)) : __builtin_inff();
-        sm.tile[buf][p] = f4v{x, y, z, n2};
+        const float n = in ? __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x)) : 0.f;
+        const uint32_t hxy = pk_bf16(x, y), hzn = pk_bf16(z, n);
+        const uint32_t lxy = pk_bf16(x - bf16_lo(hxy), y - bf16_hi(hxy));
+        const uint32_t lzn = pk_bf16(z - bf16_lo(hzn), n - bf16_hi(hzn));
+        const i32x4 p0 = {(int)hxy, (int)((hzn & 0xffffu) | (lxy << 16)), (int)((lxy >> 16) | (lzn << 16)), (int)hxy};
+        const i32x4 p1 = {in ? (int)hzn : (int)0x7f800000, in ? (int)(lzn >> 16) : 0, 0, 0};
+        sm.tile[0][p] = p0;
+        sm.tile[1][p] = p1;
     }
 }
 
 }  // namespace
 
 // Near-tie window of the matrix-core pass. For a source s' (coordinates
-// relative to the centring point) whose running min of the bracket
-// ||t'||^2 - 2 <s', t'> is b, a target t can still be the exact nearest point
-// only if its bracket is at most thr(b) = b + 2^-18 (18 |s'|^2 + 12 b). This
-// holds for any rounding with unit u <= 2^-23 of: the centring differences,
-// ||t'||^2 (two fused steps), and a 4-term fp32 dot product with any order of
-// its products and sums. For such a t the error of the bracket is at most
-// gamma_12 ((|s'| + |t'|)^2 + |s - t|^2) with |t'| <= |s'| + |s - t|, and the
-// window is twice that bound for both the true and the found minimum, written
-// with b + |s'|^2 in place of the distance.
-constexpr float kTauK = 1.0f + 12.0f * 0x1p-18f;
-constexpr float kTau0 = 18.0f * 0x1p-18f;
-
-// 4 consecutive points (12 floats), read with one 48-byte copy
-struct __attribute__((aligned(4))) ChRows4 {
-    float v[12];
-};
+// relative to the centring point) whose running min of the computed bracket
+// b~(t) = |t'|^2 - 2 <s', t'> is b, a target t can still be the exact nearest
+// point only if b~(t) <= thr(b) = b + tau (2 |s'|^2 + b). The split form
+// above drops the lo x lo products and the parts' rounding (each part
+// within 2^-9 of its remainder), and sums 11 exact products in fp32 in any
+// order (u <= 2^-23); with the centring differences and the fp32 |t'|^2 this
+// puts the computed |s'|^2 + b~(t) within E(t) = 2^-14 (|s'|^2 + |s - t|^2)
+// of the exact squared distance, using |t'| <= |s'| + |s - t|. For the exact
+// nearest point t* and the found minimum t_f, b~(t*) <= b + 2 E(t_f), and
+// E(t_f) <= 2^-14 (2 |s'|^2 + b) / (1 - 2^-14), so tau = 2^-13 / (1 - 2^-14),
+// taken 1 % larger for the fp32 rounding of thr itself.
+constexpr float kTau = 0x1.03p-13f;
+constexpr float kTauK = 1.0f + kTau;
 
 // KN source blocks of one (batch, direction) segment against its whole
 // target set: A [na, 3] holds the sources, blocks k0 .. k0+KN-1; T [nt, 3]
@@ -129,11 +169,11 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
                                            float* __restrict__ dist, int32_t* __restrict__ idx)
 {
     const int lane = threadIdx.x;
-    const int col = lane & 15, rg = lane >> 4;  // source column, target row group (= K index of A, B)
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const int col = lane & 31, h = lane >> 5;  // source column; K-half of the operands, row half of the results
+    const f32x16 zero = {};
     // centring point: the mean of the target set's first (up to) 64 points.
     // The butterfly sum gives every lane the same bits; the distances do not
-    // depend on it, only the expanded form's rounding does.
+    // depend on it, only the search's rounding does.
     float cx, cy, cz;
     {
         const int m = (int)(nt < 64 ? nt : 64);
@@ -155,85 +195,90 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
         cz = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(z * inv)));
     }
 
-    // per source of each block (clamped copies past the end): the B operand,
-    // the window constant, the running min and its tile, the second kept tile
-    float bop[KN], tau0[KN], best[KN], v1[KN];
-    int s0[KN], s1[KN];
+    // per source of each block (clamped copies past the end): the B operand
+    // (K-half h of -2 s' split into bf16 parts: hx hy hz hx hy hz lx ly | lz 1 1 0 ...),
+    // the window constant, the running min and its tile, two more kept tiles
+    i32x4 bop[KN];
+    float tau0[KN], best[KN], v1[KN], v2[KN];
+    int s0[KN], s1[KN], s2[KN];
     bool ovf[KN];
 #pragma unroll
     for (int u = 0; u < KN; ++u) {
-        int64_t sp = (k0 + u) * 16 + col;
+        int64_t sp = (k0 + u) * kChBlk + col;
         sp = sp < na ? sp : na - 1;
         const float sx = A[sp * 3] - cx, sy = A[sp * 3 + 1] - cy, sz = A[sp * 3 + 2] - cz;
-        const float comp = rg == 0 ? sx : (rg == 1 ? sy : sz);
-        bop[u] = rg < 3 ? -2.f * comp : 1.f;
-        tau0[u] = kTau0 * __builtin_fmaf(sz, sz, __builtin_fmaf(sy, sy, sx * sx));
+        const uint32_t hxy = pk_bf16(-2.f * sx, -2.f * sy), hz1 = pk_bf16(-2.f * sz, 1.f);
+        const uint32_t lxy = pk_bf16(-2.f * sx - bf16_lo(hxy), -2.f * sy - bf16_hi(hxy));
+        const uint32_t lz = pk_bf16(-2.f * sz - bf16_lo(hz1), 0.f);
+        if (h == 0)
+            bop[u] = i32x4{(int)hxy, (int)((hz1 & 0xffffu) | (hxy << 16)), (int)((hxy >> 16) | (hz1 << 16)), (int)lxy};
+        else
+            bop[u] = i32x4{(int)((lz & 0xffffu) | 0x3f800000u), 0x3f80, 0, 0};
+        tau0[u] = 2.f * kTau * __builtin_fmaf(sz, sz, __builtin_fmaf(sy, sy, sx * sx));
         best[u] = __builtin_inff();
         v1[u] = __builtin_inff();
+        v2[u] = __builtin_inff();
         s0[u] = 0;
         s1[u] = 0;
+        s2[u] = 0;
         ovf[u] = false;
     }
 
     const int64_t ntiles = (nt + kChTileT - 1) / kChTileT;
-    float raw[12];
+    float raw[kChRaw];
     cham_load_raw(T, nt, 0, lane, raw);
-    cham_prepare(sm, 0, raw, nt, 0, lane, cx, cy, cz);
+    cham_prepare(sm, raw, nt, 0, lane, cx, cy, cz);
     for (int64_t it = 0; it < ntiles; ++it) {
         const int64_t t0 = it * kChTileT;
-        const int buf = (int)(it & 1);
-        if (it + 1 < ntiles) cham_load_raw(T, nt, t0 + kChTileT, lane, raw);
+        // the next tile's coordinates (past the last tile: all padding, the
+        // preparation below is then unused; no branch in the loop body)
+        cham_load_raw(T, nt, t0 + kChTileT, lane, raw);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the tile is prepared
-        const int64_t left = nt - t0;
-        const int tbs = __builtin_amdgcn_readfirstlane(left >= kChTileT ? kChTileT / 16 : (int)((left + 15) / 16));
-        const float* tf = (const float*)&sm.tile[buf][0] + col * 4 + rg;  // A[row col][k rg] of block 0
-        // mp: this tile's min of the lane's rows, per source
+        // A rows of the tile's row blocks: lane l reads row 32 rb + l % 32 of plane l / 32
+        i32x4 av[kChRB];
+#pragma unroll
+        for (int rb = 0; rb < kChRB; ++rb) av[rb] = sm.tile[h][32 * rb + col];
+        // mp: this tile's min of the lane's rows, per source. The MFMAs of
+        // row block rb + 1 are issued before the fold of row block rb, and
+        // no later block's MFMAs move above that fold (two blocks' results
+        // live at a time)
         float mp[KN];
-        if (tbs == kChTileT / 16) {
-            // a full tile: every block's operand is read up front, and the
-            // blocks go in pairs, the MFMAs issued at raised priority (the
-            // SIMD's other waves yield the issue slots to the MFMA stream)
-            float av[kChTileT / 16];
+        auto mfmas = [&](int rb, f32x16 (&d)[KN]) {
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int tb = 0; tb < kChTileT / 16; ++tb) av[tb] = tf[tb * 64];
+            for (int u = 0; u < KN; ++u)
+                d[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[rb]),
+                                                               __builtin_bit_cast(bf16x8, bop[u]), zero, 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
+        };
+        f32x16 dc[KN], dn[KN];
+        mfmas(0, dc);
 #pragma unroll
-            for (int tb = 0; tb < kChTileT / 16; tb += 2) {
-                f32x4 d[KN], e[KN];
-                __builtin_amdgcn_s_setprio(1);
+        for (int rb = 0; rb < kChRB; ++rb) {
+            if (rb + 1 < kChRB) mfmas(rb + 1, dn);
 #pragma unroll
-                for (int u = 0; u < KN; ++u) d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[tb], bop[u], zero, 0, 0, 0);
-#pragma unroll
-                for (int u = 0; u < KN; ++u) e[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[tb + 1], bop[u], zero, 0, 0, 0);
-                __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-                for (int u = 0; u < KN; ++u) {
-                    const float x = __builtin_fminf(__builtin_fminf(d[u][0], d[u][1]), d[u][2]);
-                    const float y = __builtin_fminf(__builtin_fminf(d[u][3], e[u][0]), e[u][1]);
-                    if (tb == 0) {
-                        mp[u] = __builtin_fminf(__builtin_fminf(__builtin_fminf(e[u][2], e[u][3]), x), y);
-                    } else {
-                        const float z = __builtin_fminf(__builtin_fminf(e[u][2], e[u][3]), mp[u]);
-                        mp[u] = __builtin_fminf(__builtin_fminf(x, y), z);
-                    }
-                }
+            for (int u = 0; u < KN; ++u) {
+                const f32x16& d = dc[u];
+                const float a0 = __builtin_fminf(__builtin_fminf(d[0], d[1]), d[2]);
+                const float a1 = __builtin_fminf(__builtin_fminf(d[3], d[4]), d[5]);
+                const float a2 = __builtin_fminf(__builtin_fminf(d[6], d[7]), d[8]);
+                const float a3 = __builtin_fminf(__builtin_fminf(d[9], d[10]), d[11]);
+                const float a4 = __builtin_fminf(__builtin_fminf(d[12], d[13]), d[14]);
+                const float b0 = __builtin_fminf(__builtin_fminf(a0, a1), a2);
+                const float b1 = __builtin_fminf(__builtin_fminf(a3, a4), d[15]);
+                mp[u] = rb == 0 ? __builtin_fminf(b0, b1) : __builtin_fminf(__builtin_fminf(b0, b1), mp[u]);
             }
-        } else {
+            __builtin_amdgcn_sched_barrier(0);
+            if (rb + 1 < kChRB) {
 #pragma unroll
-            for (int u = 0; u < KN; ++u) mp[u] = __builtin_inff();
-            for (int tb = 0; tb < tbs; ++tb) {
-                const float aop = tf[tb * 64];
-#pragma unroll
-                for (int u = 0; u < KN; ++u) {
-                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop[u], zero, 0, 0, 0);
-                    mp[u] = __builtin_fminf(__builtin_fminf(__builtin_fminf(d[0], d[1]), __builtin_fminf(d[2], d[3])),
-                                            mp[u]);
-                }
+                for (int u = 0; u < KN; ++u) dc[u] = dn[u];
             }
         }
-        // the two kept tiles: a tile inside the window of the running min is
-        // kept; a lower tile becomes the best and the old best the second; a
-        // third tile inside the window while the second is still inside it
-        // overflows. Equal mins keep the earlier tile as the best.
+        // the three kept tiles: a tile inside the window of the running min
+        // is kept; a lower tile becomes the best and the old best the
+        // second; the other kept tiles move down one slot, and the one moved
+        // out of the third slot overflows the source when it is still inside
+        // the window. Equal mins keep the earlier tile as the best.
         const int step = (int)it;
 #pragma unroll
         for (int u = 0; u < KN; ++u) {
@@ -242,100 +287,97 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
             const bool lower = mp[u] < best[u];
             const float bn = __builtin_fminf(best[u], mp[u]);
             const float thr_new = __builtin_fmaf(bn, kTauK, tau0[u]);
-            ovf[u] = ovf[u] | (near & (v1[u] <= thr_new));  // bitwise: no branches
+            ovf[u] = ovf[u] | (near & (v2[u] <= thr_new));  // bitwise: no branches
+            v2[u] = near ? v1[u] : v2[u];
+            s2[u] = near ? s1[u] : s2[u];
             v1[u] = near ? __builtin_fmaxf(best[u], mp[u]) : v1[u];
             s1[u] = near ? (lower ? s0[u] : step) : s1[u];
             s0[u] = lower ? step : s0[u];
             best[u] = bn;
         }
-        if (it + 1 < ntiles) cham_prepare(sm, buf ^ 1, raw, nt, t0 + kChTileT, lane, cx, cy, cz);
+        cham_prepare(sm, raw, nt, t0 + kChTileT, lane, cx, cy, cz);
     }
 
     // the answer in the direct form: the kept tiles inside the window of the
-    // source's overall min are re-evaluated on this lane's rows from the raw
+    // source's overall min are re-evaluated on their rows from the raw
     // coordinates; the smallest value wins, the lowest index on ties, then
-    // the 4 row groups of the column are merged the same way
+    // the two row halves of the column are merged the same way
 #pragma unroll
     for (int u = 0; u < KN; ++u) {
-        int64_t sp = (k0 + u) * 16 + col;
+        int64_t sp = (k0 + u) * kChBlk + col;
         const bool own = sp < na;
         sp = own ? sp : na - 1;
         const float px = A[sp * 3], py = A[sp * 3 + 1], pz = A[sp * 3 + 2];
         float bs = best[u];
-        bs = __builtin_fminf(bs, __shfl_xor(bs, 16, 64));
         bs = __builtin_fminf(bs, __shfl_xor(bs, 32, 64));
         const float thr = __builtin_fmaf(bs, kTauK, tau0[u]);
         int lost = (ovf[u] & (best[u] <= thr)) ? 1 : 0;
-        lost |= __shfl_xor(lost, 16, 64);
         lost |= __shfl_xor(lost, 32, 64);
         float dv = __builtin_inff();
         int di = 0x7fffffff;
-        // The column's tasks are the kept tiles of its 4 lanes: bit 2j + slot
-        // is set when lane j keeps that slot (j = the lane's row group). Each
-        // task's 64 rows (rows 4j .. 4j+3 of the tile's 16 blocks) are split
-        // over the column's 4 lanes, lane rg taking blocks 4rg .. 4rg+3, so a
-        // wave makes one pass of 16 rows per task of its busiest column.
-        const int mine = ((best[u] <= thr) ? 1 : 0) | ((v1[u] <= thr) ? 2 : 0);
-        int mask = mine << (2 * rg);
-        mask |= __shfl_xor(mask, 16, 64);
+        // The column's tasks are the kept tiles of its 2 lanes: bit 3j + slot
+        // is set when lane half j keeps that slot. A task's rows (rows
+        // 32 rb + 8 g + 4 j + r of the tile, g, r < 4) are split over the
+        // column's 2 lanes, lane h taking the first or second half of the row
+        // blocks, as runs of 4 consecutive points, 8 runs at a time.
+        const int mine = ((best[u] <= thr) ? 1 : 0) | ((v1[u] <= thr) ? 2 : 0) | ((v2[u] <= thr) ? 4 : 0);
+        int mask = mine << (3 * h);
         mask |= __shfl_xor(mask, 32, 64);
-        int tile[8];
+        int tile[6];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            tile[2 * j] = __shfl(s0[u], col + 16 * j, 64);
-            tile[2 * j + 1] = __shfl(s1[u], col + 16 * j, 64);
+        for (int j = 0; j < 2; ++j) {
+            tile[3 * j] = __shfl(s0[u], col + 32 * j, 64);
+            tile[3 * j + 1] = __shfl(s1[u], col + 32 * j, 64);
+            tile[3 * j + 2] = __shfl(s2[u], col + 32 * j, 64);
         }
+        constexpr int kRuns = 4 * kChRB / 2;  // runs of 4 points per lane per task
         while (__any(mask != 0)) {
             if (mask != 0) {
                 const int q = __builtin_ctz(mask);
                 mask &= mask - 1;
                 int tq = tile[0];
 #pragma unroll
-                for (int k = 1; k < 8; ++k) tq = q == k ? tile[k] : tq;
-                const int64_t tb = (int64_t)tq * kChTileT + 4 * (q >> 1) + 64 * rg;
-                ChRows4 x[4];
+                for (int k = 1; k < 6; ++k) tq = q == k ? tile[k] : tq;
+                const int64_t tb = (int64_t)tq * kChTileT + 4 * (q >= 3 ? 1 : 0) + 32 * (kChRB / 2) * h;
+                const int64_t lim = nt * 3 - 1;
+                for (int k0 = 0; k0 < kRuns; k0 += 8) {
+                    // every load of 8 runs in flight at once (flat indices
+                    // clamped into the set; rows past its end are not evaluated)
+                    float x[8][12];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int64_t t = tb + 16 * k;
-                    if (t + 3 < nt) __builtin_memcpy(&x[k], T + t * 3, sizeof(ChRows4));
-                }
+                    for (int k = 0; k < 8; ++k) {
+                        const int kk = k0 + k;
+                        const int64_t f = (tb + 32 * (kk >> 2) + 8 * (kk & 3)) * 3;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int64_t t = tb + 16 * k;
+                        for (int e = 0; e < 12; ++e) x[k][e] = T[f + e < lim ? f + e : lim];
+                    }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float tx, ty, tz;
-                        if (t + 3 < nt) {
-                            tx = x[k].v[3 * r];
-                            ty = x[k].v[3 * r + 1];
-                            tz = x[k].v[3 * r + 2];
-                        } else if (t + r < nt) {
-                            tx = T[(t + r) * 3];
-                            ty = T[(t + r) * 3 + 1];
-                            tz = T[(t + r) * 3 + 2];
-                        } else {
-                            continue;
-                        }
-                        const float dx = px - tx, dy = py - ty, dz = pz - tz;
-                        const float v = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
-                        if (v < dv || (v == dv && (int)(t + r) < di)) {
-                            dv = v;
-                            di = (int)(t + r);
+                    for (int k = 0; k < 8; ++k) {
+                        const int kk = k0 + k;
+                        const int64_t t = tb + 32 * (kk >> 2) + 8 * (kk & 3);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (t + r >= nt) continue;
+                            const float dx = px - x[k][3 * r], dy = py - x[k][3 * r + 1], dz = pz - x[k][3 * r + 2];
+                            const float v = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+                            if (v < dv || (v == dv && (int)(t + r) < di)) {
+                                dv = v;
+                                di = (int)(t + r);
+                            }
                         }
                     }
                 }
             }
         }
-#pragma unroll
-        for (int x = 16; x <= 32; x <<= 1) {
-            const float ov = __shfl_xor(dv, x, 64);
-            const int oi = __shfl_xor(di, x, 64);
+        {
+            const float ov = __shfl_xor(dv, 32, 64);
+            const int oi = __shfl_xor(di, 32, 64);
             if (ov < dv || (ov == dv && oi < di)) {
                 dv = ov;
                 di = oi;
             }
         }
-        if (rg == 0 && own) {
+        if (h == 0 && own) {
             if (lost) {
                 idx[sp] = -1;
             } else {
@@ -481,11 +523,11 @@ __global__ __launch_bounds__(kFixThreads) void chamfer_fix_kernel(ChamferArgs a)
 // One wave per workgroup; see the file comment. Block g of the list is
 // source block g of direction 1 (P against Q) for g < B*nb1, else of
 // direction 2 (Q against P); each direction is batch-major.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void chamfer_nn_kernel(ChamferArgs a, int64_t nblocks)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MAXSIM_CH_WAVES))) void chamfer_nn_kernel(ChamferArgs a, int64_t nblocks)
 {
     __shared__ ChamLds sm;
     const int64_t nw = gridDim.x, w = blockIdx.x;
-    const int64_t nb1 = (a.N + 15) / 16, nb2 = (a.M + 15) / 16;
+    const int64_t nb1 = (a.N + kChBlk - 1) / kChBlk, nb2 = (a.M + kChBlk - 1) / kChBlk;
     const int64_t g_first = w * nblocks / nw, g_last = (w + 1) * nblocks / nw;
 
     for (int64_t g0 = g_first; g0 < g_last;) {
@@ -505,10 +547,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void ch
         int32_t* idx = (second ? a.idx2 : a.idx1) + b * na;
         switch (__builtin_amdgcn_readfirstlane((int)nk)) {
         case 1: cham_piece<1>(sm, A, na, T, nt, k0, dist, idx); break;
-        case 2: cham_piece<2>(sm, A, na, T, nt, k0, dist, idx); break;
-        case 3: cham_piece<3>(sm, A, na, T, nt, k0, dist, idx); break;
-        case 4: cham_piece<4>(sm, A, na, T, nt, k0, dist, idx); break;
-        default: cham_piece<5>(sm, A, na, T, nt, k0, dist, idx); break;
+        case 2: if constexpr (kChMaxBlocks >= 2) cham_piece<2>(sm, A, na, T, nt, k0, dist, idx); break;
+        case 3: if constexpr (kChMaxBlocks >= 3) cham_piece<3>(sm, A, na, T, nt, k0, dist, idx); break;
+        default: if constexpr (kChMaxBlocks >= 4) cham_piece<4>(sm, A, na, T, nt, k0, dist, idx); break;
         }
     }
 }
@@ -574,7 +615,7 @@ hipError_t launch_chamfer_fwd(ChamferArgs a, hipStream_t stream)
             occ = 8;
         per_cu.store(occ, std::memory_order_relaxed);
     }
-    const int64_t nblocks = a.B * ((a.N + 15) / 16 + (a.M + 15) / 16);
+    const int64_t nblocks = a.B * ((a.N + kChBlk - 1) / kChBlk + (a.M + kChBlk - 1) / kChBlk);
     int64_t waves = (int64_t)occ * device_cu_count();
     if (waves * kChMaxBlocks < nblocks) waves = (nblocks + kChMaxBlocks - 1) / kChMaxBlocks;
     if (waves > nblocks) waves = nblocks;
