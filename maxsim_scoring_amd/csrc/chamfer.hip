@@ -37,13 +37,16 @@
 // An overflowed source is written with index -1, and chamfer_fix_kernel then
 // scans its whole target set in the direct form.
 //
-// Every wave is its own workgroup and streams its own copy of the target set
-// through LDS in 256-point tiles (coalesced loads, prepared as two planes of
-// bf16 A rows), so no barriers are needed. The sources of all batches and
-// both directions form one list of 32-point blocks; wave w takes a contiguous
-// run of blocks (the runs differ by at most one block), cut where a (batch,
-// direction) segment ends, and holds up to kChMaxBlocks blocks in registers,
-// so every A row read from LDS feeds that many MFMAs.
+// A workgroup of kChWaves waves streams its segment's target set through LDS
+// in 256-point tiles (coalesced loads, prepared as two planes of bf16 A rows,
+// double-buffered): each wave prepares a quarter of every tile, one tile
+// ahead, and one barrier per tile publishes it, so the splitting work is
+// shared by the four waves. The sources of all batches and both directions
+// form one list of 32-point blocks; workgroup w takes a contiguous run of
+// blocks (the runs differ by at most one block) in pieces cut where a (batch,
+// direction) segment ends, and each wave holds up to kChMaxBlocks of a
+// piece's blocks in registers, so every A row read from LDS feeds that many
+// MFMAs.
 #include <atomic>
 
 #include "common.hpp"
@@ -66,7 +69,10 @@ constexpr int kChTileT = MAXSIM_CH_TILE;      // target points per LDS tile
 constexpr int kChBlk = 32;                    // source points per block (one MFMA column block)
 constexpr int kChMaxBlocks = MAXSIM_CH_BLOCKS;  // source blocks a wave holds at once
 constexpr int kChRB = kChTileT / 32;          // 32-row blocks per tile
-constexpr int kChRaw = kChTileT * 3 / 64;     // raw coordinates per lane per tile
+constexpr int kChWaves = 4;                   // waves per workgroup, sharing the target tiles
+constexpr int kChQuarter = kChTileT / kChWaves;  // targets each wave prepares per tile
+constexpr int kChRaw = kChQuarter * 3 / 64;   // raw coordinates per lane per tile
+static_assert(kChQuarter == 64, "one target per lane per tile");
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void cham_barrier()
@@ -86,18 +92,16 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y)
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
 
-// LDS of one wave: the prepared tile as two planes of 16-byte rows (plane h
-// holds the 8 bf16 of K-half h of every target's A row), and the raw
-// coordinates being prepared. A wave reads all of a tile's rows into
-// registers before it prepares the next tile into the same planes (the
-// wave's LDS operations complete in order), so one tile buffer suffices.
+// LDS of a workgroup: two prepared tiles, each as two planes of 16-byte
+// rows (plane h holds the 8 bf16 of K-half h of every target's A row), and
+// each wave's raw coordinates being prepared.
 struct ChamLds {
-    i32x4 tile[2][kChTileT];
-    float raw[kChTileT * 3];
+    i32x4 tile[2][2][kChTileT];
+    float raw[kChWaves][kChQuarter * 3];
 };
 
-// Coordinates [t0*3, t0*3 + 3*kChTileT) of a target set with nt points, one float
-// per (lane, m) at 64*m + lane: every load instruction reads 256 contiguous
+// Coordinates of targets [t0, t0 + 64) of a set with nt points, one float per
+// (lane, m) at 64*m + lane: every load instruction reads 256 contiguous
 // bytes. Past the set's end the value is 0.
 __device__ __forceinline__ void cham_load_raw(const float* __restrict__ T, int64_t nt, int64_t t0, int lane,
                                               float (&r)[kChRaw])
@@ -118,27 +122,28 @@ __device__ __forceinline__ void cham_load_raw(const float* __restrict__ T, int64
 // against the source columns' -2 hi / -2 lo parts (cham_piece), so one
 // bf16 MFMA gives nh + nl - 2 (<th, sh> + <tl, sh> + <th, sl>). Points past
 // the set's end get hi = lo = 0 and nh = +inf: their value is +inf.
-__device__ __forceinline__ void cham_prepare(ChamLds& sm, const float (&r)[kChRaw], int64_t nt, int64_t t0,
-                                             int lane, float cx, float cy, float cz)
+// Wave `wave` prepares targets [t0 + 64 wave, t0 + 64 wave + 64) of the tile
+// at t0 into buffer `buf`, one per lane, from its coordinates r.
+__device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (&r)[kChRaw], int64_t nt,
+                                             int64_t t0, int wave, int lane, float cx, float cy, float cz)
 {
+    float* raw = sm.raw[wave];
 #pragma unroll
-    for (int m = 0; m < kChRaw; ++m) sm.raw[64 * m + lane] = r[m];
+    for (int m = 0; m < kChRaw; ++m) raw[64 * m + lane] = r[m];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to its reads
-    // lane l prepares points l, l+64, ... (odd word stride between lanes: no
-    // LDS bank conflicts)
-#pragma unroll
-    for (int u = 0; u < kChTileT / 64; ++u) {
-        const int p = lane + 64 * u;  // point of the tile
+    // odd word stride between lanes: no LDS bank conflicts
+    {
+        const int p = kChQuarter * wave + lane;  // point of the tile
         const bool in = t0 + p < nt;
-        const float x = sm.raw[3 * p] - cx, y = sm.raw[3 * p + 1] - cy, z = sm.raw[3 * p + 2] - cz;
+        const float x = raw[3 * lane] - cx, y = raw[3 * lane + 1] - cy, z = raw[3 * lane + 2] - cz;
         const float n = in ? __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x)) : 0.f;
         const uint32_t hxy = pk_bf16(x, y), hzn = pk_bf16(z, n);
         const uint32_t lxy = pk_bf16(x - bf16_lo(hxy), y - bf16_hi(hxy));
         const uint32_t lzn = pk_bf16(z - bf16_lo(hzn), n - bf16_hi(hzn));
         const i32x4 p0 = {(int)hxy, (int)((hzn & 0xffffu) | (lxy << 16)), (int)((lxy >> 16) | (lzn << 16)), (int)hxy};
         const i32x4 p1 = {in ? (int)hzn : (int)0x7f800000, in ? (int)(lzn >> 16) : 0, 0, 0};
-        sm.tile[0][p] = p0;
-        sm.tile[1][p] = p1;
+        sm.tile[buf][0][p] = p0;
+        sm.tile[buf][1][p] = p1;
     }
 }
 
@@ -160,15 +165,20 @@ constexpr float kTau = 0x1.03p-13f;
 constexpr float kTauK = 1.0f + kTau;
 
 // KN source blocks of one (batch, direction) segment against its whole
-// target set: A [na, 3] holds the sources, blocks k0 .. k0+KN-1; T [nt, 3]
-// the targets. Writes dist[sp] and idx[sp] for the blocks' points, or
+// target set: A [na, 3] holds the sources, this wave's blocks are
+// k0, k0 + kChWaves, ... (KN of them; KN = 0 for a wave that only helps
+// prepare the tiles); T [nt, 3] the targets, streamed by the whole workgroup
+// (every wave calls this with the same T, nt, and passes the same number of
+// barriers). Writes dist[sp] and idx[sp] for the blocks' points, or
 // idx[sp] = -1 when the source's near-tie candidates overflowed.
 template <int KN>
 __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict__ A, int64_t na,
                                            const float* __restrict__ T, int64_t nt, int64_t k0,
                                            float* __restrict__ dist, int32_t* __restrict__ idx)
 {
-    const int lane = threadIdx.x;
+    constexpr int KA = KN > 0 ? KN : 1;  // array extent (a KN = 0 wave only prepares tiles)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int col = lane & 31, h = lane >> 5;  // source column; K-half of the operands, row half of the results
     const f32x16 zero = {};
     // centring point: the mean of the target set's first (up to) 64 points.
@@ -198,13 +208,13 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
     // per source of each block (clamped copies past the end): the B operand
     // (K-half h of -2 s' split into bf16 parts: hx hy hz hx hy hz lx ly | lz 1 1 0 ...),
     // the window constant, the running min and its tile, two more kept tiles
-    i32x4 bop[KN];
-    float tau0[KN], best[KN], v1[KN], v2[KN];
-    int s0[KN], s1[KN], s2[KN];
-    bool ovf[KN];
+    i32x4 bop[KA];
+    float tau0[KA], best[KA], v1[KA], v2[KA];
+    int s0[KA], s1[KA], s2[KA];
+    bool ovf[KA];
 #pragma unroll
     for (int u = 0; u < KN; ++u) {
-        int64_t sp = (k0 + u) * kChBlk + col;
+        int64_t sp = (k0 + wave + kChWaves * u) * kChBlk + col;
         sp = sp < na ? sp : na - 1;
         const float sx = A[sp * 3] - cx, sy = A[sp * 3 + 1] - cy, sz = A[sp * 3 + 2] - cz;
         const uint32_t hxy = pk_bf16(-2.f * sx, -2.f * sy), hz1 = pk_bf16(-2.f * sz, 1.f);
@@ -224,26 +234,30 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
         ovf[u] = false;
     }
 
+    // tile it sits in buffer it & 1; each wave prepares a quarter of every
+    // tile, one tile ahead, and one barrier per tile publishes it (a wave
+    // reaches that barrier only after its reads of the other buffer)
     const int64_t ntiles = (nt + kChTileT - 1) / kChTileT;
     float raw[kChRaw];
-    cham_load_raw(T, nt, 0, lane, raw);
-    cham_prepare(sm, raw, nt, 0, lane, cx, cy, cz);
+    cham_load_raw(T, nt, kChQuarter * wave, lane, raw);
+    cham_prepare(sm, 0, raw, nt, 0, wave, lane, cx, cy, cz);
+    cham_barrier();
     for (int64_t it = 0; it < ntiles; ++it) {
         const int64_t t0 = it * kChTileT;
-        // the next tile's coordinates (past the last tile: all padding, the
-        // preparation below is then unused; no branch in the loop body)
-        cham_load_raw(T, nt, t0 + kChTileT, lane, raw);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the tile is prepared
+        const int buf = (int)(it & 1);
         // A rows of the tile's row blocks: lane l reads row 32 rb + l % 32 of plane l / 32
         i32x4 av[kChRB];
 #pragma unroll
-        for (int rb = 0; rb < kChRB; ++rb) av[rb] = sm.tile[h][32 * rb + col];
+        for (int rb = 0; rb < kChRB; ++rb) av[rb] = sm.tile[buf][h][32 * rb + col];
+        // the next tile's coordinates (past the last tile: all padding, the
+        // preparation below is then unused; no branch in the loop body)
+        cham_load_raw(T, nt, t0 + kChTileT + kChQuarter * wave, lane, raw);
         // mp: this tile's min of the lane's rows, per source. The MFMAs of
         // row block rb + 1 are issued before the fold of row block rb, and
         // no later block's MFMAs move above that fold (two blocks' results
         // live at a time)
-        float mp[KN];
-        auto mfmas = [&](int rb, f32x16 (&d)[KN]) {
+        float mp[KA];
+        auto mfmas = [&](int rb, f32x16 (&d)[KA]) {
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int u = 0; u < KN; ++u)
@@ -251,7 +265,7 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
                                                                __builtin_bit_cast(bf16x8, bop[u]), zero, 0, 0, 0);
             __builtin_amdgcn_s_setprio(0);
         };
-        f32x16 dc[KN], dn[KN];
+        f32x16 dc[KA], dn[KA];
         mfmas(0, dc);
 #pragma unroll
         for (int rb = 0; rb < kChRB; ++rb) {
@@ -295,7 +309,8 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
             s0[u] = lower ? step : s0[u];
             best[u] = bn;
         }
-        cham_prepare(sm, raw, nt, t0 + kChTileT, lane, cx, cy, cz);
+        cham_prepare(sm, buf ^ 1, raw, nt, t0 + kChTileT, wave, lane, cx, cy, cz);
+        cham_barrier();
     }
 
     // the answer in the direct form: the kept tiles inside the window of the
@@ -304,7 +319,7 @@ __device__ __forceinline__ void cham_piece(ChamLds& sm, const float* __restrict_
     // the two row halves of the column are merged the same way
 #pragma unroll
     for (int u = 0; u < KN; ++u) {
-        int64_t sp = (k0 + u) * kChBlk + col;
+        int64_t sp = (k0 + wave + kChWaves * u) * kChBlk + col;
         const bool own = sp < na;
         sp = own ? sp : na - 1;
         const float px = A[sp * 3], py = A[sp * 3 + 1], pz = A[sp * 3 + 2];
@@ -520,13 +535,16 @@ __global__ __launch_bounds__(kFixThreads) void chamfer_fix_kernel(ChamferArgs a)
     }
 }
 
-// One wave per workgroup; see the file comment. Block g of the list is
-// source block g of direction 1 (P against Q) for g < B*nb1, else of
-// direction 2 (Q against P); each direction is batch-major.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MAXSIM_CH_WAVES))) void chamfer_nn_kernel(ChamferArgs a, int64_t nblocks)
+// Workgroups of kChWaves waves; see the file comment. Block g of the list
+// is source block g of direction 1 (P against Q) for g < B*nb1, else of
+// direction 2 (Q against P); each direction is batch-major. A workgroup takes
+// a contiguous run of blocks in pieces of at most kChWaves * kChMaxBlocks
+// blocks of one segment; wave v of a piece takes its blocks v, v + kChWaves, ...
+__global__ __launch_bounds__(kChWaves * 64) __attribute__((amdgpu_waves_per_eu(MAXSIM_CH_WAVES))) void chamfer_nn_kernel(ChamferArgs a, int64_t nblocks)
 {
     __shared__ ChamLds sm;
     const int64_t nw = gridDim.x, w = blockIdx.x;
+    const int wave = (int)(threadIdx.x >> 6);
     const int64_t nb1 = (a.N + kChBlk - 1) / kChBlk, nb2 = (a.M + kChBlk - 1) / kChBlk;
     const int64_t g_first = w * nblocks / nw, g_last = (w + 1) * nblocks / nw;
 
@@ -538,14 +556,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MAXSIM_CH_WA
         const int64_t b = gl / nb, k0 = gl % nb;
         int64_t nk = nb - k0;
         if (nk > g_last - g0) nk = g_last - g0;
-        if (nk > kChMaxBlocks) nk = kChMaxBlocks;
+        if (nk > kChWaves * kChMaxBlocks) nk = kChWaves * kChMaxBlocks;
         g0 += nk;
         const int64_t na = second ? a.M : a.N, nt = second ? a.N : a.M;
         const float* A = (second ? a.Q : a.P) + b * na * 3;
         const float* T = (second ? a.P : a.Q) + b * nt * 3;
         float* dist = (second ? a.dist2 : a.dist1) + b * na;
         int32_t* idx = (second ? a.idx2 : a.idx1) + b * na;
-        switch (__builtin_amdgcn_readfirstlane((int)nk)) {
+        // this wave's blocks of the piece (0 .. kChMaxBlocks)
+        const int kn = nk > wave ? (int)((nk - wave + kChWaves - 1) / kChWaves) : 0;
+        switch (__builtin_amdgcn_readfirstlane(kn)) {
+        case 0: cham_piece<0>(sm, A, na, T, nt, k0, dist, idx); break;
         case 1: cham_piece<1>(sm, A, na, T, nt, k0, dist, idx); break;
         case 2: if constexpr (kChMaxBlocks >= 2) cham_piece<2>(sm, A, na, T, nt, k0, dist, idx); break;
         case 3: if constexpr (kChMaxBlocks >= 3) cham_piece<3>(sm, A, na, T, nt, k0, dist, idx); break;
@@ -605,22 +626,24 @@ hipError_t launch_chamfer_fwd(ChamferArgs a, hipStream_t stream)
 {
     if (a.B == 0) return hipSuccess;
     hipError_t err;
-    // one wave per workgroup and as many waves as are resident at once (the
-    // runs of blocks then end together); each wave holds at most
-    // kChMaxBlocks source blocks, so larger inputs get more waves
+    // as many workgroups as are resident at once (the runs of blocks then end
+    // together); a workgroup holds at most kChWaves * kChMaxBlocks source
+    // blocks at a time, so larger inputs get more workgroups
     static std::atomic<int> per_cu{0};
     int occ = per_cu.load(std::memory_order_relaxed);
     if (occ <= 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, chamfer_nn_kernel, 64, 0) != hipSuccess || occ <= 0)
-            occ = 8;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, chamfer_nn_kernel, kChWaves * 64, 0) != hipSuccess ||
+            occ <= 0)
+            occ = 2;
         per_cu.store(occ, std::memory_order_relaxed);
     }
     const int64_t nblocks = a.B * ((a.N + kChBlk - 1) / kChBlk + (a.M + kChBlk - 1) / kChBlk);
-    int64_t waves = (int64_t)occ * device_cu_count();
-    if (waves * kChMaxBlocks < nblocks) waves = (nblocks + kChMaxBlocks - 1) / kChMaxBlocks;
-    if (waves > nblocks) waves = nblocks;
-    if (waves > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(chamfer_nn_kernel, dim3((unsigned)waves), dim3(64), 0, stream, a, nblocks);
+    constexpr int64_t kPiece = kChWaves * kChMaxBlocks;
+    int64_t wgs = (int64_t)occ * device_cu_count();
+    if (wgs * kPiece < nblocks) wgs = (nblocks + kPiece - 1) / kPiece;
+    if (wgs > nblocks) wgs = nblocks;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(chamfer_nn_kernel, dim3((unsigned)wgs), dim3(kChWaves * 64), 0, stream, a, nblocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t nsrc = a.B * (a.N + a.M);
     hipLaunchKernelGGL(chamfer_fix_kernel, dim3((unsigned)((nsrc + kFixThreads - 1) / kFixThreads)),
