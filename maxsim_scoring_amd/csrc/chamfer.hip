@@ -72,7 +72,7 @@ constexpr int kChRB = kChTileT / 32;          // 32-row blocks per tile
 constexpr int kChWaves = 4;                   // waves per workgroup, sharing the target tiles
 constexpr int kChQuarter = kChTileT / kChWaves;  // targets each wave prepares per tile
 constexpr int kChRaw = kChQuarter * 3 / 64;   // raw coordinates per lane per tile
-static_assert(kChQuarter == 64, "one target per lane per tile");
+static_assert(kChQuarter % 64 == 0, "whole targets per lane per tile");
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void cham_barrier()
@@ -100,7 +100,7 @@ struct ChamLds {
     float raw[kChWaves][kChQuarter * 3];
 };
 
-// Coordinates of targets [t0, t0 + 64) of a set with nt points, one float per
+// Coordinates of targets [t0, t0 + kChQuarter) of a set with nt points, one float per
 // (lane, m) at 64*m + lane: every load instruction reads 256 contiguous
 // bytes. Past the set's end the value is 0.
 __device__ __forceinline__ void cham_load_raw(const float* __restrict__ T, int64_t nt, int64_t t0, int lane,
@@ -122,8 +122,8 @@ __device__ __forceinline__ void cham_load_raw(const float* __restrict__ T, int64
 // against the source columns' -2 hi / -2 lo parts (cham_piece), so one
 // bf16 MFMA gives nh + nl - 2 (<th, sh> + <tl, sh> + <th, sl>). Points past
 // the set's end get hi = lo = 0 and nh = +inf: their value is +inf.
-// Wave `wave` prepares targets [t0 + 64 wave, t0 + 64 wave + 64) of the tile
-// at t0 into buffer `buf`, one per lane, from its coordinates r.
+// Wave `wave` prepares targets [t0 + q wave, t0 + q wave + q) of the tile at
+// t0 (q = kChQuarter) into buffer `buf`, from its coordinates r.
 __device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (&r)[kChRaw], int64_t nt,
                                              int64_t t0, int wave, int lane, float cx, float cy, float cz)
 {
@@ -131,11 +131,14 @@ __device__ __forceinline__ void cham_prepare(ChamLds& sm, int buf, const float (
 #pragma unroll
     for (int m = 0; m < kChRaw; ++m) raw[64 * m + lane] = r[m];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to its reads
-    // odd word stride between lanes: no LDS bank conflicts
-    {
-        const int p = kChQuarter * wave + lane;  // point of the tile
+    // lane l prepares points l, l + 64, ... of the quarter (odd word stride
+    // between lanes: no LDS bank conflicts)
+#pragma unroll
+    for (int v = 0; v < kChQuarter / 64; ++v) {
+        const int ql = lane + 64 * v;            // point of the quarter
+        const int p = kChQuarter * wave + ql;    // point of the tile
         const bool in = t0 + p < nt;
-        const float x = raw[3 * lane] - cx, y = raw[3 * lane + 1] - cy, z = raw[3 * lane + 2] - cz;
+        const float x = raw[3 * ql] - cx, y = raw[3 * ql + 1] - cy, z = raw[3 * ql + 2] - cz;
         const float n = in ? __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x)) : 0.f;
         const uint32_t hxy = pk_bf16(x, y), hzn = pk_bf16(z, n);
         const uint32_t lxy = pk_bf16(x - bf16_lo(hxy), y - bf16_hi(hxy));
