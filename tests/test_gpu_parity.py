@@ -723,6 +723,31 @@ def test_chamfer_exact_ties(ms, oracle_mod):
     _check_chamfer_fwd(oracle_mod, P, Q, got)
 
 
+def test_chamfer_tie_across_many_tiles(ms, oracle_mod):
+    """A source whose nearest distance is tied by targets in six different
+    256-point tiles, more than the search keeps per source, so its answer
+    comes from the direct-form scan of the whole set: the lowest index wins."""
+    _say("chamfer tie across tiles")
+    rng = np.random.default_rng(791)
+    M = 2000
+    Q = rng.standard_normal((1, M, 3)).astype(np.float32)
+    Q /= np.linalg.norm(Q, axis=2, keepdims=True)
+    Q *= 10.0  # every other target at distance 10 from the origin
+    axes = np.array([[1, 0, 0], [0, 1, 0], [0, 0, 1], [-1, 0, 0], [0, -1, 0], [0, 0, -1]], np.float32)
+    where = [5, 300, 700, 1100, 1500, 1900]  # six different tiles
+    for k, j in enumerate(where):
+        Q[0, j] = axes[k]
+    P = np.zeros((1, 3, 3), np.float32)
+    P[0, 1] = [0.5, 0.0, 0.0]   # nearest (1, 0, 0) alone, squared distance 0.25
+    P[0, 2] = [0.0, 0.0, -3.0]  # nearest (0, 0, -1), squared distance 4
+    P, Q = torch.from_numpy(P), torch.from_numpy(Q)
+    got = _chamfer_gpu(ms, P, Q)
+    d1, i1 = got[0], got[1]
+    assert i1[0].tolist() == [5, 5, 1900]
+    assert d1[0].tolist() == [1.0, 0.25, 4.0]
+    _check_chamfer_fwd(oracle_mod, P, Q, got)
+
+
 def test_chamfer_offset_clouds(ms, oracle_mod):
     """Point clouds far from the origin (unit spread around (100, -50, 200)):
     distances and indices still meet the tolerance and the near-tie bound,
