@@ -629,13 +629,20 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, DqLds<G>& sm, int64_t
             }
             float gv[kPerW];
             uint8_t m0[kPerW];
+            // the mask test sits outside the loads (a branch between two
+            // loads makes the second wait for the first)
+            auto load_w = [&](auto has_mask) {
 #pragma unroll
-            for (int u = 0; u < kPerW; ++u) {
-                const int jj = wave + u * kWavesB;
-                const int64_t j = j0 + (jj < nj ? jj : 0);
-                gv[u] = a.g[i * Nd + j];
-                m0[u] = a.d_mask ? a.d_mask[j * Ld + (lane < Ld ? lane : 0)] : (uint8_t)1;
-            }
+                for (int u = 0; u < kPerW; ++u) {
+                    const int jj = wave + u * kWavesB;
+                    const int64_t j = j0 + (jj < nj ? jj : 0);
+                    gv[u] = a.g[i * Nd + j];
+                    if constexpr (decltype(has_mask)::value) m0[u] = a.d_mask[j * Ld + (lane < Ld ? lane : 0)];
+                    else m0[u] = 1;
+                }
+            };
+            if (a.d_mask) load_w(std::true_type{});
+            else load_w(std::false_type{});
 #pragma unroll
             for (int u = 0; u < kPer; ++u) {
                 const int e = tid + u * kThreads, jj = e / G, gg = e % G;
@@ -761,9 +768,12 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
 
     if constexpr (TAB) {
         const int64_t nqr = a.Nq * Lq;
-        if (live && nqr > 0) {
-            // kWTab / kDdThreads entries per thread, every load issued
-            // before any is used (indices past the end read entry 0)
+        // kWTab / kDdThreads entries per thread, every load issued before any
+        // is used (indices past the end read entry 0); the mask test sits
+        // outside the loads, since a branch between two loads makes the
+        // second wait for the first
+        auto stage = [&](auto has_mask) {
+            constexpr bool kMask = decltype(has_mask)::value;
             constexpr int kW = kWTab / kDdThreads;
             SrcWalk w;
             w.init(tid, kDdThreads, Lq);
@@ -774,13 +784,17 @@ __global__ __launch_bounds__(kDdThreads) __attribute__((amdgpu_waves_per_eu(MAXS
                 const int64_t k = tid + (int64_t)u * kDdThreads;
                 const bool ok = k < nqr;
                 gk[u] = a.g[(ok ? (int64_t)w.i : 0) * Nd + j];
-                qm[u] = a.q_mask ? a.q_mask[ok ? k : 0] : (uint8_t)1;
+                if constexpr (kMask) qm[u] = a.q_mask[ok ? k : 0];
             }
 #pragma unroll
             for (int u = 0; u < kW; ++u) {
                 const int64_t k = tid + (int64_t)u * kDdThreads;
-                if (k < nqr) wtab[k] = qm[u] == 0 ? 0.f : gk[u];
+                if (k < nqr) wtab[k] = kMask && qm[u] == 0 ? 0.f : gk[u];
             }
+        };
+        if (live && nqr > 0) {
+            if (a.q_mask) stage(std::true_type{});
+            else stage(std::false_type{});
         }
         barrier_lds();
     }
